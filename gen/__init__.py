@@ -1,0 +1,231 @@
+"""Seeded synthetic inputs for the attention-forward workloads.
+
+This module holds no attention arithmetic: it only turns (seed, counter) pairs
+into numbers, and names the workload shapes. Both the CPU oracle tests and the
+GPU path consume its arrays as inputs.
+
+Uniform source (pulsatrix HIPBackend page, ``dropout_forward`` note): the k-th
+uniform of a seed is the SplitMix64 output for state ``seed + (k + 1) * gamma``
+(gamma = 0x9E3779B97F4A7C15), keeping the top 24 bits as a float in [0, 1).
+SplitMix64 is the generator of Steele, Lea and Flood (OOPSLA 2014).
+
+Normals: Box-Muller in float64 on consecutive counter pairs, scaled by sigma,
+rounded once to float32 (round to nearest even). bf16 inputs are a second
+round-to-nearest-even step from that float32, which is how the oxicuda
+``gemm_mixed_precision`` documentation describes emulating 16-bit storage.
+
+Counter streams: tensor ``t`` (Q=0, K=1, V=2) draws counters ``t * 2**40 + n``.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+import subprocess
+from typing import Dict, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgen.so")
+_lib = None
+
+
+def build_native(force: bool = True) -> str:
+    """Compile gen.c (host C, OpenMP) into gen/libgen.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared",
+                               os.path.join(_HERE, "gen.c"), "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _native():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build_native(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.gen_normal_f32.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
+                                       ctypes.c_double, ctypes.c_void_p]
+        lib.gen_normal_f32.restype = None
+        lib.gen_f32_to_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+        lib.gen_f32_to_bf16.restype = None
+        lib.gen_bf16_to_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+        lib.gen_bf16_to_f32.restype = None
+        _lib = lib
+    return _lib
+
+GAMMA = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+STREAM_STRIDE = 1 << 40
+TENSOR_STREAM = {"q": 0, "k": 1, "v": 2}
+
+_CHUNK = 1 << 22  # elements per vectorised block; bounds temporaries to ~100 MB
+
+
+def splitmix64(x: np.ndarray) -> np.ndarray:
+    """SplitMix64 output function applied to state values ``x`` (uint64, wrapping)."""
+    z = np.asarray(x, dtype=np.uint64).copy()
+    with np.errstate(over="ignore"):
+        z ^= z >> np.uint64(30)
+        z *= _M1
+        z ^= z >> np.uint64(27)
+        z *= _M2
+        z ^= z >> np.uint64(31)
+    return z
+
+
+def uniform24(seed: int, counters: np.ndarray) -> np.ndarray:
+    """uniform(seed, k) for each counter k: top 24 bits of splitmix64(seed + (k+1)*gamma), in [0, 1)."""
+    k = np.asarray(counters, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        state = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) + (k + np.uint64(1)) * GAMMA
+    z = splitmix64(state)
+    return (z >> np.uint64(40)).astype(np.float64) * (1.0 / (1 << 24))
+
+
+def normal_f64(seed: int, first_counter: int, n: int) -> np.ndarray:
+    """n standard normals from counters [first_counter, first_counter + 2*ceil(n/2)).
+
+    Pair p uses u1 = uniform(2p), u2 = uniform(2p+1); element 2p is
+    sqrt(-2 ln(1-u1)) cos(2 pi u2) and element 2p+1 the matching sine.
+    """
+    out = np.empty(n, dtype=np.float64)
+    npairs = (n + 1) // 2
+    for p0 in range(0, npairs, _CHUNK):
+        p1 = min(npairs, p0 + _CHUNK)
+        idx = np.arange(p0, p1, dtype=np.uint64)
+        base = np.uint64(first_counter) + np.uint64(2) * idx
+        u1 = uniform24(seed, base)
+        u2 = uniform24(seed, base + np.uint64(1))
+        r = np.sqrt(-2.0 * np.log1p(-u1))
+        th = (2.0 * math.pi) * u2
+        e0 = 2 * p0
+        e1 = min(n, 2 * p1)
+        blk = np.empty(2 * (p1 - p0), dtype=np.float64)
+        blk[0::2] = r * np.cos(th)
+        blk[1::2] = r * np.sin(th)
+        out[e0:e1] = blk[: e1 - e0]
+    return out
+
+
+def normal_f32(seed: int, first_counter: int, n: int, sigma: float) -> np.ndarray:
+    """The same draws as ``(normal_f64(...) * sigma).astype(float32)``, computed by gen.c."""
+    out = np.empty(n, dtype=np.float32)
+    if n:
+        _native().gen_normal_f32(seed & 0xFFFFFFFFFFFFFFFF, first_counter, n, float(sigma),
+                                 out.ctypes.data)
+    return out
+
+
+def f32_to_bf16_bits_native(x: np.ndarray) -> np.ndarray:
+    """gen.c's float32 -> bfloat16 rounding (same rule as ``f32_to_bf16_bits``)."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    if a.size:
+        _native().gen_f32_to_bf16(a.ctypes.data, out.ctypes.data, a.size)
+    return out
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bit patterns.
+
+    NaN inputs map to a quiet NaN; infinities and overflow to infinity follow
+    from the integer rounding of the bit pattern.
+    """
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (b >> np.uint64(16)) & np.uint64(1)
+    r = ((b + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    if nan.any():
+        r = r.copy()
+        r[nan] = np.uint16(0x7FC0)
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    a = np.ascontiguousarray(b, dtype=np.uint16)
+    out = np.empty(a.shape, dtype=np.float32)
+    if a.size:
+        _native().gen_bf16_to_f32(a.ctypes.data, out.ctypes.data, a.size)
+    return out
+
+
+def tensor_f32(seed: int, which: str, shape: Tuple[int, ...], sigma: float) -> np.ndarray:
+    """A float32 tensor of N(0, sigma^2) draws for stream ``which`` in {"q","k","v"}."""
+    n = int(np.prod(shape, dtype=np.int64))
+    return normal_f32(seed, TENSOR_STREAM[which] * STREAM_STRIDE, n, sigma).reshape(shape)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One attention-forward workload: shapes, dtype, mask, scale and input distribution."""
+
+    name: str
+    dtype: str  # "f32" or "bf16" (input element type; accumulation and O are fp32)
+    batch: int
+    heads: int
+    seq_q: int
+    seq_kv: int
+    head_dim: int
+    causal: bool
+    scale: float
+    sigma_qk: float
+    sigma_v: float
+    seed: int
+
+    @property
+    def q_shape(self):
+        return (self.batch, self.heads, self.seq_q, self.head_dim)
+
+    @property
+    def kv_shape(self):
+        return (self.batch, self.heads, self.seq_kv, self.head_dim)
+
+
+def _w(name, dtype, b, h, sq, skv, d, causal, scale, sqk, sv, cfg_no):
+    return Workload(name, dtype, b, h, sq, skv, d, causal, scale, sqk, sv, 20261201 + cfg_no)
+
+
+# The five workload shapes (config numbers 1..5; the cross-attention shape runs
+# both unmasked and with the bottom-right causal mask, sharing one seed).
+WORKLOADS: Dict[str, Workload] = {
+    "c1": _w("c1_f32_causal_b1h2s128d64", "f32", 1, 2, 128, 128, 64, True, 1.0 / 8.0, 1.0, 1.0, 1),
+    "c2": _w("c2_f32_b4h8s512d64", "f32", 4, 8, 512, 512, 64, False, 1.0 / math.sqrt(64), 1.0, 1.0, 2),
+    "c3": _w("c3_f32_causal_b8h16s2048d128", "f32", 8, 16, 2048, 2048, 128, True, 1.0 / math.sqrt(128), 1.0, 1.0, 3),
+    "c4n": _w("c4n_f32_cross_b2h32q256kv4096d128", "f32", 2, 32, 256, 4096, 128, False, 1.0 / math.sqrt(128), 1.0, 1.0, 4),
+    "c4c": _w("c4c_f32_cross_causal_br_b2h32q256kv4096d128", "f32", 2, 32, 256, 4096, 128, True, 1.0 / math.sqrt(128), 1.0, 1.0, 4),
+    "c5": _w("c5_bf16_causal_b1h32s16384d128", "bf16", 1, 32, 16384, 16384, 128, True, 1.0 / math.sqrt(128), 3.0, 1.0, 5),
+}
+
+
+def make_inputs(w: Workload):
+    """Host inputs for a workload.
+
+    Returns (q, k, v) as float32 arrays holding the exact input values, plus,
+    for bf16 workloads, the uint16 bit patterns (qb, kb, vb) the device consumes.
+    """
+    q = tensor_f32(w.seed, "q", w.q_shape, w.sigma_qk)
+    k = tensor_f32(w.seed, "k", w.kv_shape, w.sigma_qk)
+    v = tensor_f32(w.seed, "v", w.kv_shape, w.sigma_v)
+    if w.dtype == "f32":
+        return (q, k, v), None
+    bits = tuple(f32_to_bf16_bits_native(t) for t in (q, k, v))
+    vals = tuple(bf16_bits_to_f32(b) for b in bits)
+    return vals, bits
+
+
+def random_case(seed: int, shape_q, shape_kv, sigma_qk=1.0, sigma_v=1.0, dtype="f32"):
+    """Inputs for an ad-hoc (test) shape, from the same streams as ``make_inputs``."""
+    q = tensor_f32(seed, "q", tuple(shape_q), sigma_qk)
+    k = tensor_f32(seed, "k", tuple(shape_kv), sigma_qk)
+    v = tensor_f32(seed, "v", tuple(shape_kv), sigma_v)
+    if dtype == "f32":
+        return (q, k, v), None
+    bits = tuple(f32_to_bf16_bits_native(t) for t in (q, k, v))
+    return tuple(bf16_bits_to_f32(b) for b in bits), bits

@@ -1,0 +1,111 @@
+"""Attention-forward oracle -- TEST INFRASTRUCTURE ONLY.
+
+A plain double-precision CPU statement of the attention forward pass
+(attention_oracle.c holds the arithmetic and states the definition it follows:
+the ``attention`` call of the oxicuda ComputeBackend page, max-subtracted
+softmax and log-sum-exp as on the pulsatrix HIPBackend page, and the empty-row
+convention of the TorchLean hard-masked softmax).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The attention library never does, and
+the two share no code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attention_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True, out: str | None = None, defines=()) -> str:
+    """Compile the oracle with gcc (host only). ``defines`` is for planted-mistake builds."""
+    out = out or _LIB_PATH
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared"] + ["-D" + d for d in defines]
+        cmd += [_SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, out)
+    return out
+
+
+def _bind(lib):
+    dp = ctypes.c_void_p
+    L = ctypes.c_long
+    lib.oracle_attention_fwd.argtypes = [dp, dp, dp, L, L, L, L, L, ctypes.c_double, ctypes.c_int,
+                                         dp, L, dp, dp]
+    lib.oracle_attention_fwd.restype = ctypes.c_int
+    lib.oracle_attention_probs.argtypes = [dp, dp, L, L, L, ctypes.c_double, ctypes.c_int, dp]
+    lib.oracle_attention_probs.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    return lib
+
+
+def load(path: str | None = None):
+    """The oracle library at ``path`` (default: the in-tree build, built if missing)."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def attention_fwd(q, k, v, scale: float, causal: bool, rows=None, lib=None):
+    """O and LSE in float64.
+
+    q: [B,H,Sq,D]; k, v: [B,H,Skv,D] (values as float32, exact for bf16 inputs).
+    rows: optional flat row ids (b*H + h)*Sq + i; then O is [len(rows), D] and LSE [len(rows)].
+    """
+    lib = lib or load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    assert k.shape == (B, H, Skv, D) and v.shape == (B, H, Skv, D)
+    if rows is None:
+        o = np.empty((B, H, Sq, D), dtype=np.float64)
+        lse = np.empty((B, H, Sq), dtype=np.float64)
+        rp, nr = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        o = np.empty((rows.size, D), dtype=np.float64)
+        lse = np.empty((rows.size,), dtype=np.float64)
+        rp, nr = rows.ctypes.data, rows.size
+    rc = lib.oracle_attention_fwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Sq, Skv, D,
+                                  float(scale), int(bool(causal)), rp, nr, o.ctypes.data,
+                                  lse.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_attention_fwd rejected its arguments")
+    return o, lse
+
+
+def softmax_probs(q_bh, k_bh, scale: float, causal: bool, lib=None):
+    """P[i, j] for one (batch, head): q_bh [Sq, D], k_bh [Skv, D]."""
+    lib = lib or load()
+    q_bh, k_bh = _f32(q_bh), _f32(k_bh)
+    Sq, D = q_bh.shape
+    Skv = k_bh.shape[0]
+    p = np.empty((Sq, Skv), dtype=np.float64)
+    rc = lib.oracle_attention_probs(q_bh.ctypes.data, k_bh.ctypes.data, Sq, Skv, D, float(scale),
+                                    int(bool(causal)), p.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_attention_probs rejected its arguments")
+    return p
+
+
+def num_threads(lib=None) -> int:
+    return int((lib or load()).oracle_num_threads())

@@ -1,0 +1,70 @@
+"""The seeded input generator: published SplitMix64 values, bfloat16 rounding, determinism."""
+import json
+import os
+
+import numpy as np
+
+import gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_splitmix64_published_seed0_outputs():
+    with open(os.path.join(GOLDEN, "splitmix64_seed0.json")) as f:
+        ref = json.load(f)
+    k = np.arange(1, 4, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        states = k * gen.GAMMA
+    got = [f"{int(z):016x}" for z in gen.splitmix64(states)]
+    assert got == ref["outputs_hex"]
+
+
+def test_uniform24_is_top_24_bits():
+    u = gen.uniform24(0, np.arange(3, dtype=np.uint64))
+    with open(os.path.join(GOLDEN, "splitmix64_seed0.json")) as f:
+        ref = json.load(f)
+    exp = [(int(h, 16) >> 40) / float(1 << 24) for h in ref["outputs_hex"]]
+    assert list(u) == exp
+    big = gen.uniform24(987, np.arange(100000, dtype=np.uint64))
+    assert big.min() >= 0.0 and big.max() < 1.0
+    assert np.all((big * (1 << 24)) == np.floor(big * (1 << 24)))
+
+
+def test_bf16_round_to_nearest_even_cases():
+    with open(os.path.join(GOLDEN, "bf16_rne_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    x = np.array([c["f32"] for c in cases], dtype=np.float32)
+    exp = [int(c["bf16_hex"], 16) for c in cases]
+    assert list(gen.f32_to_bf16_bits(x)) == exp
+    assert list(gen.f32_to_bf16_bits_native(x)) == exp
+    w = gen.bf16_bits_to_f32(np.array(exp, dtype=np.uint16))
+    assert np.all(gen.f32_to_bf16_bits(w) == np.array(exp, dtype=np.uint16))
+
+
+def test_native_generator_matches_numpy_definition():
+    for seed, first, n, sigma in [(7, 0, 1001, 1.0), (20261205, 2 << 40, 4097, 3.0), (1, 1 << 40, 1, 1.0)]:
+        ref = (gen.normal_f64(seed, first, n) * sigma).astype(np.float32)
+        got = gen.normal_f32(seed, first, n, sigma)
+        assert np.array_equal(ref, got)
+    x = (np.random.default_rng(0).standard_normal(200000) * 50).astype(np.float32)
+    assert np.array_equal(gen.f32_to_bf16_bits(x), gen.f32_to_bf16_bits_native(x))
+
+
+def test_workload_inputs_deterministic_and_distinct():
+    w = gen.WORKLOADS["c1"]
+    (q1, k1, v1), _ = gen.make_inputs(w)
+    (q2, k2, v2), _ = gen.make_inputs(w)
+    assert np.array_equal(q1, q2) and np.array_equal(k1, k2) and np.array_equal(v1, v2)
+    assert not np.array_equal(q1.ravel()[:100], k1.ravel()[:100])
+    assert q1.shape == (1, 2, 128, 64)
+    assert abs(float(q1.std()) - 1.0) < 0.05 and abs(float(q1.mean())) < 0.05
+
+
+def test_bf16_workload_values_are_bf16():
+    w = gen.WORKLOADS["c1"]
+    (q, k, v), bits = gen.random_case(5, (1, 2, 64, 32), (1, 2, 48, 32), sigma_qk=3.0, dtype="bf16")
+    for vals, b in zip((q, k, v), bits):
+        assert b.dtype == np.uint16
+        assert np.array_equal(gen.bf16_bits_to_f32(b), vals)
+        assert np.all((vals.view(np.uint32) & 0xFFFF) == 0)
+    assert abs(float(q.std()) - 3.0) < 0.1
