@@ -1,0 +1,236 @@
+"""Attention-forward benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2|c1|c3|c4n|c4c|c5]
+
+A step is one attention forward (every kernel of the path) over the
+workload's synthetic inputs, already resident in HBM. Prints one JSON line:
+the headline TFLOP/s on the metric's FLOP formula (4*B*H*Sq*Skv*d, halved when
+causal), the fraction of the dtype's dense MFMA peak, a roofline object for
+the main attention kernel timed with HIP events inside the timed region, and
+the CPU oracle timed on a bounded sample of the same workload on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (4·B·H·Sq·Skv·d, causal halved) and % of MFMA peak"
+# MI355X published dense MFMA peaks (TFLOP/s) and HBM bandwidth (GB/s).
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+HBM_GBPS = 8000.0
+DEFAULT_WORKLOAD = "c2"  # the second configuration of the five
+
+
+def metric_flops(w) -> float:
+    f = 4.0 * w.batch * w.heads * w.seq_q * w.seq_kv * w.head_dim
+    return f / 2 if w.causal else f
+
+
+def allowed_pairs(w) -> int:
+    """Admitted (query, key) pairs: all, or j <= i + Skv - Sq under the causal mask."""
+    if not w.causal:
+        return w.batch * w.heads * w.seq_q * w.seq_kv
+    off = w.seq_kv - w.seq_q
+    per = 0
+    for i in range(w.seq_q):
+        per += min(max(i + off + 1, 0), w.seq_kv)
+    return per * w.batch * w.heads
+
+
+def min_bytes(w) -> int:
+    e = 4 if w.dtype == "f32" else 2
+    bh = w.batch * w.heads
+    return bh * ((w.seq_q + 2 * w.seq_kv) * w.head_dim * e + w.seq_q * w.head_dim * 4 + w.seq_q * 4)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (torch's events only see torch streams)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventSynchronize(b) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+def read_traffic(workload: str, kernel_src_digest: str):
+    """HBM bytes per launch from the committed counter summary, or None if absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_src_digest:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "scaled_masked_attention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def cpu_baseline(w, vals, target_s: float):
+    """The oracle on a bounded sample of rows of the same workload, scaled to TFLOP/s."""
+    import numpy as np
+
+    import oracle
+
+    B, H, sq, skv = w.batch, w.heads, w.seq_q, w.seq_kv
+    total_rows = B * H * sq
+    rng = np.random.default_rng(0)
+    # Calibrate on a small row sample, then size the sample for ~target_s seconds.
+    n0 = min(total_rows, 64)
+    rows0 = np.sort(rng.choice(total_rows, size=n0, replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attention_fwd(*vals, w.scale, w.causal, rows=rows0)
+    dt0 = max(time.perf_counter() - t0, 1e-4)
+    n = int(min(total_rows, max(n0, n0 * target_s / dt0)))
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False)).astype(np.int64)
+    passes = 0
+    t0 = time.perf_counter()
+    while True:  # whole passes over the sample until the time target is reached
+        oracle.attention_fwd(*vals, w.scale, w.causal, rows=rows)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s or passes >= 1000:
+            break
+    # metric FLOPs attributable to the sampled rows (each row's share of the formula)
+    frac = n / total_rows
+    flops = metric_flops(w) * frac * passes
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} of {total_rows} query rows chosen at random (seed 0), all keys each, "
+                      f"{passes} pass(es) in {dt:.1f} s; metric FLOPs scaled by the row fraction"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention path is not sharded across GPUs in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gen
+    import scaled_masked_attention_amd as sma
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w = gen.WORKLOADS[args.workload]
+    vals, bits = gen.make_inputs(w)
+    if w.dtype == "f32":
+        tq, tk, tv = (torch.from_numpy(x).to("cuda") for x in vals)
+        in_dt = sma.SMA_DTYPE_F32
+    else:
+        tq, tk, tv = (torch.from_numpy(b.view(np.int16)).to("cuda").view(torch.bfloat16) for b in bits)
+        in_dt = sma.SMA_DTYPE_BF16
+    B, H, sq, skv, d = w.batch, w.heads, w.seq_q, w.seq_kv, w.head_dim
+    out = torch.empty((B, H, sq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H, sq), dtype=torch.float32, device="cuda")
+    ws_n = sma.workspace_bytes(in_dt, B, H, sq, skv, d, w.causal)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    ev = HipEvents()
+    nev = args.steps
+    ev_a = [ev.create() for _ in range(nev)]
+    ev_b = [ev.create() for _ in range(nev)]
+    call = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(), in_dt,
+            sma.SMA_DTYPE_F32, B, H, sq, skv, d, w.scale, w.causal, ws.data_ptr(), ws_n, sptr)
+
+    for _ in range(args.warmup):
+        sma.attention_fwd_raw(*call)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        sma.attention_fwd_timed_raw(*call, ev_a[i], ev_b[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kernel_ms = [ev.elapsed_ms(ev_a[i], ev_b[i]) for i in range(args.steps)]
+    for e in ev_a + ev_b:
+        ev.destroy(e)
+    k_avg = sum(kernel_ms) / len(kernel_ms)
+    assert torch.isfinite(out).all().item(), "non-finite output"
+
+    value = metric_flops(w) / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    exact = 4.0 * d * allowed_pairs(w)
+    achieved = exact / (k_avg * 1e-3) / 1e12
+    traffic = read_traffic(args.workload, kernel_source_digest())
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded SplitMix64 + Box-Muller normals)",
+        "config": {"workload": w.name, "batch": B, "heads": H, "seq_q": sq, "seq_kv": skv,
+                   "head_dim": d, "causal": w.causal, "scale": w.scale,
+                   "input_dtype": w.dtype, "accumulate": "f32", "output": "f32", "lse": True,
+                   "key_splits_workspace_bytes": ws_n},
+        "pct_of_mfma_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": f"attn_fwd_{w.dtype}_kernel<{d},{str(w.causal).lower()}>",
+                     "kernel_avg_ms": round(k_avg, 5),
+                     "flops_per_launch": exact,
+                     "min_hbm_bytes_per_launch": min_bytes(w)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, vals, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

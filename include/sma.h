@@ -1,0 +1,134 @@
+/* sma.h -- C ABI of the scaled masked attention forward library (libsma.so, gfx950).
+ *
+ * The operation (oxicuda ComputeBackend page, documentation of `attention`):
+ * for every batch b and head h,
+ *
+ *     O = softmax(scale * Q K^T + mask) V
+ *
+ * with the scale a multiplier of QK^T (its usual value is 1/sqrt(head_dim)) and
+ * an optional causal mask that keeps the lower triangle. The pieces fixed by
+ * the other pages:
+ *   - scale, mask and softmax fuse into one pass over the scores, in that order
+ *     (MicroGPT CuBLASBackend page, `fused_attn_softmax`);
+ *   - the softmax is the max-subtracted row softmax, and the optional per-row
+ *     output is the log-sum-exp log(sum_j exp(s_ij)) of the same scores
+ *     (pulsatrix HIPBackend page, `softmax_rows` and `logsumexp_rows`);
+ *   - masked scores take no part in the row max or the denominator, and a row
+ *     in which the mask admits no key is all zeros (TorchLean Kernels page,
+ *     hard-masked softmax); its log-sum-exp is -infinity, the log of an empty sum;
+ *   - bf16 operands are multiplied with fp32 accumulation and an fp32 result
+ *     (oxicuda ComputeBackend page, `gemm_mixed_precision`).
+ *
+ * Causal alignment. With seq_q != seq_kv the mask is bottom-right aligned:
+ * query i may attend key j iff j <= i + seq_kv - seq_q. For seq_q == seq_kv
+ * this is j <= i. When seq_q > seq_kv the first seq_q - seq_kv query rows see
+ * no key and are written as +0.0 (LSE -inf).
+ *
+ * Layout (contiguous, row-major, no strides):
+ *   q, o  [batch][heads][seq_q][head_dim]
+ *   k, v  [batch][heads][seq_kv][head_dim]
+ *   lse   [batch][heads][seq_q]     fp32, natural log
+ *
+ * Ownership and threading. The caller owns every buffer (device memory on
+ * the current HIP device) and the stream. The library never allocates, frees
+ * or synchronizes; it keeps only a per-device property cache filled on first
+ * use. Calls are reentrant and may come from several host threads. Kernels
+ * run asynchronously on `stream`; a fault inside a kernel surfaces at the
+ * caller's next synchronization. Results are deterministic: the same inputs
+ * and sizes give bitwise-identical outputs (no atomics).
+ *
+ * Errors are returned as sma_status codes; nothing is thrown across the ABI.
+ * Host-side argument errors launch nothing.
+ */
+#ifndef SMA_H
+#define SMA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMA_ABI_VERSION 1
+
+/* Element types. Accumulation is always fp32. */
+typedef enum {
+  SMA_DTYPE_F32 = 0,  /* IEEE binary32 */
+  SMA_DTYPE_BF16 = 1  /* bfloat16 (binary32 with the low 16 fraction bits dropped) */
+} sma_dtype;
+
+typedef enum {
+  SMA_OK = 0,
+  SMA_ERR_NULL_POINTER = 1,  /* a required pointer is NULL */
+  SMA_ERR_INVALID_VALUE = 2, /* bad size, dtype code, non-finite scale, size overflow */
+  SMA_ERR_UNSUPPORTED = 3,   /* valid request the kernels do not implement (head_dim, dtype pair, grid limit) */
+  SMA_ERR_MISALIGNED = 4,    /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
+  SMA_ERR_ALIASING = 5,      /* o or lse overlaps q, k, v, the workspace, or each other */
+  SMA_ERR_HIP = 6            /* the HIP runtime reported an error (device query or launch) */
+} sma_status;
+
+/* Attention forward.
+ *
+ *   q, k, v    device pointers, element type in_dtype, layout above. k and v may
+ *              be NULL only when seq_kv == 0; q and o only when batch*heads*seq_q == 0.
+ *   o          device pointer, element type o_dtype, fully overwritten.
+ *   lse        device pointer to batch*heads*seq_q floats, or NULL for no LSE output.
+ *   in_dtype   SMA_DTYPE_F32 or SMA_DTYPE_BF16.
+ *   o_dtype    SMA_DTYPE_F32 (the only output type implemented; others -> UNSUPPORTED).
+ *   head_dim   64 or 128 (0 -> INVALID_VALUE, other values -> UNSUPPORTED).
+ *   scale      finite multiplier of QK^T (zero and negative values are allowed).
+ *   causal     0: no mask; nonzero: bottom-right causal mask.
+ *   workspace  optional device scratch for splitting the keys of a row across
+ *              workgroups (used when there are too few query blocks to fill the
+ *              GPU); NULL or too small just disables splitting, which stays correct.
+ *              sma_attention_fwd_workspace_bytes gives the size that enables it.
+ *              It must not overlap any other argument. Contents on entry do not matter.
+ *   stream     hipStream_t to launch on; NULL means the null stream.
+ *
+ * batch*heads*seq_q == 0 returns SMA_OK and launches nothing. seq_kv == 0 writes
+ * o = +0.0 and lse = -inf for every row.
+ */
+int sma_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
+                      size_t seq_kv, size_t head_dim, double scale, int causal, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Measurement hook: exactly sma_attention_fwd, and in addition records the
+ * caller's HIP events (hipEvent_t handles, either may be NULL) on `stream`
+ * immediately before and after the main attention kernel, so that its
+ * duration can be read with hipEventElapsedTime apart from the split-combine
+ * kernel that may follow it. The events are recorded only when the call
+ * launches (status SMA_OK with work to do). */
+int sma_attention_fwd_timed(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
+                            size_t seq_kv, size_t head_dim, double scale, int causal,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* event_before, void* event_after);
+
+/* The same checks as sma_attention_fwd, on the host only: no HIP call, nothing
+ * launched, pointers are not dereferenced. Returns the status sma_attention_fwd
+ * would return before launching. */
+int sma_attention_fwd_validate(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, int in_dtype, int o_dtype, size_t batch,
+                               size_t heads, size_t seq_q, size_t seq_kv, size_t head_dim,
+                               double scale, int causal, const void* workspace,
+                               size_t workspace_bytes);
+
+/* Workspace bytes that let sma_attention_fwd split keys across workgroups for
+ * this shape on a GPU with num_cus compute units (pass 0 for the current HIP
+ * device; if it cannot be queried, 256 is assumed). 0 means splitting is never
+ * used for this shape. Invalid arguments also give 0. */
+size_t sma_attention_fwd_workspace_bytes(int in_dtype, size_t batch, size_t heads, size_t seq_q,
+                                         size_t seq_kv, size_t head_dim, int causal, int num_cus);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* sma_status_string(int status);
+
+/* SMA_ABI_VERSION of the built library. */
+int sma_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMA_H */

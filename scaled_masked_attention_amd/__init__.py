@@ -1,0 +1,165 @@
+"""Scaled masked attention forward for MI355X (gfx950).
+
+A thin ctypes binding over libsma.so (C ABI in include/sma.h). This module only
+marshals arguments: torch provides device memory and the current stream, and
+every step of the computation runs in the library's HIP kernels. If the
+library has not been built, importing works but every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsma.so")
+
+SMA_DTYPE_F32 = 0
+SMA_DTYPE_BF16 = 1
+SMA_OK = 0
+STATUS_NAMES = {0: "SMA_OK", 1: "SMA_ERR_NULL_POINTER", 2: "SMA_ERR_INVALID_VALUE",
+                3: "SMA_ERR_UNSUPPORTED", 4: "SMA_ERR_MISALIGNED", 5: "SMA_ERR_ALIASING",
+                6: "SMA_ERR_HIP"}
+
+_lib = None
+
+
+class SMAError(RuntimeError):
+    """A non-zero status from libsma."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library():
+    """The loaded libsma (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m scaled_masked_attention_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        lib.sma_attention_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, sz, sz,
+                                          sz, sz, sz, ctypes.c_double, ctypes.c_int, vp, sz, vp]
+        lib.sma_attention_fwd.restype = ctypes.c_int
+        lib.sma_attention_fwd_timed.argtypes = lib.sma_attention_fwd.argtypes + [vp, vp]
+        lib.sma_attention_fwd_timed.restype = ctypes.c_int
+        lib.sma_attention_fwd_validate.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int,
+                                                   sz, sz, sz, sz, sz, ctypes.c_double,
+                                                   ctypes.c_int, vp, sz]
+        lib.sma_attention_fwd_validate.restype = ctypes.c_int
+        lib.sma_attention_fwd_workspace_bytes.argtypes = [ctypes.c_int, sz, sz, sz, sz, sz,
+                                                          ctypes.c_int, ctypes.c_int]
+        lib.sma_attention_fwd_workspace_bytes.restype = sz
+        lib.sma_status_string.argtypes = [ctypes.c_int]
+        lib.sma_status_string.restype = ctypes.c_char_p
+        lib.sma_abi_version.argtypes = []
+        lib.sma_abi_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return library().sma_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(library().sma_abi_version())
+
+
+def _raise(st: int):
+    if st != SMA_OK:
+        raise SMAError(st, status_string(st))
+
+
+def workspace_bytes(in_dtype: int, batch: int, heads: int, seq_q: int, seq_kv: int,
+                    head_dim: int, causal: bool, num_cus: int = 0) -> int:
+    return int(library().sma_attention_fwd_workspace_bytes(in_dtype, batch, heads, seq_q, seq_kv,
+                                                           head_dim, int(bool(causal)), num_cus))
+
+
+def validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dtype, batch, heads, seq_q, seq_kv,
+             head_dim, scale, causal, ws_ptr=None, ws_bytes=0) -> int:
+    """Host-only argument check on raw integer addresses (no HIP call); returns the status."""
+    return int(library().sma_attention_fwd_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype,
+                                                    o_dtype, batch, heads, seq_q, seq_kv, head_dim,
+                                                    float(scale), int(bool(causal)), ws_ptr,
+                                                    ws_bytes))
+
+
+def attention_fwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dtype, batch, heads,
+                      seq_q, seq_kv, head_dim, scale, causal, ws_ptr, ws_bytes, stream) -> None:
+    """sma_attention_fwd on raw addresses; raises SMAError on a non-zero status."""
+    _raise(library().sma_attention_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dtype,
+                                       batch, heads, seq_q, seq_kv, head_dim, float(scale),
+                                       int(bool(causal)), ws_ptr, ws_bytes, stream))
+
+
+def attention_fwd_timed_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dtype, batch, heads,
+                            seq_q, seq_kv, head_dim, scale, causal, ws_ptr, ws_bytes, stream,
+                            event_before, event_after) -> None:
+    """sma_attention_fwd_timed: also records two caller-owned hipEvent_t around the main kernel."""
+    _raise(library().sma_attention_fwd_timed(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype,
+                                             o_dtype, batch, heads, seq_q, seq_kv, head_dim,
+                                             float(scale), int(bool(causal)), ws_ptr, ws_bytes,
+                                             stream, event_before, event_after))
+
+
+def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=None,
+                  workspace=None, stream=None):
+    """O = softmax(scale * Q K^T + mask) V on the GPU.
+
+    q [B,H,Sq,D], k and v [B,H,Skv,D]: contiguous torch tensors on the current
+    HIP device, all float32 or all bfloat16. Returns O (float32, [B,H,Sq,D]) and,
+    with return_lse, the per-row natural-log LSE (float32, [B,H,Sq]).
+    scale=None means 1/sqrt(D). causal uses the bottom-right alignment.
+    """
+    import torch
+
+    if not (isinstance(q, torch.Tensor) and isinstance(k, torch.Tensor) and isinstance(v, torch.Tensor)):
+        raise TypeError("q, k, v must be torch tensors")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [batch, heads, seq, head_dim]")
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if tuple(k.shape) != (B, H, Skv, D) or tuple(v.shape) != (B, H, Skv, D):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    if q.dtype == torch.float32:
+        in_dt = SMA_DTYPE_F32
+    elif q.dtype == torch.bfloat16:
+        in_dt = SMA_DTYPE_BF16
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = torch.device("cuda", torch.cuda.current_device())
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the current HIP device is {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    for name, t in (("out", out), ("lse", lse)):
+        if t is not None and (t.device != dev or t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 tensor on {dev}")
+    if out.shape != (B, H, Sq, D) or (lse is not None and lse.shape != (B, H, Sq)):
+        raise ValueError("out/lse shape mismatch")
+    need = workspace_bytes(in_dt, B, H, Sq, Skv, D, causal)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    attention_fwd_raw(q.data_ptr(), k.data_ptr() if Skv else None, v.data_ptr() if Skv else None,
+                      out.data_ptr(), lse.data_ptr() if lse is not None else None, in_dt,
+                      SMA_DTYPE_F32, B, H, Sq, Skv, D, scale, causal, ws_ptr, ws_bytes,
+                      stream.cuda_stream)
+    return (out, lse) if return_lse else out

@@ -1,0 +1,297 @@
+// C-ABI host layer of libsma: argument checks, launch planning and kernel
+// launches on the caller's stream. No allocation, no synchronization.
+//
+// Conventions carried over from the backend pages: sizes and raw device
+// pointers at the boundary (oxicuda ComputeBackend `attention`), status codes
+// rather than exceptions (its BackendResult / BackendError::Unsupported),
+// outputs that must not alias inputs (pulsatrix HIPBackend `gemm_ex`), and an
+// idempotent lazily filled device cache (oxicuda `init`).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "sma.h"
+#include "sma_kernels.h"
+
+namespace {
+
+constexpr size_t kMaxSeq = size_t(1) << 30;     // keeps the kernels' int32 key/row math exact
+constexpr size_t kMaxWorkgroups = (size_t(1) << 32) / sma::kThreadsPerWG - 1;
+constexpr int kMaxSplits = 32;
+constexpr size_t kWsAlign = 256;
+
+struct Shape {
+  int in_dtype, o_dtype;
+  size_t batch, heads, seq_q, seq_kv, d;
+  size_t bh, rows;                       // batch*heads, batch*heads*seq_q
+  size_t q_bytes, kv_bytes, o_bytes, lse_bytes;
+};
+
+bool mul(size_t a, size_t b, size_t* out) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+size_t elem_bytes(int dt) { return dt == SMA_DTYPE_F32 ? 4 : 2; }
+
+// Checks that do not depend on pointers. Fills sh on success.
+int check_shape(int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
+                size_t d, double scale, Shape* sh) {
+  if (in_dtype != SMA_DTYPE_F32 && in_dtype != SMA_DTYPE_BF16) return SMA_ERR_INVALID_VALUE;
+  if (o_dtype != SMA_DTYPE_F32 && o_dtype != SMA_DTYPE_BF16) return SMA_ERR_INVALID_VALUE;
+  if (d == 0) return SMA_ERR_INVALID_VALUE;
+  if (!std::isfinite(scale)) return SMA_ERR_INVALID_VALUE;
+  Shape s{};
+  s.in_dtype = in_dtype;
+  s.o_dtype = o_dtype;
+  s.batch = batch;
+  s.heads = heads;
+  s.seq_q = seq_q;
+  s.seq_kv = seq_kv;
+  s.d = d;
+  size_t nq, nkv, t;
+  if (!mul(batch, heads, &s.bh) || !mul(s.bh, seq_q, &s.rows) || !mul(s.rows, d, &nq) ||
+      !mul(s.bh, seq_kv, &t) || !mul(t, d, &nkv) || !mul(nq, elem_bytes(in_dtype), &s.q_bytes) ||
+      !mul(nkv, elem_bytes(in_dtype), &s.kv_bytes) || !mul(nq, elem_bytes(o_dtype), &s.o_bytes) ||
+      !mul(s.rows, sizeof(float), &s.lse_bytes))
+    return SMA_ERR_INVALID_VALUE;
+  if (d != 64 && d != 128) return SMA_ERR_UNSUPPORTED;
+  if (o_dtype != SMA_DTYPE_F32) return SMA_ERR_UNSUPPORTED;
+  if (seq_q > kMaxSeq || seq_kv > kMaxSeq || s.bh > (size_t(1) << 31)) return SMA_ERR_UNSUPPORTED;
+  *sh = s;
+  return SMA_OK;
+}
+
+struct Plan {
+  int32_t nqb = 0, nsplit = 1, split_len = 0;
+  size_t nwg = 0;
+  size_t ws_bytes = 0;       // workspace the split needs (0 when nsplit == 1)
+  size_t part_lse_off = 0;   // byte offset of the partial LSE array in the workspace
+};
+
+int queries_per_wg(int dt) { return dt == SMA_DTYPE_F32 ? sma::kF32QueriesPerWG : sma::kBF16QueriesPerWG; }
+int keys_per_tile(int dt) { return dt == SMA_DTYPE_F32 ? sma::kF32KeysPerTile : sma::kBF16KeysPerTile; }
+
+size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+// Key splitting when the query blocks alone cannot fill the GPU: aim for one
+// resident workgroup per slot, keep at least four key tiles per split.
+Plan make_plan(const Shape& s, int num_cus) {
+  Plan p;
+  const size_t qpw = (size_t)queries_per_wg(s.in_dtype);
+  const size_t kt = (size_t)keys_per_tile(s.in_dtype);
+  p.nqb = (int32_t)((s.seq_q + qpw - 1) / qpw);
+  const size_t base = s.bh * (size_t)p.nqb;
+  const size_t slots = (size_t)(num_cus > 0 ? num_cus : 256) * (s.in_dtype == SMA_DTYPE_F32 ? 2 : 1);
+  size_t nsplit = 1;
+  if (base > 0 && base < slots && s.seq_kv >= 8 * kt) {
+    size_t want = (slots + base - 1) / base;
+    size_t by_keys = s.seq_kv / (4 * kt);
+    nsplit = want < by_keys ? want : by_keys;
+    if (nsplit > (size_t)kMaxSplits) nsplit = kMaxSplits;
+    if (nsplit < 1) nsplit = 1;
+  }
+  size_t split_len = s.seq_kv;
+  if (nsplit > 1) {
+    split_len = round_up((s.seq_kv + nsplit - 1) / nsplit, kt);
+    nsplit = (s.seq_kv + split_len - 1) / split_len;
+  }
+  if (split_len == 0) split_len = kt;
+  p.nsplit = (int32_t)nsplit;
+  p.split_len = (int32_t)split_len;
+  p.nwg = base * nsplit;
+  if (nsplit > 1) {
+    const size_t part_o = nsplit * s.rows * s.d * sizeof(float);
+    p.part_lse_off = round_up(part_o, kWsAlign);
+    p.ws_bytes = p.part_lse_off + round_up(nsplit * s.rows * sizeof(float), kWsAlign);
+  }
+  return p;
+}
+
+Plan plan_without_split(const Shape& s) {
+  Plan p;
+  const size_t qpw = (size_t)queries_per_wg(s.in_dtype);
+  p.nqb = (int32_t)((s.seq_q + qpw - 1) / qpw);
+  p.nsplit = 1;
+  p.split_len = (int32_t)(s.seq_kv > 0 ? s.seq_kv : keys_per_tile(s.in_dtype));
+  p.nwg = s.bh * (size_t)p.nqb;
+  return p;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_pointers(const Shape& s, const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* ws, size_t ws_bytes) {
+  if (!q || !o) return SMA_ERR_NULL_POINTER;
+  if (s.seq_kv > 0 && (!k || !v)) return SMA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(o, 16)) return SMA_ERR_MISALIGNED;
+  if (s.seq_kv > 0 && (!aligned(k, 16) || !aligned(v, 16))) return SMA_ERR_MISALIGNED;
+  if (lse && !aligned(lse, 4)) return SMA_ERR_MISALIGNED;
+  if (ws && ws_bytes > 0 && !aligned(ws, 16)) return SMA_ERR_MISALIGNED;
+  const size_t kvb = s.seq_kv > 0 ? s.kv_bytes : 0;
+  const size_t lb = lse ? s.lse_bytes : 0;
+  const size_t wb = ws ? ws_bytes : 0;
+  const void* outs[3] = {o, lse, ws};
+  const size_t out_n[3] = {s.o_bytes, lb, wb};
+  const void* ins[3] = {q, k, v};
+  const size_t in_n[3] = {s.q_bytes, kvb, kvb};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlap(outs[i], out_n[i], ins[j], in_n[j])) return SMA_ERR_ALIASING;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], out_n[i], outs[j], out_n[j])) return SMA_ERR_ALIASING;
+  }
+  return SMA_OK;
+}
+
+int validate_all(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
+                 size_t d, double scale, const void* ws, size_t ws_bytes, Shape* sh) {
+  int st = check_shape(in_dtype, o_dtype, batch, heads, seq_q, seq_kv, d, scale, sh);
+  if (st != SMA_OK) return st;
+  if (sh->rows == 0) return SMA_OK;
+  st = check_pointers(*sh, q, k, v, o, lse, ws, ws_bytes);
+  if (st != SMA_OK) return st;
+  if (plan_without_split(*sh).nwg > kMaxWorkgroups) return SMA_ERR_UNSUPPORTED;
+  if ((sh->rows * sh->d / 4 + 255) / 256 > kMaxWorkgroups) return SMA_ERR_UNSUPPORTED;
+  return SMA_OK;
+}
+
+// Compute units of each device, queried once per device.
+constexpr int kMaxDevices = 64;
+std::once_flag g_cu_once[kMaxDevices];
+int g_cus[kMaxDevices];
+
+int current_device_cus(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SMA_ERR_HIP;
+  std::call_once(g_cu_once[dev], [dev] {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    g_cus[dev] = n;
+  });
+  if (g_cus[dev] <= 0) return SMA_ERR_HIP;
+  *out = g_cus[dev];
+  return SMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sma_attention_fwd_validate(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, int in_dtype, int o_dtype, size_t batch,
+                               size_t heads, size_t seq_q, size_t seq_kv, size_t head_dim,
+                               double scale, int causal, const void* workspace,
+                               size_t workspace_bytes) {
+  (void)causal;
+  Shape sh;
+  return validate_all(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv, head_dim,
+                      scale, workspace, workspace_bytes, &sh);
+}
+
+size_t sma_attention_fwd_workspace_bytes(int in_dtype, size_t batch, size_t heads, size_t seq_q,
+                                         size_t seq_kv, size_t head_dim, int causal, int num_cus) {
+  (void)causal;
+  Shape sh;
+  if (check_shape(in_dtype, SMA_DTYPE_F32, batch, heads, seq_q, seq_kv, head_dim, 1.0, &sh) != SMA_OK)
+    return 0;
+  if (sh.rows == 0) return 0;
+  int cus = num_cus;
+  if (cus <= 0 && current_device_cus(&cus) != SMA_OK) cus = 256;
+  return make_plan(sh, cus).ws_bytes;
+}
+
+int sma_attention_fwd_timed(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
+                            size_t seq_kv, size_t head_dim, double scale, int causal,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* event_before, void* event_after) {
+  Shape sh;
+  int st = validate_all(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv, head_dim,
+                        scale, workspace, workspace_bytes, &sh);
+  if (st != SMA_OK || sh.rows == 0) return st;
+  int cus = 0;
+  st = current_device_cus(&cus);
+  if (st != SMA_OK) return st;
+  Plan p = make_plan(sh, cus);
+  if (p.nsplit > 1 && (!workspace || workspace_bytes < p.ws_bytes || p.nwg > kMaxWorkgroups))
+    p = plan_without_split(sh);
+
+  sma::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.bh = (int64_t)sh.bh;
+  a.seq_q = (int32_t)seq_q;
+  a.seq_kv = (int32_t)seq_kv;
+  a.nqb = p.nqb;
+  a.nsplit = p.nsplit;
+  a.split_len = p.split_len;
+  a.c = (float)(std::fabs(scale) * 1.44269504088896340736);  // |scale| * log2(e), one rounding
+  a.negate_q = scale < 0.0 ? 1 : 0;
+  a.nwg = (uint32_t)p.nwg;
+  if (p.nsplit == 1) {
+    a.o = static_cast<float*>(o);
+    a.lse = lse;
+  } else {
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_lse_off);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool c = causal != 0;
+  if (event_before && hipEventRecord(static_cast<hipEvent_t>(event_before), s) != hipSuccess)
+    return SMA_ERR_HIP;
+  hipError_t e = sh.in_dtype == SMA_DTYPE_F32 ? sma::launch_fwd_f32(a, (int)head_dim, c, s)
+                                              : sma::launch_fwd_bf16(a, (int)head_dim, c, s);
+  if (e != hipSuccess) return SMA_ERR_HIP;
+  if (event_after && hipEventRecord(static_cast<hipEvent_t>(event_after), s) != hipSuccess)
+    return SMA_ERR_HIP;
+  if (p.nsplit > 1) {
+    sma::CombineArgs ca{};
+    ca.part_o = a.part_o;
+    ca.part_lse = a.part_lse;
+    ca.o = static_cast<float*>(o);
+    ca.lse = lse;
+    ca.rows = (int64_t)sh.rows;
+    ca.nsplit = p.nsplit;
+    e = sma::launch_combine(ca, (int)head_dim, s);
+    if (e != hipSuccess) return SMA_ERR_HIP;
+  }
+  return SMA_OK;
+}
+
+int sma_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
+                      size_t seq_kv, size_t head_dim, double scale, int causal, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return sma_attention_fwd_timed(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv,
+                                 head_dim, scale, causal, workspace, workspace_bytes, stream,
+                                 nullptr, nullptr);
+}
+
+const char* sma_status_string(int status) {
+  switch (status) {
+    case SMA_OK: return "SMA_OK: success";
+    case SMA_ERR_NULL_POINTER: return "SMA_ERR_NULL_POINTER: a required pointer is NULL";
+    case SMA_ERR_INVALID_VALUE: return "SMA_ERR_INVALID_VALUE: invalid size, dtype code or scale";
+    case SMA_ERR_UNSUPPORTED: return "SMA_ERR_UNSUPPORTED: valid request that the kernels do not implement";
+    case SMA_ERR_MISALIGNED: return "SMA_ERR_MISALIGNED: q/k/v/o/workspace need 16-byte and lse 4-byte alignment";
+    case SMA_ERR_ALIASING: return "SMA_ERR_ALIASING: an output overlaps an input or another output";
+    case SMA_ERR_HIP: return "SMA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown sma status";
+  }
+}
+
+int sma_abi_version(void) { return SMA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Internal interface between the C-ABI host layer (sma_host.cpp) and the HIP
+// kernels. Not installed; the public ABI is include/sma.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sma {
+
+// Arguments of one attention-forward launch (one variant of dtype/head_dim/mask).
+struct FwdArgs {
+  const void* q;     // [bh][seq_q][d], f32 or bf16
+  const void* k;     // [bh][seq_kv][d]
+  const void* v;     // [bh][seq_kv][d]
+  float* o;          // nsplit == 1: final O [bh][seq_q][d] fp32
+  float* lse;        // nsplit == 1: final LSE [bh][seq_q] (natural log), may be null
+  float* part_o;     // nsplit > 1: per-split normalised O [nsplit][bh][seq_q][d]
+  float* part_lse;   // nsplit > 1: per-split LSE in log2 units [nsplit][bh][seq_q]
+  int64_t bh;        // batch * heads
+  int32_t seq_q;
+  int32_t seq_kv;
+  int32_t nqb;       // query blocks per (batch, head)
+  int32_t nsplit;    // key splits per query row (1 = none)
+  int32_t split_len; // keys per split, a multiple of the kernel's key tile
+  float c;           // |scale| * log2(e), rounded once to fp32
+  int32_t negate_q;  // scale < 0: the kernel multiplies by -q and |scale|
+  uint32_t nwg;      // bh * nqb * nsplit workgroups
+};
+
+// Arguments of the split-combine launch.
+struct CombineArgs {
+  const float* part_o;   // [nsplit][rows][d]
+  const float* part_lse; // [nsplit][rows], log2 units
+  float* o;              // [rows][d]
+  float* lse;            // [rows] natural log, may be null
+  int64_t rows;          // bh * seq_q
+  int32_t nsplit;
+};
+
+// Workgroup geometry the planner needs (must match the kernels).
+constexpr int kF32QueriesPerWG = 128;
+constexpr int kF32KeysPerTile = 32;
+constexpr int kBF16QueriesPerWG = 256;
+constexpr int kBF16KeysPerTile = 64;
+constexpr int kThreadsPerWG = 256;
+
+hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);
+hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s);
+
+}  // namespace sma

@@ -1,0 +1,279 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Small and ragged shapes compare every output; the full-size workloads run in
+the benchmark's launch configuration and compare sampled rows, plus
+properties that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import gen
+import oracle
+from helpers import (check_parity, empty_rows, run_gpu, sample_rows, to_device, workload_case)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import scaled_masked_attention_amd as sma
+
+    sma.library()  # fail loudly if the HIP library is missing
+
+
+def _case(seed, B, H, sq, skv, d, dtype, sigma_qk=1.0):
+    return gen.random_case(seed, (B, H, sq, d), (B, H, skv, d), sigma_qk=sigma_qk, dtype=dtype)
+
+
+SHAPES = [  # (B, H, sq, skv): several tiles with ragged tails, cross shapes both ways, one head
+    (1, 2, 128, 128), (2, 3, 200, 200), (1, 2, 77, 300), (2, 1, 300, 77), (1, 1, 1, 1000),
+    (1, 1, 1000, 1), (1, 1, 513, 513), (3, 2, 64, 96), (1, 4, 257, 1025),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_parity_small(shape, causal, d, dtype):
+    B, H, sq, skv = shape
+    sig = 3.0 if dtype == "bf16" else 1.0
+    (q, k, v), bits = _case(100 + sq + 7 * skv + d, B, H, sq, skv, d, dtype, sigma_qk=sig)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_gpu(*to_device((q, k, v), bits, dtype), scale, causal)
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, scale, causal)
+    check_parity(o, lse, o_ref, lse_ref, dtype, f"{shape} causal={causal} d={d} {dtype}")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_parity_small_workloads_full(name):
+    w, vals, bits = workload_case(name)
+    o, lse = run_gpu(*to_device(vals, bits, w.dtype), w.scale, w.causal)
+    o_ref, lse_ref = oracle.attention_fwd(*vals, w.scale, w.causal)
+    check_parity(o, lse, o_ref, lse_ref, w.dtype, name)
+
+
+@pytest.mark.parametrize("name", ["c3", "c4n", "c4c", "c5"])
+def test_parity_full_size_sampled(name):
+    w, vals, bits = workload_case(name)
+    o, lse = run_gpu(*to_device(vals, bits, w.dtype), w.scale, w.causal)
+    B, H, sq, skv = w.batch, w.heads, w.seq_q, w.seq_kv
+    rows = sample_rows(B, H, sq, skv, w.causal, n_random=192 if name == "c5" else 512, seed=7)
+    o_ref, lse_ref = oracle.attention_fwd(*vals, w.scale, w.causal, rows=rows)
+    o_s = o.reshape(-1, w.head_dim)[rows]
+    l_s = lse.reshape(-1)[rows]
+    stats = check_parity(o_s, l_s, o_ref, lse_ref, w.dtype, name)
+    print(f"{name}: {len(rows)} sampled rows {stats}")
+    # Everywhere: finite, and rows that see no key are exactly zero.
+    assert np.all(np.isfinite(o))
+    er = empty_rows(sq, skv, w.causal)
+    if er.any():
+        assert np.all(o.reshape(B * H, sq, -1)[:, er] == 0.0)
+
+
+# ------------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_no_keys_gives_zero_and_neg_inf(dtype):
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = torch.randn(2, 3, 70, 128, device="cuda").to(tdt)
+    k = torch.empty(2, 3, 0, 128, device="cuda", dtype=tdt)
+    out = torch.full((2, 3, 70, 128), float("nan"), device="cuda")
+    o, lse = sma.attention_fwd(q, k, k, causal=False, return_lse=True, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and not torch.any(torch.signbit(o))
+    assert torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fully_masked_rows_exact_zero_with_nan_queries(dtype):
+    sq, skv, d = 300, 100, 128
+    (q, k, v), bits = _case(31, 1, 2, sq, skv, d, dtype)
+    tq, tk, tv = to_device((q, k, v), bits, dtype)
+    tq[:, :, : sq - skv] = float("nan")  # rows with no admitted key: content must not matter
+    o, lse = run_gpu(tq, tk, tv, 0.1, True)
+    assert np.all(o[:, :, : sq - skv] == 0.0) and not np.any(np.signbit(o[:, :, : sq - skv]))
+    assert np.all(np.isneginf(lse[:, :, : sq - skv]))
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, 0.1, True)
+    check_parity(o, lse, o_ref, lse_ref, dtype, "masked rows")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_q_zero_is_prefix_mean(dtype, causal):
+    sq, skv, d = 150, 250, 64
+    (q, k, v), bits = _case(32, 1, 2, sq, skv, d, dtype)
+    q[:] = 0
+    if bits is not None:
+        bits = (np.zeros_like(bits[0]),) + bits[1:]
+    o, lse = run_gpu(*to_device((q, k, v), bits, dtype), 0.3, causal)
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, 0.3, causal)
+    check_parity(o, lse, o_ref, lse_ref, dtype, "q=0")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_v_ones_gives_ones(dtype):
+    sq, skv, d = 260, 333, 128
+    (q, k, v), bits = _case(33, 2, 2, sq, skv, d, dtype, sigma_qk=3.0)
+    v[:] = 1.0
+    if bits is not None:
+        bits = bits[:2] + (gen.f32_to_bf16_bits(v),)
+    o, _ = run_gpu(*to_device((q, k, v), bits, dtype), 1.0 / math.sqrt(d), True)
+    er = empty_rows(sq, skv, True)
+    tol = 2e-5 if dtype == "f32" else 2 ** -8
+    assert np.all(np.abs(o[:, :, ~er] - 1.0) <= tol)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_one_hot_v_extracts_probabilities(dtype):
+    """With V = I (Skv = d keys), O[i, c] = P[i, c]: the GPU's implicit P is read out."""
+    sq, d = 96, 64
+    (q, k, _), bits = _case(34, 1, 1, sq, d, d, dtype, sigma_qk=2.0)
+    v = np.eye(d, dtype=np.float32).reshape(1, 1, d, d)
+    if bits is not None:
+        bits = bits[:2] + (gen.f32_to_bf16_bits(v),)
+    o, _ = run_gpu(*to_device((q, k, v), bits, dtype), 0.2, True)
+    p = oracle.softmax_probs(q[0, 0], k[0, 0], 0.2, True)
+    tol = 2e-5 if dtype == "f32" else 2e-2
+    assert np.abs(o[0, 0] - p).max() <= tol
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_key_shift_beyond_fp32_exp_range(dtype):
+    """Every score of a row shifted by ~181 (fp32 exp overflows past ~88.7): only a
+    max-subtracted softmax stays finite. Inputs are multiples of 1/2 in [-1, 1]
+    (exact in bf16 and fp32), so every dot product is exact in fp32 and the
+    comparison isolates the softmax from dot-product rounding at |s| ~ 2000."""
+    sq, skv, d = 130, 190, 128
+    (q, k, v), _ = _case(35, 1, 2, sq, skv, d, "f32")
+    q = (np.clip(np.round(q * 2), -2, 2) / 2).astype(np.float32)
+    k = (np.clip(np.round(k * 2), -2, 2) / 2).astype(np.float32)
+    q[..., 0] = 8.0
+    k[..., 0] = 256.0  # scale * 8 * 256 = 181 added to every score of a row
+    bits = None
+    if dtype == "bf16":
+        bits = tuple(gen.f32_to_bf16_bits(x) for x in (q, k, v))
+        q, k, v = (gen.bf16_bits_to_f32(b) for b in bits)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_gpu(*to_device((q, k, v), bits, dtype), scale, True)
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, scale, True)
+    assert lse_ref[np.isfinite(lse_ref)].min() > 150
+    check_parity(o, lse, o_ref, lse_ref, dtype, "key shift")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.7])
+def test_negative_zero_and_large_scale(dtype, scale):
+    (q, k, v), bits = _case(36, 1, 2, 140, 170, 128, dtype)
+    o, lse = run_gpu(*to_device((q, k, v), bits, dtype), scale, True)
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, scale, True)
+    check_parity(o, lse, o_ref, lse_ref, dtype, f"scale={scale}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_causal_single_query_equals_unmasked(dtype):
+    (q, k, v), bits = _case(37, 2, 2, 1, 700, 128, dtype)
+    dev = to_device((q, k, v), bits, dtype)
+    o0, l0 = run_gpu(*dev, 0.1, False)
+    o1, l1 = run_gpu(*dev, 0.1, True)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_deterministic_bitwise(dtype):
+    (q, k, v), bits = _case(38, 2, 4, 333, 777, 128, dtype)
+    dev = to_device((q, k, v), bits, dtype)
+    o0, l0 = run_gpu(*dev, 0.1, True)
+    o1, l1 = run_gpu(*dev, 0.1, True)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_guard_bands_untouched_and_nan_prefill_overwritten(dtype):
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    B, H, sq, skv, d = 1, 3, 190, 260, 128
+    (q, k, v), bits = _case(39, B, H, sq, skv, d, dtype)
+    tq, tk, tv = to_device((q, k, v), bits, dtype)
+    n_o, n_l, pad = B * H * sq * d, B * H * sq, 1024
+    big_o = torch.full((n_o + 2 * pad,), 12345.0, device="cuda")
+    big_l = torch.full((n_l + 2 * pad,), 12345.0, device="cuda")
+    o_view = big_o[pad: pad + n_o].view(B, H, sq, d)
+    l_view = big_l[pad: pad + n_l].view(B, H, sq)
+    o_view.fill_(float("nan"))
+    l_view.fill_(float("nan"))
+    sma.attention_fwd(tq, tk, tv, scale=0.1, causal=True, return_lse=True, out=o_view, lse=l_view)
+    torch.cuda.synchronize()
+    assert torch.all(big_o[:pad] == 12345.0) and torch.all(big_o[pad + n_o:] == 12345.0)
+    assert torch.all(big_l[:pad] == 12345.0) and torch.all(big_l[pad + n_l:] == 12345.0)
+    assert not torch.any(torch.isnan(o_view)) and not torch.any(torch.isnan(l_view))
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, 0.1, True)
+    check_parity(o_view.cpu().numpy().astype(np.float64), l_view.cpu().numpy().astype(np.float64),
+                 o_ref, lse_ref, dtype, "guard")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_non_default_stream(dtype):
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    (q, k, v), bits = _case(40, 2, 2, 300, 300, 64, dtype)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        tq, tk, tv = to_device((q, k, v), bits, dtype)
+        o, lse = sma.attention_fwd(tq, tk, tv, scale=0.125, causal=True, return_lse=True)
+        o2 = o * 2.0  # ordered after the attention kernel on the same stream
+    s.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, 0.125, True)
+    check_parity(o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), o_ref,
+                 lse_ref, dtype, "stream")
+    assert torch.equal(o2, o * 2.0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_keys_path_matches_unsplit(dtype, causal):
+    """A shape the planner splits across workgroups: with and without workspace."""
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    B, H, sq, skv, d = 1, 4, 200, 3000, 128
+    (q, k, v), bits = _case(41, B, H, sq, skv, d, dtype)
+    in_dt = sma.SMA_DTYPE_F32 if dtype == "f32" else sma.SMA_DTYPE_BF16
+    assert sma.workspace_bytes(in_dt, B, H, sq, skv, d, causal) > 0
+    dev = to_device((q, k, v), bits, dtype)
+    o_s, l_s = run_gpu(*dev, 0.1, causal)
+    tiny = torch.empty(16, dtype=torch.uint8, device="cuda")
+    o_n, l_n = run_gpu(*dev, 0.1, causal, workspace=tiny)  # too small: no split
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, 0.1, causal)
+    check_parity(o_s, l_s, o_ref, lse_ref, dtype, "split")
+    check_parity(o_n, l_n, o_ref, lse_ref, dtype, "unsplit")
+
+
+def test_binding_rejects_bad_arguments():
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    q = torch.randn(1, 1, 8, 96, device="cuda")
+    with pytest.raises(sma.SMAError) as e:
+        sma.attention_fwd(q, q, q)
+    assert e.value.status == 3  # head_dim 96 unsupported
+    q = torch.randn(1, 1, 8, 64, device="cuda")
+    with pytest.raises(sma.SMAError) as e:
+        sma.attention_fwd(q, q, q, out=q)  # output aliases the inputs
+    assert e.value.status == 5
+    with pytest.raises(ValueError):
+        sma.attention_fwd(q, q.half(), q)
