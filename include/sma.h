@@ -61,7 +61,9 @@ typedef enum {
   SMA_OK = 0,
   SMA_ERR_NULL_POINTER = 1,  /* a required pointer is NULL */
   SMA_ERR_INVALID_VALUE = 2, /* bad size, dtype code, non-finite scale, size overflow */
-  SMA_ERR_UNSUPPORTED = 3,   /* valid request the kernels do not implement (head_dim, dtype pair, grid limit) */
+  SMA_ERR_UNSUPPORTED = 3,   /* valid request the kernels do not implement: head_dim, dtype pair,
+                                seq_q or seq_kv above 2^30, bf16 K/V of one (batch, head) of 2 GiB
+                                or more, grid limit */
   SMA_ERR_MISALIGNED = 4,    /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
   SMA_ERR_ALIASING = 5,      /* o or lse overlaps q, k, v, the workspace, or each other */
   SMA_ERR_HIP = 6            /* the HIP runtime reported an error (device query or launch) */

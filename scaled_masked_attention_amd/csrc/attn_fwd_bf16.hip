@@ -8,17 +8,24 @@
 // rounded to bf16 (nearest even) for the P V product; the row sums use the
 // fp32 probabilities.
 //
-// Workgroup: 8 waves x 32 query rows = 256 rows, two waves per SIMD, so that
-// one wave's softmax (VALU, transcendental) runs while the other's MFMAs
-// issue. Key tiles of 64 rows are staged HBM/L2 -> registers -> LDS, double
-// buffered: waves 0-3 stage K row-major, waves 4-7 stage V transposed
-// (V^T[dim][key]), so both MFMA operands are plain 16-byte LDS reads.
+// Workgroup: 8 waves x 32 query rows = 256 rows, two waves per SIMD. Key tiles
+// of 64 rows go HBM/L2 -> LDS through buffer-resource direct-to-LDS loads into
+// a ring of four slots, two tiles ahead of their use, without passing through
+// registers; loads past the last key return zeros.
 //
 // S^T = K Q^T: lane (m, h) supplies K[key m] and Q[query m] at head dims
 // h*D/2 + 8*step .. + 7 and receives the scores of query (lane % 32). K rows
-// are stored with bits 2 and 3 of the row index swapped, which makes
+// are placed with bits 2 and 3 of the row index swapped, which makes
 // accumulator register r hold key 16*(r/8) + 8*h + r%8: registers 8t..8t+7
-// are the eight keys this lane supplies to k-step t of O^T += V^T P^T.
+// are the eight keys this lane supplies to k-step t of O^T += V^T P^T. V stays
+// row-major in LDS and the V^T operand is read with the gfx950 transposing
+// read ds_read_b64_tr_b16. Both tiles are XOR-swizzled in 16-byte chunks so
+// that these reads are free of bank conflicts (see k_swz / v_swz).
+//
+// The two waves sharing a SIMD (w and w+4) run half a step apart: waves 0-3
+// do S(t), softmax(t), PV(t); waves 4-7 do PV(t-1), S(t), softmax(t). One
+// wave's softmax (VALU, transcendental) then meets the other's MFMAs in two
+// of the three phases.
 #include "attn_common.h"
 
 namespace sma {
@@ -27,29 +34,28 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct BGeom {
-  static constexpr int kThreads = 512;
   static constexpr int kWaves = 8;
-  static constexpr int kQW = 32;                       // query rows per wave
-  static constexpr int kQ = kWaves * kQW;              // query rows per workgroup
-  static constexpr int kK = kBF16KeysPerTile;          // keys per LDS tile
-  static constexpr int kKB = kK / 32;                  // 32-key sub-blocks per tile
-  static constexpr int kKStride = D + 8;               // K row in LDS (bf16), 16 B pad
-  static constexpr int kVtStride = kK + 8;             // V^T row (one head dim) in LDS, 16 B pad
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kQW = 32;                     // query rows per wave
+  static constexpr int kQ = kWaves * kQW;            // query rows per workgroup
+  static constexpr int kK = kBF16KeysPerTile;        // keys per LDS tile (two 32-key blocks)
+  static constexpr int kKB = kK / 32;
+  static constexpr int kSlots = 4;                   // LDS ring of K/V tiles
+  static constexpr int kChunksPerRow = D / 8;        // 16-byte chunks per K or V row
+  static constexpr int kTileChunks = kK * kChunksPerRow;
+  static constexpr int kLoadsPerThread = kTileChunks / kThreads;  // per tensor and tile
+  static constexpr int kLoadsPerTile = 2 * kLoadsPerThread;       // K and V
   static constexpr int kHalf = D / 2;
-  static constexpr int kSteps = D / 16;                // QK^T k-steps (8 dims per lane half)
-  static constexpr int kNch = D / 32;                  // 32-wide output chunks
-  static constexpr int kStagers = kThreads / 2;        // threads staging K (and as many for V)
-  static constexpr int kKChunks = kK * D / 8 / kStagers;         // 16-byte K chunks per thread
-  static constexpr int kVPatches = (kK / 4) * (D / 8);  // 4-key x 8-dim V patches, one per thread
+  static constexpr int kSteps = D / 16;              // QK^T k-steps (8 dims per lane half)
+  static constexpr int kNch = D / 32;                // 32-wide output chunks
   static_assert(kQ == kBF16QueriesPerWG, "planner geometry");
-  static_assert(kKChunks * 8 * kStagers == kK * D, "K tile split");
-  static_assert(kVPatches <= kStagers && kKChunks <= 4, "staging split");
+  static_assert(kLoadsPerThread >= 1 && kLoadsPerThread * kThreads == kTileChunks, "tile split");
 };
 
 constexpr float kTau = 8.0f;  // lazy running-max threshold, log2 units (see the fp32 kernel)
@@ -57,24 +63,58 @@ constexpr float kTau = 8.0f;  // lazy running-max threshold, log2 units (see the
 __device__ __forceinline__ int swap_bits_2_3(int r) {
   return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
-
-// Low (sel = 0) or high (sel = 1) bf16 of two dwords packed into one dword: {a.sel, b.sel}.
-__device__ __forceinline__ unsigned pack_lo(unsigned a, unsigned b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+// 16-byte chunk swizzles (XOR on the chunk index within a row). gfx950's LDS
+// has 64 four-byte banks and serves a ds_read_b128 in groups of 16 lanes and
+// a ds_read_b64_tr_b16 in groups of 32 lanes, so:
+//  - K: the 16 lanes of a group read 16 consecutive rows at one logical
+//    chunk; with 256-byte rows (d = 128) the chunk is XORed with row & 15,
+//    with 128-byte rows (d = 64, two rows per bank cycle) with (row >> 1) & 7;
+//  - V: a 32-lane group reads 4 consecutive rows x 4 chunks of one 64-byte
+//    group; the four rows must use four different chunk groups, so the chunk
+//    is XORed with 4*(row & 3) (d = 128) or 4*((row >> 1) & 1) (d = 64).
+template <int D>
+__device__ __forceinline__ int k_swz(int rho) {
+  return D == 128 ? (rho & 15) : ((rho >> 1) & 7);
 }
-__device__ __forceinline__ unsigned pack_hi(unsigned a, unsigned b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One 16-byte-per-lane direct-to-LDS load through a buffer resource: lane i's
+// chunk lands at LDS byte address lds_addr + 16*i (lds_addr wave-uniform, in
+// M0). Issued as inline asm so that the compiler adds no conservative waits
+// for it before unrelated LDS reads; the kernel waits explicitly (wait_vmcnt)
+// before a tile is used. The s_nop covers the M0-write hazard.
+__device__ __forceinline__ void dma_load_x4(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset,
+                                            unsigned lds_addr) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ unsigned lds_address(const void* p) {
+  return (unsigned)(size_t)(__attribute__((address_space(3))) const void*)p;
 }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   using G = BGeom<D>;
-  __shared__ __attribute__((aligned(16))) unsigned short k_lds[2][G::kK * G::kKStride];
-  __shared__ __attribute__((aligned(16))) unsigned short vt_lds[2][D * G::kVtStride];
+  __shared__ __attribute__((aligned(16))) u32x4 k_lds[G::kSlots][G::kTileChunks];
+  __shared__ __attribute__((aligned(16))) u32x4 v_lds[G::kSlots][G::kTileChunks];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int lm = lane & 31;
   const int lh = lane >> 5;
 
@@ -107,55 +147,43 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
       qr[s] = __builtin_bit_cast(bf16x8, x);
     }
   }
+  // The tile loads below are invisible to the compiler's load counting, so
+  // none of its own loads may still be in flight when they start.
+  wait_vmcnt<0>();
 
-  const unsigned short* kg = static_cast<const unsigned short*>(a.k) + (size_t)t.bh * a.seq_kv * D;
-  const unsigned short* vg = static_cast<const unsigned short*>(a.v) + (size_t)t.bh * a.seq_kv * D;
-  const bool k_stager = tid < G::kStagers;
-  const int st = k_stager ? tid : tid - G::kStagers;
-  const bool v_stager = !k_stager && st < G::kVPatches;
-  u32x4 sreg[4];  // staged chunks: K (kKChunks of them) or the 4 key rows of a V patch
+  // Buffer resources over this (batch, head)'s K and V: rows past the last key
+  // fall outside the byte range and read as zeros.
+  constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, gfx9-family dword 3
+  const unsigned kv_bytes = (unsigned)a.seq_kv * (unsigned)(2 * D);
+  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned short*>(static_cast<const unsigned short*>(a.k)) + (size_t)t.bh * a.seq_kv * D,
+      0, (int)kv_bytes, (int)kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned short*>(static_cast<const unsigned short*>(a.v)) + (size_t)t.bh * a.seq_kv * D,
+      0, (int)kv_bytes, (int)kRsrcWord3);
+  // Each wave-wide load fills 64 consecutive LDS chunks: position
+  // p = (u*waves + wave)*64 + lane is row rho = p / chunks_per_row, chunk
+  // p % chunks_per_row; the lane fetches the global chunk that belongs there
+  // under the K row permutation and the swizzles. Those depend on the lane
+  // only, so the per-lane byte offsets hold for the whole pass.
+  constexpr int kRowsPerU = G::kWaves * 64 / G::kChunksPerRow;
+  static_assert(kRowsPerU % 32 == 0, "permutation and swizzles repeat every 32 rows");
+  static_assert(D == 128 || D == 64, "swizzles are defined for d = 64 and 128");
+  const int rho0 = (wave * 64 + lane) / G::kChunksPerRow;
+  const int pc = lane % G::kChunksPerRow;
+  const unsigned k_lane_ofs = (unsigned)((rho0 & ~31) | swap_bits_2_3(rho0 & 31)) * (2 * D) +
+                              16u * (unsigned)(pc ^ k_swz<D>(rho0));
+  const unsigned v_lane_ofs = (unsigned)rho0 * (2 * D) + 16u * (unsigned)(pc ^ v_swz<D>(rho0));
 
-  auto load_tile = [&](int32_t tile) {
-    const int32_t j0 = ks + tile * G::kK;
-    if (k_stager) {
+  auto issue_tile = [&](int32_t T) {
+    const unsigned row0 = (unsigned)(ks + T * G::kK);
+    const int slot = T % G::kSlots;
 #pragma unroll
-      for (int u = 0; u < G::kKChunks; ++u) {
-        const int f = st + G::kStagers * u;
-        const int row = f / (D / 8), c8 = f % (D / 8);
-        const int32_t j = j0 + row;
-        sreg[u] = j < a.seq_kv ? *reinterpret_cast<const u32x4*>(kg + (size_t)j * D + 8 * c8)
-                               : u32x4{0u, 0u, 0u, 0u};
-      }
-    } else if (v_stager) {
-      // patch: keys 4*kgp .. 4*kgp+3, head dims 8*cg .. 8*cg+7
-      const int kgp = st % (G::kK / 4), cg = st / (G::kK / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int32_t j = j0 + 4 * kgp + r;
-        sreg[r] = j < a.seq_kv ? *reinterpret_cast<const u32x4*>(vg + (size_t)j * D + 8 * cg)
-                               : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    if (k_stager) {
-#pragma unroll
-      for (int u = 0; u < G::kKChunks; ++u) {
-        const int f = st + G::kStagers * u;
-        const int row = f / (D / 8), c8 = f % (D / 8);
-        const int krow = (row & ~31) | swap_bits_2_3(row & 31);
-        *reinterpret_cast<u32x4*>(&k_lds[buf][krow * G::kKStride + 8 * c8]) = sreg[u];
-      }
-    } else if (v_stager) {
-      const int kgp = st % (G::kK / 4), cg = st / (G::kK / 4);
-      // sreg[r] holds dims 8cg..8cg+7 of key 4kgp+r as 4 dwords (2 dims each).
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const u32x2 even = {pack_lo(sreg[0][w], sreg[1][w]), pack_lo(sreg[2][w], sreg[3][w])};
-        const u32x2 odd = {pack_hi(sreg[0][w], sreg[1][w]), pack_hi(sreg[2][w], sreg[3][w])};
-        *reinterpret_cast<u32x2*>(&vt_lds[buf][(8 * cg + 2 * w) * G::kVtStride + 4 * kgp]) = even;
-        *reinterpret_cast<u32x2*>(&vt_lds[buf][(8 * cg + 2 * w + 1) * G::kVtStride + 4 * kgp]) = odd;
-      }
+    for (int u = 0; u < G::kLoadsPerThread; ++u) {
+      const int base = (u * G::kWaves + wave) * 64;
+      const unsigned tile_ofs = (row0 + (unsigned)(u * kRowsPerU)) * (unsigned)(2 * D);
+      dma_load_x4(k_rsrc, k_lane_ofs + tile_ofs, lds_address(&k_lds[slot][base]));
+      dma_load_x4(v_rsrc, v_lane_ofs + tile_ofs, lds_address(&v_lds[slot][base]));
     }
   };
 
@@ -167,108 +195,150 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.c;
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int32_t it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < ntiles) load_tile(it + 1);
-    const int32_t j0 = ks + it * G::kK;
-    if (wave_live && j0 < wave_hi) {
-      f32x16 sacc[G::kKB];
+  // O^T += V^T P^T over a tile's 64 keys in k-steps of 16. In each 16-lane
+  // group, lane role s reads 4 dims of V row 16*t2 + 8*h + s/4 (and +4).
+  const int srole = lane & 15;
+  const int colq = 2 * ((lane >> 4) & 1) + ((srole & 3) >> 1);  // chunk within a 32-dim group
+  const int half8 = 8 * (srole & 1);
+  auto pv_tile = [&](int slot, const bf16x8 (&pb)[G::kKB][2]) {
+    const unsigned char* vtile = reinterpret_cast<const unsigned char*>(&v_lds[slot][0]);
 #pragma unroll
-      for (int kb = 0; kb < G::kKB; ++kb) {
+    for (int kb = 0; kb < G::kKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-        const unsigned short* krow = &k_lds[buf][(32 * kb + lm) * G::kKStride + lh * G::kHalf];
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int r_lo = 32 * kb + 16 * t2 + 8 * lh + srole / 4;
+        const int r_hi = r_lo + 4;
 #pragma unroll
-        for (int s = 0; s < G::kSteps; ++s) {
-          const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 8 * s));
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qr[s], sacc[kb], 0, 0, 0);
+        for (int cb = 0; cb < G::kNch; ++cb) {
+          const int chunk = 4 * cb + colq;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vtile + r_lo * (2 * D) +
+                                                         16 * (chunk ^ v_swz<D>(r_lo)) + half8));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vtile + r_hi * (2 * D) +
+                                                         16 * (chunk ^ v_swz<D>(r_hi)) + half8));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          const bf16x8 aop = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, pb[kb][t2], oacc[cb], 0, 0, 0);
         }
       }
+  };
 
-      // Row max of the raw scores (scale > 0 after the sign fold), masked keys excluded.
-      const bool need_mask = j0 + G::kK > wave_lo;
-      float mx = -INFINITY;
-      if (need_mask) {
-        const int32_t rel = lim - j0 - 8 * lh;  // key 32kb + 16(r/8) + r%8 allowed iff < rel
+  // Scores, lazy running max and probabilities of tile T (in ring slot
+  // `slot`); returns the bf16 probabilities for the PV product.
+  auto scores_and_p = [&](int32_t T, int slot, bf16x8 (&pb)[G::kKB][2]) {
+    const int32_t j0 = ks + T * G::kK;
+    f32x16 sacc[G::kKB];
 #pragma unroll
-        for (int kb = 0; kb < G::kKB; ++kb)
+    for (int kb = 0; kb < G::kKB; ++kb) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * kb + 16 * (r / 8) + (r % 8) < rel) mx = fmaxf(mx, sacc[kb][r]);
-      } else {
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      const int rho = 32 * kb + lm;
+      const unsigned char* krow = reinterpret_cast<const unsigned char*>(&k_lds[slot][rho * G::kChunksPerRow]);
 #pragma unroll
-        for (int kb = 0; kb < G::kKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      for (int st = 0; st < G::kSteps; ++st) {
+        const int chunk = lh * G::kSteps + st;
+        const bf16x8 kop = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(krow + 16 * (chunk ^ k_swz<D>(rho))));
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qr[st], sacc[kb], 0, 0, 0);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float tmax = mx == -INFINITY ? -INFINITY : mx * c;
-      if (__any(tmax > m_run + kTau)) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
-        l_run *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < G::kNch; ++cb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
-        m_run = m_new;
-      }
-      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    }
 
-      // p = 2^(s*c - m), rounded to bf16 for the PV product.
-      bf16x8 pb[G::kKB][2];
-      float psum = 0.f;
-      if (need_mask) {
-        const int32_t rel = lim - j0 - 8 * lh;
-#pragma unroll
-        for (int kb = 0; kb < G::kKB; ++kb)
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int key = 32 * kb + 16 * t2 + e;
-              float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * t2 + e], c, neg_m));
-              p = key < rel ? p : 0.f;
-              psum += p;
-              pb[kb][t2][e] = (__bf16)p;
-            }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < G::kKB; ++kb)
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * t2 + e], c, neg_m));
-              psum += p;
-              pb[kb][t2][e] = (__bf16)p;
-            }
-      }
-      l_run += psum;
-
-      // O^T += V^T P^T over the tile's 64 keys in k-steps of 16.
+    // Row max of the raw scores (scale > 0 after the sign fold), masked keys excluded.
+    const bool need_mask = j0 + G::kK > wave_lo;
+    const int32_t rel = lim - j0 - 8 * lh;  // key 32kb + 16(r/8) + r%8 allowed iff < rel
+    float mx = -INFINITY;
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < G::kKB; ++kb)
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const unsigned short* vp = &vt_lds[buf][lm * G::kVtStride + 32 * kb + 16 * t2 + 8 * lh];
+        for (int r = 0; r < 16; ++r)
+          mx = (32 * kb + 16 * (r / 8) + (r % 8) < rel) ? fmaxf(mx, sacc[kb][r]) : mx;
+    } else {
 #pragma unroll
-          for (int cb = 0; cb < G::kNch; ++cb) {
-            const bf16x8 aop =
-                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vp + 32 * cb * G::kVtStride));
-            oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, pb[kb][t2], oacc[cb], 0, 0, 0);
-          }
-        }
+      for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     }
-    if (it + 1 < ntiles) store_tile((it + 1) & 1);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float tmax = mx == -INFINITY ? -INFINITY : mx * c;
+    if (__any(tmax > m_run + kTau)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+
+    // p = 2^(s*c - m), rounded to bf16 for the PV product.
+    float psum = 0.f;
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * t2 + e], c, neg_m));
+            p = (32 * kb + 16 * t2 + e) < rel ? p : 0.f;
+            psum += p;
+            pb[kb][t2][e] = (__bf16)p;
+          }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * t2 + e], c, neg_m));
+            psum += p;
+            pb[kb][t2][e] = (__bf16)p;
+          }
+    }
+    l_run += psum;
+  };
+
+  const bool late = wave >= G::kWaves / 2;
+  bf16x8 pb_late[G::kKB][2];
+  bool late_pending = false;
+  int late_slot = 0;
+
+  // Tile T is loaded during steps T-2 and T-1 and used in step T (and in
+  // step T+1 by the late waves' PV). At the top of step T: tile T resident
+  // for every wave, every wave done with tile T-2, whose slot receives T+2.
+  if (ntiles > 0) issue_tile(0);
+  if (ntiles > 1) issue_tile(1);
+  for (int32_t T = 0; T < ntiles; ++T) {
+    if (T + 1 < ntiles) wait_vmcnt<G::kLoadsPerTile>();
+    else wait_vmcnt<0>();
     __syncthreads();
+    if (T + 2 < ntiles) issue_tile(T + 2);
+    if (late && late_pending) {
+      pv_tile(late_slot, pb_late);
+      late_pending = false;
+    }
+    const int slot = T % G::kSlots;
+    if (wave_live && ks + T * G::kK < wave_hi) {
+      bf16x8 pb[G::kKB][2];
+      scores_and_p(T, slot, pb);
+      if (late) {
+#pragma unroll
+        for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2) pb_late[kb][t2] = pb[kb][t2];
+        late_pending = true;
+        late_slot = slot;
+      } else {
+        pv_tile(slot, pb);
+      }
+    }
   }
+  if (late_pending) pv_tile(late_slot, pb_late);
 
   // Epilogue (the cross-lane sum first, while all lanes run).
   const float l_tot = l_run + __shfl_xor(l_run, 32);

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int lm = lane & 31;
   const int lh = lane >> 5;
 
@@ -116,14 +116,11 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
     for (int u = 0; u < G::kF4PerThread; ++u) {
       const int f = tid + kThreadsPerWG * u;
       const int row = f / (D / 4), c4 = f % (D / 4);
-      const int32_t j = j0 + row;
-      if (j < a.seq_kv) {
-        kreg[u] = *reinterpret_cast<const f32x4*>(kg + (size_t)j * D + 4 * c4);
-        vreg[u] = *reinterpret_cast<const f32x4*>(vg + (size_t)j * D + 4 * c4);
-      } else {
-        kreg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        vreg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      // Rows past seq_kv re-read the last key row (in bounds, finite, branch
+      // free); such keys are always masked and weigh an exact zero.
+      const int32_t j = min(j0 + row, a.seq_kv - 1);
+      kreg[u] = *reinterpret_cast<const f32x4*>(kg + (size_t)j * D + 4 * c4);
+      vreg[u] = *reinterpret_cast<const f32x4*>(vg + (size_t)j * D + 4 * c4);
     }
   };
   auto store_tile = [&](int buf) {

@@ -61,6 +61,10 @@ int check_shape(int in_dtype, int o_dtype, size_t batch, size_t heads, size_t se
   if (d != 64 && d != 128) return SMA_ERR_UNSUPPORTED;
   if (o_dtype != SMA_DTYPE_F32) return SMA_ERR_UNSUPPORTED;
   if (seq_q > kMaxSeq || seq_kv > kMaxSeq || s.bh > (size_t(1) << 31)) return SMA_ERR_UNSUPPORTED;
+  // The bf16 kernel addresses one (batch, head)'s K and V through 32-bit
+  // buffer offsets: keep them, with a tile of slack, below 2^31 bytes.
+  if (in_dtype == SMA_DTYPE_BF16 && (seq_kv + 256) * d * 2 > (size_t(1) << 31))
+    return SMA_ERR_UNSUPPORTED;
   *sh = s;
   return SMA_OK;
 }

@@ -78,6 +78,9 @@ def test_unsupported():
     assert _v(d=256) == UNSUP
     assert _v(odt=BF16, idt=BF16, d=128) == UNSUP
     assert _v(sq=(1 << 30) + 1) == UNSUP
+    assert _v(idt=BF16, d=128, skv=(1 << 23) - 256) == OK  # K/V of one head just under 2 GiB
+    assert _v(idt=BF16, d=128, skv=1 << 23) == UNSUP
+    assert _v(idt=F32, d=128, skv=1 << 23) == OK
 
 
 def test_alignment():
