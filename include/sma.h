@@ -69,6 +69,27 @@ typedef enum {
   SMA_ERR_HIP = 6            /* the HIP runtime reported an error (device query or launch) */
 } sma_status;
 
+/* Kernels the library can run for one call. Each computes the whole operation;
+ * they differ only in how the work is spread over workgroups. */
+typedef enum {
+  SMA_KERNEL_AUTO = -1,         /* let the library choose (what sma_attention_fwd does) */
+  SMA_KERNEL_F32_QBLOCK = 0,    /* fp32: 128 query rows per workgroup; keys optionally split
+                                   across workgroups, merged by a second kernel */
+  SMA_KERNEL_F32_KSPLIT = 1,    /* fp32: 32 query rows per workgroup, keys split over its four
+                                   waves and merged in-workgroup; never needs a workspace */
+  SMA_KERNEL_BF16_QBLOCK = 2    /* bf16: 256 query rows per workgroup; keys optionally split
+                                   across workgroups, merged by a second kernel */
+} sma_kernel;
+
+/* How a call is carried out: filled by sma_attention_fwd_plan, read by
+ * sma_attention_fwd_ex. */
+typedef struct sma_plan {
+  int kernel;              /* an sma_kernel other than SMA_KERNEL_AUTO */
+  int nsplit;              /* key splits per query row across workgroups, 1..32 (1 = none) */
+  size_t workgroups;       /* workgroups of the main kernel */
+  size_t workspace_bytes;  /* workspace this plan needs (0 when nsplit == 1) */
+} sma_plan;
+
 /* Attention forward.
  *
  *   q, k, v    device pointers, element type in_dtype, layout above. k and v may
@@ -122,6 +143,34 @@ int sma_attention_fwd_validate(const void* q, const void* k, const void* v, cons
  * used for this shape. Invalid arguments also give 0. */
 size_t sma_attention_fwd_workspace_bytes(int in_dtype, size_t batch, size_t heads, size_t seq_q,
                                          size_t seq_kv, size_t head_dim, int causal, int num_cus);
+
+/* The plan for a shape, on the host only (no launch). kernel: SMA_KERNEL_AUTO
+ * for the library's own choice, else the kernel to plan for (one that does not
+ * run in_dtype -> UNSUPPORTED). nsplit: 0 lets the library choose the key
+ * split; 1..32 asks for that many (the plan may merge splits so that each
+ * keeps a whole number of key tiles, and SMA_KERNEL_F32_KSPLIT accepts only
+ * 0 or 1, and only (seq_q + 32) and (seq_kv + 32) rows of head_dim floats of
+ * at most 2 GiB; otherwise UNSUPPORTED). num_cus as for sma_attention_fwd_workspace_bytes. The plan of
+ * SMA_KERNEL_AUTO is the one sma_attention_fwd follows when it is given at
+ * least plan.workspace_bytes of workspace. Shape errors as sma_attention_fwd;
+ * out NULL -> NULL_POINTER. */
+int sma_attention_fwd_plan(int in_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
+                           size_t head_dim, int causal, int kernel, int nsplit, int num_cus,
+                           sma_plan* out);
+
+/* sma_attention_fwd with the kernel and key split taken from `plan` (NULL:
+ * the library's choice, exactly sma_attention_fwd) and with the measurement
+ * events of sma_attention_fwd_timed. Only plan->kernel and plan->nsplit are
+ * read; the plan is rebuilt from them for this shape and the current device,
+ * so plan->workgroups and plan->workspace_bytes are informative. Unlike the
+ * automatic choice, an explicit split is never dropped: a workspace smaller
+ * than the rebuilt plan needs -> INVALID_VALUE. Results are the same for every
+ * plan up to floating-point rounding order. */
+int sma_attention_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
+                         size_t seq_kv, size_t head_dim, double scale, int causal, void* workspace,
+                         size_t workspace_bytes, const sma_plan* plan, void* stream,
+                         void* event_before, void* event_after);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* sma_status_string(int status);

@@ -17,11 +17,27 @@ LIB_PATH = os.path.join(PKG, "libsma.so")
 SMA_DTYPE_F32 = 0
 SMA_DTYPE_BF16 = 1
 SMA_OK = 0
+SMA_KERNEL_AUTO = -1
+SMA_KERNEL_F32_QBLOCK = 0
+SMA_KERNEL_F32_KSPLIT = 1
+SMA_KERNEL_BF16_QBLOCK = 2
+KERNEL_NAMES = {SMA_KERNEL_F32_QBLOCK: "f32_qblock", SMA_KERNEL_F32_KSPLIT: "f32_ksplit",
+                SMA_KERNEL_BF16_QBLOCK: "bf16_qblock"}
 STATUS_NAMES = {0: "SMA_OK", 1: "SMA_ERR_NULL_POINTER", 2: "SMA_ERR_INVALID_VALUE",
                 3: "SMA_ERR_UNSUPPORTED", 4: "SMA_ERR_MISALIGNED", 5: "SMA_ERR_ALIASING",
                 6: "SMA_ERR_HIP"}
 
 _lib = None
+
+
+class Plan(ctypes.Structure):
+    """struct sma_plan: kernel, key splits, workgroups, workspace bytes."""
+    _fields_ = [("kernel", ctypes.c_int), ("nsplit", ctypes.c_int),
+                ("workgroups", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
+
+    def __repr__(self):
+        return (f"Plan(kernel={KERNEL_NAMES.get(self.kernel, self.kernel)}, nsplit={self.nsplit}, "
+                f"workgroups={self.workgroups}, workspace_bytes={self.workspace_bytes})")
 
 
 class SMAError(RuntimeError):
@@ -53,6 +69,13 @@ def library():
         lib.sma_attention_fwd_workspace_bytes.argtypes = [ctypes.c_int, sz, sz, sz, sz, sz,
                                                           ctypes.c_int, ctypes.c_int]
         lib.sma_attention_fwd_workspace_bytes.restype = sz
+        lib.sma_attention_fwd_plan.argtypes = [ctypes.c_int, sz, sz, sz, sz, sz, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.POINTER(Plan)]
+        lib.sma_attention_fwd_plan.restype = ctypes.c_int
+        lib.sma_attention_fwd_ex.argtypes = (lib.sma_attention_fwd.argtypes[:16] +
+                                             [ctypes.POINTER(Plan), vp, vp, vp])
+        lib.sma_attention_fwd_ex.restype = ctypes.c_int
         lib.sma_status_string.argtypes = [ctypes.c_int]
         lib.sma_status_string.restype = ctypes.c_char_p
         lib.sma_abi_version.argtypes = []
@@ -78,6 +101,16 @@ def workspace_bytes(in_dtype: int, batch: int, heads: int, seq_q: int, seq_kv: i
                     head_dim: int, causal: bool, num_cus: int = 0) -> int:
     return int(library().sma_attention_fwd_workspace_bytes(in_dtype, batch, heads, seq_q, seq_kv,
                                                            head_dim, int(bool(causal)), num_cus))
+
+
+def plan(in_dtype: int, batch: int, heads: int, seq_q: int, seq_kv: int, head_dim: int,
+         causal: bool, kernel: int = SMA_KERNEL_AUTO, nsplit: int = 0, num_cus: int = 0) -> Plan:
+    """sma_attention_fwd_plan: the kernel, split and workspace a call would use."""
+    out = Plan()
+    _raise(library().sma_attention_fwd_plan(in_dtype, batch, heads, seq_q, seq_kv, head_dim,
+                                            int(bool(causal)), kernel, nsplit, num_cus,
+                                            ctypes.byref(out)))
+    return out
 
 
 def validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dtype, batch, heads, seq_q, seq_kv,
@@ -107,14 +140,27 @@ def attention_fwd_timed_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dty
                                              stream, event_before, event_after))
 
 
+def attention_fwd_ex_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dtype, batch, heads,
+                         seq_q, seq_kv, head_dim, scale, causal, ws_ptr, ws_bytes, plan_, stream,
+                         event_before=None, event_after=None) -> None:
+    """sma_attention_fwd_ex: explicit plan (a Plan, or None for the library's choice)."""
+    _raise(library().sma_attention_fwd_ex(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dtype,
+                                          batch, heads, seq_q, seq_kv, head_dim, float(scale),
+                                          int(bool(causal)), ws_ptr, ws_bytes,
+                                          ctypes.byref(plan_) if plan_ is not None else None,
+                                          stream, event_before, event_after))
+
+
 def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=None,
-                  workspace=None, stream=None):
+                  workspace=None, stream=None, kernel=None, nsplit=0):
     """O = softmax(scale * Q K^T + mask) V on the GPU.
 
     q [B,H,Sq,D], k and v [B,H,Skv,D]: contiguous torch tensors on the current
     HIP device, all float32 or all bfloat16. Returns O (float32, [B,H,Sq,D]) and,
     with return_lse, the per-row natural-log LSE (float32, [B,H,Sq]).
     scale=None means 1/sqrt(D). causal uses the bottom-right alignment.
+    kernel (an SMA_KERNEL_* code) and nsplit force a plan; by default the
+    library chooses. A forced split gets a workspace of the size it needs.
     """
     import torch
 
@@ -151,15 +197,20 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
             raise ValueError(f"{name} must be a contiguous float32 tensor on {dev}")
     if out.shape != (B, H, Sq, D) or (lse is not None and lse.shape != (B, H, Sq)):
         raise ValueError("out/lse shape mismatch")
-    need = workspace_bytes(in_dt, B, H, Sq, Skv, D, causal)
+    forced = None
+    if kernel is not None and kernel != SMA_KERNEL_AUTO:
+        forced = plan(in_dt, B, H, Sq, Skv, D, causal, kernel, nsplit)
+        need = forced.workspace_bytes
+    else:
+        need = workspace_bytes(in_dt, B, H, Sq, Skv, D, causal)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
         stream = torch.cuda.current_stream()
-    attention_fwd_raw(q.data_ptr(), k.data_ptr() if Skv else None, v.data_ptr() if Skv else None,
-                      out.data_ptr(), lse.data_ptr() if lse is not None else None, in_dt,
-                      SMA_DTYPE_F32, B, H, Sq, Skv, D, scale, causal, ws_ptr, ws_bytes,
-                      stream.cuda_stream)
+    attention_fwd_ex_raw(q.data_ptr(), k.data_ptr() if Skv else None, v.data_ptr() if Skv else None,
+                         out.data_ptr(), lse.data_ptr() if lse is not None else None, in_dt,
+                         SMA_DTYPE_F32, B, H, Sq, Skv, D, scale, causal, ws_ptr, ws_bytes, forced,
+                         stream.cuda_stream)
     return (out, lse) if return_lse else out

@@ -48,4 +48,36 @@ __device__ __forceinline__ int32_t key_limit(int32_t row, int32_t seq_q, int32_t
   return hi < split_end ? hi : split_end;
 }
 
+// Wait until at most N vector-memory operations of this wave are in flight
+// (expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One 16-byte-per-lane direct-to-LDS load through a buffer resource: lane i's
+// chunk lands at LDS byte address lds_addr + 16*i (lds_addr wave-uniform, in
+// M0). Issued as inline asm so that the compiler adds no conservative waits
+// for it before unrelated LDS reads; the kernel waits explicitly (wait_vmcnt)
+// before a tile is used. The s_nop covers the M0-write hazard.
+__device__ __forceinline__ void dma_load_x4(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset,
+                                            unsigned lds_addr) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ unsigned lds_address(const void* p) {
+  return (unsigned)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// Buffer resource over `bytes` bytes at `base`: loads at byte offsets at or
+// past `bytes` return zeros. Word 3 selects a raw (untyped) buffer on gfx9.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, unsigned bytes) {
+  constexpr int kRsrcWord3 = 0x00020000;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+
 }  // namespace sma

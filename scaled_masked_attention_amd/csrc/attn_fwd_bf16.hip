@@ -81,31 +81,6 @@ __device__ __forceinline__ int v_swz(int r) {
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-// Wait until at most N vector-memory operations of this wave are in flight
-// (expcnt and lgkmcnt left unconstrained).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// One 16-byte-per-lane direct-to-LDS load through a buffer resource: lane i's
-// chunk lands at LDS byte address lds_addr + 16*i (lds_addr wave-uniform, in
-// M0). Issued as inline asm so that the compiler adds no conservative waits
-// for it before unrelated LDS reads; the kernel waits explicitly (wait_vmcnt)
-// before a tile is used. The s_nop covers the M0-write hazard.
-__device__ __forceinline__ void dma_load_x4(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset,
-                                            unsigned lds_addr) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voffset), "s"(rsrc), "{m0}"(lds_addr)
-               : "memory");
-}
-
-__device__ __forceinline__ unsigned lds_address(const void* p) {
-  return (unsigned)(size_t)(__attribute__((address_space(3))) const void*)p;
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   using G = BGeom<D>;
@@ -153,14 +128,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
 
   // Buffer resources over this (batch, head)'s K and V: rows past the last key
   // fall outside the byte range and read as zeros.
-  constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, gfx9-family dword 3
   const unsigned kv_bytes = (unsigned)a.seq_kv * (unsigned)(2 * D);
-  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<unsigned short*>(static_cast<const unsigned short*>(a.k)) + (size_t)t.bh * a.seq_kv * D,
-      0, (int)kv_bytes, (int)kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<unsigned short*>(static_cast<const unsigned short*>(a.v)) + (size_t)t.bh * a.seq_kv * D,
-      0, (int)kv_bytes, (int)kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      raw_buffer(static_cast<const unsigned short*>(a.k) + (size_t)t.bh * a.seq_kv * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      raw_buffer(static_cast<const unsigned short*>(a.v) + (size_t)t.bh * a.seq_kv * D, kv_bytes);
   // Each wave-wide load fills 64 consecutive LDS chunks: position
   // p = (u*waves + wave)*64 + lane is row rho = p / chunks_per_row, chunk
   // p % chunks_per_row; the lane fetches the global chunk that belongs there

@@ -1,0 +1,323 @@
+// Attention forward, fp32 inputs, for shapes with few query rows per head
+// (too few 128-row blocks to fill the GPU) and short key ranges. Same method
+// and conventions as attn_fwd_f32.hip (oxicuda ComputeBackend `attention`;
+// pulsatrix HIPBackend `softmax_rows`, `logsumexp_rows`; TorchLean hard-masked
+// softmax).
+//
+// Workgroup: 32 query rows of one (batch, head) and 4 waves that split the
+// keys the rows admit into four contiguous ranges of 32-key blocks. At the end
+// the four partial results (running max m_w, denominator l_w and unnormalised
+// output O_w, all relative to m_w) are merged through LDS:
+//   M = max_w m_w,  L = sum_w 2^(m_w - M) l_w,  O = sum_w 2^(m_w - M) O_w / L,
+// the log-sum-exp identity of the split-combine kernel, so no workspace and
+// no second launch are needed.
+//
+// Data movement. The Q tile is copied once per workgroup into LDS, and each
+// wave streams its K blocks into a private LDS slot, both with coalesced
+// direct-to-LDS loads (1 KB of consecutive rows per instruction); the MFMA
+// operands are read back from LDS. Block b+1's K copy is in flight while
+// block b is computed. V operands are read from global memory (L2) straight
+// into registers: each load instruction already covers two whole rows.
+//
+// MFMA layouts (v_mfma_f32_32x32x2f32, lane = 32*h + m):
+//   S^T = K Q^T: step (u, e) multiplies head dims 8u + 4h + e of key m (A) and
+//     query m (B); lane (m, h) then holds the scores of query m for keys
+//     8*(r/4) + 4*h + r%4, r = 0..15.
+//   O^T += V^T P^T: step r pairs lane (m, h) with key 8*(r/4) + 4*h + r%4;
+//     the A operand is V at head dims (D/32)*m + chunk.
+#include "attn_common.h"
+
+namespace sma {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int N>
+struct FVecW;
+template <>
+struct FVecW<2> { typedef f32x2 T; };
+template <>
+struct FVecW<4> { typedef f32x4 T; };
+
+constexpr float kTauW = 8.0f;  // lazy running-max threshold, log2 units
+
+template <int D>
+struct WGeom {
+  static constexpr int kWaves = 4;
+  static constexpr int kQ = kF32WsplitQueriesPerWG;  // query rows per workgroup
+  static constexpr int kNch = D / 32;                // O^T chunks per lane
+  static constexpr int kSteps = D / 8;               // S^T MFMA groups of 4 (head dims 8u..8u+7)
+  static constexpr int kRowBytes = 4 * D;
+  static constexpr int kTileBytes = 32 * kRowBytes;  // one 32-row tile of Q or K
+  static constexpr int kDmaPerTile = kTileBytes / 1024;
+  static constexpr int kOStride = D + 4;             // padded partial-O row in LDS (floats)
+  static constexpr int kStageBytes = kTileBytes * (1 + kWaves);  // Q tile + one K slot per wave
+  static constexpr int kOPartBytes = kWaves * kQ * kOStride * 4;
+  static constexpr int kLdsBytes = kStageBytes > kOPartBytes ? kStageBytes : kOPartBytes;
+  static_assert(kQ == 32, "one 32x32 MFMA tile of queries");
+  static_assert(kDmaPerTile % kWaves == 0, "the Q tile copy splits evenly over the waves");
+};
+
+// A 32-row tile (of Q or K) in LDS: row r's 16-byte chunk c is stored at chunk
+// position c ^ (r & 15) of the row. A direct-to-LDS instruction fills 1 KB of
+// consecutive positions, so lane l of copy instruction t fetches the global
+// chunk that belongs at position p = 64t + l.
+template <int D>
+__device__ __forceinline__ unsigned tile_src_offset(int t, int lane) {
+  constexpr int kChunks = D / 4;  // 16-byte chunks per row
+  const int p = 64 * t + lane;
+  const int r = p / kChunks;
+  const int c = (p % kChunks) ^ (r & 15);
+  return (unsigned)(r * 4 * D + 16 * c);
+}
+
+// LDS byte offset, within a tile, of the 16 bytes holding head dims
+// 8u + 4h .. 8u + 4h + 3 of row m (the operand of MFMA group u).
+template <int D>
+__device__ __forceinline__ unsigned tile_operand_offset(int m, int h, int u) {
+  return (unsigned)(m * 4 * D + 16 * ((2 * u + h) ^ (m & 15)));
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
+  using G = WGeom<D>;
+  using VecN = typename FVecW<G::kNch>::T;
+  // Staging (Q tile, K slots) during the key loop; partial O afterwards.
+  __shared__ __attribute__((aligned(16))) unsigned char lds[G::kLdsBytes];
+  __shared__ float m_part[G::kWaves][G::kQ];
+  __shared__ float l_part[G::kWaves][G::kQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int lm = lane & 31;
+  const int lh = lane >> 5;
+  unsigned char* const q_tile = lds;
+  unsigned char* const k_slot = lds + G::kTileBytes * (1 + wave);
+
+  // Workgroup -> (batch*head, 32-row query block), XCD-aware order.
+  const uint32_t lam = xcd_remap(blockIdx.x, a.nwg);
+  const int64_t bh = (int64_t)(lam / (uint32_t)a.nqb);
+  const int32_t q0 = (int32_t)(lam % (uint32_t)a.nqb) * G::kQ;
+
+  const int32_t my_row = q0 + lm;
+  const int32_t last_row = min(q0 + G::kQ - 1, a.seq_q - 1);
+  const int32_t lim = key_limit<CAUSAL>(my_row, a.seq_q, a.seq_kv, a.seq_kv);
+  const int32_t lo = key_limit<CAUSAL>(q0, a.seq_q, a.seq_kv, a.seq_kv);        // first row's limit
+  const int32_t hi = key_limit<CAUSAL>(last_row, a.seq_q, a.seq_kv, a.seq_kv);  // last row's limit
+  const int32_t nblocks = (hi + 31) / 32;
+  const int32_t b_begin = (int32_t)(((int64_t)nblocks * wave) / G::kWaves);
+  const int32_t b_end = (int32_t)(((int64_t)nblocks * (wave + 1)) / G::kWaves);
+
+  // Rows past the end of Q or K lie outside these ranges and read as zeros.
+  const __amdgpu_buffer_rsrc_t q_rsrc =
+      raw_buffer(static_cast<const float*>(a.q) + (size_t)bh * a.seq_q * D,
+                 (unsigned)a.seq_q * (unsigned)G::kRowBytes);
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      raw_buffer(static_cast<const float*>(a.k) + (size_t)bh * a.seq_kv * D,
+                 (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
+  auto copy_k_block = [&](int32_t b) {
+    const unsigned row0 = (unsigned)(32 * b) * (unsigned)G::kRowBytes;
+#pragma unroll
+    for (int t = 0; t < G::kDmaPerTile; ++t)
+      dma_load_x4(k_rsrc, row0 + tile_src_offset<D>(t, lane), lds_address(k_slot + 1024 * t));
+  };
+
+  // Q tile (the waves copy a quarter each) and this wave's first K block.
+#pragma unroll
+  for (int i = 0; i < G::kDmaPerTile / G::kWaves; ++i) {
+    const int t = i * G::kWaves + wave;
+    dma_load_x4(q_rsrc, (unsigned)q0 * (unsigned)G::kRowBytes + tile_src_offset<D>(t, lane),
+                lds_address(q_tile + 1024 * t));
+  }
+  if (b_begin < b_end) copy_k_block(b_begin);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  float qr[4 * G::kSteps];  // group u, element e: head dim 8u + 4*lh + e of query lm
+#pragma unroll
+  for (int u = 0; u < G::kSteps; ++u) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(q_tile + tile_operand_offset<D>(lm, lh, u));
+    qr[4 * u + 0] = x[0];
+    qr[4 * u + 1] = x[1];
+    qr[4 * u + 2] = x[2];
+    qr[4 * u + 3] = x[3];
+  }
+  if (a.negate_q) {
+#pragma unroll
+    for (int i = 0; i < 4 * G::kSteps; ++i) qr[i] = -qr[i];
+  }
+  const float* vg = static_cast<const float*>(a.v) + (size_t)bh * a.seq_kv * D;
+
+  f32x16 oacc[G::kNch];
+#pragma unroll
+  for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int32_t b = b_begin; b < b_end; ++b) {
+    const int32_t j0 = 32 * b;
+    // K block b has landed in this wave's slot (it is the only copy in flight).
+    wait_vmcnt<0>();
+    f32x4 kk[G::kSteps];
+#pragma unroll
+    for (int u = 0; u < G::kSteps; ++u)
+      kk[u] = *reinterpret_cast<const f32x4*>(k_slot + tile_operand_offset<D>(lm, lh, u));
+    // The slot is reused for block b+1 once these reads are done. The copy is
+    // issued before the V loads below, so the compiler's own wait counts for
+    // those stay exact.
+    if (b + 1 < b_end) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the K reads have returned
+      copy_k_block(b + 1);
+    }
+    // V operands: step r pairs this lane with key 8*(r/4) + 4*h + r%4 (rows
+    // past seq_kv re-read the last key row; such keys are masked and weigh an
+    // exact zero).
+    VecN vv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int32_t j = min(j0 + 8 * (r / 4) + 4 * lh + (r % 4), a.seq_kv - 1);
+      vv[r] = *reinterpret_cast<const VecN*>(vg + (size_t)j * D + G::kNch * lm);
+    }
+
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int u = 0; u < G::kSteps; ++u) {
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(kk[u][0], qr[4 * u + 0], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(kk[u][1], qr[4 * u + 1], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(kk[u][2], qr[4 * u + 2], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(kk[u][3], qr[4 * u + 3], s, 0, 0, 0);
+    }
+    float tv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tv[r] = s[r] * a.c;
+    if (j0 + 32 > lo) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int32_t j = j0 + 8 * (r / 4) + 4 * lh + (r % 4);
+        tv[r] = j < lim ? tv[r] : -INFINITY;
+      }
+    }
+    float mx = tv[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, tv[r]);
+    {
+      // Lanes m and m + 32 hold the two key halves of query m: after the swap
+      // the pair holds (own, partner) on both sides, in the same order.
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    if (__any(mx > m_run + kTauW)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      tv[r] = __builtin_amdgcn_exp2f(tv[r] - m_use);
+      psum += tv[r];
+    }
+    l_run += psum;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int cb = 0; cb < G::kNch; ++cb)
+        oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[r][cb], tv[r], oacc[cb], 0, 0, 0);
+  }
+
+  float l_tot;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
+                                                     false, false);
+    l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  // Every wave is done with the staging area before it becomes partial O.
+  __syncthreads();
+  {
+    float* orow = reinterpret_cast<float*>(lds) + (wave * G::kQ + lm) * G::kOStride;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = 8 * (r / 4) + 4 * lh + (r % 4);
+      VecN out;
+#pragma unroll
+      for (int cb = 0; cb < G::kNch; ++cb) out[cb] = oacc[cb][r];
+      *reinterpret_cast<VecN*>(orow + G::kNch * m) = out;
+    }
+    if (lh == 0) {
+      m_part[wave][lm] = m_run;
+      l_part[wave][lm] = l_tot;
+    }
+  }
+  __syncthreads();
+
+  // Merge: thread -> (query, 4 consecutive head dims).
+  const float* o_part = reinterpret_cast<const float*>(lds);
+  constexpr int kThreadsPerRow = D / 4;
+  constexpr int kRowsPerPass = 256 / kThreadsPerRow;
+#pragma unroll
+  for (int pass = 0; pass < G::kQ / kRowsPerPass; ++pass) {
+    const int q = pass * kRowsPerPass + tid / kThreadsPerRow;
+    const int c4 = tid % kThreadsPerRow;
+    const int32_t row = q0 + q;
+    float mw[G::kWaves], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < G::kWaves; ++w) {
+      mw[w] = m_part[w][q];
+      M = fmaxf(M, mw[w]);
+    }
+    float L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < G::kWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(mw[w] - M);  // 0 for a wave with no keys
+        L += f * l_part[w][q];
+        const f32x4 x =
+            *reinterpret_cast<const f32x4*>(o_part + (w * G::kQ + q) * G::kOStride + 4 * c4);
+        acc[0] += f * x[0];
+        acc[1] += f * x[1];
+        acc[2] += f * x[2];
+        acc[3] += f * x[3];
+      }
+    }
+    if (row >= a.seq_q) continue;
+    const bool empty = !(L > 0.f);
+    const float inv = empty ? 0.f : 1.0f / L;
+    f32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = empty ? 0.f : acc[e] * inv;
+    const size_t row_id = (size_t)bh * a.seq_q + row;
+    *reinterpret_cast<f32x4*>(a.o + row_id * D + 4 * c4) = out;
+    if (a.lse && c4 == 0)
+      a.lse[row_id] = empty ? -INFINITY : (M + __builtin_amdgcn_logf(L)) * 0.69314718055994530942f;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_wsplit_variant(const FwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((attn_fwd_f32_wsplit_kernel<D, CAUSAL>), dim3(a.nwg), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32_wsplit(const FwdArgs& a, int head_dim, bool causal, hipStream_t s) {
+  if (head_dim == 64) return causal ? launch_wsplit_variant<64, true>(a, s) : launch_wsplit_variant<64, false>(a, s);
+  if (head_dim == 128) return causal ? launch_wsplit_variant<128, true>(a, s) : launch_wsplit_variant<128, false>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sma

@@ -70,26 +70,36 @@ int check_shape(int in_dtype, int o_dtype, size_t batch, size_t heads, size_t se
 }
 
 struct Plan {
+  int kernel = SMA_KERNEL_F32_QBLOCK;
   int32_t nqb = 0, nsplit = 1, split_len = 0;
   size_t nwg = 0;
   size_t ws_bytes = 0;       // workspace the split needs (0 when nsplit == 1)
   size_t part_lse_off = 0;   // byte offset of the partial LSE array in the workspace
 };
 
-int queries_per_wg(int dt) { return dt == SMA_DTYPE_F32 ? sma::kF32QueriesPerWG : sma::kBF16QueriesPerWG; }
-int keys_per_tile(int dt) { return dt == SMA_DTYPE_F32 ? sma::kF32KeysPerTile : sma::kBF16KeysPerTile; }
+int queries_per_wg(int kernel) {
+  switch (kernel) {
+    case SMA_KERNEL_F32_KSPLIT: return sma::kF32WsplitQueriesPerWG;
+    case SMA_KERNEL_BF16_QBLOCK: return sma::kBF16QueriesPerWG;
+    default: return sma::kF32QueriesPerWG;
+  }
+}
+int keys_per_tile(int kernel) {
+  return kernel == SMA_KERNEL_BF16_QBLOCK ? sma::kBF16KeysPerTile : sma::kF32KeysPerTile;
+}
+bool kernel_fits_dtype(int kernel, int in_dtype) {
+  if (in_dtype == SMA_DTYPE_BF16) return kernel == SMA_KERNEL_BF16_QBLOCK;
+  return kernel == SMA_KERNEL_F32_QBLOCK || kernel == SMA_KERNEL_F32_KSPLIT;
+}
 
 size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
-// Key splitting when the query blocks alone cannot fill the GPU: aim for one
-// resident workgroup per slot, keep at least four key tiles per split.
-Plan make_plan(const Shape& s, int num_cus) {
-  Plan p;
-  const size_t qpw = (size_t)queries_per_wg(s.in_dtype);
-  const size_t kt = (size_t)keys_per_tile(s.in_dtype);
-  p.nqb = (int32_t)((s.seq_q + qpw - 1) / qpw);
-  const size_t base = s.bh * (size_t)p.nqb;
-  const size_t slots = (size_t)(num_cus > 0 ? num_cus : 256) * (s.in_dtype == SMA_DTYPE_F32 ? 2 : 1);
+// Key splits for a query-block kernel when its blocks alone cannot fill the
+// GPU: aim for one resident workgroup per slot, keep at least four key tiles
+// per split.
+size_t auto_splits(const Shape& s, int kernel, size_t base, int num_cus) {
+  const size_t kt = (size_t)keys_per_tile(kernel);
+  const size_t slots = (size_t)num_cus * (kernel == SMA_KERNEL_BF16_QBLOCK ? 1 : 2);
   size_t nsplit = 1;
   if (base > 0 && base < slots && s.seq_kv >= 8 * kt) {
     size_t want = (slots + base - 1) / base;
@@ -98,12 +108,52 @@ Plan make_plan(const Shape& s, int num_cus) {
     if (nsplit > (size_t)kMaxSplits) nsplit = kMaxSplits;
     if (nsplit < 1) nsplit = 1;
   }
+  return nsplit;
+}
+
+// The fp32 kernel that splits keys over the waves of one 32-row workgroup
+// needs no workspace and no second launch; it wins when the 128-row blocks
+// cannot fill the GPU and each row has few keys (each workgroup reads all of
+// its head's K and V from L2, so long key ranges favour the 128-row kernel
+// with a key split).
+constexpr size_t kKsplitMaxKeys = 2048;
+constexpr size_t kKsplitAlwaysKeys = 512;
+
+// The in-workgroup key-split kernel addresses one (batch, head)'s Q and K
+// through 32-bit buffer offsets: keep them, with a tile of slack, below 2^31.
+bool ksplit_fits(const Shape& s) {
+  const size_t lim = size_t(1) << 31;
+  return (s.seq_q + 32) * s.d * 4 <= lim && (s.seq_kv + 32) * s.d * 4 <= lim;
+}
+
+int auto_kernel(const Shape& s, int num_cus) {
+  if (s.in_dtype == SMA_DTYPE_BF16) return SMA_KERNEL_BF16_QBLOCK;
+  if (!ksplit_fits(s)) return SMA_KERNEL_F32_QBLOCK;
+  const size_t base = s.bh * ((s.seq_q + sma::kF32QueriesPerWG - 1) / sma::kF32QueriesPerWG);
+  if (base >= (size_t)num_cus * 2 || s.seq_kv > kKsplitMaxKeys) return SMA_KERNEL_F32_QBLOCK;
+  const size_t nwg32 = s.bh * ((s.seq_q + sma::kF32WsplitQueriesPerWG - 1) / sma::kF32WsplitQueriesPerWG);
+  if (nwg32 >= (size_t)num_cus || s.seq_kv <= kKsplitAlwaysKeys) return SMA_KERNEL_F32_KSPLIT;
+  return SMA_KERNEL_F32_QBLOCK;
+}
+
+// Plan for `kernel` with `nsplit` key splits (0: chosen here). The caller has
+// checked that the kernel fits the dtype and that nsplit is in range.
+Plan plan_for(const Shape& s, int kernel, size_t nsplit, int num_cus) {
+  Plan p;
+  p.kernel = kernel;
+  const size_t qpw = (size_t)queries_per_wg(kernel);
+  const size_t kt = (size_t)keys_per_tile(kernel);
+  p.nqb = (int32_t)((s.seq_q + qpw - 1) / qpw);
+  const size_t base = s.bh * (size_t)p.nqb;
+  if (kernel == SMA_KERNEL_F32_KSPLIT || s.seq_kv == 0) nsplit = 1;
+  if (nsplit == 0) nsplit = auto_splits(s, kernel, base, num_cus);
   size_t split_len = s.seq_kv;
   if (nsplit > 1) {
     split_len = round_up((s.seq_kv + nsplit - 1) / nsplit, kt);
     nsplit = (s.seq_kv + split_len - 1) / split_len;
   }
   if (split_len == 0) split_len = kt;
+  if (nsplit < 1) nsplit = 1;
   p.nsplit = (int32_t)nsplit;
   p.split_len = (int32_t)split_len;
   p.nwg = base * nsplit;
@@ -115,15 +165,7 @@ Plan make_plan(const Shape& s, int num_cus) {
   return p;
 }
 
-Plan plan_without_split(const Shape& s) {
-  Plan p;
-  const size_t qpw = (size_t)queries_per_wg(s.in_dtype);
-  p.nqb = (int32_t)((s.seq_q + qpw - 1) / qpw);
-  p.nsplit = 1;
-  p.split_len = (int32_t)(s.seq_kv > 0 ? s.seq_kv : keys_per_tile(s.in_dtype));
-  p.nwg = s.bh * (size_t)p.nqb;
-  return p;
-}
+Plan auto_plan(const Shape& s, int num_cus) { return plan_for(s, auto_kernel(s, num_cus), 0, num_cus); }
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || na == 0 || nb == 0) return false;
@@ -165,7 +207,8 @@ int validate_all(const void* q, const void* k, const void* v, const void* o, con
   if (sh->rows == 0) return SMA_OK;
   st = check_pointers(*sh, q, k, v, o, lse, ws, ws_bytes);
   if (st != SMA_OK) return st;
-  if (plan_without_split(*sh).nwg > kMaxWorkgroups) return SMA_ERR_UNSUPPORTED;
+  const size_t nwg32 = sh->bh * ((sh->seq_q + sma::kF32WsplitQueriesPerWG - 1) / sma::kF32WsplitQueriesPerWG);
+  if (nwg32 > kMaxWorkgroups) return SMA_ERR_UNSUPPORTED;
   if ((sh->rows * sh->d / 4 + 255) / 256 > kMaxWorkgroups) return SMA_ERR_UNSUPPORTED;
   return SMA_OK;
 }
@@ -205,31 +248,75 @@ int sma_attention_fwd_validate(const void* q, const void* k, const void* v, cons
 
 size_t sma_attention_fwd_workspace_bytes(int in_dtype, size_t batch, size_t heads, size_t seq_q,
                                          size_t seq_kv, size_t head_dim, int causal, int num_cus) {
-  (void)causal;
-  Shape sh;
-  if (check_shape(in_dtype, SMA_DTYPE_F32, batch, heads, seq_q, seq_kv, head_dim, 1.0, &sh) != SMA_OK)
+  sma_plan p;
+  if (sma_attention_fwd_plan(in_dtype, batch, heads, seq_q, seq_kv, head_dim, causal,
+                             SMA_KERNEL_AUTO, 0, num_cus, &p) != SMA_OK)
     return 0;
-  if (sh.rows == 0) return 0;
-  int cus = num_cus;
-  if (cus <= 0 && current_device_cus(&cus) != SMA_OK) cus = 256;
-  return make_plan(sh, cus).ws_bytes;
+  return p.workspace_bytes;
 }
 
-int sma_attention_fwd_timed(const void* q, const void* k, const void* v, void* o, float* lse,
-                            int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
-                            size_t seq_kv, size_t head_dim, double scale, int causal,
-                            void* workspace, size_t workspace_bytes, void* stream,
-                            void* event_before, void* event_after) {
+int sma_attention_fwd_plan(int in_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
+                           size_t head_dim, int causal, int kernel, int nsplit, int num_cus,
+                           sma_plan* out) {
+  (void)causal;
+  if (!out) return SMA_ERR_NULL_POINTER;
+  Shape sh;
+  int st = check_shape(in_dtype, SMA_DTYPE_F32, batch, heads, seq_q, seq_kv, head_dim, 1.0, &sh);
+  if (st != SMA_OK) return st;
+  if (nsplit < 0 || nsplit > kMaxSplits) return SMA_ERR_INVALID_VALUE;
+  if (kernel != SMA_KERNEL_AUTO) {
+    if (kernel != SMA_KERNEL_F32_QBLOCK && kernel != SMA_KERNEL_F32_KSPLIT &&
+        kernel != SMA_KERNEL_BF16_QBLOCK)
+      return SMA_ERR_INVALID_VALUE;
+    if (!kernel_fits_dtype(kernel, in_dtype)) return SMA_ERR_UNSUPPORTED;
+    if (kernel == SMA_KERNEL_F32_KSPLIT && (nsplit > 1 || !ksplit_fits(sh))) return SMA_ERR_UNSUPPORTED;
+  }
+  int cus = num_cus;
+  if (cus <= 0 && current_device_cus(&cus) != SMA_OK) cus = 256;
+  Plan p;
+  if (sh.rows > 0)
+    p = kernel == SMA_KERNEL_AUTO ? auto_plan(sh, cus) : plan_for(sh, kernel, (size_t)nsplit, cus);
+  else
+    p.kernel = kernel == SMA_KERNEL_AUTO ? auto_kernel(sh, cus) : kernel;
+  out->kernel = p.kernel;
+  out->nsplit = p.nsplit;
+  out->workgroups = p.nwg;
+  out->workspace_bytes = p.ws_bytes;
+  return SMA_OK;
+}
+
+int sma_attention_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
+                         size_t seq_kv, size_t head_dim, double scale, int causal, void* workspace,
+                         size_t workspace_bytes, const sma_plan* plan, void* stream,
+                         void* event_before, void* event_after) {
   Shape sh;
   int st = validate_all(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv, head_dim,
                         scale, workspace, workspace_bytes, &sh);
-  if (st != SMA_OK || sh.rows == 0) return st;
+  if (st != SMA_OK) return st;
+  if (plan) {
+    if (plan->nsplit < 1 || plan->nsplit > kMaxSplits) return SMA_ERR_INVALID_VALUE;
+    if (plan->kernel != SMA_KERNEL_F32_QBLOCK && plan->kernel != SMA_KERNEL_F32_KSPLIT &&
+        plan->kernel != SMA_KERNEL_BF16_QBLOCK)
+      return SMA_ERR_INVALID_VALUE;
+    if (!kernel_fits_dtype(plan->kernel, in_dtype)) return SMA_ERR_UNSUPPORTED;
+    if (plan->kernel == SMA_KERNEL_F32_KSPLIT && (plan->nsplit > 1 || !ksplit_fits(sh)))
+      return SMA_ERR_UNSUPPORTED;
+  }
+  if (sh.rows == 0) return SMA_OK;
   int cus = 0;
   st = current_device_cus(&cus);
   if (st != SMA_OK) return st;
-  Plan p = make_plan(sh, cus);
-  if (p.nsplit > 1 && (!workspace || workspace_bytes < p.ws_bytes || p.nwg > kMaxWorkgroups))
-    p = plan_without_split(sh);
+  Plan p;
+  if (plan) {
+    p = plan_for(sh, plan->kernel, (size_t)plan->nsplit, cus);
+    if (p.nsplit > 1 && (!workspace || workspace_bytes < p.ws_bytes)) return SMA_ERR_INVALID_VALUE;
+    if (p.nwg > kMaxWorkgroups) return SMA_ERR_UNSUPPORTED;
+  } else {
+    p = auto_plan(sh, cus);
+    if (p.nsplit > 1 && (!workspace || workspace_bytes < p.ws_bytes || p.nwg > kMaxWorkgroups))
+      p = plan_for(sh, p.kernel, 1, cus);
+  }
 
   sma::FwdArgs a{};
   a.q = q;
@@ -253,10 +340,15 @@ int sma_attention_fwd_timed(const void* q, const void* k, const void* v, void* o
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool c = causal != 0;
+  const int d = (int)head_dim;
   if (event_before && hipEventRecord(static_cast<hipEvent_t>(event_before), s) != hipSuccess)
     return SMA_ERR_HIP;
-  hipError_t e = sh.in_dtype == SMA_DTYPE_F32 ? sma::launch_fwd_f32(a, (int)head_dim, c, s)
-                                              : sma::launch_fwd_bf16(a, (int)head_dim, c, s);
+  hipError_t e;
+  switch (p.kernel) {
+    case SMA_KERNEL_F32_KSPLIT: e = sma::launch_fwd_f32_wsplit(a, d, c, s); break;
+    case SMA_KERNEL_BF16_QBLOCK: e = sma::launch_fwd_bf16(a, d, c, s); break;
+    default: e = sma::launch_fwd_f32(a, d, c, s); break;
+  }
   if (e != hipSuccess) return SMA_ERR_HIP;
   if (event_after && hipEventRecord(static_cast<hipEvent_t>(event_after), s) != hipSuccess)
     return SMA_ERR_HIP;
@@ -268,19 +360,29 @@ int sma_attention_fwd_timed(const void* q, const void* k, const void* v, void* o
     ca.lse = lse;
     ca.rows = (int64_t)sh.rows;
     ca.nsplit = p.nsplit;
-    e = sma::launch_combine(ca, (int)head_dim, s);
+    e = sma::launch_combine(ca, d, s);
     if (e != hipSuccess) return SMA_ERR_HIP;
   }
   return SMA_OK;
+}
+
+int sma_attention_fwd_timed(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
+                            size_t seq_kv, size_t head_dim, double scale, int causal,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* event_before, void* event_after) {
+  return sma_attention_fwd_ex(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv,
+                              head_dim, scale, causal, workspace, workspace_bytes, nullptr, stream,
+                              event_before, event_after);
 }
 
 int sma_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
                       size_t seq_kv, size_t head_dim, double scale, int causal, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  return sma_attention_fwd_timed(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv,
-                                 head_dim, scale, causal, workspace, workspace_bytes, stream,
-                                 nullptr, nullptr);
+  return sma_attention_fwd_ex(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv,
+                              head_dim, scale, causal, workspace, workspace_bytes, nullptr, stream,
+                              nullptr, nullptr);
 }
 
 const char* sma_status_string(int status) {

@@ -40,11 +40,13 @@ struct CombineArgs {
 // Workgroup geometry the planner needs (must match the kernels).
 constexpr int kF32QueriesPerWG = 128;
 constexpr int kF32KeysPerTile = 32;
+constexpr int kF32WsplitQueriesPerWG = 32;  // in-workgroup key-split kernel
 constexpr int kBF16QueriesPerWG = 256;
 constexpr int kBF16KeysPerTile = 64;
 constexpr int kThreadsPerWG = 256;
 
 hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);
+hipError_t launch_fwd_f32_wsplit(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s);
 

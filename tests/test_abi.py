@@ -129,3 +129,92 @@ def test_package_does_not_reference_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f"{f} mentions the oracle"
+
+
+def test_plan_auto_choices():
+    P = sma.plan
+    p = P(F32, 4, 8, 512, 512, 64, False, num_cus=256)  # 128-row blocks cannot fill 256 CUs
+    assert (p.kernel, p.nsplit, p.workgroups, p.workspace_bytes) == (sma.SMA_KERNEL_F32_KSPLIT, 1, 512, 0)
+    p = P(F32, 8, 16, 2048, 2048, 128, True, num_cus=256)  # enough 128-row blocks
+    assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_F32_QBLOCK, 1, 8 * 16 * 16)
+    p = P(F32, 2, 32, 256, 4096, 128, False, num_cus=256)  # long keys: split across workgroups
+    assert p.kernel == sma.SMA_KERNEL_F32_QBLOCK and p.nsplit > 1
+    assert p.workspace_bytes == sma.workspace_bytes(F32, 2, 32, 256, 4096, 128, False, 256)
+    p = P(BF16, 1, 32, 16384, 16384, 128, True, num_cus=256)
+    assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_BF16_QBLOCK, 1, 32 * 64)
+    p = P(F32, 1, 1, 1, 4096, 64, False, num_cus=256)  # one query row, many keys
+    assert p.kernel == sma.SMA_KERNEL_F32_QBLOCK and p.nsplit == 32
+
+
+def test_plan_forced():
+    P = sma.plan
+    p = P(F32, 4, 8, 512, 512, 64, False, kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=1, num_cus=256)
+    assert (p.nsplit, p.workgroups, p.workspace_bytes) == (1, 4 * 8 * 4, 0)
+    p = P(F32, 4, 8, 512, 512, 64, False, kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=3, num_cus=256)
+    rows = 4 * 8 * 512
+    assert p.nsplit == 3 and p.workgroups == 3 * 4 * 8 * 4
+    assert p.workspace_bytes >= 3 * rows * 65 * 4
+    # a split is merged so that each keeps whole 32-key tiles: 100 keys -> at most 4 tiles
+    p = P(F32, 1, 1, 10, 100, 64, False, kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=32, num_cus=256)
+    assert p.nsplit == 4
+    p = P(F32, 1, 1, 10, 0, 64, False, kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=8, num_cus=256)
+    assert p.nsplit == 1 and p.workspace_bytes == 0
+    p = P(F32, 3, 5, 100, 300, 128, True, kernel=sma.SMA_KERNEL_F32_KSPLIT, num_cus=256)
+    assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_F32_KSPLIT, 1, 15 * 4)
+
+
+def test_plan_rejects():
+    P = sma.plan
+    with pytest.raises(sma.SMAError) as e:
+        P(BF16, 1, 1, 8, 8, 64, False, kernel=sma.SMA_KERNEL_F32_QBLOCK)
+    assert e.value.status == UNSUP
+    with pytest.raises(sma.SMAError) as e:
+        P(F32, 1, 1, 8, 8, 64, False, kernel=sma.SMA_KERNEL_BF16_QBLOCK)
+    assert e.value.status == UNSUP
+    with pytest.raises(sma.SMAError) as e:
+        P(F32, 1, 1, 8, 8, 64, False, kernel=sma.SMA_KERNEL_F32_KSPLIT, nsplit=2)
+    assert e.value.status == UNSUP
+    for bad_kernel in (3, -2, 99):
+        with pytest.raises(sma.SMAError) as e:
+            P(F32, 1, 1, 8, 8, 64, False, kernel=bad_kernel)
+        assert e.value.status == INVAL
+    for bad_split in (-1, 33):
+        with pytest.raises(sma.SMAError) as e:
+            P(F32, 1, 1, 8, 8, 64, False, nsplit=bad_split)
+        assert e.value.status == INVAL
+    with pytest.raises(sma.SMAError) as e:
+        P(F32, 1, 1, 8, 8, 96, False)
+    assert e.value.status == UNSUP
+    lib = sma.library()
+    assert lib.sma_attention_fwd_plan(F32, 1, 1, 8, 8, 64, 0, -1, 0, 256, None) == NULLP
+
+
+def _ex(plan, q=Q, o=O, idt=F32, ws=None, wsb=0):
+    # Error paths only: every one returns before the library touches a device.
+    return sma.library().sma_attention_fwd_ex(q, K, V, o, L, idt, F32, 1, 2, 128, 128, 64, 0.125,
+                                              1, ws, wsb, ctypes.byref(plan) if plan else None,
+                                              None, None, None)
+
+
+def test_ex_rejects_bad_plans_before_launch():
+    assert _ex(sma.Plan(kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=0)) == INVAL
+    assert _ex(sma.Plan(kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=33)) == INVAL
+    assert _ex(sma.Plan(kernel=7, nsplit=1)) == INVAL
+    assert _ex(sma.Plan(kernel=sma.SMA_KERNEL_BF16_QBLOCK, nsplit=1)) == UNSUP
+    assert _ex(sma.Plan(kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=1), idt=BF16) == UNSUP
+    assert _ex(sma.Plan(kernel=sma.SMA_KERNEL_F32_KSPLIT, nsplit=2)) == UNSUP
+    assert _ex(sma.Plan(kernel=sma.SMA_KERNEL_F32_KSPLIT, nsplit=1), q=None) == NULLP
+    assert _ex(None, o=Q) == ALIAS
+
+
+def test_plan_ksplit_offset_limit():
+    # (seq + 32) rows of d floats per head must stay within 2 GiB for the ksplit kernel
+    ok = (1 << 31) // (4 * 128) - 32
+    p = sma.plan(F32, 1, 1, 64, ok, 128, False, kernel=sma.SMA_KERNEL_F32_KSPLIT, num_cus=256)
+    assert p.kernel == sma.SMA_KERNEL_F32_KSPLIT
+    with pytest.raises(sma.SMAError) as e:
+        sma.plan(F32, 1, 1, 64, ok + 1, 128, False, kernel=sma.SMA_KERNEL_F32_KSPLIT, num_cus=256)
+    assert e.value.status == UNSUP
+    with pytest.raises(sma.SMAError) as e:
+        sma.plan(F32, 1, 1, ok + 1, 64, 128, False, kernel=sma.SMA_KERNEL_F32_KSPLIT, num_cus=256)
+    assert e.value.status == UNSUP

@@ -4,6 +4,7 @@ Small and ragged shapes compare every output; the full-size workloads run in
 the benchmark's launch configuration and compare sampled rows, plus
 properties that hold at any size.
 """
+import functools
 import math
 
 import numpy as np
@@ -36,26 +37,80 @@ SHAPES = [  # (B, H, sq, skv): several tiles with ragged tails, cross shapes bot
 ]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_parity_small(shape, causal, d, dtype):
+# Forced plans: every kernel, unsplit and split across workgroups, on the same inputs.
+PLANS = {"auto": None, "qblock": ("qblock", 1), "split3": ("qblock", 3), "ksplit": ("ksplit", 1)}
+
+
+def plan_kwargs(plan, dtype):
+    import scaled_masked_attention_amd as sma
+
+    if PLANS[plan] is None:
+        return {}
+    kind, nsplit = PLANS[plan]
+    if kind == "ksplit":
+        if dtype != "f32":
+            pytest.skip("the in-workgroup key-split kernel is fp32 only")
+        return dict(kernel=sma.SMA_KERNEL_F32_KSPLIT, nsplit=1)
+    kern = sma.SMA_KERNEL_F32_QBLOCK if dtype == "f32" else sma.SMA_KERNEL_BF16_QBLOCK
+    return dict(kernel=kern, nsplit=nsplit)
+
+
+@functools.lru_cache(maxsize=8)
+def _small_case(shape, causal, d, dtype):
     B, H, sq, skv = shape
     sig = 3.0 if dtype == "bf16" else 1.0
     (q, k, v), bits = _case(100 + sq + 7 * skv + d, B, H, sq, skv, d, dtype, sigma_qk=sig)
     scale = 1.0 / math.sqrt(d)
-    o, lse = run_gpu(*to_device((q, k, v), bits, dtype), scale, causal)
     o_ref, lse_ref = oracle.attention_fwd(q, k, v, scale, causal)
-    check_parity(o, lse, o_ref, lse_ref, dtype, f"{shape} causal={causal} d={d} {dtype}")
+    return (q, k, v), bits, scale, o_ref, lse_ref
+
+
+@pytest.mark.parametrize("plan", list(PLANS))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_parity_small(shape, causal, d, dtype, plan):
+    kw = plan_kwargs(plan, dtype)
+    vals, bits, scale, o_ref, lse_ref = _small_case(shape, causal, d, dtype)
+    o, lse = run_gpu(*to_device(vals, bits, dtype), scale, causal, **kw)
+    check_parity(o, lse, o_ref, lse_ref, dtype, f"{shape} causal={causal} d={d} {dtype} {plan}")
 
 
 @pytest.mark.parametrize("name", ["c1", "c2"])
 def test_parity_small_workloads_full(name):
     w, vals, bits = workload_case(name)
     o, lse = run_gpu(*to_device(vals, bits, w.dtype), w.scale, w.causal)
-    o_ref, lse_ref = oracle.attention_fwd(*vals, w.scale, w.causal)
+    o_ref, lse_ref = _workload_oracle(name)
     check_parity(o, lse, o_ref, lse_ref, w.dtype, name)
+
+
+@pytest.mark.parametrize("plan", ["qblock", "split3", "ksplit"])
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_parity_small_workloads_every_kernel(name, plan):
+    w, vals, bits = workload_case(name)
+    kw = plan_kwargs(plan, w.dtype)
+    o, lse = run_gpu(*to_device(vals, bits, w.dtype), w.scale, w.causal, **kw)
+    o_ref, lse_ref = _workload_oracle(name)
+    check_parity(o, lse, o_ref, lse_ref, w.dtype, f"{name} {plan}")
+
+
+@functools.lru_cache(maxsize=2)
+def _workload_oracle(name):
+    w, vals, _ = workload_case(name)
+    return oracle.attention_fwd(*vals, w.scale, w.causal)
+
+
+@pytest.mark.parametrize("name", ["c4n", "c4c"])
+def test_parity_long_keys_ksplit_sampled(name):
+    """The in-workgroup key-split kernel on 4096 keys a row (not its automatic use)."""
+    w, vals, bits = workload_case(name)
+    kw = plan_kwargs("ksplit", w.dtype)
+    o, lse = run_gpu(*to_device(vals, bits, w.dtype), w.scale, w.causal, **kw)
+    rows = sample_rows(w.batch, w.heads, w.seq_q, w.seq_kv, w.causal, n_random=256, seed=8)
+    o_ref, lse_ref = oracle.attention_fwd(*vals, w.scale, w.causal, rows=rows)
+    check_parity(o.reshape(-1, w.head_dim)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, w.dtype,
+                 f"{name} ksplit")
 
 
 @pytest.mark.parametrize("name", ["c3", "c4n", "c4c", "c5"])
@@ -77,8 +132,24 @@ def test_parity_full_size_sampled(name):
 
 
 # ------------------------------------------------------------------ edge cases
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_no_keys_gives_zero_and_neg_inf(dtype):
+# Each edge case runs on every kernel: the fp32 128-row kernel (unsplit), the
+# fp32 in-workgroup key-split kernel, and the bf16 kernel.
+VARIANTS = ["f32-qblock", "f32-ksplit", "bf16"]
+
+
+def variant_kwargs(variant):
+    import scaled_masked_attention_amd as sma
+
+    if variant == "f32-qblock":
+        return "f32", dict(kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=1)
+    if variant == "f32-ksplit":
+        return "f32", dict(kernel=sma.SMA_KERNEL_F32_KSPLIT, nsplit=1)
+    return "bf16", dict(kernel=sma.SMA_KERNEL_BF16_QBLOCK, nsplit=1)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_no_keys_gives_zero_and_neg_inf(variant):
+    dtype, kw = variant_kwargs(variant)
     import torch
 
     import scaled_masked_attention_amd as sma
@@ -87,71 +158,76 @@ def test_no_keys_gives_zero_and_neg_inf(dtype):
     q = torch.randn(2, 3, 70, 128, device="cuda").to(tdt)
     k = torch.empty(2, 3, 0, 128, device="cuda", dtype=tdt)
     out = torch.full((2, 3, 70, 128), float("nan"), device="cuda")
-    o, lse = sma.attention_fwd(q, k, k, causal=False, return_lse=True, out=out)
+    o, lse = sma.attention_fwd(q, k, k, causal=False, return_lse=True, out=out, **kw)
     torch.cuda.synchronize()
     assert torch.all(o == 0) and not torch.any(torch.signbit(o))
     assert torch.all(torch.isneginf(lse))
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_fully_masked_rows_exact_zero_with_nan_queries(dtype):
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_fully_masked_rows_exact_zero_with_nan_queries(variant):
+    dtype, kw = variant_kwargs(variant)
     sq, skv, d = 300, 100, 128
     (q, k, v), bits = _case(31, 1, 2, sq, skv, d, dtype)
     tq, tk, tv = to_device((q, k, v), bits, dtype)
     tq[:, :, : sq - skv] = float("nan")  # rows with no admitted key: content must not matter
-    o, lse = run_gpu(tq, tk, tv, 0.1, True)
+    o, lse = run_gpu(tq, tk, tv, 0.1, True, **kw)
     assert np.all(o[:, :, : sq - skv] == 0.0) and not np.any(np.signbit(o[:, :, : sq - skv]))
     assert np.all(np.isneginf(lse[:, :, : sq - skv]))
     o_ref, lse_ref = oracle.attention_fwd(q, k, v, 0.1, True)
     check_parity(o, lse, o_ref, lse_ref, dtype, "masked rows")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("causal", [False, True])
-def test_q_zero_is_prefix_mean(dtype, causal):
+def test_q_zero_is_prefix_mean(variant, causal):
+    dtype, kw = variant_kwargs(variant)
     sq, skv, d = 150, 250, 64
     (q, k, v), bits = _case(32, 1, 2, sq, skv, d, dtype)
     q[:] = 0
     if bits is not None:
         bits = (np.zeros_like(bits[0]),) + bits[1:]
-    o, lse = run_gpu(*to_device((q, k, v), bits, dtype), 0.3, causal)
+    o, lse = run_gpu(*to_device((q, k, v), bits, dtype), 0.3, causal, **kw)
     o_ref, lse_ref = oracle.attention_fwd(q, k, v, 0.3, causal)
     check_parity(o, lse, o_ref, lse_ref, dtype, "q=0")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_v_ones_gives_ones(dtype):
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_v_ones_gives_ones(variant):
+    dtype, kw = variant_kwargs(variant)
     sq, skv, d = 260, 333, 128
     (q, k, v), bits = _case(33, 2, 2, sq, skv, d, dtype, sigma_qk=3.0)
     v[:] = 1.0
     if bits is not None:
         bits = bits[:2] + (gen.f32_to_bf16_bits(v),)
-    o, _ = run_gpu(*to_device((q, k, v), bits, dtype), 1.0 / math.sqrt(d), True)
+    o, _ = run_gpu(*to_device((q, k, v), bits, dtype), 1.0 / math.sqrt(d), True, **kw)
     er = empty_rows(sq, skv, True)
     tol = 2e-5 if dtype == "f32" else 2 ** -8
     assert np.all(np.abs(o[:, :, ~er] - 1.0) <= tol)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_one_hot_v_extracts_probabilities(dtype):
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_one_hot_v_extracts_probabilities(variant):
     """With V = I (Skv = d keys), O[i, c] = P[i, c]: the GPU's implicit P is read out."""
+    dtype, kw = variant_kwargs(variant)
     sq, d = 96, 64
     (q, k, _), bits = _case(34, 1, 1, sq, d, d, dtype, sigma_qk=2.0)
     v = np.eye(d, dtype=np.float32).reshape(1, 1, d, d)
     if bits is not None:
         bits = bits[:2] + (gen.f32_to_bf16_bits(v),)
-    o, _ = run_gpu(*to_device((q, k, v), bits, dtype), 0.2, True)
+    o, _ = run_gpu(*to_device((q, k, v), bits, dtype), 0.2, True, **kw)
     p = oracle.softmax_probs(q[0, 0], k[0, 0], 0.2, True)
     tol = 2e-5 if dtype == "f32" else 2e-2
     assert np.abs(o[0, 0] - p).max() <= tol
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_key_shift_beyond_fp32_exp_range(dtype):
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_key_shift_beyond_fp32_exp_range(variant):
     """Every score of a row shifted by ~181 (fp32 exp overflows past ~88.7): only a
     max-subtracted softmax stays finite. Inputs are multiples of 1/2 in [-1, 1]
     (exact in bf16 and fp32), so every dot product is exact in fp32 and the
     comparison isolates the softmax from dot-product rounding at |s| ~ 2000."""
+    dtype, kw = variant_kwargs(variant)
     sq, skv, d = 130, 190, 128
     (q, k, v), _ = _case(35, 1, 2, sq, skv, d, "f32")
     q = (np.clip(np.round(q * 2), -2, 2) / 2).astype(np.float32)
@@ -163,41 +239,45 @@ def test_key_shift_beyond_fp32_exp_range(dtype):
         bits = tuple(gen.f32_to_bf16_bits(x) for x in (q, k, v))
         q, k, v = (gen.bf16_bits_to_f32(b) for b in bits)
     scale = 1.0 / math.sqrt(d)
-    o, lse = run_gpu(*to_device((q, k, v), bits, dtype), scale, True)
+    o, lse = run_gpu(*to_device((q, k, v), bits, dtype), scale, True, **kw)
     o_ref, lse_ref = oracle.attention_fwd(q, k, v, scale, True)
     assert lse_ref[np.isfinite(lse_ref)].min() > 150
     check_parity(o, lse, o_ref, lse_ref, dtype, "key shift")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("scale", [-0.09, 0.0, 0.7])
-def test_negative_zero_and_large_scale(dtype, scale):
+def test_negative_zero_and_large_scale(variant, scale):
+    dtype, kw = variant_kwargs(variant)
     (q, k, v), bits = _case(36, 1, 2, 140, 170, 128, dtype)
-    o, lse = run_gpu(*to_device((q, k, v), bits, dtype), scale, True)
+    o, lse = run_gpu(*to_device((q, k, v), bits, dtype), scale, True, **kw)
     o_ref, lse_ref = oracle.attention_fwd(q, k, v, scale, True)
     check_parity(o, lse, o_ref, lse_ref, dtype, f"scale={scale}")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_causal_single_query_equals_unmasked(dtype):
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_causal_single_query_equals_unmasked(variant):
+    dtype, kw = variant_kwargs(variant)
     (q, k, v), bits = _case(37, 2, 2, 1, 700, 128, dtype)
     dev = to_device((q, k, v), bits, dtype)
-    o0, l0 = run_gpu(*dev, 0.1, False)
-    o1, l1 = run_gpu(*dev, 0.1, True)
+    o0, l0 = run_gpu(*dev, 0.1, False, **kw)
+    o1, l1 = run_gpu(*dev, 0.1, True, **kw)
     assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_deterministic_bitwise(dtype):
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_deterministic_bitwise(variant):
+    dtype, kw = variant_kwargs(variant)
     (q, k, v), bits = _case(38, 2, 4, 333, 777, 128, dtype)
     dev = to_device((q, k, v), bits, dtype)
-    o0, l0 = run_gpu(*dev, 0.1, True)
-    o1, l1 = run_gpu(*dev, 0.1, True)
+    o0, l0 = run_gpu(*dev, 0.1, True, **kw)
+    o1, l1 = run_gpu(*dev, 0.1, True, **kw)
     assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_guard_bands_untouched_and_nan_prefill_overwritten(dtype):
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_guard_bands_untouched_and_nan_prefill_overwritten(variant):
+    dtype, kw = variant_kwargs(variant)
     import torch
 
     import scaled_masked_attention_amd as sma
@@ -212,7 +292,8 @@ def test_guard_bands_untouched_and_nan_prefill_overwritten(dtype):
     l_view = big_l[pad: pad + n_l].view(B, H, sq)
     o_view.fill_(float("nan"))
     l_view.fill_(float("nan"))
-    sma.attention_fwd(tq, tk, tv, scale=0.1, causal=True, return_lse=True, out=o_view, lse=l_view)
+    sma.attention_fwd(tq, tk, tv, scale=0.1, causal=True, return_lse=True, out=o_view, lse=l_view,
+                      **kw)
     torch.cuda.synchronize()
     assert torch.all(big_o[:pad] == 12345.0) and torch.all(big_o[pad + n_o:] == 12345.0)
     assert torch.all(big_l[:pad] == 12345.0) and torch.all(big_l[pad + n_l:] == 12345.0)
