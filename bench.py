@@ -1,6 +1,8 @@
 """Attention-forward benchmark on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload c2|c1|c3|c4n|c4c|c5]
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+NAME is a key of gen.WORKLOADS (default: the fp32 4x8-head, 512x512, d=64 shape).
 
 A step is one attention forward (every kernel of the path) over the
 workload's synthetic inputs, already resident in HBM. Prints one JSON line:
@@ -26,7 +28,7 @@ METRIC = "attention fwd TFLOP/s (4·B·H·Sq·Skv·d, causal halved) and % of MF
 # MI355X published dense MFMA peaks (TFLOP/s) and HBM bandwidth (GB/s).
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 HBM_GBPS = 8000.0
-DEFAULT_WORKLOAD = "c2"  # the second configuration of the five
+DEFAULT_WORKLOAD = "f32_b4h8_s512_d64"  # the shape the headline metric is quoted on
 
 
 def metric_flops(w) -> float:
@@ -51,6 +53,10 @@ def min_bytes(w) -> int:
     return bh * ((w.seq_q + 2 * w.seq_kv) * w.head_dim * e + w.seq_q * w.head_dim * 4 + w.seq_q * 4)
 
 
+# Device function of each sma_kernel code (the name rocprofv3 reports).
+KERNEL_FUNCTIONS = {0: "attn_fwd_f32_kernel", 1: "attn_fwd_f32_wsplit_kernel", 2: "attn_fwd_bf16_kernel"}
+
+
 class HipEvents:
     """hipEvent_t handles through the HIP runtime (torch's events only see torch streams)."""
 
@@ -61,6 +67,11 @@ class HipEvents:
                                                  ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def create(self):
         ev = ctypes.c_void_p()
@@ -81,9 +92,13 @@ class HipEvents:
         self.hip.hipEventDestroy(ev)
 
 
-def read_traffic(workload: str, kernel_src_digest: str):
+def traffic_summary_path(kernel_function: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel_function}_{workload}_hbm_traffic.txt")
+
+
+def read_traffic(kernel_function: str, workload: str, kernel_src_digest: str):
     """HBM bytes per launch from the committed counter summary, or None if absent or stale."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    path = traffic_summary_path(kernel_function, workload)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -144,12 +159,18 @@ def cpu_baseline(w, vals, target_s: float):
                       f"{passes} pass(es) in {dt:.1f} s; metric FLOPs scaled by the row fraction"}
 
 
+def gen_workloads():
+    import gen
+
+    return gen.WORKLOADS
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(gen_workloads()))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -157,7 +178,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the attention path is not sharded across GPUs in this build)", file=sys.stderr)
+              "(multi-GPU sharding of the attention path is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -194,33 +215,49 @@ def main():
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
+    plan = sma.plan(in_dt, B, H, sq, skv, d, w.causal)
     ev = HipEvents()
-    nev = args.steps
-    ev_a = [ev.create() for _ in range(nev)]
-    ev_b = [ev.create() for _ in range(nev)]
     call = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(), in_dt,
             sma.SMA_DTYPE_F32, B, H, sq, skv, d, w.scale, w.causal, ws.data_ptr(), ws_n, sptr)
 
     for _ in range(args.warmup):
         sma.attention_fwd_raw(*call)
     torch.cuda.synchronize()
+    # Timed region. A one-kernel step is bracketed by two events around the whole
+    # loop (events around every launch would add their own gaps to each
+    # measured launch); a step with a split-combine kernel records events around
+    # every main-kernel launch instead, so that the main kernel is timed alone.
+    per_launch = plan.nsplit > 1
+    if per_launch:
+        ev_a = [ev.create() for _ in range(args.steps)]
+        ev_b = [ev.create() for _ in range(args.steps)]
+    else:
+        ev_a, ev_b = [ev.create()], [ev.create()]
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        sma.attention_fwd_timed_raw(*call, ev_a[i], ev_b[i])
+    if per_launch:
+        for i in range(args.steps):
+            sma.attention_fwd_timed_raw(*call, ev_a[i], ev_b[i])
+    else:
+        ev.record(ev_a[0], sptr)
+        for i in range(args.steps):
+            sma.attention_fwd_raw(*call)
+        ev.record(ev_b[0], sptr)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kernel_ms = [ev.elapsed_ms(ev_a[i], ev_b[i]) for i in range(args.steps)]
+    if per_launch:
+        k_avg = sum(ev.elapsed_ms(ev_a[i], ev_b[i]) for i in range(args.steps)) / args.steps
+    else:
+        k_avg = ev.elapsed_ms(ev_a[0], ev_b[0]) / args.steps
     for e in ev_a + ev_b:
         ev.destroy(e)
-    k_avg = sum(kernel_ms) / len(kernel_ms)
     assert torch.isfinite(out).all().item(), "non-finite output"
 
     value = metric_flops(w) / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     exact = 4.0 * d * allowed_pairs(w)
     achieved = exact / (k_avg * 1e-3) / 1e12
-    traffic = read_traffic(args.workload, kernel_source_digest())
+    traffic = read_traffic(KERNEL_FUNCTIONS[plan.kernel], w.name, kernel_source_digest())
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -233,8 +270,12 @@ def main():
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": f"attn_fwd_{w.dtype}_kernel<{d},{str(w.causal).lower()}>",
+                     "kernel": f"{KERNEL_FUNCTIONS[plan.kernel]}<{d},{str(w.causal).lower()}>",
                      "kernel_avg_ms": round(k_avg, 5),
+                     "kernel_timing": ("HIP events around each launch" if per_launch else
+                                       "HIP events around the timed loop / steps"),
+                     "plan": {"kernel": sma.KERNEL_NAMES[plan.kernel], "key_splits": plan.nsplit,
+                              "workgroups": plan.workgroups},
                      "flops_per_launch": exact,
                      "min_hbm_bytes_per_launch": min_bytes(w)},
     }

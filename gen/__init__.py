@@ -188,20 +188,21 @@ class Workload:
         return (self.batch, self.heads, self.seq_kv, self.head_dim)
 
 
-def _w(name, dtype, b, h, sq, skv, d, causal, scale, sqk, sv, cfg_no):
-    return Workload(name, dtype, b, h, sq, skv, d, causal, scale, sqk, sv, 20261201 + cfg_no)
+def _w(name, dtype, b, h, sq, skv, d, causal, scale, sqk, sv, seed):
+    return Workload(name, dtype, b, h, sq, skv, d, causal, scale, sqk, sv, seed)
 
 
-# The five workload shapes (config numbers 1..5; the cross-attention shape runs
-# both unmasked and with the bottom-right causal mask, sharing one seed).
-WORKLOADS: Dict[str, Workload] = {
-    "c1": _w("c1_f32_causal_b1h2s128d64", "f32", 1, 2, 128, 128, 64, True, 1.0 / 8.0, 1.0, 1.0, 1),
-    "c2": _w("c2_f32_b4h8s512d64", "f32", 4, 8, 512, 512, 64, False, 1.0 / math.sqrt(64), 1.0, 1.0, 2),
-    "c3": _w("c3_f32_causal_b8h16s2048d128", "f32", 8, 16, 2048, 2048, 128, True, 1.0 / math.sqrt(128), 1.0, 1.0, 3),
-    "c4n": _w("c4n_f32_cross_b2h32q256kv4096d128", "f32", 2, 32, 256, 4096, 128, False, 1.0 / math.sqrt(128), 1.0, 1.0, 4),
-    "c4c": _w("c4c_f32_cross_causal_br_b2h32q256kv4096d128", "f32", 2, 32, 256, 4096, 128, True, 1.0 / math.sqrt(128), 1.0, 1.0, 4),
-    "c5": _w("c5_bf16_causal_b1h32s16384d128", "bf16", 1, 32, 16384, 16384, 128, True, 1.0 / math.sqrt(128), 3.0, 1.0, 5),
-}
+# The benchmark workload shapes, keyed by what they are: input dtype, mask,
+# batch x heads, query/key lengths, head dim. The cross-attention shape runs
+# both unmasked and with the bottom-right causal mask, on the same inputs.
+WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
+    _w("f32_causal_b1h2_s128_d64", "f32", 1, 2, 128, 128, 64, True, 1.0 / 8.0, 1.0, 1.0, 20261202),
+    _w("f32_b4h8_s512_d64", "f32", 4, 8, 512, 512, 64, False, 1.0 / math.sqrt(64), 1.0, 1.0, 20261203),
+    _w("f32_causal_b8h16_s2048_d128", "f32", 8, 16, 2048, 2048, 128, True, 1.0 / math.sqrt(128), 1.0, 1.0, 20261204),
+    _w("f32_cross_b2h32_q256_kv4096_d128", "f32", 2, 32, 256, 4096, 128, False, 1.0 / math.sqrt(128), 1.0, 1.0, 20261205),
+    _w("f32_cross_causal_b2h32_q256_kv4096_d128", "f32", 2, 32, 256, 4096, 128, True, 1.0 / math.sqrt(128), 1.0, 1.0, 20261205),
+    _w("bf16_causal_b1h32_s16384_d128", "bf16", 1, 32, 16384, 16384, 128, True, 1.0 / math.sqrt(128), 3.0, 1.0, 20261206),
+)}
 
 
 def make_inputs(w: Workload):

@@ -51,7 +51,7 @@ def test_native_generator_matches_numpy_definition():
 
 
 def test_workload_inputs_deterministic_and_distinct():
-    w = gen.WORKLOADS["c1"]
+    w = gen.WORKLOADS["f32_causal_b1h2_s128_d64"]
     (q1, k1, v1), _ = gen.make_inputs(w)
     (q2, k2, v2), _ = gen.make_inputs(w)
     assert np.array_equal(q1, q2) and np.array_equal(k1, k2) and np.array_equal(v1, v2)
@@ -61,7 +61,7 @@ def test_workload_inputs_deterministic_and_distinct():
 
 
 def test_bf16_workload_values_are_bf16():
-    w = gen.WORKLOADS["c1"]
+    w = gen.WORKLOADS["f32_causal_b1h2_s128_d64"]
     (q, k, v), bits = gen.random_case(5, (1, 2, 64, 32), (1, 2, 48, 32), sigma_qk=3.0, dtype="bf16")
     for vals, b in zip((q, k, v), bits):
         assert b.dtype == np.uint16

@@ -77,7 +77,7 @@ def test_parity_small(shape, causal, d, dtype, plan):
     check_parity(o, lse, o_ref, lse_ref, dtype, f"{shape} causal={causal} d={d} {dtype} {plan}")
 
 
-@pytest.mark.parametrize("name", ["c1", "c2"])
+@pytest.mark.parametrize("name", ["f32_causal_b1h2_s128_d64", "f32_b4h8_s512_d64"])
 def test_parity_small_workloads_full(name):
     w, vals, bits = workload_case(name)
     o, lse = run_gpu(*to_device(vals, bits, w.dtype), w.scale, w.causal)
@@ -86,7 +86,7 @@ def test_parity_small_workloads_full(name):
 
 
 @pytest.mark.parametrize("plan", ["qblock", "split3", "ksplit"])
-@pytest.mark.parametrize("name", ["c1", "c2"])
+@pytest.mark.parametrize("name", ["f32_causal_b1h2_s128_d64", "f32_b4h8_s512_d64"])
 def test_parity_small_workloads_every_kernel(name, plan):
     w, vals, bits = workload_case(name)
     kw = plan_kwargs(plan, w.dtype)
@@ -101,7 +101,7 @@ def _workload_oracle(name):
     return oracle.attention_fwd(*vals, w.scale, w.causal)
 
 
-@pytest.mark.parametrize("name", ["c4n", "c4c"])
+@pytest.mark.parametrize("name", ["f32_cross_b2h32_q256_kv4096_d128", "f32_cross_causal_b2h32_q256_kv4096_d128"])
 def test_parity_long_keys_ksplit_sampled(name):
     """The in-workgroup key-split kernel on 4096 keys a row (not its automatic use)."""
     w, vals, bits = workload_case(name)
@@ -113,12 +113,12 @@ def test_parity_long_keys_ksplit_sampled(name):
                  f"{name} ksplit")
 
 
-@pytest.mark.parametrize("name", ["c3", "c4n", "c4c", "c5"])
+@pytest.mark.parametrize("name", ["f32_causal_b8h16_s2048_d128", "f32_cross_b2h32_q256_kv4096_d128", "f32_cross_causal_b2h32_q256_kv4096_d128", "bf16_causal_b1h32_s16384_d128"])
 def test_parity_full_size_sampled(name):
     w, vals, bits = workload_case(name)
     o, lse = run_gpu(*to_device(vals, bits, w.dtype), w.scale, w.causal)
     B, H, sq, skv = w.batch, w.heads, w.seq_q, w.seq_kv
-    rows = sample_rows(B, H, sq, skv, w.causal, n_random=192 if name == "c5" else 512, seed=7)
+    rows = sample_rows(B, H, sq, skv, w.causal, n_random=192 if name == "bf16_causal_b1h32_s16384_d128" else 512, seed=7)
     o_ref, lse_ref = oracle.attention_fwd(*vals, w.scale, w.causal, rows=rows)
     o_s = o.reshape(-1, w.head_dim)[rows]
     l_s = lse.reshape(-1)[rows]
