@@ -1,10 +1,12 @@
-"""Attention-forward oracle -- TEST INFRASTRUCTURE ONLY.
+"""Attention-forward and row-softmax oracle -- TEST INFRASTRUCTURE ONLY.
 
-A plain double-precision CPU statement of the attention forward pass
-(attention_oracle.c holds the arithmetic and states the definition it follows:
-the ``attention`` call of the oxicuda ComputeBackend page, max-subtracted
-softmax and log-sum-exp as on the pulsatrix HIPBackend page, and the empty-row
-convention of the TorchLean hard-masked softmax).
+Plain double-precision CPU statements of the attention forward pass
+(attention_oracle.c: the ``attention`` call of the oxicuda ComputeBackend page,
+max-subtracted softmax and log-sum-exp as on the pulsatrix HIPBackend page,
+and the empty-row convention of the TorchLean hard-masked softmax) and of the
+row primitives on a materialised score matrix (rows_oracle.c: pulsatrix
+``softmax_rows`` / ``logsumexp_rows``, the TorchLean hard-masked softmax and
+MicroGPT's fused scale + causal mask + softmax).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package. The attention library never does, and
@@ -19,7 +21,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "attention_oracle.c")
+_SRCS = [os.path.join(_HERE, "attention_oracle.c"), os.path.join(_HERE, "rows_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
@@ -30,7 +32,7 @@ def build(force: bool = True, out: str | None = None, defines=()) -> str:
     if force or not os.path.exists(out):
         tmp = out + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared"] + ["-D" + d for d in defines]
-        cmd += [_SRC, "-o", tmp, "-lm"]
+        cmd += _SRCS + ["-o", tmp, "-lm"]
         subprocess.check_call(cmd)
         os.replace(tmp, out)
     return out
@@ -44,6 +46,13 @@ def _bind(lib):
     lib.oracle_attention_fwd.restype = ctypes.c_int
     lib.oracle_attention_probs.argtypes = [dp, dp, L, L, L, ctypes.c_double, ctypes.c_int, dp]
     lib.oracle_attention_probs.restype = ctypes.c_int
+    for name in ("oracle_softmax_rows", "oracle_logsumexp_rows"):
+        getattr(lib, name).argtypes = [dp, L, L, dp]
+        getattr(lib, name).restype = ctypes.c_int
+    lib.oracle_masked_softmax_rows.argtypes = [dp, dp, L, L, dp]
+    lib.oracle_masked_softmax_rows.restype = ctypes.c_int
+    lib.oracle_scaled_causal_softmax.argtypes = [dp, L, L, L, ctypes.c_double, ctypes.c_int, dp]
+    lib.oracle_scaled_causal_softmax.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -105,6 +114,60 @@ def softmax_probs(q_bh, k_bh, scale: float, causal: bool, lib=None):
     if rc != 0:
         raise ValueError("oracle_attention_probs rejected its arguments")
     return p
+
+
+def _rows2d(x):
+    x = _f32(x)
+    if x.ndim != 2:
+        raise ValueError("expected a (rows, cols) matrix")
+    return x
+
+
+def softmax_rows(x, lib=None):
+    """Row softmax of a (rows, cols) matrix, float64."""
+    lib = lib or load()
+    x = _rows2d(x)
+    out = np.empty(x.shape, dtype=np.float64)
+    if lib.oracle_softmax_rows(x.ctypes.data, x.shape[0], x.shape[1], out.ctypes.data) != 0:
+        raise ValueError("oracle_softmax_rows rejected its arguments")
+    return out
+
+
+def logsumexp_rows(x, lib=None):
+    """Per-row natural-log log-sum-exp of a (rows, cols) matrix, float64 [rows]."""
+    lib = lib or load()
+    x = _rows2d(x)
+    out = np.empty((x.shape[0],), dtype=np.float64)
+    if lib.oracle_logsumexp_rows(x.ctypes.data, x.shape[0], x.shape[1], out.ctypes.data) != 0:
+        raise ValueError("oracle_logsumexp_rows rejected its arguments")
+    return out
+
+
+def masked_softmax_rows(x, mask, lib=None):
+    """Hard-masked row softmax: entries with mask != 0 are admitted."""
+    lib = lib or load()
+    x, mask = _rows2d(x), _rows2d(mask)
+    if mask.shape != x.shape:
+        raise ValueError("mask shape differs")
+    out = np.empty(x.shape, dtype=np.float64)
+    if lib.oracle_masked_softmax_rows(x.ctypes.data, mask.ctypes.data, x.shape[0], x.shape[1],
+                                      out.ctypes.data) != 0:
+        raise ValueError("oracle_masked_softmax_rows rejected its arguments")
+    return out
+
+
+def scaled_causal_softmax(x, scale: float, causal: bool, lib=None):
+    """softmax(scale * x) per row of each (rows, cols) matrix of x [batch, rows, cols], with the
+    bottom-right causal mask when causal."""
+    lib = lib or load()
+    x = _f32(x)
+    if x.ndim != 3:
+        raise ValueError("expected a (batch, rows, cols) array")
+    out = np.empty(x.shape, dtype=np.float64)
+    if lib.oracle_scaled_causal_softmax(x.ctypes.data, x.shape[0], x.shape[1], x.shape[2],
+                                        float(scale), int(bool(causal)), out.ctypes.data) != 0:
+        raise ValueError("oracle_scaled_causal_softmax rejected its arguments")
+    return out
 
 
 def num_threads(lib=None) -> int:
