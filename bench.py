@@ -21,6 +21,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -114,14 +116,22 @@ def read_traffic(kernel_function: str, workload: str, kernel_src_digest: str):
         return None
 
 
-def kernel_source_digest() -> str:
+# Source file of each kernel (with the shared device header, what its traffic depends on).
+KERNEL_SOURCES = {"attn_fwd_f32_kernel": ["attn_fwd_f32.hip", "attn_common.h"],
+                  "attn_fwd_f32_wsplit_kernel": ["attn_fwd_f32_wsplit.hip", "attn_common.h"],
+                  "attn_fwd_bf16_kernel": ["attn_fwd_bf16.hip", "attn_common.h"],
+                  "row_softmax": ["row_softmax.hip"]}
+
+
+def kernel_source_digest(kernel_function: str) -> str:
+    """SHA-256 of the device sources of one kernel: a committed traffic figure is used only
+    while these are unchanged."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "scaled_masked_attention_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in KERNEL_SOURCES[kernel_function]:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
 
 
@@ -162,7 +172,120 @@ def cpu_baseline(w, vals, target_s: float):
 def gen_workloads():
     import gen
 
-    return gen.WORKLOADS
+    return list(gen.WORKLOADS) + list(gen.ROW_WORKLOADS)
+
+
+ROW_METRIC = "row-primitive GB/s (algorithmic bytes: inputs read once, outputs written once)"
+
+
+def row_algorithmic_bytes(w) -> int:
+    n = w.batch * w.rows * w.cols
+    if w.op == "logsumexp_rows":
+        return 4 * n + 4 * w.batch * w.rows
+    if w.op == "masked_softmax_rows":
+        return 12 * n
+    return 8 * n
+
+
+def row_oracle(w, x, mask, sample):
+    """The oracle on a sample: row ids, or matrix ids for the scaled op (whole matrices)."""
+    import oracle
+
+    if w.op == "scaled_causal_softmax":
+        return oracle.scaled_causal_softmax(x[sample], w.scale, w.causal)
+    if w.op == "softmax_rows":
+        return oracle.softmax_rows(x[sample])
+    if w.op == "logsumexp_rows":
+        return oracle.logsumexp_rows(x[sample])
+    return oracle.masked_softmax_rows(x[sample], mask[sample])
+
+
+def row_cpu_baseline(w, x, mask, target_s: float):
+    """The oracle on a bounded random sample, scaled to GB/s of the same algorithmic bytes."""
+    import oracle
+
+    scaled = w.op == "scaled_causal_softmax"
+    total = w.batch if scaled else w.batch * w.rows
+    rng = np.random.default_rng(0)
+    size = min(total, 1 if scaled else 256)
+    sample = np.sort(rng.choice(total, size=size, replace=False)).astype(np.int64)
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        row_oracle(w, x, mask, sample)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s or passes >= 100000:
+            break
+    frac = sample.size / total
+    unit = "matrices" if scaled else "rows"
+    return {"value": row_algorithmic_bytes(w) * frac * passes / dt / 1e9, "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{sample.size} of {total} {unit} chosen at random (seed 0), {passes} pass(es) "
+                      f"in {dt:.1f} s; algorithmic bytes scaled by the sampled fraction"}
+
+
+def bench_rows(args, w):
+    import torch
+
+    import gen
+    import scaled_masked_attention_amd as sma
+
+    x, mask = gen.make_row_inputs(w)
+    tx = torch.from_numpy(x).to("cuda")
+    tm = torch.from_numpy(mask).to("cuda") if mask is not None else None
+    if w.op == "logsumexp_rows":
+        out = torch.empty(x.shape[0], dtype=torch.float32, device="cuda")
+    else:
+        out = torch.empty_like(tx)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        if w.op == "softmax_rows":
+            sma.softmax_rows(tx, out=out, stream=stream)
+        elif w.op == "logsumexp_rows":
+            sma.logsumexp_rows(tx, out=out, stream=stream)
+        elif w.op == "masked_softmax_rows":
+            sma.masked_softmax_rows(tx, tm, out=out, stream=stream)
+        else:
+            sma.scaled_causal_softmax(tx, w.scale, w.causal, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    e0, e1 = ev.create(), ev.create()
+    t0 = time.perf_counter()
+    ev.record(e0, stream.cuda_stream)
+    for _ in range(args.steps):
+        step()
+    ev.record(e1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    k_avg = ev.elapsed_ms(e0, e1) / args.steps
+    ev.destroy(e0)
+    ev.destroy(e1)
+    nbytes = row_algorithmic_bytes(w)
+    kname = "row_softmax"
+    traffic = read_traffic(kname, w.name, kernel_source_digest(kname))
+    line = {
+        "metric": ROW_METRIC, "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded SplitMix64 + Box-Muller normals; Bernoulli mask)",
+        "config": {"workload": w.name, "op": w.op, "batch": w.batch, "rows": w.rows, "cols": w.cols,
+                   "scale": w.scale, "causal": w.causal, "sigma": w.sigma, "mask_density": w.density},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (k_avg * 1e-3) / 1e9, 1),
+                     "peak": HBM_GBPS, "unit": "GB/s",
+                     "frac": round(nbytes / (k_avg * 1e-3) / 1e9 / HBM_GBPS, 4), "traffic": traffic,
+                     "kernel": kname, "kernel_avg_ms": round(k_avg, 5),
+                     "kernel_timing": "HIP events around the timed loop / steps",
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = row_cpu_baseline(w, x, mask, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
 
 
 def main():
@@ -199,6 +322,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4}))
+        return
+    if args.workload in gen.ROW_WORKLOADS:
+        bench_rows(args, gen.ROW_WORKLOADS[args.workload])
         return
     w = gen.WORKLOADS[args.workload]
     vals, bits = gen.make_inputs(w)
@@ -257,7 +383,8 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     exact = 4.0 * d * allowed_pairs(w)
     achieved = exact / (k_avg * 1e-3) / 1e12
-    traffic = read_traffic(KERNEL_FUNCTIONS[plan.kernel], w.name, kernel_source_digest())
+    traffic = read_traffic(KERNEL_FUNCTIONS[plan.kernel], w.name,
+                           kernel_source_digest(KERNEL_FUNCTIONS[plan.kernel]))
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),

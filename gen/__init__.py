@@ -221,6 +221,48 @@ def make_inputs(w: Workload):
     return vals, bits
 
 
+@dataclasses.dataclass(frozen=True)
+class RowWorkload:
+    """A row-primitive workload: a (batch x rows x cols) fp32 score matrix and its op."""
+
+    name: str
+    op: str          # softmax_rows | logsumexp_rows | masked_softmax_rows | scaled_causal_softmax
+    batch: int
+    rows: int        # rows per matrix
+    cols: int
+    scale: float     # scaled_causal_softmax only
+    causal: bool     # scaled_causal_softmax only
+    sigma: float     # input scores ~ N(0, sigma^2)
+    density: float   # masked_softmax_rows: probability that an entry is admitted
+    seed: int
+
+
+# Score matrices of the attention shapes (one row per query row of every head):
+# the 4x8-head 512x512 shape and the 32-head 16384x16384 causal shape.
+ROW_WORKLOADS: Dict[str, RowWorkload] = {w.name: w for w in (
+    RowWorkload("softmax_rows_r16384_c512", "softmax_rows", 1, 16384, 512, 1.0, False, 4.0, 1.0, 20261211),
+    RowWorkload("logsumexp_rows_r16384_c512", "logsumexp_rows", 1, 16384, 512, 1.0, False, 4.0, 1.0, 20261212),
+    RowWorkload("masked_softmax_rows_r16384_c512", "masked_softmax_rows", 1, 16384, 512, 1.0, False, 4.0, 0.5, 20261213),
+    RowWorkload("scaled_causal_softmax_b32_r512_c512", "scaled_causal_softmax", 32, 512, 512, 0.125, True, 4.0, 1.0, 20261214),
+    RowWorkload("softmax_rows_r32768_c16384", "softmax_rows", 1, 32768, 16384, 1.0, False, 4.0, 1.0, 20261215),
+    RowWorkload("scaled_causal_softmax_b2_r16384_c16384", "scaled_causal_softmax", 2, 16384, 16384,
+                1.0 / math.sqrt(128), True, 4.0, 1.0, 20261216),
+)}
+
+
+def make_row_inputs(w: RowWorkload):
+    """(x, mask) for a row workload: x [batch*rows, cols] float32 (or [batch, rows, cols] for the
+    scaled op); mask float32 of the same shape (1 admitted, 0 blocked) or None."""
+    shape = (w.batch, w.rows, w.cols) if w.op == "scaled_causal_softmax" else (w.batch * w.rows, w.cols)
+    x = tensor_f32(w.seed, "q", shape, w.sigma)
+    mask = None
+    if w.op == "masked_softmax_rows":
+        n = int(np.prod(shape, dtype=np.int64))
+        u = uniform24(w.seed, np.uint64(TENSOR_STREAM["k"] * STREAM_STRIDE) + np.arange(n, dtype=np.uint64))
+        mask = (u < w.density).astype(np.float32).reshape(shape)
+    return x, mask
+
+
 def random_case(seed: int, shape_q, shape_kv, sigma_qk=1.0, sigma_v=1.0, dtype="f32"):
     """Inputs for an ad-hoc (test) shape, from the same streams as ``make_inputs``."""
     q = tensor_f32(seed, "q", tuple(shape_q), sigma_qk)

@@ -172,6 +172,49 @@ int sma_attention_fwd_ex(const void* q, const void* k, const void* v, void* o, f
                          size_t workspace_bytes, const sma_plan* plan, void* stream,
                          void* event_before, void* event_after);
 
+/* ------------------------------------------------------------------ row primitives
+ *
+ * Softmax-family operations on a materialised fp32 score matrix, row-major
+ * [rows][cols] (contiguous, row i at in + i*cols). Per row, over the admitted
+ * entries j:  m = max s_j,  p_j = exp(s_j - m) / sum_k exp(s_k - m),
+ * lse = m + log(sum_k exp(s_k - m)) (natural log), with s_j = x_j, or
+ * scale * x_j for sma_scaled_causal_softmax. Entries not admitted are written
+ * as exactly 0 and their input is never used (it may be NaN). An input of
+ * -infinity at an admitted position weighs zero (also under any scale); a row
+ * whose admitted inputs are all -infinity, or that admits nothing, is all
+ * zeros and its log-sum-exp is -infinity. Admitted inputs of +infinity or NaN
+ * are undefined.
+ *
+ * Pointers are device memory on the current HIP device, 4-byte aligned (16-
+ * byte alignment with cols a multiple of 4 selects vector loads). `out` may be
+ * the same buffer as `in` (in-place) but must not overlap it otherwise, nor
+ * the mask. rows and cols up to 2^31 - 1. Asynchronous on `stream`; nothing
+ * is allocated. rows*cols = 0 launches nothing, except that
+ * sma_logsumexp_rows with cols = 0 writes -infinity for every row.
+ * Errors as for the attention calls (NULL_POINTER, MISALIGNED, ALIASING,
+ * INVALID_VALUE for size overflow or a non-finite scale, UNSUPPORTED past the
+ * size limits, HIP). */
+
+/* Row softmax, max-subtracted (pulsatrix HIPBackend page, `softmax_rows`). */
+int sma_softmax_rows(const float* in, float* out, size_t rows, size_t cols, void* stream);
+
+/* Per-row log-sum-exp, max-subtracted (pulsatrix HIPBackend page,
+ * `logsumexp_rows`): out[i] for i < rows. */
+int sma_logsumexp_rows(const float* in, float* out, size_t rows, size_t cols, void* stream);
+
+/* Hard-masked row softmax (TorchLean "CUDA Buffer Kernels FFI" page, stable
+ * row-wise hard-masked softmax): entry j of row i is admitted iff
+ * mask[i][j] != 0 (mask fp32, same layout as in). */
+int sma_masked_softmax_rows(const float* in, const float* mask, float* out, size_t rows,
+                            size_t cols, void* stream);
+
+/* Scale, causal mask and softmax in one pass (MicroGPT CuBLASBackend page,
+ * `fused_attn_softmax`) over `batch` matrices of [rows][cols]: s = scale * x,
+ * and with causal nonzero row r of each matrix admits j <= r + cols - rows
+ * (bottom-right, as in the attention call). scale must be finite. */
+int sma_scaled_causal_softmax(const float* in, float* out, size_t batch, size_t rows, size_t cols,
+                              double scale, int causal, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* sma_status_string(int status);
 

@@ -76,6 +76,14 @@ def library():
         lib.sma_attention_fwd_ex.argtypes = (lib.sma_attention_fwd.argtypes[:16] +
                                              [ctypes.POINTER(Plan), vp, vp, vp])
         lib.sma_attention_fwd_ex.restype = ctypes.c_int
+        fp = ctypes.c_void_p
+        lib.sma_softmax_rows.argtypes = [fp, fp, sz, sz, vp]
+        lib.sma_logsumexp_rows.argtypes = [fp, fp, sz, sz, vp]
+        lib.sma_masked_softmax_rows.argtypes = [fp, fp, fp, sz, sz, vp]
+        lib.sma_scaled_causal_softmax.argtypes = [fp, fp, sz, sz, sz, ctypes.c_double, ctypes.c_int, vp]
+        for n in ("sma_softmax_rows", "sma_logsumexp_rows", "sma_masked_softmax_rows",
+                  "sma_scaled_causal_softmax"):
+            getattr(lib, n).restype = ctypes.c_int
         lib.sma_status_string.argtypes = [ctypes.c_int]
         lib.sma_status_string.restype = ctypes.c_char_p
         lib.sma_abi_version.argtypes = []
@@ -214,3 +222,74 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
                          SMA_DTYPE_F32, B, H, Sq, Skv, D, scale, causal, ws_ptr, ws_bytes, forced,
                          stream.cuda_stream)
     return (out, lse) if return_lse else out
+
+
+# ------------------------------------------------------------------ row primitives
+def _row_input(x, name, ndim):
+    import torch
+
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor")
+    if x.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D")
+    if x.device != torch.device("cuda", torch.cuda.current_device()):
+        raise ValueError(f"{name} must be on the current HIP device")
+    return x
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+
+def softmax_rows(x, out=None, stream=None):
+    """Row softmax of a contiguous float32 [rows, cols] tensor; out may be x (in place)."""
+    import torch
+
+    x = _row_input(x, "x", 2)
+    out = torch.empty_like(x) if out is None else _row_input(out, "out", 2)
+    if out.shape != x.shape:
+        raise ValueError("out shape differs")
+    s = (stream or torch.cuda.current_stream()).cuda_stream
+    _raise(library().sma_softmax_rows(_ptr(x), _ptr(out), x.shape[0], x.shape[1], s))
+    return out
+
+
+def logsumexp_rows(x, out=None, stream=None):
+    """Per-row natural-log log-sum-exp of a contiguous float32 [rows, cols] tensor -> [rows]."""
+    import torch
+
+    x = _row_input(x, "x", 2)
+    out = torch.empty(x.shape[0], dtype=torch.float32, device=x.device) if out is None else out
+    if out.shape != (x.shape[0],):
+        raise ValueError("out must be [rows]")
+    s = (stream or torch.cuda.current_stream()).cuda_stream
+    _raise(library().sma_logsumexp_rows(_ptr(x), _ptr(out), x.shape[0], x.shape[1], s))
+    return out
+
+
+def masked_softmax_rows(x, mask, out=None, stream=None):
+    """Hard-masked row softmax: mask (float32, same shape) nonzero admits an entry."""
+    import torch
+
+    x, mask = _row_input(x, "x", 2), _row_input(mask, "mask", 2)
+    if mask.shape != x.shape:
+        raise ValueError("mask shape differs")
+    out = torch.empty_like(x) if out is None else _row_input(out, "out", 2)
+    s = (stream or torch.cuda.current_stream()).cuda_stream
+    _raise(library().sma_masked_softmax_rows(_ptr(x), _ptr(mask), _ptr(out), x.shape[0], x.shape[1], s))
+    return out
+
+
+def scaled_causal_softmax(x, scale, causal=True, out=None, stream=None):
+    """softmax(scale * x) per row of each matrix of a float32 [batch, rows, cols] tensor, with the
+    bottom-right causal mask when causal."""
+    import torch
+
+    x = _row_input(x, "x", 3)
+    out = torch.empty_like(x) if out is None else _row_input(out, "out", 3)
+    if out.shape != x.shape:
+        raise ValueError("out shape differs")
+    s = (stream or torch.cuda.current_stream()).cuda_stream
+    _raise(library().sma_scaled_causal_softmax(_ptr(x), _ptr(out), x.shape[0], x.shape[1], x.shape[2],
+                                               float(scale), int(bool(causal)), s))
+    return out

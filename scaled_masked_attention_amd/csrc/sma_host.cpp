@@ -385,6 +385,90 @@ int sma_attention_fwd(const void* q, const void* k, const void* v, void* o, floa
                               nullptr, nullptr);
 }
 
+// ---------------------------------------------------------------- row primitives
+
+}  // extern "C"
+
+namespace {
+
+constexpr size_t kMaxRowCols = (size_t(1) << 31) - 1;  // int32 column math in the kernels
+constexpr size_t kMaxRows = (size_t(1) << 31) - 1;     // one workgroup (or a quarter) per row
+
+// Checks shared by the row primitives. out_elems: floats written (rows*cols,
+// or rows for the log-sum-exp); out may equal in but not overlap it otherwise.
+int check_rows(const float* in, const float* mask, const float* out, bool use_mask, size_t rows,
+               size_t cols, size_t out_elems, size_t* in_bytes) {
+  size_t n, nb, ob;
+  if (!mul(rows, cols, &n) || !mul(n, sizeof(float), &nb) || !mul(out_elems, sizeof(float), &ob))
+    return SMA_ERR_INVALID_VALUE;
+  if (cols > kMaxRowCols || rows > kMaxRows) return SMA_ERR_UNSUPPORTED;
+  if (out_elems > 0 && !out) return SMA_ERR_NULL_POINTER;
+  if (n > 0 && (!in || (use_mask && !mask))) return SMA_ERR_NULL_POINTER;
+  if ((in && !aligned(in, 4)) || (out && !aligned(out, 4)) || (use_mask && mask && !aligned(mask, 4)))
+    return SMA_ERR_MISALIGNED;
+  const bool same = (const void*)in == (const void*)out && ob == nb;
+  if (!same && overlap(in, nb, out, ob)) return SMA_ERR_ALIASING;
+  if (use_mask && overlap(mask, nb, out, ob)) return SMA_ERR_ALIASING;
+  *in_bytes = nb;
+  return SMA_OK;
+}
+
+int launch_row_op(int mode, const float* in, const float* mask, float* out, size_t rows, size_t cols,
+                  size_t rows_per_matrix, int causal, double scale, void* stream) {
+  sma::RowArgs a{};
+  a.in = in;
+  a.mask = mask;
+  a.out = out;
+  a.rows = (int64_t)rows;
+  a.cols = (int32_t)cols;
+  a.rows_per_matrix = (int32_t)(rows_per_matrix > 0 ? rows_per_matrix : 1);
+  a.causal = causal ? 1 : 0;
+  a.c = (float)(scale * 1.44269504088896340736);  // scale * log2(e), one rounding
+  const bool vec4 = cols % 4 == 0 && aligned(in, 16) && aligned(out, 16) &&
+                    (mode != sma::kRowMasked || aligned(mask, 16)) && mode != sma::kRowLse;
+  const bool vec4_lse = cols % 4 == 0 && aligned(in, 16);
+  const sma::RowPlan plan = sma::plan_rows((int64_t)cols, mode == sma::kRowLse ? vec4_lse : vec4);
+  const hipError_t e = sma::launch_rows(mode, a, plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SMA_OK : SMA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sma_softmax_rows(const float* in, float* out, size_t rows, size_t cols, void* stream) {
+  size_t nb;
+  int st = check_rows(in, nullptr, out, false, rows, cols, rows * cols, &nb);
+  if (st != SMA_OK || rows == 0 || cols == 0) return st;
+  return launch_row_op(sma::kRowSoftmax, in, nullptr, out, rows, cols, 0, 0, 1.0, stream);
+}
+
+int sma_logsumexp_rows(const float* in, float* out, size_t rows, size_t cols, void* stream) {
+  size_t nb;
+  int st = check_rows(in, nullptr, out, false, rows, cols, rows, &nb);
+  if (st != SMA_OK || rows == 0) return st;
+  return launch_row_op(sma::kRowLse, in, nullptr, out, rows, cols, 0, 0, 1.0, stream);
+}
+
+int sma_masked_softmax_rows(const float* in, const float* mask, float* out, size_t rows, size_t cols,
+                            void* stream) {
+  size_t nb;
+  int st = check_rows(in, mask, out, true, rows, cols, rows * cols, &nb);
+  if (st != SMA_OK || rows == 0 || cols == 0) return st;
+  return launch_row_op(sma::kRowMasked, in, mask, out, rows, cols, 0, 0, 1.0, stream);
+}
+
+int sma_scaled_causal_softmax(const float* in, float* out, size_t batch, size_t rows, size_t cols,
+                              double scale, int causal, void* stream) {
+  if (!std::isfinite(scale)) return SMA_ERR_INVALID_VALUE;
+  size_t all_rows;
+  if (!mul(batch, rows, &all_rows)) return SMA_ERR_INVALID_VALUE;
+  size_t nb;
+  int st = check_rows(in, nullptr, out, false, all_rows, cols, all_rows * cols, &nb);
+  if (st != SMA_OK || all_rows == 0 || cols == 0) return st;
+  return launch_row_op(sma::kRowScaled, in, nullptr, out, all_rows, cols, rows, causal, scale, stream);
+}
+
 const char* sma_status_string(int status) {
   switch (status) {
     case SMA_OK: return "SMA_OK: success";

@@ -45,6 +45,28 @@ constexpr int kBF16QueriesPerWG = 256;
 constexpr int kBF16KeysPerTile = 64;
 constexpr int kThreadsPerWG = 256;
 
+// Row primitives on a (rows x cols) fp32 matrix.
+enum RowMode { kRowSoftmax = 0, kRowLse = 1, kRowMasked = 2, kRowScaled = 3 };
+struct RowArgs {
+  const float* in;          // [rows][cols]
+  const float* mask;        // [rows][cols], kRowMasked only (nonzero = admitted)
+  float* out;               // [rows][cols], or [rows] for kRowLse; may equal in
+  int64_t rows;
+  int32_t cols;
+  int32_t rows_per_matrix;  // kRowScaled with causal: rows of each matrix (row r = i % this)
+  int32_t causal;           // kRowScaled: bottom-right causal mask
+  float c;                  // scale * log2(e) (log2(e) for the unscaled modes), rounded once
+};
+// How a row is mapped: `team` lanes per row holding per_lane vectors of
+// `vec` floats each in registers, or two streaming passes.
+struct RowPlan {
+  int vec = 1, team = 64, per_lane = 1;
+  bool stream = false;
+};
+constexpr int kRowMaxPerLane = 16;  // vectors per lane of a register-resident row
+RowPlan plan_rows(int64_t cols, bool vec4);
+hipError_t launch_rows(int mode, const RowArgs& a, const RowPlan& p, hipStream_t s);
+
 hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_fwd_f32_wsplit(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);

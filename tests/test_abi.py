@@ -218,3 +218,23 @@ def test_plan_ksplit_offset_limit():
     with pytest.raises(sma.SMAError) as e:
         sma.plan(F32, 1, 1, ok + 1, 64, 128, False, kernel=sma.SMA_KERNEL_F32_KSPLIT, num_cus=256)
     assert e.value.status == UNSUP
+
+
+def test_row_ops_host_checks():
+    """Argument errors of the row primitives return before any HIP call."""
+    lib = sma.library()
+    X, Y, M = 0x10_0000_0000, 0x20_0000_0000, 0x30_0000_0000
+    assert lib.sma_softmax_rows(None, None, 0, 5, None) == OK          # nothing to do
+    assert lib.sma_softmax_rows(None, Y, 3, 5, None) == NULLP
+    assert lib.sma_softmax_rows(X, None, 3, 5, None) == NULLP
+    assert lib.sma_logsumexp_rows(X, None, 3, 0, None) == NULLP         # writes -inf per row
+    assert lib.sma_softmax_rows(X + 2, Y, 3, 5, None) == MISAL
+    assert lib.sma_softmax_rows(X, X + 4, 3, 5, None) == ALIAS          # partial overlap
+    assert lib.sma_logsumexp_rows(X, X + 8, 3, 5, None) == ALIAS
+    assert lib.sma_masked_softmax_rows(X, M, M, 3, 5, None) == ALIAS     # out over the mask
+    assert lib.sma_masked_softmax_rows(X, None, Y, 3, 5, None) == NULLP
+    assert lib.sma_scaled_causal_softmax(X, Y, 2, 3, 5, float("nan"), 1, None) == INVAL
+    assert lib.sma_scaled_causal_softmax(X, Y, 1 << 40, 1 << 40, 5, 1.0, 1, None) == INVAL
+    assert lib.sma_softmax_rows(X, Y, 1 << 40, 1 << 40, None) == INVAL
+    assert lib.sma_softmax_rows(X, Y, 1, 1 << 31, None) == UNSUP
+    assert lib.sma_softmax_rows(X, Y, 1 << 31, 1, None) == UNSUP
