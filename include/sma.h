@@ -76,7 +76,8 @@ typedef enum {
   SMA_KERNEL_F32_QBLOCK = 0,    /* fp32: 128 query rows per workgroup; keys optionally split
                                    across workgroups, merged by a second kernel */
   SMA_KERNEL_F32_KSPLIT = 1,    /* fp32: 32 query rows per workgroup, keys split over its four
-                                   waves and merged in-workgroup; never needs a workspace */
+                                   waves and merged in-workgroup; never needs a workspace (the
+                                   automatic fp32 choice unless its grid is small and rows long) */
   SMA_KERNEL_BF16_QBLOCK = 2    /* bf16: 256 query rows per workgroup; keys optionally split
                                    across workgroups, merged by a second kernel */
 } sma_kernel;

@@ -1,6 +1,6 @@
-// Attention forward, fp32 inputs, for shapes with few query rows per head
-// (too few 128-row blocks to fill the GPU) and short key ranges. Same method
-// and conventions as attn_fwd_f32.hip (oxicuda ComputeBackend `attention`;
+// Attention forward, fp32 inputs: the default fp32 kernel whenever its
+// 32-row grid fills the GPU (or rows are short). Same method and conventions
+// as attn_fwd_f32.hip (oxicuda ComputeBackend `attention`;
 // pulsatrix HIPBackend `softmax_rows`, `logsumexp_rows`; TorchLean hard-masked
 // softmax).
 //
@@ -13,11 +13,10 @@
 // no second launch are needed.
 //
 // Data movement. The Q tile is copied once per workgroup into LDS, and each
-// wave streams its K blocks into a private LDS slot, both with coalesced
+// wave streams its K and V blocks into private LDS slots, all with coalesced
 // direct-to-LDS loads (1 KB of consecutive rows per instruction); the MFMA
-// operands are read back from LDS. Block b+1's K copy is in flight while
-// block b is computed. V operands are read from global memory (L2) straight
-// into registers: each load instruction already covers two whole rows.
+// operands are read back from LDS. Block b+1's K copy is in flight during
+// block b's scores and softmax, its V copy during block b+1's scores.
 //
 // MFMA layouts (v_mfma_f32_32x32x2f32, lane = 32*h + m):
 //   S^T = K Q^T: step (u, e) multiplies head dims 8u + 4h + e of key m (A) and
@@ -53,14 +52,14 @@ struct WGeom {
   static constexpr int kTileBytes = 32 * kRowBytes;  // one 32-row tile of Q or K
   static constexpr int kDmaPerTile = kTileBytes / 1024;
   static constexpr int kOStride = D + 4;             // padded partial-O row in LDS (floats)
-  static constexpr int kStageBytes = kTileBytes * (1 + kWaves);  // Q tile + one K slot per wave
+  static constexpr int kStageBytes = kTileBytes * (1 + 2 * kWaves);  // Q tile + K and V slots per wave
   static constexpr int kOPartBytes = kWaves * kQ * kOStride * 4;
   static constexpr int kLdsBytes = kStageBytes > kOPartBytes ? kStageBytes : kOPartBytes;
   static_assert(kQ == 32, "one 32x32 MFMA tile of queries");
   static_assert(kDmaPerTile % kWaves == 0, "the Q tile copy splits evenly over the waves");
 };
 
-// A 32-row tile (of Q or K) in LDS: row r's 16-byte chunk c is stored at chunk
+// A 32-row tile of Q or K in LDS: row r's 16-byte chunk c is stored at chunk
 // position c ^ (r & 15) of the row. A direct-to-LDS instruction fills 1 KB of
 // consecutive positions, so lane l of copy instruction t fetches the global
 // chunk that belongs at position p = 64t + l.
@@ -84,7 +83,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
   using G = WGeom<D>;
   using VecN = typename FVecW<G::kNch>::T;
-  // Staging (Q tile, K slots) during the key loop; partial O afterwards.
+  // Staging (Q tile, K and V slots) during the key loop; partial O afterwards.
   __shared__ __attribute__((aligned(16))) unsigned char lds[G::kLdsBytes];
   __shared__ float m_part[G::kWaves][G::kQ];
   __shared__ float l_part[G::kWaves][G::kQ];
@@ -96,6 +95,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
   const int lh = lane >> 5;
   unsigned char* const q_tile = lds;
   unsigned char* const k_slot = lds + G::kTileBytes * (1 + wave);
+  unsigned char* const v_slot = lds + G::kTileBytes * (1 + G::kWaves + wave);
 
   // Workgroup -> (batch*head, 32-row query block), XCD-aware order.
   const uint32_t lam = xcd_remap(blockIdx.x, a.nwg);
@@ -118,6 +118,17 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t k_rsrc =
       raw_buffer(static_cast<const float*>(a.k) + (size_t)bh * a.seq_kv * D,
                  (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      raw_buffer(static_cast<const float*>(a.v) + (size_t)bh * a.seq_kv * D,
+                 (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
+  // V rows are copied as they are (row-major, unswizzled): the operand reads
+  // below take 16 or 8 consecutive bytes per lane along a row.
+  auto copy_v_block = [&](int32_t b) {
+    const unsigned row0 = (unsigned)(32 * b) * (unsigned)G::kRowBytes;
+#pragma unroll
+    for (int t = 0; t < G::kDmaPerTile; ++t)
+      dma_load_x4(v_rsrc, row0 + 1024u * t + 16u * lane, lds_address(v_slot + 1024 * t));
+  };
   auto copy_k_block = [&](int32_t b) {
     const unsigned row0 = (unsigned)(32 * b) * (unsigned)G::kRowBytes;
 #pragma unroll
@@ -125,14 +136,17 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
       dma_load_x4(k_rsrc, row0 + tile_src_offset<D>(t, lane), lds_address(k_slot + 1024 * t));
   };
 
-  // Q tile (the waves copy a quarter each) and this wave's first K block.
+  // Q tile (the waves copy a quarter each) and this wave's first K and V blocks.
 #pragma unroll
   for (int i = 0; i < G::kDmaPerTile / G::kWaves; ++i) {
     const int t = i * G::kWaves + wave;
     dma_load_x4(q_rsrc, (unsigned)q0 * (unsigned)G::kRowBytes + tile_src_offset<D>(t, lane),
                 lds_address(q_tile + 1024 * t));
   }
-  if (b_begin < b_end) copy_k_block(b_begin);
+  if (b_begin < b_end) {
+    copy_k_block(b_begin);
+    copy_v_block(b_begin);
+  }
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -149,7 +163,6 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4 * G::kSteps; ++i) qr[i] = -qr[i];
   }
-  const float* vg = static_cast<const float*>(a.v) + (size_t)bh * a.seq_kv * D;
 
   f32x16 oacc[G::kNch];
 #pragma unroll
@@ -160,27 +173,16 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
 
   for (int32_t b = b_begin; b < b_end; ++b) {
     const int32_t j0 = 32 * b;
-    // K block b has landed in this wave's slot (it is the only copy in flight).
-    wait_vmcnt<0>();
+    // K block b has landed (V block b may still be in flight: it was issued
+    // after K, and in-order completion lets the wait leave it outstanding).
+    if (b > b_begin) wait_vmcnt<G::kDmaPerTile>();
     f32x4 kk[G::kSteps];
 #pragma unroll
     for (int u = 0; u < G::kSteps; ++u)
       kk[u] = *reinterpret_cast<const f32x4*>(k_slot + tile_operand_offset<D>(lm, lh, u));
-    // The slot is reused for block b+1 once these reads are done. The copy is
-    // issued before the V loads below, so the compiler's own wait counts for
-    // those stay exact.
     if (b + 1 < b_end) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the K reads have returned
       copy_k_block(b + 1);
-    }
-    // V operands: step r pairs this lane with key 8*(r/4) + 4*h + r%4 (rows
-    // past seq_kv re-read the last key row; such keys are masked and weigh an
-    // exact zero).
-    VecN vv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int32_t j = min(j0 + 8 * (r / 4) + 4 * lh + (r % 4), a.seq_kv - 1);
-      vv[r] = *reinterpret_cast<const VecN*>(vg + (size_t)j * D + G::kNch * lm);
     }
 
     f32x16 s;
@@ -231,11 +233,25 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
       psum += tv[r];
     }
     l_run += psum;
+    // V block b: wait for its copy (only the K copy of block b+1 may remain
+    // in flight), read the operands, then reuse the slot for block b+1.
+    if (b + 1 < b_end) wait_vmcnt<G::kDmaPerTile>();
+    else wait_vmcnt<0>();
+    VecN vv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r / 4) + 4 * lh + (r % 4);
+      vv[r] = *reinterpret_cast<const VecN*>(v_slot + key * G::kRowBytes + 4 * G::kNch * lm);
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r)
 #pragma unroll
       for (int cb = 0; cb < G::kNch; ++cb)
         oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[r][cb], tv[r], oacc[cb], 0, 0, 0);
+    if (b + 1 < b_end) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the V reads have returned
+      copy_v_block(b + 1);
+    }
   }
 
   float l_tot;

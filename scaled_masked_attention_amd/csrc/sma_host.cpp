@@ -112,14 +112,14 @@ size_t auto_splits(const Shape& s, int kernel, size_t base, int num_cus) {
 }
 
 // The fp32 kernel that splits keys over the waves of one 32-row workgroup
-// needs no workspace and no second launch; it wins when the 128-row blocks
-// cannot fill the GPU and each row has few keys (each workgroup reads all of
-// its head's K and V from L2, so long key ranges favour the 128-row kernel
-// with a key split).
-constexpr size_t kKsplitMaxKeys = 2048;
+// needs no workspace and no second launch, and measures faster than the
+// 128-row kernel on every shape whose 32-row grid fills the GPU (short and
+// long key ranges alike). With fewer 32-row blocks than CUs and long rows
+// (decode-like shapes), the 128-row kernel with a key split across
+// workgroups keeps more of the GPU busy.
 constexpr size_t kKsplitAlwaysKeys = 512;
 
-// The in-workgroup key-split kernel addresses one (batch, head)'s Q and K
+// The in-workgroup key-split kernel addresses one (batch, head)'s Q, K and V
 // through 32-bit buffer offsets: keep them, with a tile of slack, below 2^31.
 bool ksplit_fits(const Shape& s) {
   const size_t lim = size_t(1) << 31;
@@ -129,8 +129,6 @@ bool ksplit_fits(const Shape& s) {
 int auto_kernel(const Shape& s, int num_cus) {
   if (s.in_dtype == SMA_DTYPE_BF16) return SMA_KERNEL_BF16_QBLOCK;
   if (!ksplit_fits(s)) return SMA_KERNEL_F32_QBLOCK;
-  const size_t base = s.bh * ((s.seq_q + sma::kF32QueriesPerWG - 1) / sma::kF32QueriesPerWG);
-  if (base >= (size_t)num_cus * 2 || s.seq_kv > kKsplitMaxKeys) return SMA_KERNEL_F32_QBLOCK;
   const size_t nwg32 = s.bh * ((s.seq_q + sma::kF32WsplitQueriesPerWG - 1) / sma::kF32WsplitQueriesPerWG);
   if (nwg32 >= (size_t)num_cus || s.seq_kv <= kKsplitAlwaysKeys) return SMA_KERNEL_F32_KSPLIT;
   return SMA_KERNEL_F32_QBLOCK;

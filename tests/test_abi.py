@@ -105,10 +105,11 @@ def test_aliasing():
 
 
 def test_workspace_planner():
-    c4 = dict(in_dtype=F32, batch=2, heads=32, seq_q=256, seq_kv=4096, head_dim=128)
-    n = sma.workspace_bytes(causal=False, num_cus=256, **c4)
-    rows = 2 * 32 * 256
+    small = dict(in_dtype=F32, batch=1, heads=4, seq_q=200, seq_kv=3000, head_dim=128)
+    n = sma.workspace_bytes(causal=False, num_cus=256, **small)
+    rows = 1 * 4 * 200
     assert n >= 2 * rows * (128 + 1) * 4  # at least two splits of O and LSE
+    assert sma.workspace_bytes(F32, 2, 32, 256, 4096, 128, False, 256) == 0  # in-workgroup split
     assert sma.workspace_bytes(F32, 8, 16, 2048, 2048, 128, True, 256) == 0  # enough query blocks
     assert sma.workspace_bytes(BF16, 1, 32, 16384, 16384, 128, True, 256) == 0
     assert sma.workspace_bytes(F32, 1, 1, 100, 100, 64, True, 256) == 0  # too few keys to split
@@ -135,11 +136,13 @@ def test_plan_auto_choices():
     P = sma.plan
     p = P(F32, 4, 8, 512, 512, 64, False, num_cus=256)  # 128-row blocks cannot fill 256 CUs
     assert (p.kernel, p.nsplit, p.workgroups, p.workspace_bytes) == (sma.SMA_KERNEL_F32_KSPLIT, 1, 512, 0)
-    p = P(F32, 8, 16, 2048, 2048, 128, True, num_cus=256)  # enough 128-row blocks
-    assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_F32_QBLOCK, 1, 8 * 16 * 16)
-    p = P(F32, 2, 32, 256, 4096, 128, False, num_cus=256)  # long keys: split across workgroups
+    p = P(F32, 8, 16, 2048, 2048, 128, True, num_cus=256)  # 32-row blocks fill the GPU
+    assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_F32_KSPLIT, 1, 8 * 16 * 64)
+    p = P(F32, 2, 32, 256, 4096, 128, False, num_cus=256)
+    assert (p.kernel, p.nsplit, p.workgroups, p.workspace_bytes) == (sma.SMA_KERNEL_F32_KSPLIT, 1, 512, 0)
+    p = P(F32, 1, 4, 200, 3000, 128, False, num_cus=256)  # few 32-row blocks, long rows
     assert p.kernel == sma.SMA_KERNEL_F32_QBLOCK and p.nsplit > 1
-    assert p.workspace_bytes == sma.workspace_bytes(F32, 2, 32, 256, 4096, 128, False, 256)
+    assert p.workspace_bytes == sma.workspace_bytes(F32, 1, 4, 200, 3000, 128, False, 256)
     p = P(BF16, 1, 32, 16384, 16384, 128, True, num_cus=256)
     assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_BF16_QBLOCK, 1, 32 * 64)
     p = P(F32, 1, 1, 1, 4096, 64, False, num_cus=256)  # one query row, many keys

@@ -101,16 +101,20 @@ def _workload_oracle(name):
     return oracle.attention_fwd(*vals, w.scale, w.causal)
 
 
-@pytest.mark.parametrize("name", ["f32_cross_b2h32_q256_kv4096_d128", "f32_cross_causal_b2h32_q256_kv4096_d128"])
-def test_parity_long_keys_ksplit_sampled(name):
-    """The in-workgroup key-split kernel on 4096 keys a row (not its automatic use)."""
+@pytest.mark.parametrize("name", ["f32_causal_b8h16_s2048_d128", "f32_cross_b2h32_q256_kv4096_d128",
+                                  "f32_cross_causal_b2h32_q256_kv4096_d128"])
+def test_parity_full_size_qblock_sampled(name):
+    """The 128-row fp32 kernel (with its automatic key split) at full size; the automatic
+    plan runs the in-workgroup key-split kernel on these shapes."""
+    import scaled_masked_attention_amd as sma
+
     w, vals, bits = workload_case(name)
-    kw = plan_kwargs("ksplit", w.dtype)
+    kw = dict(kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=0)
     o, lse = run_gpu(*to_device(vals, bits, w.dtype), w.scale, w.causal, **kw)
     rows = sample_rows(w.batch, w.heads, w.seq_q, w.seq_kv, w.causal, n_random=256, seed=8)
     o_ref, lse_ref = oracle.attention_fwd(*vals, w.scale, w.causal, rows=rows)
     check_parity(o.reshape(-1, w.head_dim)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, w.dtype,
-                 f"{name} ksplit")
+                 f"{name} qblock")
 
 
 @pytest.mark.parametrize("name", ["f32_causal_b8h16_s2048_d128", "f32_cross_b2h32_q256_kv4096_d128", "f32_cross_causal_b2h32_q256_kv4096_d128", "bf16_causal_b1h32_s16384_d128"])
@@ -358,3 +362,38 @@ def test_binding_rejects_bad_arguments():
     assert e.value.status == 5
     with pytest.raises(ValueError):
         sma.attention_fwd(q, q.half(), q)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_hip_graph_replays_match_eager(variant):
+    """The call captured in a HIP graph (through torch), replayed several times with eager work
+    and synchronizations between replays: every replay equals the eager result bitwise."""
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    dtype, kw = variant_kwargs(variant)
+    (q, k, v), bits = _case(44, 2, 3, 300, 450, 64, dtype)
+    tq, tk, tv = to_device((q, k, v), bits, dtype)
+    out = torch.empty((2, 3, 300, 64), dtype=torch.float32, device="cuda")
+    lse = torch.empty((2, 3, 300), dtype=torch.float32, device="cuda")
+    sma.attention_fwd(tq, tk, tv, scale=0.1, causal=True, return_lse=True, out=out, lse=lse, **kw)
+    torch.cuda.synchronize()
+    o_eager, l_eager = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            sma.attention_fwd(tq, tk, tv, scale=0.1, causal=True, return_lse=True, out=out, lse=lse,
+                              stream=torch.cuda.current_stream(), **kw)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_eager) and torch.equal(lse, l_eager), f"replay {rep} differs"
+        _ = (tq.float() * 2).sum().item()  # eager work between replays
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, 0.1, True)
+    check_parity(o_eager.cpu().numpy().astype(np.float64), l_eager.cpu().numpy().astype(np.float64),
+                 o_ref, lse_ref, dtype, "graph")
