@@ -1,4 +1,4 @@
-"""Attention-forward and row-softmax oracle -- TEST INFRASTRUCTURE ONLY.
+"""Attention forward/backward and row-softmax oracle -- TEST INFRASTRUCTURE ONLY.
 
 Plain double-precision CPU statements of the attention forward pass
 (attention_oracle.c: the ``attention`` call of the oxicuda ComputeBackend page,
@@ -6,7 +6,9 @@ max-subtracted softmax and log-sum-exp as on the pulsatrix HIPBackend page,
 and the empty-row convention of the TorchLean hard-masked softmax) and of the
 row primitives on a materialised score matrix (rows_oracle.c: pulsatrix
 ``softmax_rows`` / ``logsumexp_rows``, the TorchLean hard-masked softmax and
-MicroGPT's fused scale + causal mask + softmax).
+MicroGPT's fused scale + causal mask + softmax), and the gradients of the
+attention forward (attention_bwd_oracle.c: the chain rule through the
+softmax, recomputed from q, k, v and the upstream gradient).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package. The attention library never does, and
@@ -21,7 +23,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "attention_oracle.c"), os.path.join(_HERE, "rows_oracle.c")]
+_SRCS = [os.path.join(_HERE, "attention_oracle.c"), os.path.join(_HERE, "rows_oracle.c"),
+         os.path.join(_HERE, "attention_bwd_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
@@ -53,6 +56,9 @@ def _bind(lib):
     lib.oracle_masked_softmax_rows.restype = ctypes.c_int
     lib.oracle_scaled_causal_softmax.argtypes = [dp, L, L, L, ctypes.c_double, ctypes.c_int, dp]
     lib.oracle_scaled_causal_softmax.restype = ctypes.c_int
+    lib.oracle_attention_bwd.argtypes = [dp, dp, dp, dp, L, L, L, L, L, ctypes.c_double, ctypes.c_int,
+                                         dp, dp, dp]
+    lib.oracle_attention_bwd.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -114,6 +120,24 @@ def softmax_probs(q_bh, k_bh, scale: float, causal: bool, lib=None):
     if rc != 0:
         raise ValueError("oracle_attention_probs rejected its arguments")
     return p
+
+
+def attention_bwd(q, k, v, dout, scale: float, causal: bool, lib=None):
+    """dQ, dK, dV (float64) of the attention forward for upstream gradient dout = dL/dO."""
+    lib = lib or load()
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    assert k.shape == (B, H, Skv, D) and v.shape == (B, H, Skv, D) and dout.shape == q.shape
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.empty(k.shape, dtype=np.float64)
+    dv = np.empty(v.shape, dtype=np.float64)
+    rc = lib.oracle_attention_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, B, H,
+                                  Sq, Skv, D, float(scale), int(bool(causal)), dq.ctypes.data,
+                                  dk.ctypes.data, dv.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_attention_bwd rejected its arguments")
+    return dq, dk, dv
 
 
 def _rows2d(x):
