@@ -62,7 +62,7 @@ GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 STREAM_STRIDE = 1 << 40
-TENSOR_STREAM = {"q": 0, "k": 1, "v": 2}
+TENSOR_STREAM = {"q": 0, "k": 1, "v": 2, "dout": 3}
 
 _CHUNK = 1 << 22  # elements per vectorised block; bounds temporaries to ~100 MB
 
@@ -157,7 +157,7 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def tensor_f32(seed: int, which: str, shape: Tuple[int, ...], sigma: float) -> np.ndarray:
-    """A float32 tensor of N(0, sigma^2) draws for stream ``which`` in {"q","k","v"}."""
+    """A float32 tensor of N(0, sigma^2) draws for stream ``which`` in {"q","k","v","dout"}."""
     n = int(np.prod(shape, dtype=np.int64))
     return normal_f32(seed, TENSOR_STREAM[which] * STREAM_STRIDE, n, sigma).reshape(shape)
 
@@ -272,3 +272,8 @@ def random_case(seed: int, shape_q, shape_kv, sigma_qk=1.0, sigma_v=1.0, dtype="
         return (q, k, v), None
     bits = tuple(f32_to_bf16_bits_native(t) for t in (q, k, v))
     return tuple(bf16_bits_to_f32(b) for b in bits), bits
+
+
+def upstream_grad(seed: int, shape, sigma: float = 1.0) -> np.ndarray:
+    """The upstream gradient dL/dO of a backward case: N(0, sigma^2) float32 on its own stream."""
+    return tensor_f32(seed, "dout", tuple(shape), sigma)

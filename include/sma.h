@@ -173,6 +173,60 @@ int sma_attention_fwd_ex(const void* q, const void* k, const void* v, void* o, f
                          size_t workspace_bytes, const sma_plan* plan, void* stream,
                          void* event_before, void* event_after);
 
+/* ------------------------------------------------------------------ backward
+ *
+ * Gradients of the forward above with respect to q, k and v, given the
+ * upstream gradient dout = dL/dO, the forward's output o and its log-sum-exp
+ * lse (the composition of the forward's two products with the softmax
+ * vector-Jacobian product dx = y (dy - sum y dy): pulsatrix HIPBackend page,
+ * `softmax_rows_backward`; MicroGPT page, the fused attention-softmax
+ * backward). Per (batch, head), over the admitted pairs (i, j):
+ *   P_ij = exp(scale q_i.k_j - lse_i),  dP_ij = dout_i . v_j,
+ *   D_i = dout_i . o_i,  dS_ij = P_ij (dP_ij - D_i),
+ *   dv_j = sum_i P_ij dout_i,  dk_j = scale sum_i dS_ij q_i,  dq_i = scale sum_j dS_ij k_j.
+ * P is recomputed from q, k and lse; o enters only through D. Both must be
+ * what sma_attention_fwd returned for these q, k, v, scale and causal (a row
+ * with no admitted key has lse = -inf and gets dq = 0; it adds nothing to dk
+ * and dv). Results are bitwise reproducible: no atomics.
+ *
+ *   q, o, dout, dq   [B,H,Sq,d];  k, v, dk, dv  [B,H,Skv,d];  lse [B,H,Sq].
+ *   in_dtype         SMA_DTYPE_F32 (q, k, v, o, dout); SMA_DTYPE_BF16 -> UNSUPPORTED.
+ *                    lse and the three gradients are fp32.
+ *   head_dim, scale, causal, stream   as for sma_attention_fwd.
+ *   workspace        required device scratch of at least
+ *                    sma_attention_bwd_workspace_bytes bytes (smaller or NULL
+ *                    when that is nonzero -> INVALID_VALUE); contents on entry
+ *                    do not matter; it must not overlap any other argument.
+ *
+ * Pointers are device memory on the current HIP device, 16-byte aligned (lse
+ * 4-byte). q, o, lse, dout and dq may be NULL only when batch*heads*seq_q == 0,
+ * k, v, dk and dv only when batch*heads*seq_kv == 0. The gradients and the
+ * workspace must not overlap the inputs or each other (ALIASING). Every
+ * element of dq, dk and dv is written: seq_kv == 0 gives dq = 0, seq_q == 0
+ * gives dk = dv = 0. Per (batch, head), (seq_q + 32) and (seq_kv + 32) rows of
+ * head_dim floats must stay within 2 GiB (else UNSUPPORTED). Other errors as
+ * for sma_attention_fwd. Asynchronous on `stream`; nothing is allocated. */
+int sma_attention_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                      int in_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
+                      size_t head_dim, double scale, int causal, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sma_attention_bwd needs for this shape (256 per 32-row query
+ * block of every (batch, head), rounded up to 256); 0 for invalid arguments. */
+size_t sma_attention_bwd_workspace_bytes(int in_dtype, size_t batch, size_t heads, size_t seq_q,
+                                         size_t seq_kv, size_t head_dim, int causal);
+
+/* Measurement hook: exactly sma_attention_bwd, and in addition records the
+ * caller's HIP events (either may be NULL) on `stream` after the preprocess
+ * kernel and after the dK/dV kernel; the dQ kernel follows. */
+int sma_attention_bwd_timed(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                            int in_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
+                            size_t head_dim, double scale, int causal, void* workspace,
+                            size_t workspace_bytes, void* stream, void* event_after_pre,
+                            void* event_after_dkdv);
+
 /* ------------------------------------------------------------------ row primitives
  *
  * Softmax-family operations on a materialised fp32 score matrix, row-major

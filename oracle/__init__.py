@@ -59,6 +59,8 @@ def _bind(lib):
     lib.oracle_attention_bwd.argtypes = [dp, dp, dp, dp, L, L, L, L, L, ctypes.c_double, ctypes.c_int,
                                          dp, dp, dp]
     lib.oracle_attention_bwd.restype = ctypes.c_int
+    lib.oracle_attention_bwd_bound.argtypes = lib.oracle_attention_bwd.argtypes
+    lib.oracle_attention_bwd_bound.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -138,6 +140,24 @@ def attention_bwd(q, k, v, dout, scale: float, causal: bool, lib=None):
     if rc != 0:
         raise ValueError("oracle_attention_bwd rejected its arguments")
     return dq, dk, dv
+
+
+def attention_bwd_bound(q, k, v, dout, scale: float, causal: bool, lib=None):
+    """Error scale (mq, mk, mv) of the gradients: their sums with every factor in magnitude."""
+    lib = lib or load()
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    assert k.shape == (B, H, Skv, D) and v.shape == (B, H, Skv, D) and dout.shape == q.shape
+    mq = np.empty(q.shape, dtype=np.float64)
+    mk = np.empty(k.shape, dtype=np.float64)
+    mv = np.empty(v.shape, dtype=np.float64)
+    rc = lib.oracle_attention_bwd_bound(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                        B, H, Sq, Skv, D, float(scale), int(bool(causal)),
+                                        mq.ctypes.data, mk.ctypes.data, mv.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_attention_bwd_bound rejected its arguments")
+    return mq, mk, mv
 
 
 def _rows2d(x):

@@ -84,6 +84,13 @@ def library():
         for n in ("sma_softmax_rows", "sma_logsumexp_rows", "sma_masked_softmax_rows",
                   "sma_scaled_causal_softmax"):
             getattr(lib, n).restype = ctypes.c_int
+        bwd = [vp] * 9 + [ctypes.c_int, sz, sz, sz, sz, sz, ctypes.c_double, ctypes.c_int, vp, sz, vp]
+        lib.sma_attention_bwd.argtypes = bwd
+        lib.sma_attention_bwd.restype = ctypes.c_int
+        lib.sma_attention_bwd_timed.argtypes = bwd + [vp, vp]
+        lib.sma_attention_bwd_timed.restype = ctypes.c_int
+        lib.sma_attention_bwd_workspace_bytes.argtypes = [ctypes.c_int, sz, sz, sz, sz, sz, ctypes.c_int]
+        lib.sma_attention_bwd_workspace_bytes.restype = sz
         lib.sma_status_string.argtypes = [ctypes.c_int]
         lib.sma_status_string.restype = ctypes.c_char_p
         lib.sma_abi_version.argtypes = []
@@ -222,6 +229,71 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
                          SMA_DTYPE_F32, B, H, Sq, Skv, D, scale, causal, ws_ptr, ws_bytes, forced,
                          stream.cuda_stream)
     return (out, lse) if return_lse else out
+
+
+# ------------------------------------------------------------------ backward
+def attention_bwd_workspace_bytes(in_dtype: int, batch: int, heads: int, seq_q: int, seq_kv: int,
+                                  head_dim: int, causal: bool) -> int:
+    return library().sma_attention_bwd_workspace_bytes(in_dtype, batch, heads, seq_q, seq_kv,
+                                                       head_dim, int(bool(causal)))
+
+
+def attention_bwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, dout_ptr, dq_ptr, dk_ptr, dv_ptr,
+                      in_dtype, batch, heads, seq_q, seq_kv, head_dim, scale, causal, ws_ptr,
+                      ws_bytes, stream, event_after_pre=None, event_after_dkdv=None) -> None:
+    """sma_attention_bwd_timed on raw addresses (events may be None); raises SMAError."""
+    _raise(library().sma_attention_bwd_timed(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, dout_ptr, dq_ptr,
+                                             dk_ptr, dv_ptr, in_dtype, batch, heads, seq_q, seq_kv,
+                                             head_dim, float(scale), int(bool(causal)), ws_ptr,
+                                             ws_bytes, stream, event_after_pre, event_after_dkdv))
+
+
+def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=None):
+    """(dQ, dK, dV) of O = softmax(scale * Q K^T + mask) V for the upstream gradient dout.
+
+    q, o, dout [B,H,Sq,D] and k, v [B,H,Skv,D] contiguous float32 tensors on the
+    current HIP device; o and lse ([B,H,Sq] float32) as attention_fwd returned
+    them for the same q, k, v, scale and causal. Returns three float32 tensors
+    shaped like q, k and v. The workspace is allocated when not given.
+    """
+    import torch
+
+    ts = {"q": q, "k": k, "v": v, "o": o, "lse": lse, "dout": dout}
+    for name, t in ts.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [batch, heads, seq, head_dim]")
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if (tuple(k.shape) != (B, H, Skv, D) or tuple(v.shape) != (B, H, Skv, D) or
+            tuple(o.shape) != (B, H, Sq, D) or tuple(dout.shape) != (B, H, Sq, D) or
+            tuple(lse.shape) != (B, H, Sq)):
+        raise ValueError("shape mismatch among q, k, v, o, lse, dout")
+    dev = torch.device("cuda", torch.cuda.current_device())
+    for name, t in ts.items():
+        if t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the current HIP device is {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    need = attention_bwd_workspace_bytes(SMA_DTYPE_F32, B, H, Sq, Skv, D, causal)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    attention_bwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                      _ptr(dv), SMA_DTYPE_F32, B, H, Sq, Skv, D, scale, causal, ws_ptr, ws_bytes,
+                      stream.cuda_stream)
+    return dq, dk, dv
 
 
 # ------------------------------------------------------------------ row primitives

@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsma.so")
-SOURCES = ["sma_host.cpp", "attn_fwd_f32.hip", "attn_fwd_f32_wsplit.hip", "attn_fwd_bf16.hip", "attn_combine.hip", "row_softmax.hip"]
+SOURCES = ["sma_host.cpp", "attn_fwd_f32.hip", "attn_fwd_f32_wsplit.hip", "attn_fwd_bf16.hip",
+           "attn_combine.hip", "row_softmax.hip", "attn_bwd_f32.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

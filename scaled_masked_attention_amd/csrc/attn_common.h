@@ -69,6 +69,15 @@ __device__ __forceinline__ void dma_load_x4(__amdgpu_buffer_rsrc_t rsrc, unsigne
                : "memory");
 }
 
+// The 4-byte form: lane i's dword lands at lds_addr + 4*i (256 bytes per instruction).
+__device__ __forceinline__ void dma_load_x1(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset,
+                                            unsigned lds_addr) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
+
 __device__ __forceinline__ unsigned lds_address(const void* p) {
   return (unsigned)(size_t)(__attribute__((address_space(3))) const void*)p;
 }
@@ -78,6 +87,36 @@ __device__ __forceinline__ unsigned lds_address(const void* p) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, unsigned bytes) {
   constexpr int kRsrcWord3 = 0x00020000;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+// A 32-row fp32 tile (of Q, K, dO or V) in LDS: row r's 16-byte chunk c is stored at chunk
+// position c ^ (r & 15) of the row. A direct-to-LDS instruction fills 1 KB of
+// consecutive positions, so lane l of copy instruction t fetches the global
+// chunk that belongs at position p = 64t + l.
+template <int D>
+__device__ __forceinline__ unsigned tile_src_offset(int t, int lane) {
+  constexpr int kChunks = D / 4;  // 16-byte chunks per row
+  const int p = 64 * t + lane;
+  const int r = p / kChunks;
+  const int c = (p % kChunks) ^ (r & 15);
+  return (unsigned)(r * 4 * D + 16 * c);
+}
+
+// LDS byte offset, within a tile, of the 16 bytes holding head dims
+// 8u + 4h .. 8u + 4h + 3 of row m (the operand of MFMA group u).
+template <int D>
+__device__ __forceinline__ unsigned tile_operand_offset(int m, int h, int u) {
+  return (unsigned)(m * 4 * D + 16 * ((2 * u + h) ^ (m & 15)));
+}
+
+// LDS byte offset, within such a tile, of the D/32 consecutive floats at head
+// dims (D/32)*j .. (D/32)*j + D/32 - 1 of row `row` (j = 0..31: one 32-lane half
+// of a wave reads one whole row).
+template <int D>
+__device__ __forceinline__ unsigned tile_row_offset(int row, int j) {
+  constexpr int kLaneBytes = 4 * (D / 32);
+  const int byte = kLaneBytes * j;
+  return (unsigned)(row * 4 * D + 16 * ((byte >> 4) ^ (row & 15)) + (byte & 15));
 }
 
 }  // namespace sma

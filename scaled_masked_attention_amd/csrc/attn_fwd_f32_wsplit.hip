@@ -59,26 +59,6 @@ struct WGeom {
   static_assert(kDmaPerTile % kWaves == 0, "the Q tile copy splits evenly over the waves");
 };
 
-// A 32-row tile of Q or K in LDS: row r's 16-byte chunk c is stored at chunk
-// position c ^ (r & 15) of the row. A direct-to-LDS instruction fills 1 KB of
-// consecutive positions, so lane l of copy instruction t fetches the global
-// chunk that belongs at position p = 64t + l.
-template <int D>
-__device__ __forceinline__ unsigned tile_src_offset(int t, int lane) {
-  constexpr int kChunks = D / 4;  // 16-byte chunks per row
-  const int p = 64 * t + lane;
-  const int r = p / kChunks;
-  const int c = (p % kChunks) ^ (r & 15);
-  return (unsigned)(r * 4 * D + 16 * c);
-}
-
-// LDS byte offset, within a tile, of the 16 bytes holding head dims
-// 8u + 4h .. 8u + 4h + 3 of row m (the operand of MFMA group u).
-template <int D>
-__device__ __forceinline__ unsigned tile_operand_offset(int m, int h, int u) {
-  return (unsigned)(m * 4 * D + 16 * ((2 * u + h) ^ (m & 15)));
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
   using G = WGeom<D>;

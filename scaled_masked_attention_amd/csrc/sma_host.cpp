@@ -383,6 +383,121 @@ int sma_attention_fwd(const void* q, const void* k, const void* v, void* o, floa
                               nullptr, nullptr);
 }
 
+// ---------------------------------------------------------------- backward
+
+}  // extern "C"
+
+namespace {
+
+struct BwdShape {
+  Shape s;
+  size_t nqb, nkb, ws_bytes;
+};
+
+// Pointer-independent checks of the backward. Fills b on success.
+int check_bwd_shape(int in_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
+                    size_t d, double scale, BwdShape* b) {
+  int st = check_shape(in_dtype, SMA_DTYPE_F32, batch, heads, seq_q, seq_kv, d, scale, &b->s);
+  if (st != SMA_OK) return st;
+  if (in_dtype != SMA_DTYPE_F32) return SMA_ERR_UNSUPPORTED;
+  const size_t blk = sma::kBwdRowsPerBlock;
+  if ((seq_q + blk) * d * 4 > (size_t(1) << 31) || (seq_kv + blk) * d * 4 > (size_t(1) << 31))
+    return SMA_ERR_UNSUPPORTED;
+  b->nqb = (seq_q + blk - 1) / blk;
+  b->nkb = (seq_kv + blk - 1) / blk;
+  size_t blocks;
+  if (!mul(b->s.bh, b->nqb, &blocks) || !mul(blocks, sma::kBwdMetaFloats * sizeof(float), &b->ws_bytes))
+    return SMA_ERR_INVALID_VALUE;
+  b->ws_bytes = round_up(b->ws_bytes, kWsAlign);
+  if (b->s.bh * b->nqb > kMaxWorkgroups || b->s.bh * b->nkb > kMaxWorkgroups) return SMA_ERR_UNSUPPORTED;
+  return SMA_OK;
+}
+
+int check_bwd_pointers(const BwdShape& b, const void* q, const void* k, const void* v,
+                       const void* o, const float* lse, const void* dout, const float* dq,
+                       const float* dk, const float* dv, const void* ws, size_t ws_bytes) {
+  const Shape& s = b.s;
+  const bool has_q = s.rows > 0, has_kv = s.bh * s.seq_kv > 0;
+  if (has_q && (!q || !o || !lse || !dout || !dq)) return SMA_ERR_NULL_POINTER;
+  if (has_kv && (!k || !v || !dk || !dv)) return SMA_ERR_NULL_POINTER;
+  if (b.ws_bytes > 0 && (!ws || ws_bytes < b.ws_bytes)) return SMA_ERR_INVALID_VALUE;
+  const void* t16[] = {q, o, dout, dq, k, v, dk, dv, ws};
+  for (const void* p : t16)
+    if (p && !aligned(p, 16)) return SMA_ERR_MISALIGNED;
+  if (lse && !aligned(lse, 4)) return SMA_ERR_MISALIGNED;
+  const size_t qb = has_q ? s.q_bytes : 0, kvb = has_kv ? s.kv_bytes : 0;
+  const size_t lb = has_q ? s.lse_bytes : 0, wb = b.ws_bytes > 0 ? b.ws_bytes : 0;
+  const void* outs[4] = {dq, dk, dv, ws};
+  const size_t out_n[4] = {qb, kvb, kvb, wb};
+  const void* ins[6] = {q, k, v, o, lse, dout};
+  const size_t in_n[6] = {qb, kvb, kvb, qb, lb, qb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], out_n[i], ins[j], in_n[j])) return SMA_ERR_ALIASING;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], out_n[i], outs[j], out_n[j])) return SMA_ERR_ALIASING;
+  }
+  return SMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sma_attention_bwd_workspace_bytes(int in_dtype, size_t batch, size_t heads, size_t seq_q,
+                                         size_t seq_kv, size_t head_dim, int causal) {
+  (void)causal;
+  BwdShape b;
+  if (check_bwd_shape(in_dtype, batch, heads, seq_q, seq_kv, head_dim, 1.0, &b) != SMA_OK) return 0;
+  return b.ws_bytes;
+}
+
+int sma_attention_bwd_timed(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                            int in_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
+                            size_t head_dim, double scale, int causal, void* workspace,
+                            size_t workspace_bytes, void* stream, void* event_after_pre,
+                            void* event_after_dkdv) {
+  BwdShape b;
+  int st = check_bwd_shape(in_dtype, batch, heads, seq_q, seq_kv, head_dim, scale, &b);
+  if (st != SMA_OK) return st;
+  st = check_bwd_pointers(b, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes);
+  if (st != SMA_OK) return st;
+  if (b.s.rows == 0 && b.s.bh * seq_kv == 0) return SMA_OK;
+  sma::BwdArgs a{};
+  a.q = static_cast<const float*>(q);
+  a.k = static_cast<const float*>(k);
+  a.v = static_cast<const float*>(v);
+  a.o = static_cast<const float*>(o);
+  a.dout = static_cast<const float*>(dout);
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.meta = static_cast<float*>(workspace);
+  a.bh = (int64_t)b.s.bh;
+  a.seq_q = (int32_t)seq_q;
+  a.seq_kv = (int32_t)seq_kv;
+  a.nqb = (int32_t)b.nqb;
+  a.nkb = (int32_t)b.nkb;
+  a.c = (float)(scale * 1.44269504088896340736);  // scale * log2(e), one rounding
+  a.scale = (float)scale;
+  hipError_t e = sma::launch_bwd_f32(a, (int)head_dim, causal != 0, static_cast<hipStream_t>(stream),
+                                     static_cast<hipEvent_t>(event_after_pre),
+                                     static_cast<hipEvent_t>(event_after_dkdv));
+  return e == hipSuccess ? SMA_OK : SMA_ERR_HIP;
+}
+
+int sma_attention_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                      int in_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
+                      size_t head_dim, double scale, int causal, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return sma_attention_bwd_timed(q, k, v, o, lse, dout, dq, dk, dv, in_dtype, batch, heads, seq_q,
+                                 seq_kv, head_dim, scale, causal, workspace, workspace_bytes,
+                                 stream, nullptr, nullptr);
+}
+
 // ---------------------------------------------------------------- row primitives
 
 }  // extern "C"

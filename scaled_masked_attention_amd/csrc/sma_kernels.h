@@ -37,6 +37,28 @@ struct CombineArgs {
   int32_t nsplit;
 };
 
+// Arguments of the attention-backward launches (fp32 inputs and gradients).
+struct BwdArgs {
+  const float* q;     // [bh][seq_q][d]
+  const float* k;     // [bh][seq_kv][d]
+  const float* v;     // [bh][seq_kv][d]
+  const float* o;     // [bh][seq_q][d], the forward's output
+  const float* dout;  // [bh][seq_q][d], upstream gradient dL/dO
+  const float* lse;   // [bh][seq_q], the forward's log-sum-exp (natural log)
+  float* dq;          // [bh][seq_q][d]
+  float* dk;          // [bh][seq_kv][d]
+  float* dv;          // [bh][seq_kv][d]
+  float* meta;        // workspace [bh][nqb][64]: per 32-row query block, lse2 then D
+  int64_t bh;
+  int32_t seq_q;
+  int32_t seq_kv;
+  int32_t nqb;        // 32-row query blocks per (batch, head)
+  int32_t nkb;        // 32-row key blocks per (batch, head)
+  float c;            // scale * log2(e) (signed), rounded once to fp32
+  float scale;        // scale rounded to fp32
+  uint32_t nwg;       // workgroups of the launch (set per launch)
+};
+
 // Workgroup geometry the planner needs (must match the kernels).
 constexpr int kF32QueriesPerWG = 128;
 constexpr int kF32KeysPerTile = 32;
@@ -70,6 +92,10 @@ hipError_t launch_rows(int mode, const RowArgs& a, const RowPlan& p, hipStream_t
 hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_fwd_f32_wsplit(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);
+constexpr int kBwdRowsPerBlock = 32;         // query and key block of the backward kernels
+constexpr int kBwdMetaFloats = 64;          // workspace floats per query block
+hipError_t launch_bwd_f32(const BwdArgs& a, int head_dim, bool causal, hipStream_t s,
+                          hipEvent_t ev_pre, hipEvent_t ev_dkdv);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s);
 
 }  // namespace sma

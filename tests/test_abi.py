@@ -241,3 +241,33 @@ def test_row_ops_host_checks():
     assert lib.sma_softmax_rows(X, Y, 1 << 40, 1 << 40, None) == INVAL
     assert lib.sma_softmax_rows(X, Y, 1, 1 << 31, None) == UNSUP
     assert lib.sma_softmax_rows(X, Y, 1 << 31, 1, None) == UNSUP
+
+
+def test_backward_workspace_and_host_checks():
+    """sma_attention_bwd's argument errors return before any HIP call."""
+    lib = sma.library()
+    assert sma.attention_bwd_workspace_bytes(F32, 2, 3, 100, 50, 64, True) == 2 * 3 * 4 * 256
+    assert sma.attention_bwd_workspace_bytes(F32, 1, 1, 0, 50, 64, False) == 0
+    assert sma.attention_bwd_workspace_bytes(F32, 1, 1, 33, 50, 96, False) == 0   # head_dim
+    assert sma.attention_bwd_workspace_bytes(BF16, 1, 1, 33, 50, 64, False) == 0  # dtype
+    base = [0x10_0000_0000 * i for i in range(1, 11)]
+    q, k, v, o, lse, g, dq, dk, dv, ws = base
+
+    def call(q=q, k=k, v=v, o=o, lse=lse, g=g, dq=dq, dk=dk, dv=dv, idt=F32, B=1, H=2, sq=100,
+             skv=70, d=64, scale=0.125, causal=1, ws=ws, wsb=1 << 20):
+        return lib.sma_attention_bwd(q, k, v, o, lse, g, dq, dk, dv, idt, B, H, sq, skv, d, scale,
+                                     causal, ws, wsb, None)
+
+    assert call(B=0) == OK and call(sq=0, skv=0) == OK                       # nothing to do
+    assert call(q=None, o=None, lse=None, g=None, dq=None, sq=0, skv=0, ws=None, wsb=0) == OK
+    for name in ("q", "o", "lse", "g", "dq", "k", "v", "dk", "dv"):
+        assert call(**{name: None}) == NULLP, name
+    assert call(ws=None) == INVAL and call(wsb=8 * 256 - 1) == INVAL        # 2 heads x 4 blocks
+    assert call(d=0) == INVAL and call(scale=float("inf")) == INVAL
+    assert call(B=1 << 40, H=1 << 40) == INVAL
+    assert call(d=96) == UNSUP and call(idt=BF16) == UNSUP
+    assert call(sq=(1 << 23), d=64) == UNSUP                                 # 32-bit tile offsets
+    assert call(q=q + 8) == MISAL and call(dk=dk + 4) == MISAL and call(lse=lse + 2) == MISAL
+    assert call(ws=ws + 8) == MISAL
+    assert call(dq=q) == ALIAS and call(dv=dk + 16) == ALIAS and call(ws=lse) == ALIAS
+    assert call(dk=o + 64) == ALIAS and call(ws=dq + 256) == ALIAS

@@ -154,3 +154,63 @@ def test_rejects_bad_arguments():
     assert lib.oracle_attention_bwd(f.ctypes.data, f.ctypes.data, f.ctypes.data, f.ctypes.data,
                                     1, 1, 1, 1, 0, 1.0, 0, z.ctypes.data, z.ctypes.data,
                                     z.ctypes.data) == -1
+
+
+# ------------------------------------------------------------------ error scale of the gradients
+@pytest.mark.parametrize("causal,sq,skv", [(False, 13, 29), (True, 29, 13), (True, 20, 20)])
+def test_bound_dominates_every_gradient(causal, sq, skv):
+    """Triangle inequality: |dq| <= mq, |dk| <= mk, |dv| <= mv elementwise."""
+    rng = np.random.default_rng(20 + sq)
+    q, k, v, g = (rng.normal(size=s).astype(np.float32) for s in
+                  ((2, 2, sq, 8), (2, 2, skv, 8), (2, 2, skv, 8), (2, 2, sq, 8)))
+    grads = oracle.attention_bwd(q, k, v, g, -0.4, causal)
+    bounds = oracle.attention_bwd_bound(q, k, v, g, -0.4, causal)
+    for a, m in zip(grads, bounds):
+        assert np.all(np.abs(a) <= m * (1 + 1e-12) + 1e-300)
+        assert np.all(m >= 0)
+
+
+def test_bound_zero_scale_closed_form():
+    """scale = 0: P is uniform over each row's prefix of hi_i keys and a_ij = |lse_i| = log hi_i,
+    so mv_j = sum over rows i admitting j of (1 + log hi_i) |dO_i| / hi_i, and mq = mk = 0."""
+    rng = np.random.default_rng(21)
+    sq, skv = 9, 6
+    q, g = rng.normal(size=(1, 1, sq, 4)).astype(np.float32), rng.normal(size=(1, 1, sq, 4)).astype(np.float32)
+    k, v = rng.normal(size=(1, 1, skv, 4)).astype(np.float32), rng.normal(size=(1, 1, skv, 4)).astype(np.float32)
+    mq, mk, mv = oracle.attention_bwd_bound(q, k, v, g, 0.0, True)
+    ref = np.zeros((skv, 4))
+    for i in range(sq):
+        hi = min(max(i + skv - sq + 1, 0), skv)
+        for j in range(hi):
+            ref[j] += (1.0 + np.log(hi)) * np.abs(g[0, 0, i].astype(np.float64)) / hi
+    assert np.abs(mv[0, 0] - ref).max() <= 1e-14 * ref.max()
+    assert np.all(mq == 0) and np.all(mk == 0)
+
+
+def test_bound_single_key_closed_form():
+    """One key: P = 1, lse_i = s_i = scale q_i.k, a_i = |scale| sum_c |q_ic k_c| + |s_i|, and with
+    b_i = sum_c |dO_ic v_c| (= dPmag_i = Dmag_i / (1 + a_i)):
+    mq_i = |scale| (1 + a_i) b_i (2 + a_i) |k|, mk = |scale| sum_i (1 + a_i) b_i (2 + a_i) |q_i|,
+    mv = sum_i (1 + a_i) |dO_i|."""
+    rng = np.random.default_rng(22)
+    q, g = rng.normal(size=(1, 1, 6, 4)).astype(np.float32), rng.normal(size=(1, 1, 6, 4)).astype(np.float32)
+    k, v = rng.normal(size=(1, 1, 1, 4)).astype(np.float32), rng.normal(size=(1, 1, 1, 4)).astype(np.float32)
+    scale = -0.7
+    mq, mk, mv = oracle.attention_bwd_bound(q, k, v, g, scale, False)
+    q64, g64 = q[0, 0].astype(np.float64), g[0, 0].astype(np.float64)
+    k64, v64 = k[0, 0, 0].astype(np.float64), v[0, 0, 0].astype(np.float64)
+    s = scale * (q64 @ k64)
+    a = abs(scale) * np.abs(q64 * k64[None, :]).sum(axis=1) + np.abs(s)
+    b = np.abs(g64 * v64[None, :]).sum(axis=1)
+    w = (1 + a) * (b + (1 + a) * b)
+    assert np.allclose(mq[0, 0], abs(scale) * w[:, None] * np.abs(k64)[None, :], rtol=1e-13, atol=0)
+    assert np.allclose(mk[0, 0, 0], abs(scale) * (w[:, None] * np.abs(q64)).sum(axis=0), rtol=1e-13, atol=0)
+    assert np.allclose(mv[0, 0, 0], ((1 + a)[:, None] * np.abs(g64)).sum(axis=0), rtol=1e-13, atol=0)
+def test_bound_zero_scale_and_rows_without_keys():
+    rng = np.random.default_rng(23)
+    q, g = rng.normal(size=(1, 1, 9, 4)).astype(np.float32), rng.normal(size=(1, 1, 9, 4)).astype(np.float32)
+    k, v = rng.normal(size=(1, 1, 4, 4)).astype(np.float32), rng.normal(size=(1, 1, 4, 4)).astype(np.float32)
+    mq, mk, mv = oracle.attention_bwd_bound(q, k, v, g, 0.0, False)
+    assert np.all(mq == 0) and np.all(mk == 0) and np.all(mv > 0)
+    mq, mk, _ = oracle.attention_bwd_bound(q, k, v, g, 0.5, True)
+    assert np.all(mq[0, 0, :5] == 0) and np.all(mq[0, 0, 5:] > 0)
