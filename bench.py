@@ -118,6 +118,7 @@ def read_traffic(kernel_function: str, workload: str, kernel_src_digest: str):
 
 # Source file of each kernel (with the shared device header, what its traffic depends on).
 KERNEL_SOURCES = {"attn_fwd_f32_kernel": ["attn_fwd_f32.hip", "attn_common.h"],
+                  "attn_bwd_dkdv_f32_kernel": ["attn_bwd_f32.hip", "attn_common.h"],
                   "attn_fwd_f32_wsplit_kernel": ["attn_fwd_f32_wsplit.hip", "attn_common.h"],
                   "attn_fwd_bf16_kernel": ["attn_fwd_bf16.hip", "attn_common.h"],
                   "row_softmax": ["row_softmax.hip"]}
@@ -169,10 +170,125 @@ def cpu_baseline(w, vals, target_s: float):
                       f"{passes} pass(es) in {dt:.1f} s; metric FLOPs scaled by the row fraction"}
 
 
+BWD_PREFIX = "bwd_"
+
+
 def gen_workloads():
     import gen
 
-    return list(gen.WORKLOADS) + list(gen.ROW_WORKLOADS)
+    bwd = [BWD_PREFIX + n for n, w in gen.WORKLOADS.items() if w.dtype == "f32"]
+    return list(gen.WORKLOADS) + bwd + list(gen.ROW_WORKLOADS)
+
+
+def dkdv_min_bytes(w) -> int:
+    """The dK/dV kernel reads Q, dO, K, V and each row's lse2 and D once and writes dK, dV."""
+    bh = w.batch * w.heads
+    return bh * ((2 * w.seq_q + 4 * w.seq_kv) * w.head_dim * 4 + 8 * w.seq_q)
+
+
+BWD_METRIC = "attention bwd TFLOP/s (10·B·H·Sq·Skv·d, causal halved) and % of MFMA peak"
+
+
+def bwd_cpu_baseline(w, q, k, v, g, target_s: float):
+    """The backward oracle on a bounded random sample of whole (batch, head) slices."""
+    import oracle
+
+    bh = w.batch * w.heads
+    rng = np.random.default_rng(0)
+    order = rng.permutation(bh)
+    qf, kf, vf, gf = (x.reshape(bh, 1, x.shape[2], x.shape[3]) for x in (q, k, v, g))
+
+    def run(ids):
+        ids = np.sort(ids)
+        oracle.attention_bwd(qf[ids], kf[ids], vf[ids], gf[ids], w.scale, w.causal)
+
+    t0 = time.perf_counter()
+    run(order[:1])
+    dt1 = max(time.perf_counter() - t0, 1e-4)
+    # one head per thread runs concurrently: size the sample in whole rounds of the threads,
+    # then repeat whole passes over it until the time target is reached
+    threads = max(1, oracle.num_threads())
+    n = int(min(bh, max(1, threads * max(1, int(target_s / dt1)))))
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        run(order[:n])
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s or passes >= 1000:
+            break
+    flops = 2.5 * metric_flops(w) * n / bh * passes
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, n), "kind": "oracle",
+            "sample": f"{n} of {bh} (batch, head) slices chosen at random (seed 0), every query and "
+                      f"key of each, {passes} pass(es) in {dt:.1f} s; metric FLOPs scaled by the "
+                      f"slice fraction"}
+
+
+def bench_bwd(args, w, name):
+    import torch
+
+    import gen
+    import scaled_masked_attention_amd as sma
+
+    vals, _ = gen.make_inputs(w)
+    g = gen.upstream_grad(w.seed, w.q_shape)
+    tq, tk, tv, tg = (torch.from_numpy(np.ascontiguousarray(x)).to("cuda") for x in (*vals, g))
+    B, H, sq, skv, d = w.batch, w.heads, w.seq_q, w.seq_kv, w.head_dim
+    o, lse = sma.attention_fwd(tq, tk, tv, scale=w.scale, causal=w.causal, return_lse=True)
+    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+    ws_n = sma.attention_bwd_workspace_bytes(sma.SMA_DTYPE_F32, B, H, sq, skv, d, w.causal)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    call = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), lse.data_ptr(), tg.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), sma.SMA_DTYPE_F32, B, H, sq, skv, d, w.scale,
+            w.causal, ws.data_ptr(), ws_n, sptr)
+    for _ in range(args.warmup):
+        sma.attention_bwd_raw(*call)
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    e_pre = [ev.create() for _ in range(args.steps)]
+    e_kv = [ev.create() for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        sma.attention_bwd_raw(*call, e_pre[i], e_kv[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    k_avg = sum(ev.elapsed_ms(e_pre[i], e_kv[i]) for i in range(args.steps)) / args.steps
+    for e in e_pre + e_kv:
+        ev.destroy(e)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all().item(), "non-finite gradient"
+
+    flops = 2.5 * metric_flops(w)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["f32"]
+    pairs = allowed_pairs(w)
+    kernel_flops = 8.0 * d * pairs  # S, dP, dV and dK: four products over the admitted pairs
+    achieved = kernel_flops / (k_avg * 1e-3) / 1e12
+    kname = "attn_bwd_dkdv_f32_kernel"
+    traffic = read_traffic(kname, name, kernel_source_digest(kname))
+    line = {
+        "metric": BWD_METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded SplitMix64 + Box-Muller normals; dO on its own stream)",
+        "config": {"workload": name, "batch": B, "heads": H, "seq_q": sq, "seq_kv": skv,
+                   "head_dim": d, "causal": w.causal, "scale": w.scale, "input_dtype": "f32",
+                   "gradients": "f32", "workspace_bytes": ws_n},
+        "pct_of_mfma_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": f"{kname}<{d},{str(w.causal).lower()}>",
+                     "kernel_avg_ms": round(k_avg, 5),
+                     "kernel_timing": "HIP events recorded by the library around each dK/dV launch",
+                     "flops_per_launch": kernel_flops,
+                     "min_hbm_bytes_per_launch": dkdv_min_bytes(w)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = bwd_cpu_baseline(w, *vals, g, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
 
 
 ROW_METRIC = "row-primitive GB/s (algorithmic bytes: inputs read once, outputs written once)"
@@ -325,6 +441,9 @@ def main():
         return
     if args.workload in gen.ROW_WORKLOADS:
         bench_rows(args, gen.ROW_WORKLOADS[args.workload])
+        return
+    if args.workload.startswith(BWD_PREFIX):
+        bench_bwd(args, gen.WORKLOADS[args.workload[len(BWD_PREFIX):]], args.workload)
         return
     w = gen.WORKLOADS[args.workload]
     vals, bits = gen.make_inputs(w)
