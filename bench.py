@@ -49,10 +49,10 @@ def allowed_pairs(w) -> int:
     return per * w.batch * w.heads
 
 
-def min_bytes(w) -> int:
+def min_bytes(w, o_elem: int = 4) -> int:
     e = 4 if w.dtype == "f32" else 2
     bh = w.batch * w.heads
-    return bh * ((w.seq_q + 2 * w.seq_kv) * w.head_dim * e + w.seq_q * w.head_dim * 4 + w.seq_q * 4)
+    return bh * ((w.seq_q + 2 * w.seq_kv) * w.head_dim * e + w.seq_q * w.head_dim * o_elem + w.seq_q * 4)
 
 
 # Device function of each sma_kernel code (the name rocprofv3 reports).
@@ -410,6 +410,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(gen_workloads()))
+    ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"],
+                    help="element type of the attention output O (bf16: rounded to nearest even)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -454,7 +456,9 @@ def main():
         tq, tk, tv = (torch.from_numpy(b.view(np.int16)).to("cuda").view(torch.bfloat16) for b in bits)
         in_dt = sma.SMA_DTYPE_BF16
     B, H, sq, skv, d = w.batch, w.heads, w.seq_q, w.seq_kv, w.head_dim
-    out = torch.empty((B, H, sq, d), dtype=torch.float32, device="cuda")
+    o16 = args.out_dtype == "bf16"
+    out = torch.empty((B, H, sq, d), dtype=torch.bfloat16 if o16 else torch.float32, device="cuda")
+    o_dt = sma.SMA_DTYPE_BF16 if o16 else sma.SMA_DTYPE_F32
     lse = torch.empty((B, H, sq), dtype=torch.float32, device="cuda")
     ws_n = sma.workspace_bytes(in_dt, B, H, sq, skv, d, w.causal)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
@@ -463,7 +467,7 @@ def main():
     plan = sma.plan(in_dt, B, H, sq, skv, d, w.causal)
     ev = HipEvents()
     call = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(), in_dt,
-            sma.SMA_DTYPE_F32, B, H, sq, skv, d, w.scale, w.causal, ws.data_ptr(), ws_n, sptr)
+            o_dt, B, H, sq, skv, d, w.scale, w.causal, ws.data_ptr(), ws_n, sptr)
 
     for _ in range(args.warmup):
         sma.attention_fwd_raw(*call)
@@ -502,8 +506,9 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     exact = 4.0 * d * allowed_pairs(w)
     achieved = exact / (k_avg * 1e-3) / 1e12
-    traffic = read_traffic(KERNEL_FUNCTIONS[plan.kernel], w.name,
-                           kernel_source_digest(KERNEL_FUNCTIONS[plan.kernel]))
+    # the committed counter passes were taken with fp32 output
+    traffic = None if o16 else read_traffic(KERNEL_FUNCTIONS[plan.kernel], w.name,
+                                            kernel_source_digest(KERNEL_FUNCTIONS[plan.kernel]))
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -511,7 +516,7 @@ def main():
         "data": "synthetic (seeded SplitMix64 + Box-Muller normals)",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_q": sq, "seq_kv": skv,
                    "head_dim": d, "causal": w.causal, "scale": w.scale,
-                   "input_dtype": w.dtype, "accumulate": "f32", "output": "f32", "lse": True,
+                   "input_dtype": w.dtype, "accumulate": "f32", "output": args.out_dtype, "lse": True,
                    "key_splits_workspace_bytes": ws_n},
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
@@ -523,7 +528,7 @@ def main():
                      "plan": {"kernel": sma.KERNEL_NAMES[plan.kernel], "key_splits": plan.nsplit,
                               "workgroups": plan.workgroups},
                      "flops_per_launch": exact,
-                     "min_hbm_bytes_per_launch": min_bytes(w)},
+                     "min_hbm_bytes_per_launch": min_bytes(w, 2 if o16 else 4)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, vals, args.cpu_seconds)

@@ -98,7 +98,8 @@ typedef struct sma_plan {
  *   o          device pointer, element type o_dtype, fully overwritten.
  *   lse        device pointer to batch*heads*seq_q floats, or NULL for no LSE output.
  *   in_dtype   SMA_DTYPE_F32 or SMA_DTYPE_BF16.
- *   o_dtype    SMA_DTYPE_F32 (the only output type implemented; others -> UNSUPPORTED).
+ *   o_dtype    SMA_DTYPE_F32, or SMA_DTYPE_BF16: the fp32 result rounded to bf16 (nearest
+ *              even) as it is stored. Either with either input type. LSE is always fp32.
  *   head_dim   64 or 128 (0 -> INVALID_VALUE, other values -> UNSUPPORTED).
  *   scale      finite multiplier of QK^T (zero and negative values are allowed).
  *   causal     0: no mask; nonzero: bottom-right causal mask.

@@ -167,12 +167,14 @@ def attention_fwd_ex_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dtype,
 
 
 def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=None,
-                  workspace=None, stream=None, kernel=None, nsplit=0):
+                  workspace=None, stream=None, kernel=None, nsplit=0, out_dtype=None):
     """O = softmax(scale * Q K^T + mask) V on the GPU.
 
     q [B,H,Sq,D], k and v [B,H,Skv,D]: contiguous torch tensors on the current
-    HIP device, all float32 or all bfloat16. Returns O (float32, [B,H,Sq,D]) and,
-    with return_lse, the per-row natural-log LSE (float32, [B,H,Sq]).
+    HIP device, all float32 or all bfloat16. Returns O ([B,H,Sq,D], float32, or
+    bfloat16 rounded to nearest even with out_dtype=torch.bfloat16 or an
+    ``out`` of that dtype) and, with return_lse, the per-row natural-log LSE
+    (float32, [B,H,Sq]).
     scale=None means 1/sqrt(D). causal uses the bottom-right alignment.
     kernel (an SMA_KERNEL_* code) and nsplit force a plan; by default the
     library chooses. A forced split gets a workspace of the size it needs.
@@ -203,13 +205,19 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
             raise ValueError(f"{name} must be contiguous")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"unsupported out_dtype {out_dtype}")
+    o_dt = SMA_DTYPE_F32 if out_dtype == torch.float32 else SMA_DTYPE_BF16
     if out is None:
-        out = torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
+        out = torch.empty((B, H, Sq, D), dtype=out_dtype, device=dev)
     if return_lse and lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
-    for name, t in (("out", out), ("lse", lse)):
-        if t is not None and (t.device != dev or t.dtype != torch.float32 or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous float32 tensor on {dev}")
+    if out.device != dev or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {out_dtype} tensor on {dev}")
+    if lse is not None and (lse.device != dev or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 tensor on {dev}")
     if out.shape != (B, H, Sq, D) or (lse is not None and lse.shape != (B, H, Sq)):
         raise ValueError("out/lse shape mismatch")
     forced = None
@@ -226,7 +234,7 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
         stream = torch.cuda.current_stream()
     attention_fwd_ex_raw(q.data_ptr(), k.data_ptr() if Skv else None, v.data_ptr() if Skv else None,
                          out.data_ptr(), lse.data_ptr() if lse is not None else None, in_dt,
-                         SMA_DTYPE_F32, B, H, Sq, Skv, D, scale, causal, ws_ptr, ws_bytes, forced,
+                         o_dt, B, H, Sq, Skv, D, scale, causal, ws_ptr, ws_bytes, forced,
                          stream.cuda_stream)
     return (out, lse) if return_lse else out
 

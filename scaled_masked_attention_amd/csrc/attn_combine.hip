@@ -5,7 +5,7 @@
 //   L = log2 sum_s 2^L_s,   O = sum_s 2^(L_s - L) O_s,
 // with empty splits (L_s = -inf) weighing zero and a row empty in every split
 // written as O = +0.0, LSE = -inf. HBM-bound: it reads nsplit*(d+1) floats per
-// row and writes d+1.
+// row and writes d+1 (the output in fp32 or, rounded to nearest even, bf16).
 #include "attn_common.h"
 
 namespace sma {
@@ -39,7 +39,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
       acc[3] += w * x[3];
     }
   }
-  *reinterpret_cast<f32x4*>(a.o + row * D + 4 * c4) = acc;
+  if (a.o_bf16) {
+    typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2_t*>(a.o_bf16 + row * D + 4 * c4) =
+        u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  } else {
+    *reinterpret_cast<f32x4*>(a.o + row * D + 4 * c4) = acc;
+  }
   if (a.lse && c4 == 0) a.lse[row] = mx == -INFINITY ? -INFINITY : lse2 * 0.69314718055994530942f;
 }
 

@@ -89,6 +89,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, u
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
 }
 
+// Two floats rounded to bf16 (nearest even, the hardware conversion), packed
+// low word first: the storage order of consecutive bf16 elements.
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(unsigned, v);
+}
+
 // A 32-row fp32 tile (of Q, K, dO or V) in LDS: row r's 16-byte chunk c is stored at chunk
 // position c ^ (r & 15) of the row. A direct-to-LDS instruction fills 1 KB of
 // consecutive positions, so lane l of copy instruction t fetches the global

@@ -319,9 +319,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   const float inv = empty ? 0.f : 1.0f / l_tot;
   const float lse2 = empty ? -INFINITY : m_run + __builtin_amdgcn_logf(l_tot);
   const size_t row_id = (size_t)t.bh * a.seq_q + my_row;
-  float* orow;
+  float* orow = nullptr;
+  unsigned short* orow16 = nullptr;
   if (a.nsplit == 1) {
-    orow = a.o + row_id * D;
+    if (a.o_bf16) orow16 = a.o_bf16 + row_id * D;
+    else orow = a.o + row_id * D;
     if (a.lse && lh == 0) a.lse[row_id] = empty ? -INFINITY : lse2 * 0.69314718055994530942f;
   } else {
     const size_t prow = (size_t)t.split * ((size_t)a.bh * a.seq_q) + row_id;
@@ -335,7 +337,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
       f32x4 out;
 #pragma unroll
       for (int e = 0; e < 4; ++e) out[e] = empty ? 0.f : oacc[cb][4 * g4 + e] * inv;
-      *reinterpret_cast<f32x4*>(orow + 32 * cb + 8 * g4 + 4 * lh) = out;
+      if (orow16)
+        *reinterpret_cast<u32x2*>(orow16 + 32 * cb + 8 * g4 + 4 * lh) =
+            u32x2{pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3])};
+      else
+        *reinterpret_cast<f32x4*>(orow + 32 * cb + 8 * g4 + 4 * lh) = out;
     }
 }
 

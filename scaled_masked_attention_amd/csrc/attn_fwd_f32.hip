@@ -222,9 +222,11 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   const float inv = empty ? 0.f : 1.0f / l_tot;
   const float lse2 = empty ? -INFINITY : m_run + __builtin_amdgcn_logf(l_tot);
   const size_t row_id = (size_t)t.bh * a.seq_q + my_row;
-  float* orow;
+  float* orow = nullptr;
+  unsigned short* orow16 = nullptr;
   if (a.nsplit == 1) {
-    orow = a.o + row_id * D;
+    if (a.o_bf16) orow16 = a.o_bf16 + row_id * D;
+    else orow = a.o + row_id * D;
     if (a.lse && lh == 0) a.lse[row_id] = empty ? -INFINITY : lse2 * 0.69314718055994530942f;
   } else {
     const size_t prow = (size_t)t.split * ((size_t)a.bh * a.seq_q) + row_id;
@@ -237,7 +239,19 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
     VecN out;
 #pragma unroll
     for (int cb = 0; cb < G::kNch; ++cb) out[cb] = empty ? 0.f : oacc[cb][r] * inv;
-    *reinterpret_cast<VecN*>(orow + G::kNch * m) = out;
+    if (orow16) {
+      unsigned packed[G::kNch / 2];
+#pragma unroll
+      for (int i = 0; i < G::kNch / 2; ++i) packed[i] = pack_bf16x2(out[2 * i], out[2 * i + 1]);
+      if constexpr (G::kNch == 4) {
+        typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2_t*>(orow16 + G::kNch * m) = u32x2_t{packed[0], packed[1]};
+      } else {
+        *reinterpret_cast<unsigned*>(orow16 + G::kNch * m) = packed[0];
+      }
+    } else {
+      *reinterpret_cast<VecN*>(orow + G::kNch * m) = out;
+    }
   }
 }
 

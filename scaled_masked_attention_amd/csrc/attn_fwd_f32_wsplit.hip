@@ -296,7 +296,13 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) out[e] = empty ? 0.f : acc[e] * inv;
     const size_t row_id = (size_t)bh * a.seq_q + row;
-    *reinterpret_cast<f32x4*>(a.o + row_id * D + 4 * c4) = out;
+    if (a.o_bf16) {
+      typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+      const u32x2_t packed = {pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3])};
+      *reinterpret_cast<u32x2_t*>(a.o_bf16 + row_id * D + 4 * c4) = packed;
+    } else {
+      *reinterpret_cast<f32x4*>(a.o + row_id * D + 4 * c4) = out;
+    }
     if (a.lse && c4 == 0)
       a.lse[row_id] = empty ? -INFINITY : (M + __builtin_amdgcn_logf(L)) * 0.69314718055994530942f;
   }

@@ -59,7 +59,6 @@ int check_shape(int in_dtype, int o_dtype, size_t batch, size_t heads, size_t se
       !mul(s.rows, sizeof(float), &s.lse_bytes))
     return SMA_ERR_INVALID_VALUE;
   if (d != 64 && d != 128) return SMA_ERR_UNSUPPORTED;
-  if (o_dtype != SMA_DTYPE_F32) return SMA_ERR_UNSUPPORTED;
   if (seq_q > kMaxSeq || seq_kv > kMaxSeq || s.bh > (size_t(1) << 31)) return SMA_ERR_UNSUPPORTED;
   // The bf16 kernel addresses one (batch, head)'s K and V through 32-bit
   // buffer offsets: keep them, with a tile of slack, below 2^31 bytes.
@@ -329,8 +328,10 @@ int sma_attention_fwd_ex(const void* q, const void* k, const void* v, void* o, f
   a.c = (float)(std::fabs(scale) * 1.44269504088896340736);  // |scale| * log2(e), one rounding
   a.negate_q = scale < 0.0 ? 1 : 0;
   a.nwg = (uint32_t)p.nwg;
+  const bool o16 = o_dtype == SMA_DTYPE_BF16;
   if (p.nsplit == 1) {
-    a.o = static_cast<float*>(o);
+    if (o16) a.o_bf16 = static_cast<unsigned short*>(o);
+    else a.o = static_cast<float*>(o);
     a.lse = lse;
   } else {
     a.part_o = static_cast<float*>(workspace);
@@ -354,7 +355,8 @@ int sma_attention_fwd_ex(const void* q, const void* k, const void* v, void* o, f
     sma::CombineArgs ca{};
     ca.part_o = a.part_o;
     ca.part_lse = a.part_lse;
-    ca.o = static_cast<float*>(o);
+    if (o16) ca.o_bf16 = static_cast<unsigned short*>(o);
+    else ca.o = static_cast<float*>(o);
     ca.lse = lse;
     ca.rows = (int64_t)sh.rows;
     ca.nsplit = p.nsplit;

@@ -12,7 +12,8 @@ struct FwdArgs {
   const void* q;     // [bh][seq_q][d], f32 or bf16
   const void* k;     // [bh][seq_kv][d]
   const void* v;     // [bh][seq_kv][d]
-  float* o;          // nsplit == 1: final O [bh][seq_q][d] fp32
+  float* o;          // nsplit == 1: final O [bh][seq_q][d] fp32 (when o_bf16 is null)
+  unsigned short* o_bf16;  // nsplit == 1: final O as bf16 (round to nearest even), or null
   float* lse;        // nsplit == 1: final LSE [bh][seq_q] (natural log), may be null
   float* part_o;     // nsplit > 1: per-split normalised O [nsplit][bh][seq_q][d]
   float* part_lse;   // nsplit > 1: per-split LSE in log2 units [nsplit][bh][seq_q]
@@ -31,7 +32,8 @@ struct FwdArgs {
 struct CombineArgs {
   const float* part_o;   // [nsplit][rows][d]
   const float* part_lse; // [nsplit][rows], log2 units
-  float* o;              // [rows][d]
+  float* o;              // [rows][d] fp32 (when o_bf16 is null)
+  unsigned short* o_bf16; // [rows][d] bf16, or null
   float* lse;            // [rows] natural log, may be null
   int64_t rows;          // bh * seq_q
   int32_t nsplit;

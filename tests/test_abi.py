@@ -50,6 +50,7 @@ def _v(q=Q, k=K, v=V, o=O, lse=L, idt=F32, odt=F32, B=1, H=2, sq=128, skv=128, d
 
 def test_valid_calls():
     assert _v() == OK
+    assert _v(odt=BF16) == OK and _v(odt=BF16, idt=BF16, d=128) == OK
     assert _v(idt=BF16, d=128) == OK
     assert _v(lse=None) == OK
     assert _v(scale=-1.0) == OK and _v(scale=0.0) == OK
@@ -76,7 +77,7 @@ def test_invalid_values():
 def test_unsupported():
     assert _v(d=96) == UNSUP
     assert _v(d=256) == UNSUP
-    assert _v(odt=BF16, idt=BF16, d=128) == UNSUP
+    assert _v(odt=BF16, idt=BF16, d=96) == UNSUP
     assert _v(sq=(1 << 30) + 1) == UNSUP
     assert _v(idt=BF16, d=128, skv=(1 << 23) - 256) == OK  # K/V of one head just under 2 GiB
     assert _v(idt=BF16, d=128, skv=1 << 23) == UNSUP
