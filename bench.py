@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (4·B·H·Sq·Skv·d, causal halved) and % of MFMA peak"
 # MI355X published dense MFMA peaks (TFLOP/s) and HBM bandwidth (GB/s).
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f16": 2500.0}
 HBM_GBPS = 8000.0
 DEFAULT_WORKLOAD = "f32_b4h8_s512_d64"  # the shape the headline metric is quoted on
 
@@ -453,8 +453,9 @@ def main():
         tq, tk, tv = (torch.from_numpy(x).to("cuda") for x in vals)
         in_dt = sma.SMA_DTYPE_F32
     else:
-        tq, tk, tv = (torch.from_numpy(b.view(np.int16)).to("cuda").view(torch.bfloat16) for b in bits)
-        in_dt = sma.SMA_DTYPE_BF16
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+        tq, tk, tv = (torch.from_numpy(b.view(np.int16)).to("cuda").view(tdt) for b in bits)
+        in_dt = sma.SMA_DTYPE_BF16 if w.dtype == "bf16" else sma.SMA_DTYPE_F16
     B, H, sq, skv, d = w.batch, w.heads, w.seq_q, w.seq_kv, w.head_dim
     o16 = args.out_dtype == "bf16"
     out = torch.empty((B, H, sq, d), dtype=torch.bfloat16 if o16 else torch.float32, device="cuda")
@@ -521,7 +522,8 @@ def main():
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": f"{KERNEL_FUNCTIONS[plan.kernel]}<{d},{str(w.causal).lower()}>",
+                     "kernel": (f"{KERNEL_FUNCTIONS[plan.kernel]}<{d},{str(w.causal).lower()}"
+                                + (",f16>" if w.dtype == "f16" else ">")),
                      "kernel_avg_ms": round(k_avg, 5),
                      "kernel_timing": ("HIP events around each launch" if per_launch else
                                        "HIP events around the timed loop / steps"),

@@ -156,6 +156,29 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return out
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (nearest, ties to even, numpy's conversion);
+    returns uint16 bit patterns."""
+    with np.errstate(over="ignore"):  # beyond the largest finite value: infinity, as IEEE rounds
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of binary16 bit patterns to float32."""
+    return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def to_16bit(x: np.ndarray, dtype: str):
+    """(exact float32 values, uint16 bit patterns) of x rounded to the 16-bit type dtype."""
+    if dtype == "bf16":
+        b = f32_to_bf16_bits_native(x)
+        return bf16_bits_to_f32(b), b
+    if dtype == "f16":
+        b = f32_to_f16_bits(x)
+        return f16_bits_to_f32(b), b
+    raise ValueError(f"not a 16-bit dtype: {dtype}")
+
+
 def tensor_f32(seed: int, which: str, shape: Tuple[int, ...], sigma: float) -> np.ndarray:
     """A float32 tensor of N(0, sigma^2) draws for stream ``which`` in {"q","k","v","dout"}."""
     n = int(np.prod(shape, dtype=np.int64))
@@ -167,7 +190,7 @@ class Workload:
     """One attention-forward workload: shapes, dtype, mask, scale and input distribution."""
 
     name: str
-    dtype: str  # "f32" or "bf16" (input element type; accumulation and O are fp32)
+    dtype: str  # "f32", "bf16" or "f16" (input element type; accumulation and O are fp32)
     batch: int
     heads: int
     seq_q: int
@@ -202,6 +225,7 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
     _w("f32_cross_b2h32_q256_kv4096_d128", "f32", 2, 32, 256, 4096, 128, False, 1.0 / math.sqrt(128), 1.0, 1.0, 20261205),
     _w("f32_cross_causal_b2h32_q256_kv4096_d128", "f32", 2, 32, 256, 4096, 128, True, 1.0 / math.sqrt(128), 1.0, 1.0, 20261205),
     _w("bf16_causal_b1h32_s16384_d128", "bf16", 1, 32, 16384, 16384, 128, True, 1.0 / math.sqrt(128), 3.0, 1.0, 20261206),
+    _w("f16_causal_b1h32_s16384_d128", "f16", 1, 32, 16384, 16384, 128, True, 1.0 / math.sqrt(128), 3.0, 1.0, 20261207),
 )}
 
 
@@ -209,16 +233,15 @@ def make_inputs(w: Workload):
     """Host inputs for a workload.
 
     Returns (q, k, v) as float32 arrays holding the exact input values, plus,
-    for bf16 workloads, the uint16 bit patterns (qb, kb, vb) the device consumes.
+    for 16-bit workloads, the uint16 bit patterns (qb, kb, vb) the device consumes.
     """
     q = tensor_f32(w.seed, "q", w.q_shape, w.sigma_qk)
     k = tensor_f32(w.seed, "k", w.kv_shape, w.sigma_qk)
     v = tensor_f32(w.seed, "v", w.kv_shape, w.sigma_v)
     if w.dtype == "f32":
         return (q, k, v), None
-    bits = tuple(f32_to_bf16_bits_native(t) for t in (q, k, v))
-    vals = tuple(bf16_bits_to_f32(b) for b in bits)
-    return vals, bits
+    pairs = [to_16bit(t, w.dtype) for t in (q, k, v)]
+    return tuple(p[0] for p in pairs), tuple(p[1] for p in pairs)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -270,8 +293,8 @@ def random_case(seed: int, shape_q, shape_kv, sigma_qk=1.0, sigma_v=1.0, dtype="
     v = tensor_f32(seed, "v", tuple(shape_kv), sigma_v)
     if dtype == "f32":
         return (q, k, v), None
-    bits = tuple(f32_to_bf16_bits_native(t) for t in (q, k, v))
-    return tuple(bf16_bits_to_f32(b) for b in bits), bits
+    pairs = [to_16bit(t, dtype) for t in (q, k, v)]
+    return tuple(p[0] for p in pairs), tuple(p[1] for p in pairs)
 
 
 def upstream_grad(seed: int, shape, sigma: float = 1.0) -> np.ndarray:

@@ -54,7 +54,8 @@ extern "C" {
 /* Element types. Accumulation is always fp32. */
 typedef enum {
   SMA_DTYPE_F32 = 0,  /* IEEE binary32 */
-  SMA_DTYPE_BF16 = 1  /* bfloat16 (binary32 with the low 16 fraction bits dropped) */
+  SMA_DTYPE_BF16 = 1, /* bfloat16 (binary32 with the low 16 fraction bits dropped) */
+  SMA_DTYPE_F16 = 2   /* IEEE binary16 (inputs of the forward only) */
 } sma_dtype;
 
 typedef enum {
@@ -78,7 +79,7 @@ typedef enum {
   SMA_KERNEL_F32_KSPLIT = 1,    /* fp32: 32 query rows per workgroup, keys split over its four
                                    waves and merged in-workgroup; never needs a workspace (the
                                    automatic fp32 choice unless its grid is small and rows long) */
-  SMA_KERNEL_BF16_QBLOCK = 2    /* bf16: 256 query rows per workgroup; keys optionally split
+  SMA_KERNEL_BF16_QBLOCK = 2    /* bf16 or fp16: 256 query rows per workgroup; keys optionally split
                                    across workgroups, merged by a second kernel */
 } sma_kernel;
 
@@ -97,9 +98,11 @@ typedef struct sma_plan {
  *              be NULL only when seq_kv == 0; q and o only when batch*heads*seq_q == 0.
  *   o          device pointer, element type o_dtype, fully overwritten.
  *   lse        device pointer to batch*heads*seq_q floats, or NULL for no LSE output.
- *   in_dtype   SMA_DTYPE_F32 or SMA_DTYPE_BF16.
+ *   in_dtype   SMA_DTYPE_F32, SMA_DTYPE_BF16 or SMA_DTYPE_F16 (16-bit inputs run on 16-bit
+ *              MFMA with fp32 accumulation; P is rounded to the input type for P V).
  *   o_dtype    SMA_DTYPE_F32, or SMA_DTYPE_BF16: the fp32 result rounded to bf16 (nearest
- *              even) as it is stored. Either with either input type. LSE is always fp32.
+ *              even) as it is stored. Either with any input type (SMA_DTYPE_F16 output ->
+ *              UNSUPPORTED). LSE is always fp32.
  *   head_dim   64 or 128 (0 -> INVALID_VALUE, other values -> UNSUPPORTED).
  *   scale      finite multiplier of QK^T (zero and negative values are allowed).
  *   causal     0: no mask; nonzero: bottom-right causal mask.

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(PKG, "libsma.so")
 
 SMA_DTYPE_F32 = 0
 SMA_DTYPE_BF16 = 1
+SMA_DTYPE_F16 = 2
 SMA_OK = 0
 SMA_KERNEL_AUTO = -1
 SMA_KERNEL_F32_QBLOCK = 0
@@ -171,7 +172,7 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
     """O = softmax(scale * Q K^T + mask) V on the GPU.
 
     q [B,H,Sq,D], k and v [B,H,Skv,D]: contiguous torch tensors on the current
-    HIP device, all float32 or all bfloat16. Returns O ([B,H,Sq,D], float32, or
+    HIP device, all float32, all bfloat16 or all float16. Returns O ([B,H,Sq,D], float32, or
     bfloat16 rounded to nearest even with out_dtype=torch.bfloat16 or an
     ``out`` of that dtype) and, with return_lse, the per-row natural-log LSE
     (float32, [B,H,Sq]).
@@ -195,6 +196,8 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
         in_dt = SMA_DTYPE_F32
     elif q.dtype == torch.bfloat16:
         in_dt = SMA_DTYPE_BF16
+    elif q.dtype == torch.float16:
+        in_dt = SMA_DTYPE_F16
     else:
         raise ValueError(f"unsupported dtype {q.dtype}")
     dev = torch.device("cuda", torch.cuda.current_device())

@@ -1,12 +1,13 @@
-// Attention forward, bf16 inputs, bf16 MFMA with fp32 accumulation
-// (v_mfma_f32_32x32x16_bf16), fp32 output, gfx950.
+// Attention forward, 16-bit inputs: bf16 (v_mfma_f32_32x32x16_bf16) or fp16
+// (v_mfma_f32_32x32x16_f16, the F16 template flag), fp32 accumulation, fp32 or
+// bf16 output, gfx950.
 //
 // Same method as the fp32 kernel (oxicuda ComputeBackend `attention`; pulsatrix
 // HIPBackend `softmax_rows`, `logsumexp_rows`; TorchLean hard-masked softmax),
 // with the operand precision of the oxicuda `gemm_mixed_precision` contract:
-// 16-bit operands, fp32 accumulation and result. The probabilities are
-// rounded to bf16 (nearest even) for the P V product; the row sums use the
-// fp32 probabilities.
+// 16-bit operands, fp32 accumulation and result (its MixedPrecision BF16 and
+// F16). The probabilities are rounded to the input's 16-bit type (nearest
+// even) for the P V product; the row sums use the fp32 probabilities.
 //
 // Workgroup: 8 waves x 32 query rows = 256 rows, two waves per SIMD. Key tiles
 // of 64 rows go HBM/L2 -> LDS through buffer-resource direct-to-LDS loads into
@@ -34,6 +35,27 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// The 16-bit element type: operand vectors, the rounding of P, and the MFMA.
+template <bool F16>
+struct Half;
+template <>
+struct Half<false> {
+  typedef __bf16 E;
+  typedef bf16x8 V8;
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Half<true> {
+  typedef _Float16 E;
+  typedef f16x8 V8;
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -81,9 +103,11 @@ __device__ __forceinline__ int v_swz(int r) {
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   using G = BGeom<D>;
+  using H = Half<F16>;
+  using V8 = typename H::V8;
   __shared__ __attribute__((aligned(16))) u32x4 k_lds[G::kSlots][G::kTileChunks];
   __shared__ __attribute__((aligned(16))) u32x4 v_lds[G::kSlots][G::kTileChunks];
 
@@ -110,7 +134,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int32_t lim = key_limit<CAUSAL>(my_row, a.seq_q, a.seq_kv, split_end);
 
   // Q operands in registers for the whole pass.
-  bf16x8 qr[G::kSteps];
+  V8 qr[G::kSteps];
   {
     const unsigned short* qp = static_cast<const unsigned short*>(a.q) +
                                ((size_t)t.bh * a.seq_q + min(my_row, a.seq_q - 1)) * D + lh * G::kHalf;
@@ -119,7 +143,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
     for (int s = 0; s < G::kSteps; ++s) {
       u32x4 x = *reinterpret_cast<const u32x4*>(qp + 8 * s);
       x ^= flip;
-      qr[s] = __builtin_bit_cast(bf16x8, x);
+      qr[s] = __builtin_bit_cast(V8, x);
     }
   }
   // The tile loads below are invisible to the compiler's load counting, so
@@ -172,7 +196,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int srole = lane & 15;
   const int colq = 2 * ((lane >> 4) & 1) + ((srole & 3) >> 1);  // chunk within a 32-dim group
   const int half8 = 8 * (srole & 1);
-  auto pv_tile = [&](int slot, const bf16x8 (&pb)[G::kKB][2]) {
+  auto pv_tile = [&](int slot, const V8 (&pb)[G::kKB][2]) {
     const unsigned char* vtile = reinterpret_cast<const unsigned char*>(&v_lds[slot][0]);
 #pragma unroll
     for (int kb = 0; kb < G::kKB; ++kb)
@@ -190,15 +214,15 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
               (__attribute__((address_space(3))) s16x4*)(vtile + r_hi * (2 * D) +
                                                          16 * (chunk ^ v_swz<D>(r_hi)) + half8));
           const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          const bf16x8 aop = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
-          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, pb[kb][t2], oacc[cb], 0, 0, 0);
+          const V8 aop = __builtin_bit_cast(V8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+          oacc[cb] = H::mfma(aop, pb[kb][t2], oacc[cb]);
         }
       }
   };
 
   // Scores, lazy running max and probabilities of tile T (in ring slot
   // `slot`); returns the bf16 probabilities for the PV product.
-  auto scores_and_p = [&](int32_t T, int slot, bf16x8 (&pb)[G::kKB][2]) {
+  auto scores_and_p = [&](int32_t T, int slot, V8 (&pb)[G::kKB][2]) {
     const int32_t j0 = ks + T * G::kK;
     f32x16 sacc[G::kKB];
 #pragma unroll
@@ -210,9 +234,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int st = 0; st < G::kSteps; ++st) {
         const int chunk = lh * G::kSteps + st;
-        const bf16x8 kop = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(krow + 16 * (chunk ^ k_swz<D>(rho))));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qr[st], sacc[kb], 0, 0, 0);
+        const V8 kop = __builtin_bit_cast(
+            V8, *reinterpret_cast<const u32x4*>(krow + 16 * (chunk ^ k_swz<D>(rho))));
+        sacc[kb] = H::mfma(kop, qr[st], sacc[kb]);
       }
     }
 
@@ -258,7 +282,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
             float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * t2 + e], c, neg_m));
             p = (32 * kb + 16 * t2 + e) < rel ? p : 0.f;
             psum += p;
-            pb[kb][t2][e] = (__bf16)p;
+            pb[kb][t2][e] = (typename H::E)p;
           }
     } else {
 #pragma unroll
@@ -269,14 +293,14 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
           for (int e = 0; e < 8; ++e) {
             const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * t2 + e], c, neg_m));
             psum += p;
-            pb[kb][t2][e] = (__bf16)p;
+            pb[kb][t2][e] = (typename H::E)p;
           }
     }
     l_run += psum;
   };
 
   const bool late = wave >= G::kWaves / 2;
-  bf16x8 pb_late[G::kKB][2];
+  V8 pb_late[G::kKB][2];
   bool late_pending = false;
   int late_slot = 0;
 
@@ -296,7 +320,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
     }
     const int slot = T % G::kSlots;
     if (wave_live && ks + T * G::kK < wave_hi) {
-      bf16x8 pb[G::kKB][2];
+      V8 pb[G::kKB][2];
       scores_and_p(T, slot, pb);
       if (late) {
 #pragma unroll
@@ -346,16 +370,19 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_bf16_variant(const FwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3(a.nwg), dim3(BGeom<D>::kThreads), 0, s, a);
+hipError_t launch_bf16_variant(const FwdArgs& a, bool f16, hipStream_t s) {
+  if (f16)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, true>), dim3(a.nwg), dim3(BGeom<D>::kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, false>), dim3(a.nwg), dim3(BGeom<D>::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, bool causal, hipStream_t s) {
-  if (head_dim == 64) return causal ? launch_bf16_variant<64, true>(a, s) : launch_bf16_variant<64, false>(a, s);
-  if (head_dim == 128) return causal ? launch_bf16_variant<128, true>(a, s) : launch_bf16_variant<128, false>(a, s);
+hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, bool causal, bool f16, hipStream_t s) {
+  if (head_dim == 64) return causal ? launch_bf16_variant<64, true>(a, f16, s) : launch_bf16_variant<64, false>(a, f16, s);
+  if (head_dim == 128) return causal ? launch_bf16_variant<128, true>(a, f16, s) : launch_bf16_variant<128, false>(a, f16, s);
   return hipErrorInvalidValue;
 }
 

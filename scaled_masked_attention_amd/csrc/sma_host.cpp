@@ -40,8 +40,10 @@ size_t elem_bytes(int dt) { return dt == SMA_DTYPE_F32 ? 4 : 2; }
 // Checks that do not depend on pointers. Fills sh on success.
 int check_shape(int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
                 size_t d, double scale, Shape* sh) {
-  if (in_dtype != SMA_DTYPE_F32 && in_dtype != SMA_DTYPE_BF16) return SMA_ERR_INVALID_VALUE;
-  if (o_dtype != SMA_DTYPE_F32 && o_dtype != SMA_DTYPE_BF16) return SMA_ERR_INVALID_VALUE;
+  if (in_dtype != SMA_DTYPE_F32 && in_dtype != SMA_DTYPE_BF16 && in_dtype != SMA_DTYPE_F16)
+    return SMA_ERR_INVALID_VALUE;
+  if (o_dtype != SMA_DTYPE_F32 && o_dtype != SMA_DTYPE_BF16 && o_dtype != SMA_DTYPE_F16)
+    return SMA_ERR_INVALID_VALUE;
   if (d == 0) return SMA_ERR_INVALID_VALUE;
   if (!std::isfinite(scale)) return SMA_ERR_INVALID_VALUE;
   Shape s{};
@@ -59,10 +61,11 @@ int check_shape(int in_dtype, int o_dtype, size_t batch, size_t heads, size_t se
       !mul(s.rows, sizeof(float), &s.lse_bytes))
     return SMA_ERR_INVALID_VALUE;
   if (d != 64 && d != 128) return SMA_ERR_UNSUPPORTED;
+  if (o_dtype == SMA_DTYPE_F16) return SMA_ERR_UNSUPPORTED;
   if (seq_q > kMaxSeq || seq_kv > kMaxSeq || s.bh > (size_t(1) << 31)) return SMA_ERR_UNSUPPORTED;
-  // The bf16 kernel addresses one (batch, head)'s K and V through 32-bit
+  // The 16-bit kernel addresses one (batch, head)'s K and V through 32-bit
   // buffer offsets: keep them, with a tile of slack, below 2^31 bytes.
-  if (in_dtype == SMA_DTYPE_BF16 && (seq_kv + 256) * d * 2 > (size_t(1) << 31))
+  if (in_dtype != SMA_DTYPE_F32 && (seq_kv + 256) * d * 2 > (size_t(1) << 31))
     return SMA_ERR_UNSUPPORTED;
   *sh = s;
   return SMA_OK;
@@ -87,7 +90,7 @@ int keys_per_tile(int kernel) {
   return kernel == SMA_KERNEL_BF16_QBLOCK ? sma::kBF16KeysPerTile : sma::kF32KeysPerTile;
 }
 bool kernel_fits_dtype(int kernel, int in_dtype) {
-  if (in_dtype == SMA_DTYPE_BF16) return kernel == SMA_KERNEL_BF16_QBLOCK;
+  if (in_dtype != SMA_DTYPE_F32) return kernel == SMA_KERNEL_BF16_QBLOCK;
   return kernel == SMA_KERNEL_F32_QBLOCK || kernel == SMA_KERNEL_F32_KSPLIT;
 }
 
@@ -126,7 +129,7 @@ bool ksplit_fits(const Shape& s) {
 }
 
 int auto_kernel(const Shape& s, int num_cus) {
-  if (s.in_dtype == SMA_DTYPE_BF16) return SMA_KERNEL_BF16_QBLOCK;
+  if (s.in_dtype != SMA_DTYPE_F32) return SMA_KERNEL_BF16_QBLOCK;
   if (!ksplit_fits(s)) return SMA_KERNEL_F32_QBLOCK;
   const size_t nwg32 = s.bh * ((s.seq_q + sma::kF32WsplitQueriesPerWG - 1) / sma::kF32WsplitQueriesPerWG);
   if (nwg32 >= (size_t)num_cus || s.seq_kv <= kKsplitAlwaysKeys) return SMA_KERNEL_F32_KSPLIT;
@@ -345,7 +348,7 @@ int sma_attention_fwd_ex(const void* q, const void* k, const void* v, void* o, f
   hipError_t e;
   switch (p.kernel) {
     case SMA_KERNEL_F32_KSPLIT: e = sma::launch_fwd_f32_wsplit(a, d, c, s); break;
-    case SMA_KERNEL_BF16_QBLOCK: e = sma::launch_fwd_bf16(a, d, c, s); break;
+    case SMA_KERNEL_BF16_QBLOCK: e = sma::launch_fwd_bf16(a, d, c, in_dtype == SMA_DTYPE_F16, s); break;
     default: e = sma::launch_fwd_f32(a, d, c, s); break;
   }
   if (e != hipSuccess) return SMA_ERR_HIP;

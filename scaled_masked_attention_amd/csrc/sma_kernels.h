@@ -9,7 +9,7 @@ namespace sma {
 
 // Arguments of one attention-forward launch (one variant of dtype/head_dim/mask).
 struct FwdArgs {
-  const void* q;     // [bh][seq_q][d], f32 or bf16
+  const void* q;     // [bh][seq_q][d], f32, bf16 or fp16
   const void* k;     // [bh][seq_kv][d]
   const void* v;     // [bh][seq_kv][d]
   float* o;          // nsplit == 1: final O [bh][seq_q][d] fp32 (when o_bf16 is null)
@@ -93,7 +93,8 @@ hipError_t launch_rows(int mode, const RowArgs& a, const RowPlan& p, hipStream_t
 
 hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_fwd_f32_wsplit(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);
-hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);
+// 16-bit inputs: bf16, or fp16 when f16.
+hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, bool causal, bool f16, hipStream_t s);
 constexpr int kBwdRowsPerBlock = 32;         // query and key block of the backward kernels
 constexpr int kBwdMetaFloats = 64;          // workspace floats per query block
 hipError_t launch_bwd_f32(const BwdArgs& a, int head_dim, bool causal, hipStream_t s,

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sma.h")
 
 OK, NULLP, INVAL, UNSUP, MISAL, ALIAS = 0, 1, 2, 3, 4, 5
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 
 
 def _declared_functions():
@@ -52,6 +52,7 @@ def test_valid_calls():
     assert _v() == OK
     assert _v(odt=BF16) == OK and _v(odt=BF16, idt=BF16, d=128) == OK
     assert _v(idt=BF16, d=128) == OK
+    assert _v(idt=F16, d=128) == OK and _v(idt=F16, odt=BF16, d=64) == OK
     assert _v(lse=None) == OK
     assert _v(scale=-1.0) == OK and _v(scale=0.0) == OK
 
@@ -78,6 +79,8 @@ def test_unsupported():
     assert _v(d=96) == UNSUP
     assert _v(d=256) == UNSUP
     assert _v(odt=BF16, idt=BF16, d=96) == UNSUP
+    assert _v(odt=F16) == UNSUP and _v(odt=F16, idt=F16) == UNSUP  # fp16 output not built
+    assert _v(idt=F16, d=128, skv=1 << 23) == UNSUP
     assert _v(sq=(1 << 30) + 1) == UNSUP
     assert _v(idt=BF16, d=128, skv=(1 << 23) - 256) == OK  # K/V of one head just under 2 GiB
     assert _v(idt=BF16, d=128, skv=1 << 23) == UNSUP
@@ -145,6 +148,8 @@ def test_plan_auto_choices():
     assert p.kernel == sma.SMA_KERNEL_F32_QBLOCK and p.nsplit > 1
     assert p.workspace_bytes == sma.workspace_bytes(F32, 1, 4, 200, 3000, 128, False, 256)
     p = P(BF16, 1, 32, 16384, 16384, 128, True, num_cus=256)
+    assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_BF16_QBLOCK, 1, 32 * 64)
+    p = P(F16, 1, 32, 16384, 16384, 128, True, num_cus=256)
     assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_BF16_QBLOCK, 1, 32 * 64)
     p = P(F32, 1, 1, 1, 4096, 64, False, num_cus=256)  # one query row, many keys
     assert p.kernel == sma.SMA_KERNEL_F32_QBLOCK and p.nsplit == 32
@@ -266,7 +271,7 @@ def test_backward_workspace_and_host_checks():
     assert call(ws=None) == INVAL and call(wsb=8 * 256 - 1) == INVAL        # 2 heads x 4 blocks
     assert call(d=0) == INVAL and call(scale=float("inf")) == INVAL
     assert call(B=1 << 40, H=1 << 40) == INVAL
-    assert call(d=96) == UNSUP and call(idt=BF16) == UNSUP
+    assert call(d=96) == UNSUP and call(idt=BF16) == UNSUP and call(idt=F16) == UNSUP
     assert call(sq=(1 << 23), d=64) == UNSUP                                 # 32-bit tile offsets
     assert call(q=q + 8) == MISAL and call(dk=dk + 4) == MISAL and call(lse=lse + 2) == MISAL
     assert call(ws=ws + 8) == MISAL

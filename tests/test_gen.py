@@ -68,3 +68,24 @@ def test_bf16_workload_values_are_bf16():
         assert np.array_equal(gen.bf16_bits_to_f32(b), vals)
         assert np.all((vals.view(np.uint32) & 0xFFFF) == 0)
     assert abs(float(q.std()) - 3.0) < 0.1
+
+
+def test_f16_rounding_matches_the_binary16_encoding():
+    """Known binary16 encodings: exact values, ties to even, the largest finite value,
+    subnormals and the overflow to infinity."""
+    x = np.array([1.0, -2.0, 0.5, 65504.0, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 2.0 ** -24,
+                  2.0 ** -25, 3 * 2.0 ** -25, 65520.0, 0.0, -0.0], dtype=np.float32)
+    want = [0x3C00, 0xC000, 0x3800, 0x7BFF, 0x3C00, 0x3C02, 0x0001, 0x0000, 0x0002, 0x7C00, 0x0000, 0x8000]
+    assert gen.f32_to_f16_bits(x).tolist() == want
+    back = gen.f16_bits_to_f32(np.array(want, dtype=np.uint16))
+    assert back[0] == 1.0 and back[3] == 65504.0 and back[6] == 2.0 ** -24 and np.isinf(back[9])
+
+
+def test_to_16bit_values_are_exact_images_of_the_bits():
+    x = gen.tensor_f32(5, "q", (3, 7), 3.0)
+    for dt in ("bf16", "f16"):
+        vals, bits = gen.to_16bit(x, dt)
+        assert vals.dtype == np.float32 and bits.dtype == np.uint16
+        widened = gen.bf16_bits_to_f32(bits) if dt == "bf16" else gen.f16_bits_to_f32(bits)
+        assert np.array_equal(vals, widened)
+        assert np.abs(vals - x).max() <= (2.0 ** -8 if dt == "bf16" else 2.0 ** -11) * np.abs(x).max()

@@ -13,7 +13,7 @@ import pytest
 
 import gen
 import oracle
-from helpers import BF16_MAX_ABS, F32_MAX_ABS, empty_rows, to_device
+from helpers import BF16_MAX_ABS, F16_MAX_ABS, F32_MAX_ABS, empty_rows, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -52,7 +52,7 @@ def _bits(t):
 
 
 @pytest.mark.parametrize("plan", list(PLANS))
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(2, 3, 200, 200), (1, 2, 77, 300), (2, 1, 300, 77), (1, 4, 257, 1025)],
@@ -65,7 +65,7 @@ def test_bf16_output_is_the_rounded_fp32_output(shape, causal, d, dtype, plan):
     kw = _plan_kwargs(plan, dtype)
     B, H, sq, skv = shape
     (q, k, v), bits = gen.random_case(700 + sq + 3 * skv + d, (B, H, sq, d), (B, H, skv, d),
-                                      sigma_qk=3.0 if dtype == "bf16" else 1.0, dtype=dtype)
+                                      sigma_qk=1.0 if dtype == "f32" else 3.0, dtype=dtype)
     tq, tk, tv = to_device((q, k, v), bits, dtype)
     scale = 1.0 / math.sqrt(d)
     o32, l32 = sma.attention_fwd(tq, tk, tv, scale=scale, causal=causal, return_lse=True, **kw)
@@ -78,7 +78,8 @@ def test_bf16_output_is_the_rounded_fp32_output(shape, causal, d, dtype, plan):
     assert torch.equal(l16, l32), "LSE changed with the output dtype"
     o_ref, _ = oracle.attention_fwd(q, k, v, scale, causal)
     got = gen.bf16_bits_to_f32(_bits(o16)).astype(np.float64)
-    bar = (F32_MAX_ABS if dtype == "f32" else BF16_MAX_ABS) + 2.0 ** -8 * np.abs(f32.astype(np.float64))
+    bar = ({"f32": F32_MAX_ABS, "bf16": BF16_MAX_ABS, "f16": F16_MAX_ABS}[dtype]
+           + 2.0 ** -8 * np.abs(f32.astype(np.float64)))
     assert np.all(np.abs(got - o_ref) <= bar)
     er = empty_rows(sq, skv, causal)
     if er.any():

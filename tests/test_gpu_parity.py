@@ -58,7 +58,7 @@ def plan_kwargs(plan, dtype):
 @functools.lru_cache(maxsize=8)
 def _small_case(shape, causal, d, dtype):
     B, H, sq, skv = shape
-    sig = 3.0 if dtype == "bf16" else 1.0
+    sig = 1.0 if dtype == "f32" else 3.0
     (q, k, v), bits = _case(100 + sq + 7 * skv + d, B, H, sq, skv, d, dtype, sigma_qk=sig)
     scale = 1.0 / math.sqrt(d)
     o_ref, lse_ref = oracle.attention_fwd(q, k, v, scale, causal)
@@ -66,7 +66,7 @@ def _small_case(shape, causal, d, dtype):
 
 
 @pytest.mark.parametrize("plan", list(PLANS))
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -117,12 +117,14 @@ def test_parity_full_size_qblock_sampled(name):
                  f"{name} qblock")
 
 
-@pytest.mark.parametrize("name", ["f32_causal_b8h16_s2048_d128", "f32_cross_b2h32_q256_kv4096_d128", "f32_cross_causal_b2h32_q256_kv4096_d128", "bf16_causal_b1h32_s16384_d128"])
+@pytest.mark.parametrize("name", ["f32_causal_b8h16_s2048_d128", "f32_cross_b2h32_q256_kv4096_d128",
+                                  "f32_cross_causal_b2h32_q256_kv4096_d128", "bf16_causal_b1h32_s16384_d128",
+                                  "f16_causal_b1h32_s16384_d128"])
 def test_parity_full_size_sampled(name):
     w, vals, bits = workload_case(name)
     o, lse = run_gpu(*to_device(vals, bits, w.dtype), w.scale, w.causal)
     B, H, sq, skv = w.batch, w.heads, w.seq_q, w.seq_kv
-    rows = sample_rows(B, H, sq, skv, w.causal, n_random=192 if name == "bf16_causal_b1h32_s16384_d128" else 512, seed=7)
+    rows = sample_rows(B, H, sq, skv, w.causal, n_random=512 if w.dtype == "f32" else 192, seed=7)
     o_ref, lse_ref = oracle.attention_fwd(*vals, w.scale, w.causal, rows=rows)
     o_s = o.reshape(-1, w.head_dim)[rows]
     l_s = lse.reshape(-1)[rows]
@@ -137,8 +139,8 @@ def test_parity_full_size_sampled(name):
 
 # ------------------------------------------------------------------ edge cases
 # Each edge case runs on every kernel: the fp32 128-row kernel (unsplit), the
-# fp32 in-workgroup key-split kernel, and the bf16 kernel.
-VARIANTS = ["f32-qblock", "f32-ksplit", "bf16"]
+# fp32 in-workgroup key-split kernel, and the 16-bit kernel with bf16 and fp16 inputs.
+VARIANTS = ["f32-qblock", "f32-ksplit", "bf16", "f16"]
 
 
 def variant_kwargs(variant):
@@ -148,7 +150,7 @@ def variant_kwargs(variant):
         return "f32", dict(kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=1)
     if variant == "f32-ksplit":
         return "f32", dict(kernel=sma.SMA_KERNEL_F32_KSPLIT, nsplit=1)
-    return "bf16", dict(kernel=sma.SMA_KERNEL_BF16_QBLOCK, nsplit=1)
+    return variant, dict(kernel=sma.SMA_KERNEL_BF16_QBLOCK, nsplit=1)
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -158,7 +160,7 @@ def test_no_keys_gives_zero_and_neg_inf(variant):
 
     import scaled_masked_attention_amd as sma
 
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
     q = torch.randn(2, 3, 70, 128, device="cuda").to(tdt)
     k = torch.empty(2, 3, 0, 128, device="cuda", dtype=tdt)
     out = torch.full((2, 3, 70, 128), float("nan"), device="cuda")
@@ -203,10 +205,10 @@ def test_v_ones_gives_ones(variant):
     (q, k, v), bits = _case(33, 2, 2, sq, skv, d, dtype, sigma_qk=3.0)
     v[:] = 1.0
     if bits is not None:
-        bits = bits[:2] + (gen.f32_to_bf16_bits(v),)
+        bits = bits[:2] + (gen.to_16bit(v, dtype)[1],)
     o, _ = run_gpu(*to_device((q, k, v), bits, dtype), 1.0 / math.sqrt(d), True, **kw)
     er = empty_rows(sq, skv, True)
-    tol = 2e-5 if dtype == "f32" else 2 ** -8
+    tol = {"f32": 2e-5, "bf16": 2 ** -8, "f16": 2 ** -11}[dtype]
     assert np.all(np.abs(o[:, :, ~er] - 1.0) <= tol)
 
 
@@ -218,10 +220,10 @@ def test_one_hot_v_extracts_probabilities(variant):
     (q, k, _), bits = _case(34, 1, 1, sq, d, d, dtype, sigma_qk=2.0)
     v = np.eye(d, dtype=np.float32).reshape(1, 1, d, d)
     if bits is not None:
-        bits = bits[:2] + (gen.f32_to_bf16_bits(v),)
+        bits = bits[:2] + (gen.to_16bit(v, dtype)[1],)
     o, _ = run_gpu(*to_device((q, k, v), bits, dtype), 0.2, True, **kw)
     p = oracle.softmax_probs(q[0, 0], k[0, 0], 0.2, True)
-    tol = 2e-5 if dtype == "f32" else 2e-2
+    tol = {"f32": 2e-5, "bf16": 2e-2, "f16": 4e-3}[dtype]
     assert np.abs(o[0, 0] - p).max() <= tol
 
 
@@ -239,9 +241,9 @@ def test_key_shift_beyond_fp32_exp_range(variant):
     q[..., 0] = 8.0
     k[..., 0] = 256.0  # scale * 8 * 256 = 181 added to every score of a row
     bits = None
-    if dtype == "bf16":
-        bits = tuple(gen.f32_to_bf16_bits(x) for x in (q, k, v))
-        q, k, v = (gen.bf16_bits_to_f32(b) for b in bits)
+    if dtype != "f32":
+        pairs = [gen.to_16bit(x, dtype) for x in (q, k, v)]
+        (q, k, v), bits = tuple(p[0] for p in pairs), tuple(p[1] for p in pairs)
     scale = 1.0 / math.sqrt(d)
     o, lse = run_gpu(*to_device((q, k, v), bits, dtype), scale, True, **kw)
     o_ref, lse_ref = oracle.attention_fwd(q, k, v, scale, True)
@@ -307,7 +309,7 @@ def test_guard_bands_untouched_and_nan_prefill_overwritten(variant):
                  o_ref, lse_ref, dtype, "guard")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_non_default_stream(dtype):
     import torch
 
@@ -326,7 +328,7 @@ def test_non_default_stream(dtype):
     assert torch.equal(o2, o * 2.0)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_split_keys_path_matches_unsplit(dtype, causal):
     """A shape the planner splits across workgroups: with and without workspace."""
@@ -336,7 +338,7 @@ def test_split_keys_path_matches_unsplit(dtype, causal):
 
     B, H, sq, skv, d = 1, 4, 200, 3000, 128
     (q, k, v), bits = _case(41, B, H, sq, skv, d, dtype)
-    in_dt = sma.SMA_DTYPE_F32 if dtype == "f32" else sma.SMA_DTYPE_BF16
+    in_dt = {"f32": sma.SMA_DTYPE_F32, "bf16": sma.SMA_DTYPE_BF16, "f16": sma.SMA_DTYPE_F16}[dtype]
     assert sma.workspace_bytes(in_dt, B, H, sq, skv, d, causal) > 0
     dev = to_device((q, k, v), bits, dtype)
     o_s, l_s = run_gpu(*dev, 0.1, causal)
