@@ -412,6 +412,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(gen_workloads()))
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"],
                     help="element type of the attention output O (bf16: rounded to nearest even)")
+    ap.add_argument("--layout", default="bhsd", choices=["bhsd", "bshd"],
+                    help="memory layout of q, k, v and O: [B,H,S,d] or [B,S,H,d]")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -457,8 +459,12 @@ def main():
         tq, tk, tv = (torch.from_numpy(b.view(np.int16)).to("cuda").view(tdt) for b in bits)
         in_dt = sma.SMA_DTYPE_BF16 if w.dtype == "bf16" else sma.SMA_DTYPE_F16
     B, H, sq, skv, d = w.batch, w.heads, w.seq_q, w.seq_kv, w.head_dim
+    lay = sma.LAYOUTS[args.layout]
+    if args.layout == "bshd":  # the same data, heads of one position adjacent
+        tq, tk, tv = (t.transpose(1, 2).contiguous() for t in (tq, tk, tv))
     o16 = args.out_dtype == "bf16"
-    out = torch.empty((B, H, sq, d), dtype=torch.bfloat16 if o16 else torch.float32, device="cuda")
+    o_shape = (B, sq, H, d) if args.layout == "bshd" else (B, H, sq, d)
+    out = torch.empty(o_shape, dtype=torch.bfloat16 if o16 else torch.float32, device="cuda")
     o_dt = sma.SMA_DTYPE_BF16 if o16 else sma.SMA_DTYPE_F32
     lse = torch.empty((B, H, sq), dtype=torch.float32, device="cuda")
     ws_n = sma.workspace_bytes(in_dt, B, H, sq, skv, d, w.causal)
@@ -468,10 +474,13 @@ def main():
     plan = sma.plan(in_dt, B, H, sq, skv, d, w.causal)
     ev = HipEvents()
     call = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(), in_dt,
-            o_dt, B, H, sq, skv, d, w.scale, w.causal, ws.data_ptr(), ws_n, sptr)
+            o_dt, B, H, sq, skv, d, w.scale, w.causal, ws.data_ptr(), ws_n)
+
+    def run(e0=None, e1=None):
+        sma.attention_fwd_ex_raw(*call, None, sptr, e0, e1, layout=lay)
 
     for _ in range(args.warmup):
-        sma.attention_fwd_raw(*call)
+        run()
     torch.cuda.synchronize()
     # Timed region. A one-kernel step is bracketed by two events around the whole
     # loop (events around every launch would add their own gaps to each
@@ -486,11 +495,11 @@ def main():
     t0 = time.perf_counter()
     if per_launch:
         for i in range(args.steps):
-            sma.attention_fwd_timed_raw(*call, ev_a[i], ev_b[i])
+            run(ev_a[i], ev_b[i])
     else:
         ev.record(ev_a[0], sptr)
         for i in range(args.steps):
-            sma.attention_fwd_raw(*call)
+            run()
         ev.record(ev_b[0], sptr)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -507,8 +516,8 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     exact = 4.0 * d * allowed_pairs(w)
     achieved = exact / (k_avg * 1e-3) / 1e12
-    # the committed counter passes were taken with fp32 output
-    traffic = None if o16 else read_traffic(KERNEL_FUNCTIONS[plan.kernel], w.name,
+    # the committed counter passes were taken with fp32 output in [B,H,S,d]
+    traffic = None if (o16 or args.layout != "bhsd") else read_traffic(KERNEL_FUNCTIONS[plan.kernel], w.name,
                                             kernel_source_digest(KERNEL_FUNCTIONS[plan.kernel]))
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -518,6 +527,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_q": sq, "seq_kv": skv,
                    "head_dim": d, "causal": w.causal, "scale": w.scale,
                    "input_dtype": w.dtype, "accumulate": "f32", "output": args.out_dtype, "lse": True,
+                   "layout": args.layout,
                    "key_splits_workspace_bytes": ws_n},
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SMA_ABI_VERSION 1
+#define SMA_ABI_VERSION 2
 
 /* Element types. Accumulation is always fp32. */
 typedef enum {
@@ -69,6 +69,14 @@ typedef enum {
   SMA_ERR_ALIASING = 5,      /* o or lse overlaps q, k, v, the workspace, or each other */
   SMA_ERR_HIP = 6            /* the HIP runtime reported an error (device query or launch) */
 } sma_status;
+
+/* Memory layout of q, k, v and o (lse is always [B,H,Sq]). Both are dense and
+ * row-major with the head dim contiguous. */
+typedef enum {
+  SMA_LAYOUT_BHSD = 0, /* [batch, heads, seq, head_dim] (what sma_attention_fwd takes) */
+  SMA_LAYOUT_BSHD = 1  /* [batch, seq, heads, head_dim]: the heads of one position adjacent, as
+                          a fused projection writes them; no transposition is needed */
+} sma_layout;
 
 /* Kernels the library can run for one call. Each computes the whole operation;
  * they differ only in how the work is spread over workgroups. */
@@ -163,9 +171,10 @@ int sma_attention_fwd_plan(int in_dtype, size_t batch, size_t heads, size_t seq_
                            size_t head_dim, int causal, int kernel, int nsplit, int num_cus,
                            sma_plan* out);
 
-/* sma_attention_fwd with the kernel and key split taken from `plan` (NULL:
- * the library's choice, exactly sma_attention_fwd) and with the measurement
- * events of sma_attention_fwd_timed. Only plan->kernel and plan->nsplit are
+/* sma_attention_fwd with the memory layout of sma_attention_fwd_layout, the
+ * kernel and key split taken from `plan` (NULL: the library's choice, exactly
+ * sma_attention_fwd for SMA_LAYOUT_BHSD) and the measurement events of
+ * sma_attention_fwd_timed. Only plan->kernel and plan->nsplit are
  * read; the plan is rebuilt from them for this shape and the current device,
  * so plan->workgroups and plan->workspace_bytes are informative. Unlike the
  * automatic choice, an explicit split is never dropped: a workspace smaller
@@ -173,9 +182,22 @@ int sma_attention_fwd_plan(int in_dtype, size_t batch, size_t heads, size_t seq_
  * plan up to floating-point rounding order. */
 int sma_attention_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                          int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
-                         size_t seq_kv, size_t head_dim, double scale, int causal, void* workspace,
-                         size_t workspace_bytes, const sma_plan* plan, void* stream,
-                         void* event_before, void* event_after);
+                         size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
+                         void* workspace, size_t workspace_bytes, const sma_plan* plan,
+                         void* stream, void* event_before, void* event_after);
+
+/* sma_attention_fwd on tensors in `layout` (an sma_layout; other values ->
+ * INVALID_VALUE), with the library's plan. The result is bitwise the same as
+ * for the same data in [B,H,S,d]. The size checks apply to the layout's row
+ * stride: with SMA_LAYOUT_BSHD one row of a head is heads*head_dim elements
+ * from the next, so the 2 GiB limits on (seq + tile) rows are reached at
+ * 1/heads the sequence length. sma_attention_fwd_workspace_bytes and
+ * sma_attention_fwd_plan describe [B,H,S,d]; a workspace too small for the
+ * plan chosen here only disables the key split. */
+int sma_attention_fwd_layout(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
+                             size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------ backward
  *

@@ -17,6 +17,9 @@ LIB_PATH = os.path.join(PKG, "libsma.so")
 SMA_DTYPE_F32 = 0
 SMA_DTYPE_BF16 = 1
 SMA_DTYPE_F16 = 2
+SMA_LAYOUT_BHSD = 0
+SMA_LAYOUT_BSHD = 1
+LAYOUTS = {"bhsd": SMA_LAYOUT_BHSD, "bshd": SMA_LAYOUT_BSHD}
 SMA_OK = 0
 SMA_KERNEL_AUTO = -1
 SMA_KERNEL_F32_QBLOCK = 0
@@ -74,9 +77,12 @@ def library():
                                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                ctypes.POINTER(Plan)]
         lib.sma_attention_fwd_plan.restype = ctypes.c_int
-        lib.sma_attention_fwd_ex.argtypes = (lib.sma_attention_fwd.argtypes[:16] +
+        fwd = lib.sma_attention_fwd.argtypes
+        lib.sma_attention_fwd_ex.argtypes = (fwd[:14] + [ctypes.c_int] + fwd[14:16] +
                                              [ctypes.POINTER(Plan), vp, vp, vp])
         lib.sma_attention_fwd_ex.restype = ctypes.c_int
+        lib.sma_attention_fwd_layout.argtypes = fwd[:14] + [ctypes.c_int] + fwd[14:17]
+        lib.sma_attention_fwd_layout.restype = ctypes.c_int
         fp = ctypes.c_void_p
         lib.sma_softmax_rows.argtypes = [fp, fp, sz, sz, vp]
         lib.sma_logsumexp_rows.argtypes = [fp, fp, sz, sz, vp]
@@ -158,17 +164,17 @@ def attention_fwd_timed_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dty
 
 def attention_fwd_ex_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dtype, batch, heads,
                          seq_q, seq_kv, head_dim, scale, causal, ws_ptr, ws_bytes, plan_, stream,
-                         event_before=None, event_after=None) -> None:
-    """sma_attention_fwd_ex: explicit plan (a Plan, or None for the library's choice)."""
+                         event_before=None, event_after=None, layout=SMA_LAYOUT_BHSD) -> None:
+    """sma_attention_fwd_ex: explicit plan (a Plan, or None for the library's choice) and layout."""
     _raise(library().sma_attention_fwd_ex(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dtype,
                                           batch, heads, seq_q, seq_kv, head_dim, float(scale),
-                                          int(bool(causal)), ws_ptr, ws_bytes,
+                                          int(bool(causal)), int(layout), ws_ptr, ws_bytes,
                                           ctypes.byref(plan_) if plan_ is not None else None,
                                           stream, event_before, event_after))
 
 
 def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=None,
-                  workspace=None, stream=None, kernel=None, nsplit=0, out_dtype=None):
+                  workspace=None, stream=None, kernel=None, nsplit=0, out_dtype=None, layout="bhsd"):
     """O = softmax(scale * Q K^T + mask) V on the GPU.
 
     q [B,H,Sq,D], k and v [B,H,Skv,D]: contiguous torch tensors on the current
@@ -177,6 +183,8 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
     ``out`` of that dtype) and, with return_lse, the per-row natural-log LSE
     (float32, [B,H,Sq]).
     scale=None means 1/sqrt(D). causal uses the bottom-right alignment.
+    layout="bshd" takes q [B,Sq,H,D], k and v [B,Skv,H,D] and returns O in that
+    layout (LSE stays [B,H,Sq]).
     kernel (an SMA_KERNEL_* code) and nsplit force a plan; by default the
     library chooses. A forced split gets a workspace of the size it needs.
     """
@@ -186,9 +194,18 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
         raise TypeError("q, k, v must be torch tensors")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [batch, heads, seq, head_dim]")
-    B, H, Sq, D = q.shape
-    Skv = k.shape[2]
-    if tuple(k.shape) != (B, H, Skv, D) or tuple(v.shape) != (B, H, Skv, D):
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    bshd = layout == "bshd"
+    if bshd:
+        B, Sq, H, D = q.shape
+        Skv = k.shape[1]
+        kv_shape, o_shape = (B, Skv, H, D), (B, Sq, H, D)
+    else:
+        B, H, Sq, D = q.shape
+        Skv = k.shape[2]
+        kv_shape, o_shape = (B, H, Skv, D), (B, H, Sq, D)
+    if tuple(k.shape) != kv_shape or tuple(v.shape) != kv_shape:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share one dtype")
@@ -214,14 +231,14 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
         raise ValueError(f"unsupported out_dtype {out_dtype}")
     o_dt = SMA_DTYPE_F32 if out_dtype == torch.float32 else SMA_DTYPE_BF16
     if out is None:
-        out = torch.empty((B, H, Sq, D), dtype=out_dtype, device=dev)
+        out = torch.empty(o_shape, dtype=out_dtype, device=dev)
     if return_lse and lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
     if out.device != dev or out.dtype != out_dtype or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous {out_dtype} tensor on {dev}")
     if lse is not None and (lse.device != dev or lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise ValueError(f"lse must be a contiguous float32 tensor on {dev}")
-    if out.shape != (B, H, Sq, D) or (lse is not None and lse.shape != (B, H, Sq)):
+    if tuple(out.shape) != o_shape or (lse is not None and lse.shape != (B, H, Sq)):
         raise ValueError("out/lse shape mismatch")
     forced = None
     if kernel is not None and kernel != SMA_KERNEL_AUTO:
@@ -238,7 +255,7 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
     attention_fwd_ex_raw(q.data_ptr(), k.data_ptr() if Skv else None, v.data_ptr() if Skv else None,
                          out.data_ptr(), lse.data_ptr() if lse is not None else None, in_dt,
                          o_dt, B, H, Sq, Skv, D, scale, causal, ws_ptr, ws_bytes, forced,
-                         stream.cuda_stream)
+                         stream.cuda_stream, layout=LAYOUTS[layout])
     return (out, lse) if return_lse else out
 
 

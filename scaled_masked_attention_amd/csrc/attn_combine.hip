@@ -39,12 +39,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
       acc[3] += w * x[3];
     }
   }
+  const int64_t bh = row / a.seq_q;
+  const int64_t o_off = head_offset(bh, a.heads, a.os_b, a.os_h) + (row - bh * a.seq_q) * a.os_s + 4 * c4;
   if (a.o_bf16) {
     typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-    *reinterpret_cast<u32x2_t*>(a.o_bf16 + row * D + 4 * c4) =
+    *reinterpret_cast<u32x2_t*>(a.o_bf16 + o_off) =
         u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
   } else {
-    *reinterpret_cast<f32x4*>(a.o + row * D + 4 * c4) = acc;
+    *reinterpret_cast<f32x4*>(a.o + o_off) = acc;
   }
   if (a.lse && c4 == 0) a.lse[row] = mx == -INFINITY ? -INFINITY : lse2 * 0.69314718055994530942f;
 }

@@ -19,6 +19,11 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t wg, uint32_t nwg) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
+// Element offset of the first row of (batch*head index bh) under strides (sb, sh).
+__device__ __forceinline__ int64_t head_offset(int64_t bh, int64_t heads, int64_t sb, int64_t sh) {
+  return (bh / heads) * sb + (bh % heads) * sh;
+}
+
 struct TileId {
   int64_t bh;
   int32_t qb;
@@ -108,6 +113,28 @@ __device__ __forceinline__ unsigned tile_src_offset(int t, int lane) {
   const int r = p / kChunks;
   const int c = (p % kChunks) ^ (r & 15);
   return (unsigned)(r * 4 * D + 16 * c);
+}
+// The same with rows row_bytes apart in global memory (a strided layout).
+template <int D>
+__device__ __forceinline__ unsigned tile_src_offset(int t, int lane, unsigned row_bytes) {
+  constexpr int kChunks = D / 4;
+  const int p = 64 * t + lane;
+  const int r = p / kChunks;
+  const int c = (p % kChunks) ^ (r & 15);
+  return (unsigned)r * row_bytes + 16u * (unsigned)c;
+}
+// Unswizzled copy: lane l of instruction t fetches chunk p = 64t + l in row order.
+template <int D>
+__device__ __forceinline__ unsigned tile_src_offset_linear(int t, int lane, unsigned row_bytes) {
+  constexpr int kChunks = D / 4;
+  const int p = 64 * t + lane;
+  return (unsigned)(p / kChunks) * row_bytes + 16u * (unsigned)(p % kChunks);
+}
+// Bytes a buffer resource must span to cover `rows` rows of `row_elems`
+// elements each, `stride_elems` apart: the last row ends the range.
+__device__ __forceinline__ unsigned strided_range(int32_t rows, int64_t stride_elems,
+                                                  int row_elems, int elem_bytes) {
+  return rows > 0 ? (unsigned)(((int64_t)(rows - 1) * stride_elems + row_elems) * elem_bytes) : 0u;
 }
 
 // LDS byte offset, within a tile, of the 16 bytes holding head dims

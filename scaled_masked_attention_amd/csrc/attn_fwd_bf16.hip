@@ -137,7 +137,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   V8 qr[G::kSteps];
   {
     const unsigned short* qp = static_cast<const unsigned short*>(a.q) +
-                               ((size_t)t.bh * a.seq_q + min(my_row, a.seq_q - 1)) * D + lh * G::kHalf;
+                               head_offset(t.bh, a.heads, a.qs_b, a.qs_h) +
+                               (int64_t)min(my_row, a.seq_q - 1) * a.qs_s + lh * G::kHalf;
     const unsigned flip = a.negate_q ? 0x80008000u : 0u;
 #pragma unroll
     for (int s = 0; s < G::kSteps; ++s) {
@@ -152,11 +153,13 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
 
   // Buffer resources over this (batch, head)'s K and V: rows past the last key
   // fall outside the byte range and read as zeros.
-  const unsigned kv_bytes = (unsigned)a.seq_kv * (unsigned)(2 * D);
+  const unsigned kv_bytes = strided_range(a.seq_kv, a.kvs_s, D, 2);
+  const unsigned kv_row = (unsigned)(a.kvs_s * 2);  // bytes between consecutive key rows
+  const int64_t kv_off = head_offset(t.bh, a.heads, a.kvs_b, a.kvs_h);
   const __amdgpu_buffer_rsrc_t k_rsrc =
-      raw_buffer(static_cast<const unsigned short*>(a.k) + (size_t)t.bh * a.seq_kv * D, kv_bytes);
+      raw_buffer(static_cast<const unsigned short*>(a.k) + kv_off, kv_bytes);
   const __amdgpu_buffer_rsrc_t v_rsrc =
-      raw_buffer(static_cast<const unsigned short*>(a.v) + (size_t)t.bh * a.seq_kv * D, kv_bytes);
+      raw_buffer(static_cast<const unsigned short*>(a.v) + kv_off, kv_bytes);
   // Each wave-wide load fills 64 consecutive LDS chunks: position
   // p = (u*waves + wave)*64 + lane is row rho = p / chunks_per_row, chunk
   // p % chunks_per_row; the lane fetches the global chunk that belongs there
@@ -167,9 +170,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   static_assert(D == 128 || D == 64, "swizzles are defined for d = 64 and 128");
   const int rho0 = (wave * 64 + lane) / G::kChunksPerRow;
   const int pc = lane % G::kChunksPerRow;
-  const unsigned k_lane_ofs = (unsigned)((rho0 & ~31) | swap_bits_2_3(rho0 & 31)) * (2 * D) +
+  const unsigned k_lane_ofs = (unsigned)((rho0 & ~31) | swap_bits_2_3(rho0 & 31)) * kv_row +
                               16u * (unsigned)(pc ^ k_swz<D>(rho0));
-  const unsigned v_lane_ofs = (unsigned)rho0 * (2 * D) + 16u * (unsigned)(pc ^ v_swz<D>(rho0));
+  const unsigned v_lane_ofs = (unsigned)rho0 * kv_row + 16u * (unsigned)(pc ^ v_swz<D>(rho0));
 
   auto issue_tile = [&](int32_t T) {
     const unsigned row0 = (unsigned)(ks + T * G::kK);
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int u = 0; u < G::kLoadsPerThread; ++u) {
       const int base = (u * G::kWaves + wave) * 64;
-      const unsigned tile_ofs = (row0 + (unsigned)(u * kRowsPerU)) * (unsigned)(2 * D);
+      const unsigned tile_ofs = (row0 + (unsigned)(u * kRowsPerU)) * kv_row;
       dma_load_x4(k_rsrc, k_lane_ofs + tile_ofs, lds_address(&k_lds[slot][base]));
       dma_load_x4(v_rsrc, v_lane_ofs + tile_ofs, lds_address(&v_lds[slot][base]));
     }
@@ -346,8 +349,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   float* orow = nullptr;
   unsigned short* orow16 = nullptr;
   if (a.nsplit == 1) {
-    if (a.o_bf16) orow16 = a.o_bf16 + row_id * D;
-    else orow = a.o + row_id * D;
+    const int64_t o_off = head_offset(t.bh, a.heads, a.qs_b, a.qs_h) + (int64_t)my_row * a.qs_s;
+    if (a.o_bf16) orow16 = a.o_bf16 + o_off;
+    else orow = a.o + o_off;
     if (a.lse && lh == 0) a.lse[row_id] = empty ? -INFINITY : lse2 * 0.69314718055994530942f;
   } else {
     const size_t prow = (size_t)t.split * ((size_t)a.bh * a.seq_q) + row_id;

@@ -90,8 +90,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   // This lane's half of its query row, kept in registers for the whole pass.
   float qr[G::kHalf];
   {
-    const float* qp = static_cast<const float*>(a.q) +
-                      ((size_t)t.bh * a.seq_q + ld_row) * D + lh * G::kHalf;
+    const float* qp = static_cast<const float*>(a.q) + head_offset(t.bh, a.heads, a.qs_b, a.qs_h) +
+                      (int64_t)ld_row * a.qs_s + lh * G::kHalf;
 #pragma unroll
     for (int u = 0; u < G::kHalf / 4; ++u) {
       const f32x4 x = *reinterpret_cast<const f32x4*>(qp + 4 * u);
@@ -106,8 +106,9 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
     }
   }
 
-  const float* kg = static_cast<const float*>(a.k) + (size_t)t.bh * a.seq_kv * D;
-  const float* vg = static_cast<const float*>(a.v) + (size_t)t.bh * a.seq_kv * D;
+  const int64_t kv_off = head_offset(t.bh, a.heads, a.kvs_b, a.kvs_h);
+  const float* kg = static_cast<const float*>(a.k) + kv_off;
+  const float* vg = static_cast<const float*>(a.v) + kv_off;
   f32x4 kreg[G::kF4PerThread], vreg[G::kF4PerThread];
 
   auto load_tile = [&](int32_t tile) {
@@ -119,8 +120,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
       // Rows past seq_kv re-read the last key row (in bounds, finite, branch
       // free); such keys are always masked and weigh an exact zero.
       const int32_t j = min(j0 + row, a.seq_kv - 1);
-      kreg[u] = *reinterpret_cast<const f32x4*>(kg + (size_t)j * D + 4 * c4);
-      vreg[u] = *reinterpret_cast<const f32x4*>(vg + (size_t)j * D + 4 * c4);
+      kreg[u] = *reinterpret_cast<const f32x4*>(kg + (int64_t)j * a.kvs_s + 4 * c4);
+      vreg[u] = *reinterpret_cast<const f32x4*>(vg + (int64_t)j * a.kvs_s + 4 * c4);
     }
   };
   auto store_tile = [&](int buf) {
@@ -225,8 +226,9 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   float* orow = nullptr;
   unsigned short* orow16 = nullptr;
   if (a.nsplit == 1) {
-    if (a.o_bf16) orow16 = a.o_bf16 + row_id * D;
-    else orow = a.o + row_id * D;
+    const int64_t o_off = head_offset(t.bh, a.heads, a.qs_b, a.qs_h) + (int64_t)my_row * a.qs_s;
+    if (a.o_bf16) orow16 = a.o_bf16 + o_off;
+    else orow = a.o + o_off;
     if (a.lse && lh == 0) a.lse[row_id] = empty ? -INFINITY : lse2 * 0.69314718055994530942f;
   } else {
     const size_t prow = (size_t)t.split * ((size_t)a.bh * a.seq_q) + row_id;

@@ -92,35 +92,37 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
   const int32_t b_end = (int32_t)(((int64_t)nblocks * (wave + 1)) / G::kWaves);
 
   // Rows past the end of Q or K lie outside these ranges and read as zeros.
+  // Rows are q_row / kv_row bytes apart (the layout's row strides).
+  const unsigned q_row = (unsigned)(a.qs_s * 4), kv_row = (unsigned)(a.kvs_s * 4);
   const __amdgpu_buffer_rsrc_t q_rsrc =
-      raw_buffer(static_cast<const float*>(a.q) + (size_t)bh * a.seq_q * D,
-                 (unsigned)a.seq_q * (unsigned)G::kRowBytes);
+      raw_buffer(static_cast<const float*>(a.q) + head_offset(bh, a.heads, a.qs_b, a.qs_h),
+                 strided_range(a.seq_q, a.qs_s, D, 4));
+  const int64_t kv_off = head_offset(bh, a.heads, a.kvs_b, a.kvs_h);
   const __amdgpu_buffer_rsrc_t k_rsrc =
-      raw_buffer(static_cast<const float*>(a.k) + (size_t)bh * a.seq_kv * D,
-                 (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
+      raw_buffer(static_cast<const float*>(a.k) + kv_off, strided_range(a.seq_kv, a.kvs_s, D, 4));
   const __amdgpu_buffer_rsrc_t v_rsrc =
-      raw_buffer(static_cast<const float*>(a.v) + (size_t)bh * a.seq_kv * D,
-                 (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
+      raw_buffer(static_cast<const float*>(a.v) + kv_off, strided_range(a.seq_kv, a.kvs_s, D, 4));
   // V rows are copied as they are (row-major, unswizzled): the operand reads
   // below take 16 or 8 consecutive bytes per lane along a row.
   auto copy_v_block = [&](int32_t b) {
-    const unsigned row0 = (unsigned)(32 * b) * (unsigned)G::kRowBytes;
+    const unsigned row0 = (unsigned)(32 * b) * kv_row;
 #pragma unroll
     for (int t = 0; t < G::kDmaPerTile; ++t)
-      dma_load_x4(v_rsrc, row0 + 1024u * t + 16u * lane, lds_address(v_slot + 1024 * t));
+      dma_load_x4(v_rsrc, row0 + tile_src_offset_linear<D>(t, lane, kv_row),
+                  lds_address(v_slot + 1024 * t));
   };
   auto copy_k_block = [&](int32_t b) {
-    const unsigned row0 = (unsigned)(32 * b) * (unsigned)G::kRowBytes;
+    const unsigned row0 = (unsigned)(32 * b) * kv_row;
 #pragma unroll
     for (int t = 0; t < G::kDmaPerTile; ++t)
-      dma_load_x4(k_rsrc, row0 + tile_src_offset<D>(t, lane), lds_address(k_slot + 1024 * t));
+      dma_load_x4(k_rsrc, row0 + tile_src_offset<D>(t, lane, kv_row), lds_address(k_slot + 1024 * t));
   };
 
   // Q tile (the waves copy a quarter each) and this wave's first K and V blocks.
 #pragma unroll
   for (int i = 0; i < G::kDmaPerTile / G::kWaves; ++i) {
     const int t = i * G::kWaves + wave;
-    dma_load_x4(q_rsrc, (unsigned)q0 * (unsigned)G::kRowBytes + tile_src_offset<D>(t, lane),
+    dma_load_x4(q_rsrc, (unsigned)q0 * q_row + tile_src_offset<D>(t, lane, q_row),
                 lds_address(q_tile + 1024 * t));
   }
   if (b_begin < b_end) {
@@ -296,12 +298,13 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) out[e] = empty ? 0.f : acc[e] * inv;
     const size_t row_id = (size_t)bh * a.seq_q + row;
+    const int64_t o_off = head_offset(bh, a.heads, a.qs_b, a.qs_h) + (int64_t)row * a.qs_s + 4 * c4;
     if (a.o_bf16) {
       typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
       const u32x2_t packed = {pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3])};
-      *reinterpret_cast<u32x2_t*>(a.o_bf16 + row_id * D + 4 * c4) = packed;
+      *reinterpret_cast<u32x2_t*>(a.o_bf16 + o_off) = packed;
     } else {
-      *reinterpret_cast<f32x4*>(a.o + row_id * D + 4 * c4) = out;
+      *reinterpret_cast<f32x4*>(a.o + o_off) = out;
     }
     if (a.lse && c4 == 0)
       a.lse[row_id] = empty ? -INFINITY : (M + __builtin_amdgcn_logf(L)) * 0.69314718055994530942f;

@@ -24,7 +24,9 @@ constexpr size_t kWsAlign = 256;
 
 struct Shape {
   int in_dtype, o_dtype;
+  int layout;                            // SMA_LAYOUT_*
   size_t batch, heads, seq_q, seq_kv, d;
+  size_t row_elems;                      // elements between consecutive rows of one head
   size_t bh, rows;                       // batch*heads, batch*heads*seq_q
   size_t q_bytes, kv_bytes, o_bytes, lse_bytes;
 };
@@ -39,7 +41,8 @@ size_t elem_bytes(int dt) { return dt == SMA_DTYPE_F32 ? 4 : 2; }
 
 // Checks that do not depend on pointers. Fills sh on success.
 int check_shape(int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
-                size_t d, double scale, Shape* sh) {
+                size_t d, double scale, Shape* sh, int layout = SMA_LAYOUT_BHSD) {
+  if (layout != SMA_LAYOUT_BHSD && layout != SMA_LAYOUT_BSHD) return SMA_ERR_INVALID_VALUE;
   if (in_dtype != SMA_DTYPE_F32 && in_dtype != SMA_DTYPE_BF16 && in_dtype != SMA_DTYPE_F16)
     return SMA_ERR_INVALID_VALUE;
   if (o_dtype != SMA_DTYPE_F32 && o_dtype != SMA_DTYPE_BF16 && o_dtype != SMA_DTYPE_F16)
@@ -49,6 +52,7 @@ int check_shape(int in_dtype, int o_dtype, size_t batch, size_t heads, size_t se
   Shape s{};
   s.in_dtype = in_dtype;
   s.o_dtype = o_dtype;
+  s.layout = layout;
   s.batch = batch;
   s.heads = heads;
   s.seq_q = seq_q;
@@ -63,9 +67,11 @@ int check_shape(int in_dtype, int o_dtype, size_t batch, size_t heads, size_t se
   if (d != 64 && d != 128) return SMA_ERR_UNSUPPORTED;
   if (o_dtype == SMA_DTYPE_F16) return SMA_ERR_UNSUPPORTED;
   if (seq_q > kMaxSeq || seq_kv > kMaxSeq || s.bh > (size_t(1) << 31)) return SMA_ERR_UNSUPPORTED;
+  if (heads > (size_t(1) << 20)) return SMA_ERR_UNSUPPORTED;
+  s.row_elems = layout == SMA_LAYOUT_BSHD ? heads * d : d;
   // The 16-bit kernel addresses one (batch, head)'s K and V through 32-bit
   // buffer offsets: keep them, with a tile of slack, below 2^31 bytes.
-  if (in_dtype != SMA_DTYPE_F32 && (seq_kv + 256) * d * 2 > (size_t(1) << 31))
+  if (in_dtype != SMA_DTYPE_F32 && (seq_kv + 256) * s.row_elems * 2 > (size_t(1) << 31))
     return SMA_ERR_UNSUPPORTED;
   *sh = s;
   return SMA_OK;
@@ -125,7 +131,7 @@ constexpr size_t kKsplitAlwaysKeys = 512;
 // through 32-bit buffer offsets: keep them, with a tile of slack, below 2^31.
 bool ksplit_fits(const Shape& s) {
   const size_t lim = size_t(1) << 31;
-  return (s.seq_q + 32) * s.d * 4 <= lim && (s.seq_kv + 32) * s.d * 4 <= lim;
+  return (s.seq_q + 32) * s.row_elems * 4 <= lim && (s.seq_kv + 32) * s.row_elems * 4 <= lim;
 }
 
 int auto_kernel(const Shape& s, int num_cus) {
@@ -201,8 +207,9 @@ int check_pointers(const Shape& s, const void* q, const void* k, const void* v, 
 
 int validate_all(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
-                 size_t d, double scale, const void* ws, size_t ws_bytes, Shape* sh) {
-  int st = check_shape(in_dtype, o_dtype, batch, heads, seq_q, seq_kv, d, scale, sh);
+                 size_t d, double scale, const void* ws, size_t ws_bytes, Shape* sh,
+                 int layout = SMA_LAYOUT_BHSD) {
+  int st = check_shape(in_dtype, o_dtype, batch, heads, seq_q, seq_kv, d, scale, sh, layout);
   if (st != SMA_OK) return st;
   if (sh->rows == 0) return SMA_OK;
   st = check_pointers(*sh, q, k, v, o, lse, ws, ws_bytes);
@@ -287,12 +294,12 @@ int sma_attention_fwd_plan(int in_dtype, size_t batch, size_t heads, size_t seq_
 
 int sma_attention_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                          int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
-                         size_t seq_kv, size_t head_dim, double scale, int causal, void* workspace,
-                         size_t workspace_bytes, const sma_plan* plan, void* stream,
-                         void* event_before, void* event_after) {
+                         size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
+                         void* workspace, size_t workspace_bytes, const sma_plan* plan,
+                         void* stream, void* event_before, void* event_after) {
   Shape sh;
   int st = validate_all(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv, head_dim,
-                        scale, workspace, workspace_bytes, &sh);
+                        scale, workspace, workspace_bytes, &sh, layout);
   if (st != SMA_OK) return st;
   if (plan) {
     if (plan->nsplit < 1 || plan->nsplit > kMaxSplits) return SMA_ERR_INVALID_VALUE;
@@ -331,6 +338,19 @@ int sma_attention_fwd_ex(const void* q, const void* k, const void* v, void* o, f
   a.c = (float)(std::fabs(scale) * 1.44269504088896340736);  // |scale| * log2(e), one rounding
   a.negate_q = scale < 0.0 ? 1 : 0;
   a.nwg = (uint32_t)p.nwg;
+  a.heads = (int64_t)heads;
+  if (layout == SMA_LAYOUT_BSHD) {  // element (b, s, h, c) at ((b*S + s)*H + h)*d + c
+    a.qs_b = (int64_t)(seq_q * heads * head_dim);
+    a.kvs_b = (int64_t)(seq_kv * heads * head_dim);
+    a.qs_h = a.kvs_h = (int64_t)head_dim;
+    a.qs_s = a.kvs_s = (int64_t)(heads * head_dim);
+  } else {  // element (b, h, s, c) at ((b*H + h)*S + s)*d + c
+    a.qs_b = (int64_t)(heads * seq_q * head_dim);
+    a.kvs_b = (int64_t)(heads * seq_kv * head_dim);
+    a.qs_h = (int64_t)(seq_q * head_dim);
+    a.kvs_h = (int64_t)(seq_kv * head_dim);
+    a.qs_s = a.kvs_s = (int64_t)head_dim;
+  }
   const bool o16 = o_dtype == SMA_DTYPE_BF16;
   if (p.nsplit == 1) {
     if (o16) a.o_bf16 = static_cast<unsigned short*>(o);
@@ -363,6 +383,11 @@ int sma_attention_fwd_ex(const void* q, const void* k, const void* v, void* o, f
     ca.lse = lse;
     ca.rows = (int64_t)sh.rows;
     ca.nsplit = p.nsplit;
+    ca.seq_q = (int32_t)seq_q;
+    ca.heads = a.heads;
+    ca.os_b = a.qs_b;
+    ca.os_h = a.qs_h;
+    ca.os_s = a.qs_s;
     e = sma::launch_combine(ca, d, s);
     if (e != hipSuccess) return SMA_ERR_HIP;
   }
@@ -375,8 +400,8 @@ int sma_attention_fwd_timed(const void* q, const void* k, const void* v, void* o
                             void* workspace, size_t workspace_bytes, void* stream,
                             void* event_before, void* event_after) {
   return sma_attention_fwd_ex(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv,
-                              head_dim, scale, causal, workspace, workspace_bytes, nullptr, stream,
-                              event_before, event_after);
+                              head_dim, scale, causal, SMA_LAYOUT_BHSD, workspace, workspace_bytes,
+                              nullptr, stream, event_before, event_after);
 }
 
 int sma_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -384,8 +409,17 @@ int sma_attention_fwd(const void* q, const void* k, const void* v, void* o, floa
                       size_t seq_kv, size_t head_dim, double scale, int causal, void* workspace,
                       size_t workspace_bytes, void* stream) {
   return sma_attention_fwd_ex(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv,
-                              head_dim, scale, causal, workspace, workspace_bytes, nullptr, stream,
-                              nullptr, nullptr);
+                              head_dim, scale, causal, SMA_LAYOUT_BHSD, workspace, workspace_bytes,
+                              nullptr, stream, nullptr, nullptr);
+}
+
+int sma_attention_fwd_layout(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
+                             size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return sma_attention_fwd_ex(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv,
+                              head_dim, scale, causal, layout, workspace, workspace_bytes, nullptr,
+                              stream, nullptr, nullptr);
 }
 
 // ---------------------------------------------------------------- backward

@@ -26,6 +26,12 @@ struct FwdArgs {
   float c;           // |scale| * log2(e), rounded once to fp32
   int32_t negate_q;  // scale < 0: the kernel multiplies by -q and |scale|
   uint32_t nwg;      // bh * nqb * nsplit workgroups
+  // Element strides (the head dim is contiguous): (batch, head, row) of Q and
+  // O, and of K and V. [B,H,S,d] gives (H*S*d, S*d, d); [B,S,H,d] gives
+  // (S*H*d, d, H*d).
+  int64_t heads;
+  int64_t qs_b, qs_h, qs_s;
+  int64_t kvs_b, kvs_h, kvs_s;
 };
 
 // Arguments of the split-combine launch.
@@ -37,6 +43,9 @@ struct CombineArgs {
   float* lse;            // [rows] natural log, may be null
   int64_t rows;          // bh * seq_q
   int32_t nsplit;
+  int32_t seq_q;
+  int64_t heads;         // O's strides, as FwdArgs
+  int64_t os_b, os_h, os_s;
 };
 
 // Arguments of the attention-backward launches (fp32 inputs and gradients).

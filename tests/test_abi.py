@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert sma.abi_version() == 1
+    assert sma.abi_version() == 2
     for st in range(7):
         assert sma.status_string(st).startswith(sma.STATUS_NAMES[st])
     assert sma.status_string(99) == "unknown sma status"
@@ -198,11 +198,11 @@ def test_plan_rejects():
     assert lib.sma_attention_fwd_plan(F32, 1, 1, 8, 8, 64, 0, -1, 0, 256, None) == NULLP
 
 
-def _ex(plan, q=Q, o=O, idt=F32, ws=None, wsb=0):
+def _ex(plan, q=Q, o=O, idt=F32, ws=None, wsb=0, layout=0, H=2, skv=128):
     # Error paths only: every one returns before the library touches a device.
-    return sma.library().sma_attention_fwd_ex(q, K, V, o, L, idt, F32, 1, 2, 128, 128, 64, 0.125,
-                                              1, ws, wsb, ctypes.byref(plan) if plan else None,
-                                              None, None, None)
+    return sma.library().sma_attention_fwd_ex(q, K, V, o, L, idt, F32, 1, H, 128, skv, 64, 0.125,
+                                              1, layout, ws, wsb,
+                                              ctypes.byref(plan) if plan else None, None, None, None)
 
 
 def test_ex_rejects_bad_plans_before_launch():
@@ -277,3 +277,20 @@ def test_backward_workspace_and_host_checks():
     assert call(ws=ws + 8) == MISAL
     assert call(dq=q) == ALIAS and call(dv=dk + 16) == ALIAS and call(ws=lse) == ALIAS
     assert call(dk=o + 64) == ALIAS and call(ws=dq + 256) == ALIAS
+
+
+def test_layout_argument_and_its_limits():
+    """Layout codes other than BHSD/BSHD are invalid; under BSHD the 2 GiB offset limits apply to
+    rows heads*head_dim apart, so the in-workgroup key-split kernel stops fitting at 1/heads
+    the sequence length."""
+    ks = sma.Plan(kernel=sma.SMA_KERNEL_F32_KSPLIT, nsplit=1)
+    assert _ex(ks, layout=2) == INVAL and _ex(ks, layout=-1) == INVAL
+    assert _ex(ks, layout=1, q=None) == NULLP  # valid layout: the next check fails
+    # 64 heads x d 64 x 4 B = 16 KiB per row: (skv + 32) rows stay below 2 GiB up to skv = 131040
+    assert _ex(ks, layout=1, H=64, skv=131041) == UNSUP
+    lib = sma.library()
+    b = [0x10_0000_0000 * i for i in range(1, 6)]
+    assert lib.sma_attention_fwd_layout(b[0], b[1], b[2], b[3], b[4], F32, F32, 1, 2, 8, 8, 64, 0.1, 0,
+                                        5, None, 0, None) == INVAL
+    assert lib.sma_attention_fwd_layout(None, b[1], b[2], b[3], b[4], F32, F32, 1, 2, 8, 8, 64, 0.1, 0,
+                                        1, None, 0, None) == NULLP
