@@ -6,9 +6,11 @@ max-subtracted softmax and log-sum-exp as on the pulsatrix HIPBackend page,
 and the empty-row convention of the TorchLean hard-masked softmax) and of the
 row primitives on a materialised score matrix (rows_oracle.c: pulsatrix
 ``softmax_rows`` / ``logsumexp_rows``, the TorchLean hard-masked softmax and
-MicroGPT's fused scale + causal mask + softmax), and the gradients of the
+MicroGPT's fused scale + causal mask + softmax), the gradients of the
 attention forward (attention_bwd_oracle.c: the chain rule through the
-softmax, recomputed from q, k, v and the upstream gradient).
+softmax, recomputed from q, k, v and the upstream gradient), and the forward
+with an explicit hard mask (attention_masked_oracle.c: the TorchLean
+hard-masked softmax inside the attention).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package. The attention library never does, and
@@ -24,7 +26,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRCS = [os.path.join(_HERE, "attention_oracle.c"), os.path.join(_HERE, "rows_oracle.c"),
-         os.path.join(_HERE, "attention_bwd_oracle.c")]
+         os.path.join(_HERE, "attention_bwd_oracle.c"), os.path.join(_HERE, "attention_masked_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
@@ -61,6 +63,9 @@ def _bind(lib):
     lib.oracle_attention_bwd.restype = ctypes.c_int
     lib.oracle_attention_bwd_bound.argtypes = lib.oracle_attention_bwd.argtypes
     lib.oracle_attention_bwd_bound.restype = ctypes.c_int
+    lib.oracle_attention_fwd_masked.argtypes = [dp, dp, dp, dp, L, L, L, L, L, L, L, ctypes.c_double,
+                                                ctypes.c_int, dp, dp]
+    lib.oracle_attention_fwd_masked.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -158,6 +163,29 @@ def attention_bwd_bound(q, k, v, dout, scale: float, causal: bool, lib=None):
     if rc != 0:
         raise ValueError("oracle_attention_bwd_bound rejected its arguments")
     return mq, mk, mv
+
+
+def attention_fwd_masked(q, k, v, mask, scale: float, causal: bool, lib=None):
+    """O and LSE (float64) with a hard mask: mask is [B or 1, H or 1, Sq, Skv], nonzero admits
+    (combined with the causal bound when causal)."""
+    lib = lib or load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    assert k.shape == (B, H, Skv, D) and v.shape == (B, H, Skv, D)
+    m = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+    if m.ndim != 4 or m.shape[2:] != (Sq, Skv) or m.shape[0] not in (1, B) or m.shape[1] not in (1, H):
+        raise ValueError(f"mask shape {m.shape} does not broadcast to {(B, H, Sq, Skv)}")
+    sh = Sq * Skv if m.shape[1] == H else 0
+    sb = m.shape[1] * Sq * Skv if m.shape[0] == B else 0
+    o = np.empty((B, H, Sq, D), dtype=np.float64)
+    lse = np.empty((B, H, Sq), dtype=np.float64)
+    rc = lib.oracle_attention_fwd_masked(q.ctypes.data, k.ctypes.data, v.ctypes.data, m.ctypes.data,
+                                         sb, sh, B, H, Sq, Skv, D, float(scale), int(bool(causal)),
+                                         o.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_attention_fwd_masked rejected its arguments")
+    return o, lse
 
 
 def _rows2d(x):
