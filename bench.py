@@ -412,6 +412,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(gen_workloads()))
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"],
                     help="element type of the attention output O (bf16: rounded to nearest even)")
+    ap.add_argument("--mask-density", type=float, default=None,
+                    help="apply a hard mask [1,1,Sq,Skv] admitting each pair with this probability")
     ap.add_argument("--layout", default="bhsd", choices=["bhsd", "bshd"],
                     help="memory layout of q, k, v and O: [B,H,S,d] or [B,S,H,d]")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -467,7 +469,14 @@ def main():
     out = torch.empty(o_shape, dtype=torch.bfloat16 if o16 else torch.float32, device="cuda")
     o_dt = sma.SMA_DTYPE_BF16 if o16 else sma.SMA_DTYPE_F32
     lse = torch.empty((B, H, sq), dtype=torch.float32, device="cuda")
-    ws_n = sma.workspace_bytes(in_dt, B, H, sq, skv, d, w.causal)
+    masked = args.mask_density is not None
+    if masked:
+        mask_np = gen.bernoulli_mask(w.seed, (1, 1, sq, skv), args.mask_density)
+        tmask = torch.from_numpy(mask_np).to("cuda")
+        ws_n = sma.library().sma_attention_fwd_masked_workspace_bytes(in_dt, B, H, sq, skv, d,
+                                                                      int(w.causal), lay, 1, 1)
+    else:
+        ws_n = sma.workspace_bytes(in_dt, B, H, sq, skv, d, w.causal)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
@@ -477,7 +486,11 @@ def main():
             o_dt, B, H, sq, skv, d, w.scale, w.causal, ws.data_ptr(), ws_n)
 
     def run(e0=None, e1=None):
-        sma.attention_fwd_ex_raw(*call, None, sptr, e0, e1, layout=lay)
+        if masked:
+            sma.attention_fwd_masked_raw(*call[:5], tmask.data_ptr(), 1, 1, *call[5:14], lay, *call[14:],
+                                         None, sptr, e0, e1)
+        else:
+            sma.attention_fwd_ex_raw(*call, None, sptr, e0, e1, layout=lay)
 
     for _ in range(args.warmup):
         run()
@@ -486,7 +499,7 @@ def main():
     # loop (events around every launch would add their own gaps to each
     # measured launch); a step with a split-combine kernel records events around
     # every main-kernel launch instead, so that the main kernel is timed alone.
-    per_launch = plan.nsplit > 1
+    per_launch = plan.nsplit > 1 or masked
     if per_launch:
         ev_a = [ev.create() for _ in range(args.steps)]
         ev_b = [ev.create() for _ in range(args.steps)]
@@ -517,7 +530,7 @@ def main():
     exact = 4.0 * d * allowed_pairs(w)
     achieved = exact / (k_avg * 1e-3) / 1e12
     # the committed counter passes were taken with fp32 output in [B,H,S,d]
-    traffic = None if (o16 or args.layout != "bhsd") else read_traffic(KERNEL_FUNCTIONS[plan.kernel], w.name,
+    traffic = None if (o16 or masked or args.layout != "bhsd") else read_traffic(KERNEL_FUNCTIONS[plan.kernel], w.name,
                                             kernel_source_digest(KERNEL_FUNCTIONS[plan.kernel]))
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -527,7 +540,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_q": sq, "seq_kv": skv,
                    "head_dim": d, "causal": w.causal, "scale": w.scale,
                    "input_dtype": w.dtype, "accumulate": "f32", "output": args.out_dtype, "lse": True,
-                   "layout": args.layout,
+                   "layout": args.layout, "mask_density": args.mask_density,
                    "key_splits_workspace_bytes": ws_n},
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
@@ -543,8 +556,32 @@ def main():
                      "min_hbm_bytes_per_launch": min_bytes(w, 2 if o16 else 4)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, vals, args.cpu_seconds)
+        line["cpu_baseline"] = (masked_cpu_baseline(w, vals, mask_np, args.cpu_seconds) if masked
+                                else cpu_baseline(w, vals, args.cpu_seconds))
     print(json.dumps(line), flush=True)
+
+
+def masked_cpu_baseline(w, vals, mask, target_s: float):
+    """The masked oracle on a bounded random sample of whole (batch, head) slices."""
+    import oracle
+
+    bh = w.batch * w.heads
+    q, k, v = (x.reshape(bh, 1, x.shape[2], x.shape[3]) for x in vals)
+    order = np.random.default_rng(0).permutation(bh)
+    threads = max(1, oracle.num_threads())
+    n, passes = min(bh, threads), 0
+    t0 = time.perf_counter()
+    while True:
+        ids = np.sort(order[:n])
+        oracle.attention_fwd_masked(q[ids], k[ids], v[ids], mask, w.scale, w.causal)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s or passes >= 1000:
+            break
+    return {"value": metric_flops(w) * n / bh * passes / dt / 1e12, "unit": "TFLOP/s",
+            "cores": min(threads, n), "kind": "oracle",
+            "sample": f"{n} of {bh} (batch, head) slices chosen at random (seed 0), every row of each, "
+                      f"{passes} pass(es) in {dt:.1f} s; metric FLOPs scaled by the slice fraction"}
 
 
 if __name__ == "__main__":

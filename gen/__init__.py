@@ -62,7 +62,7 @@ GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 STREAM_STRIDE = 1 << 40
-TENSOR_STREAM = {"q": 0, "k": 1, "v": 2, "dout": 3}
+TENSOR_STREAM = {"q": 0, "k": 1, "v": 2, "dout": 3, "mask": 4}
 
 _CHUNK = 1 << 22  # elements per vectorised block; bounds temporaries to ~100 MB
 
@@ -300,3 +300,10 @@ def random_case(seed: int, shape_q, shape_kv, sigma_qk=1.0, sigma_v=1.0, dtype="
 def upstream_grad(seed: int, shape, sigma: float = 1.0) -> np.ndarray:
     """The upstream gradient dL/dO of a backward case: N(0, sigma^2) float32 on its own stream."""
     return tensor_f32(seed, "dout", tuple(shape), sigma)
+
+
+def bernoulli_mask(seed: int, shape, density: float) -> np.ndarray:
+    """A uint8 0/1 mask of the given shape: entry n is 1 iff uniform(seed, mask stream + n) < density."""
+    n = int(np.prod(shape, dtype=np.int64))
+    u = uniform24(seed, np.uint64(TENSOR_STREAM["mask"] * STREAM_STRIDE) + np.arange(n, dtype=np.uint64))
+    return (u < density).astype(np.uint8).reshape(tuple(shape))

@@ -199,6 +199,44 @@ int sma_attention_fwd_layout(const void* q, const void* k, const void* v, void* 
                              size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------ hard mask
+ *
+ * sma_attention_fwd_ex with an explicit hard mask, as the TorchLean page's
+ * stable row-wise hard-masked softmax defines it: key j takes part in query
+ * row i's max and sum only if mask byte (b, h, i, j) is nonzero (and, with
+ * `causal`, j <= i + seq_kv - seq_q as well); blocked keys weigh exactly zero
+ * and are never read into the arithmetic; a row that admits nothing is +0.0
+ * with LSE -inf.
+ *
+ *   mask           device bytes [mask_batches][mask_heads][seq_q][seq_kv],
+ *                  contiguous; mask_batches is 1 or batch and mask_heads 1 or
+ *                  heads (1 broadcasts the mask over that dimension). Must not
+ *                  overlap o, lse or the workspace (ALIASING).
+ *   workspace      required: the mask packed to one bit per pair (4 bytes per
+ *                  32 keys of a row, 256-byte aligned) comes first, else
+ *                  INVALID_VALUE; a key split across workgroups uses the bytes
+ *                  after it (too few of them only disables the library's split,
+ *                  as for sma_attention_fwd). sma_attention_fwd_masked_workspace_bytes
+ *                  gives both.
+ *   plan           as for sma_attention_fwd_ex: every kernel applies the mask.
+ * Everything else as for sma_attention_fwd_ex. mask NULL with nonzero
+ * mask_batches or mask_heads -> NULL_POINTER (when there is work); a mask
+ * with mask_batches = mask_heads = 0 is INVALID_VALUE. */
+int sma_attention_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const void* mask, size_t mask_batches, size_t mask_heads, int in_dtype,
+                             int o_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
+                             size_t head_dim, double scale, int causal, int layout, void* workspace,
+                             size_t workspace_bytes, const sma_plan* plan, void* stream,
+                             void* event_before, void* event_after);
+
+/* Workspace bytes sma_attention_fwd_masked needs: the packed mask plus the
+ * library's key split on the current HIP device (256 CUs assumed if it cannot
+ * be queried); 0 for invalid arguments. */
+size_t sma_attention_fwd_masked_workspace_bytes(int in_dtype, size_t batch, size_t heads,
+                                                size_t seq_q, size_t seq_kv, size_t head_dim,
+                                                int causal, int layout, size_t mask_batches,
+                                                size_t mask_heads);
+
 /* ------------------------------------------------------------------ backward
  *
  * Gradients of the forward above with respect to q, k and v, given the

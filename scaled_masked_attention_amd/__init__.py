@@ -83,6 +83,12 @@ def library():
         lib.sma_attention_fwd_ex.restype = ctypes.c_int
         lib.sma_attention_fwd_layout.argtypes = fwd[:14] + [ctypes.c_int] + fwd[14:17]
         lib.sma_attention_fwd_layout.restype = ctypes.c_int
+        lib.sma_attention_fwd_masked.argtypes = (fwd[:5] + [vp, sz, sz] + fwd[5:14] + [ctypes.c_int] +
+                                                 fwd[14:16] + [ctypes.POINTER(Plan), vp, vp, vp])
+        lib.sma_attention_fwd_masked.restype = ctypes.c_int
+        lib.sma_attention_fwd_masked_workspace_bytes.argtypes = [ctypes.c_int, sz, sz, sz, sz, sz,
+                                                                 ctypes.c_int, ctypes.c_int, sz, sz]
+        lib.sma_attention_fwd_masked_workspace_bytes.restype = sz
         fp = ctypes.c_void_p
         lib.sma_softmax_rows.argtypes = [fp, fp, sz, sz, vp]
         lib.sma_logsumexp_rows.argtypes = [fp, fp, sz, sz, vp]
@@ -173,8 +179,22 @@ def attention_fwd_ex_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dtype,
                                           stream, event_before, event_after))
 
 
+def attention_fwd_masked_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, mask_ptr, mask_batches, mask_heads,
+                             in_dtype, o_dtype, batch, heads, seq_q, seq_kv, head_dim, scale, causal,
+                             layout, ws_ptr, ws_bytes, plan_, stream, event_before=None,
+                             event_after=None) -> None:
+    """sma_attention_fwd_masked on raw addresses; raises SMAError on a non-zero status."""
+    _raise(library().sma_attention_fwd_masked(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, mask_ptr,
+                                              mask_batches, mask_heads, in_dtype, o_dtype, batch,
+                                              heads, seq_q, seq_kv, head_dim, float(scale),
+                                              int(bool(causal)), int(layout), ws_ptr, ws_bytes,
+                                              ctypes.byref(plan_) if plan_ is not None else None,
+                                              stream, event_before, event_after))
+
+
 def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=None,
-                  workspace=None, stream=None, kernel=None, nsplit=0, out_dtype=None, layout="bhsd"):
+                  workspace=None, stream=None, kernel=None, nsplit=0, out_dtype=None, layout="bhsd",
+                  mask=None):
     """O = softmax(scale * Q K^T + mask) V on the GPU.
 
     q [B,H,Sq,D], k and v [B,H,Skv,D]: contiguous torch tensors on the current
@@ -184,7 +204,9 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
     (float32, [B,H,Sq]).
     scale=None means 1/sqrt(D). causal uses the bottom-right alignment.
     layout="bshd" takes q [B,Sq,H,D], k and v [B,Skv,H,D] and returns O in that
-    layout (LSE stays [B,H,Sq]).
+    layout (LSE stays [B,H,Sq]). mask: a bool or uint8 tensor [Sq,Skv] or
+    [B or 1, H or 1, Sq, Skv] on the device; key j is admitted to row i only
+    where it is nonzero (and, with causal, under the causal bound too).
     kernel (an SMA_KERNEL_* code) and nsplit force a plan; by default the
     library chooses. A forced split gets a workspace of the size it needs.
     """
@@ -245,17 +267,39 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
         forced = plan(in_dt, B, H, Sq, Skv, D, causal, kernel, nsplit)
         need = forced.workspace_bytes
     else:
-        need = workspace_bytes(in_dt, B, H, Sq, Skv, D, causal)
+        need = 0 if mask is not None else workspace_bytes(in_dt, B, H, Sq, Skv, D, causal)
+    if mask is not None:
+        if not isinstance(mask, torch.Tensor) or mask.dtype not in (torch.bool, torch.uint8):
+            raise ValueError("mask must be a bool or uint8 torch tensor")
+        if mask.dim() == 2:
+            mask = mask.view(1, 1, *mask.shape)
+        if (mask.dim() != 4 or tuple(mask.shape[2:]) != (Sq, Skv) or mask.shape[0] not in (1, B)
+                or mask.shape[1] not in (1, H)):
+            raise ValueError(f"mask shape {tuple(mask.shape)} does not broadcast to {(B, H, Sq, Skv)}")
+        if mask.device != dev or not mask.is_contiguous():
+            raise ValueError(f"mask must be a contiguous tensor on {dev}")
+        mb, mh = mask.shape[0], mask.shape[1]
+        need += library().sma_attention_fwd_masked_workspace_bytes(in_dt, B, H, Sq, Skv, D,
+                                                                   int(bool(causal)),
+                                                                   LAYOUTS[layout], mb, mh)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
         stream = torch.cuda.current_stream()
-    attention_fwd_ex_raw(q.data_ptr(), k.data_ptr() if Skv else None, v.data_ptr() if Skv else None,
-                         out.data_ptr(), lse.data_ptr() if lse is not None else None, in_dt,
-                         o_dt, B, H, Sq, Skv, D, scale, causal, ws_ptr, ws_bytes, forced,
-                         stream.cuda_stream, layout=LAYOUTS[layout])
+    if mask is not None:
+        attention_fwd_masked_raw(q.data_ptr(), k.data_ptr() if Skv else None,
+                                 v.data_ptr() if Skv else None, out.data_ptr(),
+                                 lse.data_ptr() if lse is not None else None,
+                                 mask.data_ptr() if mask.numel() else None, mb, mh, in_dt, o_dt, B, H,
+                                 Sq, Skv, D, scale, causal, LAYOUTS[layout], ws_ptr, ws_bytes, forced,
+                                 stream.cuda_stream)
+    else:
+        attention_fwd_ex_raw(q.data_ptr(), k.data_ptr() if Skv else None, v.data_ptr() if Skv else None,
+                             out.data_ptr(), lse.data_ptr() if lse is not None else None, in_dt,
+                             o_dt, B, H, Sq, Skv, D, scale, causal, ws_ptr, ws_bytes, forced,
+                             stream.cuda_stream, layout=LAYOUTS[layout])
     return (out, lse) if return_lse else out
 
 

@@ -103,13 +103,17 @@ __device__ __forceinline__ int v_swz(int r) {
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-template <int D, bool CAUSAL, bool F16>
+template <int D, bool CAUSAL, bool F16, bool MASKED>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   using G = BGeom<D>;
   using H = Half<F16>;
   using V8 = typename H::V8;
   __shared__ __attribute__((aligned(16))) u32x4 k_lds[G::kSlots][G::kTileChunks];
   __shared__ __attribute__((aligned(16))) u32x4 v_lds[G::kSlots][G::kTileChunks];
+  // With a hard mask: per ring slot, each wave's two mask words (64 keys) for
+  // its 32 rows, word w of row r at [w * 32 + r].
+  __shared__ uint32_t mask_lds[MASKED ? G::kSlots : 1][MASKED ? G::kWaves : 1][64];
+  constexpr int kMaskOps = MASKED ? 1 : 0;  // loads per wave per tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -174,9 +178,18 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
                               16u * (unsigned)(pc ^ k_swz<D>(rho0));
   const unsigned v_lane_ofs = (unsigned)rho0 * kv_row + 16u * (unsigned)(pc ^ v_swz<D>(rho0));
 
+  __amdgpu_buffer_rsrc_t m_rsrc;
+  if (MASKED)
+    m_rsrc = raw_buffer(a.mask_bits + head_offset(t.bh, a.heads, a.mbits_sb, a.mbits_sh),
+                        (unsigned)a.seq_q * (unsigned)a.mask_words * 4u);
   auto issue_tile = [&](int32_t T) {
     const unsigned row0 = (unsigned)(ks + T * G::kK);
     const int slot = T % G::kSlots;
+    if (MASKED)  // words (ks + 64T)/32 + {0, 1} of this wave's rows (rows past seq_q read as 0)
+      dma_load_x1(m_rsrc,
+                  ((unsigned)(qw0 + (lane & 31)) * (unsigned)a.mask_words + row0 / 32u +
+                   (unsigned)(lane >> 5)) * 4u,
+                  lds_address(&mask_lds[MASKED ? slot : 0][MASKED ? wave : 0][0]));
 #pragma unroll
     for (int u = 0; u < G::kLoadsPerThread; ++u) {
       const int base = (u * G::kWaves + wave) * 64;
@@ -244,15 +257,25 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
     }
 
     // Row max of the raw scores (scale > 0 after the sign fold), masked keys excluded.
-    const bool need_mask = j0 + G::kK > wave_lo;
+    const bool need_mask = MASKED || j0 + G::kK > wave_lo;
     const int32_t rel = lim - j0 - 8 * lh;  // key 32kb + 16(r/8) + r%8 allowed iff < rel
+    uint32_t mword[G::kKB];
+#pragma unroll
+    for (int kb = 0; kb < G::kKB; ++kb)
+      mword[kb] = MASKED ? mask_lds[MASKED ? slot : 0][MASKED ? wave : 0][32 * kb + lm] : ~0u;
+    // Key 32kb + 16(r/8) + 8h + r%8 of the tile: under the causal/length bound, and
+    // admitted by the mask (bit 16(r/8) + 8h + r%8 of word kb).
+    auto admitted = [&](int kb, int r) {
+      return (32 * kb + 16 * (r / 8) + (r % 8) < rel) &&
+             (!MASKED || ((mword[kb] >> (16 * (r / 8) + 8 * lh + (r % 8))) & 1u));
+    };
     float mx = -INFINITY;
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < G::kKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          mx = (32 * kb + 16 * (r / 8) + (r % 8) < rel) ? fmaxf(mx, sacc[kb][r]) : mx;
+          mx = admitted(kb, r) ? fmaxf(mx, sacc[kb][r]) : mx;
     } else {
 #pragma unroll
       for (int kb = 0; kb < G::kKB; ++kb)
@@ -283,7 +306,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * t2 + e], c, neg_m));
-            p = (32 * kb + 16 * t2 + e) < rel ? p : 0.f;
+            p = admitted(kb, 8 * t2 + e) ? p : 0.f;
             psum += p;
             pb[kb][t2][e] = (typename H::E)p;
           }
@@ -313,7 +336,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   if (ntiles > 0) issue_tile(0);
   if (ntiles > 1) issue_tile(1);
   for (int32_t T = 0; T < ntiles; ++T) {
-    if (T + 1 < ntiles) wait_vmcnt<G::kLoadsPerTile>();
+    if (T + 1 < ntiles) wait_vmcnt<G::kLoadsPerTile + kMaskOps>();
     else wait_vmcnt<0>();
     __syncthreads();
     if (T + 2 < ntiles) issue_tile(T + 2);
@@ -375,10 +398,14 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_bf16_variant(const FwdArgs& a, bool f16, hipStream_t s) {
-  if (f16)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, true>), dim3(a.nwg), dim3(BGeom<D>::kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, false>), dim3(a.nwg), dim3(BGeom<D>::kThreads), 0, s, a);
+  const dim3 grid(a.nwg), block(BGeom<D>::kThreads);
+  if (a.mask_bits) {
+    if (f16) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, false, true>), grid, block, 0, s, a);
+  } else {
+    if (f16) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, false, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ struct FVec<4> { typedef f32x4 T; };
 // numerator and denominator share the stale max.
 constexpr float kTau = 8.0f;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   using G = F32Geom<D>;
   using VecN = typename FVec<G::kNch>::T;
@@ -107,6 +107,11 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   }
 
   const int64_t kv_off = head_offset(t.bh, a.heads, a.kvs_b, a.kvs_h);
+  // With a hard mask: this row's packed admission words (one per 32 keys).
+  const uint32_t* mrow = nullptr;
+  if (MASKED)
+    mrow = a.mask_bits + head_offset(t.bh, a.heads, a.mbits_sb, a.mbits_sh) +
+           (int64_t)ld_row * a.mask_words;
   const float* kg = static_cast<const float*>(a.k) + kv_off;
   const float* vg = static_cast<const float*>(a.v) + kv_off;
   f32x4 kreg[G::kF4PerThread], vreg[G::kF4PerThread];
@@ -176,6 +181,12 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
           const int32_t j = j0 + 8 * (r / 4) + 4 * lh + (r % 4);
           tv[r] = j < lim ? tv[r] : -INFINITY;
         }
+      }
+      if (MASKED) {
+        const uint32_t mword = mrow[j0 >> 5];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          tv[r] = (mword >> (8 * (r / 4) + 4 * lh + (r % 4))) & 1u ? tv[r] : -INFINITY;
       }
       float mx = tv[0];
 #pragma unroll
@@ -259,7 +270,10 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_f32_variant(const FwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL>), dim3(a.nwg), dim3(kThreadsPerWG), 0, s, a);
+  if (a.mask_bits)
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL, true>), dim3(a.nwg), dim3(kThreadsPerWG), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL, false>), dim3(a.nwg), dim3(kThreadsPerWG), 0, s, a);
   return hipGetLastError();
 }
 

@@ -59,7 +59,7 @@ struct WGeom {
   static_assert(kDmaPerTile % kWaves == 0, "the Q tile copy splits evenly over the waves");
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
   using G = WGeom<D>;
   using VecN = typename FVecW<G::kNch>::T;
@@ -67,6 +67,10 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[G::kLdsBytes];
   __shared__ float m_part[G::kWaves][G::kQ];
   __shared__ float l_part[G::kWaves][G::kQ];
+  // With a hard mask: each wave's copy of its current block's mask words (one
+  // per query row; the copy's upper 32 lanes repeat the lower ones).
+  __shared__ uint32_t mask_lds[MASKED ? G::kWaves : 1][64];
+  constexpr int kMaskOps = MASKED ? 1 : 0;  // loads issued with each K block
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -111,11 +115,18 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
       dma_load_x4(v_rsrc, row0 + tile_src_offset_linear<D>(t, lane, kv_row),
                   lds_address(v_slot + 1024 * t));
   };
+  __amdgpu_buffer_rsrc_t m_rsrc;
+  if (MASKED)
+    m_rsrc = raw_buffer(a.mask_bits + head_offset(bh, a.heads, a.mbits_sb, a.mbits_sh),
+                        (unsigned)a.seq_q * (unsigned)a.mask_words * 4u);
   auto copy_k_block = [&](int32_t b) {
     const unsigned row0 = (unsigned)(32 * b) * kv_row;
 #pragma unroll
     for (int t = 0; t < G::kDmaPerTile; ++t)
       dma_load_x4(k_rsrc, row0 + tile_src_offset<D>(t, lane, kv_row), lds_address(k_slot + 1024 * t));
+    if (MASKED)  // word b of rows q0 .. q0 + 31 (rows past seq_q read as 0)
+      dma_load_x1(m_rsrc, ((unsigned)(q0 + (lane & 31)) * (unsigned)a.mask_words + (unsigned)b) * 4u,
+                  lds_address(&mask_lds[MASKED ? wave : 0][0]));
   };
 
   // Q tile (the waves copy a quarter each) and this wave's first K and V blocks.
@@ -155,13 +166,15 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
 
   for (int32_t b = b_begin; b < b_end; ++b) {
     const int32_t j0 = 32 * b;
-    // K block b has landed (V block b may still be in flight: it was issued
-    // after K, and in-order completion lets the wait leave it outstanding).
+    // K block b (and its mask words) have landed; V block b may still be in
+    // flight: it was issued after them, and in-order completion lets the wait
+    // leave it outstanding.
     if (b > b_begin) wait_vmcnt<G::kDmaPerTile>();
     f32x4 kk[G::kSteps];
 #pragma unroll
     for (int u = 0; u < G::kSteps; ++u)
       kk[u] = *reinterpret_cast<const f32x4*>(k_slot + tile_operand_offset<D>(lm, lh, u));
+    const uint32_t mword = MASKED ? mask_lds[MASKED ? wave : 0][lm] : ~0u;
     if (b + 1 < b_end) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the K reads have returned
       copy_k_block(b + 1);
@@ -186,6 +199,11 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
         const int32_t j = j0 + 8 * (r / 4) + 4 * lh + (r % 4);
         tv[r] = j < lim ? tv[r] : -INFINITY;
       }
+    }
+    if (MASKED) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        tv[r] = (mword >> (8 * (r / 4) + 4 * lh + (r % 4))) & 1u ? tv[r] : -INFINITY;
     }
     float mx = tv[0];
 #pragma unroll
@@ -217,7 +235,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
     l_run += psum;
     // V block b: wait for its copy (only the K copy of block b+1 may remain
     // in flight), read the operands, then reuse the slot for block b+1.
-    if (b + 1 < b_end) wait_vmcnt<G::kDmaPerTile>();
+    if (b + 1 < b_end) wait_vmcnt<G::kDmaPerTile + kMaskOps>();
     else wait_vmcnt<0>();
     VecN vv[16];
 #pragma unroll
@@ -313,7 +331,10 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_wsplit_variant(const FwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_f32_wsplit_kernel<D, CAUSAL>), dim3(a.nwg), dim3(256), 0, s, a);
+  if (a.mask_bits)
+    hipLaunchKernelGGL((attn_fwd_f32_wsplit_kernel<D, CAUSAL, true>), dim3(a.nwg), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_f32_wsplit_kernel<D, CAUSAL, false>), dim3(a.nwg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

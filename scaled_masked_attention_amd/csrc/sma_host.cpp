@@ -240,6 +240,170 @@ int current_device_cus(int* out) {
 
 }  // namespace
 
+namespace {
+
+// An optional hard mask: bytes [batches][heads][seq_q][seq_kv], batches 1 or
+// B and heads 1 or H (broadcast), nonzero admitting.
+struct MaskArg {
+  const void* mask = nullptr;
+  size_t batches = 0, heads = 0;
+};
+
+size_t mask_words(size_t seq_kv) { return (seq_kv + 31) / 32; }
+
+// Workspace bytes for the packed mask bits (0 without a mask).
+size_t mask_bits_bytes(const Shape& s, const MaskArg& m) {
+  if (!m.mask) return 0;
+  return round_up(m.batches * m.heads * s.seq_q * mask_words(s.seq_kv) * 4, kWsAlign);
+}
+
+int check_mask(const Shape& s, const MaskArg& m, const void* o, const float* lse, const void* ws,
+               size_t ws_bytes) {
+  if (!m.mask) return SMA_OK;
+  if ((m.batches != 1 && m.batches != s.batch) || (m.heads != 1 && m.heads != s.heads))
+    return SMA_ERR_INVALID_VALUE;
+  size_t n;
+  if (!mul(m.batches * m.heads, s.seq_q, &n) || !mul(n, s.seq_kv, &n)) return SMA_ERR_INVALID_VALUE;
+  if (n > (size_t(1) << 40)) return SMA_ERR_UNSUPPORTED;
+  if (s.seq_q * mask_words(s.seq_kv) * 4 > (size_t(1) << 31)) return SMA_ERR_UNSUPPORTED;
+  if (overlap(o, s.o_bytes, m.mask, n) || overlap(lse, lse ? s.lse_bytes : 0, m.mask, n) ||
+      overlap(ws, ws ? ws_bytes : 0, m.mask, n))
+    return SMA_ERR_ALIASING;
+  return SMA_OK;
+}
+
+
+int fwd_core(const void* q, const void* k, const void* v, void* o, float* lse, int in_dtype,
+             int o_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv, size_t head_dim,
+             double scale, int causal, int layout, const MaskArg& mask, void* workspace,
+             size_t workspace_bytes, const sma_plan* plan, void* stream, void* event_before,
+             void* event_after) {
+  Shape sh;
+  int st = validate_all(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv, head_dim,
+                        scale, workspace, workspace_bytes, &sh, layout);
+  if (st != SMA_OK) return st;
+  const bool masked = mask.mask != nullptr;
+  if (masked || mask.batches || mask.heads) {
+    if (!masked && sh.rows > 0 && seq_kv > 0) return SMA_ERR_NULL_POINTER;
+    st = check_mask(sh, mask, o, lse, workspace, workspace_bytes);
+    if (st != SMA_OK) return st;
+  }
+  if (plan) {
+    if (plan->nsplit < 1 || plan->nsplit > kMaxSplits) return SMA_ERR_INVALID_VALUE;
+    if (plan->kernel != SMA_KERNEL_F32_QBLOCK && plan->kernel != SMA_KERNEL_F32_KSPLIT &&
+        plan->kernel != SMA_KERNEL_BF16_QBLOCK)
+      return SMA_ERR_INVALID_VALUE;
+    if (!kernel_fits_dtype(plan->kernel, in_dtype)) return SMA_ERR_UNSUPPORTED;
+    if (plan->kernel == SMA_KERNEL_F32_KSPLIT && (plan->nsplit > 1 || !ksplit_fits(sh)))
+      return SMA_ERR_UNSUPPORTED;
+  }
+  if (sh.rows == 0) return SMA_OK;
+  // The packed mask occupies the front of the workspace; a key split uses the rest.
+  const size_t bits_bytes = mask_bits_bytes(sh, mask);
+  if (masked && (!workspace || workspace_bytes < bits_bytes)) return SMA_ERR_INVALID_VALUE;
+  void* split_ws = workspace ? static_cast<char*>(workspace) + bits_bytes : nullptr;
+  const size_t split_ws_bytes = workspace ? workspace_bytes - bits_bytes : 0;
+  int cus = 0;
+  st = current_device_cus(&cus);
+  if (st != SMA_OK) return st;
+  Plan p;
+  if (plan) {
+    p = plan_for(sh, plan->kernel, (size_t)plan->nsplit, cus);
+    if (p.nsplit > 1 && (!split_ws || split_ws_bytes < p.ws_bytes)) return SMA_ERR_INVALID_VALUE;
+    if (p.nwg > kMaxWorkgroups) return SMA_ERR_UNSUPPORTED;
+  } else {
+    p = auto_plan(sh, cus);
+    if (p.nsplit > 1 && (!split_ws || split_ws_bytes < p.ws_bytes || p.nwg > kMaxWorkgroups))
+      p = plan_for(sh, p.kernel, 1, cus);
+  }
+
+  sma::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.bh = (int64_t)sh.bh;
+  a.seq_q = (int32_t)seq_q;
+  a.seq_kv = (int32_t)seq_kv;
+  a.nqb = p.nqb;
+  a.nsplit = p.nsplit;
+  a.split_len = p.split_len;
+  a.c = (float)(std::fabs(scale) * 1.44269504088896340736);  // |scale| * log2(e), one rounding
+  a.negate_q = scale < 0.0 ? 1 : 0;
+  a.nwg = (uint32_t)p.nwg;
+  a.heads = (int64_t)heads;
+  if (layout == SMA_LAYOUT_BSHD) {  // element (b, s, h, c) at ((b*S + s)*H + h)*d + c
+    a.qs_b = (int64_t)(seq_q * heads * head_dim);
+    a.kvs_b = (int64_t)(seq_kv * heads * head_dim);
+    a.qs_h = a.kvs_h = (int64_t)head_dim;
+    a.qs_s = a.kvs_s = (int64_t)(heads * head_dim);
+  } else {  // element (b, h, s, c) at ((b*H + h)*S + s)*d + c
+    a.qs_b = (int64_t)(heads * seq_q * head_dim);
+    a.kvs_b = (int64_t)(heads * seq_kv * head_dim);
+    a.qs_h = (int64_t)(seq_q * head_dim);
+    a.kvs_h = (int64_t)(seq_kv * head_dim);
+    a.qs_s = a.kvs_s = (int64_t)head_dim;
+  }
+  const bool o16 = o_dtype == SMA_DTYPE_BF16;
+  if (p.nsplit == 1) {
+    if (o16) a.o_bf16 = static_cast<unsigned short*>(o);
+    else a.o = static_cast<float*>(o);
+    a.lse = lse;
+  } else {
+    a.part_o = static_cast<float*>(split_ws);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(split_ws) + p.part_lse_off);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool c = causal != 0;
+  const int d = (int)head_dim;
+  hipError_t e;
+  if (masked && seq_kv > 0) {
+    sma::MaskPackArgs mp{};
+    mp.mask = static_cast<const unsigned char*>(mask.mask);
+    mp.bits = static_cast<uint32_t*>(workspace);
+    mp.slabs = (int64_t)(mask.batches * mask.heads);
+    mp.seq_q = (int32_t)seq_q;
+    mp.seq_kv = (int32_t)seq_kv;
+    mp.words = (int32_t)mask_words(seq_kv);
+    e = sma::launch_mask_pack(mp, s);
+    if (e != hipSuccess) return SMA_ERR_HIP;
+    a.mask_bits = mp.bits;
+    a.mask_words = mp.words;
+    const int64_t slab = (int64_t)seq_q * mp.words;
+    a.mbits_sh = mask.heads == heads && heads > 1 ? slab : 0;
+    a.mbits_sb = mask.batches == batch && batch > 1 ? (int64_t)mask.heads * slab : 0;
+  }
+  if (event_before && hipEventRecord(static_cast<hipEvent_t>(event_before), s) != hipSuccess)
+    return SMA_ERR_HIP;
+  switch (p.kernel) {
+    case SMA_KERNEL_F32_KSPLIT: e = sma::launch_fwd_f32_wsplit(a, d, c, s); break;
+    case SMA_KERNEL_BF16_QBLOCK: e = sma::launch_fwd_bf16(a, d, c, in_dtype == SMA_DTYPE_F16, s); break;
+    default: e = sma::launch_fwd_f32(a, d, c, s); break;
+  }
+  if (e != hipSuccess) return SMA_ERR_HIP;
+  if (event_after && hipEventRecord(static_cast<hipEvent_t>(event_after), s) != hipSuccess)
+    return SMA_ERR_HIP;
+  if (p.nsplit > 1) {
+    sma::CombineArgs ca{};
+    ca.part_o = a.part_o;
+    ca.part_lse = a.part_lse;
+    if (o16) ca.o_bf16 = static_cast<unsigned short*>(o);
+    else ca.o = static_cast<float*>(o);
+    ca.lse = lse;
+    ca.rows = (int64_t)sh.rows;
+    ca.nsplit = p.nsplit;
+    ca.seq_q = (int32_t)seq_q;
+    ca.heads = a.heads;
+    ca.os_b = a.qs_b;
+    ca.os_h = a.qs_h;
+    ca.os_s = a.qs_s;
+    e = sma::launch_combine(ca, d, s);
+    if (e != hipSuccess) return SMA_ERR_HIP;
+  }
+  return SMA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int sma_attention_fwd_validate(const void* q, const void* k, const void* v, const void* o,
@@ -297,101 +461,42 @@ int sma_attention_fwd_ex(const void* q, const void* k, const void* v, void* o, f
                          size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
                          void* workspace, size_t workspace_bytes, const sma_plan* plan,
                          void* stream, void* event_before, void* event_after) {
-  Shape sh;
-  int st = validate_all(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv, head_dim,
-                        scale, workspace, workspace_bytes, &sh, layout);
-  if (st != SMA_OK) return st;
-  if (plan) {
-    if (plan->nsplit < 1 || plan->nsplit > kMaxSplits) return SMA_ERR_INVALID_VALUE;
-    if (plan->kernel != SMA_KERNEL_F32_QBLOCK && plan->kernel != SMA_KERNEL_F32_KSPLIT &&
-        plan->kernel != SMA_KERNEL_BF16_QBLOCK)
-      return SMA_ERR_INVALID_VALUE;
-    if (!kernel_fits_dtype(plan->kernel, in_dtype)) return SMA_ERR_UNSUPPORTED;
-    if (plan->kernel == SMA_KERNEL_F32_KSPLIT && (plan->nsplit > 1 || !ksplit_fits(sh)))
-      return SMA_ERR_UNSUPPORTED;
-  }
-  if (sh.rows == 0) return SMA_OK;
-  int cus = 0;
-  st = current_device_cus(&cus);
-  if (st != SMA_OK) return st;
-  Plan p;
-  if (plan) {
-    p = plan_for(sh, plan->kernel, (size_t)plan->nsplit, cus);
-    if (p.nsplit > 1 && (!workspace || workspace_bytes < p.ws_bytes)) return SMA_ERR_INVALID_VALUE;
-    if (p.nwg > kMaxWorkgroups) return SMA_ERR_UNSUPPORTED;
-  } else {
-    p = auto_plan(sh, cus);
-    if (p.nsplit > 1 && (!workspace || workspace_bytes < p.ws_bytes || p.nwg > kMaxWorkgroups))
-      p = plan_for(sh, p.kernel, 1, cus);
-  }
+  return fwd_core(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv, head_dim, scale,
+                  causal, layout, MaskArg{}, workspace, workspace_bytes, plan, stream, event_before,
+                  event_after);
+}
 
-  sma::FwdArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.bh = (int64_t)sh.bh;
-  a.seq_q = (int32_t)seq_q;
-  a.seq_kv = (int32_t)seq_kv;
-  a.nqb = p.nqb;
-  a.nsplit = p.nsplit;
-  a.split_len = p.split_len;
-  a.c = (float)(std::fabs(scale) * 1.44269504088896340736);  // |scale| * log2(e), one rounding
-  a.negate_q = scale < 0.0 ? 1 : 0;
-  a.nwg = (uint32_t)p.nwg;
-  a.heads = (int64_t)heads;
-  if (layout == SMA_LAYOUT_BSHD) {  // element (b, s, h, c) at ((b*S + s)*H + h)*d + c
-    a.qs_b = (int64_t)(seq_q * heads * head_dim);
-    a.kvs_b = (int64_t)(seq_kv * heads * head_dim);
-    a.qs_h = a.kvs_h = (int64_t)head_dim;
-    a.qs_s = a.kvs_s = (int64_t)(heads * head_dim);
-  } else {  // element (b, h, s, c) at ((b*H + h)*S + s)*d + c
-    a.qs_b = (int64_t)(heads * seq_q * head_dim);
-    a.kvs_b = (int64_t)(heads * seq_kv * head_dim);
-    a.qs_h = (int64_t)(seq_q * head_dim);
-    a.kvs_h = (int64_t)(seq_kv * head_dim);
-    a.qs_s = a.kvs_s = (int64_t)head_dim;
-  }
-  const bool o16 = o_dtype == SMA_DTYPE_BF16;
-  if (p.nsplit == 1) {
-    if (o16) a.o_bf16 = static_cast<unsigned short*>(o);
-    else a.o = static_cast<float*>(o);
-    a.lse = lse;
-  } else {
-    a.part_o = static_cast<float*>(workspace);
-    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_lse_off);
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool c = causal != 0;
-  const int d = (int)head_dim;
-  if (event_before && hipEventRecord(static_cast<hipEvent_t>(event_before), s) != hipSuccess)
-    return SMA_ERR_HIP;
-  hipError_t e;
-  switch (p.kernel) {
-    case SMA_KERNEL_F32_KSPLIT: e = sma::launch_fwd_f32_wsplit(a, d, c, s); break;
-    case SMA_KERNEL_BF16_QBLOCK: e = sma::launch_fwd_bf16(a, d, c, in_dtype == SMA_DTYPE_F16, s); break;
-    default: e = sma::launch_fwd_f32(a, d, c, s); break;
-  }
-  if (e != hipSuccess) return SMA_ERR_HIP;
-  if (event_after && hipEventRecord(static_cast<hipEvent_t>(event_after), s) != hipSuccess)
-    return SMA_ERR_HIP;
-  if (p.nsplit > 1) {
-    sma::CombineArgs ca{};
-    ca.part_o = a.part_o;
-    ca.part_lse = a.part_lse;
-    if (o16) ca.o_bf16 = static_cast<unsigned short*>(o);
-    else ca.o = static_cast<float*>(o);
-    ca.lse = lse;
-    ca.rows = (int64_t)sh.rows;
-    ca.nsplit = p.nsplit;
-    ca.seq_q = (int32_t)seq_q;
-    ca.heads = a.heads;
-    ca.os_b = a.qs_b;
-    ca.os_h = a.qs_h;
-    ca.os_s = a.qs_s;
-    e = sma::launch_combine(ca, d, s);
-    if (e != hipSuccess) return SMA_ERR_HIP;
-  }
-  return SMA_OK;
+int sma_attention_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const void* mask, size_t mask_batches, size_t mask_heads, int in_dtype,
+                             int o_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
+                             size_t head_dim, double scale, int causal, int layout, void* workspace,
+                             size_t workspace_bytes, const sma_plan* plan, void* stream,
+                             void* event_before, void* event_after) {
+  MaskArg m;
+  m.mask = mask;
+  m.batches = mask_batches;
+  m.heads = mask_heads;
+  return fwd_core(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv, head_dim, scale,
+                  causal, layout, m, workspace, workspace_bytes, plan, stream, event_before,
+                  event_after);
+}
+
+size_t sma_attention_fwd_masked_workspace_bytes(int in_dtype, size_t batch, size_t heads,
+                                                size_t seq_q, size_t seq_kv, size_t head_dim,
+                                                int causal, int layout, size_t mask_batches,
+                                                size_t mask_heads) {
+  Shape sh;
+  if (check_shape(in_dtype, SMA_DTYPE_F32, batch, heads, seq_q, seq_kv, head_dim, 1.0, &sh,
+                  layout) != SMA_OK)
+    return 0;
+  MaskArg m;
+  m.mask = &sh;  // any non-null address: only the sizes matter here
+  m.batches = mask_batches;
+  m.heads = mask_heads;
+  if ((mask_batches != 1 && mask_batches != batch) || (mask_heads != 1 && mask_heads != heads)) return 0;
+  // The packed mask, then what the library's key split needs on the current device.
+  return mask_bits_bytes(sh, m) + sma_attention_fwd_workspace_bytes(in_dtype, batch, heads, seq_q,
+                                                                    seq_kv, head_dim, causal, 0);
 }
 
 int sma_attention_fwd_timed(const void* q, const void* k, const void* v, void* o, float* lse,

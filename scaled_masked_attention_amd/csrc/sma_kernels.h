@@ -32,7 +32,23 @@ struct FwdArgs {
   int64_t heads;
   int64_t qs_b, qs_h, qs_s;
   int64_t kvs_b, kvs_h, kvs_s;
+  // Optional hard mask, packed: bit j % 32 of word (row, j / 32) admits key j
+  // of query row `row`. mask_words words per row; word strides over batch and
+  // head (0 broadcasts). Null when there is no mask.
+  const uint32_t* mask_bits;
+  int32_t mask_words;
+  int64_t mbits_sb, mbits_sh;
 };
+
+// Packing of a byte mask [mask_batches][mask_heads][seq_q][seq_kv] (nonzero
+// admits) into the bit words above, one slab per (mask batch, mask head).
+struct MaskPackArgs {
+  const unsigned char* mask;
+  uint32_t* bits;
+  int64_t slabs;
+  int32_t seq_q, seq_kv, words;
+};
+hipError_t launch_mask_pack(const MaskPackArgs& a, hipStream_t s);
 
 // Arguments of the split-combine launch.
 struct CombineArgs {

@@ -294,3 +294,25 @@ def test_layout_argument_and_its_limits():
                                         5, None, 0, None) == INVAL
     assert lib.sma_attention_fwd_layout(None, b[1], b[2], b[3], b[4], F32, F32, 1, 2, 8, 8, 64, 0.1, 0,
                                         1, None, 0, None) == NULLP
+
+
+def test_masked_entry_point_host_checks():
+    """Argument errors of sma_attention_fwd_masked return before any HIP call."""
+    lib = sma.library()
+    M, WS = 0x70_0000_0000, 0x60_0000_0000
+    need = lib.sma_attention_fwd_masked_workspace_bytes(F32, 1, 2, 128, 100, 64, 1, 0, 1, 2)
+    split = sma.workspace_bytes(F32, 1, 2, 128, 100, 64, 1)
+    assert need == 2 * 128 * 4 * 4 + split  # 2 head slabs x 128 rows x ceil(100/32) words x 4 B
+    assert lib.sma_attention_fwd_masked_workspace_bytes(F32, 1, 2, 128, 100, 64, 1, 0, 3, 1) == 0
+
+    def call(mask=M, mb=1, mh=2, idt=F32, ws=WS, wsb=1 << 20, plan=None, o=O, skv=100, causal=1):
+        return lib.sma_attention_fwd_masked(Q, K, V, o, L, mask, mb, mh, idt, F32, 1, 2, 128, skv, 64,
+                                            0.125, causal, 0, ws, wsb,
+                                            ctypes.byref(plan) if plan else None, None, None, None)
+
+    assert call(mb=2) == INVAL and call(mh=3) == INVAL and call(mb=0, mh=0) == INVAL
+    assert call(mask=None) == NULLP
+    assert call(o=M - 64) == ALIAS                     # o runs into the mask bytes
+    assert call(ws=M + 128, wsb=4096) == ALIAS         # workspace on top of the mask
+    assert call(ws=None, wsb=0) == INVAL and call(wsb=2 * 128 * 4 * 4 - 1) == INVAL
+    assert call(idt=BF16, plan=sma.Plan(kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=1)) == UNSUP

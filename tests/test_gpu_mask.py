@@ -1,0 +1,166 @@
+"""Attention with an explicit hard mask, through the C ABI, against the masked oracle.
+
+Random masks at several densities (rows admitting nothing included), every broadcast form
+of the mask, causal and not, ragged key counts, both layouts and bf16 output. The all-ones
+mask must reproduce the unmasked kernel bit for bit (the same arithmetic with a select that
+never fires), and mask bytes other than 1 admit like 1.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import gen
+import oracle
+from helpers import check_parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import scaled_masked_attention_amd as sma
+
+    sma.library()
+
+
+def _run(q, k, v, mask, scale, causal, **kw):
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x)).to("cuda") for x in (q, k, v))
+    tm = torch.from_numpy(np.ascontiguousarray(mask)).to("cuda") if mask is not None else None
+    o, lse = sma.attention_fwd(tq, tk, tv, scale=scale, causal=causal, return_lse=True, mask=tm, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _mask(seed, shape, density):
+    return gen.uniform24(seed, np.arange(int(np.prod(shape)), dtype=np.uint64)).reshape(shape) < density
+
+
+BROADCAST = {"shared": (1, 1), "per_batch": ("B", 1), "per_head": (1, "H"), "full": ("B", "H")}
+
+
+@pytest.mark.parametrize("form", list(BROADCAST))
+@pytest.mark.parametrize("density", [0.03, 0.5, 0.97])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 3, 130, 77), (1, 2, 64, 300), (2, 1, 257, 129)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_masked_parity(shape, causal, d, density, form):
+    B, H, sq, skv = shape
+    (q, k, v), _ = gen.random_case(1100 + sq + skv + d, (B, H, sq, d), (B, H, skv, d))
+    mb = B if BROADCAST[form][0] == "B" else 1
+    mh = H if BROADCAST[form][1] == "H" else 1
+    mask = _mask(int(density * 1000) + sq, (mb, mh, sq, skv), density).astype(np.uint8)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _run(q, k, v, mask, scale, causal)
+    o_ref, lse_ref = oracle.attention_fwd_masked(q, k, v, mask, scale, causal)
+    check_parity(_np(o), _np(lse), o_ref, lse_ref, "f32", f"mask {form} {density}")
+
+
+def test_all_ones_mask_is_bitwise_the_unmasked_kernel():
+    import scaled_masked_attention_amd as sma
+
+    (q, k, v), _ = gen.random_case(1201, (2, 2, 200, 128), (2, 2, 333, 128))
+    ones = np.ones((1, 1, 200, 333), np.uint8)
+    kw = dict(kernel=sma.SMA_KERNEL_F32_KSPLIT, nsplit=1)
+    for causal in (False, True):
+        o1, l1 = _run(q, k, v, ones, 0.09, causal, **kw)
+        o2, l2 = _run(q, k, v, None, 0.09, causal, **kw)
+        assert np.array_equal(_np(o1), _np(o2)) and np.array_equal(_np(l1), _np(l2))
+
+
+def test_nonzero_bytes_admit_and_empty_rows_are_zero():
+    (q, k, v), _ = gen.random_case(1202, (1, 2, 90, 64), (1, 2, 70, 64))
+    m = _mask(5, (1, 2, 90, 70), 0.4)
+    m[0, 1, 10:20] = False  # ten rows of head 1 admit nothing
+    bytes_ = np.where(m, np.uint8(1) + (np.arange(70, dtype=np.uint8) % 255), np.uint8(0))
+    o1, l1 = _run(q, k, v, bytes_, 0.125, False)
+    o2, l2 = _run(q, k, v, m.astype(np.uint8), 0.125, False)
+    assert np.array_equal(_np(o1), _np(o2)) and np.array_equal(_np(l1), _np(l2))
+    assert np.all(_np(o1)[0, 1, 10:20] == 0.0) and np.all(np.isneginf(_np(l1)[0, 1, 10:20]))
+    o_ref, lse_ref = oracle.attention_fwd_masked(q, k, v, m, 0.125, False)
+    check_parity(_np(o1), _np(l1), o_ref, lse_ref, "f32", "bytes")
+
+
+def test_mask_with_bshd_layout_and_bf16_output():
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    (q, k, v), _ = gen.random_case(1203, (2, 3, 100, 64), (2, 3, 150, 64))
+    m = _mask(6, (1, 3, 100, 150), 0.3).astype(np.uint8)
+    o1, l1 = _run(q, k, v, m, 0.125, True)
+    tq, tk, tv = (torch.from_numpy(x).to("cuda").transpose(1, 2).contiguous() for x in (q, k, v))
+    tm = torch.from_numpy(m).to("cuda")
+    o2, l2 = sma.attention_fwd(tq, tk, tv, scale=0.125, causal=True, return_lse=True, mask=tm,
+                               layout="bshd")
+    o3 = sma.attention_fwd(tq, tk, tv, scale=0.125, causal=True, mask=tm, layout="bshd",
+                           out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.transpose(1, 2), o1) and torch.equal(l1, l2)
+    assert np.array_equal(o3.view(torch.int16).cpu().numpy().view(np.uint16),
+                          gen.f32_to_bf16_bits(o2.cpu().numpy()))
+
+
+def test_mask_bool_2d_and_binding_checks():
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    (q, k, v), _ = gen.random_case(1204, (1, 2, 40, 64), (1, 2, 50, 64))
+    m = _mask(7, (40, 50), 0.6)
+    tq, tk, tv = (torch.from_numpy(x).to("cuda") for x in (q, k, v))
+    o, lse = sma.attention_fwd(tq, tk, tv, scale=0.2, return_lse=True, mask=torch.from_numpy(m).to("cuda"))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd_masked(q, k, v, m[None, None], 0.2, False)
+    check_parity(_np(o), _np(lse), o_ref, lse_ref, "f32", "2d bool")
+    with pytest.raises(ValueError):
+        sma.attention_fwd(tq, tk, tv, mask=torch.ones(40, 51, dtype=torch.bool, device="cuda"))
+    with pytest.raises(ValueError):
+        sma.attention_fwd(tq, tk, tv, mask=torch.ones(40, 50, device="cuda"))  # float mask
+
+
+KERNELS = {  # name: (input dtype, kernel, key splits)
+    "f32-qblock": ("f32", "F32_QBLOCK", 1),
+    "f32-split3": ("f32", "F32_QBLOCK", 3),
+    "f32-ksplit": ("f32", "F32_KSPLIT", 1),
+    "bf16": ("bf16", "BF16_QBLOCK", 1),
+    "bf16-split2": ("bf16", "BF16_QBLOCK", 2),
+    "f16": ("f16", "BF16_QBLOCK", 1),
+}
+
+
+@pytest.mark.parametrize("form", ["shared", "full"])
+@pytest.mark.parametrize("kern", list(KERNELS))
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_masked_parity_every_kernel(kern, causal, d, form):
+    import torch
+
+    import scaled_masked_attention_amd as sma
+    from helpers import to_device
+
+    dtype, kname, nsplit = KERNELS[kern]
+    B, H, sq, skv = 2, 2, 300, 333
+    (q, k, v), bits = gen.random_case(1300 + d, (B, H, sq, d), (B, H, skv, d),
+                                      sigma_qk=1.0 if dtype == "f32" else 3.0, dtype=dtype)
+    shape = (1, 1, sq, skv) if form == "shared" else (B, H, sq, skv)
+    mask = _mask(1301 + causal, shape, 0.5).astype(np.uint8)
+    tq, tk, tv = to_device((q, k, v), bits, dtype)
+    o, lse = sma.attention_fwd(tq, tk, tv, scale=1.0 / math.sqrt(d), causal=causal, return_lse=True,
+                               mask=torch.from_numpy(mask).to("cuda"),
+                               kernel=getattr(sma, "SMA_KERNEL_" + kname), nsplit=nsplit)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd_masked(q, k, v, mask, 1.0 / math.sqrt(d), causal)
+    check_parity(_np(o), _np(lse), o_ref, lse_ref, dtype, f"mask {kern}")
