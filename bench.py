@@ -94,6 +94,25 @@ class HipEvents:
         self.hip.hipEventDestroy(ev)
 
 
+def settle(step, ms: float) -> int:
+    """Run the measured step, untimed, for about `ms` milliseconds of wall time before the
+    warmup steps; returns how many steps that took. The GPU's clock settles to the running
+    workload over tens of milliseconds: a short kernel timed right after an idle (or a
+    differently loaded) period runs part of its timed steps on the ramp."""
+    import torch
+
+    if ms <= 0:
+        return 0
+    n = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            step()
+        n += 8
+        torch.cuda.synchronize()
+    return n
+
+
 def traffic_summary_path(kernel_function: str, workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"{kernel_function}_{workload}_hbm_traffic.txt")
 
@@ -243,6 +262,7 @@ def bench_bwd(args, w, name):
     call = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), lse.data_ptr(), tg.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), sma.SMA_DTYPE_F32, B, H, sq, skv, d, w.scale,
             w.causal, ws.data_ptr(), ws_n, sptr)
+    settled = settle(lambda: sma.attention_bwd_raw(*call), args.settle_ms)
     for _ in range(args.warmup):
         sma.attention_bwd_raw(*call)
     torch.cuda.synchronize()
@@ -271,7 +291,7 @@ def bench_bwd(args, w, name):
     traffic = read_traffic(kname, name, kernel_source_digest(kname))
     line = {
         "metric": BWD_METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": args.steps, "warmup": args.warmup, "settle_steps": settled, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded SplitMix64 + Box-Muller normals; dO on its own stream)",
         "config": {"workload": name, "batch": B, "heads": H, "seq_q": sq, "seq_kv": skv,
@@ -355,17 +375,26 @@ def bench_rows(args, w):
     else:
         out = torch.empty_like(tx)
     stream = torch.cuda.current_stream()
+    lib = sma.library()
+    s = stream.cuda_stream
+    rows, cols = x.shape[0], x.shape[1]
+    # One C call per step on an argument tuple built once (see the attention loop).
+    if w.op == "softmax_rows":
+        fn, call = lib.sma_softmax_rows, (tx.data_ptr(), out.data_ptr(), rows, cols, s)
+    elif w.op == "logsumexp_rows":
+        fn, call = lib.sma_logsumexp_rows, (tx.data_ptr(), out.data_ptr(), rows, cols, s)
+    elif w.op == "masked_softmax_rows":
+        fn, call = lib.sma_masked_softmax_rows, (tx.data_ptr(), tm.data_ptr(), out.data_ptr(), rows, cols, s)
+    else:
+        fn, call = (lib.sma_scaled_causal_softmax,
+                    (tx.data_ptr(), out.data_ptr(), w.batch, w.rows, w.cols, float(w.scale), int(w.causal), s))
 
     def step():
-        if w.op == "softmax_rows":
-            sma.softmax_rows(tx, out=out, stream=stream)
-        elif w.op == "logsumexp_rows":
-            sma.logsumexp_rows(tx, out=out, stream=stream)
-        elif w.op == "masked_softmax_rows":
-            sma.masked_softmax_rows(tx, tm, out=out, stream=stream)
-        else:
-            sma.scaled_causal_softmax(tx, w.scale, w.causal, out=out, stream=stream)
+        st = fn(*call)
+        if st != 0:
+            raise RuntimeError(sma.status_string(st))
 
+    settled = settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -387,7 +416,7 @@ def bench_rows(args, w):
     traffic = read_traffic(kname, w.name, kernel_source_digest(kname))
     line = {
         "metric": ROW_METRIC, "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_steps": settled, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded SplitMix64 + Box-Muller normals; Bernoulli mask)",
         "config": {"workload": w.name, "op": w.op, "batch": w.batch, "rows": w.rows, "cols": w.cols,
@@ -417,6 +446,8 @@ def main():
     ap.add_argument("--layout", default="bhsd", choices=["bhsd", "bshd"],
                     help="memory layout of q, k, v and O: [B,H,S,d] or [B,S,H,d]")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="wall milliseconds of untimed steps before the warmup steps (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
@@ -485,13 +516,23 @@ def main():
     call = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(), in_dt,
             o_dt, B, H, sq, skv, d, w.scale, w.causal, ws.data_ptr(), ws_n)
 
-    def run(e0=None, e1=None):
-        if masked:
-            sma.attention_fwd_masked_raw(*call[:5], tmask.data_ptr(), 1, 1, *call[5:14], lay, *call[14:],
-                                         None, sptr, e0, e1)
-        else:
-            sma.attention_fwd_ex_raw(*call, None, sptr, e0, e1, layout=lay)
+    # One C call per step on argument tuples built once: the Python wrapper's own
+    # per-call work would otherwise hold back the launches of a ~25 us kernel.
+    lib = sma.library()
+    if masked:
+        fn = lib.sma_attention_fwd_masked
+        base = (*call[:5], tmask.data_ptr(), 1, 1, *call[5:14], lay, *call[14:], None, sptr)
+    else:
+        fn = lib.sma_attention_fwd_ex
+        base = (*call[:14], lay, *call[14:], None, sptr)
+    no_events = base + (None, None)
 
+    def run(events=no_events):
+        st = fn(*events)
+        if st != 0:
+            raise RuntimeError(sma.status_string(st))
+
+    settled = settle(run, args.settle_ms)
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
@@ -503,12 +544,13 @@ def main():
     if per_launch:
         ev_a = [ev.create() for _ in range(args.steps)]
         ev_b = [ev.create() for _ in range(args.steps)]
+        with_events = [base + (ev_a[i], ev_b[i]) for i in range(args.steps)]
     else:
         ev_a, ev_b = [ev.create()], [ev.create()]
     t0 = time.perf_counter()
     if per_launch:
         for i in range(args.steps):
-            run(ev_a[i], ev_b[i])
+            run(with_events[i])
     else:
         ev.record(ev_a[0], sptr)
         for i in range(args.steps):
@@ -534,7 +576,7 @@ def main():
                                             kernel_source_digest(KERNEL_FUNCTIONS[plan.kernel]))
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": args.steps, "warmup": args.warmup, "settle_steps": settled, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded SplitMix64 + Box-Muller normals)",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_q": sq, "seq_kv": skv,

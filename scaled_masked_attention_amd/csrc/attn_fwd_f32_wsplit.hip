@@ -16,7 +16,8 @@
 // wave streams its K and V blocks into private LDS slots, all with coalesced
 // direct-to-LDS loads (1 KB of consecutive rows per instruction); the MFMA
 // operands are read back from LDS. Block b+1's K copy is in flight during
-// block b's scores and softmax, its V copy during block b+1's scores.
+// block b's scores and softmax, its V copy during block b+1's scores; the
+// first V copy overlaps the first block's scores.
 //
 // MFMA layouts (v_mfma_f32_32x32x2f32, lane = 32*h + m):
 //   S^T = K Q^T: step (u, e) multiplies head dims 8u + 4h + e of key m (A) and
@@ -139,8 +140,12 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
   if (b_begin < b_end) {
     copy_k_block(b_begin);
     copy_v_block(b_begin);
+    // Q and the first K block (with its mask words); the first V block, not
+    // needed before the first block's softmax, stays in flight.
+    wait_vmcnt<G::kDmaPerTile>();
+  } else {
+    wait_vmcnt<0>();
   }
-  wait_vmcnt<0>();
   __syncthreads();
 
   float qr[4 * G::kSteps];  // group u, element e: head dim 8u + 4*lh + e of query lm
