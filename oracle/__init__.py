@@ -56,6 +56,8 @@ def _bind(lib):
         getattr(lib, name).restype = ctypes.c_int
     lib.oracle_masked_softmax_rows.argtypes = [dp, dp, L, L, dp]
     lib.oracle_masked_softmax_rows.restype = ctypes.c_int
+    lib.oracle_softmax_rows_backward.argtypes = [dp, dp, L, L, ctypes.c_double, dp]
+    lib.oracle_softmax_rows_backward.restype = ctypes.c_int
     lib.oracle_scaled_causal_softmax.argtypes = [dp, L, L, L, ctypes.c_double, ctypes.c_int, dp]
     lib.oracle_scaled_causal_softmax.restype = ctypes.c_int
     lib.oracle_attention_bwd.argtypes = [dp, dp, dp, dp, L, L, L, L, L, ctypes.c_double, ctypes.c_int,
@@ -212,6 +214,19 @@ def logsumexp_rows(x, lib=None):
     out = np.empty((x.shape[0],), dtype=np.float64)
     if lib.oracle_logsumexp_rows(x.ctypes.data, x.shape[0], x.shape[1], out.ctypes.data) != 0:
         raise ValueError("oracle_logsumexp_rows rejected its arguments")
+    return out
+
+
+def softmax_rows_backward(y, dy, scale: float = 1.0, lib=None):
+    """dx = scale * y * (dy - rowsum(y * dy)) in float64, from the softmax output y and dL/dy."""
+    lib = lib or load()
+    y, dy = _rows2d(y), _rows2d(dy)
+    if y.shape != dy.shape:
+        raise ValueError("y and dy differ in shape")
+    out = np.empty(y.shape, dtype=np.float64)
+    if lib.oracle_softmax_rows_backward(y.ctypes.data, dy.ctypes.data, y.shape[0], y.shape[1],
+                                        float(scale), out.ctypes.data) != 0:
+        raise ValueError("oracle_softmax_rows_backward rejected its arguments")
     return out
 
 

@@ -132,3 +132,33 @@ int oracle_scaled_causal_softmax(const float* in, long batch, long rows, long co
                        cols, 1, scale, out + (size_t)i * cols, 0);
   return 0;
 }
+
+/* Softmax backward from its output (pulsatrix HIPBackend `softmax_rows_backward`;
+ * scaled, MicroGPT `fused_attn_softmax_backward`): for each row,
+ *   dot = sum_k y[k] * dy[k],   dx[j] = scale * y[j] * (dy[j] - dot),
+ * in double, k ascending. scale = 1 is the plain softmax backward; for the fused
+ * scale + mask + softmax forward it is the forward's scale (masked entries have
+ * y = 0 and so get 0). */
+int oracle_softmax_rows_backward(const float* y, const float* dy, long rows, long cols,
+                                 double scale, double* dx) {
+  if (rows < 0 || cols < 0) return -1;
+#pragma omp parallel for schedule(static)
+  for (long r = 0; r < rows; ++r) {
+    const float* yr = y + (size_t)r * cols;
+    const float* gr = dy + (size_t)r * cols;
+    double* o = dx + (size_t)r * cols;
+    double dot = 0.0;
+    for (long k = 0; k < cols; ++k) dot += (double)yr[k] * (double)gr[k];
+#if defined(ROWS_PLANT_BWD_NO_DOT)
+    dot = 0.0;
+#endif
+    for (long j = 0; j < cols; ++j) {
+#if defined(ROWS_PLANT_BWD_SIGN)
+      o[j] = scale * (double)yr[j] * (dot - (double)gr[j]);
+#else
+      o[j] = scale * (double)yr[j] * ((double)gr[j] - dot);
+#endif
+    }
+  }
+  return 0;
+}

@@ -8,7 +8,7 @@ import pytest
 import oracle
 import test_rows_oracle_pins as pins
 
-MUTANTS = ["NO_MAX", "MASK_IN_MAX", "TOP_LEFT", "LSE_LOG2", "EMPTY_UNIFORM"]
+MUTANTS = ["NO_MAX", "MASK_IN_MAX", "TOP_LEFT", "LSE_LOG2", "EMPTY_UNIFORM", "BWD_NO_DOT", "BWD_SIGN"]
 
 
 def _pin_calls():
@@ -22,6 +22,9 @@ def _pin_calls():
         ("empty", pins.test_rows_admitting_nothing_are_zero, ()),
         ("causal", pins.test_scaled_causal_matches_scipy_on_the_admitted_prefix, (20, 7, True, 0.125)),
         ("causal_wide", pins.test_scaled_causal_matches_scipy_on_the_admitted_prefix, (7, 20, True, 1.0)),
+        ("bwd_fd", pins.test_softmax_backward_matches_finite_differences, (0.25,)),
+        ("bwd_torch", pins.test_softmax_backward_matches_torch_float64_autograd, ()),
+        ("bwd_closed", pins.test_softmax_backward_closed_forms, ()),
     ]
 
 

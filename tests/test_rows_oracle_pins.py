@@ -164,3 +164,71 @@ def test_rejects_bad_shapes():
         oracle.masked_softmax_rows(np.zeros((2, 3), np.float32), np.zeros((3, 2), np.float32))
     with pytest.raises(ValueError):
         oracle.scaled_causal_softmax(np.zeros((2, 3), np.float32), 1.0, True)
+
+
+# ------------------------------------------------------------------ softmax backward
+def _softmax_grid(rng, rows, cols):
+    return (np.round(rng.uniform(-3, 3, size=(rows, cols)) * 64) / 64).astype(np.float32)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.25, -0.5])
+def test_softmax_backward_matches_finite_differences(scale):
+    """d/dx of L = sum(dy * softmax(scale x)), by Richardson-extrapolated central differences of
+    the forward oracle on inputs where the perturbations are exact in fp32, equals
+    scale * y * (dy - sum y dy) with y = softmax(scale x)."""
+    rng = np.random.default_rng(31)
+    x = _softmax_grid(rng, 3, 6)
+    dy = rng.normal(size=(3, 6))
+    y = oracle.scaled_causal_softmax(x[None], scale, False)[0]
+
+    def loss(xx):
+        return float(np.sum(dy * oracle.scaled_causal_softmax(xx[None], scale, False)[0]))
+
+    num = np.zeros_like(dy)
+    for idx in np.ndindex(x.shape):
+        est = []
+        for h in (2.0 ** -8, 2.0 ** -9):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            est.append((loss(xp) - loss(xm)) / (2 * h))
+        num[idx] = (4 * est[1] - est[0]) / 3
+    got = oracle.softmax_rows_backward(y.astype(np.float32), dy.astype(np.float32), scale)
+    # y and dy rounded to fp32 for the call: compare within that rounding
+    assert np.abs(got - num).max() <= 1e-6 * max(1.0, np.abs(num).max())
+
+
+def test_softmax_backward_matches_torch_float64_autograd():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(32)
+    x = rng.normal(size=(5, 40)).astype(np.float32)
+    dy = rng.normal(size=(5, 40)).astype(np.float32)
+    tx = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    ty = torch.softmax(tx, dim=-1)
+    (ty * torch.tensor(dy, dtype=torch.float64)).sum().backward()
+    y32 = ty.detach().numpy().astype(np.float32)
+    got = oracle.softmax_rows_backward(y32, dy)
+    # the oracle sees y rounded to fp32: recompute torch's gradient from that y exactly
+    yd, gd = y32.astype(np.float64), dy.astype(np.float64)
+    assert np.abs(got - tx.grad.numpy()).max() <= 1e-6
+    assert np.abs(got - yd * (gd - (yd * gd).sum(axis=1, keepdims=True))).max() <= 1e-15
+
+
+def test_softmax_backward_closed_forms():
+    rng = np.random.default_rng(33)
+    y = oracle.softmax_rows(rng.normal(size=(4, 30)).astype(np.float32)).astype(np.float32)
+    y = y / y.sum(axis=1, keepdims=True, dtype=np.float64).astype(np.float32)
+    c = np.repeat(rng.normal(size=(4, 1)), 30, axis=1).astype(np.float32)
+    # constant dy per row: dx = y * c * (1 - sum y), i.e. zero up to sum(y) - 1
+    dx = oracle.softmax_rows_backward(y, c)
+    s = y.astype(np.float64).sum(axis=1, keepdims=True)
+    assert np.abs(dx - y * c * (1.0 - s)).max() <= 1e-15
+    # one-hot y: every entry zero
+    oh = np.zeros((3, 9), np.float32)
+    oh[np.arange(3), [1, 4, 8]] = 1.0
+    assert np.all(oracle.softmax_rows_backward(oh, rng.normal(size=(3, 9)).astype(np.float32)) == 0.0)
+    # linear in the scale; entries with y = 0 (masked) stay 0
+    g = rng.normal(size=(4, 30)).astype(np.float32)
+    y[:, 5] = 0.0
+    a1, a3 = oracle.softmax_rows_backward(y, g, 1.0), oracle.softmax_rows_backward(y, g, -3.0)
+    assert np.abs(a3 + 3.0 * a1).max() <= 1e-15 and np.all(a1[:, 5] == 0.0)
