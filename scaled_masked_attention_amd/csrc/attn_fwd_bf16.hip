@@ -205,7 +205,10 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const float c = a.c;
+  // c = |scale| log2 e, kept positive so that an excluded score (-inf) gives
+  // -inf, never NaN: with scale 0 every allowed |s| c is then below 2^-26 for
+  // |s| < 2^100, and 2^(s c - m) rounds to 1, the uniform weights of scale 0.
+  const float c = fmaxf(a.c, 1.17549435e-38f);
 
   // O^T += V^T P^T over a tile's 64 keys in k-steps of 16. In each 16-lane
   // group, lane role s reads 4 dims of V row 16*t2 + 8*h + s/4 (and +4).
@@ -214,74 +217,101 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int half8 = 8 * (srole & 1);
   auto pv_tile = [&](int slot, const V8 (&pb)[G::kKB][2]) {
     const unsigned char* vtile = reinterpret_cast<const unsigned char*>(&v_lds[slot][0]);
+    // MFMA i = 4 (2 kb + t2) + cb: output chunk cb, keys 32 kb + 16 t2 .. + 15.
+    auto v_operand = [&](int i) {
+      const int kb = i / (2 * G::kNch), t2 = (i / G::kNch) % 2, cb = i % G::kNch;
+      const int r_lo = 32 * kb + 16 * t2 + 8 * lh + srole / 4;
+      const int r_hi = r_lo + 4;
+      const int chunk = 4 * cb + colq;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vtile + r_lo * (2 * D) +
+                                                     16 * (chunk ^ v_swz<D>(r_lo)) + half8));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vtile + r_hi * (2 * D) +
+                                                     16 * (chunk ^ v_swz<D>(r_hi)) + half8));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+      return __builtin_bit_cast(V8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+    };
+    constexpr int kN = 2 * G::kKB * G::kNch;  // MFMAs per tile
+    constexpr int kPf = 3;                    // operands in flight ahead of the MFMAs
+    V8 vop[kPf + 1];
 #pragma unroll
-    for (int kb = 0; kb < G::kKB; ++kb)
+    for (int i = 0; i < kPf; ++i) vop[i] = v_operand(i);
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const int r_lo = 32 * kb + 16 * t2 + 8 * lh + srole / 4;
-        const int r_hi = r_lo + 4;
-#pragma unroll
-        for (int cb = 0; cb < G::kNch; ++cb) {
-          const int chunk = 4 * cb + colq;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vtile + r_lo * (2 * D) +
-                                                         16 * (chunk ^ v_swz<D>(r_lo)) + half8));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vtile + r_hi * (2 * D) +
-                                                         16 * (chunk ^ v_swz<D>(r_hi)) + half8));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          const V8 aop = __builtin_bit_cast(V8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
-          oacc[cb] = H::mfma(aop, pb[kb][t2], oacc[cb]);
-        }
-      }
+    for (int i = 0; i < kN; ++i) {
+      if (i + kPf < kN) vop[(i + kPf) % (kPf + 1)] = v_operand(i + kPf);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this MFMA
+      const int kb = i / (2 * G::kNch), t2 = (i / G::kNch) % 2, cb = i % G::kNch;
+      oacc[cb] = H::mfma(vop[i % (kPf + 1)], pb[kb][t2], oacc[cb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // Scores, lazy running max and probabilities of tile T (in ring slot
   // `slot`); returns the bf16 probabilities for the PV product.
   auto scores_and_p = [&](int32_t T, int slot, V8 (&pb)[G::kKB][2]) {
     const int32_t j0 = ks + T * G::kK;
+    // The k-steps of the key blocks interleave, and the K operands of step
+    // st + kPf are read before the MFMAs of step st, so that every LDS read has
+    // 2 kPf MFMAs' time to land.
     f32x16 sacc[G::kKB];
+    const unsigned char* ktile = reinterpret_cast<const unsigned char*>(&k_lds[slot][0]);
+    auto k_operand = [&](int kb, int st) {
+      const int rho = 32 * kb + lm;
+      const int chunk = lh * G::kSteps + st;
+      return __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(
+                                        ktile + rho * (2 * D) + 16 * (chunk ^ k_swz<D>(rho))));
+    };
+    constexpr int kPf = 2;  // k-steps of K operands in flight ahead of the MFMAs
+    V8 kop[kPf + 1][G::kKB];
 #pragma unroll
-    for (int kb = 0; kb < G::kKB; ++kb) {
+    for (int kb = 0; kb < G::kKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-      const int rho = 32 * kb + lm;
-      const unsigned char* krow = reinterpret_cast<const unsigned char*>(&k_lds[slot][rho * G::kChunksPerRow]);
 #pragma unroll
-      for (int st = 0; st < G::kSteps; ++st) {
-        const int chunk = lh * G::kSteps + st;
-        const V8 kop = __builtin_bit_cast(
-            V8, *reinterpret_cast<const u32x4*>(krow + 16 * (chunk ^ k_swz<D>(rho))));
-        sacc[kb] = H::mfma(kop, qr[st], sacc[kb]);
+    for (int st = 0; st < kPf; ++st)
+#pragma unroll
+      for (int kb = 0; kb < G::kKB; ++kb) kop[st][kb] = k_operand(kb, st);
+#pragma unroll
+    for (int st = 0; st < G::kSteps; ++st) {
+      if (st + kPf < G::kSteps)
+#pragma unroll
+        for (int kb = 0; kb < G::kKB; ++kb) kop[(st + kPf) % (kPf + 1)][kb] = k_operand(kb, st + kPf);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of these MFMAs
+#pragma unroll
+      for (int kb = 0; kb < G::kKB; ++kb)
+        sacc[kb] = H::mfma(kop[st % (kPf + 1)][kb], qr[st], sacc[kb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Boundary tiles (the causal diagonal, the end of the keys, a hard mask):
+    // excluded scores become -inf, so that they enter neither the max nor the
+    // sum (2^-inf = 0; c > 0). The empty asm keeps the bound, and with it the
+    // comparisons, inside this branch instead of on every tile.
+    if (MASKED || j0 + G::kK > wave_lo) {
+      int32_t rel = lim - j0 - 8 * lh;  // key 32kb + 16(r/8) + r%8 allowed iff < rel
+      asm volatile("" : "+v"(rel));
+#pragma unroll
+      for (int kb = 0; kb < G::kKB; ++kb) {
+        // Key 32kb + 16(r/8) + 8h + r%8 of the tile: under the causal/length bound, and
+        // admitted by the mask (bit 16(r/8) + 8h + r%8 of word kb).
+        const uint32_t mword =
+            MASKED ? mask_lds[MASKED ? slot : 0][MASKED ? wave : 0][32 * kb + lm] : ~0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = (32 * kb + 16 * (r / 8) + (r % 8) < rel) &&
+                          (!MASKED || ((mword >> (16 * (r / 8) + 8 * lh + (r % 8))) & 1u));
+          sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
+        }
       }
     }
 
-    // Row max of the raw scores (scale > 0 after the sign fold), masked keys excluded.
-    const bool need_mask = MASKED || j0 + G::kK > wave_lo;
-    const int32_t rel = lim - j0 - 8 * lh;  // key 32kb + 16(r/8) + r%8 allowed iff < rel
-    uint32_t mword[G::kKB];
+    // Row max of the raw scores (scale > 0 after the sign fold).
+    float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < G::kKB; ++kb)
-      mword[kb] = MASKED ? mask_lds[MASKED ? slot : 0][MASKED ? wave : 0][32 * kb + lm] : ~0u;
-    // Key 32kb + 16(r/8) + 8h + r%8 of the tile: under the causal/length bound, and
-    // admitted by the mask (bit 16(r/8) + 8h + r%8 of word kb).
-    auto admitted = [&](int kb, int r) {
-      return (32 * kb + 16 * (r / 8) + (r % 8) < rel) &&
-             (!MASKED || ((mword[kb] >> (16 * (r / 8) + 8 * lh + (r % 8))) & 1u));
-    };
-    float mx = -INFINITY;
-    if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < G::kKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          mx = admitted(kb, r) ? fmaxf(mx, sacc[kb][r]) : mx;
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < G::kKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float tmax = mx == -INFINITY ? -INFINITY : mx * c;
     if (__any(tmax > m_run + kTau)) {
@@ -298,30 +328,16 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
 
     // p = 2^(s*c - m), rounded to bf16 for the PV product.
     float psum = 0.f;
-    if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < G::kKB; ++kb)
+    for (int kb = 0; kb < G::kKB; ++kb)
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * t2 + e], c, neg_m));
-            p = admitted(kb, 8 * t2 + e) ? p : 0.f;
-            psum += p;
-            pb[kb][t2][e] = (typename H::E)p;
-          }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < G::kKB; ++kb)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * t2 + e], c, neg_m));
-            psum += p;
-            pb[kb][t2][e] = (typename H::E)p;
-          }
-    }
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * t2 + e], c, neg_m));
+          psum += p;
+          pb[kb][t2][e] = (typename H::E)p;
+        }
     l_run += psum;
   };
 
