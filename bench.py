@@ -318,8 +318,8 @@ def row_algorithmic_bytes(w) -> int:
     n = w.batch * w.rows * w.cols
     if w.op == "logsumexp_rows":
         return 4 * n + 4 * w.batch * w.rows
-    if w.op == "masked_softmax_rows":
-        return 12 * n
+    if w.op in ("masked_softmax_rows", "softmax_rows_backward"):
+        return 12 * n  # two inputs read, one output written
     return 8 * n
 
 
@@ -333,6 +333,9 @@ def row_oracle(w, x, mask, sample):
         return oracle.softmax_rows(x[sample])
     if w.op == "logsumexp_rows":
         return oracle.logsumexp_rows(x[sample])
+    if w.op == "softmax_rows_backward":  # `mask` carries dy; y is the oracle's own forward
+        y = oracle.softmax_rows(x[sample]).astype(np.float32)
+        return oracle.softmax_rows_backward(y, mask[sample], w.scale)
     return oracle.masked_softmax_rows(x[sample], mask[sample])
 
 
@@ -368,6 +371,8 @@ def bench_rows(args, w):
     import scaled_masked_attention_amd as sma
 
     x, mask = gen.make_row_inputs(w)
+    if w.op == "softmax_rows_backward":
+        mask = gen.make_row_grad(w)  # dy, passed where the masked op takes its mask
     tx = torch.from_numpy(x).to("cuda")
     tm = torch.from_numpy(mask).to("cuda") if mask is not None else None
     if w.op == "logsumexp_rows":
@@ -385,6 +390,10 @@ def bench_rows(args, w):
         fn, call = lib.sma_logsumexp_rows, (tx.data_ptr(), out.data_ptr(), rows, cols, s)
     elif w.op == "masked_softmax_rows":
         fn, call = lib.sma_masked_softmax_rows, (tx.data_ptr(), tm.data_ptr(), out.data_ptr(), rows, cols, s)
+    elif w.op == "softmax_rows_backward":
+        ty = sma.softmax_rows(tx)  # the forward's output y, untimed
+        fn, call = (lib.sma_softmax_rows_backward,
+                    (ty.data_ptr(), tm.data_ptr(), out.data_ptr(), rows, cols, float(w.scale), s))
     else:
         fn, call = (lib.sma_scaled_causal_softmax,
                     (tx.data_ptr(), out.data_ptr(), w.batch, w.rows, w.cols, float(w.scale), int(w.causal), s))
@@ -418,7 +427,9 @@ def bench_rows(args, w):
         "metric": ROW_METRIC, "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_steps": settled, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic (seeded SplitMix64 + Box-Muller normals; Bernoulli mask)",
+        "data": ("synthetic (seeded SplitMix64 + Box-Muller normals; y = the GPU row softmax of the "
+                 "scores, untimed)" if w.op == "softmax_rows_backward" else
+                 "synthetic (seeded SplitMix64 + Box-Muller normals; Bernoulli mask)"),
         "config": {"workload": w.name, "op": w.op, "batch": w.batch, "rows": w.rows, "cols": w.cols,
                    "scale": w.scale, "causal": w.causal, "sigma": w.sigma, "mask_density": w.density},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / (k_avg * 1e-3) / 1e9, 1),

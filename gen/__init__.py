@@ -250,6 +250,7 @@ class RowWorkload:
 
     name: str
     op: str          # softmax_rows | logsumexp_rows | masked_softmax_rows | scaled_causal_softmax
+                     # | softmax_rows_backward (x: the forward's scores; dy ~ N(0, 1))
     batch: int
     rows: int        # rows per matrix
     cols: int
@@ -270,6 +271,10 @@ ROW_WORKLOADS: Dict[str, RowWorkload] = {w.name: w for w in (
     RowWorkload("softmax_rows_r32768_c16384", "softmax_rows", 1, 32768, 16384, 1.0, False, 4.0, 1.0, 20261215),
     RowWorkload("scaled_causal_softmax_b2_r16384_c16384", "scaled_causal_softmax", 2, 16384, 16384,
                 1.0 / math.sqrt(128), True, 4.0, 1.0, 20261216),
+    RowWorkload("softmax_rows_backward_r16384_c512", "softmax_rows_backward", 1, 16384, 512, 1.0, False,
+                4.0, 1.0, 20261217),
+    RowWorkload("softmax_rows_backward_r32768_c16384", "softmax_rows_backward", 1, 32768, 16384, 1.0,
+                False, 4.0, 1.0, 20261218),
 )}
 
 
@@ -284,6 +289,11 @@ def make_row_inputs(w: RowWorkload):
         u = uniform24(w.seed, np.uint64(TENSOR_STREAM["k"] * STREAM_STRIDE) + np.arange(n, dtype=np.uint64))
         mask = (u < w.density).astype(np.float32).reshape(shape)
     return x, mask
+
+
+def make_row_grad(w: RowWorkload) -> np.ndarray:
+    """dL/dy for a softmax-backward row workload: float32 N(0, 1), the shape of its scores."""
+    return tensor_f32(w.seed, "v", (w.batch * w.rows, w.cols), 1.0)
 
 
 def random_case(seed: int, shape_q, shape_kv, sigma_qk=1.0, sigma_v=1.0, dtype="f32"):

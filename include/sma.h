@@ -334,6 +334,23 @@ int sma_masked_softmax_rows(const float* in, const float* mask, float* out, size
 int sma_scaled_causal_softmax(const float* in, float* out, size_t batch, size_t rows, size_t cols,
                               double scale, int causal, void* stream);
 
+/* Softmax backward from the forward's output (pulsatrix HIPBackend page,
+ * `softmax_rows_backward`; with scale, the backward of the MicroGPT
+ * CuBLASBackend page's fused scale + mask + softmax, `fused_attn_softmax_backward`):
+ * for each of `rows` rows of `cols` fp32 entries,
+ *     dx_j = scale * y_j * (dy_j - sum_k y_k * dy_k),
+ * with y the softmax output and dy the gradient with respect to it, both
+ * row-major [rows][cols]. Entries the forward blocked have y = 0 and get
+ * dx = 0. scale = 1 is the plain softmax backward; the fused op's scale
+ * gives the gradient with respect to its unscaled input. The dot product is
+ * accumulated in fp32 (fused multiply-adds, then a tree over the lanes).
+ * dx may be the same buffer as y or dy (in place) but must not overlap them
+ * otherwise; y and dy may overlap each other. Alignment, sizes, errors and
+ * asynchrony as for the row primitives above; scale must be finite;
+ * rows*cols = 0 launches nothing. */
+int sma_softmax_rows_backward(const float* y, const float* dy, float* dx, size_t rows, size_t cols,
+                              double scale, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* sma_status_string(int status);
 

@@ -94,8 +94,9 @@ def library():
         lib.sma_logsumexp_rows.argtypes = [fp, fp, sz, sz, vp]
         lib.sma_masked_softmax_rows.argtypes = [fp, fp, fp, sz, sz, vp]
         lib.sma_scaled_causal_softmax.argtypes = [fp, fp, sz, sz, sz, ctypes.c_double, ctypes.c_int, vp]
+        lib.sma_softmax_rows_backward.argtypes = [fp, fp, fp, sz, sz, ctypes.c_double, vp]
         for n in ("sma_softmax_rows", "sma_logsumexp_rows", "sma_masked_softmax_rows",
-                  "sma_scaled_causal_softmax"):
+                  "sma_scaled_causal_softmax", "sma_softmax_rows_backward"):
             getattr(lib, n).restype = ctypes.c_int
         bwd = [vp] * 9 + [ctypes.c_int, sz, sz, sz, sz, sz, ctypes.c_double, ctypes.c_int, vp, sz, vp]
         lib.sma_attention_bwd.argtypes = bwd
@@ -421,6 +422,23 @@ def masked_softmax_rows(x, mask, out=None, stream=None):
     out = torch.empty_like(x) if out is None else _row_input(out, "out", 2)
     s = (stream or torch.cuda.current_stream()).cuda_stream
     _raise(library().sma_masked_softmax_rows(_ptr(x), _ptr(mask), _ptr(out), x.shape[0], x.shape[1], s))
+    return out
+
+
+def softmax_rows_backward(y, dy, scale=1.0, out=None, stream=None):
+    """dx = scale * y * (dy - rowsum(y * dy)) for contiguous float32 [rows, cols] tensors y (the
+    softmax output) and dy; out may be y or dy (in place)."""
+    import torch
+
+    y, dy = _row_input(y, "y", 2), _row_input(dy, "dy", 2)
+    if dy.shape != y.shape:
+        raise ValueError("dy shape differs")
+    out = torch.empty_like(y) if out is None else _row_input(out, "out", 2)
+    if out.shape != y.shape:
+        raise ValueError("out shape differs")
+    s = (stream or torch.cuda.current_stream()).cuda_stream
+    _raise(library().sma_softmax_rows_backward(_ptr(y), _ptr(dy), _ptr(out), y.shape[0], y.shape[1],
+                                               float(scale), s))
     return out
 
 

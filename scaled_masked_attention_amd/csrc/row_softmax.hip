@@ -4,7 +4,10 @@
 //   "CUDA Buffer Kernels FFI": max and denominator over admitted entries,
 //   blocked entries exactly zero, a row admitting nothing all zeros) and the
 //   fused scale + causal mask + softmax (MicroGPT CuBLASBackend
-//   `fused_attn_softmax`, bottom-right causal alignment as in attention).
+//   `fused_attn_softmax`, bottom-right causal alignment as in attention),
+//   and the softmax backward from the forward's output (pulsatrix
+//   `softmax_rows_backward`; with a scale, the backward of MicroGPT's fused
+//   scale + mask + softmax): dx_j = scale * y_j * (dy_j - sum_k y_k dy_k).
 //
 // HBM-bound: a row is read once and written once when it fits in the
 // registers of its team (a wave for rows up to 4096 floats, a 256-thread
@@ -232,6 +235,117 @@ __global__ __launch_bounds__(256) void row_softmax_stream_kernel(RowArgs a) {
   }
 }
 
+// Softmax backward, register-resident rows: each lane holds E vectors of VEC
+// floats of y and of dy (element j = VEC * (lane_in_team + TEAM * k) + e),
+// the row's dot product is reduced over the team, and dx is written from
+// the registers. Every input is read before any output is written, so dx
+// may be y or dy.
+template <int VEC, int E, int TEAM>
+__global__ __launch_bounds__(256) void row_softmax_bwd_kernel(RowBwdArgs a) {
+  using V = Vec<VEC>;
+  using VT = typename V::T;
+  __shared__ float red[8];
+  constexpr int kRowsPerWG = 256 / TEAM;
+  const int t = threadIdx.x % TEAM;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerWG + threadIdx.x / TEAM;
+  const bool live = row < a.rows;  // uniform per team
+  const float* yr = a.y + (live ? row : 0) * (int64_t)a.cols;
+  const float* gr = a.dy + (live ? row : 0) * (int64_t)a.cols;
+  VT y[E], g[E];
+  float dot = 0.f;
+#pragma unroll
+  for (int k = 0; k < E; ++k) {
+    const int32_t j0 = VEC * (t + TEAM * k);
+    if (live && j0 < a.cols) {
+      y[k] = *reinterpret_cast<const VT*>(yr + j0);
+      g[k] = *reinterpret_cast<const VT*>(gr + j0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        V::set(y[k], e, 0.f);
+        V::set(g[k], e, 0.f);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dot = __builtin_fmaf(V::get(y[k], e), V::get(g[k], e), dot);
+  }
+  dot = team_sum<TEAM>(dot, red);
+  if (!live) return;
+  float* orow = a.dx + row * (int64_t)a.cols;
+#pragma unroll
+  for (int k = 0; k < E; ++k) {
+    const int32_t j0 = VEC * (t + TEAM * k);
+    if (j0 < a.cols) {
+      VT o;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+        V::set(o, e, a.scale * (V::get(y[k], e) * (V::get(g[k], e) - dot)));
+      *reinterpret_cast<VT*>(orow + j0) = o;
+    }
+  }
+}
+
+// Softmax backward of rows longer than a team's registers: a workgroup per
+// row, the dot product in a first pass, dx in a second (each element is read
+// by the thread that then writes it, after the first pass has ended).
+template <int VEC>
+__global__ __launch_bounds__(256) void row_softmax_bwd_stream_kernel(RowBwdArgs a) {
+  using V = Vec<VEC>;
+  using VT = typename V::T;
+  __shared__ float red[8];
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const float* yr = a.y + row * (int64_t)a.cols;
+  const float* gr = a.dy + row * (int64_t)a.cols;
+  constexpr int kStep = 256 * VEC;
+  float dot = 0.f;
+  for (int32_t j0 = VEC * t; j0 < a.cols; j0 += kStep) {
+    const VT y = *reinterpret_cast<const VT*>(yr + j0);
+    const VT g = *reinterpret_cast<const VT*>(gr + j0);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dot = __builtin_fmaf(V::get(y, e), V::get(g, e), dot);
+  }
+  dot = team_sum<256>(dot, red);
+  float* orow = a.dx + row * (int64_t)a.cols;
+  for (int32_t j0 = VEC * t; j0 < a.cols; j0 += kStep) {
+    const VT y = *reinterpret_cast<const VT*>(yr + j0);
+    const VT g = *reinterpret_cast<const VT*>(gr + j0);
+    VT o;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) V::set(o, e, a.scale * (V::get(y, e) * (V::get(g, e) - dot)));
+    *reinterpret_cast<VT*>(orow + j0) = o;
+  }
+}
+
+template <int VEC, int E, int TEAM>
+hipError_t launch_bwd_resident(const RowBwdArgs& a, hipStream_t st) {
+  const int64_t nwg = (a.rows + (256 / TEAM) - 1) / (256 / TEAM);
+  hipLaunchKernelGGL((row_softmax_bwd_kernel<VEC, E, TEAM>), dim3((uint32_t)nwg), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int VEC, int TEAM>
+hipError_t launch_bwd_team(const RowBwdArgs& a, int e, hipStream_t st) {
+  switch (e) {
+    case 1: return launch_bwd_resident<VEC, 1, TEAM>(a, st);
+    case 2: return launch_bwd_resident<VEC, 2, TEAM>(a, st);
+    case 4: return launch_bwd_resident<VEC, 4, TEAM>(a, st);
+    case 8: return launch_bwd_resident<VEC, 8, TEAM>(a, st);
+    case 16: return launch_bwd_resident<VEC, 16, TEAM>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int VEC>
+hipError_t launch_bwd_vec(const RowBwdArgs& a, const RowPlan& p, hipStream_t st) {
+  if (p.stream) {
+    hipLaunchKernelGGL((row_softmax_bwd_stream_kernel<VEC>), dim3((uint32_t)a.rows), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  return p.team == 64 ? launch_bwd_team<VEC, 64>(a, p.per_lane, st)
+                      : launch_bwd_team<VEC, 256>(a, p.per_lane, st);
+}
+
 template <int MODE, int VEC, int E, int TEAM>
 hipError_t launch_resident(const RowArgs& a, hipStream_t st) {
   const int64_t nwg = (a.rows + (256 / TEAM) - 1) / (256 / TEAM);
@@ -286,6 +400,10 @@ RowPlan plan_rows(int64_t cols, bool vec4) {
   p.per_lane = 0;
   p.stream = true;
   return p;
+}
+
+hipError_t launch_rows_bwd(const RowBwdArgs& a, const RowPlan& p, hipStream_t st) {
+  return p.vec == 4 ? launch_bwd_vec<4>(a, p, st) : launch_bwd_vec<1>(a, p, st);
 }
 
 hipError_t launch_rows(int mode, const RowArgs& a, const RowPlan& p, hipStream_t st) {

@@ -726,6 +726,32 @@ int sma_scaled_causal_softmax(const float* in, float* out, size_t batch, size_t 
   return launch_row_op(sma::kRowScaled, in, nullptr, out, all_rows, cols, rows, causal, scale, stream);
 }
 
+int sma_softmax_rows_backward(const float* y, const float* dy, float* dx, size_t rows, size_t cols,
+                              double scale, void* stream) {
+  if (!std::isfinite(scale)) return SMA_ERR_INVALID_VALUE;
+  size_t n, nb;
+  if (!mul(rows, cols, &n) || !mul(n, sizeof(float), &nb)) return SMA_ERR_INVALID_VALUE;
+  if (cols > kMaxRowCols || rows > kMaxRows) return SMA_ERR_UNSUPPORTED;
+  if (n == 0) return SMA_OK;
+  if (!y || !dy || !dx) return SMA_ERR_NULL_POINTER;
+  if (!aligned(y, 4) || !aligned(dy, 4) || !aligned(dx, 4)) return SMA_ERR_MISALIGNED;
+  // dx may be y or dy itself (in place), but may not overlap either otherwise.
+  if (((const void*)dx != (const void*)y && overlap(y, nb, dx, nb)) ||
+      ((const void*)dx != (const void*)dy && overlap(dy, nb, dx, nb)))
+    return SMA_ERR_ALIASING;
+  sma::RowBwdArgs a{};
+  a.y = y;
+  a.dy = dy;
+  a.dx = dx;
+  a.rows = (int64_t)rows;
+  a.cols = (int32_t)cols;
+  a.scale = (float)scale;
+  const bool vec4 = cols % 4 == 0 && aligned(y, 16) && aligned(dy, 16) && aligned(dx, 16);
+  const sma::RowPlan plan = sma::plan_rows((int64_t)cols, vec4);
+  return sma::launch_rows_bwd(a, plan, static_cast<hipStream_t>(stream)) == hipSuccess ? SMA_OK
+                                                                                       : SMA_ERR_HIP;
+}
+
 const char* sma_status_string(int status) {
   switch (status) {
     case SMA_OK: return "SMA_OK: success";

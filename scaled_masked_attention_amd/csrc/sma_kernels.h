@@ -115,6 +115,16 @@ struct RowPlan {
 constexpr int kRowMaxPerLane = 16;  // vectors per lane of a register-resident row
 RowPlan plan_rows(int64_t cols, bool vec4);
 hipError_t launch_rows(int mode, const RowArgs& a, const RowPlan& p, hipStream_t s);
+// Softmax backward on (rows x cols) fp32: dx = scale * y * (dy - rowsum(y * dy)).
+struct RowBwdArgs {
+  const float* y;   // softmax output [rows][cols]
+  const float* dy;  // upstream gradient [rows][cols]
+  float* dx;        // [rows][cols]; may equal y or dy
+  int64_t rows;
+  int32_t cols;
+  float scale;
+};
+hipError_t launch_rows_bwd(const RowBwdArgs& a, const RowPlan& p, hipStream_t s);
 
 hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_fwd_f32_wsplit(const FwdArgs& a, int head_dim, bool causal, hipStream_t s);

@@ -249,6 +249,27 @@ def test_row_ops_host_checks():
     assert lib.sma_softmax_rows(X, Y, 1 << 31, 1, None) == UNSUP
 
 
+def test_softmax_backward_host_checks():
+    """sma_softmax_rows_backward's argument errors return before any HIP call."""
+    lib = sma.library()
+    Y, G, D = 0x10_0000_0000, 0x20_0000_0000, 0x30_0000_0000
+    f = lib.sma_softmax_rows_backward
+    assert f(None, None, None, 0, 5, 1.0, None) == OK                   # nothing to do
+    assert f(None, None, None, 4, 0, 1.0, None) == OK
+    assert f(Y, G, None, 3, 5, 1.0, None) == NULLP
+    assert f(None, G, D, 3, 5, 1.0, None) == NULLP
+    assert f(Y, None, D, 3, 5, 1.0, None) == NULLP
+    assert f(Y + 2, G, D, 3, 5, 1.0, None) == MISAL
+    assert f(Y, G, D + 2, 3, 5, 1.0, None) == MISAL
+    assert f(Y, G, Y + 4, 3, 5, 1.0, None) == ALIAS                    # partial overlap with y
+    assert f(Y, G, G + 8, 3, 5, 1.0, None) == ALIAS                    # partial overlap with dy
+    assert f(Y, G, D, 3, 5, float("nan"), None) == INVAL
+    assert f(Y, G, D, 3, 5, float("inf"), None) == INVAL
+    assert f(Y, G, D, 1 << 40, 1 << 40, 1.0, None) == INVAL
+    assert f(Y, G, D, 1, 1 << 31, 1.0, None) == UNSUP
+    assert f(Y, G, D, 1 << 31, 1, 1.0, None) == UNSUP
+
+
 def test_backward_workspace_and_host_checks():
     """sma_attention_bwd's argument errors return before any HIP call."""
     lib = sma.library()

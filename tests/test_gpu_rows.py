@@ -156,6 +156,78 @@ def test_in_place(cols):
     _check_p(_host(t), oracle.softmax_rows(x), "in place")
 
 
+# Softmax backward: dx = scale * y * (dy - sum_k y_k dy_k). The kernel's dot product runs in fp32
+# over at most 72 terms in sequence (64 per lane, then an 8-level tree over the lanes), so its
+# error is at most 72 * 2^-24 = 4.3e-6 of sum_k y_k |dy_k|; with the final products this gives
+# |dx_j - ref_j| <= BWD_TOL * |scale| * y_j * (|dy_j| + sum_k y_k |dy_k|) with a factor of 2 to spare.
+BWD_TOL = 1e-5
+
+
+def _check_bwd(dx, y, dy, scale, label):
+    ref = oracle.softmax_rows_backward(y, dy, scale)
+    y64, dy64 = y.astype(np.float64), np.abs(dy.astype(np.float64))
+    bound = BWD_TOL * abs(scale) * y64 * (dy64 + (y64 * dy64).sum(axis=1, keepdims=True))
+    assert dx.shape == ref.shape and np.all(np.isfinite(dx)), label
+    err = np.abs(dx - ref)
+    worst = float(np.max(err - bound, initial=0.0))
+    assert worst <= 0.0, f"{label}: error beyond the bound by {worst:.3e}"
+    assert np.all(dx[y == 0] == 0.0), f"{label}: nonzero gradient where y = 0"
+
+
+def _y_dy(rows, cols, seed, masked=False):
+    x = _x(rows, cols, seed)
+    if masked:
+        m = (np.random.default_rng(seed + 1).random((rows, cols)) < 0.5).astype(np.float32)
+        y = oracle.masked_softmax_rows(x, m).astype(np.float32)
+    else:
+        y = oracle.softmax_rows(x).astype(np.float32)
+    dy = np.random.default_rng(seed + 2).normal(size=(rows, cols)).astype(np.float32)
+    return y, dy
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.125, -0.5])
+@pytest.mark.parametrize("offset", [0, 1])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_softmax_rows_backward(shape, offset, scale):
+    import scaled_masked_attention_amd as sma
+
+    rows, cols = shape
+    y, dy = _y_dy(rows, cols, 11 * rows + cols, masked=(rows + cols) % 2 == 1)
+    dx = _host(sma.softmax_rows_backward(_dev(y, offset), _dev(dy, offset), scale=scale))
+    _check_bwd(dx, y, dy, scale, f"bwd {shape} +{offset} scale={scale}")
+
+
+@pytest.mark.parametrize("target", ["y", "dy"])
+@pytest.mark.parametrize("cols", [100, 4096, 40000])
+def test_softmax_rows_backward_in_place(cols, target):
+    import scaled_masked_attention_amd as sma
+
+    y, dy = _y_dy(5, cols, 3 * cols)
+    ty, tg = _dev(y), _dev(dy)
+    out = ty if target == "y" else tg
+    r = sma.softmax_rows_backward(ty, tg, scale=0.3, out=out)
+    assert r.data_ptr() == out.data_ptr()
+    _check_bwd(_host(out), y, dy, 0.3, f"in place over {target}")
+
+
+def test_softmax_rows_backward_closed_form_on_gpu():
+    """A one-hot y gives dx = 0 (dy_j - dot vanishes where y_j = 1, y_k = 0 elsewhere), and a
+    uniform y with dy = e_0 gives dx_j = scale * (delta_j0 - 1/n) / n."""
+    import scaled_masked_attention_amd as sma
+
+    n = 64
+    y = np.zeros((3, n), dtype=np.float32)
+    y[np.arange(3), [0, 17, 63]] = 1.0
+    dy = np.random.default_rng(4).normal(size=(3, n)).astype(np.float32)
+    assert np.all(_host(sma.softmax_rows_backward(_dev(y), _dev(dy))) == 0.0)
+    yu = np.full((2, n), 1.0 / n, dtype=np.float32)  # 1/64 is exact in fp32
+    e0 = np.zeros((2, n), dtype=np.float32)
+    e0[:, 0] = 1.0
+    dx = _host(sma.softmax_rows_backward(_dev(yu), _dev(e0), scale=2.0))
+    expect = 2.0 * (np.eye(1, n).repeat(2, 0) - 1.0 / n) / n
+    assert np.allclose(dx, expect, rtol=0, atol=1e-9)
+
+
 def test_empty_shapes():
     import torch
 
@@ -169,6 +241,8 @@ def test_empty_shapes():
     assert sma.softmax_rows(e).shape == (0, 9)
     assert sma.logsumexp_rows(e).shape == (0,)
     assert sma.scaled_causal_softmax(torch.zeros((0, 3, 3), device="cuda"), 1.0).shape == (0, 3, 3)
+    assert sma.softmax_rows_backward(e, e).shape == (0, 9)
+    assert sma.softmax_rows_backward(z, z).shape == (4, 0)
 
 
 def test_binding_rejects():
