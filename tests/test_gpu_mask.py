@@ -164,3 +164,29 @@ def test_masked_parity_every_kernel(kern, causal, d, form):
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_fwd_masked(q, k, v, mask, 1.0 / math.sqrt(d), causal)
     check_parity(_np(o), _np(lse), o_ref, lse_ref, dtype, f"mask {kern}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2])
+@pytest.mark.parametrize("kern", list(KERNELS))
+def test_masked_zero_and_negative_scale_every_kernel(kern, scale):
+    """Scale 0 (uniform weights over the admitted keys) and a negative scale, under a hard mask
+    with the causal mask on top, including rows the mask empties."""
+    import torch
+
+    import scaled_masked_attention_amd as sma
+    from helpers import to_device
+
+    dtype, kname, nsplit = KERNELS[kern]
+    B, H, sq, skv, d = 1, 2, 150, 170, 128
+    (q, k, v), bits = gen.random_case(1400, (B, H, sq, d), (B, H, skv, d),
+                                      sigma_qk=1.0 if dtype == "f32" else 3.0, dtype=dtype)
+    mask = _mask(1401, (1, 1, sq, skv), 0.5)
+    mask[0, 0, 30:34] = False  # four rows admit nothing
+    mask = mask.astype(np.uint8)
+    tq, tk, tv = to_device((q, k, v), bits, dtype)
+    o, lse = sma.attention_fwd(tq, tk, tv, scale=scale, causal=True, return_lse=True,
+                               mask=torch.from_numpy(mask).to("cuda"),
+                               kernel=getattr(sma, "SMA_KERNEL_" + kname), nsplit=nsplit)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd_masked(q, k, v, mask, scale, True)
+    check_parity(_np(o), _np(lse), o_ref, lse_ref, dtype, f"mask {kern} scale={scale}")
