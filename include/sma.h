@@ -111,7 +111,9 @@ typedef struct sma_plan {
  *   o_dtype    SMA_DTYPE_F32, or SMA_DTYPE_BF16: the fp32 result rounded to bf16 (nearest
  *              even) as it is stored. Either with any input type (SMA_DTYPE_F16 output ->
  *              UNSUPPORTED). LSE is always fp32.
- *   head_dim   64 or 128 (0 -> INVALID_VALUE, other values -> UNSUPPORTED).
+ *   head_dim   64 or 128 with every input type; also 32 or 256 with fp32 inputs, which
+ *              run on SMA_KERNEL_F32_QBLOCK only (0 -> INVALID_VALUE, other values and
+ *              other kernels -> UNSUPPORTED).
  *   scale      finite multiplier of QK^T (zero and negative values are allowed).
  *   causal     0: no mask; nonzero: bottom-right causal mask.
  *   workspace  optional device scratch for splitting the keys of a row across
@@ -159,7 +161,7 @@ size_t sma_attention_fwd_workspace_bytes(int in_dtype, size_t batch, size_t head
 
 /* The plan for a shape, on the host only (no launch). kernel: SMA_KERNEL_AUTO
  * for the library's own choice, else the kernel to plan for (one that does not
- * run in_dtype -> UNSUPPORTED). nsplit: 0 lets the library choose the key
+ * run in_dtype or head_dim -> UNSUPPORTED). nsplit: 0 lets the library choose the key
  * split; 1..32 asks for that many (the plan may merge splits so that each
  * keeps a whole number of key tiles, and SMA_KERNEL_F32_KSPLIT accepts only
  * 0 or 1, and only (seq_q + 32) and (seq_kv + 32) rows of head_dim floats of
@@ -256,7 +258,8 @@ size_t sma_attention_fwd_masked_workspace_bytes(int in_dtype, size_t batch, size
  *   q, o, dout, dq   [B,H,Sq,d];  k, v, dk, dv  [B,H,Skv,d];  lse [B,H,Sq].
  *   in_dtype         SMA_DTYPE_F32 (q, k, v, o, dout); SMA_DTYPE_BF16 -> UNSUPPORTED.
  *                    lse and the three gradients are fp32.
- *   head_dim, scale, causal, stream   as for sma_attention_fwd.
+ *   head_dim         64 or 128 (others -> UNSUPPORTED).
+ *   scale, causal, stream   as for sma_attention_fwd.
  *   workspace        required device scratch of at least
  *                    sma_attention_bwd_workspace_bytes bytes (smaller or NULL
  *                    when that is nonzero -> INVALID_VALUE); contents on entry

@@ -62,9 +62,13 @@ hipError_t launch_combine_variant(const CombineArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s) {
-  if (head_dim == 64) return launch_combine_variant<64>(a, s);
-  if (head_dim == 128) return launch_combine_variant<128>(a, s);
-  return hipErrorInvalidValue;
+  switch (head_dim) {
+    case 32: return launch_combine_variant<32>(a, s);
+    case 64: return launch_combine_variant<64>(a, s);
+    case 128: return launch_combine_variant<128>(a, s);
+    case 256: return launch_combine_variant<256>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace sma

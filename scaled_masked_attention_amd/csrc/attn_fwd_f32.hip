@@ -42,12 +42,11 @@ struct F32Geom {
   static_assert(kF4PerThread * 4 * kThreadsPerWG == kK * D, "tile split");
 };
 
+// D/32 consecutive floats: a lane's share of one output row, or of one V row.
 template <int N>
-struct FVec;
-template <>
-struct FVec<2> { typedef f32x2 T; };
-template <>
-struct FVec<4> { typedef f32x4 T; };
+struct FVec {
+  typedef float T __attribute__((ext_vector_type(N)));
+};
 
 // Lazy max: the running max moves only when a tile raises it by more than
 // this many log2 units, so most tiles skip the rescale of O. Probabilities
@@ -253,14 +252,14 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
     for (int cb = 0; cb < G::kNch; ++cb) out[cb] = empty ? 0.f : oacc[cb][r] * inv;
     if (orow16) {
-      unsigned packed[G::kNch / 2];
-#pragma unroll
-      for (int i = 0; i < G::kNch / 2; ++i) packed[i] = pack_bf16x2(out[2 * i], out[2 * i + 1]);
-      if constexpr (G::kNch == 4) {
-        typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<u32x2_t*>(orow16 + G::kNch * m) = u32x2_t{packed[0], packed[1]};
+      if constexpr (G::kNch == 1) {
+        orow16[m] = (unsigned short)(pack_bf16x2(out[0], 0.f) & 0xffffu);
       } else {
-        *reinterpret_cast<unsigned*>(orow16 + G::kNch * m) = packed[0];
+        typedef unsigned PackedT __attribute__((ext_vector_type(G::kNch / 2)));
+        PackedT packed;
+#pragma unroll
+        for (int i = 0; i < G::kNch / 2; ++i) packed[i] = pack_bf16x2(out[2 * i], out[2 * i + 1]);
+        *reinterpret_cast<PackedT*>(orow16 + G::kNch * m) = packed;
       }
     } else {
       *reinterpret_cast<VecN*>(orow + G::kNch * m) = out;
@@ -280,9 +279,13 @@ hipError_t launch_f32_variant(const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, bool causal, hipStream_t s) {
-  if (head_dim == 64) return causal ? launch_f32_variant<64, true>(a, s) : launch_f32_variant<64, false>(a, s);
-  if (head_dim == 128) return causal ? launch_f32_variant<128, true>(a, s) : launch_f32_variant<128, false>(a, s);
-  return hipErrorInvalidValue;
+  switch (head_dim) {
+    case 32: return causal ? launch_f32_variant<32, true>(a, s) : launch_f32_variant<32, false>(a, s);
+    case 64: return causal ? launch_f32_variant<64, true>(a, s) : launch_f32_variant<64, false>(a, s);
+    case 128: return causal ? launch_f32_variant<128, true>(a, s) : launch_f32_variant<128, false>(a, s);
+    case 256: return causal ? launch_f32_variant<256, true>(a, s) : launch_f32_variant<256, false>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace sma

@@ -64,7 +64,10 @@ int check_shape(int in_dtype, int o_dtype, size_t batch, size_t heads, size_t se
       !mul(nkv, elem_bytes(in_dtype), &s.kv_bytes) || !mul(nq, elem_bytes(o_dtype), &s.o_bytes) ||
       !mul(s.rows, sizeof(float), &s.lse_bytes))
     return SMA_ERR_INVALID_VALUE;
-  if (d != 64 && d != 128) return SMA_ERR_UNSUPPORTED;
+  // Head dims 64 and 128 run on every kernel; 32 and 256 on the fp32
+  // query-block kernel only (fp32 inputs).
+  if (d != 64 && d != 128 && !(in_dtype == SMA_DTYPE_F32 && (d == 32 || d == 256)))
+    return SMA_ERR_UNSUPPORTED;
   if (o_dtype == SMA_DTYPE_F16) return SMA_ERR_UNSUPPORTED;
   if (seq_q > kMaxSeq || seq_kv > kMaxSeq || s.bh > (size_t(1) << 31)) return SMA_ERR_UNSUPPORTED;
   if (heads > (size_t(1) << 20)) return SMA_ERR_UNSUPPORTED;
@@ -107,7 +110,10 @@ size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 // per split.
 size_t auto_splits(const Shape& s, int kernel, size_t base, int num_cus) {
   const size_t kt = (size_t)keys_per_tile(kernel);
-  const size_t slots = (size_t)num_cus * (kernel == SMA_KERNEL_BF16_QBLOCK ? 1 : 2);
+  // Resident workgroups per CU: one for the 16-bit kernel and for head dim 256
+  // (LDS-limited), two otherwise.
+  const size_t per_cu = kernel == SMA_KERNEL_BF16_QBLOCK || s.d > 128 ? 1 : 2;
+  const size_t slots = (size_t)num_cus * per_cu;
   size_t nsplit = 1;
   if (base > 0 && base < slots && s.seq_kv >= 8 * kt) {
     size_t want = (slots + base - 1) / base;
@@ -134,9 +140,14 @@ bool ksplit_fits(const Shape& s) {
   return (s.seq_q + 32) * s.row_elems * 4 <= lim && (s.seq_kv + 32) * s.row_elems * 4 <= lim;
 }
 
+// Kernels built for a head dim (the fp32 query-block kernel also for 32 and 256).
+bool kernel_fits_head_dim(int kernel, size_t d) {
+  return d == 64 || d == 128 || kernel == SMA_KERNEL_F32_QBLOCK;
+}
+
 int auto_kernel(const Shape& s, int num_cus) {
   if (s.in_dtype != SMA_DTYPE_F32) return SMA_KERNEL_BF16_QBLOCK;
-  if (!ksplit_fits(s)) return SMA_KERNEL_F32_QBLOCK;
+  if (!ksplit_fits(s) || !kernel_fits_head_dim(SMA_KERNEL_F32_KSPLIT, s.d)) return SMA_KERNEL_F32_QBLOCK;
   const size_t nwg32 = s.bh * ((s.seq_q + sma::kF32WsplitQueriesPerWG - 1) / sma::kF32WsplitQueriesPerWG);
   if (nwg32 >= (size_t)num_cus || s.seq_kv <= kKsplitAlwaysKeys) return SMA_KERNEL_F32_KSPLIT;
   return SMA_KERNEL_F32_QBLOCK;
@@ -293,7 +304,8 @@ int fwd_core(const void* q, const void* k, const void* v, void* o, float* lse, i
     if (plan->kernel != SMA_KERNEL_F32_QBLOCK && plan->kernel != SMA_KERNEL_F32_KSPLIT &&
         plan->kernel != SMA_KERNEL_BF16_QBLOCK)
       return SMA_ERR_INVALID_VALUE;
-    if (!kernel_fits_dtype(plan->kernel, in_dtype)) return SMA_ERR_UNSUPPORTED;
+    if (!kernel_fits_dtype(plan->kernel, in_dtype) || !kernel_fits_head_dim(plan->kernel, sh.d))
+      return SMA_ERR_UNSUPPORTED;
     if (plan->kernel == SMA_KERNEL_F32_KSPLIT && (plan->nsplit > 1 || !ksplit_fits(sh)))
       return SMA_ERR_UNSUPPORTED;
   }
@@ -439,7 +451,8 @@ int sma_attention_fwd_plan(int in_dtype, size_t batch, size_t heads, size_t seq_
     if (kernel != SMA_KERNEL_F32_QBLOCK && kernel != SMA_KERNEL_F32_KSPLIT &&
         kernel != SMA_KERNEL_BF16_QBLOCK)
       return SMA_ERR_INVALID_VALUE;
-    if (!kernel_fits_dtype(kernel, in_dtype)) return SMA_ERR_UNSUPPORTED;
+    if (!kernel_fits_dtype(kernel, in_dtype) || !kernel_fits_head_dim(kernel, sh.d))
+      return SMA_ERR_UNSUPPORTED;
     if (kernel == SMA_KERNEL_F32_KSPLIT && (nsplit > 1 || !ksplit_fits(sh))) return SMA_ERR_UNSUPPORTED;
   }
   int cus = num_cus;
@@ -543,7 +556,7 @@ int check_bwd_shape(int in_dtype, size_t batch, size_t heads, size_t seq_q, size
                     size_t d, double scale, BwdShape* b) {
   int st = check_shape(in_dtype, SMA_DTYPE_F32, batch, heads, seq_q, seq_kv, d, scale, &b->s);
   if (st != SMA_OK) return st;
-  if (in_dtype != SMA_DTYPE_F32) return SMA_ERR_UNSUPPORTED;
+  if (in_dtype != SMA_DTYPE_F32 || (d != 64 && d != 128)) return SMA_ERR_UNSUPPORTED;
   const size_t blk = sma::kBwdRowsPerBlock;
   if ((seq_q + blk) * d * 4 > (size_t(1) << 31) || (seq_kv + blk) * d * 4 > (size_t(1) << 31))
     return SMA_ERR_UNSUPPORTED;

@@ -55,6 +55,7 @@ def test_valid_calls():
     assert _v(idt=F16, d=128) == OK and _v(idt=F16, odt=BF16, d=64) == OK
     assert _v(lse=None) == OK
     assert _v(scale=-1.0) == OK and _v(scale=0.0) == OK
+    assert _v(d=32) == OK and _v(d=256) == OK and _v(d=256, odt=BF16) == OK  # fp32 inputs only
 
 
 def test_null_pointers():
@@ -76,8 +77,9 @@ def test_invalid_values():
 
 
 def test_unsupported():
-    assert _v(d=96) == UNSUP
-    assert _v(d=256) == UNSUP
+    assert _v(d=96) == UNSUP and _v(d=16) == UNSUP and _v(d=512) == UNSUP
+    for d in (32, 256):  # head dims the 16-bit kernel is not built for
+        assert _v(idt=BF16, d=d) == UNSUP and _v(idt=F16, odt=BF16, d=d) == UNSUP
     assert _v(odt=BF16, idt=BF16, d=96) == UNSUP
     assert _v(odt=F16) == UNSUP and _v(odt=F16, idt=F16) == UNSUP  # fp16 output not built
     assert _v(idt=F16, d=128, skv=1 << 23) == UNSUP
@@ -153,6 +155,16 @@ def test_plan_auto_choices():
     assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_BF16_QBLOCK, 1, 32 * 64)
     p = P(F32, 1, 1, 1, 4096, 64, False, num_cus=256)  # one query row, many keys
     assert p.kernel == sma.SMA_KERNEL_F32_QBLOCK and p.nsplit == 32
+    # head dims 32 and 256 go to the 128-row fp32 kernel; at 256 one workgroup fits a CU
+    p = P(F32, 8, 16, 2048, 2048, 32, True, num_cus=256)
+    assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_F32_QBLOCK, 1, 8 * 16 * 16)
+    p = P(F32, 1, 4, 256, 8192, 256, False, num_cus=256)  # 8 blocks: split to 32 per block
+    assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_F32_QBLOCK, 32, 8 * 32)
+    assert p.workspace_bytes == sma.workspace_bytes(F32, 1, 4, 256, 8192, 256, False, 256)
+    assert p.workspace_bytes >= 32 * 4 * 256 * 257 * 4
+    p = P(F32, 1, 4, 256, 8192, 64, False, num_cus=256)  # two workgroups per CU at 64
+    assert p.nsplit == 32 and P(F32, 1, 16, 256, 8192, 256, False, num_cus=256).nsplit == 8
+    assert P(F32, 1, 16, 256, 8192, 64, False, num_cus=256).nsplit == 16
 
 
 def test_plan_forced():
@@ -194,6 +206,12 @@ def test_plan_rejects():
     with pytest.raises(sma.SMAError) as e:
         P(F32, 1, 1, 8, 8, 96, False)
     assert e.value.status == UNSUP
+    for d in (32, 256):  # only the 128-row fp32 kernel is built for these head dims
+        for kern, idt in ((sma.SMA_KERNEL_F32_KSPLIT, F32), (sma.SMA_KERNEL_BF16_QBLOCK, BF16)):
+            with pytest.raises(sma.SMAError) as e:
+                P(idt, 1, 1, 8, 8, d, False, kernel=kern)
+            assert e.value.status == UNSUP
+        assert P(F32, 1, 1, 8, 8, d, False, kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=1).nsplit == 1
     lib = sma.library()
     assert lib.sma_attention_fwd_plan(F32, 1, 1, 8, 8, 64, 0, -1, 0, 256, None) == NULLP
 
@@ -293,6 +311,8 @@ def test_backward_workspace_and_host_checks():
     assert call(d=0) == INVAL and call(scale=float("inf")) == INVAL
     assert call(B=1 << 40, H=1 << 40) == INVAL
     assert call(d=96) == UNSUP and call(idt=BF16) == UNSUP and call(idt=F16) == UNSUP
+    assert call(d=32) == UNSUP and call(d=256) == UNSUP                      # forward-only head dims
+    assert sma.attention_bwd_workspace_bytes(F32, 1, 1, 33, 50, 256, False) == 0
     assert call(sq=(1 << 23), d=64) == UNSUP                                 # 32-bit tile offsets
     assert call(q=q + 8) == MISAL and call(dk=dk + 4) == MISAL and call(lse=lse + 2) == MISAL
     assert call(ws=ws + 8) == MISAL

@@ -1,0 +1,194 @@
+"""Head dims 32 and 256 (fp32 inputs, the 128-row fp32 kernel and the split combine), through
+the C ABI, against the oracle.
+
+Ragged shapes that span several query blocks and key tiles, causal and not, unsplit and split
+across workgroups (forced and automatic), a hard mask, the bshd layout, bf16 output, rows
+with no admitted key, and zero and negative scales.
+"""
+import functools
+import math
+
+import numpy as np
+import pytest
+
+import gen
+import oracle
+from helpers import check_parity, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+HEAD_DIMS = [32, 256]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import scaled_masked_attention_amd as sma
+
+    sma.library()
+
+
+def _qblock(nsplit):
+    import scaled_masked_attention_amd as sma
+
+    return dict(kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=nsplit)
+
+
+SHAPES = [(1, 2, 128, 128), (2, 3, 200, 200), (1, 2, 77, 300), (2, 1, 300, 77), (1, 1, 1, 1000),
+          (1, 1, 513, 513), (1, 3, 257, 1025)]
+
+
+@functools.lru_cache(maxsize=4)
+def _case(shape, causal, d):
+    B, H, sq, skv = shape
+    (q, k, v), _ = gen.random_case(500 + sq + 7 * skv + d, (B, H, sq, d), (B, H, skv, d))
+    scale = 1.0 / math.sqrt(d)
+    return (q, k, v), scale, oracle.attention_fwd(q, k, v, scale, causal)
+
+
+@pytest.mark.parametrize("plan", ["auto", "unsplit", "split3"])
+@pytest.mark.parametrize("d", HEAD_DIMS)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_parity(shape, causal, d, plan):
+    (q, k, v), scale, (o_ref, lse_ref) = _case(shape, causal, d)
+    kw = {} if plan == "auto" else _qblock(1 if plan == "unsplit" else 3)
+    o, lse = run_gpu(*to_device((q, k, v), None, "f32"), scale, causal, **kw)
+    check_parity(o, lse, o_ref, lse_ref, "f32", f"{shape} causal={causal} d={d} {plan}")
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_automatic_split_matches_oracle_and_unsplit(d, causal):
+    """Few query blocks and long rows: the planner splits keys across workgroups."""
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    B, H, sq, skv = 1, 2, 200, 3000
+    (q, k, v), _ = gen.random_case(600 + d, (B, H, sq, d), (B, H, skv, d))
+    assert sma.plan(sma.SMA_DTYPE_F32, B, H, sq, skv, d, causal).nsplit > 1
+    dev = to_device((q, k, v), None, "f32")
+    o_s, l_s = run_gpu(*dev, 0.07, causal)
+    o_n, l_n = run_gpu(*dev, 0.07, causal, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, 0.07, causal)
+    check_parity(o_s, l_s, o_ref, lse_ref, "f32", f"d={d} split")
+    check_parity(o_n, l_n, o_ref, lse_ref, "f32", f"d={d} unsplit")
+
+
+@pytest.mark.parametrize("nsplit", [1, 3])
+@pytest.mark.parametrize("form", ["shared", "full"])
+@pytest.mark.parametrize("d", HEAD_DIMS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_masked(causal, d, form, nsplit):
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    B, H, sq, skv = 2, 2, 300, 333
+    (q, k, v), _ = gen.random_case(700 + d, (B, H, sq, d), (B, H, skv, d))
+    shape = (1, 1, sq, skv) if form == "shared" else (B, H, sq, skv)
+    n = int(np.prod(shape))
+    mask = gen.uniform24(701 + causal, np.arange(n, dtype=np.uint64)).reshape(shape) < 0.5
+    mask[..., 40:44, :] = False  # rows that admit nothing
+    mask = mask.astype(np.uint8)
+    tq, tk, tv = to_device((q, k, v), None, "f32")
+    o, lse = sma.attention_fwd(tq, tk, tv, scale=0.1, causal=causal, return_lse=True,
+                               mask=torch.from_numpy(mask).to("cuda"), **_qblock(nsplit))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd_masked(q, k, v, mask, 0.1, causal)
+    check_parity(o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), o_ref,
+                 lse_ref, "f32", f"mask d={d} {form} nsplit={nsplit}")
+
+
+@pytest.mark.parametrize("nsplit", [1, 3])
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_bshd_layout_and_bf16_output(d, nsplit):
+    """bshd equals bhsd transposed, bit for bit; bf16 output is the fp32 output rounded to
+    nearest even."""
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    B, H, sq, skv = 2, 3, 190, 230
+    (q, k, v), _ = gen.random_case(800 + d, (B, H, sq, d), (B, H, skv, d))
+    tq, tk, tv = to_device((q, k, v), None, "f32")
+    kw = _qblock(nsplit)
+    o1, l1 = sma.attention_fwd(tq, tk, tv, scale=0.1, causal=True, return_lse=True, **kw)
+    t2 = [x.transpose(1, 2).contiguous() for x in (tq, tk, tv)]
+    o2, l2 = sma.attention_fwd(*t2, scale=0.1, causal=True, return_lse=True, layout="bshd", **kw)
+    o3 = sma.attention_fwd(tq, tk, tv, scale=0.1, causal=True, out_dtype=torch.bfloat16, **kw)
+    o4 = sma.attention_fwd(*t2, scale=0.1, causal=True, layout="bshd", out_dtype=torch.bfloat16, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.transpose(1, 2), o1) and torch.equal(l1, l2)
+    bits = gen.f32_to_bf16_bits(o1.cpu().numpy())
+    assert np.array_equal(o3.view(torch.int16).cpu().numpy().view(np.uint16), bits)
+    assert np.array_equal(o4.transpose(1, 2).contiguous().view(torch.int16).cpu().numpy()
+                          .view(np.uint16), bits)
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, 0.1, True)
+    check_parity(o1.cpu().numpy().astype(np.float64), l1.cpu().numpy().astype(np.float64), o_ref,
+                 lse_ref, "f32", f"d={d}")
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_no_keys_and_rows_without_keys(d):
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    q = torch.randn(1, 2, 70, d, device="cuda")
+    k = torch.empty(1, 2, 0, d, device="cuda")
+    out = torch.full((1, 2, 70, d), float("nan"), device="cuda")
+    o, lse = sma.attention_fwd(q, k, k, causal=False, return_lse=True, out=out, **_qblock(1))
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and not torch.any(torch.signbit(o)) and torch.all(torch.isneginf(lse))
+    # causal with more queries than keys: the first sq - skv rows admit nothing
+    (qn, kn, vn), _ = gen.random_case(900 + d, (1, 2, 150, d), (1, 2, 100, d))
+    for nsplit in (1, 2):
+        o, lse = run_gpu(*to_device((qn, kn, vn), None, "f32"), 0.2, True, **_qblock(nsplit))
+        assert np.all(o[:, :, :50] == 0) and np.all(np.isneginf(lse[:, :, :50]))
+        o_ref, lse_ref = oracle.attention_fwd(qn, kn, vn, 0.2, True)
+        check_parity(o, lse, o_ref, lse_ref, "f32", f"d={d} nsplit={nsplit}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 2.5])
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_zero_negative_and_large_scale(d, scale):
+    """Inputs are multiples of 1/2 in [-1, 1], so every dot product is exact in fp32 and the
+    fp32 bar holds even where scale * |s| reaches the hundreds."""
+    (q, k, v), _ = gen.random_case(1000 + d, (1, 2, 160, d), (1, 2, 200, d))
+    q, k = ((np.clip(np.round(x * 2), -2, 2) / 2).astype(np.float32) for x in (q, k))
+    for nsplit in (1, 2):
+        o, lse = run_gpu(*to_device((q, k, v), None, "f32"), scale, True, **_qblock(nsplit))
+        o_ref, lse_ref = oracle.attention_fwd(q, k, v, scale, True)
+        check_parity(o, lse, o_ref, lse_ref, "f32", f"d={d} scale={scale} nsplit={nsplit}")
+
+
+def test_large_scale_random_scores_within_rounding_bound():
+    """N(0, 1) inputs at head dim 256 and scale 2.5. Each score is a dot product rounded in
+    fp32, and exp turns its absolute error into a relative error of p. So O moves by about
+    scale * u * sum_c |q_c k_c| * max|v| (u = 2^-24): about 1.4e-4 here, beyond the plain fp32
+    bar. Bound used: 2e-5 plus twice that, with the largest sum over all (i, j)."""
+    d, scale = 256, 2.5
+    (q, k, v), _ = gen.random_case(1050, (1, 2, 160, d), (1, 2, 200, d))
+    o, lse = run_gpu(*to_device((q, k, v), None, "f32"), scale, True, **_qblock(1))
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, scale, True)
+    absdot = np.einsum("bhic,bhjc->bhij", np.abs(q.astype(np.float64)), np.abs(k.astype(np.float64)))
+    tol = 2e-5 + 2 * 2.0**-24 * scale * absdot.max() * np.abs(v).max()
+    err = float(np.abs(o - o_ref).max())
+    assert err <= tol, (err, tol)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lse_ref))
+    fin = np.isfinite(lse_ref)
+    assert np.all(np.abs(lse[fin] - lse_ref[fin]) <= tol * np.maximum(1.0, np.abs(lse_ref[fin])))
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_deterministic_bitwise(d):
+    (q, k, v), _ = gen.random_case(1100 + d, (2, 2, 300, d), (2, 2, 400, d))
+    dev = to_device((q, k, v), None, "f32")
+    for nsplit in (1, 3):
+        a = run_gpu(*dev, 0.1, False, **_qblock(nsplit))
+        b = run_gpu(*dev, 0.1, False, **_qblock(nsplit))
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
