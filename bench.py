@@ -195,7 +195,7 @@ BWD_PREFIX = "bwd_"
 def gen_workloads():
     import gen
 
-    bwd = [BWD_PREFIX + n for n, w in gen.WORKLOADS.items() if w.dtype == "f32"]
+    bwd = [BWD_PREFIX + n for n, w in gen.WORKLOADS.items() if w.dtype == "f32" and w.head_dim in (64, 128)]
     return list(gen.WORKLOADS) + bwd + list(gen.ROW_WORKLOADS)
 
 

@@ -226,6 +226,8 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
     _w("f32_cross_causal_b2h32_q256_kv4096_d128", "f32", 2, 32, 256, 4096, 128, True, 1.0 / math.sqrt(128), 1.0, 1.0, 20261205),
     _w("bf16_causal_b1h32_s16384_d128", "bf16", 1, 32, 16384, 16384, 128, True, 1.0 / math.sqrt(128), 3.0, 1.0, 20261206),
     _w("f16_causal_b1h32_s16384_d128", "f16", 1, 32, 16384, 16384, 128, True, 1.0 / math.sqrt(128), 3.0, 1.0, 20261207),
+    _w("f32_causal_b8h16_s2048_d32", "f32", 8, 16, 2048, 2048, 32, True, 1.0 / math.sqrt(32), 1.0, 1.0, 20261220),
+    _w("f32_causal_b8h16_s2048_d256", "f32", 8, 16, 2048, 2048, 256, True, 1.0 / math.sqrt(256), 1.0, 1.0, 20261221),
 )}
 
 

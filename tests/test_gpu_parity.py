@@ -119,7 +119,8 @@ def test_parity_full_size_qblock_sampled(name):
 
 @pytest.mark.parametrize("name", ["f32_causal_b8h16_s2048_d128", "f32_cross_b2h32_q256_kv4096_d128",
                                   "f32_cross_causal_b2h32_q256_kv4096_d128", "bf16_causal_b1h32_s16384_d128",
-                                  "f16_causal_b1h32_s16384_d128"])
+                                  "f16_causal_b1h32_s16384_d128", "f32_causal_b8h16_s2048_d32",
+                                  "f32_causal_b8h16_s2048_d256"])
 def test_parity_full_size_sampled(name):
     w, vals, bits = workload_case(name)
     o, lse = run_gpu(*to_device(vals, bits, w.dtype), w.scale, w.causal)
