@@ -44,6 +44,22 @@ struct Vec<4> {
   static __device__ __forceinline__ void set(T& v, int e, float x) { v[e] = x; }
 };
 
+// Streaming memory access. Every output row is written with non-temporal
+// stores (it is not read again by this launch), which measured 12-17 %
+// faster on 512-column rows and no slower elsewhere. A register-resident row
+// of a 256-thread team is also read with non-temporal loads (1-3 % faster
+// there); shorter rows, and logsumexp (no store stream), use ordinary loads,
+// which measured faster for them.
+template <bool NT, class T>
+__device__ __forceinline__ T load_row(const float* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  else return *reinterpret_cast<const T*>(p);
+}
+template <class T>
+__device__ __forceinline__ void store_row(float* p, const T& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
+}
+
 // Keys j < limit are admitted by the causal mask (bottom-right: j <= r + cols
 // - rows_per_matrix for row r of its matrix); every key without the mask.
 __device__ __forceinline__ int32_t causal_limit(const RowArgs& a, int64_t row) {
@@ -111,6 +127,7 @@ __global__ __launch_bounds__(256) void row_softmax_kernel(RowArgs a) {
   const float* mr = MODE == kRowMasked ? a.mask + (live ? row : 0) * (int64_t)a.cols : nullptr;
   const int32_t lim = MODE == kRowScaled ? causal_limit(a, live ? row : 0) : a.cols;
 
+  constexpr bool kNtLoad = TEAM == 256 && MODE != kRowLse;
   VT s[E];
   float m = -INFINITY;
 #pragma unroll
@@ -118,8 +135,8 @@ __global__ __launch_bounds__(256) void row_softmax_kernel(RowArgs a) {
     const int32_t j0 = VEC * (t + TEAM * k);
     VT x, mv;
     if (live && j0 < a.cols) {
-      x = *reinterpret_cast<const VT*>(xr + j0);
-      if (MODE == kRowMasked) mv = *reinterpret_cast<const VT*>(mr + j0);
+      x = load_row<kNtLoad, VT>(xr + j0);
+      if (MODE == kRowMasked) mv = load_row<kNtLoad, VT>(mr + j0);
     } else {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) V::set(x, e, -INFINITY);
@@ -165,7 +182,7 @@ __global__ __launch_bounds__(256) void row_softmax_kernel(RowArgs a) {
       VT o;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) V::set(o, e, V::get(s[k], e) * inv);
-      *reinterpret_cast<VT*>(orow + j0) = o;
+      store_row(orow + j0, o);
     }
   }
 }
@@ -231,7 +248,7 @@ __global__ __launch_bounds__(256) void row_softmax_stream_kernel(RowArgs a) {
       const float p = (empty || sc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sc - m) * cabs) * inv;
       V::set(o, e, p);
     }
-    *reinterpret_cast<VT*>(orow + j0) = o;
+    store_row(orow + j0, o);
   }
 }
 
@@ -257,8 +274,8 @@ __global__ __launch_bounds__(256) void row_softmax_bwd_kernel(RowBwdArgs a) {
   for (int k = 0; k < E; ++k) {
     const int32_t j0 = VEC * (t + TEAM * k);
     if (live && j0 < a.cols) {
-      y[k] = *reinterpret_cast<const VT*>(yr + j0);
-      g[k] = *reinterpret_cast<const VT*>(gr + j0);
+      y[k] = load_row<TEAM == 256, VT>(yr + j0);
+      g[k] = load_row<TEAM == 256, VT>(gr + j0);
     } else {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
@@ -280,7 +297,7 @@ __global__ __launch_bounds__(256) void row_softmax_bwd_kernel(RowBwdArgs a) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e)
         V::set(o, e, a.scale * (V::get(y[k], e) * (V::get(g[k], e) - dot)));
-      *reinterpret_cast<VT*>(orow + j0) = o;
+      store_row(orow + j0, o);
     }
   }
 }
@@ -313,7 +330,7 @@ __global__ __launch_bounds__(256) void row_softmax_bwd_stream_kernel(RowBwdArgs 
     VT o;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) V::set(o, e, a.scale * (V::get(y, e) * (V::get(g, e) - dot)));
-    *reinterpret_cast<VT*>(orow + j0) = o;
+    store_row(orow + j0, o);
   }
 }
 
