@@ -324,10 +324,11 @@ def attention_bwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, dout_ptr, dq_ptr, dk_
 def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=None):
     """(dQ, dK, dV) of O = softmax(scale * Q K^T + mask) V for the upstream gradient dout.
 
-    q, o, dout [B,H,Sq,D] and k, v [B,H,Skv,D] contiguous float32 tensors on the
-    current HIP device; o and lse ([B,H,Sq] float32) as attention_fwd returned
-    them for the same q, k, v, scale and causal. Returns three float32 tensors
-    shaped like q, k and v. The workspace is allocated when not given.
+    q, o, dout [B,H,Sq,D] and k, v [B,H,Skv,D] contiguous tensors on the current
+    HIP device: q, k, v all float32 or all bfloat16 (then on 16-bit MFMA), o, dout
+    and lse ([B,H,Sq]) float32, o and lse as attention_fwd returned them for the
+    same q, k, v, scale and causal. Returns three float32 tensors shaped like q, k
+    and v. The workspace is allocated when not given.
     """
     import torch
 
@@ -344,8 +345,11 @@ def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=Non
             tuple(lse.shape) != (B, H, Sq)):
         raise ValueError("shape mismatch among q, k, v, o, lse, dout")
     dev = torch.device("cuda", torch.cuda.current_device())
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("q, k, v must be all float32 or all bfloat16")
+    in_dt = SMA_DTYPE_F32 if q.dtype == torch.float32 else SMA_DTYPE_BF16
     for name, t in ts.items():
-        if t.dtype != torch.float32:
+        if name in ("o", "lse", "dout") and t.dtype != torch.float32:
             raise ValueError(f"{name} must be float32")
         if t.device != dev:
             raise ValueError(f"{name} is on {t.device}, the current HIP device is {dev}")
@@ -353,10 +357,10 @@ def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=Non
             raise ValueError(f"{name} must be contiguous")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
-    need = attention_bwd_workspace_bytes(SMA_DTYPE_F32, B, H, Sq, Skv, D, causal)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    need = attention_bwd_workspace_bytes(in_dt, B, H, Sq, Skv, D, causal)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -364,7 +368,7 @@ def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=Non
     if stream is None:
         stream = torch.cuda.current_stream()
     attention_bwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
-                      _ptr(dv), SMA_DTYPE_F32, B, H, Sq, Skv, D, scale, causal, ws_ptr, ws_bytes,
+                      _ptr(dv), in_dt, B, H, Sq, Skv, D, scale, causal, ws_ptr, ws_bytes,
                       stream.cuda_stream)
     return dq, dk, dv
 

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsma.so")
 SOURCES = ["sma_host.cpp", "attn_fwd_f32.hip", "attn_fwd_f32_wsplit.hip", "attn_fwd_bf16.hip",
-           "attn_combine.hip", "row_softmax.hip", "attn_bwd_f32.hip", "mask_pack.hip"]
+           "attn_combine.hip", "row_softmax.hip", "attn_bwd_f32.hip", "attn_bwd_bf16.hip",
+           "mask_pack.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

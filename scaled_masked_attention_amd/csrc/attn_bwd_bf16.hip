@@ -1,0 +1,559 @@
+// Attention backward with bf16 Q, K, V on 16-bit MFMA (v_mfma_f32_32x32x16_bf16, fp32
+// accumulation): dQ, dK and dV (fp32) of O = softmax(scale * Q K^T + causal mask) V, from
+// the forward's fp32 O and log-sum-exp and an fp32 upstream gradient dO (oxicuda
+// ComputeBackend `attention` for the forward; the softmax vector-Jacobian product of
+// pulsatrix HIPBackend `softmax_rows_backward` and of MicroGPT's fused attention-softmax
+// backward; the operand precision of oxicuda `gemm_mixed_precision`: 16-bit operands, fp32
+// accumulation and result).
+//
+// The arithmetic and the three launches are those of the fp32 backward:
+//   P_ij = 2^(c s_ij - lse2_i), D_i = dO_i . O_i, dP_ij = dO_i . v_j, dS_ij = P_ij (dP_ij - D_i),
+//   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j,
+// with three roundings to bf16 (nearest even) for the products: dO once, in the
+// preprocess (D stays the fp32 dot product of the fp32 dO and O); P for dV; dS for dK
+// and dQ. P and dS themselves are formed in fp32 from fp32 scores.
+//
+// MFMA layouts (lane = 32*h + m; accumulator register r of lane (n, h) holds row
+// 8*(r/4) + 4*h + r%4 of output column n):
+//  - The tiles that are A operands of the score products (Q and dO in the dK/dV kernel,
+//    K and V in the dQ kernel) are stored with bits 2 and 3 of the row index swapped.
+//    Register r of a score accumulator then holds original row 16*(r/8) + 8*h + r%8, so
+//    registers 8t..8t+7 are the eight rows this lane supplies, as the B operand, to k-step
+//    t of the next product (dV^T += dO^T P, dK^T += Q^T dS, dQ^T += K^T dS^T).
+//  - The A operands of those products (dO^T, Q^T, K^T) come from the same tiles through
+//    the transposing read ds_read_b64_tr_b16: tile rows 16t + 4h + 0..3 and
+//    16t + 8 + 4h + 0..3 hold original rows 16t + 8h + 0..7.
+//  - The B operands of the score products (K and V in the dK/dV kernel, Q and dO in the
+//    dQ kernel) stay in registers for the whole pass, read once from unpermuted tiles.
+//  - Every tile is XOR-swizzled in 16-byte chunks (swz below), which keeps both the
+//    16-byte row reads (16 lanes, 16 consecutive rows, one chunk) and the transposing
+//    reads (32 lanes, 4 consecutive rows, one 64-byte group) free of bank conflicts.
+#include "attn_common.h"
+
+namespace sma {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+template <int D>
+struct HGeom {
+  static constexpr int kWaves = 4;
+  static constexpr int kRows = kBwdRowsPerBlock;    // rows per query / key block
+  static constexpr int kSteps = D / 16;             // k-steps of the score products
+  static constexpr int kNch = D / 32;               // 32-wide output chunks
+  static constexpr int kRowBytes = 2 * D;           // one bf16 row
+  static constexpr int kChunks = D / 8;             // 16-byte chunks per row
+  static constexpr int kTileBytes = kRows * kRowBytes;
+  static constexpr int kDmaPerTile = kTileBytes / 1024;
+  static constexpr int kMetaBytes = kBwdMetaFloats * 4;
+  static constexpr int kPStride = D + 4;            // padded partial-gradient row (floats)
+  static constexpr int kPartBytes = kWaves * kRows * kPStride * 4;
+  static_assert(kRows == 32, "one 32x32 MFMA tile per block");
+  static_assert(kDmaPerTile % kWaves == 0, "shared tile copies split evenly over the waves");
+  static_assert(kBwdMetaFloats == 64, "one 4-byte direct-to-LDS load per block's lse2 and D");
+};
+
+__device__ __forceinline__ f32x16 mfma16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Original row held in accumulator register r of half h under the row permutation.
+__device__ __forceinline__ int perm_acc_row(int r, int h) { return 16 * (r / 8) + 8 * h + (r % 8); }
+// Bits 2 and 3 of a tile row swapped (its own inverse).
+__device__ __forceinline__ int swap_bits_2_3(int p) {
+  return (p & ~0xC) | ((p & 4) << 1) | ((p & 8) >> 1);
+}
+// Chunk swizzle of tile row p. d = 128 (256-byte rows, every row on all 64 banks): the
+// 16 rows of a row read must land on 16 different chunks, and the 4 rows of a
+// transposing read on 4 different 64-byte groups; 4*(p&3) + ((p>>2)&3) does both.
+// d = 64 (128-byte rows, two rows per bank cycle): the same over rows of one parity,
+// 4*((p>>1)&1) + ((p>>2)&3).
+template <int D>
+__device__ __forceinline__ int swz(int p) {
+  return D == 128 ? 4 * (p & 3) + ((p >> 2) & 3) : 4 * ((p >> 1) & 1) + ((p >> 2) & 3);
+}
+
+// Byte offset, from the tile's first row in global memory, of the 16 bytes that lane
+// `lane` of direct-to-LDS copy instruction t fetches: LDS chunk position P = 64t + lane is
+// tile row p = P / chunks, chunk slot P % chunks, which holds logical chunk
+// slot ^ swz(p) of source row p (or of row swap_bits_2_3(p) in a permuted tile).
+template <int D, bool PERM>
+__device__ __forceinline__ unsigned tile_src(int t, int lane) {
+  constexpr int kC = D / 8;
+  const int pos = 64 * t + lane;
+  const int p = pos / kC;
+  const int c = (pos % kC) ^ swz<D>(p);
+  return (unsigned)((PERM ? swap_bits_2_3(p) : p) * 2 * D + 16 * c);
+}
+
+// The 8 bf16 at logical chunk c of tile row p (a row read).
+template <int D>
+__device__ __forceinline__ bf16x8 row_chunk(const unsigned char* tile, int p, int c) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                        tile + p * 2 * D + 16 * (c ^ swz<D>(p))));
+}
+
+// Transposed A operand of k-step t2 and output chunk cb from a permuted tile: lane
+// (c, h) receives original rows 16*t2 + 8*h + 0..7 at head dim 32*cb + c. In each 16-lane
+// group, lane role s reads 4 dims of tile row 16*t2 + 4*h + s/4 (elements 0..3) and of
+// that row + 8 (elements 4..7).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, int lane, int t2, int cb) {
+  const int s = lane & 15;
+  const int colq = 2 * ((lane >> 4) & 1) + ((s & 3) >> 1);  // chunk within a 32-dim group
+  const int half8 = 8 * (s & 1);
+  const int r_lo = 16 * t2 + 4 * (lane >> 5) + s / 4;
+  const int r_hi = r_lo + 8;
+  const int chunk = 4 * cb + colq;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(tile + r_lo * 2 * D + 16 * (chunk ^ swz<D>(r_lo)) + half8));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(tile + r_hi * 2 * D + 16 * (chunk ^ swz<D>(r_hi)) + half8));
+  const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+}
+
+// ---------------------------------------------------------------- preprocess
+
+// Per 32-row query block: lse2 = LSE log2(e) (+inf for a row without admitted keys or past
+// the end, which makes its P exactly 0) and D = dO . O in fp32, as 64 floats of meta; and
+// dO rounded to bf16 into the workspace copy the products read.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(BwdArgs a) {
+  constexpr int kT = D / 4;  // threads per row, 4 head dims each
+  constexpr int kRowsPerPass = 256 / kT;
+  const int64_t blk = blockIdx.x;  // (batch*head, query block)
+  const int64_t bh = blk / a.nqb;
+  const int32_t i0 = (int32_t)(blk % a.nqb) * kBwdRowsPerBlock;
+  const int tid = threadIdx.x;
+  const int c4 = tid % kT;
+  float* const meta = a.meta + blk * kBwdMetaFloats;
+#pragma unroll
+  for (int pass = 0; pass < kBwdRowsPerBlock / kRowsPerPass; ++pass) {
+    const int r = pass * kRowsPerPass + tid / kT;
+    const int32_t row = i0 + r;
+    const bool live = row < a.seq_q;
+    float d = 0.f;
+    if (live) {
+      const size_t off = ((size_t)bh * a.seq_q + row) * D + 4 * c4;
+      const f32x4 g = *reinterpret_cast<const f32x4*>(a.dout + off);
+      const f32x4 o = *reinterpret_cast<const f32x4*>(a.o + off);
+      d = g[0] * o[0] + g[1] * o[1] + g[2] * o[2] + g[3] * o[3];
+      *reinterpret_cast<u32x2*>(a.dout16 + off) = u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+    }
+#pragma unroll
+    for (int w = kT / 2; w >= 1; w >>= 1) d += __shfl_xor(d, w);
+    if (c4 == 0) {
+      float l2 = INFINITY;
+      if (live) {
+        const float lse = a.lse[(size_t)bh * a.seq_q + row];
+        l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+      }
+      meta[r] = l2;
+      meta[kBwdRowsPerBlock + r] = live ? d : 0.f;
+    }
+  }
+}
+
+// Partial gradients of the 4 waves, [wave][row][head dim] in LDS, from accumulators whose
+// lane (n, h) holds head dims 32*cb + 8*(r/4) + 4*h + r%4 of row n.
+template <int D>
+__device__ __forceinline__ void store_partial(float* part, int wave, int lm, int lh,
+                                              const f32x16 (&acc)[HGeom<D>::kNch]) {
+  using G = HGeom<D>;
+  float* const row = part + (wave * G::kRows + lm) * G::kPStride;
+#pragma unroll
+  for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+      *reinterpret_cast<f32x4*>(row + 32 * cb + 8 * g4 + 4 * lh) =
+          f32x4{acc[cb][4 * g4], acc[cb][4 * g4 + 1], acc[cb][4 * g4 + 2], acc[cb][4 * g4 + 3]};
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+// A workgroup owns 32 keys; K and V stay in registers as the B operands of S = Q K^T and
+// dP = dO V^T. Its 4 waves split the query blocks that admit any of the keys; each
+// streams its Q and dO tiles (permuted) and the block's lse2/D into private LDS slots.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
+  using G = HGeom<D>;
+  constexpr int kSlotBytes = 2 * G::kTileBytes + G::kMetaBytes;  // Q tile, dO tile, lse2/D
+  constexpr int kStageBytes = G::kWaves * kSlotBytes;
+  constexpr int kLdsBytes = kStageBytes > 2 * G::kPartBytes ? kStageBytes : 2 * G::kPartBytes;
+  static_assert(2 * G::kTileBytes <= kSlotBytes, "K and V prologue tiles fit in wave 0's slot");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lm = lane & 31;
+  const int lh = lane >> 5;
+  unsigned char* const q_slot = lds + wave * kSlotBytes;
+  unsigned char* const g_slot = q_slot + G::kTileBytes;
+  unsigned char* const m_slot = g_slot + G::kTileBytes;
+
+  const uint32_t lam = xcd_remap(blockIdx.x, a.nwg);
+  const int64_t bh = (int64_t)(lam / (uint32_t)a.nkb);
+  const int32_t j0 = (int32_t)(lam % (uint32_t)a.nkb) * G::kRows;
+  const int32_t delta = a.seq_kv - a.seq_q;
+  // Query blocks holding a row that admits some key of this block: row i admits key j0
+  // iff i >= j0 - delta.
+  int32_t qb_first = 0;
+  if (CAUSAL) {
+    const int32_t i_min = j0 - delta;
+    qb_first = i_min <= 0 ? 0 : i_min / G::kRows;
+  }
+  const int32_t nq = a.nqb - qb_first;
+  const int32_t b_begin = qb_first + (int32_t)(((int64_t)nq * wave) / G::kWaves);
+  const int32_t b_end = qb_first + (int32_t)(((int64_t)nq * (wave + 1)) / G::kWaves);
+
+  // Rows past the end of each array lie outside these ranges and read as zeros.
+  const __amdgpu_buffer_rsrc_t q_rsrc =
+      raw_buffer(a.q16 + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * (unsigned)G::kRowBytes);
+  const __amdgpu_buffer_rsrc_t g_rsrc =
+      raw_buffer(a.dout16 + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * (unsigned)G::kRowBytes);
+  const __amdgpu_buffer_rsrc_t m_rsrc =
+      raw_buffer(a.meta + (size_t)bh * a.nqb * kBwdMetaFloats, (unsigned)a.nqb * (unsigned)G::kMetaBytes);
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      raw_buffer(a.k16 + (size_t)bh * a.seq_kv * D, (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      raw_buffer(a.v16 + (size_t)bh * a.seq_kv * D, (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
+
+  auto copy_q = [&](int32_t qb) {
+    const unsigned row0 = (unsigned)(G::kRows * qb) * (unsigned)G::kRowBytes;
+#pragma unroll
+    for (int t = 0; t < G::kDmaPerTile; ++t)
+      dma_load_x4(q_rsrc, row0 + tile_src<D, true>(t, lane), lds_address(q_slot + 1024 * t));
+  };
+  auto copy_g = [&](int32_t qb) {  // dO tile, then the block's lse2 and D
+    const unsigned row0 = (unsigned)(G::kRows * qb) * (unsigned)G::kRowBytes;
+#pragma unroll
+    for (int t = 0; t < G::kDmaPerTile; ++t)
+      dma_load_x4(g_rsrc, row0 + tile_src<D, true>(t, lane), lds_address(g_slot + 1024 * t));
+    dma_load_x1(m_rsrc, (unsigned)qb * (unsigned)G::kMetaBytes + 4u * lane, lds_address(m_slot));
+  };
+
+  // This block's K and V tiles (unpermuted), staged through wave 0's slot (each wave
+  // copies a share), into the B operands: lane (key m, h) holds head dims
+  // 16*st + 8*h .. + 7 of key m for k-step st.
+  bf16x8 kr[G::kSteps], vr[G::kSteps];
+  {
+    unsigned char* const k_tile = lds;
+    unsigned char* const v_tile = lds + G::kTileBytes;
+    const unsigned row0 = (unsigned)j0 * (unsigned)G::kRowBytes;
+#pragma unroll
+    for (int i = 0; i < G::kDmaPerTile / G::kWaves; ++i) {
+      const int t = i * G::kWaves + wave;
+      dma_load_x4(k_rsrc, row0 + tile_src<D, false>(t, lane), lds_address(k_tile + 1024 * t));
+      dma_load_x4(v_rsrc, row0 + tile_src<D, false>(t, lane), lds_address(v_tile + 1024 * t));
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < G::kSteps; ++st) {
+      kr[st] = row_chunk<D>(k_tile, lm, 2 * st + lh);
+      vr[st] = row_chunk<D>(v_tile, lm, 2 * st + lh);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the operand reads have returned
+    __syncthreads();                     // before wave 0 reuses its slot
+  }
+
+  f32x16 dv[G::kNch], dk[G::kNch];
+#pragma unroll
+  for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dv[cb][r] = dk[cb][r] = 0.f;
+
+  if (b_begin < b_end) {
+    copy_g(b_begin);
+    copy_q(b_begin);
+  }
+  for (int32_t qb = b_begin; qb < b_end; ++qb) {
+    const int32_t i0 = G::kRows * qb;
+    // The dO tile and lse2/D of block qb have landed (its Q tile, issued after them, may
+    // still be in flight).
+    wait_vmcnt<G::kDmaPerTile>();
+    // lse2 and D of this lane's queries perm_acc_row(r, lh): rows 16t + 8h + 0..7, t = 0, 1.
+    f32x4 l2[4], dd[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int row = 16 * (q4 / 2) + 8 * lh + 4 * (q4 % 2);
+      l2[q4] = *reinterpret_cast<const f32x4*>(m_slot + 4 * row);
+      dd[q4] = *reinterpret_cast<const f32x4*>(m_slot + 4 * (G::kRows + row));
+    }
+    f32x16 dp, s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dp[r] = s[r] = 0.f;
+#pragma unroll
+    for (int st = 0; st < G::kSteps; ++st) dp = mfma16(row_chunk<D>(g_slot, lm, 2 * st + lh), vr[st], dp);
+    wait_vmcnt<0>();  // the Q tile
+#pragma unroll
+    for (int st = 0; st < G::kSteps; ++st) s = mfma16(row_chunk<D>(q_slot, lm, 2 * st + lh), kr[st], s);
+    // Some pair of this block is masked iff its last key lies past its first row's limit.
+    const bool diag = CAUSAL && (j0 + G::kRows - 1 > i0 + delta);
+    bf16x8 pp[2], pds[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float t = s[r] * a.c - l2[r / 4][r % 4];
+      if (diag) t = (j0 + lm <= i0 + perm_acc_row(r, lh) + delta) ? t : -INFINITY;
+      const float p = __builtin_amdgcn_exp2f(t);
+      const float ds = p * (dp[r] - dd[r / 4][r % 4]);
+      pp[r / 8][r % 8] = (__bf16)p;
+      pds[r / 8][r % 8] = (__bf16)ds;
+    }
+    // dV^T += dO^T P
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int cb = 0; cb < G::kNch; ++cb) dv[cb] = mfma16(tr_operand<D>(g_slot, lane, t2, cb), pp[t2], dv[cb]);
+    if (qb + 1 < b_end) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading the dO and lse2/D slots
+      copy_g(qb + 1);
+    }
+    // dK^T += Q^T dS (the scale is applied once, at the end)
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int cb = 0; cb < G::kNch; ++cb) dk[cb] = mfma16(tr_operand<D>(q_slot, lane, t2, cb), pds[t2], dk[cb]);
+    if (qb + 1 < b_end) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading the Q slot
+      copy_q(qb + 1);
+    }
+  }
+
+  // Partials -> LDS as [wave][key][head dim], then summed over the waves.
+  __syncthreads();
+  float* const part_v = reinterpret_cast<float*>(lds);
+  float* const part_k = part_v + G::kWaves * G::kRows * G::kPStride;
+  store_partial<D>(part_v, wave, lm, lh, dv);
+  store_partial<D>(part_k, wave, lm, lh, dk);
+  __syncthreads();
+  constexpr int kThreadsPerRow = D / 4;
+  constexpr int kRowsPerPass = 256 / kThreadsPerRow;
+#pragma unroll
+  for (int pass = 0; pass < G::kRows / kRowsPerPass; ++pass) {
+    const int key = pass * kRowsPerPass + tid / kThreadsPerRow;
+    const int c4 = tid % kThreadsPerRow;
+    const int32_t j = j0 + key;
+    f32x4 sv = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < G::kWaves; ++w) {
+      const f32x4 xv = *reinterpret_cast<const f32x4*>(part_v + (w * G::kRows + key) * G::kPStride + 4 * c4);
+      const f32x4 xk = *reinterpret_cast<const f32x4*>(part_k + (w * G::kRows + key) * G::kPStride + 4 * c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sv[e] += xv[e];
+        sk[e] += xk[e];
+      }
+    }
+    if (j >= a.seq_kv) continue;
+    const size_t off = ((size_t)bh * a.seq_kv + j) * D + 4 * c4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sk[e] *= a.scale;
+    *reinterpret_cast<f32x4*>(a.dv + off) = sv;
+    *reinterpret_cast<f32x4*>(a.dk + off) = sk;
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+
+// A workgroup owns 32 queries; Q and dO stay in registers as the B operands of
+// S^T = K Q^T and dP^T = V dO^T. Its 4 waves split the key blocks the rows admit; each
+// streams its K and V tiles (permuted) into private LDS slots.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
+  using G = HGeom<D>;
+  constexpr int kSlotBytes = 2 * G::kTileBytes;  // K tile, V tile
+  constexpr int kStageBytes = G::kWaves * kSlotBytes;
+  constexpr int kLdsBytes = kStageBytes > G::kPartBytes ? kStageBytes : G::kPartBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lm = lane & 31;
+  const int lh = lane >> 5;
+  unsigned char* const k_slot = lds + wave * kSlotBytes;
+  unsigned char* const v_slot = k_slot + G::kTileBytes;
+
+  // Workgroup -> (batch*head, query block), the longest causal blocks first.
+  const uint32_t lam = xcd_remap(blockIdx.x, a.nwg);
+  const int64_t bh = (int64_t)(lam / (uint32_t)a.nqb);
+  const int32_t qb = a.nqb - 1 - (int32_t)(lam % (uint32_t)a.nqb);
+  const int32_t q0 = qb * G::kRows;
+
+  const int32_t my_row = q0 + lm;
+  const int32_t last_row = min(q0 + G::kRows - 1, a.seq_q - 1);
+  const int32_t lim = key_limit<CAUSAL>(my_row, a.seq_q, a.seq_kv, a.seq_kv);
+  const int32_t lo = key_limit<CAUSAL>(q0, a.seq_q, a.seq_kv, a.seq_kv);
+  const int32_t hi = key_limit<CAUSAL>(last_row, a.seq_q, a.seq_kv, a.seq_kv);
+  const int32_t nblocks = (hi + G::kRows - 1) / G::kRows;
+  const int32_t b_begin = (int32_t)(((int64_t)nblocks * wave) / G::kWaves);
+  const int32_t b_end = (int32_t)(((int64_t)nblocks * (wave + 1)) / G::kWaves);
+
+  // lse2 and D of this lane's query (the preprocess pads past seq_q).
+  const float* const meta = a.meta + ((size_t)bh * a.nqb + qb) * kBwdMetaFloats;
+  const float my_l2 = meta[lm];
+  const float my_d = meta[G::kRows + lm];
+
+  const __amdgpu_buffer_rsrc_t q_rsrc =
+      raw_buffer(a.q16 + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * (unsigned)G::kRowBytes);
+  const __amdgpu_buffer_rsrc_t g_rsrc =
+      raw_buffer(a.dout16 + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * (unsigned)G::kRowBytes);
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      raw_buffer(a.k16 + (size_t)bh * a.seq_kv * D, (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      raw_buffer(a.v16 + (size_t)bh * a.seq_kv * D, (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
+  auto copy_k = [&](int32_t b) {
+    const unsigned row0 = (unsigned)(G::kRows * b) * (unsigned)G::kRowBytes;
+#pragma unroll
+    for (int t = 0; t < G::kDmaPerTile; ++t)
+      dma_load_x4(k_rsrc, row0 + tile_src<D, true>(t, lane), lds_address(k_slot + 1024 * t));
+  };
+  auto copy_v = [&](int32_t b) {
+    const unsigned row0 = (unsigned)(G::kRows * b) * (unsigned)G::kRowBytes;
+#pragma unroll
+    for (int t = 0; t < G::kDmaPerTile; ++t)
+      dma_load_x4(v_rsrc, row0 + tile_src<D, true>(t, lane), lds_address(v_slot + 1024 * t));
+  };
+
+  // The Q and dO tiles of this block (unpermuted), staged through wave 0's slot, into the
+  // B operands: lane (query m, h) holds head dims 16*st + 8*h .. + 7 of query m.
+  bf16x8 qr[G::kSteps], gr[G::kSteps];
+  {
+    const unsigned row0 = (unsigned)q0 * (unsigned)G::kRowBytes;
+#pragma unroll
+    for (int i = 0; i < G::kDmaPerTile / G::kWaves; ++i) {
+      const int t = i * G::kWaves + wave;
+      dma_load_x4(q_rsrc, row0 + tile_src<D, false>(t, lane), lds_address(lds + 1024 * t));
+      dma_load_x4(g_rsrc, row0 + tile_src<D, false>(t, lane), lds_address(lds + G::kTileBytes + 1024 * t));
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < G::kSteps; ++st) {
+      qr[st] = row_chunk<D>(lds, lm, 2 * st + lh);
+      gr[st] = row_chunk<D>(lds + G::kTileBytes, lm, 2 * st + lh);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __syncthreads();                     // before wave 0 reuses its slot
+  }
+
+  f32x16 dq[G::kNch];
+#pragma unroll
+  for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[cb][r] = 0.f;
+
+  if (b_begin < b_end) {
+    copy_v(b_begin);
+    copy_k(b_begin);
+  }
+  for (int32_t b = b_begin; b < b_end; ++b) {
+    const int32_t j0 = G::kRows * b;
+    wait_vmcnt<G::kDmaPerTile>();  // V block b (K block b may still be in flight)
+    f32x16 dp, s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dp[r] = s[r] = 0.f;
+#pragma unroll
+    for (int st = 0; st < G::kSteps; ++st) dp = mfma16(row_chunk<D>(v_slot, lm, 2 * st + lh), gr[st], dp);
+    if (b + 1 < b_end) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading the V slot
+      copy_v(b + 1);
+      wait_vmcnt<G::kDmaPerTile>();        // K block b (V block b+1 may still be in flight)
+    } else {
+      wait_vmcnt<0>();
+    }
+#pragma unroll
+    for (int st = 0; st < G::kSteps; ++st) s = mfma16(row_chunk<D>(k_slot, lm, 2 * st + lh), qr[st], s);
+    const bool edge = j0 + G::kRows > lo;  // some key of the block lies past the first row's limit
+    bf16x8 pds[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float t = s[r] * a.c - my_l2;
+      if (edge) t = (j0 + perm_acc_row(r, lh) < lim) ? t : -INFINITY;
+      const float p = __builtin_amdgcn_exp2f(t);
+      pds[r / 8][r % 8] = (__bf16)(p * (dp[r] - my_d));
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int cb = 0; cb < G::kNch; ++cb) dq[cb] = mfma16(tr_operand<D>(k_slot, lane, t2, cb), pds[t2], dq[cb]);
+    if (b + 1 < b_end) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading the K slot
+      copy_k(b + 1);
+    }
+  }
+
+  __syncthreads();
+  float* const part = reinterpret_cast<float*>(lds);
+  store_partial<D>(part, wave, lm, lh, dq);
+  __syncthreads();
+  constexpr int kThreadsPerRow = D / 4;
+  constexpr int kRowsPerPass = 256 / kThreadsPerRow;
+#pragma unroll
+  for (int pass = 0; pass < G::kRows / kRowsPerPass; ++pass) {
+    const int qi = pass * kRowsPerPass + tid / kThreadsPerRow;
+    const int c4 = tid % kThreadsPerRow;
+    const int32_t row = q0 + qi;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < G::kWaves; ++w) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(part + (w * G::kRows + qi) * G::kPStride + 4 * c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += x[e];
+    }
+    if (row >= a.seq_q) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= a.scale;
+    *reinterpret_cast<f32x4*>(a.dq + ((size_t)bh * a.seq_q + row) * D + 4 * c4) = acc;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_bf16_variant(const BwdArgs& a0, hipStream_t s, hipEvent_t ev_pre,
+                                   hipEvent_t ev_dkdv) {
+  BwdArgs a = a0;
+  const uint32_t nq = (uint32_t)(a.bh * a.nqb), nk = (uint32_t)(a.bh * a.nkb);
+  if (nq > 0) {
+    hipLaunchKernelGGL((attn_bwd_pre_bf16_kernel<D>), dim3(nq), dim3(256), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  if (ev_pre && hipEventRecord(ev_pre, s) != hipSuccess) return hipErrorInvalidValue;
+  if (nk > 0) {
+    a.nwg = nk;
+    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3(nk), dim3(256), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  if (ev_dkdv && hipEventRecord(ev_dkdv, s) != hipSuccess) return hipErrorInvalidValue;
+  if (nq > 0) {
+    a.nwg = nq;
+    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, CAUSAL>), dim3(nq), dim3(256), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, bool causal, hipStream_t s,
+                           hipEvent_t ev_pre, hipEvent_t ev_dkdv) {
+  if (head_dim == 64)
+    return causal ? launch_bwd_bf16_variant<64, true>(a, s, ev_pre, ev_dkdv)
+                  : launch_bwd_bf16_variant<64, false>(a, s, ev_pre, ev_dkdv);
+  if (head_dim == 128)
+    return causal ? launch_bwd_bf16_variant<128, true>(a, s, ev_pre, ev_dkdv)
+                  : launch_bwd_bf16_variant<128, false>(a, s, ev_pre, ev_dkdv);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sma

@@ -549,6 +549,8 @@ namespace {
 struct BwdShape {
   Shape s;
   size_t nqb, nkb, ws_bytes;
+  size_t meta_bytes;     // workspace bytes of the per-block lse2/D (the bf16 dO copy follows)
+  size_t q32, kv32;      // bytes of one fp32 [B,H,Sq,d] / [B,H,Skv,d] tensor (o, dout, gradients)
 };
 
 // Pointer-independent checks of the backward. Fills b on success.
@@ -556,16 +558,25 @@ int check_bwd_shape(int in_dtype, size_t batch, size_t heads, size_t seq_q, size
                     size_t d, double scale, BwdShape* b) {
   int st = check_shape(in_dtype, SMA_DTYPE_F32, batch, heads, seq_q, seq_kv, d, scale, &b->s);
   if (st != SMA_OK) return st;
-  if (in_dtype != SMA_DTYPE_F32 || (d != 64 && d != 128)) return SMA_ERR_UNSUPPORTED;
+  // fp32, or bf16 Q, K, V; fp16 (whose narrow exponent range dS would need rescaling for)
+  // is not built.
+  if ((in_dtype != SMA_DTYPE_F32 && in_dtype != SMA_DTYPE_BF16) || (d != 64 && d != 128))
+    return SMA_ERR_UNSUPPORTED;
   const size_t blk = sma::kBwdRowsPerBlock;
   if ((seq_q + blk) * d * 4 > (size_t(1) << 31) || (seq_kv + blk) * d * 4 > (size_t(1) << 31))
     return SMA_ERR_UNSUPPORTED;
   b->nqb = (seq_q + blk - 1) / blk;
   b->nkb = (seq_kv + blk - 1) / blk;
+  size_t nq, nkv;
+  if (!mul(b->s.rows, d, &nq) || !mul(nq, 4, &b->q32) || !mul(b->s.bh, seq_kv, &nkv) ||
+      !mul(nkv, d, &nkv) || !mul(nkv, 4, &b->kv32))
+    return SMA_ERR_INVALID_VALUE;
   size_t blocks;
   if (!mul(b->s.bh, b->nqb, &blocks) || !mul(blocks, sma::kBwdMetaFloats * sizeof(float), &b->ws_bytes))
     return SMA_ERR_INVALID_VALUE;
   b->ws_bytes = round_up(b->ws_bytes, kWsAlign);
+  b->meta_bytes = b->ws_bytes;
+  if (in_dtype == SMA_DTYPE_BF16) b->ws_bytes += round_up(b->q32 / 2, kWsAlign);  // dO as bf16
   if (b->s.bh * b->nqb > kMaxWorkgroups || b->s.bh * b->nkb > kMaxWorkgroups) return SMA_ERR_UNSUPPORTED;
   return SMA_OK;
 }
@@ -582,12 +593,14 @@ int check_bwd_pointers(const BwdShape& b, const void* q, const void* k, const vo
   for (const void* p : t16)
     if (p && !aligned(p, 16)) return SMA_ERR_MISALIGNED;
   if (lse && !aligned(lse, 4)) return SMA_ERR_MISALIGNED;
+  // Q, K, V in the input type; O, dO and the gradients in fp32.
   const size_t qb = has_q ? s.q_bytes : 0, kvb = has_kv ? s.kv_bytes : 0;
+  const size_t q32 = has_q ? b.q32 : 0, kv32 = has_kv ? b.kv32 : 0;
   const size_t lb = has_q ? s.lse_bytes : 0, wb = b.ws_bytes > 0 ? b.ws_bytes : 0;
   const void* outs[4] = {dq, dk, dv, ws};
-  const size_t out_n[4] = {qb, kvb, kvb, wb};
+  const size_t out_n[4] = {q32, kv32, kv32, wb};
   const void* ins[6] = {q, k, v, o, lse, dout};
-  const size_t in_n[6] = {qb, kvb, kvb, qb, lb, qb};
+  const size_t in_n[6] = {qb, kvb, kvb, q32, lb, q32};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlap(outs[i], out_n[i], ins[j], in_n[j])) return SMA_ERR_ALIASING;
@@ -632,6 +645,12 @@ int sma_attention_bwd_timed(const void* q, const void* k, const void* v, const v
   a.dk = dk;
   a.dv = dv;
   a.meta = static_cast<float*>(workspace);
+  if (in_dtype == SMA_DTYPE_BF16) {
+    a.q16 = static_cast<const unsigned short*>(q);
+    a.k16 = static_cast<const unsigned short*>(k);
+    a.v16 = static_cast<const unsigned short*>(v);
+    a.dout16 = reinterpret_cast<unsigned short*>(static_cast<unsigned char*>(workspace) + b.meta_bytes);
+  }
   a.bh = (int64_t)b.s.bh;
   a.seq_q = (int32_t)seq_q;
   a.seq_kv = (int32_t)seq_kv;
@@ -639,9 +658,10 @@ int sma_attention_bwd_timed(const void* q, const void* k, const void* v, const v
   a.nkb = (int32_t)b.nkb;
   a.c = (float)(scale * 1.44269504088896340736);  // scale * log2(e), one rounding
   a.scale = (float)scale;
-  hipError_t e = sma::launch_bwd_f32(a, (int)head_dim, causal != 0, static_cast<hipStream_t>(stream),
-                                     static_cast<hipEvent_t>(event_after_pre),
-                                     static_cast<hipEvent_t>(event_after_dkdv));
+  const auto launch = in_dtype == SMA_DTYPE_BF16 ? sma::launch_bwd_bf16 : sma::launch_bwd_f32;
+  hipError_t e = launch(a, (int)head_dim, causal != 0, static_cast<hipStream_t>(stream),
+                        static_cast<hipEvent_t>(event_after_pre),
+                        static_cast<hipEvent_t>(event_after_dkdv));
   return e == hipSuccess ? SMA_OK : SMA_ERR_HIP;
 }
 

@@ -64,7 +64,8 @@ struct CombineArgs {
   int64_t os_b, os_h, os_s;
 };
 
-// Arguments of the attention-backward launches (fp32 inputs and gradients).
+// Arguments of the attention-backward launches (fp32 or bf16 Q, K, V; fp32 O, dO and
+// gradients).
 struct BwdArgs {
   const float* q;     // [bh][seq_q][d]
   const float* k;     // [bh][seq_kv][d]
@@ -76,6 +77,12 @@ struct BwdArgs {
   float* dk;          // [bh][seq_kv][d]
   float* dv;          // [bh][seq_kv][d]
   float* meta;        // workspace [bh][nqb][64]: per 32-row query block, lse2 then D
+  // bf16 inputs (the bf16 backward): q, k, v as bf16, and the workspace copy of dO
+  // rounded to bf16 ([bh][seq_q][d]); o and dout stay fp32.
+  const unsigned short* q16;
+  const unsigned short* k16;
+  const unsigned short* v16;
+  unsigned short* dout16;
   int64_t bh;
   int32_t seq_q;
   int32_t seq_kv;
@@ -134,6 +141,8 @@ constexpr int kBwdRowsPerBlock = 32;         // query and key block of the backw
 constexpr int kBwdMetaFloats = 64;          // workspace floats per query block
 hipError_t launch_bwd_f32(const BwdArgs& a, int head_dim, bool causal, hipStream_t s,
                           hipEvent_t ev_pre, hipEvent_t ev_dkdv);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, bool causal, hipStream_t s,
+                           hipEvent_t ev_pre, hipEvent_t ev_dkdv);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s);
 
 }  // namespace sma
