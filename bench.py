@@ -138,6 +138,7 @@ def read_traffic(kernel_function: str, workload: str, kernel_src_digest: str):
 # Source file of each kernel (with the shared device header, what its traffic depends on).
 KERNEL_SOURCES = {"attn_fwd_f32_kernel": ["attn_fwd_f32.hip", "attn_common.h"],
                   "attn_bwd_dkdv_f32_kernel": ["attn_bwd_f32.hip", "attn_common.h"],
+                  "attn_bwd_dkdv_bf16_kernel": ["attn_bwd_bf16.hip", "attn_common.h"],
                   "attn_fwd_f32_wsplit_kernel": ["attn_fwd_f32_wsplit.hip", "attn_common.h"],
                   "attn_fwd_bf16_kernel": ["attn_fwd_bf16.hip", "attn_common.h"],
                   "row_softmax": ["row_softmax.hip"]}
@@ -195,17 +196,53 @@ BWD_PREFIX = "bwd_"
 def gen_workloads():
     import gen
 
-    bwd = [BWD_PREFIX + n for n, w in gen.WORKLOADS.items() if w.dtype == "f32" and w.head_dim in (64, 128)]
+    bwd = [BWD_PREFIX + n for n, w in gen.WORKLOADS.items() if w.dtype in ("f32", "bf16") and w.head_dim in (64, 128)]
     return list(gen.WORKLOADS) + bwd + list(gen.ROW_WORKLOADS)
 
 
 def dkdv_min_bytes(w) -> int:
-    """The dK/dV kernel reads Q, dO, K, V and each row's lse2 and D once and writes dK, dV."""
+    """The dK/dV kernel reads Q, dO, K, V (in the input type; dO as the bf16 copy for bf16
+    inputs) and each row's lse2 and D once, and writes dK, dV (fp32)."""
     bh = w.batch * w.heads
-    return bh * ((2 * w.seq_q + 4 * w.seq_kv) * w.head_dim * 4 + 8 * w.seq_q)
+    e = 4 if w.dtype == "f32" else 2
+    return bh * ((2 * w.seq_q + 2 * w.seq_kv) * w.head_dim * e + 2 * w.seq_kv * w.head_dim * 4 + 8 * w.seq_q)
 
 
 BWD_METRIC = "attention bwd TFLOP/s (10·B·H·Sq·Skv·d, causal halved) and % of MFMA peak"
+
+
+def bwd_cpu_baseline_last_rows(w, q, k, v, g, target_s: float):
+    """The backward oracle on exact sub-problems of a square causal workload too large for
+    whole heads: the last T query rows of a head with every key keep the bottom-right mask
+    (row i' admits keys up to i' + S - T), one head per thread. T grows until a round takes
+    a few seconds; FLOPs are the metric's per admitted pair times the pairs processed."""
+    import oracle
+
+    bh, S, d = w.batch * w.heads, w.seq_q, w.head_dim
+    qf, kf, vf, gf = (x.reshape(bh, 1, x.shape[2], x.shape[3]) for x in (q, k, v, g))
+    threads = max(1, oracle.num_threads())
+    n = min(bh, threads)
+    ids = np.sort(np.random.default_rng(0).permutation(bh)[:n])
+    per_pair = 2.5 * metric_flops(w) / allowed_pairs(w)
+    T = 8
+    while True:
+        t0 = time.perf_counter()
+        oracle.attention_bwd(qf[ids, :, S - T:], kf[ids], vf[ids], gf[ids, :, S - T:], w.scale, True)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 4 or 2 * T > S:
+            break
+        T *= 2
+    passes, total = 0, 0.0
+    while total < target_s and passes < 1000:
+        t0 = time.perf_counter()
+        oracle.attention_bwd(qf[ids, :, S - T:], kf[ids], vf[ids], gf[ids, :, S - T:], w.scale, True)
+        total += time.perf_counter() - t0
+        passes += 1
+    pairs = n * sum(S - T + i + 1 for i in range(T)) * passes
+    return {"value": per_pair * pairs / total / 1e12, "unit": "TFLOP/s", "cores": n, "kind": "oracle",
+            "sample": f"the last {T} query rows (all {S} keys) of {n} of {bh} (batch, head) slices "
+                      f"chosen at random (seed 0), {passes} pass(es) in {total:.1f} s; metric FLOPs "
+                      f"per admitted pair times the pairs processed"}
 
 
 def bwd_cpu_baseline(w, q, k, v, g, target_s: float):
@@ -213,6 +250,8 @@ def bwd_cpu_baseline(w, q, k, v, g, target_s: float):
     import oracle
 
     bh = w.batch * w.heads
+    if w.causal and w.seq_q == w.seq_kv and w.seq_q * w.seq_kv * w.head_dim > (1 << 33):
+        return bwd_cpu_baseline_last_rows(w, q, k, v, g, target_s)
     rng = np.random.default_rng(0)
     order = rng.permutation(bh)
     qf, kf, vf, gf = (x.reshape(bh, 1, x.shape[2], x.shape[3]) for x in (q, k, v, g))
@@ -243,24 +282,36 @@ def bwd_cpu_baseline(w, q, k, v, g, target_s: float):
                       f"slice fraction"}
 
 
+def to_device_inputs(vals, bits, dtype):
+    """q, k, v on the device: fp32 values, or 16-bit tensors from the exact bit patterns."""
+    import torch
+
+    if dtype == "f32":
+        return tuple(torch.from_numpy(np.ascontiguousarray(x)).to("cuda") for x in vals)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    return tuple(torch.from_numpy(b.view(np.int16)).to("cuda").view(tdt) for b in bits)
+
+
 def bench_bwd(args, w, name):
     import torch
 
     import gen
     import scaled_masked_attention_amd as sma
 
-    vals, _ = gen.make_inputs(w)
+    vals, bits = gen.make_inputs(w)
     g = gen.upstream_grad(w.seed, w.q_shape)
-    tq, tk, tv, tg = (torch.from_numpy(np.ascontiguousarray(x)).to("cuda") for x in (*vals, g))
+    tq, tk, tv = to_device_inputs(vals, bits, w.dtype)
+    tg = torch.from_numpy(np.ascontiguousarray(g)).to("cuda")
+    in_dt = sma.SMA_DTYPE_F32 if w.dtype == "f32" else sma.SMA_DTYPE_BF16
     B, H, sq, skv, d = w.batch, w.heads, w.seq_q, w.seq_kv, w.head_dim
     o, lse = sma.attention_fwd(tq, tk, tv, scale=w.scale, causal=w.causal, return_lse=True)
-    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
-    ws_n = sma.attention_bwd_workspace_bytes(sma.SMA_DTYPE_F32, B, H, sq, skv, d, w.causal)
+    dq, dk, dv = (torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in (tq, tk, tv))
+    ws_n = sma.attention_bwd_workspace_bytes(in_dt, B, H, sq, skv, d, w.causal)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     call = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), lse.data_ptr(), tg.data_ptr(),
-            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), sma.SMA_DTYPE_F32, B, H, sq, skv, d, w.scale,
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), in_dt, B, H, sq, skv, d, w.scale,
             w.causal, ws.data_ptr(), ws_n, sptr)
     settled = settle(lambda: sma.attention_bwd_raw(*call), args.settle_ms)
     for _ in range(args.warmup):
@@ -283,20 +334,20 @@ def bench_bwd(args, w, name):
 
     flops = 2.5 * metric_flops(w)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    peak = PEAK_TFLOPS["f32"]
+    peak = PEAK_TFLOPS[w.dtype]
     pairs = allowed_pairs(w)
     kernel_flops = 8.0 * d * pairs  # S, dP, dV and dK: four products over the admitted pairs
     achieved = kernel_flops / (k_avg * 1e-3) / 1e12
-    kname = "attn_bwd_dkdv_f32_kernel"
+    kname = "attn_bwd_dkdv_f32_kernel" if w.dtype == "f32" else "attn_bwd_dkdv_bf16_kernel"
     traffic = read_traffic(kname, name, kernel_source_digest(kname))
     line = {
         "metric": BWD_METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "settle_steps": settled, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded SplitMix64 + Box-Muller normals; dO on its own stream)",
         "config": {"workload": name, "batch": B, "heads": H, "seq_q": sq, "seq_kv": skv,
-                   "head_dim": d, "causal": w.causal, "scale": w.scale, "input_dtype": "f32",
-                   "gradients": "f32", "workspace_bytes": ws_n},
+                   "head_dim": d, "causal": w.causal, "scale": w.scale, "input_dtype": w.dtype,
+                   "o_and_dout": "f32", "gradients": "f32", "workspace_bytes": ws_n},
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -495,13 +546,8 @@ def main():
         return
     w = gen.WORKLOADS[args.workload]
     vals, bits = gen.make_inputs(w)
-    if w.dtype == "f32":
-        tq, tk, tv = (torch.from_numpy(x).to("cuda") for x in vals)
-        in_dt = sma.SMA_DTYPE_F32
-    else:
-        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
-        tq, tk, tv = (torch.from_numpy(b.view(np.int16)).to("cuda").view(tdt) for b in bits)
-        in_dt = sma.SMA_DTYPE_BF16 if w.dtype == "bf16" else sma.SMA_DTYPE_F16
+    tq, tk, tv = to_device_inputs(vals, bits, w.dtype)
+    in_dt = {"f32": sma.SMA_DTYPE_F32, "bf16": sma.SMA_DTYPE_BF16, "f16": sma.SMA_DTYPE_F16}[w.dtype]
     B, H, sq, skv, d = w.batch, w.heads, w.seq_q, w.seq_kv, w.head_dim
     lay = sma.LAYOUTS[args.layout]
     if args.layout == "bshd":  # the same data, heads of one position adjacent

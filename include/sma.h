@@ -256,8 +256,13 @@ size_t sma_attention_fwd_masked_workspace_bytes(int in_dtype, size_t batch, size
  * and dv). Results are bitwise reproducible: no atomics.
  *
  *   q, o, dout, dq   [B,H,Sq,d];  k, v, dk, dv  [B,H,Skv,d];  lse [B,H,Sq].
- *   in_dtype         SMA_DTYPE_F32 (q, k, v, o, dout); SMA_DTYPE_BF16 -> UNSUPPORTED.
- *                    lse and the three gradients are fp32.
+ *   in_dtype         element type of q, k and v: SMA_DTYPE_F32 (fp32 MFMA), or
+ *                    SMA_DTYPE_BF16 (16-bit MFMA with fp32 accumulation, under the
+ *                    forward's mixed-precision contract: dout is rounded once to bf16
+ *                    for the products, and P and dS are rounded to bf16 for the
+ *                    products that take them; D = dout . o stays fp32);
+ *                    SMA_DTYPE_F16 -> UNSUPPORTED. o, dout, lse and the three
+ *                    gradients are always fp32 (o as sma_attention_fwd returns it).
  *   head_dim         64 or 128 (others -> UNSUPPORTED).
  *   scale, causal, stream   as for sma_attention_fwd.
  *   workspace        required device scratch of at least
@@ -279,8 +284,10 @@ int sma_attention_bwd(const void* q, const void* k, const void* v, const void* o
                       size_t head_dim, double scale, int causal, void* workspace,
                       size_t workspace_bytes, void* stream);
 
-/* Workspace bytes sma_attention_bwd needs for this shape (256 per 32-row query
- * block of every (batch, head), rounded up to 256); 0 for invalid arguments. */
+/* Workspace bytes sma_attention_bwd needs for this shape: 256 per 32-row query
+ * block of every (batch, head), rounded up to 256; with SMA_DTYPE_BF16 also
+ * batch*heads*seq_q*head_dim*2 bytes (dout as bf16), rounded up to 256. 0 for
+ * invalid arguments. */
 size_t sma_attention_bwd_workspace_bytes(int in_dtype, size_t batch, size_t heads, size_t seq_q,
                                          size_t seq_kv, size_t head_dim, int causal);
 
