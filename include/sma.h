@@ -284,6 +284,19 @@ int sma_attention_bwd(const void* q, const void* k, const void* v, const void* o
                       size_t head_dim, double scale, int causal, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* sma_attention_bwd with the memory layout of sma_attention_fwd_layout: with
+ * SMA_LAYOUT_BSHD, q, o, dout and dq are [B,Sq,H,d] and k, v, dk and dv
+ * [B,Skv,H,d] (lse stays [B,H,Sq]); SMA_LAYOUT_BHSD is sma_attention_bwd. The
+ * workspace is the same size for both layouts. The 2 GiB limit counts rows of
+ * heads*head_dim elements under SMA_LAYOUT_BSHD. Gradients are bitwise those of
+ * SMA_LAYOUT_BHSD on the transposed tensors. Other arguments and errors as for
+ * sma_attention_bwd; a layout code other than the two -> INVALID_VALUE. */
+int sma_attention_bwd_layout(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                             int in_dtype, size_t batch, size_t heads, size_t seq_q,
+                             size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes sma_attention_bwd needs for this shape: 256 per 32-row query
  * block of every (batch, head), rounded up to 256; with SMA_DTYPE_BF16 also
  * batch*heads*seq_q*head_dim*2 bytes (dout as bf16), rounded up to 256. 0 for

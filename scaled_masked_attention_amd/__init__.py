@@ -103,6 +103,8 @@ def library():
         lib.sma_attention_bwd.restype = ctypes.c_int
         lib.sma_attention_bwd_timed.argtypes = bwd + [vp, vp]
         lib.sma_attention_bwd_timed.restype = ctypes.c_int
+        lib.sma_attention_bwd_layout.argtypes = bwd[:17] + [ctypes.c_int] + bwd[17:]
+        lib.sma_attention_bwd_layout.restype = ctypes.c_int
         lib.sma_attention_bwd_workspace_bytes.argtypes = [ctypes.c_int, sz, sz, sz, sz, sz, ctypes.c_int]
         lib.sma_attention_bwd_workspace_bytes.restype = sz
         lib.sma_status_string.argtypes = [ctypes.c_int]
@@ -321,14 +323,16 @@ def attention_bwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, dout_ptr, dq_ptr, dk_
                                              ws_bytes, stream, event_after_pre, event_after_dkdv))
 
 
-def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=None):
+def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=None,
+                  layout="bhsd"):
     """(dQ, dK, dV) of O = softmax(scale * Q K^T + mask) V for the upstream gradient dout.
 
     q, o, dout [B,H,Sq,D] and k, v [B,H,Skv,D] contiguous tensors on the current
     HIP device: q, k, v all float32 or all bfloat16 (then on 16-bit MFMA), o, dout
     and lse ([B,H,Sq]) float32, o and lse as attention_fwd returned them for the
-    same q, k, v, scale and causal. Returns three float32 tensors shaped like q, k
-    and v. The workspace is allocated when not given.
+    same q, k, v, scale and causal. layout="bshd" takes q, o, dout [B,Sq,H,D] and
+    k, v [B,Skv,H,D] (lse stays [B,H,Sq]). Returns three float32 tensors shaped
+    like q, k and v. The workspace is allocated when not given.
     """
     import torch
 
@@ -338,11 +342,18 @@ def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=Non
             raise TypeError(f"{name} must be a torch tensor")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [batch, heads, seq, head_dim]")
-    B, H, Sq, D = q.shape
-    Skv = k.shape[2]
-    if (tuple(k.shape) != (B, H, Skv, D) or tuple(v.shape) != (B, H, Skv, D) or
-            tuple(o.shape) != (B, H, Sq, D) or tuple(dout.shape) != (B, H, Sq, D) or
-            tuple(lse.shape) != (B, H, Sq)):
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    if layout == "bshd":
+        B, Sq, H, D = q.shape
+        Skv = k.shape[1]
+        kv_shape, q_shape = (B, Skv, H, D), (B, Sq, H, D)
+    else:
+        B, H, Sq, D = q.shape
+        Skv = k.shape[2]
+        kv_shape, q_shape = (B, H, Skv, D), (B, H, Sq, D)
+    if (tuple(k.shape) != kv_shape or tuple(v.shape) != kv_shape or tuple(o.shape) != q_shape or
+            tuple(dout.shape) != q_shape or tuple(lse.shape) != (B, H, Sq)):
         raise ValueError("shape mismatch among q, k, v, o, lse, dout")
     dev = torch.device("cuda", torch.cuda.current_device())
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float32, torch.bfloat16):
@@ -367,9 +378,16 @@ def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=Non
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
         stream = torch.cuda.current_stream()
-    attention_bwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
-                      _ptr(dv), in_dt, B, H, Sq, Skv, D, scale, causal, ws_ptr, ws_bytes,
-                      stream.cuda_stream)
+    if layout == "bhsd":
+        attention_bwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                          _ptr(dk), _ptr(dv), in_dt, B, H, Sq, Skv, D, scale, causal, ws_ptr,
+                          ws_bytes, stream.cuda_stream)
+    else:
+        _raise(library().sma_attention_bwd_layout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                                  _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), in_dt,
+                                                  B, H, Sq, Skv, D, float(scale),
+                                                  int(bool(causal)), LAYOUTS[layout], ws_ptr,
+                                                  ws_bytes, stream.cuda_stream))
     return dq, dk, dv
 
 

@@ -80,17 +80,18 @@ __device__ __forceinline__ int swz(int p) {
   return D == 128 ? 4 * (p & 3) + ((p >> 2) & 3) : 4 * ((p >> 1) & 1) + ((p >> 2) & 3);
 }
 
-// Byte offset, from the tile's first row in global memory, of the 16 bytes that lane
-// `lane` of direct-to-LDS copy instruction t fetches: LDS chunk position P = 64t + lane is
-// tile row p = P / chunks, chunk slot P % chunks, which holds logical chunk
-// slot ^ swz(p) of source row p (or of row swap_bits_2_3(p) in a permuted tile).
+// Byte offset, from the tile's first row in global memory (rows row_bytes apart), of the
+// 16 bytes that lane `lane` of direct-to-LDS copy instruction t fetches: LDS chunk
+// position P = 64t + lane is tile row p = P / chunks, chunk slot P % chunks, which holds
+// logical chunk slot ^ swz(p) of source row p (or of row swap_bits_2_3(p) in a permuted
+// tile).
 template <int D, bool PERM>
-__device__ __forceinline__ unsigned tile_src(int t, int lane) {
+__device__ __forceinline__ unsigned tile_src(int t, int lane, unsigned row_bytes) {
   constexpr int kC = D / 8;
   const int pos = 64 * t + lane;
   const int p = pos / kC;
   const int c = (pos % kC) ^ swz<D>(p);
-  return (unsigned)((PERM ? swap_bits_2_3(p) : p) * 2 * D + 16 * c);
+  return (unsigned)(PERM ? swap_bits_2_3(p) : p) * row_bytes + 16u * (unsigned)c;
 }
 
 // The 8 bf16 at logical chunk c of tile row p (a row read).
@@ -142,11 +143,12 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(BwdArgs a) {
     const bool live = row < a.seq_q;
     float d = 0.f;
     if (live) {
-      const size_t off = ((size_t)bh * a.seq_q + row) * D + 4 * c4;
+      const int64_t off = head_offset(bh, a.heads, a.qs_b, a.qs_h) + (int64_t)row * a.qs_s + 4 * c4;
       const f32x4 g = *reinterpret_cast<const f32x4*>(a.dout + off);
       const f32x4 o = *reinterpret_cast<const f32x4*>(a.o + off);
       d = g[0] * o[0] + g[1] * o[1] + g[2] * o[2] + g[3] * o[3];
-      *reinterpret_cast<u32x2*>(a.dout16 + off) = u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+      const size_t off16 = ((size_t)bh * a.seq_q + row) * D + 4 * c4;  // the copy is [bh][seq_q][d]
+      *reinterpret_cast<u32x2*>(a.dout16 + off16) = u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
     }
 #pragma unroll
     for (int w = kT / 2; w >= 1; w >>= 1) d += __shfl_xor(d, w);
@@ -215,29 +217,33 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int32_t b_begin = qb_first + (int32_t)(((int64_t)nq * wave) / G::kWaves);
   const int32_t b_end = qb_first + (int32_t)(((int64_t)nq * (wave + 1)) / G::kWaves);
 
-  // Rows past the end of each array lie outside these ranges and read as zeros.
-  const __amdgpu_buffer_rsrc_t q_rsrc =
-      raw_buffer(a.q16 + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * (unsigned)G::kRowBytes);
+  // Rows past the end of each array lie outside these ranges and read as zeros. Q, K and
+  // V rows are q_row / kv_row bytes apart (the layout's row strides); the bf16 copy of dO
+  // is contiguous.
+  const int64_t q_off = head_offset(bh, a.heads, a.qs_b, a.qs_h);
+  const int64_t kv_off = head_offset(bh, a.heads, a.kvs_b, a.kvs_h);
+  const unsigned q_row = (unsigned)(a.qs_s * 2), kv_row = (unsigned)(a.kvs_s * 2);
+  const unsigned g_row = (unsigned)G::kRowBytes;
+  const __amdgpu_buffer_rsrc_t q_rsrc = raw_buffer(a.q16 + q_off, strided_range(a.seq_q, a.qs_s, D, 2));
   const __amdgpu_buffer_rsrc_t g_rsrc =
-      raw_buffer(a.dout16 + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * (unsigned)G::kRowBytes);
+      raw_buffer(a.dout16 + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * g_row);
   const __amdgpu_buffer_rsrc_t m_rsrc =
       raw_buffer(a.meta + (size_t)bh * a.nqb * kBwdMetaFloats, (unsigned)a.nqb * (unsigned)G::kMetaBytes);
-  const __amdgpu_buffer_rsrc_t k_rsrc =
-      raw_buffer(a.k16 + (size_t)bh * a.seq_kv * D, (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
-  const __amdgpu_buffer_rsrc_t v_rsrc =
-      raw_buffer(a.v16 + (size_t)bh * a.seq_kv * D, (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
+  const unsigned kv_range = strided_range(a.seq_kv, a.kvs_s, D, 2);
+  const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(a.k16 + kv_off, kv_range);
+  const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(a.v16 + kv_off, kv_range);
 
   auto copy_q = [&](int32_t qb) {
-    const unsigned row0 = (unsigned)(G::kRows * qb) * (unsigned)G::kRowBytes;
+    const unsigned row0 = (unsigned)(G::kRows * qb) * q_row;
 #pragma unroll
     for (int t = 0; t < G::kDmaPerTile; ++t)
-      dma_load_x4(q_rsrc, row0 + tile_src<D, true>(t, lane), lds_address(q_slot + 1024 * t));
+      dma_load_x4(q_rsrc, row0 + tile_src<D, true>(t, lane, q_row), lds_address(q_slot + 1024 * t));
   };
   auto copy_g = [&](int32_t qb) {  // dO tile, then the block's lse2 and D
-    const unsigned row0 = (unsigned)(G::kRows * qb) * (unsigned)G::kRowBytes;
+    const unsigned row0 = (unsigned)(G::kRows * qb) * g_row;
 #pragma unroll
     for (int t = 0; t < G::kDmaPerTile; ++t)
-      dma_load_x4(g_rsrc, row0 + tile_src<D, true>(t, lane), lds_address(g_slot + 1024 * t));
+      dma_load_x4(g_rsrc, row0 + tile_src<D, true>(t, lane, g_row), lds_address(g_slot + 1024 * t));
     dma_load_x1(m_rsrc, (unsigned)qb * (unsigned)G::kMetaBytes + 4u * lane, lds_address(m_slot));
   };
 
@@ -248,12 +254,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   {
     unsigned char* const k_tile = lds;
     unsigned char* const v_tile = lds + G::kTileBytes;
-    const unsigned row0 = (unsigned)j0 * (unsigned)G::kRowBytes;
+    const unsigned row0 = (unsigned)j0 * kv_row;
 #pragma unroll
     for (int i = 0; i < G::kDmaPerTile / G::kWaves; ++i) {
       const int t = i * G::kWaves + wave;
-      dma_load_x4(k_rsrc, row0 + tile_src<D, false>(t, lane), lds_address(k_tile + 1024 * t));
-      dma_load_x4(v_rsrc, row0 + tile_src<D, false>(t, lane), lds_address(v_tile + 1024 * t));
+      dma_load_x4(k_rsrc, row0 + tile_src<D, false>(t, lane, kv_row), lds_address(k_tile + 1024 * t));
+      dma_load_x4(v_rsrc, row0 + tile_src<D, false>(t, lane, kv_row), lds_address(v_tile + 1024 * t));
     }
     wait_vmcnt<0>();
     __syncthreads();
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
       }
     }
     if (j >= a.seq_kv) continue;
-    const size_t off = ((size_t)bh * a.seq_kv + j) * D + 4 * c4;
+    const int64_t off = kv_off + (int64_t)j * a.kvs_s + 4 * c4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) sk[e] *= a.scale;
     *reinterpret_cast<f32x4*>(a.dv + off) = sv;
@@ -404,37 +410,39 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   const float my_l2 = meta[lm];
   const float my_d = meta[G::kRows + lm];
 
-  const __amdgpu_buffer_rsrc_t q_rsrc =
-      raw_buffer(a.q16 + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * (unsigned)G::kRowBytes);
+  const int64_t q_off = head_offset(bh, a.heads, a.qs_b, a.qs_h);
+  const int64_t kv_off = head_offset(bh, a.heads, a.kvs_b, a.kvs_h);
+  const unsigned q_row = (unsigned)(a.qs_s * 2), kv_row = (unsigned)(a.kvs_s * 2);
+  const unsigned g_row = (unsigned)G::kRowBytes;
+  const __amdgpu_buffer_rsrc_t q_rsrc = raw_buffer(a.q16 + q_off, strided_range(a.seq_q, a.qs_s, D, 2));
   const __amdgpu_buffer_rsrc_t g_rsrc =
-      raw_buffer(a.dout16 + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * (unsigned)G::kRowBytes);
-  const __amdgpu_buffer_rsrc_t k_rsrc =
-      raw_buffer(a.k16 + (size_t)bh * a.seq_kv * D, (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
-  const __amdgpu_buffer_rsrc_t v_rsrc =
-      raw_buffer(a.v16 + (size_t)bh * a.seq_kv * D, (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
+      raw_buffer(a.dout16 + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * g_row);
+  const unsigned kv_range = strided_range(a.seq_kv, a.kvs_s, D, 2);
+  const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(a.k16 + kv_off, kv_range);
+  const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(a.v16 + kv_off, kv_range);
   auto copy_k = [&](int32_t b) {
-    const unsigned row0 = (unsigned)(G::kRows * b) * (unsigned)G::kRowBytes;
+    const unsigned row0 = (unsigned)(G::kRows * b) * kv_row;
 #pragma unroll
     for (int t = 0; t < G::kDmaPerTile; ++t)
-      dma_load_x4(k_rsrc, row0 + tile_src<D, true>(t, lane), lds_address(k_slot + 1024 * t));
+      dma_load_x4(k_rsrc, row0 + tile_src<D, true>(t, lane, kv_row), lds_address(k_slot + 1024 * t));
   };
   auto copy_v = [&](int32_t b) {
-    const unsigned row0 = (unsigned)(G::kRows * b) * (unsigned)G::kRowBytes;
+    const unsigned row0 = (unsigned)(G::kRows * b) * kv_row;
 #pragma unroll
     for (int t = 0; t < G::kDmaPerTile; ++t)
-      dma_load_x4(v_rsrc, row0 + tile_src<D, true>(t, lane), lds_address(v_slot + 1024 * t));
+      dma_load_x4(v_rsrc, row0 + tile_src<D, true>(t, lane, kv_row), lds_address(v_slot + 1024 * t));
   };
 
   // The Q and dO tiles of this block (unpermuted), staged through wave 0's slot, into the
   // B operands: lane (query m, h) holds head dims 16*st + 8*h .. + 7 of query m.
   bf16x8 qr[G::kSteps], gr[G::kSteps];
   {
-    const unsigned row0 = (unsigned)q0 * (unsigned)G::kRowBytes;
 #pragma unroll
     for (int i = 0; i < G::kDmaPerTile / G::kWaves; ++i) {
       const int t = i * G::kWaves + wave;
-      dma_load_x4(q_rsrc, row0 + tile_src<D, false>(t, lane), lds_address(lds + 1024 * t));
-      dma_load_x4(g_rsrc, row0 + tile_src<D, false>(t, lane), lds_address(lds + G::kTileBytes + 1024 * t));
+      dma_load_x4(q_rsrc, (unsigned)q0 * q_row + tile_src<D, false>(t, lane, q_row), lds_address(lds + 1024 * t));
+      dma_load_x4(g_rsrc, (unsigned)q0 * g_row + tile_src<D, false>(t, lane, g_row),
+                  lds_address(lds + G::kTileBytes + 1024 * t));
     }
     wait_vmcnt<0>();
     __syncthreads();
@@ -515,7 +523,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
     if (row >= a.seq_q) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] *= a.scale;
-    *reinterpret_cast<f32x4*>(a.dq + ((size_t)bh * a.seq_q + row) * D + 4 * c4) = acc;
+    *reinterpret_cast<f32x4*>(a.dq + q_off + (int64_t)row * a.qs_s + 4 * c4) = acc;
   }
 }
 

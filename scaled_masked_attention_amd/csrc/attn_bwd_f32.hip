@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(BwdArgs a) {
     const bool live = row < a.seq_q;
     float d = 0.f;
     if (live) {
-      const size_t off = ((size_t)bh * a.seq_q + row) * D + 4 * c4;
+      const int64_t off = head_offset(bh, a.heads, a.qs_b, a.qs_h) + (int64_t)row * a.qs_s + 4 * c4;
       const f32x4 g = *reinterpret_cast<const f32x4*>(a.dout + off);
       const f32x4 o = *reinterpret_cast<const f32x4*>(a.o + off);
       d = g[0] * o[0] + g[1] * o[1] + g[2] * o[2] + g[3] * o[3];
@@ -150,29 +150,31 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32_kernel(BwdArgs a) {
   const int32_t b_begin = qb_first + (int32_t)(((int64_t)nq * wave) / G::kWaves);
   const int32_t b_end = qb_first + (int32_t)(((int64_t)nq * (wave + 1)) / G::kWaves);
 
-  // Rows past the end of each array lie outside these ranges and read as zeros.
-  const __amdgpu_buffer_rsrc_t q_rsrc =
-      raw_buffer(a.q + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * (unsigned)G::kRowBytes);
-  const __amdgpu_buffer_rsrc_t g_rsrc =
-      raw_buffer(a.dout + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * (unsigned)G::kRowBytes);
+  // Rows past the end of each array lie outside these ranges and read as zeros. Rows
+  // are q_row / kv_row bytes apart (the layout's row strides).
+  const int64_t q_off = head_offset(bh, a.heads, a.qs_b, a.qs_h);
+  const int64_t kv_off = head_offset(bh, a.heads, a.kvs_b, a.kvs_h);
+  const unsigned q_row = (unsigned)(a.qs_s * 4), kv_row = (unsigned)(a.kvs_s * 4);
+  const unsigned q_range = strided_range(a.seq_q, a.qs_s, D, 4);
+  const unsigned kv_range = strided_range(a.seq_kv, a.kvs_s, D, 4);
+  const __amdgpu_buffer_rsrc_t q_rsrc = raw_buffer(a.q + q_off, q_range);
+  const __amdgpu_buffer_rsrc_t g_rsrc = raw_buffer(a.dout + q_off, q_range);
   const __amdgpu_buffer_rsrc_t m_rsrc =
       raw_buffer(a.meta + (size_t)bh * a.nqb * kBwdMetaFloats, (unsigned)a.nqb * (unsigned)G::kMetaBytes);
-  const __amdgpu_buffer_rsrc_t k_rsrc =
-      raw_buffer(a.k + (size_t)bh * a.seq_kv * D, (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
-  const __amdgpu_buffer_rsrc_t v_rsrc =
-      raw_buffer(a.v + (size_t)bh * a.seq_kv * D, (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
+  const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(a.k + kv_off, kv_range);
+  const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(a.v + kv_off, kv_range);
 
   auto copy_q = [&](int32_t qb) {
-    const unsigned row0 = (unsigned)(G::kRows * qb) * (unsigned)G::kRowBytes;
+    const unsigned row0 = (unsigned)(G::kRows * qb) * q_row;
 #pragma unroll
     for (int t = 0; t < G::kDmaPerTile; ++t)
-      dma_load_x4(q_rsrc, row0 + tile_src_offset<D>(t, lane), lds_address(q_slot + 1024 * t));
+      dma_load_x4(q_rsrc, row0 + tile_src_offset<D>(t, lane, q_row), lds_address(q_slot + 1024 * t));
   };
   auto copy_g = [&](int32_t qb) {  // dO tile, then the block's lse2 and D
-    const unsigned row0 = (unsigned)(G::kRows * qb) * (unsigned)G::kRowBytes;
+    const unsigned row0 = (unsigned)(G::kRows * qb) * q_row;
 #pragma unroll
     for (int t = 0; t < G::kDmaPerTile; ++t)
-      dma_load_x4(g_rsrc, row0 + tile_src_offset<D>(t, lane), lds_address(g_slot + 1024 * t));
+      dma_load_x4(g_rsrc, row0 + tile_src_offset<D>(t, lane, q_row), lds_address(g_slot + 1024 * t));
     dma_load_x1(m_rsrc, (unsigned)qb * (unsigned)G::kMetaBytes + 4u * lane, lds_address(m_slot));
   };
 
@@ -181,12 +183,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32_kernel(BwdArgs a) {
   {
     unsigned char* const k_tile = lds;
     unsigned char* const v_tile = lds + G::kTileBytes;
-    const unsigned row0 = (unsigned)j0 * (unsigned)G::kRowBytes;
+    const unsigned row0 = (unsigned)j0 * kv_row;
 #pragma unroll
     for (int i = 0; i < G::kDmaPerTile / G::kWaves; ++i) {
       const int t = i * G::kWaves + wave;
-      dma_load_x4(k_rsrc, row0 + tile_src_offset<D>(t, lane), lds_address(k_tile + 1024 * t));
-      dma_load_x4(v_rsrc, row0 + tile_src_offset<D>(t, lane), lds_address(v_tile + 1024 * t));
+      dma_load_x4(k_rsrc, row0 + tile_src_offset<D>(t, lane, kv_row), lds_address(k_tile + 1024 * t));
+      dma_load_x4(v_rsrc, row0 + tile_src_offset<D>(t, lane, kv_row), lds_address(v_tile + 1024 * t));
     }
     wait_vmcnt<0>();
     __syncthreads();
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32_kernel(BwdArgs a) {
       sk += *reinterpret_cast<const f32x4*>(part_k + (w * G::kRows + key) * G::kPStride + 4 * c4);
     }
     if (j >= a.seq_kv) continue;
-    const size_t off = ((size_t)bh * a.seq_kv + j) * D + 4 * c4;
+    const int64_t off = kv_off + (int64_t)j * a.kvs_s + 4 * c4;
     *reinterpret_cast<f32x4*>(a.dv + off) = sv;
     *reinterpret_cast<f32x4*>(a.dk + off) = sk * a.scale;
   }
@@ -359,36 +361,37 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(BwdArgs a) {
   const float my_l2 = meta[lm];
   const float my_d = meta[G::kRows + lm];
 
-  const __amdgpu_buffer_rsrc_t q_rsrc =
-      raw_buffer(a.q + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * (unsigned)G::kRowBytes);
-  const __amdgpu_buffer_rsrc_t g_rsrc =
-      raw_buffer(a.dout + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * (unsigned)G::kRowBytes);
-  const __amdgpu_buffer_rsrc_t k_rsrc =
-      raw_buffer(a.k + (size_t)bh * a.seq_kv * D, (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
-  const __amdgpu_buffer_rsrc_t v_rsrc =
-      raw_buffer(a.v + (size_t)bh * a.seq_kv * D, (unsigned)a.seq_kv * (unsigned)G::kRowBytes);
+  const int64_t q_off = head_offset(bh, a.heads, a.qs_b, a.qs_h);
+  const int64_t kv_off = head_offset(bh, a.heads, a.kvs_b, a.kvs_h);
+  const unsigned q_row = (unsigned)(a.qs_s * 4), kv_row = (unsigned)(a.kvs_s * 4);
+  const unsigned q_range = strided_range(a.seq_q, a.qs_s, D, 4);
+  const unsigned kv_range = strided_range(a.seq_kv, a.kvs_s, D, 4);
+  const __amdgpu_buffer_rsrc_t q_rsrc = raw_buffer(a.q + q_off, q_range);
+  const __amdgpu_buffer_rsrc_t g_rsrc = raw_buffer(a.dout + q_off, q_range);
+  const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(a.k + kv_off, kv_range);
+  const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(a.v + kv_off, kv_range);
   auto copy_k = [&](int32_t b) {
-    const unsigned row0 = (unsigned)(G::kRows * b) * (unsigned)G::kRowBytes;
+    const unsigned row0 = (unsigned)(G::kRows * b) * kv_row;
 #pragma unroll
     for (int t = 0; t < G::kDmaPerTile; ++t)
-      dma_load_x4(k_rsrc, row0 + tile_src_offset<D>(t, lane), lds_address(k_slot + 1024 * t));
+      dma_load_x4(k_rsrc, row0 + tile_src_offset<D>(t, lane, kv_row), lds_address(k_slot + 1024 * t));
   };
   auto copy_v = [&](int32_t b) {
-    const unsigned row0 = (unsigned)(G::kRows * b) * (unsigned)G::kRowBytes;
+    const unsigned row0 = (unsigned)(G::kRows * b) * kv_row;
 #pragma unroll
     for (int t = 0; t < G::kDmaPerTile; ++t)
-      dma_load_x4(v_rsrc, row0 + tile_src_offset<D>(t, lane), lds_address(v_slot + 1024 * t));
+      dma_load_x4(v_rsrc, row0 + tile_src_offset<D>(t, lane, kv_row), lds_address(v_slot + 1024 * t));
   };
 
   // The Q and dO tiles of this block, staged through wave 0's slot, into the
   // B operands of S^T and dP^T.
   {
-    const unsigned row0 = (unsigned)q0 * (unsigned)G::kRowBytes;
+    const unsigned row0 = (unsigned)q0 * q_row;
 #pragma unroll
     for (int i = 0; i < G::kDmaPerTile / G::kWaves; ++i) {
       const int t = i * G::kWaves + wave;
-      dma_load_x4(q_rsrc, row0 + tile_src_offset<D>(t, lane), lds_address(lds + 1024 * t));
-      dma_load_x4(g_rsrc, row0 + tile_src_offset<D>(t, lane),
+      dma_load_x4(q_rsrc, row0 + tile_src_offset<D>(t, lane, q_row), lds_address(lds + 1024 * t));
+      dma_load_x4(g_rsrc, row0 + tile_src_offset<D>(t, lane, q_row),
                   lds_address(lds + G::kTileBytes + 1024 * t));
     }
     wait_vmcnt<0>();
@@ -494,7 +497,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(BwdArgs a) {
     for (int w = 0; w < G::kWaves; ++w)
       acc += *reinterpret_cast<const f32x4*>(part + (w * G::kRows + qi) * G::kPStride + 4 * c4);
     if (row >= a.seq_q) continue;
-    *reinterpret_cast<f32x4*>(a.dq + ((size_t)bh * a.seq_q + row) * D + 4 * c4) = acc * a.scale;
+    *reinterpret_cast<f32x4*>(a.dq + q_off + (int64_t)row * a.qs_s + 4 * c4) = acc * a.scale;
   }
 }
 

@@ -555,15 +555,18 @@ struct BwdShape {
 
 // Pointer-independent checks of the backward. Fills b on success.
 int check_bwd_shape(int in_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
-                    size_t d, double scale, BwdShape* b) {
-  int st = check_shape(in_dtype, SMA_DTYPE_F32, batch, heads, seq_q, seq_kv, d, scale, &b->s);
+                    size_t d, double scale, BwdShape* b, int layout = SMA_LAYOUT_BHSD) {
+  int st = check_shape(in_dtype, SMA_DTYPE_F32, batch, heads, seq_q, seq_kv, d, scale, &b->s, layout);
   if (st != SMA_OK) return st;
   // fp32, or bf16 Q, K, V; fp16 (whose narrow exponent range dS would need rescaling for)
   // is not built.
   if ((in_dtype != SMA_DTYPE_F32 && in_dtype != SMA_DTYPE_BF16) || (d != 64 && d != 128))
     return SMA_ERR_UNSUPPORTED;
+  // The kernels address one (batch, head) through 32-bit buffer offsets: rows of
+  // row_elems elements (heads*d under [B,S,H,d]), with a block of slack.
   const size_t blk = sma::kBwdRowsPerBlock;
-  if ((seq_q + blk) * d * 4 > (size_t(1) << 31) || (seq_kv + blk) * d * 4 > (size_t(1) << 31))
+  const size_t re = b->s.row_elems;
+  if ((seq_q + blk) * re * 4 > (size_t(1) << 31) || (seq_kv + blk) * re * 4 > (size_t(1) << 31))
     return SMA_ERR_UNSUPPORTED;
   b->nqb = (seq_q + blk - 1) / blk;
   b->nkb = (seq_kv + blk - 1) / blk;
@@ -622,14 +625,17 @@ size_t sma_attention_bwd_workspace_bytes(int in_dtype, size_t batch, size_t head
   return b.ws_bytes;
 }
 
-int sma_attention_bwd_timed(const void* q, const void* k, const void* v, const void* o,
-                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                            int in_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
-                            size_t head_dim, double scale, int causal, void* workspace,
-                            size_t workspace_bytes, void* stream, void* event_after_pre,
-                            void* event_after_dkdv) {
+}  // extern "C"
+
+namespace {
+
+int bwd_core(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, float* dq, float* dk, float* dv, int in_dtype, size_t batch,
+             size_t heads, size_t seq_q, size_t seq_kv, size_t head_dim, double scale, int causal,
+             int layout, void* workspace, size_t workspace_bytes, void* stream,
+             void* event_after_pre, void* event_after_dkdv) {
   BwdShape b;
-  int st = check_bwd_shape(in_dtype, batch, heads, seq_q, seq_kv, head_dim, scale, &b);
+  int st = check_bwd_shape(in_dtype, batch, heads, seq_q, seq_kv, head_dim, scale, &b, layout);
   if (st != SMA_OK) return st;
   st = check_bwd_pointers(b, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes);
   if (st != SMA_OK) return st;
@@ -658,6 +664,19 @@ int sma_attention_bwd_timed(const void* q, const void* k, const void* v, const v
   a.nkb = (int32_t)b.nkb;
   a.c = (float)(scale * 1.44269504088896340736);  // scale * log2(e), one rounding
   a.scale = (float)scale;
+  a.heads = (int64_t)heads;
+  if (layout == SMA_LAYOUT_BSHD) {  // element (b, s, h, c) at ((b*S + s)*H + h)*d + c
+    a.qs_b = (int64_t)(seq_q * heads * head_dim);
+    a.kvs_b = (int64_t)(seq_kv * heads * head_dim);
+    a.qs_h = a.kvs_h = (int64_t)head_dim;
+    a.qs_s = a.kvs_s = (int64_t)(heads * head_dim);
+  } else {  // element (b, h, s, c) at ((b*H + h)*S + s)*d + c
+    a.qs_b = (int64_t)(heads * seq_q * head_dim);
+    a.kvs_b = (int64_t)(heads * seq_kv * head_dim);
+    a.qs_h = (int64_t)(seq_q * head_dim);
+    a.kvs_h = (int64_t)(seq_kv * head_dim);
+    a.qs_s = a.kvs_s = (int64_t)head_dim;
+  }
   const auto launch = in_dtype == SMA_DTYPE_BF16 ? sma::launch_bwd_bf16 : sma::launch_bwd_f32;
   hipError_t e = launch(a, (int)head_dim, causal != 0, static_cast<hipStream_t>(stream),
                         static_cast<hipEvent_t>(event_after_pre),
@@ -665,14 +684,39 @@ int sma_attention_bwd_timed(const void* q, const void* k, const void* v, const v
   return e == hipSuccess ? SMA_OK : SMA_ERR_HIP;
 }
 
+}  // namespace
+
+extern "C" {
+
+int sma_attention_bwd_timed(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                            int in_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
+                            size_t head_dim, double scale, int causal, void* workspace,
+                            size_t workspace_bytes, void* stream, void* event_after_pre,
+                            void* event_after_dkdv) {
+  return bwd_core(q, k, v, o, lse, dout, dq, dk, dv, in_dtype, batch, heads, seq_q, seq_kv,
+                  head_dim, scale, causal, SMA_LAYOUT_BHSD, workspace, workspace_bytes, stream,
+                  event_after_pre, event_after_dkdv);
+}
+
 int sma_attention_bwd(const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, float* dq, float* dk, float* dv,
                       int in_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
                       size_t head_dim, double scale, int causal, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  return sma_attention_bwd_timed(q, k, v, o, lse, dout, dq, dk, dv, in_dtype, batch, heads, seq_q,
-                                 seq_kv, head_dim, scale, causal, workspace, workspace_bytes,
-                                 stream, nullptr, nullptr);
+  return bwd_core(q, k, v, o, lse, dout, dq, dk, dv, in_dtype, batch, heads, seq_q, seq_kv,
+                  head_dim, scale, causal, SMA_LAYOUT_BHSD, workspace, workspace_bytes, stream,
+                  nullptr, nullptr);
+}
+
+int sma_attention_bwd_layout(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                             int in_dtype, size_t batch, size_t heads, size_t seq_q,
+                             size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_core(q, k, v, o, lse, dout, dq, dk, dv, in_dtype, batch, heads, seq_q, seq_kv,
+                  head_dim, scale, causal, layout, workspace, workspace_bytes, stream, nullptr,
+                  nullptr);
 }
 
 // ---------------------------------------------------------------- row primitives

@@ -65,17 +65,17 @@ struct CombineArgs {
 };
 
 // Arguments of the attention-backward launches (fp32 or bf16 Q, K, V; fp32 O, dO and
-// gradients).
+// gradients). Tensors are addressed through the strides below.
 struct BwdArgs {
-  const float* q;     // [bh][seq_q][d]
-  const float* k;     // [bh][seq_kv][d]
-  const float* v;     // [bh][seq_kv][d]
-  const float* o;     // [bh][seq_q][d], the forward's output
-  const float* dout;  // [bh][seq_q][d], upstream gradient dL/dO
+  const float* q;     // Q rows
+  const float* k;     // K rows
+  const float* v;     // V rows
+  const float* o;     // the forward's output, Q's layout
+  const float* dout;  // upstream gradient dL/dO, Q's layout
   const float* lse;   // [bh][seq_q], the forward's log-sum-exp (natural log)
-  float* dq;          // [bh][seq_q][d]
-  float* dk;          // [bh][seq_kv][d]
-  float* dv;          // [bh][seq_kv][d]
+  float* dq;          // Q's layout
+  float* dk;          // K's layout
+  float* dv;          // K's layout
   float* meta;        // workspace [bh][nqb][64]: per 32-row query block, lse2 then D
   // bf16 inputs (the bf16 backward): q, k, v as bf16, and the workspace copy of dO
   // rounded to bf16 ([bh][seq_q][d]); o and dout stay fp32.
@@ -91,6 +91,11 @@ struct BwdArgs {
   float c;            // scale * log2(e) (signed), rounded once to fp32
   float scale;        // scale rounded to fp32
   uint32_t nwg;       // workgroups of the launch (set per launch)
+  // Element strides (the head dim is contiguous), as in FwdArgs: (batch, head, row) of
+  // Q, O, dO and dQ, and of K, V, dK and dV. The bf16 copy of dO is always [bh][seq_q][d].
+  int64_t heads;
+  int64_t qs_b, qs_h, qs_s;
+  int64_t kvs_b, kvs_h, kvs_s;
 };
 
 // Workgroup geometry the planner needs (must match the kernels).

@@ -325,6 +325,27 @@ def test_backward_workspace_and_host_checks():
     assert call(dk=o + 64) == ALIAS and call(ws=dq + 256) == ALIAS
 
 
+def test_backward_layout_host_checks():
+    """sma_attention_bwd_layout: the layout code and the [B,S,H,d] 32-bit offset limit are
+    checked before any HIP call."""
+    lib = sma.library()
+    base = [0x10_0000_0000 * i for i in range(1, 11)]
+    q, k, v, o, lse, g, dq, dk, dv, ws = base
+
+    def call(layout, H=2, sq=100, skv=70, d=64, idt=F32, wsb=1 << 30, dq=dq):
+        return lib.sma_attention_bwd_layout(q, k, v, o, lse, g, dq, dk, dv, idt, 1, H, sq, skv, d,
+                                            0.125, 1, layout, ws, wsb, None)
+
+    assert call(7) == INVAL and call(-1) == INVAL
+    # one head's rows are heads*d elements apart under [B,S,H,d]: 64 heads x 128 dims x 2^17
+    # rows pass under [B,H,S,d] and exceed 2 GiB of offsets under [B,S,H,d]
+    big = dict(H=64, sq=1 << 17, skv=64, d=128)
+    assert call(sma.SMA_LAYOUT_BSHD, **big) == UNSUP
+    assert call(sma.SMA_LAYOUT_BSHD, idt=F16) == UNSUP and call(sma.SMA_LAYOUT_BSHD, d=96) == UNSUP
+    assert call(sma.SMA_LAYOUT_BSHD, wsb=16) == INVAL  # workspace too small
+    assert call(sma.SMA_LAYOUT_BSHD, dq=q) == ALIAS
+
+
 def test_layout_argument_and_its_limits():
     """Layout codes other than BHSD/BSHD are invalid; under BSHD the 2 GiB offset limits apply to
     rows heads*head_dim apart, so the in-workgroup key-split kernel stops fitting at 1/heads
