@@ -8,9 +8,11 @@ row primitives on a materialised score matrix (rows_oracle.c: pulsatrix
 ``softmax_rows`` / ``logsumexp_rows``, the TorchLean hard-masked softmax and
 MicroGPT's fused scale + causal mask + softmax), the gradients of the
 attention forward (attention_bwd_oracle.c: the chain rule through the
-softmax, recomputed from q, k, v and the upstream gradient), and the forward
+softmax, recomputed from q, k, v and the upstream gradient), the forward
 with an explicit hard mask (attention_masked_oracle.c: the TorchLean
-hard-masked softmax inside the attention).
+hard-masked softmax inside the attention), and its gradients
+(attention_bwd_masked_oracle.c: the same chain rule over each row's admitted
+keys).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package. The attention library never does, and
@@ -26,7 +28,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRCS = [os.path.join(_HERE, "attention_oracle.c"), os.path.join(_HERE, "rows_oracle.c"),
-         os.path.join(_HERE, "attention_bwd_oracle.c"), os.path.join(_HERE, "attention_masked_oracle.c")]
+         os.path.join(_HERE, "attention_bwd_oracle.c"), os.path.join(_HERE, "attention_masked_oracle.c"),
+         os.path.join(_HERE, "attention_bwd_masked_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
@@ -68,6 +71,10 @@ def _bind(lib):
     lib.oracle_attention_fwd_masked.argtypes = [dp, dp, dp, dp, L, L, L, L, L, L, L, ctypes.c_double,
                                                 ctypes.c_int, dp, dp]
     lib.oracle_attention_fwd_masked.restype = ctypes.c_int
+    for name in ("oracle_attention_bwd_masked", "oracle_attention_bwd_masked_bound"):
+        getattr(lib, name).argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, L, L, ctypes.c_double,
+                                       ctypes.c_int, dp, dp, dp]
+        getattr(lib, name).restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -188,6 +195,44 @@ def attention_fwd_masked(q, k, v, mask, scale: float, causal: bool, lib=None):
     if rc != 0:
         raise ValueError("oracle_attention_fwd_masked rejected its arguments")
     return o, lse
+
+
+def _mask_bytes(mask, B, H, Sq, Skv):
+    """The mask as contiguous 0/1 bytes and its (batch, head) strides (0 broadcasts)."""
+    m = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+    if m.ndim != 4 or m.shape[2:] != (Sq, Skv) or m.shape[0] not in (1, B) or m.shape[1] not in (1, H):
+        raise ValueError(f"mask shape {m.shape} does not broadcast to {(B, H, Sq, Skv)}")
+    sh = Sq * Skv if m.shape[1] == H else 0
+    sb = m.shape[1] * Sq * Skv if m.shape[0] == B else 0
+    return m, sb, sh
+
+
+def _bwd_masked_call(fn, q, k, v, dout, mask, scale, causal, lib):
+    lib = lib or load()
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    assert k.shape == (B, H, Skv, D) and v.shape == (B, H, Skv, D) and dout.shape == q.shape
+    m, sb, sh = _mask_bytes(mask, B, H, Sq, Skv)
+    a = np.empty(q.shape, dtype=np.float64)
+    b = np.empty(k.shape, dtype=np.float64)
+    c = np.empty(v.shape, dtype=np.float64)
+    rc = getattr(lib, fn)(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, m.ctypes.data,
+                          sb, sh, B, H, Sq, Skv, D, float(scale), int(bool(causal)), a.ctypes.data,
+                          b.ctypes.data, c.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"{fn} rejected its arguments")
+    return a, b, c
+
+
+def attention_bwd_masked(q, k, v, dout, mask, scale: float, causal: bool, lib=None):
+    """dQ, dK, dV (float64) of the hard-masked forward (mask as attention_fwd_masked takes it)."""
+    return _bwd_masked_call("oracle_attention_bwd_masked", q, k, v, dout, mask, scale, causal, lib)
+
+
+def attention_bwd_masked_bound(q, k, v, dout, mask, scale: float, causal: bool, lib=None):
+    """Error scale (mq, mk, mv) of the masked gradients, as attention_bwd_bound over the admitted pairs."""
+    return _bwd_masked_call("oracle_attention_bwd_masked_bound", q, k, v, dout, mask, scale, causal, lib)
 
 
 def _rows2d(x):
