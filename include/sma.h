@@ -297,6 +297,32 @@ int sma_attention_bwd_layout(const void* q, const void* k, const void* v, const 
                              size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* sma_attention_bwd_layout with the hard mask of sma_attention_fwd_masked:
+ * the gradients of that forward (TorchLean page, hard-masked softmax: a pair
+ * whose mask byte is zero has no probability, so it adds nothing to any
+ * gradient; a row that admits nothing gets dq = 0). o and lse must be what
+ * sma_attention_fwd_masked returned for the same mask. mask, mask_batches and
+ * mask_heads as for sma_attention_fwd_masked (device bytes, nonzero admits, a
+ * size of 1 broadcasts; combined with the causal bound when causal). The
+ * workspace (sma_attention_bwd_masked_workspace_bytes) holds the packed mask
+ * after what sma_attention_bwd needs. The mask must not overlap dq, dk, dv or
+ * the workspace (ALIASING). Other arguments and errors as for
+ * sma_attention_bwd_layout. */
+int sma_attention_bwd_masked(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                             const void* mask, size_t mask_batches, size_t mask_heads,
+                             int in_dtype, size_t batch, size_t heads, size_t seq_q,
+                             size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sma_attention_bwd_masked needs: those of sma_attention_bwd,
+ * then the packed mask (one 32-bit word per 32 keys of each row of each
+ * (mask batch, mask head), rounded up to 256). 0 for invalid arguments. */
+size_t sma_attention_bwd_masked_workspace_bytes(int in_dtype, size_t batch, size_t heads,
+                                                size_t seq_q, size_t seq_kv, size_t head_dim,
+                                                int causal, int layout, size_t mask_batches,
+                                                size_t mask_heads);
+
 /* Workspace bytes sma_attention_bwd needs for this shape: 256 per 32-row query
  * block of every (batch, head), rounded up to 256; with SMA_DTYPE_BF16 also
  * batch*heads*seq_q*head_dim*2 bytes (dout as bf16), rounded up to 256. 0 for

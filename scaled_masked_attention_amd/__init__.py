@@ -105,6 +105,11 @@ def library():
         lib.sma_attention_bwd_timed.restype = ctypes.c_int
         lib.sma_attention_bwd_layout.argtypes = bwd[:17] + [ctypes.c_int] + bwd[17:]
         lib.sma_attention_bwd_layout.restype = ctypes.c_int
+        lib.sma_attention_bwd_masked.argtypes = bwd[:9] + [vp, sz, sz] + bwd[9:17] + [ctypes.c_int] + bwd[17:]
+        lib.sma_attention_bwd_masked.restype = ctypes.c_int
+        lib.sma_attention_bwd_masked_workspace_bytes.argtypes = [ctypes.c_int, sz, sz, sz, sz, sz,
+                                                                 ctypes.c_int, ctypes.c_int, sz, sz]
+        lib.sma_attention_bwd_masked_workspace_bytes.restype = sz
         lib.sma_attention_bwd_workspace_bytes.argtypes = [ctypes.c_int, sz, sz, sz, sz, sz, ctypes.c_int]
         lib.sma_attention_bwd_workspace_bytes.restype = sz
         lib.sma_status_string.argtypes = [ctypes.c_int]
@@ -324,15 +329,16 @@ def attention_bwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, dout_ptr, dq_ptr, dk_
 
 
 def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=None,
-                  layout="bhsd"):
+                  layout="bhsd", mask=None):
     """(dQ, dK, dV) of O = softmax(scale * Q K^T + mask) V for the upstream gradient dout.
 
     q, o, dout [B,H,Sq,D] and k, v [B,H,Skv,D] contiguous tensors on the current
     HIP device: q, k, v all float32 or all bfloat16 (then on 16-bit MFMA), o, dout
     and lse ([B,H,Sq]) float32, o and lse as attention_fwd returned them for the
     same q, k, v, scale and causal. layout="bshd" takes q, o, dout [B,Sq,H,D] and
-    k, v [B,Skv,H,D] (lse stays [B,H,Sq]). Returns three float32 tensors shaped
-    like q, k and v. The workspace is allocated when not given.
+    k, v [B,Skv,H,D] (lse stays [B,H,Sq]). mask: the hard mask attention_fwd was
+    given (bool or uint8, [Sq,Skv] or [B or 1, H or 1, Sq, Skv]). Returns three
+    float32 tensors shaped like q, k and v. The workspace is allocated when not given.
     """
     import torch
 
@@ -371,14 +377,35 @@ def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=Non
     dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
     dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
     dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
-    need = attention_bwd_workspace_bytes(in_dt, B, H, Sq, Skv, D, causal)
+    if mask is not None:
+        if not isinstance(mask, torch.Tensor) or mask.dtype not in (torch.bool, torch.uint8):
+            raise ValueError("mask must be a bool or uint8 torch tensor")
+        if mask.dim() == 2:
+            mask = mask.view(1, 1, *mask.shape)
+        if (mask.dim() != 4 or tuple(mask.shape[2:]) != (Sq, Skv) or mask.shape[0] not in (1, B)
+                or mask.shape[1] not in (1, H)):
+            raise ValueError(f"mask shape {tuple(mask.shape)} does not broadcast to {(B, H, Sq, Skv)}")
+        if mask.device != dev or not mask.is_contiguous():
+            raise ValueError(f"mask must be a contiguous tensor on {dev}")
+        need = library().sma_attention_bwd_masked_workspace_bytes(in_dt, B, H, Sq, Skv, D,
+                                                                  int(bool(causal)), LAYOUTS[layout],
+                                                                  mask.shape[0], mask.shape[1])
+    else:
+        need = attention_bwd_workspace_bytes(in_dt, B, H, Sq, Skv, D, causal)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
         stream = torch.cuda.current_stream()
-    if layout == "bhsd":
+    if mask is not None:
+        _raise(library().sma_attention_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                                  _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                                  _ptr(mask), mask.shape[0], mask.shape[1], in_dt,
+                                                  B, H, Sq, Skv, D, float(scale),
+                                                  int(bool(causal)), LAYOUTS[layout], ws_ptr,
+                                                  ws_bytes, stream.cuda_stream))
+    elif layout == "bhsd":
         attention_bwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                           _ptr(dk), _ptr(dv), in_dt, B, H, Sq, Skv, D, scale, causal, ws_ptr,
                           ws_bytes, stream.cuda_stream)

@@ -184,10 +184,12 @@ __device__ __forceinline__ void store_partial(float* part, int wave, int lm, int
 // A workgroup owns 32 keys; K and V stay in registers as the B operands of S = Q K^T and
 // dP = dO V^T. Its 4 waves split the query blocks that admit any of the keys; each
 // streams its Q and dO tiles (permuted) and the block's lse2/D into private LDS slots.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   using G = HGeom<D>;
-  constexpr int kSlotBytes = 2 * G::kTileBytes + G::kMetaBytes;  // Q tile, dO tile, lse2/D
+  // Q tile, dO tile, lse2/D, and with a hard mask the block's 32 mask words (this key block's
+  // word of each query row; the upper 32 lanes of the copy repeat them).
+  constexpr int kSlotBytes = 2 * G::kTileBytes + G::kMetaBytes + (MASKED ? 256 : 0);
   constexpr int kStageBytes = G::kWaves * kSlotBytes;
   constexpr int kLdsBytes = kStageBytes > 2 * G::kPartBytes ? kStageBytes : 2 * G::kPartBytes;
   static_assert(2 * G::kTileBytes <= kSlotBytes, "K and V prologue tiles fit in wave 0's slot");
@@ -201,6 +203,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   unsigned char* const q_slot = lds + wave * kSlotBytes;
   unsigned char* const g_slot = q_slot + G::kTileBytes;
   unsigned char* const m_slot = g_slot + G::kTileBytes;
+  unsigned char* const w_slot = m_slot + G::kMetaBytes;  // mask words (MASKED)
 
   const uint32_t lam = xcd_remap(blockIdx.x, a.nwg);
   const int64_t bh = (int64_t)(lam / (uint32_t)a.nkb);
@@ -232,6 +235,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   const unsigned kv_range = strided_range(a.seq_kv, a.kvs_s, D, 2);
   const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(a.k16 + kv_off, kv_range);
   const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(a.v16 + kv_off, kv_range);
+  __amdgpu_buffer_rsrc_t w_rsrc;  // rows past seq_q read as 0: nothing admitted
+  if (MASKED)
+    w_rsrc = raw_buffer(a.mask_bits + head_offset(bh, a.heads, a.mbits_sb, a.mbits_sh),
+                        (unsigned)a.seq_q * (unsigned)a.mask_words * 4u);
 
   auto copy_q = [&](int32_t qb) {
     const unsigned row0 = (unsigned)(G::kRows * qb) * q_row;
@@ -245,6 +252,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
     for (int t = 0; t < G::kDmaPerTile; ++t)
       dma_load_x4(g_rsrc, row0 + tile_src<D, true>(t, lane, g_row), lds_address(g_slot + 1024 * t));
     dma_load_x1(m_rsrc, (unsigned)qb * (unsigned)G::kMetaBytes + 4u * lane, lds_address(m_slot));
+    if (MASKED)
+      dma_load_x1(w_rsrc, ((unsigned)(G::kRows * qb + (lane & 31)) * (unsigned)a.mask_words +
+                           (unsigned)(j0 / G::kRows)) * 4u, lds_address(w_slot));
   };
 
   // This block's K and V tiles (unpermuted), staged through wave 0's slot (each wave
@@ -305,11 +315,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
     for (int st = 0; st < G::kSteps; ++st) s = mfma16(row_chunk<D>(q_slot, lm, 2 * st + lh), kr[st], s);
     // Some pair of this block is masked iff its last key lies past its first row's limit.
     const bool diag = CAUSAL && (j0 + G::kRows - 1 > i0 + delta);
+    uint32_t mw[16];  // mask word of query row perm_acc_row(r, lh); bit lm is this lane's key
+    if (MASKED) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x4 w4 = *reinterpret_cast<const u32x4*>(w_slot + 4 * (16 * (q4 / 2) + 8 * lh + 4 * (q4 % 2)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mw[4 * q4 + e] = w4[e];
+      }
+    }
     bf16x8 pp[2], pds[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float t = s[r] * a.c - l2[r / 4][r % 4];
       if (diag) t = (j0 + lm <= i0 + perm_acc_row(r, lh) + delta) ? t : -INFINITY;
+      if (MASKED) t = ((mw[r] >> lm) & 1u) ? t : -INFINITY;
       const float p = __builtin_amdgcn_exp2f(t);
       const float ds = p * (dp[r] - dd[r / 4][r % 4]);
       pp[r / 8][r % 8] = (__bf16)p;
@@ -374,10 +394,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
 // A workgroup owns 32 queries; Q and dO stay in registers as the B operands of
 // S^T = K Q^T and dP^T = V dO^T. Its 4 waves split the key blocks the rows admit; each
 // streams its K and V tiles (permuted) into private LDS slots.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   using G = HGeom<D>;
-  constexpr int kSlotBytes = 2 * G::kTileBytes;  // K tile, V tile
+  // K tile, V tile, and with a hard mask each query row's word of the key block.
+  constexpr int kSlotBytes = 2 * G::kTileBytes + (MASKED ? 256 : 0);
   constexpr int kStageBytes = G::kWaves * kSlotBytes;
   constexpr int kLdsBytes = kStageBytes > G::kPartBytes ? kStageBytes : G::kPartBytes;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
@@ -389,6 +410,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   const int lh = lane >> 5;
   unsigned char* const k_slot = lds + wave * kSlotBytes;
   unsigned char* const v_slot = k_slot + G::kTileBytes;
+  unsigned char* const w_slot = v_slot + G::kTileBytes;  // mask words (MASKED)
 
   // Workgroup -> (batch*head, query block), the longest causal blocks first.
   const uint32_t lam = xcd_remap(blockIdx.x, a.nwg);
@@ -420,11 +442,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   const unsigned kv_range = strided_range(a.seq_kv, a.kvs_s, D, 2);
   const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(a.k16 + kv_off, kv_range);
   const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(a.v16 + kv_off, kv_range);
-  auto copy_k = [&](int32_t b) {
+  __amdgpu_buffer_rsrc_t w_rsrc;  // rows past seq_q read as 0: nothing admitted
+  if (MASKED)
+    w_rsrc = raw_buffer(a.mask_bits + head_offset(bh, a.heads, a.mbits_sb, a.mbits_sh),
+                        (unsigned)a.seq_q * (unsigned)a.mask_words * 4u);
+  auto copy_k = [&](int32_t b) {  // K tile, then the rows' mask words of block b
     const unsigned row0 = (unsigned)(G::kRows * b) * kv_row;
 #pragma unroll
     for (int t = 0; t < G::kDmaPerTile; ++t)
       dma_load_x4(k_rsrc, row0 + tile_src<D, true>(t, lane, kv_row), lds_address(k_slot + 1024 * t));
+    if (MASKED)
+      dma_load_x1(w_rsrc, ((unsigned)(q0 + (lane & 31)) * (unsigned)a.mask_words + (unsigned)b) * 4u,
+                  lds_address(w_slot));
   };
   auto copy_v = [&](int32_t b) {
     const unsigned row0 = (unsigned)(G::kRows * b) * kv_row;
@@ -483,11 +512,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int st = 0; st < G::kSteps; ++st) s = mfma16(row_chunk<D>(k_slot, lm, 2 * st + lh), qr[st], s);
     const bool edge = j0 + G::kRows > lo;  // some key of the block lies past the first row's limit
+    const uint32_t mw = MASKED ? *reinterpret_cast<const uint32_t*>(w_slot + 4 * lm) : ~0u;
     bf16x8 pds[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float t = s[r] * a.c - my_l2;
       if (edge) t = (j0 + perm_acc_row(r, lh) < lim) ? t : -INFINITY;
+      if (MASKED) t = ((mw >> perm_acc_row(r, lh)) & 1u) ? t : -INFINITY;
       const float p = __builtin_amdgcn_exp2f(t);
       pds[r / 8][r % 8] = (__bf16)(p * (dp[r] - my_d));
     }
@@ -527,7 +558,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASKED>
 hipError_t launch_bwd_bf16_variant(const BwdArgs& a0, hipStream_t s, hipEvent_t ev_pre,
                                    hipEvent_t ev_dkdv) {
   BwdArgs a = a0;
@@ -539,28 +570,34 @@ hipError_t launch_bwd_bf16_variant(const BwdArgs& a0, hipStream_t s, hipEvent_t 
   if (ev_pre && hipEventRecord(ev_pre, s) != hipSuccess) return hipErrorInvalidValue;
   if (nk > 0) {
     a.nwg = nk;
-    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3(nk), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, CAUSAL, MASKED>), dim3(nk), dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   if (ev_dkdv && hipEventRecord(ev_dkdv, s) != hipSuccess) return hipErrorInvalidValue;
   if (nq > 0) {
     a.nwg = nq;
-    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, CAUSAL>), dim3(nq), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, CAUSAL, MASKED>), dim3(nq), dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   return hipSuccess;
+}
+
+template <int D>
+hipError_t launch_bwd_bf16_d(const BwdArgs& a, bool causal, hipStream_t s, hipEvent_t ev_pre,
+                             hipEvent_t ev_dkdv) {
+  if (a.mask_bits)
+    return causal ? launch_bwd_bf16_variant<D, true, true>(a, s, ev_pre, ev_dkdv)
+                  : launch_bwd_bf16_variant<D, false, true>(a, s, ev_pre, ev_dkdv);
+  return causal ? launch_bwd_bf16_variant<D, true, false>(a, s, ev_pre, ev_dkdv)
+                : launch_bwd_bf16_variant<D, false, false>(a, s, ev_pre, ev_dkdv);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, bool causal, hipStream_t s,
                            hipEvent_t ev_pre, hipEvent_t ev_dkdv) {
-  if (head_dim == 64)
-    return causal ? launch_bwd_bf16_variant<64, true>(a, s, ev_pre, ev_dkdv)
-                  : launch_bwd_bf16_variant<64, false>(a, s, ev_pre, ev_dkdv);
-  if (head_dim == 128)
-    return causal ? launch_bwd_bf16_variant<128, true>(a, s, ev_pre, ev_dkdv)
-                  : launch_bwd_bf16_variant<128, false>(a, s, ev_pre, ev_dkdv);
+  if (head_dim == 64) return launch_bwd_bf16_d<64>(a, causal, s, ev_pre, ev_dkdv);
+  if (head_dim == 128) return launch_bwd_bf16_d<128>(a, causal, s, ev_pre, ev_dkdv);
   return hipErrorInvalidValue;
 }
 

@@ -629,14 +629,42 @@ size_t sma_attention_bwd_workspace_bytes(int in_dtype, size_t batch, size_t head
 
 namespace {
 
+// A hard mask of the backward: sizes, the packed bits appended to the workspace (b->ws_bytes
+// grows by their size, *bits_at is where they start), and no overlap with an output.
+int check_bwd_mask(BwdShape* b, const MaskArg& m, const float* dq, const float* dk,
+                   const float* dv, const void* ws, size_t* bits_at) {
+  const Shape& s = b->s;
+  if ((m.batches != 1 && m.batches != s.batch) || (m.heads != 1 && m.heads != s.heads))
+    return SMA_ERR_INVALID_VALUE;
+  size_t n;
+  if (!mul(m.batches * m.heads, s.seq_q, &n) || !mul(n, s.seq_kv, &n)) return SMA_ERR_INVALID_VALUE;
+  if (n > (size_t(1) << 40)) return SMA_ERR_UNSUPPORTED;
+  if (s.seq_q * mask_words(s.seq_kv) * 4 > (size_t(1) << 31)) return SMA_ERR_UNSUPPORTED;
+  *bits_at = b->ws_bytes;
+  b->ws_bytes += mask_bits_bytes(s, m);
+  if (overlap(dq, s.rows ? b->q32 : 0, m.mask, n) || overlap(dk, b->kv32, m.mask, n) ||
+      overlap(dv, b->kv32, m.mask, n) || overlap(ws, ws ? b->ws_bytes : 0, m.mask, n))
+    return SMA_ERR_ALIASING;
+  return SMA_OK;
+}
+
 int bwd_core(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dout, float* dq, float* dk, float* dv, int in_dtype, size_t batch,
              size_t heads, size_t seq_q, size_t seq_kv, size_t head_dim, double scale, int causal,
-             int layout, void* workspace, size_t workspace_bytes, void* stream,
+             int layout, const MaskArg& mask, void* workspace, size_t workspace_bytes, void* stream,
              void* event_after_pre, void* event_after_dkdv) {
   BwdShape b;
   int st = check_bwd_shape(in_dtype, batch, heads, seq_q, seq_kv, head_dim, scale, &b, layout);
   if (st != SMA_OK) return st;
+  const bool masked = mask.mask != nullptr;
+  size_t bits_at = 0;
+  if (masked || mask.batches || mask.heads) {
+    if (!masked && b.s.rows > 0 && seq_kv > 0) return SMA_ERR_NULL_POINTER;
+    if (masked) {
+      st = check_bwd_mask(&b, mask, dq, dk, dv, workspace, &bits_at);
+      if (st != SMA_OK) return st;
+    }
+  }
   st = check_bwd_pointers(b, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes);
   if (st != SMA_OK) return st;
   if (b.s.rows == 0 && b.s.bh * seq_kv == 0) return SMA_OK;
@@ -677,9 +705,24 @@ int bwd_core(const void* q, const void* k, const void* v, const void* o, const f
     a.kvs_h = (int64_t)(seq_kv * head_dim);
     a.qs_s = a.kvs_s = (int64_t)head_dim;
   }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (masked && seq_kv > 0 && seq_q > 0) {
+    sma::MaskPackArgs mp{};
+    mp.mask = static_cast<const unsigned char*>(mask.mask);
+    mp.bits = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) + bits_at);
+    mp.slabs = (int64_t)(mask.batches * mask.heads);
+    mp.seq_q = (int32_t)seq_q;
+    mp.seq_kv = (int32_t)seq_kv;
+    mp.words = (int32_t)mask_words(seq_kv);
+    if (sma::launch_mask_pack(mp, hs) != hipSuccess) return SMA_ERR_HIP;
+    a.mask_bits = mp.bits;
+    a.mask_words = mp.words;
+    const int64_t slab = (int64_t)seq_q * mp.words;
+    a.mbits_sh = mask.heads == heads && heads > 1 ? slab : 0;
+    a.mbits_sb = mask.batches == batch && batch > 1 ? (int64_t)mask.heads * slab : 0;
+  }
   const auto launch = in_dtype == SMA_DTYPE_BF16 ? sma::launch_bwd_bf16 : sma::launch_bwd_f32;
-  hipError_t e = launch(a, (int)head_dim, causal != 0, static_cast<hipStream_t>(stream),
-                        static_cast<hipEvent_t>(event_after_pre),
+  hipError_t e = launch(a, (int)head_dim, causal != 0, hs, static_cast<hipEvent_t>(event_after_pre),
                         static_cast<hipEvent_t>(event_after_dkdv));
   return e == hipSuccess ? SMA_OK : SMA_ERR_HIP;
 }
@@ -695,8 +738,8 @@ int sma_attention_bwd_timed(const void* q, const void* k, const void* v, const v
                             size_t workspace_bytes, void* stream, void* event_after_pre,
                             void* event_after_dkdv) {
   return bwd_core(q, k, v, o, lse, dout, dq, dk, dv, in_dtype, batch, heads, seq_q, seq_kv,
-                  head_dim, scale, causal, SMA_LAYOUT_BHSD, workspace, workspace_bytes, stream,
-                  event_after_pre, event_after_dkdv);
+                  head_dim, scale, causal, SMA_LAYOUT_BHSD, MaskArg(), workspace, workspace_bytes,
+                  stream, event_after_pre, event_after_dkdv);
 }
 
 int sma_attention_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -705,8 +748,8 @@ int sma_attention_bwd(const void* q, const void* k, const void* v, const void* o
                       size_t head_dim, double scale, int causal, void* workspace,
                       size_t workspace_bytes, void* stream) {
   return bwd_core(q, k, v, o, lse, dout, dq, dk, dv, in_dtype, batch, heads, seq_q, seq_kv,
-                  head_dim, scale, causal, SMA_LAYOUT_BHSD, workspace, workspace_bytes, stream,
-                  nullptr, nullptr);
+                  head_dim, scale, causal, SMA_LAYOUT_BHSD, MaskArg(), workspace, workspace_bytes,
+                  stream, nullptr, nullptr);
 }
 
 int sma_attention_bwd_layout(const void* q, const void* k, const void* v, const void* o,
@@ -715,8 +758,39 @@ int sma_attention_bwd_layout(const void* q, const void* k, const void* v, const 
                              size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
                              void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_core(q, k, v, o, lse, dout, dq, dk, dv, in_dtype, batch, heads, seq_q, seq_kv,
-                  head_dim, scale, causal, layout, workspace, workspace_bytes, stream, nullptr,
+                  head_dim, scale, causal, layout, MaskArg(), workspace, workspace_bytes, stream,
+                  nullptr, nullptr);
+}
+
+int sma_attention_bwd_masked(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                             const void* mask, size_t mask_batches, size_t mask_heads,
+                             int in_dtype, size_t batch, size_t heads, size_t seq_q,
+                             size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  MaskArg m;
+  m.mask = mask;
+  m.batches = mask_batches;
+  m.heads = mask_heads;
+  return bwd_core(q, k, v, o, lse, dout, dq, dk, dv, in_dtype, batch, heads, seq_q, seq_kv,
+                  head_dim, scale, causal, layout, m, workspace, workspace_bytes, stream, nullptr,
                   nullptr);
+}
+
+size_t sma_attention_bwd_masked_workspace_bytes(int in_dtype, size_t batch, size_t heads,
+                                                size_t seq_q, size_t seq_kv, size_t head_dim,
+                                                int causal, int layout, size_t mask_batches,
+                                                size_t mask_heads) {
+  (void)causal;
+  BwdShape b;
+  if (check_bwd_shape(in_dtype, batch, heads, seq_q, seq_kv, head_dim, 1.0, &b, layout) != SMA_OK)
+    return 0;
+  if ((mask_batches != 1 && mask_batches != batch) || (mask_heads != 1 && mask_heads != heads)) return 0;
+  MaskArg m;
+  m.mask = &b;  // any non-null address: only the sizes matter here
+  m.batches = mask_batches;
+  m.heads = mask_heads;
+  return b.ws_bytes + mask_bits_bytes(b.s, m);
 }
 
 // ---------------------------------------------------------------- row primitives

@@ -96,6 +96,11 @@ struct BwdArgs {
   int64_t heads;
   int64_t qs_b, qs_h, qs_s;
   int64_t kvs_b, kvs_h, kvs_s;
+  // Optional hard mask, packed as in FwdArgs (bit j % 32 of word (row, j / 32) admits key
+  // j); null when there is none.
+  const uint32_t* mask_bits;
+  int32_t mask_words;
+  int64_t mbits_sb, mbits_sh;
 };
 
 // Workgroup geometry the planner needs (must match the kernels).

@@ -383,3 +383,25 @@ def test_masked_entry_point_host_checks():
     assert call(ws=M + 128, wsb=4096) == ALIAS         # workspace on top of the mask
     assert call(ws=None, wsb=0) == INVAL and call(wsb=2 * 128 * 4 * 4 - 1) == INVAL
     assert call(idt=BF16, plan=sma.Plan(kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=1)) == UNSUP
+
+
+def test_backward_masked_host_checks():
+    """sma_attention_bwd_masked: mask broadcast sizes, a missing mask, aliasing with an
+    output and a workspace without room for the packed mask fail before any HIP call."""
+    lib = sma.library()
+    base = [0x10_0000_0000 * i for i in range(1, 12)]
+    q, k, v, o, lse, g, dq, dk, dv, ws, m = base
+    plain = sma.attention_bwd_workspace_bytes(F32, 2, 3, 100, 70, 64, True)
+    # 3 heads x 100 rows x 3 words (70 keys) x 4 bytes = 3600 -> 3840 after rounding to 256
+    assert lib.sma_attention_bwd_masked_workspace_bytes(F32, 2, 3, 100, 70, 64, 1, 0, 1, 3) == plain + 3840
+    assert lib.sma_attention_bwd_masked_workspace_bytes(F32, 2, 3, 100, 70, 64, 1, 0, 2, 2) == 0
+
+    def call(mb=1, mh=3, mask=m, dq=dq, wsb=1 << 30):
+        return lib.sma_attention_bwd_masked(q, k, v, o, lse, g, dq, dk, dv, mask, mb, mh, F32, 2, 3, 100,
+                                            70, 64, 0.125, 1, 0, ws, wsb, None)
+
+    assert call(mb=3) == INVAL and call(mh=2) == INVAL
+    assert call(mask=None) == NULLP
+    assert call(dq=m - 4096) == ALIAS  # dq (100 rows of 64 floats per head) runs into the mask
+    assert call(wsb=plain) == INVAL     # no room for the packed mask
+

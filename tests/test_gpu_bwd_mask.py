@@ -1,0 +1,128 @@
+"""Attention backward with a hard mask, through the C ABI, against the masked-backward oracle.
+
+The GPU backward takes the GPU masked forward's O and LSE, as a training step would. Masks
+at two densities in every broadcast form, rows that admit nothing, causal and not, fp32
+(bar 1e-5 of the oracle's error scale, as in test_gpu_bwd.py) and bf16 inputs (bar 2^-7 of
+it, as in test_gpu_bwd_bf16.py). An all-ones mask must reproduce the unmasked backward bit
+for bit, and the [B,S,H,d] layout must equal [B,H,S,d] on transposed data bit for bit.
+"""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+from helpers import to_device
+
+pytestmark = pytest.mark.gpu
+
+TAU = {"f32": 1e-5, "bf16": 2.0**-7}
+L2 = {"f32": 1e-5, "bf16": 2.0**-9}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import scaled_masked_attention_amd as sma
+
+    sma.library()
+
+
+def _mask(seed, shape, density, empty_rows=()):
+    m = gen.uniform24(seed, np.arange(int(np.prod(shape)), dtype=np.uint64)).reshape(shape) < density
+    for r in empty_rows:
+        m[..., r, :] = False
+    return m.astype(np.uint8)
+
+
+def _run(q, k, v, bits, g, mask, scale, causal, dtype, layout="bhsd"):
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    tq, tk, tv = to_device((q, k, v), bits, dtype)
+    tg = torch.from_numpy(np.ascontiguousarray(g)).to("cuda")
+    tm = torch.from_numpy(np.ascontiguousarray(mask)).to("cuda") if mask is not None else None
+    o, lse = sma.attention_fwd(tq, tk, tv, scale=scale, causal=causal, return_lse=True, mask=tm)
+    if layout == "bshd":
+        tq, tk, tv, o, tg = (x.transpose(1, 2).contiguous() for x in (tq, tk, tv, o, tg))
+    grads = sma.attention_bwd(tq, tk, tv, o, lse, tg, scale=scale, causal=causal, mask=tm, layout=layout)
+    torch.cuda.synchronize()
+    if layout == "bshd":
+        grads = tuple(x.transpose(1, 2) for x in grads)
+    return tuple(x.contiguous() for x in grads)
+
+
+def _check(got, ref, bound, dtype, label):
+    for name, t, b, m in zip(("dq", "dk", "dv"), got, ref, bound):
+        a = t.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(a)), f"{label}: non-finite {name}"
+        err = np.abs(a - b)
+        zero = m == 0
+        assert np.all(a[zero] == 0.0), f"{label}: {name} nonzero where every term is zero"
+        ratio = np.where(zero, 0.0, err / np.where(zero, 1.0, m))
+        assert float(ratio.max()) <= TAU[dtype], f"{label}: {name} error {float(ratio.max()):.3e} of its scale"
+        assert float(np.linalg.norm(a - b)) <= L2[dtype] * float(np.linalg.norm(m)) + 1e-5 * float(np.linalg.norm(b)), \
+            f"{label}: {name} L2 error"
+
+
+FORMS = {"shared": (1, 1), "per_head": (1, "H"), "full": ("B", "H")}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("form", list(FORMS))
+@pytest.mark.parametrize("density", [0.3, 0.9])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_masked_backward_parity(causal, d, density, form, dtype):
+    B, H, sq, skv = 2, 2, 130, 177
+    (q, k, v), bits = gen.random_case(1600 + d + int(density * 10), (B, H, sq, d), (B, H, skv, d), dtype=dtype)
+    g = gen.upstream_grad(1601 + d, (B, H, sq, d))
+    mb = B if FORMS[form][0] == "B" else 1
+    mh = H if FORMS[form][1] == "H" else 1
+    mask = _mask(1602 + causal, (mb, mh, sq, skv), density, empty_rows=(5, 6))
+    scale = 1.0 / np.sqrt(d)
+    got = _run(q, k, v, bits, g, mask, scale, causal, dtype)
+    ref = oracle.attention_bwd_masked(q, k, v, g, mask, scale, causal)
+    bound = oracle.attention_bwd_masked_bound(q, k, v, g, mask, scale, causal)
+    _check(got, ref, bound, dtype, f"{form} {density} {dtype}")
+    assert np.all(got[0].cpu().numpy()[:, :, 5:7] == 0.0)  # rows that admit nothing
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_all_ones_mask_is_bitwise_the_unmasked_backward(dtype, causal):
+    (q, k, v), bits = gen.random_case(1610, (1, 3, 200, 128), (1, 3, 230, 128), dtype=dtype)
+    g = gen.upstream_grad(1610, (1, 3, 200, 128))
+    ones = np.ones((1, 1, 200, 230), np.uint8)
+    a = _run(q, k, v, bits, g, ones, 0.09, causal, dtype)
+    b = _run(q, k, v, bits, g, None, 0.09, causal, dtype)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.cpu().numpy(), y.cpu().numpy())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_masked_backward_bshd_equals_bhsd(dtype):
+    (q, k, v), bits = gen.random_case(1620, (2, 3, 150, 64), (2, 3, 190, 64), dtype=dtype)
+    g = gen.upstream_grad(1620, (2, 3, 150, 64))
+    mask = _mask(1621, (2, 1, 150, 190), 0.5, empty_rows=(0,))
+    a = _run(q, k, v, bits, g, mask, 0.125, True, dtype)
+    b = _run(q, k, v, bits, g, mask, 0.125, True, dtype, layout="bshd")
+    for x, y in zip(a, b):
+        assert np.array_equal(x.cpu().numpy(), y.cpu().numpy())
+
+
+def test_masked_backward_binding_checks():
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    q = torch.randn(1, 2, 40, 64, device="cuda")
+    k = torch.randn(1, 2, 50, 64, device="cuda")
+    m = torch.ones(40, 50, dtype=torch.bool, device="cuda")
+    o, lse = sma.attention_fwd(q, k, k, return_lse=True, mask=m)
+    with pytest.raises(ValueError):
+        sma.attention_bwd(q, k, k, o, lse, o, mask=torch.ones(40, 51, dtype=torch.bool, device="cuda"))
+    with pytest.raises(ValueError):
+        sma.attention_bwd(q, k, k, o, lse, o, mask=torch.ones(40, 50, device="cuda"))  # float mask
