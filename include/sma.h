@@ -108,9 +108,9 @@ typedef struct sma_plan {
  *   lse        device pointer to batch*heads*seq_q floats, or NULL for no LSE output.
  *   in_dtype   SMA_DTYPE_F32, SMA_DTYPE_BF16 or SMA_DTYPE_F16 (16-bit inputs run on 16-bit
  *              MFMA with fp32 accumulation; P is rounded to the input type for P V).
- *   o_dtype    SMA_DTYPE_F32, or SMA_DTYPE_BF16: the fp32 result rounded to bf16 (nearest
- *              even) as it is stored. Either with any input type (SMA_DTYPE_F16 output ->
- *              UNSUPPORTED). LSE is always fp32.
+ *   o_dtype    SMA_DTYPE_F32, or SMA_DTYPE_BF16 / SMA_DTYPE_F16: the fp32 result rounded
+ *              to that type (nearest even; beyond fp16's range, infinity) as it is stored.
+ *              Any with any input type. LSE is always fp32.
  *   head_dim   64 or 128 with every input type; also 32 or 256 with fp32 inputs, which
  *              run on SMA_KERNEL_F32_QBLOCK only (0 -> INVALID_VALUE, other values and
  *              other kernels -> UNSUPPORTED).

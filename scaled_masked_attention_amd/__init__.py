@@ -207,8 +207,8 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
 
     q [B,H,Sq,D], k and v [B,H,Skv,D]: contiguous torch tensors on the current
     HIP device, all float32, all bfloat16 or all float16. Returns O ([B,H,Sq,D], float32, or
-    bfloat16 rounded to nearest even with out_dtype=torch.bfloat16 or an
-    ``out`` of that dtype) and, with return_lse, the per-row natural-log LSE
+    bfloat16 / float16 rounded to nearest even with out_dtype=torch.bfloat16 /
+    torch.float16 or an ``out`` of that dtype) and, with return_lse, the per-row natural-log LSE
     (float32, [B,H,Sq]).
     scale=None means 1/sqrt(D). causal uses the bottom-right alignment.
     layout="bshd" takes q [B,Sq,H,D], k and v [B,Skv,H,D] and returns O in that
@@ -257,9 +257,10 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
         scale = 1.0 / math.sqrt(D)
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else torch.float32
-    if out_dtype not in (torch.float32, torch.bfloat16):
+    if out_dtype not in (torch.float32, torch.bfloat16, torch.float16):
         raise ValueError(f"unsupported out_dtype {out_dtype}")
-    o_dt = SMA_DTYPE_F32 if out_dtype == torch.float32 else SMA_DTYPE_BF16
+    o_dt = {torch.float32: SMA_DTYPE_F32, torch.bfloat16: SMA_DTYPE_BF16,
+            torch.float16: SMA_DTYPE_F16}[out_dtype]
     if out is None:
         out = torch.empty(o_shape, dtype=out_dtype, device=dev)
     if return_lse and lse is None:

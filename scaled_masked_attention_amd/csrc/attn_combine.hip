@@ -5,7 +5,7 @@
 //   L = log2 sum_s 2^L_s,   O = sum_s 2^(L_s - L) O_s,
 // with empty splits (L_s = -inf) weighing zero and a row empty in every split
 // written as O = +0.0, LSE = -inf. HBM-bound: it reads nsplit*(d+1) floats per
-// row and writes d+1 (the output in fp32 or, rounded to nearest even, bf16),
+// row and writes d+1 (the output in fp32 or, rounded to nearest even, bf16 or fp16),
 // the output with non-temporal stores (written once, not read here again).
 #include "attn_common.h"
 
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
   const int64_t o_off = head_offset(bh, a.heads, a.os_b, a.os_h) + (row - bh * a.seq_q) * a.os_s + 4 * c4;
   if (a.o_bf16) {
     typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-    __builtin_nontemporal_store(u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])},
+    __builtin_nontemporal_store(u32x2_t{pack_out16(acc[0], acc[1], a.o_f16), pack_out16(acc[2], acc[3], a.o_f16)},
                                 reinterpret_cast<u32x2_t*>(a.o_bf16 + o_off));
   } else {
     __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(a.o + o_off));

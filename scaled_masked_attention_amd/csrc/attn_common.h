@@ -101,6 +101,16 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
   const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(unsigned, v);
 }
+// The same for fp16 (the hardware conversion under the default rounding mode, nearest even).
+__device__ __forceinline__ unsigned pack_f16x2(float lo, float hi) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(unsigned, v);
+}
+// A 16-bit output pair: fp16 when f16, else bf16.
+__device__ __forceinline__ unsigned pack_out16(float lo, float hi, bool f16) {
+  return f16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+}
 
 // A 32-row fp32 tile (of Q, K, dO or V) in LDS: row r's 16-byte chunk c is stored at chunk
 // position c ^ (r & 15) of the row. A direct-to-LDS instruction fills 1 KB of

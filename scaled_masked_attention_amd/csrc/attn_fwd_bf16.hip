@@ -1,6 +1,6 @@
 // Attention forward, 16-bit inputs: bf16 (v_mfma_f32_32x32x16_bf16) or fp16
-// (v_mfma_f32_32x32x16_f16, the F16 template flag), fp32 accumulation, fp32 or
-// bf16 output, gfx950.
+// (v_mfma_f32_32x32x16_f16, the F16 template flag), fp32 accumulation, fp32,
+// bf16 or fp16 output, gfx950.
 //
 // Same method as the fp32 kernel (oxicuda ComputeBackend `attention`; pulsatrix
 // HIPBackend `softmax_rows`, `logsumexp_rows`; TorchLean hard-masked softmax),
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
       for (int e = 0; e < 4; ++e) out[e] = empty ? 0.f : oacc[cb][4 * g4 + e] * inv;
       if (orow16)
         *reinterpret_cast<u32x2*>(orow16 + 32 * cb + 8 * g4 + 4 * lh) =
-            u32x2{pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3])};
+            u32x2{pack_out16(out[0], out[1], a.o_f16), pack_out16(out[2], out[3], a.o_f16)};
       else
         *reinterpret_cast<f32x4*>(orow + 32 * cb + 8 * g4 + 4 * lh) = out;
     }

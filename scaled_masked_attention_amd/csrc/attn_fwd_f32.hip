@@ -253,12 +253,12 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
     for (int cb = 0; cb < G::kNch; ++cb) out[cb] = empty ? 0.f : oacc[cb][r] * inv;
     if (orow16) {
       if constexpr (G::kNch == 1) {
-        orow16[m] = (unsigned short)(pack_bf16x2(out[0], 0.f) & 0xffffu);
+        orow16[m] = (unsigned short)(pack_out16(out[0], 0.f, a.o_f16) & 0xffffu);
       } else {
         typedef unsigned PackedT __attribute__((ext_vector_type(G::kNch / 2)));
         PackedT packed;
 #pragma unroll
-        for (int i = 0; i < G::kNch / 2; ++i) packed[i] = pack_bf16x2(out[2 * i], out[2 * i + 1]);
+        for (int i = 0; i < G::kNch / 2; ++i) packed[i] = pack_out16(out[2 * i], out[2 * i + 1], a.o_f16);
         *reinterpret_cast<PackedT*>(orow16 + G::kNch * m) = packed;
       }
     } else {

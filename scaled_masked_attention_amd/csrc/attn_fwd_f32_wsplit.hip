@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_wsplit_kernel(FwdArgs a) {
     const int64_t o_off = head_offset(bh, a.heads, a.qs_b, a.qs_h) + (int64_t)row * a.qs_s + 4 * c4;
     if (a.o_bf16) {
       typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-      const u32x2_t packed = {pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3])};
+      const u32x2_t packed = {pack_out16(out[0], out[1], a.o_f16), pack_out16(out[2], out[3], a.o_f16)};
       __builtin_nontemporal_store(packed, reinterpret_cast<u32x2_t*>(a.o_bf16 + o_off));
     } else {
       __builtin_nontemporal_store(out, reinterpret_cast<f32x4*>(a.o + o_off));

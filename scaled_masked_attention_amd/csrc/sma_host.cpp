@@ -68,7 +68,6 @@ int check_shape(int in_dtype, int o_dtype, size_t batch, size_t heads, size_t se
   // query-block kernel only (fp32 inputs).
   if (d != 64 && d != 128 && !(in_dtype == SMA_DTYPE_F32 && (d == 32 || d == 256)))
     return SMA_ERR_UNSUPPORTED;
-  if (o_dtype == SMA_DTYPE_F16) return SMA_ERR_UNSUPPORTED;
   if (seq_q > kMaxSeq || seq_kv > kMaxSeq || s.bh > (size_t(1) << 31)) return SMA_ERR_UNSUPPORTED;
   if (heads > (size_t(1) << 20)) return SMA_ERR_UNSUPPORTED;
   s.row_elems = layout == SMA_LAYOUT_BSHD ? heads * d : d;
@@ -355,7 +354,8 @@ int fwd_core(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.kvs_h = (int64_t)(seq_kv * head_dim);
     a.qs_s = a.kvs_s = (int64_t)head_dim;
   }
-  const bool o16 = o_dtype == SMA_DTYPE_BF16;
+  const bool o16 = o_dtype != SMA_DTYPE_F32;
+  a.o_f16 = o_dtype == SMA_DTYPE_F16 ? 1 : 0;
   if (p.nsplit == 1) {
     if (o16) a.o_bf16 = static_cast<unsigned short*>(o);
     else a.o = static_cast<float*>(o);
@@ -400,6 +400,7 @@ int fwd_core(const void* q, const void* k, const void* v, void* o, float* lse, i
     ca.part_lse = a.part_lse;
     if (o16) ca.o_bf16 = static_cast<unsigned short*>(o);
     else ca.o = static_cast<float*>(o);
+    ca.o_f16 = a.o_f16;
     ca.lse = lse;
     ca.rows = (int64_t)sh.rows;
     ca.nsplit = p.nsplit;

@@ -13,7 +13,8 @@ struct FwdArgs {
   const void* k;     // [bh][seq_kv][d]
   const void* v;     // [bh][seq_kv][d]
   float* o;          // nsplit == 1: final O [bh][seq_q][d] fp32 (when o_bf16 is null)
-  unsigned short* o_bf16;  // nsplit == 1: final O as bf16 (round to nearest even), or null
+  unsigned short* o_bf16;  // nsplit == 1: final O as 16 bits (round to nearest even), or null
+  int32_t o_f16;           // the 16-bit O is fp16 (else bf16)
   float* lse;        // nsplit == 1: final LSE [bh][seq_q] (natural log), may be null
   float* part_o;     // nsplit > 1: per-split normalised O [nsplit][bh][seq_q][d]
   float* part_lse;   // nsplit > 1: per-split LSE in log2 units [nsplit][bh][seq_q]
@@ -55,7 +56,8 @@ struct CombineArgs {
   const float* part_o;   // [nsplit][rows][d]
   const float* part_lse; // [nsplit][rows], log2 units
   float* o;              // [rows][d] fp32 (when o_bf16 is null)
-  unsigned short* o_bf16; // [rows][d] bf16, or null
+  unsigned short* o_bf16; // [rows][d] as 16 bits (bf16, or fp16 when o_f16), or null
+  int32_t o_f16;
   float* lse;            // [rows] natural log, may be null
   int64_t rows;          // bh * seq_q
   int32_t nsplit;

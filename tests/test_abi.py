@@ -81,7 +81,7 @@ def test_unsupported():
     for d in (32, 256):  # head dims the 16-bit kernel is not built for
         assert _v(idt=BF16, d=d) == UNSUP and _v(idt=F16, odt=BF16, d=d) == UNSUP
     assert _v(odt=BF16, idt=BF16, d=96) == UNSUP
-    assert _v(odt=F16) == UNSUP and _v(odt=F16, idt=F16) == UNSUP  # fp16 output not built
+    assert _v(odt=F16) == OK and _v(odt=F16, idt=F16) == OK and _v(odt=F16, idt=BF16) == OK
     assert _v(idt=F16, d=128, skv=1 << 23) == UNSUP
     assert _v(sq=(1 << 30) + 1) == UNSUP
     assert _v(idt=BF16, d=128, skv=(1 << 23) - 256) == OK  # K/V of one head just under 2 GiB

@@ -1,10 +1,12 @@
-"""bf16 output of the attention forward, on every kernel and plan, through the C ABI.
+"""16-bit output (bf16 and fp16) of the attention forward, on every kernel and plan, through
+the C ABI.
 
-The bf16 O must be the fp32 O of the same plan rounded to nearest even, bit for
-bit (both sides take the rounding decision from the same fp32 value), and it
-must sit within the input dtype's parity bar of the oracle plus the rounding
-itself: |O16 - O_ref| <= bar + 2^-8 |O| elementwise (half a bf16 ulp is at most
-2^-8 of the value). Rows without keys are +0.0 exactly.
+The 16-bit O must be the fp32 O of the same plan rounded to nearest even, bit for bit (both
+sides take the rounding decision from the same fp32 value; numpy's float32 -> float16
+conversion, pinned by textbook encodings in test_gen.py, rounds to nearest even), and it
+must sit within the input dtype's parity bar of the oracle plus the rounding itself:
+|O16 - O_ref| <= bar + u |O| elementwise, u = 2^-8 for bf16 and 2^-11 for fp16 (half an
+ulp), plus 2^-25 for fp16's subnormal spacing. Rows without keys are +0.0 exactly.
 """
 import math
 
@@ -96,3 +98,52 @@ def test_bf16_output_with_no_keys_is_positive_zero():
     o, lse = sma.attention_fwd(q, k, k, causal=False, return_lse=True, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert np.all(_bits(o) == 0) and torch.isneginf(lse).all()
+
+
+@pytest.mark.parametrize("plan", list(PLANS))
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 3, 200, 200), (1, 4, 257, 1025)], ids=lambda s: "x".join(map(str, s)))
+def test_f16_output_is_the_rounded_fp32_output(shape, causal, d, dtype, plan):
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    kw = _plan_kwargs(plan, dtype)
+    B, H, sq, skv = shape
+    (q, k, v), bits = gen.random_case(720 + sq + 3 * skv + d, (B, H, sq, d), (B, H, skv, d),
+                                      sigma_qk=1.0 if dtype == "f32" else 3.0, dtype=dtype)
+    tq, tk, tv = to_device((q, k, v), bits, dtype)
+    scale = 1.0 / math.sqrt(d)
+    o32, l32 = sma.attention_fwd(tq, tk, tv, scale=scale, causal=causal, return_lse=True, **kw)
+    o16, l16 = sma.attention_fwd(tq, tk, tv, scale=scale, causal=causal, return_lse=True,
+                                 out_dtype=torch.float16, **kw)
+    torch.cuda.synchronize()
+    assert o16.dtype == torch.float16
+    f32 = o32.cpu().numpy()
+    assert np.array_equal(_bits(o16), f32.astype(np.float16).view(np.uint16)), "fp16 O is not RNE of the fp32 O"
+    assert torch.equal(l16, l32), "LSE changed with the output dtype"
+    o_ref, _ = oracle.attention_fwd(q, k, v, scale, causal)
+    got = o16.float().cpu().numpy().astype(np.float64)
+    bar = ({"f32": F32_MAX_ABS, "bf16": BF16_MAX_ABS, "f16": F16_MAX_ABS}[dtype]
+           + 2.0 ** -11 * np.abs(f32.astype(np.float64)) + 2.0 ** -25)
+    assert np.all(np.abs(got - o_ref) <= bar)
+    er = empty_rows(sq, skv, causal)
+    if er.any():
+        assert np.all(_bits(o16)[:, :, er] == 0)
+
+
+def test_f16_output_with_a_mask_and_bshd_layout():
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    (q, k, v), _ = gen.random_case(740, (2, 3, 100, 64), (2, 3, 150, 64))
+    m = torch.from_numpy((gen.uniform24(741, np.arange(100 * 150, dtype=np.uint64)) < 0.4).reshape(100, 150)).to("cuda")
+    tq, tk, tv = (torch.from_numpy(x).to("cuda").transpose(1, 2).contiguous() for x in (q, k, v))
+    o32 = sma.attention_fwd(tq, tk, tv, scale=0.125, causal=True, mask=m, layout="bshd")
+    o16 = sma.attention_fwd(tq, tk, tv, scale=0.125, causal=True, mask=m, layout="bshd", out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(o16), o32.cpu().numpy().astype(np.float16).view(np.uint16))
+
