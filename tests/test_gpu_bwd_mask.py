@@ -4,7 +4,8 @@ The GPU backward takes the GPU masked forward's O and LSE, as a training step wo
 at two densities in every broadcast form, rows that admit nothing, causal and not, fp32
 (bar 1e-5 of the oracle's error scale, as in test_gpu_bwd.py) and bf16 inputs (bar 2^-7 of
 it, as in test_gpu_bwd_bf16.py). An all-ones mask must reproduce the unmasked backward bit
-for bit, and the [B,S,H,d] layout must equal [B,H,S,d] on transposed data bit for bit.
+for bit, the [B,S,H,d] layout must equal [B,H,S,d] on transposed data bit for bit, and HIP-graph
+replays of the backward must equal the eager call bit for bit.
 """
 import numpy as np
 import pytest
@@ -126,3 +127,45 @@ def test_masked_backward_binding_checks():
         sma.attention_bwd(q, k, k, o, lse, o, mask=torch.ones(40, 51, dtype=torch.bool, device="cuda"))
     with pytest.raises(ValueError):
         sma.attention_bwd(q, k, k, o, lse, o, mask=torch.ones(40, 50, device="cuda"))  # float mask
+
+
+@pytest.mark.parametrize("masked", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_hip_graph_replays_match_eager(dtype, masked):
+    """The backward (with its mask packing when masked) captured in a HIP graph through torch,
+    replayed several times with eager work and synchronizations between replays and the
+    gradients refilled with NaN before each: every replay equals the eager result bitwise."""
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    (q, k, v), bits = gen.random_case(1630, (2, 2, 180, 64), (2, 2, 210, 64), dtype=dtype)
+    g = gen.upstream_grad(1630, (2, 2, 180, 64))
+    tq, tk, tv = to_device((q, k, v), bits, dtype)
+    tg = torch.from_numpy(g).to("cuda")
+    tm = torch.from_numpy(_mask(1631, (1, 2, 180, 210), 0.6, empty_rows=(3,))).to("cuda") if masked else None
+    o, lse = sma.attention_fwd(tq, tk, tv, scale=0.12, causal=True, return_lse=True, mask=tm)
+    in_dt = sma.SMA_DTYPE_F32 if dtype == "f32" else sma.SMA_DTYPE_BF16
+    if masked:
+        n = sma.library().sma_attention_bwd_masked_workspace_bytes(in_dt, 2, 2, 180, 210, 64, 1, 0, 1, 2)
+    else:
+        n = sma.attention_bwd_workspace_bytes(in_dt, 2, 2, 180, 210, 64, True)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    eager = sma.attention_bwd(tq, tk, tv, o, lse, tg, scale=0.12, causal=True, mask=tm, workspace=ws)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in eager]
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            grads = sma.attention_bwd(tq, tk, tv, o, lse, tg, scale=0.12, causal=True, mask=tm, workspace=ws,
+                                      stream=torch.cuda.current_stream())
+    for rep in range(4):
+        for t in grads:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), grads, eager):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs"
+        _ = (tg * 2).sum().item()  # eager work between replays
