@@ -40,6 +40,9 @@ SHAPES = [  # (B, H, sq, skv): several tiles with ragged tails, cross shapes bot
 # Forced plans: every kernel, unsplit and split across workgroups, on the same inputs.
 PLANS = {"auto": None, "qblock": ("qblock", 1), "split3": ("qblock", 3), "ksplit": ("ksplit", 1)}
 
+# The in-workgroup key-split kernel is fp32 only: it is paired with fp32 inputs alone.
+DTYPE_PLANS = [(dt, pl) for dt in ("f32", "bf16", "f16") for pl in PLANS if dt == "f32" or pl != "ksplit"]
+
 
 def plan_kwargs(plan, dtype):
     import scaled_masked_attention_amd as sma
@@ -48,8 +51,7 @@ def plan_kwargs(plan, dtype):
         return {}
     kind, nsplit = PLANS[plan]
     if kind == "ksplit":
-        if dtype != "f32":
-            pytest.skip("the in-workgroup key-split kernel is fp32 only")
+        assert dtype == "f32", "the in-workgroup key-split kernel is fp32 only"
         return dict(kernel=sma.SMA_KERNEL_F32_KSPLIT, nsplit=1)
     kern = sma.SMA_KERNEL_F32_QBLOCK if dtype == "f32" else sma.SMA_KERNEL_BF16_QBLOCK
     return dict(kernel=kern, nsplit=nsplit)
@@ -65,8 +67,7 @@ def _small_case(shape, causal, d, dtype):
     return (q, k, v), bits, scale, o_ref, lse_ref
 
 
-@pytest.mark.parametrize("plan", list(PLANS))
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("dtype,plan", DTYPE_PLANS)
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
