@@ -196,13 +196,13 @@ BWD_PREFIX = "bwd_"
 def gen_workloads():
     import gen
 
-    bwd = [BWD_PREFIX + n for n, w in gen.WORKLOADS.items() if w.dtype in ("f32", "bf16") and w.head_dim in (64, 128)]
+    bwd = [BWD_PREFIX + n for n, w in gen.WORKLOADS.items() if w.head_dim in (64, 128)]
     return list(gen.WORKLOADS) + bwd + list(gen.ROW_WORKLOADS)
 
 
 def dkdv_min_bytes(w) -> int:
-    """The dK/dV kernel reads Q, dO, K, V (in the input type; dO as the bf16 copy for bf16
-    inputs) and each row's lse2 and D once, and writes dK, dV (fp32)."""
+    """The dK/dV kernel reads Q, dO, K, V (in the input type; dO as the 16-bit copy for
+    16-bit inputs) and each row's lse2 and D once, and writes dK, dV (fp32)."""
     bh = w.batch * w.heads
     e = 4 if w.dtype == "f32" else 2
     return bh * ((2 * w.seq_q + 2 * w.seq_kv) * w.head_dim * e + 2 * w.seq_kv * w.head_dim * 4 + 8 * w.seq_q)
@@ -302,7 +302,7 @@ def bench_bwd(args, w, name):
     g = gen.upstream_grad(w.seed, w.q_shape)
     tq, tk, tv = to_device_inputs(vals, bits, w.dtype)
     tg = torch.from_numpy(np.ascontiguousarray(g)).to("cuda")
-    in_dt = sma.SMA_DTYPE_F32 if w.dtype == "f32" else sma.SMA_DTYPE_BF16
+    in_dt = {"f32": sma.SMA_DTYPE_F32, "bf16": sma.SMA_DTYPE_BF16, "f16": sma.SMA_DTYPE_F16}[w.dtype]
     B, H, sq, skv, d = w.batch, w.heads, w.seq_q, w.seq_kv, w.head_dim
     o, lse = sma.attention_fwd(tq, tk, tv, scale=w.scale, causal=w.causal, return_lse=True)
     dq, dk, dv = (torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in (tq, tk, tv))
@@ -351,7 +351,7 @@ def bench_bwd(args, w, name):
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": f"{kname}<{d},{str(w.causal).lower()}>",
+                     "kernel": f"{kname}<{d},{str(w.causal).lower()}" + (",f16>" if w.dtype == "f16" else ">"),
                      "kernel_avg_ms": round(k_avg, 5),
                      "kernel_timing": "HIP events recorded by the library around each dK/dV launch",
                      "flops_per_launch": kernel_flops,

@@ -55,7 +55,7 @@ extern "C" {
 typedef enum {
   SMA_DTYPE_F32 = 0,  /* IEEE binary32 */
   SMA_DTYPE_BF16 = 1, /* bfloat16 (binary32 with the low 16 fraction bits dropped) */
-  SMA_DTYPE_F16 = 2   /* IEEE binary16 (inputs of the forward only) */
+  SMA_DTYPE_F16 = 2   /* IEEE binary16 */
 } sma_dtype;
 
 typedef enum {
@@ -257,11 +257,14 @@ size_t sma_attention_fwd_masked_workspace_bytes(int in_dtype, size_t batch, size
  *
  *   q, o, dout, dq   [B,H,Sq,d];  k, v, dk, dv  [B,H,Skv,d];  lse [B,H,Sq].
  *   in_dtype         element type of q, k and v: SMA_DTYPE_F32 (fp32 MFMA), or
- *                    SMA_DTYPE_BF16 (16-bit MFMA with fp32 accumulation, under the
- *                    forward's mixed-precision contract: dout is rounded once to bf16
- *                    for the products, and P and dS are rounded to bf16 for the
- *                    products that take them; D = dout . o stays fp32);
- *                    SMA_DTYPE_F16 -> UNSUPPORTED. o, dout, lse and the three
+ *                    SMA_DTYPE_BF16 or SMA_DTYPE_F16 (16-bit MFMA with fp32
+ *                    accumulation, under the forward's mixed-precision contract:
+ *                    dout is rounded once to the input type for the products, and
+ *                    P and dS are rounded to it for the products that take them;
+ *                    D = dout . o stays fp32). fp16 is not rescaled: the caller keeps
+ *                    dout, and with it dS = P (dout . v - D), inside fp16's range
+ *                    (beyond 65504 the results are not finite; under 2^-14 bits are
+ *                    lost), as loss scaling does. o, dout, lse and the three
  *                    gradients are always fp32 (o as sma_attention_fwd returns it).
  *   head_dim         64 or 128 (others -> UNSUPPORTED).
  *   scale, causal, stream   as for sma_attention_fwd.
@@ -324,8 +327,8 @@ size_t sma_attention_bwd_masked_workspace_bytes(int in_dtype, size_t batch, size
                                                 size_t mask_heads);
 
 /* Workspace bytes sma_attention_bwd needs for this shape: 256 per 32-row query
- * block of every (batch, head), rounded up to 256; with SMA_DTYPE_BF16 also
- * batch*heads*seq_q*head_dim*2 bytes (dout as bf16), rounded up to 256. 0 for
+ * block of every (batch, head), rounded up to 256; with 16-bit inputs also
+ * batch*heads*seq_q*head_dim*2 bytes (dout in 16 bits), rounded up to 256. 0 for
  * invalid arguments. */
 size_t sma_attention_bwd_workspace_bytes(int in_dtype, size_t batch, size_t heads, size_t seq_q,
                                          size_t seq_kv, size_t head_dim, int causal);

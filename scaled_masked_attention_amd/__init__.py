@@ -334,7 +334,8 @@ def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=Non
     """(dQ, dK, dV) of O = softmax(scale * Q K^T + mask) V for the upstream gradient dout.
 
     q, o, dout [B,H,Sq,D] and k, v [B,H,Skv,D] contiguous tensors on the current
-    HIP device: q, k, v all float32 or all bfloat16 (then on 16-bit MFMA), o, dout
+    HIP device: q, k, v all float32, all bfloat16 or all float16 (then on 16-bit MFMA;
+    float16 is not rescaled, so dout must keep dS inside its range), o, dout
     and lse ([B,H,Sq]) float32, o and lse as attention_fwd returned them for the
     same q, k, v, scale and causal. layout="bshd" takes q, o, dout [B,Sq,H,D] and
     k, v [B,Skv,H,D] (lse stays [B,H,Sq]). mask: the hard mask attention_fwd was
@@ -363,9 +364,10 @@ def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=Non
             tuple(dout.shape) != q_shape or tuple(lse.shape) != (B, H, Sq)):
         raise ValueError("shape mismatch among q, k, v, o, lse, dout")
     dev = torch.device("cuda", torch.cuda.current_device())
-    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float32, torch.bfloat16):
-        raise ValueError("q, k, v must be all float32 or all bfloat16")
-    in_dt = SMA_DTYPE_F32 if q.dtype == torch.float32 else SMA_DTYPE_BF16
+    dts = {torch.float32: SMA_DTYPE_F32, torch.bfloat16: SMA_DTYPE_BF16, torch.float16: SMA_DTYPE_F16}
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in dts:
+        raise ValueError("q, k, v must be all float32, all bfloat16 or all float16")
+    in_dt = dts[q.dtype]
     for name, t in ts.items():
         if name in ("o", "lse", "dout") and t.dtype != torch.float32:
             raise ValueError(f"{name} must be float32")

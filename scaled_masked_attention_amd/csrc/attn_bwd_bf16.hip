@@ -1,5 +1,5 @@
-// Attention backward with bf16 Q, K, V on 16-bit MFMA (v_mfma_f32_32x32x16_bf16, fp32
-// accumulation): dQ, dK and dV (fp32) of O = softmax(scale * Q K^T + causal mask) V, from
+// Attention backward with bf16 or fp16 Q, K, V on 16-bit MFMA (v_mfma_f32_32x32x16_bf16,
+// or _f16 under the F16 template flag; fp32 accumulation): dQ, dK and dV (fp32) of O = softmax(scale * Q K^T + causal mask) V, from
 // the forward's fp32 O and log-sum-exp and an fp32 upstream gradient dO (oxicuda
 // ComputeBackend `attention` for the forward; the softmax vector-Jacobian product of
 // pulsatrix HIPBackend `softmax_rows_backward` and of MicroGPT's fused attention-softmax
@@ -9,9 +9,13 @@
 // The arithmetic and the three launches are those of the fp32 backward:
 //   P_ij = 2^(c s_ij - lse2_i), D_i = dO_i . O_i, dP_ij = dO_i . v_j, dS_ij = P_ij (dP_ij - D_i),
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j,
-// with three roundings to bf16 (nearest even) for the products: dO once, in the
-// preprocess (D stays the fp32 dot product of the fp32 dO and O); P for dV; dS for dK
-// and dQ. P and dS themselves are formed in fp32 from fp32 scores.
+// with three roundings to the input type (nearest even) for the products: dO once, in
+// the preprocess (D stays the fp32 dot product of the fp32 dO and O); P for dV; dS for dK
+// and dQ. P and dS themselves are formed in fp32 from fp32 scores. fp16 is rounded the
+// same way, with no rescaling: values past its range become infinite and those under its
+// normal range lose bits, so the caller keeps dO (and with it dS) inside that range, as
+// with loss scaling. The 16-bit registers below are typed bf16 and hold raw bits either
+// way; only the MFMA and the roundings read them as numbers.
 //
 // MFMA layouts (lane = 32*h + m; accumulator register r of lane (n, h) holds row
 // 8*(r/4) + 4*h + r%4 of output column n):
@@ -36,6 +40,7 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -60,8 +65,22 @@ struct HGeom {
   static_assert(kBwdMetaFloats == 64, "one 4-byte direct-to-LDS load per block's lse2 and D");
 };
 
+template <bool F16>
 __device__ __forceinline__ f32x16 mfma16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// x rounded to nearest even in the input type, as the raw bits of one 16-bit lane.
+template <bool F16>
+__device__ __forceinline__ __bf16 round16(float x) {
+  if constexpr (F16)
+    return __builtin_bit_cast(__bf16, (_Float16)x);
+  else
+    return (__bf16)x;
 }
 
 // Original row held in accumulator register r of half h under the row permutation.
@@ -125,8 +144,8 @@ __device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, int lane
 
 // Per 32-row query block: lse2 = LSE log2(e) (+inf for a row without admitted keys or past
 // the end, which makes its P exactly 0) and D = dO . O in fp32, as 64 floats of meta; and
-// dO rounded to bf16 into the workspace copy the products read.
-template <int D>
+// dO rounded to the input type into the workspace copy the products read.
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(BwdArgs a) {
   constexpr int kT = D / 4;  // threads per row, 4 head dims each
   constexpr int kRowsPerPass = 256 / kT;
@@ -148,7 +167,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(BwdArgs a) {
       const f32x4 o = *reinterpret_cast<const f32x4*>(a.o + off);
       d = g[0] * o[0] + g[1] * o[1] + g[2] * o[2] + g[3] * o[3];
       const size_t off16 = ((size_t)bh * a.seq_q + row) * D + 4 * c4;  // the copy is [bh][seq_q][d]
-      *reinterpret_cast<u32x2*>(a.dout16 + off16) = u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+      *reinterpret_cast<u32x2*>(a.dout16 + off16) = u32x2{pack_out16(g[0], g[1], F16), pack_out16(g[2], g[3], F16)};
     }
 #pragma unroll
     for (int w = kT / 2; w >= 1; w >>= 1) d += __shfl_xor(d, w);
@@ -184,7 +203,7 @@ __device__ __forceinline__ void store_partial(float* part, int wave, int lm, int
 // A workgroup owns 32 keys; K and V stay in registers as the B operands of S = Q K^T and
 // dP = dO V^T. Its 4 waves split the query blocks that admit any of the keys; each
 // streams its Q and dO tiles (permuted) and the block's lse2/D into private LDS slots.
-template <int D, bool CAUSAL, bool MASKED>
+template <int D, bool CAUSAL, bool MASKED, bool F16>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   using G = HGeom<D>;
   // Q tile, dO tile, lse2/D, and with a hard mask the block's 32 mask words (this key block's
@@ -309,10 +328,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dp[r] = s[r] = 0.f;
 #pragma unroll
-    for (int st = 0; st < G::kSteps; ++st) dp = mfma16(row_chunk<D>(g_slot, lm, 2 * st + lh), vr[st], dp);
+    for (int st = 0; st < G::kSteps; ++st) dp = mfma16<F16>(row_chunk<D>(g_slot, lm, 2 * st + lh), vr[st], dp);
     wait_vmcnt<0>();  // the Q tile
 #pragma unroll
-    for (int st = 0; st < G::kSteps; ++st) s = mfma16(row_chunk<D>(q_slot, lm, 2 * st + lh), kr[st], s);
+    for (int st = 0; st < G::kSteps; ++st) s = mfma16<F16>(row_chunk<D>(q_slot, lm, 2 * st + lh), kr[st], s);
     // Some pair of this block is masked iff its last key lies past its first row's limit.
     const bool diag = CAUSAL && (j0 + G::kRows - 1 > i0 + delta);
     uint32_t mw[16];  // mask word of query row perm_acc_row(r, lh); bit lm is this lane's key
@@ -332,14 +351,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
       if (MASKED) t = ((mw[r] >> lm) & 1u) ? t : -INFINITY;
       const float p = __builtin_amdgcn_exp2f(t);
       const float ds = p * (dp[r] - dd[r / 4][r % 4]);
-      pp[r / 8][r % 8] = (__bf16)p;
-      pds[r / 8][r % 8] = (__bf16)ds;
+      pp[r / 8][r % 8] = round16<F16>(p);
+      pds[r / 8][r % 8] = round16<F16>(ds);
     }
     // dV^T += dO^T P
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int cb = 0; cb < G::kNch; ++cb) dv[cb] = mfma16(tr_operand<D>(g_slot, lane, t2, cb), pp[t2], dv[cb]);
+      for (int cb = 0; cb < G::kNch; ++cb) dv[cb] = mfma16<F16>(tr_operand<D>(g_slot, lane, t2, cb), pp[t2], dv[cb]);
     if (qb + 1 < b_end) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading the dO and lse2/D slots
       copy_g(qb + 1);
@@ -348,7 +367,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int cb = 0; cb < G::kNch; ++cb) dk[cb] = mfma16(tr_operand<D>(q_slot, lane, t2, cb), pds[t2], dk[cb]);
+      for (int cb = 0; cb < G::kNch; ++cb) dk[cb] = mfma16<F16>(tr_operand<D>(q_slot, lane, t2, cb), pds[t2], dk[cb]);
     if (qb + 1 < b_end) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading the Q slot
       copy_q(qb + 1);
@@ -394,7 +413,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
 // A workgroup owns 32 queries; Q and dO stay in registers as the B operands of
 // S^T = K Q^T and dP^T = V dO^T. Its 4 waves split the key blocks the rows admit; each
 // streams its K and V tiles (permuted) into private LDS slots.
-template <int D, bool CAUSAL, bool MASKED>
+template <int D, bool CAUSAL, bool MASKED, bool F16>
 __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   using G = HGeom<D>;
   // K tile, V tile, and with a hard mask each query row's word of the key block.
@@ -501,7 +520,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dp[r] = s[r] = 0.f;
 #pragma unroll
-    for (int st = 0; st < G::kSteps; ++st) dp = mfma16(row_chunk<D>(v_slot, lm, 2 * st + lh), gr[st], dp);
+    for (int st = 0; st < G::kSteps; ++st) dp = mfma16<F16>(row_chunk<D>(v_slot, lm, 2 * st + lh), gr[st], dp);
     if (b + 1 < b_end) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading the V slot
       copy_v(b + 1);
@@ -510,7 +529,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
       wait_vmcnt<0>();
     }
 #pragma unroll
-    for (int st = 0; st < G::kSteps; ++st) s = mfma16(row_chunk<D>(k_slot, lm, 2 * st + lh), qr[st], s);
+    for (int st = 0; st < G::kSteps; ++st) s = mfma16<F16>(row_chunk<D>(k_slot, lm, 2 * st + lh), qr[st], s);
     const bool edge = j0 + G::kRows > lo;  // some key of the block lies past the first row's limit
     const uint32_t mw = MASKED ? *reinterpret_cast<const uint32_t*>(w_slot + 4 * lm) : ~0u;
     bf16x8 pds[2];
@@ -520,13 +539,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
       if (edge) t = (j0 + perm_acc_row(r, lh) < lim) ? t : -INFINITY;
       if (MASKED) t = ((mw >> perm_acc_row(r, lh)) & 1u) ? t : -INFINITY;
       const float p = __builtin_amdgcn_exp2f(t);
-      pds[r / 8][r % 8] = (__bf16)(p * (dp[r] - my_d));
+      pds[r / 8][r % 8] = round16<F16>(p * (dp[r] - my_d));
     }
     // dQ^T += K^T dS^T
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int cb = 0; cb < G::kNch; ++cb) dq[cb] = mfma16(tr_operand<D>(k_slot, lane, t2, cb), pds[t2], dq[cb]);
+      for (int cb = 0; cb < G::kNch; ++cb) dq[cb] = mfma16<F16>(tr_operand<D>(k_slot, lane, t2, cb), pds[t2], dq[cb]);
     if (b + 1 < b_end) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading the K slot
       copy_k(b + 1);
@@ -558,46 +577,50 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, bool MASKED>
+template <int D, bool CAUSAL, bool MASKED, bool F16>
 hipError_t launch_bwd_bf16_variant(const BwdArgs& a0, hipStream_t s, hipEvent_t ev_pre,
                                    hipEvent_t ev_dkdv) {
   BwdArgs a = a0;
   const uint32_t nq = (uint32_t)(a.bh * a.nqb), nk = (uint32_t)(a.bh * a.nkb);
   if (nq > 0) {
-    hipLaunchKernelGGL((attn_bwd_pre_bf16_kernel<D>), dim3(nq), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_bwd_pre_bf16_kernel<D, F16>), dim3(nq), dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   if (ev_pre && hipEventRecord(ev_pre, s) != hipSuccess) return hipErrorInvalidValue;
   if (nk > 0) {
     a.nwg = nk;
-    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, CAUSAL, MASKED>), dim3(nk), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, CAUSAL, MASKED, F16>), dim3(nk), dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   if (ev_dkdv && hipEventRecord(ev_dkdv, s) != hipSuccess) return hipErrorInvalidValue;
   if (nq > 0) {
     a.nwg = nq;
-    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, CAUSAL, MASKED>), dim3(nq), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, CAUSAL, MASKED, F16>), dim3(nq), dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   return hipSuccess;
 }
 
-template <int D>
+template <int D, bool F16>
 hipError_t launch_bwd_bf16_d(const BwdArgs& a, bool causal, hipStream_t s, hipEvent_t ev_pre,
                              hipEvent_t ev_dkdv) {
   if (a.mask_bits)
-    return causal ? launch_bwd_bf16_variant<D, true, true>(a, s, ev_pre, ev_dkdv)
-                  : launch_bwd_bf16_variant<D, false, true>(a, s, ev_pre, ev_dkdv);
-  return causal ? launch_bwd_bf16_variant<D, true, false>(a, s, ev_pre, ev_dkdv)
-                : launch_bwd_bf16_variant<D, false, false>(a, s, ev_pre, ev_dkdv);
+    return causal ? launch_bwd_bf16_variant<D, true, true, F16>(a, s, ev_pre, ev_dkdv)
+                  : launch_bwd_bf16_variant<D, false, true, F16>(a, s, ev_pre, ev_dkdv);
+  return causal ? launch_bwd_bf16_variant<D, true, false, F16>(a, s, ev_pre, ev_dkdv)
+                : launch_bwd_bf16_variant<D, false, false, F16>(a, s, ev_pre, ev_dkdv);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, bool causal, hipStream_t s,
                            hipEvent_t ev_pre, hipEvent_t ev_dkdv) {
-  if (head_dim == 64) return launch_bwd_bf16_d<64>(a, causal, s, ev_pre, ev_dkdv);
-  if (head_dim == 128) return launch_bwd_bf16_d<128>(a, causal, s, ev_pre, ev_dkdv);
+  if (head_dim == 64)
+    return a.in_f16 ? launch_bwd_bf16_d<64, true>(a, causal, s, ev_pre, ev_dkdv)
+                    : launch_bwd_bf16_d<64, false>(a, causal, s, ev_pre, ev_dkdv);
+  if (head_dim == 128)
+    return a.in_f16 ? launch_bwd_bf16_d<128, true>(a, causal, s, ev_pre, ev_dkdv)
+                    : launch_bwd_bf16_d<128, false>(a, causal, s, ev_pre, ev_dkdv);
   return hipErrorInvalidValue;
 }
 

@@ -559,10 +559,8 @@ int check_bwd_shape(int in_dtype, size_t batch, size_t heads, size_t seq_q, size
                     size_t d, double scale, BwdShape* b, int layout = SMA_LAYOUT_BHSD) {
   int st = check_shape(in_dtype, SMA_DTYPE_F32, batch, heads, seq_q, seq_kv, d, scale, &b->s, layout);
   if (st != SMA_OK) return st;
-  // fp32, or bf16 Q, K, V; fp16 (whose narrow exponent range dS would need rescaling for)
-  // is not built.
-  if ((in_dtype != SMA_DTYPE_F32 && in_dtype != SMA_DTYPE_BF16) || (d != 64 && d != 128))
-    return SMA_ERR_UNSUPPORTED;
+  // fp32, bf16 or fp16 Q, K, V.
+  if (d != 64 && d != 128) return SMA_ERR_UNSUPPORTED;
   // The kernels address one (batch, head) through 32-bit buffer offsets: rows of
   // row_elems elements (heads*d under [B,S,H,d]), with a block of slack.
   const size_t blk = sma::kBwdRowsPerBlock;
@@ -580,7 +578,7 @@ int check_bwd_shape(int in_dtype, size_t batch, size_t heads, size_t seq_q, size
     return SMA_ERR_INVALID_VALUE;
   b->ws_bytes = round_up(b->ws_bytes, kWsAlign);
   b->meta_bytes = b->ws_bytes;
-  if (in_dtype == SMA_DTYPE_BF16) b->ws_bytes += round_up(b->q32 / 2, kWsAlign);  // dO as bf16
+  if (in_dtype != SMA_DTYPE_F32) b->ws_bytes += round_up(b->q32 / 2, kWsAlign);  // dO in 16 bits
   if (b->s.bh * b->nqb > kMaxWorkgroups || b->s.bh * b->nkb > kMaxWorkgroups) return SMA_ERR_UNSUPPORTED;
   return SMA_OK;
 }
@@ -680,7 +678,8 @@ int bwd_core(const void* q, const void* k, const void* v, const void* o, const f
   a.dk = dk;
   a.dv = dv;
   a.meta = static_cast<float*>(workspace);
-  if (in_dtype == SMA_DTYPE_BF16) {
+  if (in_dtype != SMA_DTYPE_F32) {
+    a.in_f16 = in_dtype == SMA_DTYPE_F16 ? 1 : 0;
     a.q16 = static_cast<const unsigned short*>(q);
     a.k16 = static_cast<const unsigned short*>(k);
     a.v16 = static_cast<const unsigned short*>(v);
@@ -722,7 +721,7 @@ int bwd_core(const void* q, const void* k, const void* v, const void* o, const f
     a.mbits_sh = mask.heads == heads && heads > 1 ? slab : 0;
     a.mbits_sb = mask.batches == batch && batch > 1 ? (int64_t)mask.heads * slab : 0;
   }
-  const auto launch = in_dtype == SMA_DTYPE_BF16 ? sma::launch_bwd_bf16 : sma::launch_bwd_f32;
+  const auto launch = in_dtype != SMA_DTYPE_F32 ? sma::launch_bwd_bf16 : sma::launch_bwd_f32;
   hipError_t e = launch(a, (int)head_dim, causal != 0, hs, static_cast<hipEvent_t>(event_after_pre),
                         static_cast<hipEvent_t>(event_after_dkdv));
   return e == hipSuccess ? SMA_OK : SMA_ERR_HIP;

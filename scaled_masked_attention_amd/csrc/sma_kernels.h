@@ -79,12 +79,13 @@ struct BwdArgs {
   float* dk;          // K's layout
   float* dv;          // K's layout
   float* meta;        // workspace [bh][nqb][64]: per 32-row query block, lse2 then D
-  // bf16 inputs (the bf16 backward): q, k, v as bf16, and the workspace copy of dO
-  // rounded to bf16 ([bh][seq_q][d]); o and dout stay fp32.
+  // 16-bit inputs (the 16-bit backward): q, k, v as bf16, or fp16 when in_f16, and the
+  // workspace copy of dO rounded to that type ([bh][seq_q][d]); o and dout stay fp32.
   const unsigned short* q16;
   const unsigned short* k16;
   const unsigned short* v16;
   unsigned short* dout16;
+  int32_t in_f16;
   int64_t bh;
   int32_t seq_q;
   int32_t seq_kv;
@@ -153,6 +154,7 @@ constexpr int kBwdRowsPerBlock = 32;         // query and key block of the backw
 constexpr int kBwdMetaFloats = 64;          // workspace floats per query block
 hipError_t launch_bwd_f32(const BwdArgs& a, int head_dim, bool causal, hipStream_t s,
                           hipEvent_t ev_pre, hipEvent_t ev_dkdv);
+// 16-bit inputs: bf16, or fp16 when a.in_f16.
 hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, bool causal, hipStream_t s,
                            hipEvent_t ev_pre, hipEvent_t ev_dkdv);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s);

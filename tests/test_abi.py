@@ -294,10 +294,12 @@ def test_backward_workspace_and_host_checks():
     assert sma.attention_bwd_workspace_bytes(F32, 2, 3, 100, 50, 64, True) == 2 * 3 * 4 * 256
     assert sma.attention_bwd_workspace_bytes(F32, 1, 1, 0, 50, 64, False) == 0
     assert sma.attention_bwd_workspace_bytes(F32, 1, 1, 33, 50, 96, False) == 0   # head_dim
-    assert sma.attention_bwd_workspace_bytes(F16, 1, 1, 33, 50, 64, False) == 0   # dtype
+    assert sma.attention_bwd_workspace_bytes(7, 1, 1, 33, 50, 64, False) == 0     # dtype
     # bf16 Q, K, V: the per-block lse2/D, then dO rounded to bf16 (256-byte aligned)
     assert sma.attention_bwd_workspace_bytes(BF16, 2, 3, 100, 50, 64, True) == 2 * 3 * 4 * 256 + 76800
     assert sma.attention_bwd_workspace_bytes(BF16, 1, 1, 33, 50, 64, False) == 2 * 256 + 4352
+    # fp16 Q, K, V take the same layout, with dO rounded to fp16
+    assert sma.attention_bwd_workspace_bytes(F16, 2, 3, 100, 50, 64, True) == 2 * 3 * 4 * 256 + 76800
     base = [0x10_0000_0000 * i for i in range(1, 11)]
     q, k, v, o, lse, g, dq, dk, dv, ws = base
 
@@ -313,9 +315,10 @@ def test_backward_workspace_and_host_checks():
     assert call(ws=None) == INVAL and call(wsb=8 * 256 - 1) == INVAL        # 2 heads x 4 blocks
     assert call(d=0) == INVAL and call(scale=float("inf")) == INVAL
     assert call(B=1 << 40, H=1 << 40) == INVAL
-    assert call(d=96) == UNSUP and call(idt=F16) == UNSUP
-    # bf16 takes a larger workspace (the bf16 copy of dO): the fp32 size is too small
+    assert call(d=96) == UNSUP and call(idt=7) == INVAL
+    # 16-bit inputs take a larger workspace (the 16-bit copy of dO): the fp32 size is too small
     assert call(idt=BF16, wsb=8 * 256) == INVAL and call(idt=BF16, d=96) == UNSUP
+    assert call(idt=F16, wsb=8 * 256) == INVAL and call(idt=F16, d=96) == UNSUP
     assert call(d=32) == UNSUP and call(d=256) == UNSUP                      # forward-only head dims
     assert sma.attention_bwd_workspace_bytes(F32, 1, 1, 33, 50, 256, False) == 0
     assert call(sq=(1 << 23), d=64) == UNSUP                                 # 32-bit tile offsets
@@ -341,7 +344,7 @@ def test_backward_layout_host_checks():
     # rows pass under [B,H,S,d] and exceed 2 GiB of offsets under [B,S,H,d]
     big = dict(H=64, sq=1 << 17, skv=64, d=128)
     assert call(sma.SMA_LAYOUT_BSHD, **big) == UNSUP
-    assert call(sma.SMA_LAYOUT_BSHD, idt=F16) == UNSUP and call(sma.SMA_LAYOUT_BSHD, d=96) == UNSUP
+    assert call(sma.SMA_LAYOUT_BSHD, idt=F16, wsb=8 * 256) == INVAL and call(sma.SMA_LAYOUT_BSHD, d=96) == UNSUP
     assert call(sma.SMA_LAYOUT_BSHD, wsb=16) == INVAL  # workspace too small
     assert call(sma.SMA_LAYOUT_BSHD, dq=q) == ALIAS
 

@@ -5,15 +5,16 @@ The GPU backward consumes the GPU bf16 forward's O and LSE, as a training step w
 oracle recomputes every gradient in double from the exact bf16 values of Q, K, V and the
 fp32 dO.
 
-Parity bar (derived): the kernels round three factors to bf16 (unit roundoff u = 2^-9):
-dO (for dP and dV), P (for dV) and dS (for dK and dQ). Each term of a gradient then carries
-a relative error of at most about 2u beyond the fp32 rounding, relative to the magnitudes
-the oracle's error scale M sums (oracle.attention_bwd_bound: every factor in magnitude,
-|dP| and |D| bounded by dPmag and Dmag, each P weighted by the size of its exponent). So
-elementwise |gpu - ref| <= BF16_GRAD_TAU * M with BF16_GRAD_TAU = 4u = 2^-7, twice that
-estimate; an element whose M is 0 must be exactly 0. Per tensor, the roundings of
-independent terms add up like a random walk, far below their sum of magnitudes:
-||gpu - ref||_2 <= BF16_GRAD_L2 * ||M||_2 with BF16_GRAD_L2 = u.
+Parity bar (derived): the kernels round three factors to bf16 (8 significant bits, unit
+roundoff u = 2^-8): dO (for dP and dV), P (for dV) and dS (for dK and dQ). Each term of a
+gradient then carries a relative error of at most about 2u (to first order) beyond the fp32
+rounding, relative to the magnitudes the oracle's error scale M sums
+(oracle.attention_bwd_bound: every factor in magnitude, |dP| and |D| bounded by dPmag and
+Dmag, each P weighted by the size of its exponent). So elementwise
+|gpu - ref| <= BF16_GRAD_TAU * M with BF16_GRAD_TAU = 2u = 2^-7, that bound; an element
+whose M is 0 must be exactly 0. Per tensor, the roundings of independent terms add up like a
+random walk, far below their sum of magnitudes: ||gpu - ref||_2 <= BF16_GRAD_L2 * ||M||_2
+with BF16_GRAD_L2 = u/2.
 """
 import functools
 import math
@@ -208,8 +209,8 @@ def test_bwd_bf16_binding_checks():
     lse = torch.zeros(1, 1, 8, device="cuda")
     with pytest.raises(ValueError):  # mixed input dtypes
         sma.attention_bwd(q, q.float(), q, o, lse, o)
-    with pytest.raises(ValueError):  # fp16 inputs are not built
-        sma.attention_bwd(q.half(), q.half(), q.half(), o, lse, o)
+    with pytest.raises(ValueError):  # bf16 and fp16 mixed
+        sma.attention_bwd(q.half(), q, q, o, lse, o)
     with pytest.raises(ValueError):  # dO must be fp32
         sma.attention_bwd(q, q, q, o, lse, o.to(torch.bfloat16))
 
