@@ -5,7 +5,7 @@ at two densities in every broadcast form, rows that admit nothing, causal and no
 (bar 1e-5 of the oracle's error scale, as in test_gpu_bwd.py) and bf16 inputs (bar 2^-7 of
 it, as in test_gpu_bwd_bf16.py). An all-ones mask must reproduce the unmasked backward bit
 for bit, the [B,S,H,d] layout must equal [B,H,S,d] on transposed data bit for bit, and HIP-graph
-replays of the backward must equal the eager call bit for bit.
+replays of the backward (fp32, bf16 and fp16 inputs) must equal the eager call bit for bit.
 """
 import numpy as np
 import pytest
@@ -130,7 +130,7 @@ def test_masked_backward_binding_checks():
 
 
 @pytest.mark.parametrize("masked", [False, True])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_backward_hip_graph_replays_match_eager(dtype, masked):
     """The backward (with its mask packing when masked) captured in a HIP graph through torch,
     replayed several times with eager work and synchronizations between replays and the
@@ -145,7 +145,7 @@ def test_backward_hip_graph_replays_match_eager(dtype, masked):
     tg = torch.from_numpy(g).to("cuda")
     tm = torch.from_numpy(_mask(1631, (1, 2, 180, 210), 0.6, empty_rows=(3,))).to("cuda") if masked else None
     o, lse = sma.attention_fwd(tq, tk, tv, scale=0.12, causal=True, return_lse=True, mask=tm)
-    in_dt = sma.SMA_DTYPE_F32 if dtype == "f32" else sma.SMA_DTYPE_BF16
+    in_dt = {"f32": sma.SMA_DTYPE_F32, "bf16": sma.SMA_DTYPE_BF16, "f16": sma.SMA_DTYPE_F16}[dtype]
     if masked:
         n = sma.library().sma_attention_bwd_masked_workspace_bytes(in_dt, 2, 2, 180, 210, 64, 1, 0, 1, 2)
     else:
