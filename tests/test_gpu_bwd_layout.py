@@ -1,6 +1,6 @@
 """Attention backward in the [B,S,H,d] layout, through the C ABI: the gradients must equal
 those of the [B,H,S,d] backward on the same data, bit for bit (the kernels do the same
-arithmetic through different strides), for fp32 and bf16 inputs, causal and not, on ragged
+arithmetic through different strides), for fp32, bf16 and fp16 inputs, causal and not, on ragged
 shapes. The [B,H,S,d] backward itself is checked against the oracle in test_gpu_bwd.py and
 test_gpu_bwd_bf16.py.
 """
@@ -23,7 +23,7 @@ def _gpu():
     sma.library()
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(2, 3, 130, 77), (1, 2, 200, 333), (2, 1, 257, 129)],

@@ -91,7 +91,7 @@ def test_masked_backward_parity(causal, d, density, form, dtype):
     assert np.all(got[0].cpu().numpy()[:, :, 5:7] == 0.0)  # rows that admit nothing
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_all_ones_mask_is_bitwise_the_unmasked_backward(dtype, causal):
     (q, k, v), bits = gen.random_case(1610, (1, 3, 200, 128), (1, 3, 230, 128), dtype=dtype)
@@ -103,7 +103,7 @@ def test_all_ones_mask_is_bitwise_the_unmasked_backward(dtype, causal):
         assert np.array_equal(x.cpu().numpy(), y.cpu().numpy())
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_masked_backward_bshd_equals_bhsd(dtype):
     (q, k, v), bits = gen.random_case(1620, (2, 3, 150, 64), (2, 3, 190, 64), dtype=dtype)
     g = gen.upstream_grad(1620, (2, 3, 150, 64))
