@@ -2,7 +2,9 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
-NAME is a key of gen.WORKLOADS (default: the fp32 4x8-head, 512x512, d=64 shape).
+NAME is a key of gen.WORKLOADS (default: bf16 inputs, causal, 1 x 32 heads,
+16384 x 16384 tokens, head dim 128), a backward workload (bwd_ + a forward key)
+or a row-primitive workload.
 
 A step is one attention forward (every kernel of the path) over the
 workload's synthetic inputs, already resident in HBM. Prints one JSON line:
@@ -30,7 +32,10 @@ METRIC = "attention fwd TFLOP/s (4·B·H·Sq·Skv·d, causal halved) and % of MF
 # MI355X published dense MFMA peaks (TFLOP/s) and HBM bandwidth (GB/s).
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f16": 2500.0}
 HBM_GBPS = 8000.0
-DEFAULT_WORKLOAD = "f32_b4h8_s512_d64"  # the shape the headline metric is quoted on
+# The largest workload that fits one GPU, and the one the >= 50 %-of-peak target is
+# about: bf16 inputs, causal, 1 x 32 heads, 16384 x 16384 tokens, head dim 128.
+DEFAULT_WORKLOAD = "bf16_causal_b1h32_s16384_d128"
+PEAK_SCLK_MHZ = 2400.0  # the engine clock the published peaks assume
 
 
 def metric_flops(w) -> float:
@@ -92,6 +97,131 @@ class HipEvents:
 
     def destroy(self, ev):
         self.hip.hipEventDestroy(ev)
+
+
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class ClockSampler:
+    """Engine (SCLK) and memory (MCLK) clocks of the GPU in use, read through the amd-smi
+    library from a host thread every few milliseconds while the timed loop runs. Values
+    are MHz; SCLK is the mean over the XCDs of each sample."""
+
+    NA = 0xFFFF  # amd-smi's marker for a field the firmware does not report
+
+    def __init__(self, period_s: float = 0.004):
+        self.period_s = period_s
+        self.samples, self.mclk = [], []
+        self.error = None
+        self.field = None
+        self.handle = None
+        self._stop = None
+        self._thread = None
+        try:
+            import amdsmi
+            import torch
+
+            self.amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if len(handles) == 1:
+                self.handle = handles[0]
+            else:  # match the PCI bus of torch's device 0
+                props = torch.cuda.get_device_properties(0)
+                bus = getattr(props, "pci_bus_id", None)
+                for h in handles:
+                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                    if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                        self.handle = h
+                        break
+            if self.handle is None:
+                raise RuntimeError(f"no amd-smi handle matches the device ({len(handles)} found)")
+            self._read()  # fail here, not in the thread, if the metrics are unreadable
+            self.samples.clear()
+            self.mclk.clear()
+        except Exception as e:  # noqa: BLE001 - report, never fail the bench for it
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+
+        def ok(x):
+            return isinstance(x, (int, float)) and 0 < x < self.NA
+
+        xs = [x for x in (m.get("current_gfxclks") or []) if ok(x)]
+        if xs:
+            self.field = "current_gfxclks (mean over XCDs)"
+            self.samples.append(sum(xs) / len(xs))
+        elif ok(m.get("current_gfxclk")):
+            self.field = "current_gfxclk"
+            self.samples.append(float(m["current_gfxclk"]))
+        elif ok(m.get("average_gfxclk_frequency")):
+            self.field = "average_gfxclk_frequency"
+            self.samples.append(float(m["average_gfxclk_frequency"]))
+        u = m.get("current_uclk")
+        if ok(u):
+            self.mclk.append(float(u))
+
+    def start(self):
+        import threading
+
+        if self.error:
+            return
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    self._read()
+                except Exception as e:  # noqa: BLE001
+                    self.error = f"{type(e).__name__}: {e}"
+                    return
+                self._stop.wait(self.period_s)
+
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+
+    def stop(self) -> dict:
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        out = {"source": "amd-smi gpu metrics, sampled during the timed loop"}
+        if self.samples:
+            out.update(sclk_mhz_mean=round(float(np.mean(self.samples)), 1),
+                       sclk_mhz_min=round(float(np.min(self.samples)), 1),
+                       sclk_mhz_max=round(float(np.max(self.samples)), 1),
+                       sclk_field=self.field, samples=len(self.samples))
+        if self.mclk:
+            out["mclk_mhz_mean"] = round(float(np.mean(self.mclk)), 1)
+        if self.error or not self.samples:
+            out["error"] = self.error or "no clock samples"
+        return out
+
+
+def with_host(baseline: dict) -> dict:
+    """The CPU baseline with the host's processor model beside its thread count."""
+    baseline["cpu_model"] = host_cpu_model()
+    return baseline
+
+
+def clock_adjusted(frac: float, clocks: dict):
+    """The roofline fraction against the peak at the sampled engine clock (the published
+    peak assumes 2.4 GHz), or None without clock samples."""
+    s = clocks.get("sclk_mhz_mean")
+    return round(frac * PEAK_SCLK_MHZ / s, 4) if s else None
+
+
+def step_stats(durations_ms):
+    d = np.asarray(durations_ms, dtype=np.float64)
+    return {"median": round(float(np.median(d)), 5), "min": round(float(d.min()), 5),
+            "max": round(float(d.max()), 5), "n": int(d.size)}
 
 
 def settle(step, ms: float) -> int:
@@ -320,13 +450,17 @@ def bench_bwd(args, w, name):
     ev = HipEvents()
     e_pre = [ev.create() for _ in range(args.steps)]
     e_kv = [ev.create() for _ in range(args.steps)]
+    clocks = ClockSampler()
+    clocks.start()
     t0 = time.perf_counter()
     for i in range(args.steps):
         sma.attention_bwd_raw(*call, e_pre[i], e_kv[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    clock_info = clocks.stop()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    k_avg = sum(ev.elapsed_ms(e_pre[i], e_kv[i]) for i in range(args.steps)) / args.steps
+    launches = [ev.elapsed_ms(e_pre[i], e_kv[i]) for i in range(args.steps)]
+    k_avg = sum(launches) / args.steps
     for e in e_pre + e_kv:
         ev.destroy(e)
     for t in (dq, dk, dv):
@@ -345,6 +479,7 @@ def bench_bwd(args, w, name):
         "steps": args.steps, "warmup": args.warmup, "settle_steps": settled, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded SplitMix64 + Box-Muller normals; dO on its own stream)",
+        "clocks": clock_info, "gpu": torch.cuda.get_device_name(0),
         "config": {"workload": name, "batch": B, "heads": H, "seq_q": sq, "seq_kv": skv,
                    "head_dim": d, "causal": w.causal, "scale": w.scale, "input_dtype": w.dtype,
                    "o_and_dout": "f32", "gradients": "f32", "workspace_bytes": ws_n},
@@ -352,13 +487,14 @@ def bench_bwd(args, w, name):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": f"{kname}<{d},{str(w.causal).lower()}" + (",f16>" if w.dtype == "f16" else ">"),
-                     "kernel_avg_ms": round(k_avg, 5),
+                     "kernel_avg_ms": round(k_avg, 5), "kernel_ms": step_stats(launches),
+                     "frac_at_sampled_sclk": clock_adjusted(achieved / peak, clock_info),
                      "kernel_timing": "HIP events recorded by the library around each dK/dV launch",
                      "flops_per_launch": kernel_flops,
                      "min_hbm_bytes_per_launch": dkdv_min_bytes(w)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = bwd_cpu_baseline(w, *vals, g, args.cpu_seconds)
+        line["cpu_baseline"] = with_host(bwd_cpu_baseline(w, *vals, g, args.cpu_seconds))
     print(json.dumps(line), flush=True)
 
 
@@ -460,6 +596,8 @@ def bench_rows(args, w):
     torch.cuda.synchronize()
     ev = HipEvents()
     e0, e1 = ev.create(), ev.create()
+    clocks = ClockSampler()
+    clocks.start()
     t0 = time.perf_counter()
     ev.record(e0, stream.cuda_stream)
     for _ in range(args.steps):
@@ -467,6 +605,7 @@ def bench_rows(args, w):
     ev.record(e1, stream.cuda_stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    clock_info = clocks.stop()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     k_avg = ev.elapsed_ms(e0, e1) / args.steps
     ev.destroy(e0)
@@ -478,6 +617,7 @@ def bench_rows(args, w):
         "metric": ROW_METRIC, "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_steps": settled, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "clocks": clock_info, "gpu": torch.cuda.get_device_name(0),
         "data": ("synthetic (seeded SplitMix64 + Box-Muller normals; y = the GPU row softmax of the "
                  "scores, untimed)" if w.op == "softmax_rows_backward" else
                  "synthetic (seeded SplitMix64 + Box-Muller normals; Bernoulli mask)"),
@@ -491,7 +631,7 @@ def bench_rows(args, w):
                      "algorithmic_bytes_per_launch": nbytes},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = row_cpu_baseline(w, x, mask, args.cpu_seconds)
+        line["cpu_baseline"] = with_host(row_cpu_baseline(w, x, mask, args.cpu_seconds))
     print(json.dumps(line), flush=True)
 
 
@@ -593,34 +733,41 @@ def main():
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
-    # Timed region. A one-kernel step is bracketed by two events around the whole
-    # loop (events around every launch would add their own gaps to each
-    # measured launch); a step with a split-combine kernel records events around
-    # every main-kernel launch instead, so that the main kernel is timed alone.
+    # Timed region. A one-kernel step gets one event between consecutive launches
+    # (K + 1 events: the first before step 0), so each launch's duration is read
+    # apart without bracketing it twice; a step with a split-combine kernel (or the
+    # mask packing) records events around every main-kernel launch instead, so
+    # that the main kernel is timed alone.
     per_launch = plan.nsplit > 1 or masked
     if per_launch:
         ev_a = [ev.create() for _ in range(args.steps)]
         ev_b = [ev.create() for _ in range(args.steps)]
         with_events = [base + (ev_a[i], ev_b[i]) for i in range(args.steps)]
     else:
-        ev_a, ev_b = [ev.create()], [ev.create()]
+        marks = [ev.create() for _ in range(args.steps + 1)]
+    clocks = ClockSampler()
+    clocks.start()
     t0 = time.perf_counter()
     if per_launch:
         for i in range(args.steps):
             run(with_events[i])
     else:
-        ev.record(ev_a[0], sptr)
+        ev.record(marks[0], sptr)
         for i in range(args.steps):
             run()
-        ev.record(ev_b[0], sptr)
+            ev.record(marks[i + 1], sptr)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    clock_info = clocks.stop()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     if per_launch:
-        k_avg = sum(ev.elapsed_ms(ev_a[i], ev_b[i]) for i in range(args.steps)) / args.steps
+        launches = [ev.elapsed_ms(ev_a[i], ev_b[i]) for i in range(args.steps)]
+        events = ev_a + ev_b
     else:
-        k_avg = ev.elapsed_ms(ev_a[0], ev_b[0]) / args.steps
-    for e in ev_a + ev_b:
+        launches = [ev.elapsed_ms(marks[i], marks[i + 1]) for i in range(args.steps)]
+        events = marks
+    k_avg = sum(launches) / len(launches)
+    for e in events:
         ev.destroy(e)
     assert torch.isfinite(out).all().item(), "non-finite output"
 
@@ -636,6 +783,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "settle_steps": settled, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded SplitMix64 + Box-Muller normals)",
+        "clocks": clock_info, "gpu": torch.cuda.get_device_name(0),
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_q": sq, "seq_kv": skv,
                    "head_dim": d, "causal": w.causal, "scale": w.scale,
                    "input_dtype": w.dtype, "accumulate": "f32", "output": args.out_dtype, "lse": True,
@@ -647,16 +795,18 @@ def main():
                      "kernel": (f"{KERNEL_FUNCTIONS[plan.kernel]}<{d},{str(w.causal).lower()}"
                                 + (",f16>" if w.dtype == "f16" else ">")),
                      "kernel_avg_ms": round(k_avg, 5),
-                     "kernel_timing": ("HIP events around each launch" if per_launch else
-                                       "HIP events around the timed loop / steps"),
+                     "kernel_ms": step_stats(launches),
+                     "frac_at_sampled_sclk": clock_adjusted(achieved / peak, clock_info),
+                     "kernel_timing": ("HIP events around each main-kernel launch" if per_launch else
+                                       "HIP events between consecutive launches in the timed loop"),
                      "plan": {"kernel": sma.KERNEL_NAMES[plan.kernel], "key_splits": plan.nsplit,
                               "workgroups": plan.workgroups},
                      "flops_per_launch": exact,
                      "min_hbm_bytes_per_launch": min_bytes(w, 2 if o16 else 4)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = (masked_cpu_baseline(w, vals, mask_np, args.cpu_seconds) if masked
-                                else cpu_baseline(w, vals, args.cpu_seconds))
+        line["cpu_baseline"] = with_host(masked_cpu_baseline(w, vals, mask_np, args.cpu_seconds)
+                                         if masked else cpu_baseline(w, vals, args.cpu_seconds))
     print(json.dumps(line), flush=True)
 
 

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SMA_ABI_VERSION 2
+#define SMA_ABI_VERSION 3
 
 /* Element types. Accumulation is always fp32. */
 typedef enum {
@@ -145,7 +145,9 @@ int sma_attention_fwd_timed(const void* q, const void* k, const void* v, void* o
 
 /* The same checks as sma_attention_fwd, on the host only: no HIP call, nothing
  * launched, pointers are not dereferenced. Returns the status sma_attention_fwd
- * would return before launching. */
+ * would return before launching. This is the validating no-op backend of the
+ * oxicuda ComputeBackend page (its `NullBackend` implementor, which checks a call's
+ * arguments and computes nothing), for the attention call alone. */
 int sma_attention_fwd_validate(const void* q, const void* k, const void* v, const void* o,
                                const float* lse, int in_dtype, int o_dtype, size_t batch,
                                size_t heads, size_t seq_q, size_t seq_kv, size_t head_dim,
@@ -153,25 +155,29 @@ int sma_attention_fwd_validate(const void* q, const void* k, const void* v, cons
                                size_t workspace_bytes);
 
 /* Workspace bytes that let sma_attention_fwd split keys across workgroups for
- * this shape on a GPU with num_cus compute units (pass 0 for the current HIP
- * device; if it cannot be queried, 256 is assumed). 0 means splitting is never
- * used for this shape. Invalid arguments also give 0. */
+ * this shape ([B,H,S,d]) on the current HIP device (if its compute units
+ * cannot be queried, as on a host without a GPU, 256 are assumed). 0 means
+ * splitting is never used for this shape. Invalid arguments also give 0.
+ * sma_attention_fwd_plan gives the same figure for another layout or CU count. */
 size_t sma_attention_fwd_workspace_bytes(int in_dtype, size_t batch, size_t heads, size_t seq_q,
-                                         size_t seq_kv, size_t head_dim, int causal, int num_cus);
+                                         size_t seq_kv, size_t head_dim, int causal);
 
-/* The plan for a shape, on the host only (no launch). kernel: SMA_KERNEL_AUTO
- * for the library's own choice, else the kernel to plan for (one that does not
- * run in_dtype or head_dim -> UNSUPPORTED). nsplit: 0 lets the library choose the key
- * split; 1..32 asks for that many (the plan may merge splits so that each
- * keeps a whole number of key tiles, and SMA_KERNEL_F32_KSPLIT accepts only
- * 0 or 1, and only (seq_q + 32) and (seq_kv + 32) rows of head_dim floats of
- * at most 2 GiB; otherwise UNSUPPORTED). num_cus as for sma_attention_fwd_workspace_bytes. The plan of
- * SMA_KERNEL_AUTO is the one sma_attention_fwd follows when it is given at
- * least plan.workspace_bytes of workspace. Shape errors as sma_attention_fwd;
- * out NULL -> NULL_POINTER. */
+/* The plan for a shape in `layout` (an sma_layout: the row stride it implies
+ * enters the size limits and the kernel choice), on the host only (no launch).
+ * kernel: SMA_KERNEL_AUTO for the library's own choice, else the kernel to plan
+ * for (one that does not run in_dtype or head_dim -> UNSUPPORTED). nsplit: 0
+ * lets the library choose the key split; 1..32 asks for that many (the plan may
+ * merge splits so that each keeps a whole number of key tiles, and
+ * SMA_KERNEL_F32_KSPLIT accepts only 0 or 1, and only (seq_q + 32) and
+ * (seq_kv + 32) rows of head_dim floats of at most 2 GiB; otherwise
+ * UNSUPPORTED). num_cus: compute units to plan for; 0 for the current HIP
+ * device (256 if it cannot be queried). The plan of SMA_KERNEL_AUTO with
+ * num_cus = 0 is the one sma_attention_fwd_layout follows when it is given at
+ * least plan.workspace_bytes of workspace. Shape errors as
+ * sma_attention_fwd_layout; out NULL -> NULL_POINTER. */
 int sma_attention_fwd_plan(int in_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
-                           size_t head_dim, int causal, int kernel, int nsplit, int num_cus,
-                           sma_plan* out);
+                           size_t head_dim, int causal, int layout, int kernel, int nsplit,
+                           int num_cus, sma_plan* out);
 
 /* sma_attention_fwd with the memory layout of sma_attention_fwd_layout, the
  * kernel and key split taken from `plan` (NULL: the library's choice, exactly
@@ -193,9 +199,9 @@ int sma_attention_fwd_ex(const void* q, const void* k, const void* v, void* o, f
  * for the same data in [B,H,S,d]. The size checks apply to the layout's row
  * stride: with SMA_LAYOUT_BSHD one row of a head is heads*head_dim elements
  * from the next, so the 2 GiB limits on (seq + tile) rows are reached at
- * 1/heads the sequence length. sma_attention_fwd_workspace_bytes and
- * sma_attention_fwd_plan describe [B,H,S,d]; a workspace too small for the
- * plan chosen here only disables the key split. */
+ * 1/heads the sequence length. sma_attention_fwd_plan with the same layout
+ * gives the plan and the workspace that enables its key split; a workspace too
+ * small for that plan only disables the key split. */
 int sma_attention_fwd_layout(const void* q, const void* k, const void* v, void* o, float* lse,
                              int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
                              size_t seq_kv, size_t head_dim, double scale, int causal, int layout,

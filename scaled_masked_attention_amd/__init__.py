@@ -71,11 +71,11 @@ def library():
                                                    ctypes.c_int, vp, sz]
         lib.sma_attention_fwd_validate.restype = ctypes.c_int
         lib.sma_attention_fwd_workspace_bytes.argtypes = [ctypes.c_int, sz, sz, sz, sz, sz,
-                                                          ctypes.c_int, ctypes.c_int]
+                                                          ctypes.c_int]
         lib.sma_attention_fwd_workspace_bytes.restype = sz
         lib.sma_attention_fwd_plan.argtypes = [ctypes.c_int, sz, sz, sz, sz, sz, ctypes.c_int,
                                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                               ctypes.POINTER(Plan)]
+                                               ctypes.c_int, ctypes.POINTER(Plan)]
         lib.sma_attention_fwd_plan.restype = ctypes.c_int
         fwd = lib.sma_attention_fwd.argtypes
         lib.sma_attention_fwd_ex.argtypes = (fwd[:14] + [ctypes.c_int] + fwd[14:16] +
@@ -134,18 +134,30 @@ def _raise(st: int):
 
 
 def workspace_bytes(in_dtype: int, batch: int, heads: int, seq_q: int, seq_kv: int,
-                    head_dim: int, causal: bool, num_cus: int = 0) -> int:
-    return int(library().sma_attention_fwd_workspace_bytes(in_dtype, batch, heads, seq_q, seq_kv,
-                                                           head_dim, int(bool(causal)), num_cus))
+                    head_dim: int, causal: bool, num_cus: int = 0, layout: str = "bhsd") -> int:
+    """Workspace that enables the library's key split (0: it never splits this shape, or
+    the arguments are invalid). With the defaults this is sma_attention_fwd_workspace_bytes;
+    another CU count or the [B,S,H,d] layout goes through sma_attention_fwd_plan."""
+    if num_cus == 0 and layout == "bhsd":
+        return int(library().sma_attention_fwd_workspace_bytes(in_dtype, batch, heads, seq_q,
+                                                               seq_kv, head_dim, int(bool(causal))))
+    try:
+        return int(plan(in_dtype, batch, heads, seq_q, seq_kv, head_dim, causal, num_cus=num_cus,
+                        layout=layout).workspace_bytes)
+    except SMAError:
+        return 0
 
 
 def plan(in_dtype: int, batch: int, heads: int, seq_q: int, seq_kv: int, head_dim: int,
-         causal: bool, kernel: int = SMA_KERNEL_AUTO, nsplit: int = 0, num_cus: int = 0) -> Plan:
+         causal: bool, kernel: int = SMA_KERNEL_AUTO, nsplit: int = 0, num_cus: int = 0,
+         layout: str = "bhsd") -> Plan:
     """sma_attention_fwd_plan: the kernel, split and workspace a call would use."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
     out = Plan()
     _raise(library().sma_attention_fwd_plan(in_dtype, batch, heads, seq_q, seq_kv, head_dim,
-                                            int(bool(causal)), kernel, nsplit, num_cus,
-                                            ctypes.byref(out)))
+                                            int(bool(causal)), LAYOUTS[layout], kernel, nsplit,
+                                            num_cus, ctypes.byref(out)))
     return out
 
 
@@ -217,7 +229,23 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
     where it is nonzero (and, with causal, under the causal bound too).
     kernel (an SMA_KERNEL_* code) and nsplit force a plan; by default the
     library chooses. A forced split gets a workspace of the size it needs.
+    stream: the torch.cuda.Stream to launch on (default: the current stream); the
+    outputs and workspace allocated here are allocated on it.
     """
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    # Outputs and workspace are allocated on the launch stream: the caching
+    # allocator then never hands their blocks to other work while the kernels
+    # still use them, whichever stream the caller launches on.
+    with torch.cuda.stream(stream):
+        return _attention_fwd(q, k, v, scale, causal, return_lse, out, lse, workspace, stream,
+                              kernel, nsplit, out_dtype, layout, mask)
+
+
+def _attention_fwd(q, k, v, scale, causal, return_lse, out, lse, workspace, stream, kernel, nsplit,
+                   out_dtype, layout, mask):
     import torch
 
     if not (isinstance(q, torch.Tensor) and isinstance(k, torch.Tensor) and isinstance(v, torch.Tensor)):
@@ -273,10 +301,11 @@ def attention_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None,
         raise ValueError("out/lse shape mismatch")
     forced = None
     if kernel is not None and kernel != SMA_KERNEL_AUTO:
-        forced = plan(in_dt, B, H, Sq, Skv, D, causal, kernel, nsplit)
+        forced = plan(in_dt, B, H, Sq, Skv, D, causal, kernel, nsplit, layout=layout)
         need = forced.workspace_bytes
     else:
-        need = 0 if mask is not None else workspace_bytes(in_dt, B, H, Sq, Skv, D, causal)
+        need = 0 if mask is not None else workspace_bytes(in_dt, B, H, Sq, Skv, D, causal,
+                                                          layout=layout)
     if mask is not None:
         if not isinstance(mask, torch.Tensor) or mask.dtype not in (torch.bool, torch.uint8):
             raise ValueError("mask must be a bool or uint8 torch tensor")
@@ -342,6 +371,15 @@ def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, workspace=Non
     given (bool or uint8, [Sq,Skv] or [B or 1, H or 1, Sq, Skv]). Returns three
     float32 tensors shaped like q, k and v. The workspace is allocated when not given.
     """
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    with torch.cuda.stream(stream):  # allocations on the launch stream, as in attention_fwd
+        return _attention_bwd(q, k, v, o, lse, dout, scale, causal, workspace, stream, layout, mask)
+
+
+def _attention_bwd(q, k, v, o, lse, dout, scale, causal, workspace, stream, layout, mask):
     import torch
 
     ts = {"q": q, "k": k, "v": v, "o": o, "lse": lse, "dout": dout}
@@ -442,39 +480,45 @@ def softmax_rows(x, out=None, stream=None):
     """Row softmax of a contiguous float32 [rows, cols] tensor; out may be x (in place)."""
     import torch
 
-    x = _row_input(x, "x", 2)
-    out = torch.empty_like(x) if out is None else _row_input(out, "out", 2)
-    if out.shape != x.shape:
-        raise ValueError("out shape differs")
-    s = (stream or torch.cuda.current_stream()).cuda_stream
-    _raise(library().sma_softmax_rows(_ptr(x), _ptr(out), x.shape[0], x.shape[1], s))
-    return out
+    stream = stream or torch.cuda.current_stream()
+    with torch.cuda.stream(stream):  # allocate on the launch stream
+        x = _row_input(x, "x", 2)
+        out = torch.empty_like(x) if out is None else _row_input(out, "out", 2)
+        if out.shape != x.shape:
+            raise ValueError("out shape differs")
+        s = stream.cuda_stream
+        _raise(library().sma_softmax_rows(_ptr(x), _ptr(out), x.shape[0], x.shape[1], s))
+        return out
 
 
 def logsumexp_rows(x, out=None, stream=None):
     """Per-row natural-log log-sum-exp of a contiguous float32 [rows, cols] tensor -> [rows]."""
     import torch
 
-    x = _row_input(x, "x", 2)
-    out = torch.empty(x.shape[0], dtype=torch.float32, device=x.device) if out is None else out
-    if out.shape != (x.shape[0],):
-        raise ValueError("out must be [rows]")
-    s = (stream or torch.cuda.current_stream()).cuda_stream
-    _raise(library().sma_logsumexp_rows(_ptr(x), _ptr(out), x.shape[0], x.shape[1], s))
-    return out
+    stream = stream or torch.cuda.current_stream()
+    with torch.cuda.stream(stream):  # allocate on the launch stream
+        x = _row_input(x, "x", 2)
+        out = torch.empty(x.shape[0], dtype=torch.float32, device=x.device) if out is None else out
+        if out.shape != (x.shape[0],):
+            raise ValueError("out must be [rows]")
+        s = stream.cuda_stream
+        _raise(library().sma_logsumexp_rows(_ptr(x), _ptr(out), x.shape[0], x.shape[1], s))
+        return out
 
 
 def masked_softmax_rows(x, mask, out=None, stream=None):
     """Hard-masked row softmax: mask (float32, same shape) nonzero admits an entry."""
     import torch
 
-    x, mask = _row_input(x, "x", 2), _row_input(mask, "mask", 2)
-    if mask.shape != x.shape:
-        raise ValueError("mask shape differs")
-    out = torch.empty_like(x) if out is None else _row_input(out, "out", 2)
-    s = (stream or torch.cuda.current_stream()).cuda_stream
-    _raise(library().sma_masked_softmax_rows(_ptr(x), _ptr(mask), _ptr(out), x.shape[0], x.shape[1], s))
-    return out
+    stream = stream or torch.cuda.current_stream()
+    with torch.cuda.stream(stream):  # allocate on the launch stream
+        x, mask = _row_input(x, "x", 2), _row_input(mask, "mask", 2)
+        if mask.shape != x.shape:
+            raise ValueError("mask shape differs")
+        out = torch.empty_like(x) if out is None else _row_input(out, "out", 2)
+        s = stream.cuda_stream
+        _raise(library().sma_masked_softmax_rows(_ptr(x), _ptr(mask), _ptr(out), x.shape[0], x.shape[1], s))
+        return out
 
 
 def softmax_rows_backward(y, dy, scale=1.0, out=None, stream=None):
@@ -482,16 +526,18 @@ def softmax_rows_backward(y, dy, scale=1.0, out=None, stream=None):
     softmax output) and dy; out may be y or dy (in place)."""
     import torch
 
-    y, dy = _row_input(y, "y", 2), _row_input(dy, "dy", 2)
-    if dy.shape != y.shape:
-        raise ValueError("dy shape differs")
-    out = torch.empty_like(y) if out is None else _row_input(out, "out", 2)
-    if out.shape != y.shape:
-        raise ValueError("out shape differs")
-    s = (stream or torch.cuda.current_stream()).cuda_stream
-    _raise(library().sma_softmax_rows_backward(_ptr(y), _ptr(dy), _ptr(out), y.shape[0], y.shape[1],
-                                               float(scale), s))
-    return out
+    stream = stream or torch.cuda.current_stream()
+    with torch.cuda.stream(stream):  # allocate on the launch stream
+        y, dy = _row_input(y, "y", 2), _row_input(dy, "dy", 2)
+        if dy.shape != y.shape:
+            raise ValueError("dy shape differs")
+        out = torch.empty_like(y) if out is None else _row_input(out, "out", 2)
+        if out.shape != y.shape:
+            raise ValueError("out shape differs")
+        s = stream.cuda_stream
+        _raise(library().sma_softmax_rows_backward(_ptr(y), _ptr(dy), _ptr(out), y.shape[0], y.shape[1],
+                                                   float(scale), s))
+        return out
 
 
 def scaled_causal_softmax(x, scale, causal=True, out=None, stream=None):
@@ -499,11 +545,13 @@ def scaled_causal_softmax(x, scale, causal=True, out=None, stream=None):
     bottom-right causal mask when causal."""
     import torch
 
-    x = _row_input(x, "x", 3)
-    out = torch.empty_like(x) if out is None else _row_input(out, "out", 3)
-    if out.shape != x.shape:
-        raise ValueError("out shape differs")
-    s = (stream or torch.cuda.current_stream()).cuda_stream
-    _raise(library().sma_scaled_causal_softmax(_ptr(x), _ptr(out), x.shape[0], x.shape[1], x.shape[2],
-                                               float(scale), int(bool(causal)), s))
-    return out
+    stream = stream or torch.cuda.current_stream()
+    with torch.cuda.stream(stream):  # allocate on the launch stream
+        x = _row_input(x, "x", 3)
+        out = torch.empty_like(x) if out is None else _row_input(out, "out", 3)
+        if out.shape != x.shape:
+            raise ValueError("out shape differs")
+        s = stream.cuda_stream
+        _raise(library().sma_scaled_causal_softmax(_ptr(x), _ptr(out), x.shape[0], x.shape[1], x.shape[2],
+                                                   float(scale), int(bool(causal)), s))
+        return out

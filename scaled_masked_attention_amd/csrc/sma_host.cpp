@@ -431,21 +431,22 @@ int sma_attention_fwd_validate(const void* q, const void* k, const void* v, cons
 }
 
 size_t sma_attention_fwd_workspace_bytes(int in_dtype, size_t batch, size_t heads, size_t seq_q,
-                                         size_t seq_kv, size_t head_dim, int causal, int num_cus) {
+                                         size_t seq_kv, size_t head_dim, int causal) {
   sma_plan p;
   if (sma_attention_fwd_plan(in_dtype, batch, heads, seq_q, seq_kv, head_dim, causal,
-                             SMA_KERNEL_AUTO, 0, num_cus, &p) != SMA_OK)
+                             SMA_LAYOUT_BHSD, SMA_KERNEL_AUTO, 0, 0, &p) != SMA_OK)
     return 0;
   return p.workspace_bytes;
 }
 
 int sma_attention_fwd_plan(int in_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv,
-                           size_t head_dim, int causal, int kernel, int nsplit, int num_cus,
-                           sma_plan* out) {
+                           size_t head_dim, int causal, int layout, int kernel, int nsplit,
+                           int num_cus, sma_plan* out) {
   (void)causal;
   if (!out) return SMA_ERR_NULL_POINTER;
   Shape sh;
-  int st = check_shape(in_dtype, SMA_DTYPE_F32, batch, heads, seq_q, seq_kv, head_dim, 1.0, &sh);
+  int st = check_shape(in_dtype, SMA_DTYPE_F32, batch, heads, seq_q, seq_kv, head_dim, 1.0, &sh,
+                       layout);
   if (st != SMA_OK) return st;
   if (nsplit < 0 || nsplit > kMaxSplits) return SMA_ERR_INVALID_VALUE;
   if (kernel != SMA_KERNEL_AUTO) {
@@ -509,8 +510,11 @@ size_t sma_attention_fwd_masked_workspace_bytes(int in_dtype, size_t batch, size
   m.heads = mask_heads;
   if ((mask_batches != 1 && mask_batches != batch) || (mask_heads != 1 && mask_heads != heads)) return 0;
   // The packed mask, then what the library's key split needs on the current device.
-  return mask_bits_bytes(sh, m) + sma_attention_fwd_workspace_bytes(in_dtype, batch, heads, seq_q,
-                                                                    seq_kv, head_dim, causal, 0);
+  sma_plan p;
+  if (sma_attention_fwd_plan(in_dtype, batch, heads, seq_q, seq_kv, head_dim, causal, layout,
+                             SMA_KERNEL_AUTO, 0, 0, &p) != SMA_OK)
+    return 0;
+  return mask_bits_bytes(sh, m) + p.workspace_bytes;
 }
 
 int sma_attention_fwd_timed(const void* q, const void* k, const void* v, void* o, float* lse,

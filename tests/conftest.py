@@ -22,3 +22,13 @@ def _announce(request):
     if request.node.get_closest_marker("gpu") is not None:
         print(f"\n[gpu-case] {request.node.nodeid}", flush=True)
     yield
+
+
+def pytest_terminal_summary(terminalreporter):
+    # Errors of the full-size parity runs, shown even under -q.
+    mod = sys.modules.get("helpers")
+    lines = getattr(mod, "SUMMARY", None) if mod is not None else None
+    if lines:
+        terminalreporter.write_sep("-", "parity statistics (every output against the oracle)")
+        for line in lines:
+            terminalreporter.write_line(line)

@@ -16,6 +16,9 @@ BF16_MAX_ABS = 2e-2
 BF16_REL_L2 = 1e-2
 F16_MAX_ABS = 4e-3
 F16_REL_L2 = 2e-3
+# Lines printed at the end of the session by the terminal-summary hook in conftest.py.
+SUMMARY = []
+
 # LSE (natural log): |d| <= tol * max(1, |lse|).
 F32_LSE_TOL = 1e-5
 BF16_LSE_TOL = 1e-4

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert sma.abi_version() == 2
+    assert sma.abi_version() == 3
     for st in range(7):
         assert sma.status_string(st).startswith(sma.STATUS_NAMES[st])
     assert sma.status_string(99) == "unknown sma status"
@@ -120,6 +120,44 @@ def test_workspace_planner():
     assert sma.workspace_bytes(BF16, 1, 32, 16384, 16384, 128, True, 256) == 0
     assert sma.workspace_bytes(F32, 1, 1, 100, 100, 64, True, 256) == 0  # too few keys to split
     assert sma.workspace_bytes(F32, 1, 1, 100, 4096, 96, True, 256) == 0  # invalid -> 0
+
+
+def test_workspace_query_has_the_boundary_signature():
+    """sma_attention_fwd_workspace_bytes takes exactly the shape arguments of the call (no CU
+    count). Without a GPU here the planner assumes 256 CUs, so it equals the 256-CU plan."""
+    lib = ctypes.CDLL(sma.LIB_PATH)
+    f = lib.sma_attention_fwd_workspace_bytes
+    sz = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int, sz, sz, sz, sz, sz, ctypes.c_int]
+    f.restype = sz
+    n = f(F32, 1, 4, 200, 3000, 128, 0)
+    assert n > 0 and n == sma.plan(F32, 1, 4, 200, 3000, 128, False, num_cus=256).workspace_bytes
+    assert f(F32, 1, 4, 200, 3000, 96, 0) == 0  # invalid head dim -> 0
+    assert f(BF16, 1, 32, 16384, 16384, 128, 1) == 0
+
+
+def test_plan_follows_the_layout():
+    """Under [B,S,H,d] a head's rows are heads*head_dim apart, which moves the size limits:
+    the plan and workspace queries take the layout, so they agree with the call."""
+    # The 16-bit kernel reaches one head's K/V through 32-bit byte offsets: (seq_kv + 256)
+    # rows of the row stride must stay below 2 GiB. 300000 keys at a stride of 32 heads x 128
+    # dims (8 KiB per row in bf16) span 2.46e9 bytes under [B,S,H,d], 77 MB under [B,H,S,d].
+    args = (BF16, 1, 32, 1024, 300000, 128, True)
+    assert sma.plan(*args, num_cus=256).kernel == sma.SMA_KERNEL_BF16_QBLOCK
+    with pytest.raises(sma.SMAError) as e:
+        sma.plan(*args, num_cus=256, layout="bshd")
+    assert e.value.status == UNSUP
+    assert sma.workspace_bytes(*args, num_cus=256, layout="bshd") == 0
+    # fp32: the in-workgroup key split needs its per-head span under 2 GiB; with the [B,S,H,d]
+    # stride the automatic choice moves to the 128-row kernel, whose split needs a workspace
+    a32 = (F32, 1, 64, 256, 140000, 64, False)
+    p_bhsd = sma.plan(*a32, num_cus=256)
+    p_bshd = sma.plan(*a32, num_cus=256, layout="bshd")
+    assert p_bhsd.kernel == sma.SMA_KERNEL_F32_KSPLIT and p_bhsd.workspace_bytes == 0
+    assert p_bshd.kernel == sma.SMA_KERNEL_F32_QBLOCK and p_bshd.nsplit > 1
+    assert sma.workspace_bytes(*a32, num_cus=256, layout="bshd") == p_bshd.workspace_bytes > 0
+    with pytest.raises(ValueError):
+        sma.plan(*a32, layout="sbhd")
 
 
 def test_product_path_fails_loudly_without_library(tmp_path):
@@ -213,7 +251,8 @@ def test_plan_rejects():
             assert e.value.status == UNSUP
         assert P(F32, 1, 1, 8, 8, d, False, kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=1).nsplit == 1
     lib = sma.library()
-    assert lib.sma_attention_fwd_plan(F32, 1, 1, 8, 8, 64, 0, -1, 0, 256, None) == NULLP
+    assert lib.sma_attention_fwd_plan(F32, 1, 1, 8, 8, 64, 0, 0, -1, 0, 256, None) == NULLP
+    assert lib.sma_attention_fwd_plan(F32, 1, 1, 8, 8, 64, 0, 2, -1, 0, 256, ctypes.byref(sma.Plan())) == INVAL
 
 
 def _ex(plan, q=Q, o=O, idt=F32, ws=None, wsb=0, layout=0, H=2, skv=128):

@@ -1,8 +1,9 @@
 """HIP path vs the CPU oracle, element by element, through the C ABI.
 
-Small and ragged shapes compare every output; the full-size workloads run in
-the benchmark's launch configuration and compare sampled rows, plus
-properties that hold at any size.
+Small and ragged shapes compare every output. The full-size workloads run in
+the benchmark's launch configuration and compare every output against the
+whole oracle run; sampled-row variants (and the 128-row fp32 kernel on the
+fp32 workloads) run alongside.
 """
 import functools
 import math
@@ -11,6 +12,7 @@ import numpy as np
 import pytest
 
 import gen
+import helpers
 import oracle
 from helpers import (check_parity, empty_rows, run_gpu, sample_rows, to_device, workload_case)
 
@@ -137,6 +139,25 @@ def test_parity_full_size_sampled(name):
     er = empty_rows(sq, skv, w.causal)
     if er.any():
         assert np.all(o.reshape(B * H, sq, -1)[:, er] == 0.0)
+
+
+@pytest.mark.parametrize("name", ["f32_causal_b8h16_s2048_d128", "f32_cross_b2h32_q256_kv4096_d128",
+                                  "f32_cross_causal_b2h32_q256_kv4096_d128", "bf16_causal_b1h32_s16384_d128",
+                                  "f16_causal_b1h32_s16384_d128", "f32_causal_b8h16_s2048_d32",
+                                  "f32_causal_b8h16_s2048_d256"])
+@pytest.mark.timeout(600)  # the whole oracle takes about a minute per 16384-token workload
+def test_parity_full_size_whole(name):
+    """The large workloads at full size in the benchmark's launch configuration (the
+    library's own plan), every element of O and LSE against the whole oracle run: max-abs
+    and, for 16-bit inputs, relative L2 over the whole O tensor."""
+    w, vals, bits = workload_case(name)
+    o, lse = run_gpu(*to_device(vals, bits, w.dtype), w.scale, w.causal)
+    o_ref, lse_ref = oracle.attention_fwd(*vals, w.scale, w.causal)
+    stats = check_parity(o, lse, o_ref, lse_ref, w.dtype, f"{name} whole")
+    line = (f"{name}: all {o.size} outputs, max_abs {stats['max_abs']:.3e}, rel_l2 "
+            f"{stats['rel_l2']:.3e}, lse_rel {stats['lse_rel']:.3e}")
+    helpers.SUMMARY.append(line)
+    print(line, flush=True)
 
 
 # ------------------------------------------------------------------ edge cases
@@ -328,6 +349,51 @@ def test_non_default_stream(dtype):
     check_parity(o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), o_ref,
                  lse_ref, dtype, "stream")
     assert torch.equal(o2, o * 2.0)
+
+
+def _segment_stream(torch, ptr):
+    """The stream the caching allocator holds the block at `ptr` for."""
+    for seg in torch.cuda.memory_snapshot():
+        if seg["address"] <= ptr < seg["address"] + seg["total_size"]:
+            return seg["stream"]
+    raise AssertionError("pointer not in any allocator segment")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stream_argument_allocates_on_the_launch_stream(dtype):
+    """With stream= other than the current stream, the outputs and the workspace (a forced key
+    split, and a mask's packed bits) are allocated on the launch stream, so the caching
+    allocator cannot hand the freed workspace to work queued on the current stream while the
+    kernels still use it. The side stream is held back by a sleep while the current stream
+    allocates and fills blocks of the workspace's size."""
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    (q, k, v), bits = _case(41, 2, 2, 300, 1100, 64, dtype)
+    tq, tk, tv = to_device((q, k, v), bits, dtype)
+    mask_np = gen.bernoulli_mask(41, (1, 1, 300, 1100), 0.7)
+    tmask = torch.from_numpy(mask_np).to("cuda")
+    kern = sma.SMA_KERNEL_F32_QBLOCK if dtype == "f32" else sma.SMA_KERNEL_BF16_QBLOCK
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    results = []
+    for mask in (None, tmask):
+        with torch.cuda.stream(s):
+            torch.cuda._sleep(20_000_000)
+        o, lse = sma.attention_fwd(tq, tk, tv, scale=0.125, causal=True, return_lse=True, stream=s,
+                                   kernel=kern, nsplit=3, mask=mask)
+        junk = [torch.full((1 << 20,), float("nan"), device="cuda") for _ in range(8)]
+        assert _segment_stream(torch, o.data_ptr()) == s.cuda_stream
+        assert _segment_stream(torch, lse.data_ptr()) == s.cuda_stream
+        results.append((o, lse, junk))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, 0.125, True)
+    m_ref, mlse_ref = oracle.attention_fwd_masked(q, k, v, mask_np, 0.125, True)
+    for (o, lse, _), (r, lr), lab in zip(results, ((o_ref, lse_ref), (m_ref, mlse_ref)),
+                                         ("split", "masked split")):
+        check_parity(o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), r,
+                     lr, dtype, f"side stream {lab}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
