@@ -67,7 +67,9 @@ typedef enum {
                                 or more, grid limit */
   SMA_ERR_MISALIGNED = 4,    /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
   SMA_ERR_ALIASING = 5,      /* o or lse overlaps q, k, v, the workspace, or each other */
-  SMA_ERR_HIP = 6            /* the HIP runtime reported an error (device query or launch) */
+  SMA_ERR_HIP = 6,           /* the HIP runtime reported an error (device query or launch) */
+  SMA_ERR_SCRATCH = 7        /* sma_attention_fwd_noalloc: the requested key split needs more
+                                than its device scratch (SMA_NOALLOC_SCRATCH_BYTES) */
 } sma_status;
 
 /* Memory layout of q, k, v and o (lse is always [B,H,Sq]). Both are dense and
@@ -206,6 +208,35 @@ int sma_attention_fwd_layout(const void* q, const void* k, const void* v, void* 
                              int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
                              size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ no allocation
+ *
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): sma_attention_fwd_layout
+ * with an optional explicit plan (as sma_attention_fwd_ex), whose key-split
+ * partials go to a device array of SMA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on until the process ends, instead of a caller
+ * workspace. It allocates nothing: no hipMalloc, no hipFree, no allocating
+ * library call.
+ *
+ *   plan   NULL: the library's plan (every automatic plan on a 256-CU GPU fits
+ *          the scratch; one that would not runs without a key split, which stays
+ *          correct). An explicit plan whose split needs more than the scratch ->
+ *          SMA_ERR_SCRATCH, before anything is launched.
+ *
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ * partials (nothing in it needs to start at zero: each call writes every
+ * partial it reads). Calls on one stream are ordered; calls that may overlap on
+ * one GPU (other streams, other host threads) race on the scratch and must be
+ * serialised by the caller. Results are bitwise those of sma_attention_fwd_ex
+ * with the same plan. Other arguments, errors and asynchrony as for
+ * sma_attention_fwd_ex. */
+#define SMA_NOALLOC_SCRATCH_BYTES (72u * 1024u * 1024u)
+
+int sma_attention_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
+                              size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
+                              const sma_plan* plan, void* stream);
 
 /* ------------------------------------------------------------------ hard mask
  *

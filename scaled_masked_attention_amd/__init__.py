@@ -29,7 +29,9 @@ KERNEL_NAMES = {SMA_KERNEL_F32_QBLOCK: "f32_qblock", SMA_KERNEL_F32_KSPLIT: "f32
                 SMA_KERNEL_BF16_QBLOCK: "bf16_qblock"}
 STATUS_NAMES = {0: "SMA_OK", 1: "SMA_ERR_NULL_POINTER", 2: "SMA_ERR_INVALID_VALUE",
                 3: "SMA_ERR_UNSUPPORTED", 4: "SMA_ERR_MISALIGNED", 5: "SMA_ERR_ALIASING",
-                6: "SMA_ERR_HIP"}
+                6: "SMA_ERR_HIP", 7: "SMA_ERR_SCRATCH"}
+SMA_ERR_SCRATCH = 7
+NOALLOC_SCRATCH_BYTES = 72 * 1024 * 1024  # SMA_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -83,6 +85,8 @@ def library():
         lib.sma_attention_fwd_ex.restype = ctypes.c_int
         lib.sma_attention_fwd_layout.argtypes = fwd[:14] + [ctypes.c_int] + fwd[14:17]
         lib.sma_attention_fwd_layout.restype = ctypes.c_int
+        lib.sma_attention_fwd_noalloc.argtypes = fwd[:14] + [ctypes.c_int, ctypes.POINTER(Plan), vp]
+        lib.sma_attention_fwd_noalloc.restype = ctypes.c_int
         lib.sma_attention_fwd_masked.argtypes = (fwd[:5] + [vp, sz, sz] + fwd[5:14] + [ctypes.c_int] +
                                                  fwd[14:16] + [ctypes.POINTER(Plan), vp, vp, vp])
         lib.sma_attention_fwd_masked.restype = ctypes.c_int
@@ -197,6 +201,18 @@ def attention_fwd_ex_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dtype,
                                           int(bool(causal)), int(layout), ws_ptr, ws_bytes,
                                           ctypes.byref(plan_) if plan_ is not None else None,
                                           stream, event_before, event_after))
+
+
+def attention_fwd_noalloc_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype, o_dtype, batch, heads,
+                              seq_q, seq_kv, head_dim, scale, causal, plan_, stream,
+                              layout=SMA_LAYOUT_BHSD) -> None:
+    """sma_attention_fwd_noalloc: no workspace argument, nothing allocated (the key split uses
+    the library's device scratch); plan_ a Plan or None. Raises SMAError."""
+    _raise(library().sma_attention_fwd_noalloc(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, in_dtype,
+                                               o_dtype, batch, heads, seq_q, seq_kv, head_dim,
+                                               float(scale), int(bool(causal)), int(layout),
+                                               ctypes.byref(plan_) if plan_ is not None else None,
+                                               stream))
 
 
 def attention_fwd_masked_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, mask_ptr, mask_batches, mask_heads,

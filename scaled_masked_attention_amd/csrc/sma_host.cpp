@@ -283,11 +283,43 @@ int check_mask(const Shape& s, const MaskArg& m, const void* o, const float* lse
 }
 
 
+// Device scratch of sma_attention_fwd_noalloc: the key-split partials (O and
+// log2-unit LSE per split and row). Every automatic plan on a 256-CU device fits
+// (at most (2*slots - 2) split-blocks of 256 rows x 129 floats, about 64.5 MiB).
+// In host code `scratch` only names the variable: its device address, one per
+// GPU, comes from hipGetSymbolAddress (scratch_address below).
+constexpr size_t kScratchBytes = size_t(SMA_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch`, looked up once per device with that
+// device current.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SMA_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess ? ptr : nullptr;
+  });
+  if (!g_scratch[dev]) return SMA_ERR_HIP;
+  *out = g_scratch[dev];
+  return SMA_OK;
+}
+
+// use_scratch: the workspace is the device's `scratch` (workspace and
+// workspace_bytes are ignored); an explicit split that does not fit it is
+// SMA_ERR_SCRATCH.
 int fwd_core(const void* q, const void* k, const void* v, void* o, float* lse, int in_dtype,
              int o_dtype, size_t batch, size_t heads, size_t seq_q, size_t seq_kv, size_t head_dim,
              double scale, int causal, int layout, const MaskArg& mask, void* workspace,
              size_t workspace_bytes, const sma_plan* plan, void* stream, void* event_before,
-             void* event_after) {
+             void* event_after, bool use_scratch = false) {
+  if (use_scratch) {
+    workspace = nullptr;
+    workspace_bytes = 0;
+  }
   Shape sh;
   int st = validate_all(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv, head_dim,
                         scale, workspace, workspace_bytes, &sh, layout);
@@ -310,6 +342,12 @@ int fwd_core(const void* q, const void* k, const void* v, void* o, float* lse, i
   }
   if (sh.rows == 0) return SMA_OK;
   // The packed mask occupies the front of the workspace; a key split uses the rest.
+  if (use_scratch) {
+    if (mask.mask) return SMA_ERR_INVALID_VALUE;
+    st = scratch_address(&workspace);
+    if (st != SMA_OK) return st;
+    workspace_bytes = kScratchBytes;
+  }
   const size_t bits_bytes = mask_bits_bytes(sh, mask);
   if (masked && (!workspace || workspace_bytes < bits_bytes)) return SMA_ERR_INVALID_VALUE;
   void* split_ws = workspace ? static_cast<char*>(workspace) + bits_bytes : nullptr;
@@ -320,7 +358,8 @@ int fwd_core(const void* q, const void* k, const void* v, void* o, float* lse, i
   Plan p;
   if (plan) {
     p = plan_for(sh, plan->kernel, (size_t)plan->nsplit, cus);
-    if (p.nsplit > 1 && (!split_ws || split_ws_bytes < p.ws_bytes)) return SMA_ERR_INVALID_VALUE;
+    if (p.nsplit > 1 && (!split_ws || split_ws_bytes < p.ws_bytes))
+      return use_scratch ? SMA_ERR_SCRATCH : SMA_ERR_INVALID_VALUE;
     if (p.nwg > kMaxWorkgroups) return SMA_ERR_UNSUPPORTED;
   } else {
     p = auto_plan(sh, cus);
@@ -534,6 +573,14 @@ int sma_attention_fwd(const void* q, const void* k, const void* v, void* o, floa
   return sma_attention_fwd_ex(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv,
                               head_dim, scale, causal, SMA_LAYOUT_BHSD, workspace, workspace_bytes,
                               nullptr, stream, nullptr, nullptr);
+}
+
+int sma_attention_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int in_dtype, int o_dtype, size_t batch, size_t heads, size_t seq_q,
+                              size_t seq_kv, size_t head_dim, double scale, int causal, int layout,
+                              const sma_plan* plan, void* stream) {
+  return fwd_core(q, k, v, o, lse, in_dtype, o_dtype, batch, heads, seq_q, seq_kv, head_dim, scale,
+                  causal, layout, MaskArg{}, nullptr, 0, plan, stream, nullptr, nullptr, true);
 }
 
 int sma_attention_fwd_layout(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -916,6 +963,9 @@ const char* sma_status_string(int status) {
     case SMA_ERR_MISALIGNED: return "SMA_ERR_MISALIGNED: q/k/v/o/workspace need 16-byte and lse 4-byte alignment";
     case SMA_ERR_ALIASING: return "SMA_ERR_ALIASING: an output overlaps an input or another output";
     case SMA_ERR_HIP: return "SMA_ERR_HIP: the HIP runtime reported an error";
+    case SMA_ERR_SCRATCH:
+      return "SMA_ERR_SCRATCH: the plan's key split needs more than the no-allocation entry "
+             "point's device scratch (SMA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown sma status";
   }
 }

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert sma.abi_version() == 3
-    for st in range(7):
+    for st in range(8):
         assert sma.status_string(st).startswith(sma.STATUS_NAMES[st])
     assert sma.status_string(99) == "unknown sma status"
 
