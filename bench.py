@@ -110,18 +110,20 @@ def host_cpu_model() -> str:
 
 
 class ClockSampler:
-    """Engine (SCLK) and memory (MCLK) clocks of the GPU in use, read through the amd-smi
-    library from a host thread every few milliseconds while the timed loop runs. Values
-    are MHz; SCLK is the mean over the XCDs of each sample."""
+    """Engine (SCLK) and memory (MCLK) clocks of the GPU in use, from the amd-smi library's
+    GPU metrics table, read by a host thread every few milliseconds. The firmware refreshes
+    that table about once a second, so only reads that carry a new table (a new
+    system_clock_counter) count as samples. Values are MHz; SCLK is the mean over the XCDs."""
 
     NA = 0xFFFF  # amd-smi's marker for a field the firmware does not report
 
-    def __init__(self, period_s: float = 0.004):
+    def __init__(self, period_s: float = 0.01):
         self.period_s = period_s
         self.samples, self.mclk = [], []
         self.error = None
         self.field = None
         self.handle = None
+        self.last_stamp = None
         self._stop = None
         self._thread = None
         try:
@@ -143,18 +145,21 @@ class ClockSampler:
                         break
             if self.handle is None:
                 raise RuntimeError(f"no amd-smi handle matches the device ({len(handles)} found)")
-            self._read()  # fail here, not in the thread, if the metrics are unreadable
-            self.samples.clear()
-            self.mclk.clear()
+            self._read(first=True)  # fail here, not in the thread, if the metrics are unreadable
         except Exception as e:  # noqa: BLE001 - report, never fail the bench for it
             self.error = f"{type(e).__name__}: {e}"
 
-    def _read(self):
+    def _read(self, first=False):
         m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        stamp = m.get("system_clock_counter")
+        if first or stamp == self.last_stamp:
+            self.last_stamp = stamp  # the table on entry describes the time before the run
+            return
 
         def ok(x):
             return isinstance(x, (int, float)) and 0 < x < self.NA
 
+        self.last_stamp = stamp
         xs = [x for x in (m.get("current_gfxclks") or []) if ok(x)]
         if xs:
             self.field = "current_gfxclks (mean over XCDs)"
@@ -162,9 +167,6 @@ class ClockSampler:
         elif ok(m.get("current_gfxclk")):
             self.field = "current_gfxclk"
             self.samples.append(float(m["current_gfxclk"]))
-        elif ok(m.get("average_gfxclk_frequency")):
-            self.field = "average_gfxclk_frequency"
-            self.samples.append(float(m["average_gfxclk_frequency"]))
         u = m.get("current_uclk")
         if ok(u):
             self.mclk.append(float(u))
@@ -188,21 +190,43 @@ class ClockSampler:
         self._thread = threading.Thread(target=loop, daemon=True)
         self._thread.start()
 
+    def fresh(self) -> int:
+        return len(self.samples)
+
     def stop(self) -> dict:
         if self._thread is not None:
             self._stop.set()
             self._thread.join()
-        out = {"source": "amd-smi gpu metrics, sampled during the timed loop"}
-        if self.samples:
-            out.update(sclk_mhz_mean=round(float(np.mean(self.samples)), 1),
-                       sclk_mhz_min=round(float(np.min(self.samples)), 1),
-                       sclk_mhz_max=round(float(np.max(self.samples)), 1),
-                       sclk_field=self.field, samples=len(self.samples))
+        out = {"source": "amd-smi GPU metrics (refreshed about once a second), read while the "
+                         "measured step runs"}
+        # The first refreshed table can still average in time from before the run.
+        xs = self.samples[1:] if len(self.samples) > 1 else self.samples
+        if xs:
+            out.update(sclk_mhz_mean=round(float(np.mean(xs)), 1),
+                       sclk_mhz_min=round(float(np.min(xs)), 1),
+                       sclk_mhz_max=round(float(np.max(xs)), 1),
+                       sclk_field=self.field, samples=len(xs))
         if self.mclk:
-            out["mclk_mhz_mean"] = round(float(np.mean(self.mclk)), 1)
+            out["mclk_mhz_mean"] = round(float(np.mean(self.mclk[1:] or self.mclk)), 1)
         if self.error or not self.samples:
-            out["error"] = self.error or "no clock samples"
+            out["error"] = self.error or "no refreshed metrics table during the run"
         return out
+
+
+def clock_window(sampler, step, seconds: float = 3.0, min_samples: int = 3) -> float:
+    """After a timed loop too short for the metrics table to refresh a few times, keep
+    running the same step, untimed, until `min_samples` refreshed tables have been read or
+    `seconds` have passed; returns the wall seconds spent."""
+    import torch
+
+    if sampler.error:
+        return 0.0
+    t0 = time.perf_counter()
+    while sampler.fresh() < min_samples and time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    return round(time.perf_counter() - t0, 2)
 
 
 def with_host(baseline: dict) -> dict:
@@ -457,7 +481,9 @@ def bench_bwd(args, w, name):
         sma.attention_bwd_raw(*call, e_pre[i], e_kv[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    window = clock_window(clocks, lambda: sma.attention_bwd_raw(*call))
     clock_info = clocks.stop()
+    clock_info["untimed_seconds_after_the_timed_loop"] = window
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     launches = [ev.elapsed_ms(e_pre[i], e_kv[i]) for i in range(args.steps)]
     k_avg = sum(launches) / args.steps
@@ -605,7 +631,9 @@ def bench_rows(args, w):
     ev.record(e1, stream.cuda_stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    window = clock_window(clocks, step)
     clock_info = clocks.stop()
+    clock_info["untimed_seconds_after_the_timed_loop"] = window
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     k_avg = ev.elapsed_ms(e0, e1) / args.steps
     ev.destroy(e0)
@@ -758,7 +786,9 @@ def main():
             ev.record(marks[i + 1], sptr)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    window = clock_window(clocks, run)
     clock_info = clocks.stop()
+    clock_info["untimed_seconds_after_the_timed_loop"] = window
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     if per_launch:
         launches = [ev.elapsed_ms(ev_a[i], ev_b[i]) for i in range(args.steps)]

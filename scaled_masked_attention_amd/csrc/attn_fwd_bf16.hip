@@ -312,7 +312,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
     for (int kb = 0; kb < G::kKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    {  // lanes m and m + 32 hold the two key halves of query m (a VALU swap, not an LDS round trip)
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float tmax = mx == -INFINITY ? -INFINITY : mx * c;
     if (__any(tmax > m_run + kTau)) {
       const float m_new = fmaxf(m_run, tmax);

@@ -190,7 +190,11 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
       float mx = tv[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, tv[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      {  // lanes m and m + 32 hold the two key halves of query m (VALU swap, no LDS round trip)
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
       const bool raise = mx > m_run + kTau;
       if (__any(raise)) {
         const float m_new = fmaxf(m_run, mx);
