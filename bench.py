@@ -213,13 +213,17 @@ class ClockSampler:
         return out
 
 
-def clock_window(sampler, step, seconds: float = 3.0, min_samples: int = 3) -> float:
+CLOCK_SECONDS = 3.0  # set from --clock-seconds
+
+
+def clock_window(sampler, step, seconds: float = None, min_samples: int = 3) -> float:
     """After a timed loop too short for the metrics table to refresh a few times, keep
     running the same step, untimed, until `min_samples` refreshed tables have been read or
     `seconds` have passed; returns the wall seconds spent."""
     import torch
 
-    if sampler.error:
+    seconds = CLOCK_SECONDS if seconds is None else seconds
+    if sampler.error or seconds <= 0:
         return 0.0
     t0 = time.perf_counter()
     while sampler.fresh() < min_samples and time.perf_counter() - t0 < seconds:
@@ -679,9 +683,14 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=100.0,
                     help="wall milliseconds of untimed steps before the warmup steps (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--clock-seconds", type=float, default=3.0,
+                    help="untimed run of the step after the timed loop while engine-clock samples "
+                         "are still missing (0: none; counter-collection runs use 0)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
+    global CLOCK_SECONDS
+    CLOCK_SECONDS = args.clock_seconds
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(multi-GPU sharding of the attention path is not implemented)", file=sys.stderr)
