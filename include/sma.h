@@ -251,11 +251,15 @@ int sma_attention_fwd_noalloc(const void* q, const void* k, const void* v, void*
  *                  contiguous; mask_batches is 1 or batch and mask_heads 1 or
  *                  heads (1 broadcasts the mask over that dimension). Must not
  *                  overlap o, lse or the workspace (ALIASING).
- *   workspace      required: the mask packed to one bit per pair (4 bytes per
- *                  32 keys of a row, 256-byte aligned) comes first, else
- *                  INVALID_VALUE; a key split across workgroups uses the bytes
- *                  after it (too few of them only disables the library's split,
- *                  as for sma_attention_fwd). sma_attention_fwd_masked_workspace_bytes
+ *   workspace      required: the mask packed to one bit per pair comes first,
+ *                  else INVALID_VALUE: for fp32 inputs 4 bytes per 32 keys of a
+ *                  row; for 16-bit inputs 4 bytes per key of each 32-row block
+ *                  (keys rounded up to 64) plus 4 bytes per 64-key tile of each
+ *                  block, which class the tile as admitting nothing (skipped),
+ *                  everything (run unmasked) or a mix; each part 256-byte
+ *                  aligned. A key split across workgroups uses the bytes after
+ *                  it (too few of them only disables the library's split, as for
+ *                  sma_attention_fwd). sma_attention_fwd_masked_workspace_bytes
  *                  gives both.
  *   plan           as for sma_attention_fwd_ex: every kernel applies the mask.
  * Everything else as for sma_attention_fwd_ex. mask NULL with nonzero

@@ -80,6 +80,14 @@ struct BGeom {
   static_assert(kLoadsPerThread >= 1 && kLoadsPerThread * kThreads == kTileChunks, "tile split");
 };
 
+// A load through the constant address space: with a wave-uniform address it
+// becomes a scalar (s_load) load into SGPRs. Only for memory no kernel of the
+// launch writes.
+template <typename T>
+__device__ __forceinline__ T scalar_load(const void* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 constexpr float kTau = 8.0f;  // lazy running-max threshold, log2 units (see the fp32 kernel)
 
 __device__ __forceinline__ int swap_bits_2_3(int r) {
@@ -110,10 +118,6 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   using V8 = typename H::V8;
   __shared__ __attribute__((aligned(16))) u32x4 k_lds[G::kSlots][G::kTileChunks];
   __shared__ __attribute__((aligned(16))) u32x4 v_lds[G::kSlots][G::kTileChunks];
-  // With a hard mask: per ring slot, each wave's two mask words (64 keys) for
-  // its 32 rows, word w of row r at [w * 32 + r].
-  __shared__ uint32_t mask_lds[MASKED ? G::kSlots : 1][MASKED ? G::kWaves : 1][64];
-  constexpr int kMaskOps = MASKED ? 1 : 0;  // loads per wave per tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -178,18 +182,22 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
                               16u * (unsigned)(pc ^ k_swz<D>(rho0));
   const unsigned v_lane_ofs = (unsigned)rho0 * kv_row + 16u * (unsigned)(pc ^ v_swz<D>(rho0));
 
-  __amdgpu_buffer_rsrc_t m_rsrc;
-  if (MASKED)
-    m_rsrc = raw_buffer(a.mask_bits + head_offset(t.bh, a.heads, a.mbits_sb, a.mbits_sh),
-                        (unsigned)a.seq_q * (unsigned)a.mask_words * 4u);
+  // A hard mask, packed by columns (MaskColArgs): this wave's 32-row block has
+  // one row-bit word per key and a class per 64-key tile (0 nothing admitted,
+  // 1 everything admitted, 2 mixed). Both are read with scalar loads: a tile
+  // that admits nothing is skipped, one that admits everything runs unmasked,
+  // and in a mixed tile two key words side by side are the 64-lane mask of one
+  // score register, applied with a single v_cndmask.
+  const uint32_t* mcols = nullptr;
+  const uint32_t* mcls = nullptr;
+  if (MASKED) {
+    const int64_t rb = qw0 / 32;
+    mcols = a.mask_bits + head_offset(t.bh, a.heads, a.mbits_sb, a.mbits_sh) + rb * a.mask_words;
+    mcls = a.mask_cls + head_offset(t.bh, a.heads, a.mcls_sb, a.mcls_sh) + rb * a.mask_tiles;
+  }
   auto issue_tile = [&](int32_t T) {
     const unsigned row0 = (unsigned)(ks + T * G::kK);
     const int slot = T % G::kSlots;
-    if (MASKED)  // words (ks + 64T)/32 + {0, 1} of this wave's rows (rows past seq_q read as 0)
-      dma_load_x1(m_rsrc,
-                  ((unsigned)(qw0 + (lane & 31)) * (unsigned)a.mask_words + row0 / 32u +
-                   (unsigned)(lane >> 5)) * 4u,
-                  lds_address(&mask_lds[MASKED ? slot : 0][MASKED ? wave : 0][0]));
 #pragma unroll
     for (int u = 0; u < G::kLoadsPerThread; ++u) {
       const int base = (u * G::kWaves + wave) * 64;
@@ -249,7 +257,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
 
   // Scores, lazy running max and probabilities of tile T (in ring slot
   // `slot`); returns the bf16 probabilities for the PV product.
-  auto scores_and_p = [&](int32_t T, int slot, V8 (&pb)[G::kKB][2]) {
+  auto scores_and_p = [&](int32_t T, int slot, V8 (&pb)[G::kKB][2], uint32_t cls) {
     const int32_t j0 = ks + T * G::kK;
     // The k-steps of the key blocks interleave, and the K operands of step
     // st + kPf are read before the MFMAs of step st, so that every LDS read has
@@ -284,26 +292,38 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Boundary tiles (the causal diagonal, the end of the keys, a hard mask):
-    // excluded scores become -inf, so that they enter neither the max nor the
-    // sum (2^-inf = 0; c > 0). The empty asm keeps the bound, and with it the
+    // Boundary tiles (the causal diagonal, the end of the keys): excluded
+    // scores become -inf, so that they enter neither the max nor the sum
+    // (2^-inf = 0; c > 0). The empty asm keeps the bound, and with it the
     // comparisons, inside this branch instead of on every tile.
-    if (MASKED || j0 + G::kK > wave_lo) {
+    if (j0 + G::kK > wave_lo) {
       int32_t rel = lim - j0 - 8 * lh;  // key 32kb + 16(r/8) + r%8 allowed iff < rel
       asm volatile("" : "+v"(rel));
 #pragma unroll
-      for (int kb = 0; kb < G::kKB; ++kb) {
-        // Key 32kb + 16(r/8) + 8h + r%8 of the tile: under the causal/length bound, and
-        // admitted by the mask (bit 16(r/8) + 8h + r%8 of word kb).
-        const uint32_t mword =
-            MASKED ? mask_lds[MASKED ? slot : 0][MASKED ? wave : 0][32 * kb + lm] : ~0u;
+      for (int kb = 0; kb < G::kKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool ok = (32 * kb + 16 * (r / 8) + (r % 8) < rel) &&
-                          (!MASKED || ((mword >> (16 * (r / 8) + 8 * lh + (r % 8))) & 1u));
-          sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
+        for (int r = 0; r < 16; ++r)
+          sacc[kb][r] = (32 * kb + 16 * (r / 8) + (r % 8) < rel) ? sacc[kb][r] : -INFINITY;
+    }
+    // A mixed tile of the hard mask: score register r of key block kb holds key
+    // 16(r/8) + r%8 (lanes 0-31) and that key + 8 (lanes 32-63) of the block;
+    // their two column words, stored side by side, are its lane mask.
+    if (MASKED && cls == 2u) {
+      const float ninf = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          typedef unsigned u32x16 __attribute__((ext_vector_type(16)));
+          const u32x16 w = scalar_load<u32x16>(mcols + (j0 + 32 * kb + 16 * g));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint64_t lanes = (uint64_t)w[2 * i] | ((uint64_t)w[2 * i + 1] << 32);
+            float x = sacc[kb][8 * g + i];
+            asm("v_cndmask_b32_e64 %0, %1, %0, %2" : "+v"(x) : "v"(ninf), "s"(lanes));
+            sacc[kb][8 * g + i] = x;
+          }
         }
-      }
     }
 
     // Row max of the raw scores (scale > 0 after the sign fold).
@@ -356,7 +376,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   if (ntiles > 0) issue_tile(0);
   if (ntiles > 1) issue_tile(1);
   for (int32_t T = 0; T < ntiles; ++T) {
-    if (T + 1 < ntiles) wait_vmcnt<G::kLoadsPerTile + kMaskOps>();
+    if (T + 1 < ntiles) wait_vmcnt<G::kLoadsPerTile>();
     else wait_vmcnt<0>();
     __syncthreads();
     if (T + 2 < ntiles) issue_tile(T + 2);
@@ -365,9 +385,13 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
       late_pending = false;
     }
     const int slot = T % G::kSlots;
-    if (wave_live && ks + T * G::kK < wave_hi) {
+    // The tile's mask class (1 without a mask); a tile the mask closes is skipped.
+    uint32_t cls = 1u;
+    if (MASKED && wave_live && ks + T * G::kK < wave_hi)
+      cls = scalar_load<uint32_t>(mcls + (ks / G::kK + T));
+    if (wave_live && ks + T * G::kK < wave_hi && cls != 0u) {
       V8 pb[G::kKB][2];
-      scores_and_p(T, slot, pb);
+      scores_and_p(T, slot, pb, cls);
       if (late) {
 #pragma unroll
         for (int kb = 0; kb < G::kKB; ++kb)

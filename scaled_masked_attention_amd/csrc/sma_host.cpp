@@ -261,10 +261,31 @@ struct MaskArg {
 
 size_t mask_words(size_t seq_kv) { return (seq_kv + 31) / 32; }
 
-// Workspace bytes for the packed mask bits (0 without a mask).
-size_t mask_bits_bytes(const Shape& s, const MaskArg& m) {
+// The column packing of the 16-bit kernel: 32-row blocks and key positions
+// (keys rounded up to the 64-key tile).
+size_t mask_row_blocks(size_t seq_q) { return (seq_q + 31) / 32; }
+size_t mask_key_positions(size_t seq_kv) { return round_up(seq_kv, 64); }
+size_t mask_cols_bytes(const Shape& s, const MaskArg& m) {
+  return round_up(m.batches * m.heads * mask_row_blocks(s.seq_q) * mask_key_positions(s.seq_kv) * 4,
+                  kWsAlign);
+}
+
+// Workspace bytes of the mask packed as row words (the fp32 forward kernels
+// and every backward kernel); 0 without a mask.
+size_t mask_rows_bytes(const Shape& s, const MaskArg& m) {
   if (!m.mask) return 0;
   return round_up(m.batches * m.heads * s.seq_q * mask_words(s.seq_kv) * 4, kWsAlign);
+}
+
+// Workspace bytes for the forward's packed mask (0 without a mask): row words
+// for the fp32 kernels, column words and tile classes for the 16-bit kernel.
+size_t mask_bits_bytes(const Shape& s, const MaskArg& m) {
+  if (!m.mask) return 0;
+  if (s.in_dtype != SMA_DTYPE_F32)
+    return mask_cols_bytes(s, m) +
+           round_up(m.batches * m.heads * mask_row_blocks(s.seq_q) * (mask_key_positions(s.seq_kv) / 64) * 4,
+                    kWsAlign);
+  return mask_rows_bytes(s, m);
 }
 
 int check_mask(const Shape& s, const MaskArg& m, const void* o, const float* lse, const void* ws,
@@ -407,7 +428,29 @@ int fwd_core(const void* q, const void* k, const void* v, void* o, float* lse, i
   const bool c = causal != 0;
   const int d = (int)head_dim;
   hipError_t e;
-  if (masked && seq_kv > 0) {
+  if (masked && seq_kv > 0 && in_dtype != SMA_DTYPE_F32) {
+    sma::MaskColArgs mc{};
+    mc.mask = static_cast<const unsigned char*>(mask.mask);
+    mc.cols = static_cast<uint32_t*>(workspace);
+    mc.cls = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + mask_cols_bytes(sh, mask));
+    mc.slabs = (int64_t)(mask.batches * mask.heads);
+    mc.seq_q = (int32_t)seq_q;
+    mc.seq_kv = (int32_t)seq_kv;
+    mc.nrb = (int32_t)mask_row_blocks(seq_q);
+    mc.kpad = (int32_t)mask_key_positions(seq_kv);
+    e = sma::launch_mask_pack_cols(mc, s);
+    if (e != hipSuccess) return SMA_ERR_HIP;
+    a.mask_bits = mc.cols;
+    a.mask_words = mc.kpad;
+    const int64_t slab = (int64_t)mc.nrb * mc.kpad;
+    a.mbits_sh = mask.heads == heads && heads > 1 ? slab : 0;
+    a.mbits_sb = mask.batches == batch && batch > 1 ? (int64_t)mask.heads * slab : 0;
+    a.mask_cls = mc.cls;
+    a.mask_tiles = mc.kpad / 64;
+    const int64_t cslab = (int64_t)mc.nrb * a.mask_tiles;
+    a.mcls_sh = mask.heads == heads && heads > 1 ? cslab : 0;
+    a.mcls_sb = mask.batches == batch && batch > 1 ? (int64_t)mask.heads * cslab : 0;
+  } else if (masked && seq_kv > 0) {
     sma::MaskPackArgs mp{};
     mp.mask = static_cast<const unsigned char*>(mask.mask);
     mp.bits = static_cast<uint32_t*>(workspace);
@@ -691,7 +734,7 @@ int check_bwd_mask(BwdShape* b, const MaskArg& m, const float* dq, const float* 
   if (n > (size_t(1) << 40)) return SMA_ERR_UNSUPPORTED;
   if (s.seq_q * mask_words(s.seq_kv) * 4 > (size_t(1) << 31)) return SMA_ERR_UNSUPPORTED;
   *bits_at = b->ws_bytes;
-  b->ws_bytes += mask_bits_bytes(s, m);
+  b->ws_bytes += mask_rows_bytes(s, m);
   if (overlap(dq, s.rows ? b->q32 : 0, m.mask, n) || overlap(dk, b->kv32, m.mask, n) ||
       overlap(dv, b->kv32, m.mask, n) || overlap(ws, ws ? b->ws_bytes : 0, m.mask, n))
     return SMA_ERR_ALIASING;
@@ -841,7 +884,7 @@ size_t sma_attention_bwd_masked_workspace_bytes(int in_dtype, size_t batch, size
   m.mask = &b;  // any non-null address: only the sizes matter here
   m.batches = mask_batches;
   m.heads = mask_heads;
-  return b.ws_bytes + mask_bits_bytes(b.s, m);
+  return b.ws_bytes + mask_rows_bytes(b.s, m);
 }
 
 // ---------------------------------------------------------------- row primitives

@@ -39,7 +39,31 @@ struct FwdArgs {
   const uint32_t* mask_bits;
   int32_t mask_words;
   int64_t mbits_sb, mbits_sh;
+  // The 16-bit kernel takes the mask packed by launch_mask_pack_cols instead:
+  // mask_bits is then the column words (mask_words = key positions per 32-row
+  // block, mbits_* slab strides in words) and mask_cls the per-tile classes
+  // (mask_tiles per 32-row block, mcls_* slab strides in words).
+  const uint32_t* mask_cls;
+  int32_t mask_tiles;
+  int64_t mcls_sb, mcls_sh;
 };
+
+// Column packing of a byte mask [slabs][seq_q][seq_kv] for the 16-bit kernel:
+// per slab and 32-row block rb, one 32-bit word per key j, bit i admitting key
+// j for row 32 rb + i (rows past seq_q admit, keys past seq_kv block). Words are
+// stored at position (j & ~15) | ((j & 7) << 1) | ((j >> 3) & 1) of the block's
+// kpad positions (kpad = seq_kv rounded up to 64), so that keys j and j + 8 of a
+// 16-key group sit side by side: a 64-lane mask for the 32x32 MFMA's score
+// layout. Each 64-key tile of each block gets a class: 0 nothing admitted, 1
+// everything admitted, 2 mixed.
+struct MaskColArgs {
+  const unsigned char* mask;
+  uint32_t* cols;     // [slabs][nrb][kpad]
+  uint32_t* cls;      // [slabs][nrb][kpad / 64]
+  int64_t slabs;
+  int32_t seq_q, seq_kv, nrb, kpad;
+};
+hipError_t launch_mask_pack_cols(const MaskColArgs& a, hipStream_t s);
 
 // Packing of a byte mask [mask_batches][mask_heads][seq_q][seq_kv] (nonzero
 // admits) into the bit words above, one slab per (mask batch, mask head).

@@ -190,3 +190,69 @@ def test_masked_zero_and_negative_scale_every_kernel(kern, scale):
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_fwd_masked(q, k, v, mask, scale, True)
     check_parity(_np(o), _np(lse), o_ref, lse_ref, dtype, f"mask {kern} scale={scale}")
+
+
+def _block_mask(seed, shape, sq, skv):
+    """A mask made of 32-row x 64-key blocks that admit nothing, admit everything, or are
+    random at density 0.5 (one third each, by a seeded draw), on the block grid the 16-bit
+    kernel classifies, so that every class meets ragged edges."""
+    nrb, ntk = (sq + 31) // 32, (skv + 63) // 64
+    kind = np.floor(gen.uniform24(seed, np.arange(int(np.prod(shape[:2])) * nrb * ntk,
+                                                  dtype=np.uint64)) * 3).reshape(shape[:2] + (nrb, ntk))
+    rnd = _mask(seed + 1, shape[:2] + (sq, skv), 0.5)
+    m = np.zeros(shape[:2] + (sq, skv), dtype=bool)
+    for r in range(nrb):
+        for t in range(ntk):
+            rs, ts = slice(32 * r, 32 * r + 32), slice(64 * t, 64 * t + 64)
+            k = kind[..., r, t][..., None, None]
+            m[..., rs, ts] = np.where(k == 1, True, np.where(k == 2, rnd[..., rs, ts], False))
+    return m.astype(np.uint8)
+
+
+@pytest.mark.parametrize("kern", ["bf16", "bf16-split2", "f16", "f32-ksplit"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 2, 300, 333), (1, 3, 257, 700), (1, 1, 64, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_block_structured_mask(shape, causal, kern):
+    """Whole 32x64 blocks that admit nothing (skipped by the 16-bit kernel), everything (its
+    unmasked path) or a random half (its per-register lane masks), per (batch, head)."""
+    import torch
+
+    import scaled_masked_attention_amd as sma
+    from helpers import to_device
+
+    dtype, kname, nsplit = KERNELS[kern]
+    B, H, sq, skv = shape
+    d = 128
+    (q, k, v), bits = gen.random_case(1500 + sq, (B, H, sq, d), (B, H, skv, d),
+                                      sigma_qk=1.0 if dtype == "f32" else 3.0, dtype=dtype)
+    mask = _block_mask(1501 + sq, (B, H), sq, skv)
+    tq, tk, tv = to_device((q, k, v), bits, dtype)
+    o, lse = sma.attention_fwd(tq, tk, tv, scale=1.0 / math.sqrt(d), causal=causal, return_lse=True,
+                               mask=torch.from_numpy(mask).to("cuda"),
+                               kernel=getattr(sma, "SMA_KERNEL_" + kname), nsplit=nsplit)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd_masked(q, k, v, mask, 1.0 / math.sqrt(d), causal)
+    check_parity(_np(o), _np(lse), o_ref, lse_ref, dtype, f"block mask {kern}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_all_ones_mask_is_bitwise_the_unmasked_16bit_kernel(dtype):
+    """Every tile of an all-ones mask is classed 'everything admitted', so the 16-bit kernel
+    runs its unmasked arithmetic: bit for bit the result without a mask."""
+    import torch
+
+    import scaled_masked_attention_amd as sma
+    from helpers import to_device
+
+    (q, k, v), bits = gen.random_case(1210, (2, 2, 300, 128), (2, 2, 333, 128), sigma_qk=3.0,
+                                      dtype=dtype)
+    tq, tk, tv = to_device((q, k, v), bits, dtype)
+    ones = torch.ones((1, 1, 300, 333), dtype=torch.uint8, device="cuda")
+    for causal in (False, True):
+        o1, l1 = sma.attention_fwd(tq, tk, tv, scale=0.09, causal=causal, return_lse=True, mask=ones,
+                                   kernel=sma.SMA_KERNEL_BF16_QBLOCK, nsplit=1)
+        o2, l2 = sma.attention_fwd(tq, tk, tv, scale=0.09, causal=causal, return_lse=True,
+                                   kernel=sma.SMA_KERNEL_BF16_QBLOCK, nsplit=1)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
