@@ -228,6 +228,8 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
     _w("f16_causal_b1h32_s16384_d128", "f16", 1, 32, 16384, 16384, 128, True, 1.0 / math.sqrt(128), 3.0, 1.0, 20261207),
     _w("f32_causal_b8h16_s2048_d32", "f32", 8, 16, 2048, 2048, 32, True, 1.0 / math.sqrt(32), 1.0, 1.0, 20261220),
     _w("f32_causal_b8h16_s2048_d256", "f32", 8, 16, 2048, 2048, 256, True, 1.0 / math.sqrt(256), 1.0, 1.0, 20261221),
+    _w("bf16_causal_b1h32_s16384_d32", "bf16", 1, 32, 16384, 16384, 32, True, 1.0 / math.sqrt(32), 3.0, 1.0, 20261222),
+    _w("bf16_causal_b1h32_s16384_d256", "bf16", 1, 32, 16384, 16384, 256, True, 1.0 / math.sqrt(256), 3.0, 1.0, 20261223),
 )}
 
 

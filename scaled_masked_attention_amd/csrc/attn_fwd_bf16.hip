@@ -60,24 +60,31 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
+// Geometry per head dim. At d = 256 a 32-row wave's O alone takes 128
+// registers, so the workgroup is 4 waves (one per SIMD, 512 registers each)
+// and tiles have 32 keys (64 KB of K and V per ring slot would not fit 4 slots).
+// At d = 32 a tensor's tile is 256 chunks: waves 0-3 copy K, waves 4-7 copy V.
 template <int D>
 struct BGeom {
-  static constexpr int kWaves = 8;
+  static constexpr int kWaves = D == 256 ? 4 : 8;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kQW = 32;                     // query rows per wave
   static constexpr int kQ = kWaves * kQW;            // query rows per workgroup
-  static constexpr int kK = kBF16KeysPerTile;        // keys per LDS tile (two 32-key blocks)
-  static constexpr int kKB = kK / 32;
+  static constexpr int kK = D == 256 ? kBF16D256KeysPerTile : kBF16KeysPerTile;  // keys per tile
+  static constexpr int kKB = kK / 32;                // 32-key blocks per tile
   static constexpr int kSlots = 4;                   // LDS ring of K/V tiles
   static constexpr int kChunksPerRow = D / 8;        // 16-byte chunks per K or V row
   static constexpr int kTileChunks = kK * kChunksPerRow;
-  static constexpr int kLoadsPerThread = kTileChunks / kThreads;  // per tensor and tile
-  static constexpr int kLoadsPerTile = 2 * kLoadsPerThread;       // K and V
+  static constexpr bool kSplitKV = kTileChunks < kThreads;      // half the waves per tensor
+  static constexpr int kCopyWaves = kSplitKV ? kWaves / 2 : kWaves;  // waves copying a tensor
+  static constexpr int kLoadsPerThread = kTileChunks / (64 * kCopyWaves);  // per copied tensor
+  static constexpr int kLoadsPerTile = kSplitKV ? kLoadsPerThread : 2 * kLoadsPerThread;
   static constexpr int kHalf = D / 2;
   static constexpr int kSteps = D / 16;              // QK^T k-steps (8 dims per lane half)
   static constexpr int kNch = D / 32;                // 32-wide output chunks
-  static_assert(kQ == kBF16QueriesPerWG, "planner geometry");
-  static_assert(kLoadsPerThread >= 1 && kLoadsPerThread * kThreads == kTileChunks, "tile split");
+  static_assert(kQ == (D == 256 ? kBF16D256QueriesPerWG : kBF16QueriesPerWG), "planner geometry");
+  static_assert(kLoadsPerThread >= 1 && kLoadsPerThread * 64 * kCopyWaves == kTileChunks,
+                "tile split");
 };
 
 // A load through the constant address space: with a wave-uniform address it
@@ -97,22 +104,25 @@ __device__ __forceinline__ int swap_bits_2_3(int r) {
 // has 64 four-byte banks and serves a ds_read_b128 in groups of 16 lanes and
 // a ds_read_b64_tr_b16 in groups of 32 lanes, so:
 //  - K: the 16 lanes of a group read 16 consecutive rows at one logical
-//    chunk; with 256-byte rows (d = 128) the chunk is XORed with row & 15,
-//    with 128-byte rows (d = 64, two rows per bank cycle) with (row >> 1) & 7;
+//    chunk; with rows of 256 bytes or more (d >= 128) the chunk is XORed with
+//    row & 15, with 128-byte rows (d = 64, two rows per bank cycle) with
+//    (row >> 1) & 7, with 64-byte rows (d = 32, four rows per bank cycle)
+//    with (row >> 2) & 3;
 //  - V: a 32-lane group reads 4 consecutive rows x 4 chunks of one 64-byte
-//    group; the four rows must use four different chunk groups, so the chunk
-//    is XORed with 4*(row & 3) (d = 128) or 4*((row >> 1) & 1) (d = 64).
+//    group; the four rows must use four different 64-byte bank groups, so the
+//    chunk is XORed with 4*(row & 3) (d >= 128) or 4*((row >> 1) & 1) (d = 64);
+//    at d = 32 the four 64-byte rows are already 256 consecutive bytes.
 template <int D>
 __device__ __forceinline__ int k_swz(int rho) {
-  return D == 128 ? (rho & 15) : ((rho >> 1) & 7);
+  return D >= 128 ? (rho & 15) : D == 64 ? ((rho >> 1) & 7) : ((rho >> 2) & 3);
 }
 template <int D>
 __device__ __forceinline__ int v_swz(int r) {
-  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+  return D >= 128 ? 4 * (r & 3) : D == 64 ? 4 * ((r >> 1) & 1) : 0;
 }
 
 template <int D, bool CAUSAL, bool F16, bool MASKED>
-__global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdArgs a) {
   using G = BGeom<D>;
   using H = Half<F16>;
   using V8 = typename H::V8;
@@ -169,18 +179,25 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t v_rsrc =
       raw_buffer(static_cast<const unsigned short*>(a.v) + kv_off, kv_bytes);
   // Each wave-wide load fills 64 consecutive LDS chunks: position
-  // p = (u*waves + wave)*64 + lane is row rho = p / chunks_per_row, chunk
-  // p % chunks_per_row; the lane fetches the global chunk that belongs there
-  // under the K row permutation and the swizzles. Those depend on the lane
-  // only, so the per-lane byte offsets hold for the whole pass.
-  constexpr int kRowsPerU = G::kWaves * 64 / G::kChunksPerRow;
-  static_assert(kRowsPerU % 32 == 0, "permutation and swizzles repeat every 32 rows");
-  static_assert(D == 128 || D == 64, "swizzles are defined for d = 64 and 128");
-  const int rho0 = (wave * 64 + lane) / G::kChunksPerRow;
+  // p = (u*copy_waves + w)*64 + lane (w the wave's index among the waves that
+  // copy this tensor) is row rho = p / chunks_per_row, chunk p % chunks_per_row;
+  // the lane fetches the global chunk that belongs there under the K row
+  // permutation and the swizzles, which depend on the lane and on u only.
+  constexpr int kRowsPerU = G::kCopyWaves * 64 / G::kChunksPerRow;
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "swizzles are defined for these");
+  const int cw = G::kSplitKV ? wave % G::kCopyWaves : wave;  // index among the copying waves
+  const bool copies_k = !G::kSplitKV || wave < G::kCopyWaves;
+  const bool copies_v = !G::kSplitKV || wave >= G::kCopyWaves;
+  const int rho0 = (cw * 64 + lane) / G::kChunksPerRow;
   const int pc = lane % G::kChunksPerRow;
-  const unsigned k_lane_ofs = (unsigned)((rho0 & ~31) | swap_bits_2_3(rho0 & 31)) * kv_row +
-                              16u * (unsigned)(pc ^ k_swz<D>(rho0));
-  const unsigned v_lane_ofs = (unsigned)rho0 * kv_row + 16u * (unsigned)(pc ^ v_swz<D>(rho0));
+  auto k_src = [&](int u) {
+    const int rho = rho0 + u * kRowsPerU;
+    return (unsigned)((rho & ~31) | swap_bits_2_3(rho & 31)) * kv_row + 16u * (unsigned)(pc ^ k_swz<D>(rho));
+  };
+  auto v_src = [&](int u) {
+    const int rho = rho0 + u * kRowsPerU;
+    return (unsigned)rho * kv_row + 16u * (unsigned)(pc ^ v_swz<D>(rho));
+  };
 
   // A hard mask, packed by columns (MaskColArgs): this wave's 32-row block has
   // one row-bit word per key and a class per 64-key tile (0 nothing admitted,
@@ -200,10 +217,10 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
     const int slot = T % G::kSlots;
 #pragma unroll
     for (int u = 0; u < G::kLoadsPerThread; ++u) {
-      const int base = (u * G::kWaves + wave) * 64;
-      const unsigned tile_ofs = (row0 + (unsigned)(u * kRowsPerU)) * kv_row;
-      dma_load_x4(k_rsrc, k_lane_ofs + tile_ofs, lds_address(&k_lds[slot][base]));
-      dma_load_x4(v_rsrc, v_lane_ofs + tile_ofs, lds_address(&v_lds[slot][base]));
+      const int base = (u * G::kCopyWaves + cw) * 64;
+      const unsigned tile_ofs = row0 * kv_row;
+      if (copies_k) dma_load_x4(k_rsrc, k_src(u) + tile_ofs, lds_address(&k_lds[slot][base]));
+      if (copies_v) dma_load_x4(v_rsrc, v_src(u) + tile_ofs, lds_address(&v_lds[slot][base]));
     }
   };
 
@@ -388,7 +405,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(FwdArgs a) {
     // The tile's mask class (1 without a mask); a tile the mask closes is skipped.
     uint32_t cls = 1u;
     if (MASKED && wave_live && ks + T * G::kK < wave_hi)
-      cls = scalar_load<uint32_t>(mcls + (ks / G::kK + T));
+      cls = scalar_load<uint32_t>(mcls + (ks + T * G::kK) / 64);  // the class of its 64-key tile
     if (wave_live && ks + T * G::kK < wave_hi && cls != 0u) {
       V8 pb[G::kKB][2];
       scores_and_p(T, slot, pb, cls);
@@ -456,9 +473,13 @@ hipError_t launch_bf16_variant(const FwdArgs& a, bool f16, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, bool causal, bool f16, hipStream_t s) {
-  if (head_dim == 64) return causal ? launch_bf16_variant<64, true>(a, f16, s) : launch_bf16_variant<64, false>(a, f16, s);
-  if (head_dim == 128) return causal ? launch_bf16_variant<128, true>(a, f16, s) : launch_bf16_variant<128, false>(a, f16, s);
-  return hipErrorInvalidValue;
+  switch (head_dim) {
+    case 32: return causal ? launch_bf16_variant<32, true>(a, f16, s) : launch_bf16_variant<32, false>(a, f16, s);
+    case 64: return causal ? launch_bf16_variant<64, true>(a, f16, s) : launch_bf16_variant<64, false>(a, f16, s);
+    case 128: return causal ? launch_bf16_variant<128, true>(a, f16, s) : launch_bf16_variant<128, false>(a, f16, s);
+    case 256: return causal ? launch_bf16_variant<256, true>(a, f16, s) : launch_bf16_variant<256, false>(a, f16, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace sma

@@ -64,10 +64,9 @@ int check_shape(int in_dtype, int o_dtype, size_t batch, size_t heads, size_t se
       !mul(nkv, elem_bytes(in_dtype), &s.kv_bytes) || !mul(nq, elem_bytes(o_dtype), &s.o_bytes) ||
       !mul(s.rows, sizeof(float), &s.lse_bytes))
     return SMA_ERR_INVALID_VALUE;
-  // Head dims 64 and 128 run on every kernel; 32 and 256 on the fp32
-  // query-block kernel only (fp32 inputs).
-  if (d != 64 && d != 128 && !(in_dtype == SMA_DTYPE_F32 && (d == 32 || d == 256)))
-    return SMA_ERR_UNSUPPORTED;
+  // Head dims 64 and 128 run on every kernel; 32 and 256 on the query-block
+  // kernels (fp32 and 16-bit), not on the fp32 in-workgroup key-split one.
+  if (d != 32 && d != 64 && d != 128 && d != 256) return SMA_ERR_UNSUPPORTED;
   if (seq_q > kMaxSeq || seq_kv > kMaxSeq || s.bh > (size_t(1) << 31)) return SMA_ERR_UNSUPPORTED;
   if (heads > (size_t(1) << 20)) return SMA_ERR_UNSUPPORTED;
   s.row_elems = layout == SMA_LAYOUT_BSHD ? heads * d : d;
@@ -87,15 +86,16 @@ struct Plan {
   size_t part_lse_off = 0;   // byte offset of the partial LSE array in the workspace
 };
 
-int queries_per_wg(int kernel) {
+int queries_per_wg(int kernel, size_t d) {
   switch (kernel) {
     case SMA_KERNEL_F32_KSPLIT: return sma::kF32WsplitQueriesPerWG;
-    case SMA_KERNEL_BF16_QBLOCK: return sma::kBF16QueriesPerWG;
+    case SMA_KERNEL_BF16_QBLOCK: return d == 256 ? sma::kBF16D256QueriesPerWG : sma::kBF16QueriesPerWG;
     default: return sma::kF32QueriesPerWG;
   }
 }
-int keys_per_tile(int kernel) {
-  return kernel == SMA_KERNEL_BF16_QBLOCK ? sma::kBF16KeysPerTile : sma::kF32KeysPerTile;
+int keys_per_tile(int kernel, size_t d) {
+  if (kernel == SMA_KERNEL_BF16_QBLOCK) return d == 256 ? sma::kBF16D256KeysPerTile : sma::kBF16KeysPerTile;
+  return sma::kF32KeysPerTile;
 }
 bool kernel_fits_dtype(int kernel, int in_dtype) {
   if (in_dtype != SMA_DTYPE_F32) return kernel == SMA_KERNEL_BF16_QBLOCK;
@@ -108,7 +108,7 @@ size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 // GPU: aim for one resident workgroup per slot, keep at least four key tiles
 // per split.
 size_t auto_splits(const Shape& s, int kernel, size_t base, int num_cus) {
-  const size_t kt = (size_t)keys_per_tile(kernel);
+  const size_t kt = (size_t)keys_per_tile(kernel, s.d);
   // Resident workgroups per CU: one for the 16-bit kernel and for head dim 256
   // (LDS-limited), two otherwise.
   const size_t per_cu = kernel == SMA_KERNEL_BF16_QBLOCK || s.d > 128 ? 1 : 2;
@@ -139,9 +139,9 @@ bool ksplit_fits(const Shape& s) {
   return (s.seq_q + 32) * s.row_elems * 4 <= lim && (s.seq_kv + 32) * s.row_elems * 4 <= lim;
 }
 
-// Kernels built for a head dim (the fp32 query-block kernel also for 32 and 256).
+// Kernels built for a head dim (the query-block kernels also for 32 and 256).
 bool kernel_fits_head_dim(int kernel, size_t d) {
-  return d == 64 || d == 128 || kernel == SMA_KERNEL_F32_QBLOCK;
+  return d == 64 || d == 128 || kernel == SMA_KERNEL_F32_QBLOCK || kernel == SMA_KERNEL_BF16_QBLOCK;
 }
 
 int auto_kernel(const Shape& s, int num_cus) {
@@ -157,8 +157,8 @@ int auto_kernel(const Shape& s, int num_cus) {
 Plan plan_for(const Shape& s, int kernel, size_t nsplit, int num_cus) {
   Plan p;
   p.kernel = kernel;
-  const size_t qpw = (size_t)queries_per_wg(kernel);
-  const size_t kt = (size_t)keys_per_tile(kernel);
+  const size_t qpw = (size_t)queries_per_wg(kernel, s.d);
+  const size_t kt = (size_t)keys_per_tile(kernel, s.d);
   p.nqb = (int32_t)((s.seq_q + qpw - 1) / qpw);
   const size_t base = s.bh * (size_t)p.nqb;
   if (kernel == SMA_KERNEL_F32_KSPLIT || s.seq_kv == 0) nsplit = 1;

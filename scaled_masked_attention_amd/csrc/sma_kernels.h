@@ -136,6 +136,9 @@ constexpr int kF32KeysPerTile = 32;
 constexpr int kF32WsplitQueriesPerWG = 32;  // in-workgroup key-split kernel
 constexpr int kBF16QueriesPerWG = 256;
 constexpr int kBF16KeysPerTile = 64;
+// The 16-bit kernel at head dim 256 (one wave per SIMD, 32-key tiles).
+constexpr int kBF16D256QueriesPerWG = 128;
+constexpr int kBF16D256KeysPerTile = 32;
 constexpr int kThreadsPerWG = 256;
 
 // Row primitives on a (rows x cols) fp32 matrix.

@@ -78,8 +78,8 @@ def test_invalid_values():
 
 def test_unsupported():
     assert _v(d=96) == UNSUP and _v(d=16) == UNSUP and _v(d=512) == UNSUP
-    for d in (32, 256):  # head dims the 16-bit kernel is not built for
-        assert _v(idt=BF16, d=d) == UNSUP and _v(idt=F16, odt=BF16, d=d) == UNSUP
+    for d in (32, 256):  # the 16-bit kernel is built for these head dims too
+        assert _v(idt=BF16, d=d) == OK and _v(idt=F16, odt=BF16, d=d) == OK
     assert _v(odt=BF16, idt=BF16, d=96) == UNSUP
     assert _v(odt=F16) == OK and _v(odt=F16, idt=F16) == OK and _v(odt=F16, idt=BF16) == OK
     assert _v(idt=F16, d=128, skv=1 << 23) == UNSUP
@@ -244,12 +244,18 @@ def test_plan_rejects():
     with pytest.raises(sma.SMAError) as e:
         P(F32, 1, 1, 8, 8, 96, False)
     assert e.value.status == UNSUP
-    for d in (32, 256):  # only the 128-row fp32 kernel is built for these head dims
-        for kern, idt in ((sma.SMA_KERNEL_F32_KSPLIT, F32), (sma.SMA_KERNEL_BF16_QBLOCK, BF16)):
-            with pytest.raises(sma.SMAError) as e:
-                P(idt, 1, 1, 8, 8, d, False, kernel=kern)
-            assert e.value.status == UNSUP
+    for d in (32, 256):  # the query-block kernels are built for these head dims, ksplit is not
+        with pytest.raises(sma.SMAError) as e:
+            P(F32, 1, 1, 8, 8, d, False, kernel=sma.SMA_KERNEL_F32_KSPLIT)
+        assert e.value.status == UNSUP
         assert P(F32, 1, 1, 8, 8, d, False, kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=1).nsplit == 1
+        assert P(BF16, 1, 1, 8, 8, d, False, kernel=sma.SMA_KERNEL_BF16_QBLOCK, nsplit=1).nsplit == 1
+    # the 16-bit kernel's geometry: 256 rows and 64-key tiles, 128 rows and 32-key tiles at d = 256
+    K16 = sma.SMA_KERNEL_BF16_QBLOCK
+    assert P(BF16, 1, 4, 1000, 1000, 32, True, kernel=K16, nsplit=1).workgroups == 4 * 4
+    assert P(BF16, 1, 4, 1000, 1000, 256, True, kernel=K16, nsplit=1).workgroups == 4 * 8
+    p = P(F16, 1, 1, 128, 4096, 256, False, num_cus=256)  # one 128-row block: split in 32-key tiles
+    assert p.nsplit == 32 and p.workspace_bytes >= 32 * 128 * 257 * 4
     lib = sma.library()
     assert lib.sma_attention_fwd_plan(F32, 1, 1, 8, 8, 64, 0, 0, -1, 0, 256, None) == NULLP
     assert lib.sma_attention_fwd_plan(F32, 1, 1, 8, 8, 64, 0, 2, -1, 0, 256, ctypes.byref(sma.Plan())) == INVAL

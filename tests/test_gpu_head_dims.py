@@ -1,4 +1,5 @@
-"""Head dims 32 and 256 (fp32 inputs, the 128-row fp32 kernel and the split combine), through
+"""Head dims 32 and 256 (fp32 inputs on the 128-row fp32 kernel, 16-bit inputs on the 16-bit kernel,
+and the split combine), through
 the C ABI, against the oracle.
 
 Ragged shapes that span several query blocks and key tiles, causal and not, unsplit and split
@@ -192,3 +193,122 @@ def test_deterministic_bitwise(d):
         a = run_gpu(*dev, 0.1, False, **_qblock(nsplit))
         b = run_gpu(*dev, 0.1, False, **_qblock(nsplit))
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------ 16-bit inputs
+# The 16-bit kernel at head dims 32 (8 waves, 64-key tiles, K and V copied by half the
+# waves each) and 256 (4 waves of 32 rows, 32-key tiles).
+def _k16(nsplit):
+    import scaled_masked_attention_amd as sma
+
+    return dict(kernel=sma.SMA_KERNEL_BF16_QBLOCK, nsplit=nsplit)
+
+
+@functools.lru_cache(maxsize=4)
+def _case16(shape, causal, d, dtype):
+    B, H, sq, skv = shape
+    (q, k, v), bits = gen.random_case(900 + sq + 7 * skv + d, (B, H, sq, d), (B, H, skv, d),
+                                      sigma_qk=3.0, dtype=dtype)
+    scale = 1.0 / math.sqrt(d)
+    return (q, k, v), bits, scale, oracle.attention_fwd(q, k, v, scale, causal)
+
+
+@pytest.mark.parametrize("plan", ["auto", "unsplit", "split3"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", HEAD_DIMS)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_parity_16bit(shape, causal, d, dtype, plan):
+    (q, k, v), bits, scale, (o_ref, lse_ref) = _case16(shape, causal, d, dtype)
+    kw = {} if plan == "auto" else _k16(1 if plan == "unsplit" else 3)
+    o, lse = run_gpu(*to_device((q, k, v), bits, dtype), scale, causal, **kw)
+    check_parity(o, lse, o_ref, lse_ref, dtype, f"{shape} causal={causal} d={d} {dtype} {plan}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_16bit_edge_cases(d, dtype):
+    """No keys at all (O = +0, LSE = -inf); causal rows before the first key exactly zero with
+    NaN queries; Q = 0 (the mean of V over the admitted keys); zero and negative scales."""
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    q0 = torch.randn(1, 2, 70, d, device="cuda").to(tdt)
+    k0 = torch.empty(1, 2, 0, d, device="cuda", dtype=tdt)
+    o, lse = sma.attention_fwd(q0, k0, k0, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and not torch.any(torch.signbit(o)) and torch.all(torch.isneginf(lse))
+    B, H, sq, skv = 1, 2, 300, 100
+    (q, k, v), bits = gen.random_case(950 + d, (B, H, sq, d), (B, H, skv, d), sigma_qk=3.0, dtype=dtype)
+    q = q.copy()
+    qb = bits[0].copy()
+    qb[:, :, : sq - skv] = 0x7FC0 if dtype == "bf16" else 0x7E00  # NaN in rows that see no key
+    q[:, :, : sq - skv] = np.nan
+    for scale, nsplit in ((1.0 / math.sqrt(d), 1), (0.0, 1), (-0.2, 3)):
+        o, lse = run_gpu(*to_device((q, k, v), (qb, bits[1], bits[2]), dtype), scale, True,
+                         **_k16(nsplit))
+        assert np.all(o[:, :, : sq - skv] == 0.0) and np.all(np.isneginf(lse[:, :, : sq - skv]))
+        qn = np.nan_to_num(q, nan=0.0)
+        o_ref, lse_ref = oracle.attention_fwd(qn, k, v, scale, True)
+        check_parity(o, lse, o_ref, lse_ref, dtype, f"d={d} {dtype} scale={scale}")
+    zero = np.zeros((B, H, sq, d), np.float32)
+    zbits = np.zeros((B, H, sq, d), np.uint16)
+    o, lse = run_gpu(*to_device((zero, k, v), (zbits, bits[1], bits[2]), dtype), 0.3, False)
+    o_ref, lse_ref = oracle.attention_fwd(zero, k, v, 0.3, False)
+    check_parity(o, lse, o_ref, lse_ref, dtype, f"d={d} {dtype} Q=0")
+
+
+@pytest.mark.parametrize("nsplit", [1, 2])
+@pytest.mark.parametrize("d", HEAD_DIMS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_16bit_masked(causal, d, nsplit):
+    """A mask of whole 32x64 blocks admitting nothing, everything or a random half (every
+    tile class of the 16-bit kernel), per (batch, head)."""
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    B, H, sq, skv = 2, 2, 300, 333
+    (q, k, v), bits = gen.random_case(960 + d, (B, H, sq, d), (B, H, skv, d), sigma_qk=3.0,
+                                      dtype="bf16")
+    nrb, ntk = (sq + 31) // 32, (skv + 63) // 64
+    kind = np.floor(gen.uniform24(961 + d, np.arange(B * H * nrb * ntk, dtype=np.uint64)) * 3
+                    ).reshape(B, H, nrb, ntk)
+    rnd = gen.uniform24(962 + d, np.arange(B * H * sq * skv, dtype=np.uint64)).reshape(B, H, sq, skv) < 0.5
+    mask = np.zeros((B, H, sq, skv), bool)
+    for r in range(nrb):
+        for t in range(ntk):
+            rs, ts = slice(32 * r, 32 * r + 32), slice(64 * t, 64 * t + 64)
+            kk = kind[:, :, r, t][:, :, None, None]
+            mask[:, :, rs, ts] = np.where(kk == 1, True, np.where(kk == 2, rnd[:, :, rs, ts], False))
+    mask = mask.astype(np.uint8)
+    tq, tk, tv = to_device((q, k, v), bits, "bf16")
+    o, lse = sma.attention_fwd(tq, tk, tv, scale=0.1, causal=causal, return_lse=True,
+                               mask=torch.from_numpy(mask).to("cuda"), **_k16(nsplit))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd_masked(q, k, v, mask, 0.1, causal)
+    check_parity(o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), o_ref,
+                 lse_ref, "bf16", f"16-bit mask d={d} nsplit={nsplit}")
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_16bit_bshd_layout_and_16bit_output(d):
+    """bshd equals bhsd transposed, bit for bit; bf16 output is the fp32 output rounded."""
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
+    B, H, sq, skv = 2, 3, 190, 230
+    (q, k, v), bits = gen.random_case(970 + d, (B, H, sq, d), (B, H, skv, d), sigma_qk=3.0,
+                                      dtype="bf16")
+    tq, tk, tv = to_device((q, k, v), bits, "bf16")
+    o1, l1 = sma.attention_fwd(tq, tk, tv, scale=0.1, causal=True, return_lse=True)
+    t2 = [x.transpose(1, 2).contiguous() for x in (tq, tk, tv)]
+    o2, l2 = sma.attention_fwd(*t2, scale=0.1, causal=True, return_lse=True, layout="bshd")
+    o3 = sma.attention_fwd(tq, tk, tv, scale=0.1, causal=True, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.transpose(1, 2), o1) and torch.equal(l1, l2)
+    assert np.array_equal(o3.view(torch.int16).cpu().numpy().view(np.uint16),
+                          gen.f32_to_bf16_bits(o1.cpu().numpy()))

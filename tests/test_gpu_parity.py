@@ -123,7 +123,8 @@ def test_parity_full_size_qblock_sampled(name):
 @pytest.mark.parametrize("name", ["f32_causal_b8h16_s2048_d128", "f32_cross_b2h32_q256_kv4096_d128",
                                   "f32_cross_causal_b2h32_q256_kv4096_d128", "bf16_causal_b1h32_s16384_d128",
                                   "f16_causal_b1h32_s16384_d128", "f32_causal_b8h16_s2048_d32",
-                                  "f32_causal_b8h16_s2048_d256"])
+                                  "f32_causal_b8h16_s2048_d256", "bf16_causal_b1h32_s16384_d32",
+                                  "bf16_causal_b1h32_s16384_d256"])
 def test_parity_full_size_sampled(name):
     w, vals, bits = workload_case(name)
     o, lse = run_gpu(*to_device(vals, bits, w.dtype), w.scale, w.causal)
@@ -144,7 +145,7 @@ def test_parity_full_size_sampled(name):
 @pytest.mark.parametrize("name", ["f32_causal_b8h16_s2048_d128", "f32_cross_b2h32_q256_kv4096_d128",
                                   "f32_cross_causal_b2h32_q256_kv4096_d128", "bf16_causal_b1h32_s16384_d128",
                                   "f16_causal_b1h32_s16384_d128", "f32_causal_b8h16_s2048_d32",
-                                  "f32_causal_b8h16_s2048_d256"])
+                                  "f32_causal_b8h16_s2048_d256", "bf16_causal_b1h32_s16384_d32"])
 @pytest.mark.timeout(600)  # the whole oracle takes about a minute per 16384-token workload
 def test_parity_full_size_whole(name):
     """The large workloads at full size in the benchmark's launch configuration (the
