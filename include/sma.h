@@ -113,9 +113,9 @@ typedef struct sma_plan {
  *   o_dtype    SMA_DTYPE_F32, or SMA_DTYPE_BF16 / SMA_DTYPE_F16: the fp32 result rounded
  *              to that type (nearest even; beyond fp16's range, infinity) as it is stored.
  *              Any with any input type. LSE is always fp32.
- *   head_dim   64 or 128 with every input type; also 32 or 256 with fp32 inputs, which
- *              run on SMA_KERNEL_F32_QBLOCK only (0 -> INVALID_VALUE, other values and
- *              other kernels -> UNSUPPORTED).
+ *   head_dim   32, 64, 128 or 256 with every input type; SMA_KERNEL_F32_KSPLIT runs
+ *              32, 64 and 128 only (0 -> INVALID_VALUE; other values, and 256 forced
+ *              onto that kernel -> UNSUPPORTED).
  *   scale      finite multiplier of QK^T (zero and negative values are allowed).
  *   causal     0: no mask; nonzero: bottom-right causal mask.
  *   workspace  optional device scratch for splitting the keys of a row across

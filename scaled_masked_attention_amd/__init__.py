@@ -30,6 +30,12 @@ KERNEL_NAMES = {SMA_KERNEL_F32_QBLOCK: "f32_qblock", SMA_KERNEL_F32_KSPLIT: "f32
 STATUS_NAMES = {0: "SMA_OK", 1: "SMA_ERR_NULL_POINTER", 2: "SMA_ERR_INVALID_VALUE",
                 3: "SMA_ERR_UNSUPPORTED", 4: "SMA_ERR_MISALIGNED", 5: "SMA_ERR_ALIASING",
                 6: "SMA_ERR_HIP", 7: "SMA_ERR_SCRATCH"}
+SMA_ERR_NULL_POINTER = 1
+SMA_ERR_INVALID_VALUE = 2
+SMA_ERR_UNSUPPORTED = 3
+SMA_ERR_MISALIGNED = 4
+SMA_ERR_ALIASING = 5
+SMA_ERR_HIP = 6
 SMA_ERR_SCRATCH = 7
 NOALLOC_SCRATCH_BYTES = 72 * 1024 * 1024  # SMA_NOALLOC_SCRATCH_BYTES
 

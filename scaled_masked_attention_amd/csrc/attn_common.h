@@ -112,16 +112,26 @@ __device__ __forceinline__ unsigned pack_out16(float lo, float hi, bool f16) {
   return f16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
 }
 
-// A 32-row fp32 tile (of Q, K, dO or V) in LDS: row r's 16-byte chunk c is stored at chunk
-// position c ^ (r & 15) of the row. A direct-to-LDS instruction fills 1 KB of
-// consecutive positions, so lane l of copy instruction t fetches the global
-// chunk that belongs at position p = 64t + l.
+// A 32-row fp32 tile (of Q, K, dO or V) in LDS: row r's 16-byte chunk c is
+// stored at chunk position c ^ tile_swz<D>(r) of the row. The operand reads
+// take one chunk from each of 16 consecutive rows per ds_read_b128 group of 16
+// lanes; rows of 256 bytes or more all start at bank 0, so XOR with r & 15
+// spreads those 16 lanes over the 64 banks, while 128-byte rows (d = 32)
+// alternate between the two bank halves, so XOR with (r >> 1) & 7 does.
+// A direct-to-LDS instruction fills 1 KB of consecutive positions, so lane l
+// of copy instruction t fetches the global chunk that belongs at position
+// p = 64t + l.
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "fp32 tile swizzle");
+  return D >= 64 ? (r & 15) : ((r >> 1) & 7);
+}
 template <int D>
 __device__ __forceinline__ unsigned tile_src_offset(int t, int lane) {
   constexpr int kChunks = D / 4;  // 16-byte chunks per row
   const int p = 64 * t + lane;
   const int r = p / kChunks;
-  const int c = (p % kChunks) ^ (r & 15);
+  const int c = (p % kChunks) ^ tile_swz<D>(r);
   return (unsigned)(r * 4 * D + 16 * c);
 }
 // The same with rows row_bytes apart in global memory (a strided layout).
@@ -130,7 +140,7 @@ __device__ __forceinline__ unsigned tile_src_offset(int t, int lane, unsigned ro
   constexpr int kChunks = D / 4;
   const int p = 64 * t + lane;
   const int r = p / kChunks;
-  const int c = (p % kChunks) ^ (r & 15);
+  const int c = (p % kChunks) ^ tile_swz<D>(r);
   return (unsigned)r * row_bytes + 16u * (unsigned)c;
 }
 // Unswizzled copy: lane l of instruction t fetches chunk p = 64t + l in row order.
@@ -151,7 +161,7 @@ __device__ __forceinline__ unsigned strided_range(int32_t rows, int64_t stride_e
 // 8u + 4h .. 8u + 4h + 3 of row m (the operand of MFMA group u).
 template <int D>
 __device__ __forceinline__ unsigned tile_operand_offset(int m, int h, int u) {
-  return (unsigned)(m * 4 * D + 16 * ((2 * u + h) ^ (m & 15)));
+  return (unsigned)(m * 4 * D + 16 * ((2 * u + h) ^ tile_swz<D>(m)));
 }
 
 // LDS byte offset, within such a tile, of the D/32 consecutive floats at head
@@ -161,7 +171,7 @@ template <int D>
 __device__ __forceinline__ unsigned tile_row_offset(int row, int j) {
   constexpr int kLaneBytes = 4 * (D / 32);
   const int byte = kLaneBytes * j;
-  return (unsigned)(row * 4 * D + 16 * ((byte >> 4) ^ (row & 15)) + (byte & 15));
+  return (unsigned)(row * 4 * D + 16 * ((byte >> 4) ^ tile_swz<D>(row)) + (byte & 15));
 }
 
 }  // namespace sma

@@ -8,7 +8,8 @@
 //
 // Workgroup: 4 waves x 32 query rows = 128 rows of one (batch, head), with a
 // range of keys (all of them, or one split). Key tiles of 32 rows stream
-// HBM/L2 -> registers -> LDS (double buffered, one barrier per tile).
+// HBM/L2 -> LDS with direct-to-LDS loads (no registers on the way; double
+// buffered, one barrier per tile): tile t+1 is in flight while tile t is used.
 //
 // Each wave computes S^T = K Q^T for its 32 queries and a 32-key tile: lane
 // (m, h) = (lane % 32, lane / 32) supplies K[key m] and Q[query m] along head
@@ -33,14 +34,21 @@ struct F32Geom {
   static constexpr int kQW = 32;                    // query rows per wave
   static constexpr int kQ = kWaves * kQW;           // query rows per workgroup
   static constexpr int kK = kF32KeysPerTile;        // keys per tile
-  static constexpr int kKStride = D + 4;            // padded K row in LDS (floats)
-  static constexpr int kVStride = D;                // V row in LDS (floats)
   static constexpr int kHalf = D / 2;               // head dims per lane half in QK^T
   static constexpr int kNch = D / 32;               // 32-wide output chunks
-  static constexpr int kF4PerThread = kK * D / 4 / kThreadsPerWG;
+  static constexpr int kChunks = D / 4;             // 16-byte chunks per row
+  static constexpr int kDma = kK * D * 4 / 1024;    // 1 KB copy instructions per tile and tensor
+  static constexpr int kDmaPerWave = kDma / kWaves;
+  static constexpr int kRowsPerDma = 64 / kChunks;  // rows one copy instruction covers
   static_assert(kQ == kF32QueriesPerWG, "planner geometry");
-  static_assert(kF4PerThread * 4 * kThreadsPerWG == kK * D, "tile split");
+  static_assert(kDmaPerWave >= 1 && kDmaPerWave * kWaves == kDma, "tile split");
 };
+
+// K tiles in LDS use the fp32 tile swizzle (tile_swz: row r's 16-byte chunk
+// c at position c ^ tile_swz(r)), so the 16 lanes of each ds_read_b128 group
+// in the QK^T operand read hit 64 different banks. V tiles are stored as they
+// are: a half-wave reads one whole row, the other half the row 4 below, and
+// each group of 16 lanes reads 256 consecutive bytes.
 
 // D/32 consecutive floats: a lane's share of one output row, or of one V row.
 template <int N>
@@ -58,8 +66,8 @@ template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   using G = F32Geom<D>;
   using VecN = typename FVec<G::kNch>::T;
-  __shared__ __attribute__((aligned(16))) float k_lds[2][G::kK * G::kKStride];
-  __shared__ __attribute__((aligned(16))) float v_lds[2][G::kK * G::kVStride];
+  __shared__ __attribute__((aligned(16))) float k_lds[2][G::kK * D];
+  __shared__ __attribute__((aligned(16))) float v_lds[2][G::kK * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -113,28 +121,27 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
            (int64_t)ld_row * a.mask_words;
   const float* kg = static_cast<const float*>(a.k) + kv_off;
   const float* vg = static_cast<const float*>(a.v) + kv_off;
-  f32x4 kreg[G::kF4PerThread], vreg[G::kF4PerThread];
+  const unsigned kv_row = (unsigned)(a.kvs_s * 4);  // bytes between key rows
 
-  auto load_tile = [&](int32_t tile) {
+  // Copy key tile `tile` into LDS buffer `buf`. The buffer resources start at
+  // the tile's first row and end after its last real one, so rows past seq_kv
+  // read as zeros (such keys are always excluded) and the 32-bit offsets stay
+  // within one tile. Lane l of instruction i (of this wave) fills LDS chunk
+  // position p = 64*(i*waves + wave) + l: row p / chunks, position p % chunks.
+  auto issue_tile = [&](int32_t tile, int buf) {
     const int32_t j0 = ks + tile * G::kK;
+    const int32_t rows = min(G::kK, a.seq_kv - j0);
+    const unsigned bytes = strided_range(rows, a.kvs_s, D, 4);
+    const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(kg + (int64_t)j0 * a.kvs_s, bytes);
+    const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(vg + (int64_t)j0 * a.kvs_s, bytes);
 #pragma unroll
-    for (int u = 0; u < G::kF4PerThread; ++u) {
-      const int f = tid + kThreadsPerWG * u;
-      const int row = f / (D / 4), c4 = f % (D / 4);
-      // Rows past seq_kv re-read the last key row (in bounds, finite, branch
-      // free); such keys are always masked and weigh an exact zero.
-      const int32_t j = min(j0 + row, a.seq_kv - 1);
-      kreg[u] = *reinterpret_cast<const f32x4*>(kg + (int64_t)j * a.kvs_s + 4 * c4);
-      vreg[u] = *reinterpret_cast<const f32x4*>(vg + (int64_t)j * a.kvs_s + 4 * c4);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < G::kF4PerThread; ++u) {
-      const int f = tid + kThreadsPerWG * u;
-      const int row = f / (D / 4), c4 = f % (D / 4);
-      *reinterpret_cast<f32x4*>(&k_lds[buf][row * G::kKStride + 4 * c4]) = kreg[u];
-      *reinterpret_cast<f32x4*>(&v_lds[buf][row * G::kVStride + 4 * c4]) = vreg[u];
+    for (int i = 0; i < G::kDmaPerWave; ++i) {
+      const int ti = i * G::kWaves + wave;
+      const int r = ti * G::kRowsPerDma + lane / G::kChunks;
+      const int c = lane % G::kChunks;
+      dma_load_x4(k_rsrc, (unsigned)r * kv_row + 16u * (unsigned)(c ^ tile_swz<D>(r)),
+                  lds_address(&k_lds[buf][256 * ti]));
+      dma_load_x4(v_rsrc, (unsigned)r * kv_row + 16u * (unsigned)c, lds_address(&v_lds[buf][256 * ti]));
     }
   };
 
@@ -146,25 +153,37 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   float m_run = -INFINITY;  // running row max, log2 units (shared by both lane halves)
   float l_run = 0.f;        // this lane half's share of the row denominator
 
+  // The mask word of the tile about to be used is loaded one tile ahead, so
+  // that its wait (which the compiler places, counting only its own loads)
+  // never waits for a tile copy as well.
+  uint32_t mword_next = 0u;
   if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+    issue_tile(0, 0);
+    if (MASKED) mword_next = mrow[ks >> 5];
+    wait_vmcnt<0>();
   }
   __syncthreads();
 
   for (int32_t it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
-    if (it + 1 < ntiles) load_tile(it + 1);
+    uint32_t mword = ~0u;
+    if (MASKED) {
+      mword = mword_next;
+      asm volatile("" : "+v"(mword));  // consumed here: no copy is in flight yet
+    }
+    // Buffer buf ^ 1 was last read in the previous iteration, before its barrier.
+    if (it + 1 < ntiles) issue_tile(it + 1, buf ^ 1);
     const int32_t j0 = ks + it * G::kK;
     if (wave_live && j0 < wave_hi) {
       // S^T tile = K Q^T over the head dim.
       f32x16 s;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = 0.f;
-      const float* krow = &k_lds[buf][lm * G::kKStride + lh * G::kHalf];
+      const float* krow = &k_lds[buf][lm * D];
 #pragma unroll
       for (int u = 0; u < G::kHalf / 4; ++u) {
-        const f32x4 kk = *reinterpret_cast<const f32x4*>(krow + 4 * u);
+        const int c = lh * (G::kHalf / 4) + u;  // this lane half's chunk u
+        const f32x4 kk = *reinterpret_cast<const f32x4*>(krow + 4 * (c ^ tile_swz<D>(lm)));
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(kk[0], qr[4 * u + 0], s, 0, 0, 0);
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(kk[1], qr[4 * u + 1], s, 0, 0, 0);
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(kk[2], qr[4 * u + 2], s, 0, 0, 0);
@@ -182,7 +201,6 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
         }
       }
       if (MASKED) {
-        const uint32_t mword = mrow[j0 >> 5];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           tv[r] = (mword >> (8 * (r / 4) + 4 * lh + (r % 4))) & 1u ? tv[r] : -INFINITY;
@@ -220,14 +238,17 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int vrow = 8 * (r / 4) + 4 * lh + (r % 4);
-        const VecN vv = *reinterpret_cast<const VecN*>(&v_lds[buf][vrow * G::kVStride + G::kNch * lm]);
+        const VecN vv = *reinterpret_cast<const VecN*>(&v_lds[buf][vrow * D + G::kNch * lm]);
 #pragma unroll
         for (int cb = 0; cb < G::kNch; ++cb)
           oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[cb], tv[r], oacc[cb], 0, 0, 0);
       }
     }
-    if (it + 1 < ntiles) store_tile((it + 1) & 1);
-    __syncthreads();
+    if (it + 1 < ntiles) {
+      if (MASKED) mword_next = mrow[(j0 + G::kK) >> 5];
+      wait_vmcnt<0>();  // this wave's copies of tile it + 1 (and the mask word) have landed
+    }
+    __syncthreads();  // everyone's copies landed; everyone is done with buffer buf
   }
 
   // Epilogue: combine the two lane halves' denominators, normalise, write.

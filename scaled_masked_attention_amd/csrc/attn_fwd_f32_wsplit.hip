@@ -34,12 +34,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// D/32 consecutive floats: a lane's share of one output row, or of one V row.
 template <int N>
-struct FVecW;
-template <>
-struct FVecW<2> { typedef f32x2 T; };
-template <>
-struct FVecW<4> { typedef f32x4 T; };
+struct FVecW {
+  typedef float T __attribute__((ext_vector_type(N)));
+};
 
 constexpr float kTauW = 8.0f;  // lazy running-max threshold, log2 units
 
@@ -347,10 +346,15 @@ hipError_t launch_wsplit_variant(const FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// Head dims 32, 64 and 128. At 256 a wave's private K and V slots (32 KB
+// each) for four waves, plus the Q tile, would take 288 KB of LDS.
 hipError_t launch_fwd_f32_wsplit(const FwdArgs& a, int head_dim, bool causal, hipStream_t s) {
-  if (head_dim == 64) return causal ? launch_wsplit_variant<64, true>(a, s) : launch_wsplit_variant<64, false>(a, s);
-  if (head_dim == 128) return causal ? launch_wsplit_variant<128, true>(a, s) : launch_wsplit_variant<128, false>(a, s);
-  return hipErrorInvalidValue;
+  switch (head_dim) {
+    case 32: return causal ? launch_wsplit_variant<32, true>(a, s) : launch_wsplit_variant<32, false>(a, s);
+    case 64: return causal ? launch_wsplit_variant<64, true>(a, s) : launch_wsplit_variant<64, false>(a, s);
+    case 128: return causal ? launch_wsplit_variant<128, true>(a, s) : launch_wsplit_variant<128, false>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace sma

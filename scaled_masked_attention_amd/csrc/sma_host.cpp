@@ -64,7 +64,7 @@ int check_shape(int in_dtype, int o_dtype, size_t batch, size_t heads, size_t se
       !mul(nkv, elem_bytes(in_dtype), &s.kv_bytes) || !mul(nq, elem_bytes(o_dtype), &s.o_bytes) ||
       !mul(s.rows, sizeof(float), &s.lse_bytes))
     return SMA_ERR_INVALID_VALUE;
-  // Head dims 64 and 128 run on every kernel; 32 and 256 on the query-block
+  // Head dims 32, 64 and 128 run on every kernel; 256 on the query-block
   // kernels (fp32 and 16-bit), not on the fp32 in-workgroup key-split one.
   if (d != 32 && d != 64 && d != 128 && d != 256) return SMA_ERR_UNSUPPORTED;
   if (seq_q > kMaxSeq || seq_kv > kMaxSeq || s.bh > (size_t(1) << 31)) return SMA_ERR_UNSUPPORTED;
@@ -139,9 +139,10 @@ bool ksplit_fits(const Shape& s) {
   return (s.seq_q + 32) * s.row_elems * 4 <= lim && (s.seq_kv + 32) * s.row_elems * 4 <= lim;
 }
 
-// Kernels built for a head dim (the query-block kernels also for 32 and 256).
+// Kernels built for a head dim (the query-block kernels also for 256: the
+// in-workgroup key-split kernel's per-wave K and V slots would not fit LDS).
 bool kernel_fits_head_dim(int kernel, size_t d) {
-  return d == 64 || d == 128 || kernel == SMA_KERNEL_F32_QBLOCK || kernel == SMA_KERNEL_BF16_QBLOCK;
+  return d != 256 || kernel == SMA_KERNEL_F32_QBLOCK || kernel == SMA_KERNEL_BF16_QBLOCK;
 }
 
 int auto_kernel(const Shape& s, int num_cus) {

@@ -193,9 +193,10 @@ def test_plan_auto_choices():
     assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_BF16_QBLOCK, 1, 32 * 64)
     p = P(F32, 1, 1, 1, 4096, 64, False, num_cus=256)  # one query row, many keys
     assert p.kernel == sma.SMA_KERNEL_F32_QBLOCK and p.nsplit == 32
-    # head dims 32 and 256 go to the 128-row fp32 kernel; at 256 one workgroup fits a CU
+    # head dim 32 follows the 64/128 rule; 256 goes to the 128-row fp32 kernel, where one
+    # workgroup fits a CU
     p = P(F32, 8, 16, 2048, 2048, 32, True, num_cus=256)
-    assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_F32_QBLOCK, 1, 8 * 16 * 16)
+    assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_F32_KSPLIT, 1, 8 * 16 * 64)
     p = P(F32, 1, 4, 256, 8192, 256, False, num_cus=256)  # 8 blocks: split to 32 per block
     assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_F32_QBLOCK, 32, 8 * 32)
     assert p.workspace_bytes == sma.workspace_bytes(F32, 1, 4, 256, 8192, 256, False, 256)
@@ -244,10 +245,14 @@ def test_plan_rejects():
     with pytest.raises(sma.SMAError) as e:
         P(F32, 1, 1, 8, 8, 96, False)
     assert e.value.status == UNSUP
-    for d in (32, 256):  # the query-block kernels are built for these head dims, ksplit is not
-        with pytest.raises(sma.SMAError) as e:
-            P(F32, 1, 1, 8, 8, d, False, kernel=sma.SMA_KERNEL_F32_KSPLIT)
-        assert e.value.status == UNSUP
+    # every kernel is built for head dims 32 and 256, except ksplit for 256 (LDS)
+    with pytest.raises(sma.SMAError) as e:
+        P(F32, 1, 1, 8, 8, 256, False, kernel=sma.SMA_KERNEL_F32_KSPLIT)
+    assert e.value.status == UNSUP
+    assert P(F32, 1, 1, 8, 8, 32, False, kernel=sma.SMA_KERNEL_F32_KSPLIT).kernel == sma.SMA_KERNEL_F32_KSPLIT
+    assert P(F32, 8, 16, 2048, 2048, 32, True, num_cus=256).kernel == sma.SMA_KERNEL_F32_KSPLIT
+    assert P(F32, 8, 16, 2048, 2048, 256, True, num_cus=256).kernel == sma.SMA_KERNEL_F32_QBLOCK
+    for d in (32, 256):
         assert P(F32, 1, 1, 8, 8, d, False, kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=1).nsplit == 1
         assert P(BF16, 1, 1, 8, 8, d, False, kernel=sma.SMA_KERNEL_BF16_QBLOCK, nsplit=1).nsplit == 1
     # the 16-bit kernel's geometry: 256 rows and 64-key tiles, 128 rows and 32-key tiles at d = 256

@@ -1,6 +1,6 @@
-"""Head dims 32 and 256 (fp32 inputs on the 128-row fp32 kernel, 16-bit inputs on the 16-bit kernel,
-and the split combine), through
-the C ABI, against the oracle.
+"""Head dims 32 and 256 through the C ABI, against the oracle: fp32 inputs on the 128-row fp32
+kernel (with the split combine) and, at d = 32, on the in-workgroup key-split kernel; 16-bit
+inputs on the 16-bit kernel.
 
 Ragged shapes that span several query blocks and key tiles, causal and not, unsplit and split
 across workgroups (forced and automatic), a hard mask, the bshd layout, bf16 output, rows
@@ -37,6 +37,18 @@ def _qblock(nsplit):
     return dict(kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=nsplit)
 
 
+def _ksplit():
+    import scaled_masked_attention_amd as sma
+
+    return dict(kernel=sma.SMA_KERNEL_F32_KSPLIT, nsplit=1)
+
+
+def _plans(d, nsplit):
+    """The 128-row kernel unsplit and split nsplit ways, and at d = 32 the in-workgroup
+    key-split kernel."""
+    return [_qblock(1), _qblock(nsplit)] + ([_ksplit()] if d == 32 else [])
+
+
 SHAPES = [(1, 2, 128, 128), (2, 3, 200, 200), (1, 2, 77, 300), (2, 1, 300, 77), (1, 1, 1, 1000),
           (1, 1, 513, 513), (1, 3, 257, 1025)]
 
@@ -49,14 +61,22 @@ def _case(shape, causal, d):
     return (q, k, v), scale, oracle.attention_fwd(q, k, v, scale, causal)
 
 
-@pytest.mark.parametrize("plan", ["auto", "unsplit", "split3"])
+@pytest.mark.parametrize("plan", ["auto", "unsplit", "split3", "ksplit"])
 @pytest.mark.parametrize("d", HEAD_DIMS)
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_parity(shape, causal, d, plan):
+    import scaled_masked_attention_amd as sma
+
     (q, k, v), scale, (o_ref, lse_ref) = _case(shape, causal, d)
-    kw = {} if plan == "auto" else _qblock(1 if plan == "unsplit" else 3)
-    o, lse = run_gpu(*to_device((q, k, v), None, "f32"), scale, causal, **kw)
+    kw = {"auto": {}, "unsplit": _qblock(1), "split3": _qblock(3), "ksplit": _ksplit()}[plan]
+    dev = to_device((q, k, v), None, "f32")
+    if plan == "ksplit" and d == 256:  # its per-wave K/V slots would not fit LDS
+        with pytest.raises(sma.SMAError) as e:
+            run_gpu(*dev, scale, causal, **kw)
+        assert e.value.status == sma.SMA_ERR_UNSUPPORTED
+        return
+    o, lse = run_gpu(*dev, scale, causal, **kw)
     check_parity(o, lse, o_ref, lse_ref, "f32", f"{shape} causal={causal} d={d} {plan}")
 
 
@@ -79,11 +99,13 @@ def test_automatic_split_matches_oracle_and_unsplit(d, causal):
     check_parity(o_n, l_n, o_ref, lse_ref, "f32", f"d={d} unsplit")
 
 
-@pytest.mark.parametrize("nsplit", [1, 3])
+@pytest.mark.parametrize("nsplit", [1, 3, "ksplit"])
 @pytest.mark.parametrize("form", ["shared", "full"])
 @pytest.mark.parametrize("d", HEAD_DIMS)
 @pytest.mark.parametrize("causal", [False, True])
 def test_masked(causal, d, form, nsplit):
+    if nsplit == "ksplit" and d == 256:
+        pytest.skip("the in-workgroup key-split kernel is not built for head dim 256")
     import torch
 
     import scaled_masked_attention_amd as sma
@@ -97,14 +119,15 @@ def test_masked(causal, d, form, nsplit):
     mask = mask.astype(np.uint8)
     tq, tk, tv = to_device((q, k, v), None, "f32")
     o, lse = sma.attention_fwd(tq, tk, tv, scale=0.1, causal=causal, return_lse=True,
-                               mask=torch.from_numpy(mask).to("cuda"), **_qblock(nsplit))
+                               mask=torch.from_numpy(mask).to("cuda"),
+                               **(_ksplit() if nsplit == "ksplit" else _qblock(nsplit)))
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_fwd_masked(q, k, v, mask, 0.1, causal)
     check_parity(o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), o_ref,
                  lse_ref, "f32", f"mask d={d} {form} nsplit={nsplit}")
 
 
-@pytest.mark.parametrize("nsplit", [1, 3])
+@pytest.mark.parametrize("nsplit", [1, 3, "ksplit"])
 @pytest.mark.parametrize("d", HEAD_DIMS)
 def test_bshd_layout_and_bf16_output(d, nsplit):
     """bshd equals bhsd transposed, bit for bit; bf16 output is the fp32 output rounded to
@@ -116,7 +139,9 @@ def test_bshd_layout_and_bf16_output(d, nsplit):
     B, H, sq, skv = 2, 3, 190, 230
     (q, k, v), _ = gen.random_case(800 + d, (B, H, sq, d), (B, H, skv, d))
     tq, tk, tv = to_device((q, k, v), None, "f32")
-    kw = _qblock(nsplit)
+    if nsplit == "ksplit" and d == 256:
+        pytest.skip("the in-workgroup key-split kernel is not built for head dim 256")
+    kw = _ksplit() if nsplit == "ksplit" else _qblock(nsplit)
     o1, l1 = sma.attention_fwd(tq, tk, tv, scale=0.1, causal=True, return_lse=True, **kw)
     t2 = [x.transpose(1, 2).contiguous() for x in (tq, tk, tv)]
     o2, l2 = sma.attention_fwd(*t2, scale=0.1, causal=True, return_lse=True, layout="bshd", **kw)
@@ -142,16 +167,18 @@ def test_no_keys_and_rows_without_keys(d):
     q = torch.randn(1, 2, 70, d, device="cuda")
     k = torch.empty(1, 2, 0, d, device="cuda")
     out = torch.full((1, 2, 70, d), float("nan"), device="cuda")
-    o, lse = sma.attention_fwd(q, k, k, causal=False, return_lse=True, out=out, **_qblock(1))
-    torch.cuda.synchronize()
-    assert torch.all(o == 0) and not torch.any(torch.signbit(o)) and torch.all(torch.isneginf(lse))
+    for kw in _plans(d, 1)[1:]:
+        out.fill_(float("nan"))
+        o, lse = sma.attention_fwd(q, k, k, causal=False, return_lse=True, out=out, **kw)
+        torch.cuda.synchronize()
+        assert torch.all(o == 0) and not torch.any(torch.signbit(o)) and torch.all(torch.isneginf(lse))
     # causal with more queries than keys: the first sq - skv rows admit nothing
     (qn, kn, vn), _ = gen.random_case(900 + d, (1, 2, 150, d), (1, 2, 100, d))
-    for nsplit in (1, 2):
-        o, lse = run_gpu(*to_device((qn, kn, vn), None, "f32"), 0.2, True, **_qblock(nsplit))
+    for kw in _plans(d, 2):
+        o, lse = run_gpu(*to_device((qn, kn, vn), None, "f32"), 0.2, True, **kw)
         assert np.all(o[:, :, :50] == 0) and np.all(np.isneginf(lse[:, :, :50]))
         o_ref, lse_ref = oracle.attention_fwd(qn, kn, vn, 0.2, True)
-        check_parity(o, lse, o_ref, lse_ref, "f32", f"d={d} nsplit={nsplit}")
+        check_parity(o, lse, o_ref, lse_ref, "f32", f"d={d} {kw}")
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.3, 2.5])
@@ -161,10 +188,10 @@ def test_zero_negative_and_large_scale(d, scale):
     fp32 bar holds even where scale * |s| reaches the hundreds."""
     (q, k, v), _ = gen.random_case(1000 + d, (1, 2, 160, d), (1, 2, 200, d))
     q, k = ((np.clip(np.round(x * 2), -2, 2) / 2).astype(np.float32) for x in (q, k))
-    for nsplit in (1, 2):
-        o, lse = run_gpu(*to_device((q, k, v), None, "f32"), scale, True, **_qblock(nsplit))
+    for kw in _plans(d, 2):
+        o, lse = run_gpu(*to_device((q, k, v), None, "f32"), scale, True, **kw)
         o_ref, lse_ref = oracle.attention_fwd(q, k, v, scale, True)
-        check_parity(o, lse, o_ref, lse_ref, "f32", f"d={d} scale={scale} nsplit={nsplit}")
+        check_parity(o, lse, o_ref, lse_ref, "f32", f"d={d} scale={scale} {kw}")
 
 
 def test_large_scale_random_scores_within_rounding_bound():
@@ -189,9 +216,9 @@ def test_large_scale_random_scores_within_rounding_bound():
 def test_deterministic_bitwise(d):
     (q, k, v), _ = gen.random_case(1100 + d, (2, 2, 300, d), (2, 2, 400, d))
     dev = to_device((q, k, v), None, "f32")
-    for nsplit in (1, 3):
-        a = run_gpu(*dev, 0.1, False, **_qblock(nsplit))
-        b = run_gpu(*dev, 0.1, False, **_qblock(nsplit))
+    for kw in _plans(d, 3):
+        a = run_gpu(*dev, 0.1, False, **kw)
+        b = run_gpu(*dev, 0.1, False, **kw)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
