@@ -200,212 +200,263 @@ __device__ __forceinline__ void store_partial(float* part, int wave, int lm, int
 
 // ---------------------------------------------------------------- dK, dV
 
-// A workgroup owns 32 keys; K and V stay in registers as the B operands of S = Q K^T and
-// dP = dO V^T. Its 4 waves split the query blocks that admit any of the keys; each
-// streams its Q and dO tiles (permuted) and the block's lse2/D into private LDS slots.
+// A workgroup owns 128 keys of one (batch, head), as four 32-key blocks, and 8 waves. For
+// key block kb, wave kb (the P wave) forms S = Q K^T and P = 2^(c S - lse2) and
+// accumulates dV^T += dO^T P; wave 4 + kb (the dS wave) forms dP = dO V^T, reads that P
+// back from LDS, forms dS = P (dP - D) and accumulates dK^T += Q^T dS. A wave keeps only
+// its key block's K or V (the B operand of S or dP) and one accumulator set in registers,
+// so two waves fit a SIMD; the two waves of a key block share one, and one's MFMAs run
+// while the other works on the VALU.
+//
+// All 8 waves step through the query blocks together. Query block T's Q and dO tiles
+// (permuted), its lse2/D and, with a hard mask, the four key blocks' mask words of its rows
+// are copied straight into a ring of four LDS slots two steps ahead, each wave issuing a
+// share. In step T the P waves work on block T and the dS waves on block T - 1, whose P
+// the P waves left in LDS (fp32, double buffered) in step T - 1. One barrier per step.
+template <int D>
+struct KVGeom {
+  static constexpr int kWaves = 8;
+  static constexpr int kKB = 4;                                 // 32-key blocks per workgroup
+  static constexpr int kKeys = 32 * kKB;
+  static constexpr int kSlots = 4;
+  static constexpr int kTileBytes = HGeom<D>::kTileBytes;
+  static constexpr int kDma = HGeom<D>::kDmaPerTile;            // 1 KB copies per tile
+  static constexpr int kTileCopiesPerWave = 2 * kDma / kWaves;  // Q and dO of one block
+  static constexpr int kXBytes = 16 * 64 * 4;                   // a wave's 16 P values per lane
+  static_assert(kTileCopiesPerWave >= 1 && kTileCopiesPerWave * kWaves == 2 * kDma, "copy split");
+  static_assert(2 * kKB * kTileBytes <= kSlots * 2 * kTileBytes, "K and V stage in the ring");
+};
+
 template <int D, bool CAUSAL, bool MASKED, bool F16>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   using G = HGeom<D>;
-  // Q tile, dO tile, lse2/D, and with a hard mask the block's 32 mask words (this key block's
-  // word of each query row; the upper 32 lanes of the copy repeat them).
-  constexpr int kSlotBytes = 2 * G::kTileBytes + G::kMetaBytes + (MASKED ? 256 : 0);
-  constexpr int kStageBytes = G::kWaves * kSlotBytes;
-  constexpr int kLdsBytes = kStageBytes > 2 * G::kPartBytes ? kStageBytes : 2 * G::kPartBytes;
-  static_assert(2 * G::kTileBytes <= kSlotBytes, "K and V prologue tiles fit in wave 0's slot");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  using W = KVGeom<D>;
+  // Slot: Q tile, dO tile, lse2/D, and with a hard mask [key block][row] words.
+  constexpr int kMaskBytes = MASKED ? W::kKB * G::kRows * 4 : 0;
+  constexpr int kSlotBytes = 2 * G::kTileBytes + G::kMetaBytes + kMaskBytes;
+  constexpr int kRingBytes = W::kSlots * kSlotBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kRingBytes + 2 * W::kKB * W::kXBytes];
+  unsigned char* const xbuf = lds + kRingBytes;  // [key block][parity][4][64 lanes][4 floats]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = wave & (W::kKB - 1);
+  const bool pwave = wave < W::kKB;
   const int lm = lane & 31;
   const int lh = lane >> 5;
-  unsigned char* const q_slot = lds + wave * kSlotBytes;
-  unsigned char* const g_slot = q_slot + G::kTileBytes;
-  unsigned char* const m_slot = g_slot + G::kTileBytes;
-  unsigned char* const w_slot = m_slot + G::kMetaBytes;  // mask words (MASKED)
 
+  // Workgroups of a head are consecutive, the lowest keys (the most query blocks under a
+  // causal mask) first.
+  const uint32_t nkw = (uint32_t)(a.nkb + W::kKB - 1) / W::kKB;
   const uint32_t lam = xcd_remap(blockIdx.x, a.nwg);
-  const int64_t bh = (int64_t)(lam / (uint32_t)a.nkb);
-  const int32_t j0 = (int32_t)(lam % (uint32_t)a.nkb) * G::kRows;
+  const int64_t bh = (int64_t)(lam / nkw);
+  const int32_t j0 = (int32_t)(lam % nkw) * W::kKeys;
+  const int32_t jk = j0 + 32 * kb;  // this wave's first key
   const int32_t delta = a.seq_kv - a.seq_q;
-  // Query blocks holding a row that admits some key of this block: row i admits key j0
+  // Query blocks holding a row that admits some key of the workgroup: row i admits key j0
   // iff i >= j0 - delta.
   int32_t qb_first = 0;
   if (CAUSAL) {
     const int32_t i_min = j0 - delta;
     qb_first = i_min <= 0 ? 0 : i_min / G::kRows;
   }
-  const int32_t nq = a.nqb - qb_first;
-  const int32_t b_begin = qb_first + (int32_t)(((int64_t)nq * wave) / G::kWaves);
-  const int32_t b_end = qb_first + (int32_t)(((int64_t)nq * (wave + 1)) / G::kWaves);
+  const int32_t nblk = a.nqb > qb_first ? a.nqb - qb_first : 0;
 
-  // Rows past the end of each array lie outside these ranges and read as zeros. Q, K and
-  // V rows are q_row / kv_row bytes apart (the layout's row strides); the bf16 copy of dO
-  // is contiguous.
   const int64_t q_off = head_offset(bh, a.heads, a.qs_b, a.qs_h);
   const int64_t kv_off = head_offset(bh, a.heads, a.kvs_b, a.kvs_h);
   const unsigned q_row = (unsigned)(a.qs_s * 2), kv_row = (unsigned)(a.kvs_s * 2);
   const unsigned g_row = (unsigned)G::kRowBytes;
+  // Rows past the end of each array lie outside these ranges and read as zeros.
   const __amdgpu_buffer_rsrc_t q_rsrc = raw_buffer(a.q16 + q_off, strided_range(a.seq_q, a.qs_s, D, 2));
   const __amdgpu_buffer_rsrc_t g_rsrc =
       raw_buffer(a.dout16 + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * g_row);
   const __amdgpu_buffer_rsrc_t m_rsrc =
       raw_buffer(a.meta + (size_t)bh * a.nqb * kBwdMetaFloats, (unsigned)a.nqb * (unsigned)G::kMetaBytes);
-  const unsigned kv_range = strided_range(a.seq_kv, a.kvs_s, D, 2);
-  const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(a.k16 + kv_off, kv_range);
-  const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(a.v16 + kv_off, kv_range);
   __amdgpu_buffer_rsrc_t w_rsrc;  // rows past seq_q read as 0: nothing admitted
   if (MASKED)
     w_rsrc = raw_buffer(a.mask_bits + head_offset(bh, a.heads, a.mbits_sb, a.mbits_sh),
                         (unsigned)a.seq_q * (unsigned)a.mask_words * 4u);
 
-  auto copy_q = [&](int32_t qb) {
-    const unsigned row0 = (unsigned)(G::kRows * qb) * q_row;
+  // Copies of query block T (absolute block qb_first + T) into its ring slot: the Q and dO
+  // tiles split over the 8 waves; wave 0 adds lse2/D, waves 1 and 2 the mask words
+  // (lane l of wave 1 + h: key block 2h + l / 32, row l % 32).
+  auto issue = [&](int32_t T) {
+    const int32_t qb = qb_first + T;
+    unsigned char* const slot = lds + (T % W::kSlots) * kSlotBytes;
 #pragma unroll
-    for (int t = 0; t < G::kDmaPerTile; ++t)
-      dma_load_x4(q_rsrc, row0 + tile_src<D, true>(t, lane, q_row), lds_address(q_slot + 1024 * t));
-  };
-  auto copy_g = [&](int32_t qb) {  // dO tile, then the block's lse2 and D
-    const unsigned row0 = (unsigned)(G::kRows * qb) * g_row;
-#pragma unroll
-    for (int t = 0; t < G::kDmaPerTile; ++t)
-      dma_load_x4(g_rsrc, row0 + tile_src<D, true>(t, lane, g_row), lds_address(g_slot + 1024 * t));
-    dma_load_x1(m_rsrc, (unsigned)qb * (unsigned)G::kMetaBytes + 4u * lane, lds_address(m_slot));
-    if (MASKED)
+    for (int u = 0; u < W::kTileCopiesPerWave; ++u) {
+      const int c = u * W::kWaves + wave;  // 0 .. 2 kDma - 1: Q copies, then dO copies
+      if (c < W::kDma)
+        dma_load_x4(q_rsrc, (unsigned)(G::kRows * qb) * q_row + tile_src<D, true>(c, lane, q_row),
+                    lds_address(slot + 1024 * c));
+      else
+        dma_load_x4(g_rsrc, (unsigned)(G::kRows * qb) * g_row + tile_src<D, true>(c - W::kDma, lane, g_row),
+                    lds_address(slot + 1024 * c));
+    }
+    if (wave == 0)
+      dma_load_x1(m_rsrc, (unsigned)qb * (unsigned)G::kMetaBytes + 4u * lane,
+                  lds_address(slot + 2 * G::kTileBytes));
+    if (MASKED && (wave == 1 || wave == 2)) {
+      const int kbw = 2 * (wave - 1) + (lane >> 5);
       dma_load_x1(w_rsrc, ((unsigned)(G::kRows * qb + (lane & 31)) * (unsigned)a.mask_words +
-                           (unsigned)(j0 / G::kRows)) * 4u, lds_address(w_slot));
+                           (unsigned)(j0 / 32 + kbw)) * 4u,
+                  lds_address(slot + 2 * G::kTileBytes + G::kMetaBytes + 256 * (wave - 1)));
+    }
+  };
+  // Wait until this wave's copies of every block but the last one issued have landed.
+  auto wait_all_but_last_block = [&]() {
+    if (wave == 0 || (MASKED && (wave == 1 || wave == 2))) wait_vmcnt<W::kTileCopiesPerWave + 1>();
+    else wait_vmcnt<W::kTileCopiesPerWave>();
   };
 
-  // This block's K and V tiles (unpermuted), staged through wave 0's slot (each wave
-  // copies a share), into the B operands: lane (key m, h) holds head dims
-  // 16*st + 8*h .. + 7 of key m for k-step st.
-  bf16x8 kr[G::kSteps], vr[G::kSteps];
+  // The four key blocks' K and V tiles (unpermuted), staged through the ring (each wave
+  // copies a share), into the B operands: the P wave of key block kb takes K, the dS wave
+  // V; lane (key m, h) holds head dims 16*st + 8*h .. + 7 of key jk + m for k-step st.
+  const unsigned kv_range = strided_range(a.seq_kv, a.kvs_s, D, 2);
+  bf16x8 kv[G::kSteps];
   {
-    unsigned char* const k_tile = lds;
-    unsigned char* const v_tile = lds + G::kTileBytes;
-    const unsigned row0 = (unsigned)j0 * kv_row;
+    const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(a.k16 + kv_off, kv_range);
+    const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(a.v16 + kv_off, kv_range);
+    constexpr int kCopies = 2 * W::kKB * W::kDma;  // K tiles, then V tiles
 #pragma unroll
-    for (int i = 0; i < G::kDmaPerTile / G::kWaves; ++i) {
-      const int t = i * G::kWaves + wave;
-      dma_load_x4(k_rsrc, row0 + tile_src<D, false>(t, lane, kv_row), lds_address(k_tile + 1024 * t));
-      dma_load_x4(v_rsrc, row0 + tile_src<D, false>(t, lane, kv_row), lds_address(v_tile + 1024 * t));
+    for (int u = 0; u < kCopies / W::kWaves; ++u) {
+      const int c = u * W::kWaves + wave;
+      const int tensor = c / (W::kKB * W::kDma), kbc = (c / W::kDma) % W::kKB, t = c % W::kDma;
+      const unsigned src = (unsigned)(j0 + 32 * kbc) * kv_row + tile_src<D, false>(t, lane, kv_row);
+      dma_load_x4(tensor == 0 ? k_rsrc : v_rsrc, src, lds_address(lds + 1024 * c));
     }
     wait_vmcnt<0>();
     __syncthreads();
+    const unsigned char* tile = lds + (pwave ? kb : W::kKB + kb) * G::kTileBytes;
 #pragma unroll
-    for (int st = 0; st < G::kSteps; ++st) {
-      kr[st] = row_chunk<D>(k_tile, lm, 2 * st + lh);
-      vr[st] = row_chunk<D>(v_tile, lm, 2 * st + lh);
-    }
+    for (int st = 0; st < G::kSteps; ++st) kv[st] = row_chunk<D>(tile, lm, 2 * st + lh);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the operand reads have returned
-    __syncthreads();                     // before wave 0 reuses its slot
+    __syncthreads();                     // before the ring takes the space
   }
 
-  f32x16 dv[G::kNch], dk[G::kNch];
+  f32x16 acc[G::kNch];  // dV (P waves) or dK (dS waves)
 #pragma unroll
   for (int cb = 0; cb < G::kNch; ++cb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dv[cb][r] = dk[cb][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
-  if (b_begin < b_end) {
-    copy_g(b_begin);
-    copy_q(b_begin);
-  }
-  for (int32_t qb = b_begin; qb < b_end; ++qb) {
-    const int32_t i0 = G::kRows * qb;
-    // The dO tile and lse2/D of block qb have landed (its Q tile, issued after them, may
-    // still be in flight).
-    wait_vmcnt<G::kDmaPerTile>();
-    // lse2 and D of this lane's queries perm_acc_row(r, lh): rows 16t + 8h + 0..7, t = 0, 1.
-    f32x4 l2[4], dd[4];
+  // Whether query block qb reaches this wave's keys at all, and whether some of its pairs
+  // are masked by the causal bound (its last key past its first row's limit).
+  auto reaches = [&](int32_t qb) {
+    return jk < a.seq_kv && (!CAUSAL || G::kRows * qb + G::kRows - 1 + delta >= jk);
+  };
+
+  if (nblk > 0) issue(0);
+  if (nblk > 1) issue(1);
+  for (int32_t T = 0; T <= nblk; ++T) {
+    if (T + 1 < nblk) wait_all_but_last_block();
+    else wait_vmcnt<0>();
+    __syncthreads();  // block T has landed; step T - 1 is done with its slots and P
+    if (T + 2 < nblk) issue(T + 2);
+    if (pwave) {
+      const int32_t qb = qb_first + T;
+      if (T < nblk && reaches(qb)) {
+        const int32_t i0 = G::kRows * qb;
+        const unsigned char* const q_slot = lds + (T % W::kSlots) * kSlotBytes;
+        const unsigned char* const g_slot = q_slot + G::kTileBytes;
+        const unsigned char* const m_slot = g_slot + G::kTileBytes;
+        // lse2 of this lane's queries perm_acc_row(r, lh): rows 16t + 8h + 0..7, t = 0, 1.
+        f32x4 l2[4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int row = 16 * (q4 / 2) + 8 * lh + 4 * (q4 % 2);
-      l2[q4] = *reinterpret_cast<const f32x4*>(m_slot + 4 * row);
-      dd[q4] = *reinterpret_cast<const f32x4*>(m_slot + 4 * (G::kRows + row));
-    }
-    f32x16 dp, s;
+        for (int q4 = 0; q4 < 4; ++q4)
+          l2[q4] = *reinterpret_cast<const f32x4*>(m_slot + 4 * (16 * (q4 / 2) + 8 * lh + 4 * (q4 % 2)));
+        f32x16 s;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dp[r] = s[r] = 0.f;
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int st = 0; st < G::kSteps; ++st) dp = mfma16<F16>(row_chunk<D>(g_slot, lm, 2 * st + lh), vr[st], dp);
-    wait_vmcnt<0>();  // the Q tile
+        for (int st = 0; st < G::kSteps; ++st) s = mfma16<F16>(row_chunk<D>(q_slot, lm, 2 * st + lh), kv[st], s);
+        __builtin_amdgcn_s_setprio(0);
+        const bool diag = CAUSAL && (jk + G::kRows - 1 > i0 + delta);
+        uint32_t mw[16];  // mask word of query row perm_acc_row(r, lh); bit lm is this lane's key
+        if (MASKED) {
+          const unsigned char* const w_slot = m_slot + G::kMetaBytes + 4 * G::kRows * kb;
 #pragma unroll
-    for (int st = 0; st < G::kSteps; ++st) s = mfma16<F16>(row_chunk<D>(q_slot, lm, 2 * st + lh), kr[st], s);
-    // Some pair of this block is masked iff its last key lies past its first row's limit.
-    const bool diag = CAUSAL && (j0 + G::kRows - 1 > i0 + delta);
-    uint32_t mw[16];  // mask word of query row perm_acc_row(r, lh); bit lm is this lane's key
-    if (MASKED) {
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const u32x4 w4 = *reinterpret_cast<const u32x4*>(w_slot + 4 * (16 * (q4 / 2) + 8 * lh + 4 * (q4 % 2)));
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const u32x4 w4 = *reinterpret_cast<const u32x4*>(w_slot + 4 * (16 * (q4 / 2) + 8 * lh + 4 * (q4 % 2)));
+            for (int e = 0; e < 4; ++e) mw[4 * q4 + e] = w4[e];
+          }
+        }
+        f32x4 p32[4];
+        bf16x8 pp[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mw[4 * q4 + e] = w4[e];
+        for (int r = 0; r < 16; ++r) {
+          float t = s[r] * a.c - l2[r / 4][r % 4];
+          if (diag) t = (jk + lm <= i0 + perm_acc_row(r, lh) + delta) ? t : -INFINITY;
+          if (MASKED) t = ((mw[r] >> lm) & 1u) ? t : -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(t);
+          p32[r / 4][r % 4] = p;
+          pp[r / 8][r % 8] = round16<F16>(p);
+        }
+        unsigned char* const xp = xbuf + (2 * kb + (T & 1)) * W::kXBytes + 16 * lane;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) *reinterpret_cast<f32x4*>(xp + 1024 * c4) = p32[c4];
+        // dV^T += dO^T P
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int cb = 0; cb < G::kNch; ++cb) acc[cb] = mfma16<F16>(tr_operand<D>(g_slot, lane, t2, cb), pp[t2], acc[cb]);
+        __builtin_amdgcn_s_setprio(0);
+      }
+    } else {
+      const int32_t qb = qb_first + T - 1;
+      if (T >= 1 && reaches(qb)) {
+        const unsigned char* const q_slot = lds + ((T - 1) % W::kSlots) * kSlotBytes;
+        const unsigned char* const g_slot = q_slot + G::kTileBytes;
+        const unsigned char* const m_slot = g_slot + G::kTileBytes;
+        f32x16 dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int st = 0; st < G::kSteps; ++st) dp = mfma16<F16>(row_chunk<D>(g_slot, lm, 2 * st + lh), kv[st], dp);
+        __builtin_amdgcn_s_setprio(0);
+        f32x4 dd[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          dd[q4] = *reinterpret_cast<const f32x4*>(m_slot + 4 * (G::kRows + 16 * (q4 / 2) + 8 * lh + 4 * (q4 % 2)));
+        const unsigned char* const xp = xbuf + (2 * kb + ((T - 1) & 1)) * W::kXBytes + 16 * lane;
+        bf16x8 pds[2];
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const f32x4 p4 = *reinterpret_cast<const f32x4*>(xp + 1024 * c4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * c4 + e;
+            pds[r / 8][r % 8] = round16<F16>(p4[e] * (dp[r] - dd[c4][e]));
+          }
+        }
+        // dK^T += Q^T dS (the scale is applied once, at the end)
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int cb = 0; cb < G::kNch; ++cb) acc[cb] = mfma16<F16>(tr_operand<D>(q_slot, lane, t2, cb), pds[t2], acc[cb]);
+        __builtin_amdgcn_s_setprio(0);
       }
     }
-    bf16x8 pp[2], pds[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float t = s[r] * a.c - l2[r / 4][r % 4];
-      if (diag) t = (j0 + lm <= i0 + perm_acc_row(r, lh) + delta) ? t : -INFINITY;
-      if (MASKED) t = ((mw[r] >> lm) & 1u) ? t : -INFINITY;
-      const float p = __builtin_amdgcn_exp2f(t);
-      const float ds = p * (dp[r] - dd[r / 4][r % 4]);
-      pp[r / 8][r % 8] = round16<F16>(p);
-      pds[r / 8][r % 8] = round16<F16>(ds);
-    }
-    // dV^T += dO^T P
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int cb = 0; cb < G::kNch; ++cb) dv[cb] = mfma16<F16>(tr_operand<D>(g_slot, lane, t2, cb), pp[t2], dv[cb]);
-    if (qb + 1 < b_end) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading the dO and lse2/D slots
-      copy_g(qb + 1);
-    }
-    // dK^T += Q^T dS (the scale is applied once, at the end)
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int cb = 0; cb < G::kNch; ++cb) dk[cb] = mfma16<F16>(tr_operand<D>(q_slot, lane, t2, cb), pds[t2], dk[cb]);
-    if (qb + 1 < b_end) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading the Q slot
-      copy_q(qb + 1);
-    }
   }
 
-  // Partials -> LDS as [wave][key][head dim], then summed over the waves.
-  __syncthreads();
-  float* const part_v = reinterpret_cast<float*>(lds);
-  float* const part_k = part_v + G::kWaves * G::kRows * G::kPStride;
-  store_partial<D>(part_v, wave, lm, lh, dv);
-  store_partial<D>(part_k, wave, lm, lh, dk);
-  __syncthreads();
-  constexpr int kThreadsPerRow = D / 4;
-  constexpr int kRowsPerPass = 256 / kThreadsPerRow;
+  // Lane (key m, h) holds head dims 32*cb + 8*g4 + 4*h .. + 3 of key jk + m.
+  const int32_t j = jk + lm;
+  if (j >= a.seq_kv) return;
+  float* const out = (pwave ? a.dv : a.dk) + kv_off + (int64_t)j * a.kvs_s;
+  const float mul = pwave ? 1.0f : a.scale;
 #pragma unroll
-  for (int pass = 0; pass < G::kRows / kRowsPerPass; ++pass) {
-    const int key = pass * kRowsPerPass + tid / kThreadsPerRow;
-    const int c4 = tid % kThreadsPerRow;
-    const int32_t j = j0 + key;
-    f32x4 sv = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < G::kNch; ++cb)
 #pragma unroll
-    for (int w = 0; w < G::kWaves; ++w) {
-      const f32x4 xv = *reinterpret_cast<const f32x4*>(part_v + (w * G::kRows + key) * G::kPStride + 4 * c4);
-      const f32x4 xk = *reinterpret_cast<const f32x4*>(part_k + (w * G::kRows + key) * G::kPStride + 4 * c4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sv[e] += xv[e];
-        sk[e] += xk[e];
-      }
-    }
-    if (j >= a.seq_kv) continue;
-    const int64_t off = kv_off + (int64_t)j * a.kvs_s + 4 * c4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sk[e] *= a.scale;
-    *reinterpret_cast<f32x4*>(a.dv + off) = sv;
-    *reinterpret_cast<f32x4*>(a.dk + off) = sk;
-  }
+    for (int g4 = 0; g4 < 4; ++g4)
+      *reinterpret_cast<f32x4*>(out + 32 * cb + 8 * g4 + 4 * lh) =
+          f32x4{acc[cb][4 * g4] * mul, acc[cb][4 * g4 + 1] * mul, acc[cb][4 * g4 + 2] * mul,
+                acc[cb][4 * g4 + 3] * mul};
 }
 
 // ---------------------------------------------------------------- dQ
@@ -588,8 +639,8 @@ hipError_t launch_bwd_bf16_variant(const BwdArgs& a0, hipStream_t s, hipEvent_t 
   }
   if (ev_pre && hipEventRecord(ev_pre, s) != hipSuccess) return hipErrorInvalidValue;
   if (nk > 0) {
-    a.nwg = nk;
-    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, CAUSAL, MASKED, F16>), dim3(nk), dim3(256), 0, s, a);
+    a.nwg = (uint32_t)(a.bh * ((a.nkb + KVGeom<D>::kKB - 1) / KVGeom<D>::kKB));
+    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, CAUSAL, MASKED, F16>), dim3(a.nwg), dim3(512), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   if (ev_dkdv && hipEventRecord(ev_dkdv, s) != hipSuccess) return hipErrorInvalidValue;

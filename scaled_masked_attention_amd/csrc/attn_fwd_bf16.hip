@@ -262,6 +262,7 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
     V8 vop[kPf + 1];
 #pragma unroll
     for (int i = 0; i < kPf; ++i) vop[i] = v_operand(i);
+    __builtin_amdgcn_s_setprio(1);  // as for the score MFMAs
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
       if (i + kPf < kN) vop[(i + kPf) % (kPf + 1)] = v_operand(i + kPf);
@@ -270,6 +271,7 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
       oacc[cb] = H::mfma(vop[i % (kPf + 1)], pb[kb][t2], oacc[cb]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Scores, lazy running max and probabilities of tile T (in ring slot
@@ -297,6 +299,10 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
     for (int st = 0; st < kPf; ++st)
 #pragma unroll
       for (int kb = 0; kb < G::kKB; ++kb) kop[st][kb] = k_operand(kb, st);
+    // While a wave issues its MFMAs it runs at raised priority, so that the
+    // other wave on the SIMD (in its softmax, on the VALU) fills the issue
+    // slots between them rather than competing for the matrix core.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int st = 0; st < G::kSteps; ++st) {
       if (st + kPf < G::kSteps)
@@ -308,6 +314,8 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
         sacc[kb] = H::mfma(kop[st % (kPf + 1)][kb], qr[st], sacc[kb]);
       __builtin_amdgcn_sched_barrier(0);
     }
+
+    __builtin_amdgcn_s_setprio(0);
 
     // Boundary tiles (the causal diagonal, the end of the keys): excluded
     // scores become -inf, so that they enter neither the max nor the sum
