@@ -49,7 +49,6 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 template <int D>
 struct HGeom {
-  static constexpr int kWaves = 4;
   static constexpr int kRows = kBwdRowsPerBlock;    // rows per query / key block
   static constexpr int kSteps = D / 16;             // k-steps of the score products
   static constexpr int kNch = D / 32;               // 32-wide output chunks
@@ -58,10 +57,7 @@ struct HGeom {
   static constexpr int kTileBytes = kRows * kRowBytes;
   static constexpr int kDmaPerTile = kTileBytes / 1024;
   static constexpr int kMetaBytes = kBwdMetaFloats * 4;
-  static constexpr int kPStride = D + 4;            // padded partial-gradient row (floats)
-  static constexpr int kPartBytes = kWaves * kRows * kPStride * 4;
   static_assert(kRows == 32, "one 32x32 MFMA tile per block");
-  static_assert(kDmaPerTile % kWaves == 0, "shared tile copies split evenly over the waves");
   static_assert(kBwdMetaFloats == 64, "one 4-byte direct-to-LDS load per block's lse2 and D");
 };
 
@@ -181,21 +177,6 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(BwdArgs a) {
       meta[kBwdRowsPerBlock + r] = live ? d : 0.f;
     }
   }
-}
-
-// Partial gradients of the 4 waves, [wave][row][head dim] in LDS, from accumulators whose
-// lane (n, h) holds head dims 32*cb + 8*(r/4) + 4*h + r%4 of row n.
-template <int D>
-__device__ __forceinline__ void store_partial(float* part, int wave, int lm, int lh,
-                                              const f32x16 (&acc)[HGeom<D>::kNch]) {
-  using G = HGeom<D>;
-  float* const row = part + (wave * G::kRows + lm) * G::kPStride;
-#pragma unroll
-  for (int cb = 0; cb < G::kNch; ++cb)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4)
-      *reinterpret_cast<f32x4*>(row + 32 * cb + 8 * g4 + 4 * lh) =
-          f32x4{acc[cb][4 * g4], acc[cb][4 * g4 + 1], acc[cb][4 * g4 + 2], acc[cb][4 * g4 + 3]};
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -384,14 +365,27 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
             for (int e = 0; e < 4; ++e) mw[4 * q4 + e] = w4[e];
           }
         }
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[r] = s[r] * a.c - l2[r / 4][r % 4];
+        if (diag) {
+          // Key jk + lm is admitted to row i0 + perm_acc_row(r, lh) iff
+          // 16 (r / 8) + r % 8 >= rel. The empty asm keeps the bound, and with it the
+          // comparisons, inside this branch.
+          int32_t rel = jk + lm - i0 - delta - 8 * lh;
+          asm volatile("" : "+v"(rel));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) t[r] = 16 * (r / 8) + r % 8 >= rel ? t[r] : -INFINITY;
+        }
+        if (MASKED) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) t[r] = ((mw[r] >> lm) & 1u) ? t[r] : -INFINITY;
+        }
         f32x4 p32[4];
         bf16x8 pp[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float t = s[r] * a.c - l2[r / 4][r % 4];
-          if (diag) t = (jk + lm <= i0 + perm_acc_row(r, lh) + delta) ? t : -INFINITY;
-          if (MASKED) t = ((mw[r] >> lm) & 1u) ? t : -INFINITY;
-          const float p = __builtin_amdgcn_exp2f(t);
+          const float p = __builtin_amdgcn_exp2f(t[r]);
           p32[r / 4][r % 4] = p;
           pp[r / 8][r % 8] = round16<F16>(p);
         }
@@ -461,54 +455,56 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- dQ
 
-// A workgroup owns 32 queries; Q and dO stay in registers as the B operands of
-// S^T = K Q^T and dP^T = V dO^T. Its 4 waves split the key blocks the rows admit; each
-// streams its K and V tiles (permuted) into private LDS slots.
+// A workgroup owns 256 queries of one (batch, head), a 32-row block per wave; each wave
+// keeps its rows' Q and dO in registers as the B operands of S^T = K Q^T and
+// dP^T = V dO^T, and accumulates dQ^T += K^T dS^T. The waves step through the key blocks
+// the workgroup's rows admit together: key block T's K and V tiles (permuted) and, with a
+// hard mask, the rows' words of block T are copied straight into a ring of four LDS slots
+// three steps ahead, each wave issuing a share. One barrier per step.
+template <int D>
+struct QGeom {
+  static constexpr int kWaves = 8;
+  static constexpr int kQ = 32 * kWaves;  // queries per workgroup
+  static constexpr int kSlots = 4;
+  static constexpr int kDma = HGeom<D>::kDmaPerTile;
+  static constexpr int kTileCopiesPerWave = 2 * kDma / kWaves;  // K and V of one block
+  static_assert(kTileCopiesPerWave >= 1 && kTileCopiesPerWave * kWaves == 2 * kDma, "copy split");
+};
+
 template <int D, bool CAUSAL, bool MASKED, bool F16>
-__global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   using G = HGeom<D>;
-  // K tile, V tile, and with a hard mask each query row's word of the key block.
-  constexpr int kSlotBytes = 2 * G::kTileBytes + (MASKED ? 256 : 0);
-  constexpr int kStageBytes = G::kWaves * kSlotBytes;
-  constexpr int kLdsBytes = kStageBytes > G::kPartBytes ? kStageBytes : G::kPartBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  using W = QGeom<D>;
+  // Slot: K tile, V tile, and with a hard mask the workgroup rows' words of the key block.
+  constexpr int kMaskBytes = MASKED ? 4 * W::kQ : 0;
+  constexpr int kSlotBytes = 2 * G::kTileBytes + kMaskBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[W::kSlots * kSlotBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lm = lane & 31;
   const int lh = lane >> 5;
-  unsigned char* const k_slot = lds + wave * kSlotBytes;
-  unsigned char* const v_slot = k_slot + G::kTileBytes;
-  unsigned char* const w_slot = v_slot + G::kTileBytes;  // mask words (MASKED)
 
-  // Workgroup -> (batch*head, query block), the longest causal blocks first.
+  // Workgroups of a head are consecutive, the last queries (the most key blocks under a
+  // causal mask) first.
+  const uint32_t nqw = (uint32_t)(a.nqb + W::kWaves - 1) / W::kWaves;
   const uint32_t lam = xcd_remap(blockIdx.x, a.nwg);
-  const int64_t bh = (int64_t)(lam / (uint32_t)a.nqb);
-  const int32_t qb = a.nqb - 1 - (int32_t)(lam % (uint32_t)a.nqb);
-  const int32_t q0 = qb * G::kRows;
+  const int64_t bh = (int64_t)(lam / nqw);
+  const int32_t q0 = (int32_t)(nqw - 1 - lam % nqw) * W::kQ;
+  const int32_t qw0 = q0 + 32 * wave;  // this wave's first row
+  const bool wave_live = qw0 < a.seq_q;
 
-  const int32_t my_row = q0 + lm;
-  const int32_t last_row = min(q0 + G::kRows - 1, a.seq_q - 1);
+  const int32_t my_row = qw0 + lm;
+  const int32_t last_row = min(q0 + W::kQ - 1, a.seq_q - 1);
+  const int32_t nblk = (key_limit<CAUSAL>(last_row, a.seq_q, a.seq_kv, a.seq_kv) + G::kRows - 1) / G::kRows;
   const int32_t lim = key_limit<CAUSAL>(my_row, a.seq_q, a.seq_kv, a.seq_kv);
-  const int32_t lo = key_limit<CAUSAL>(q0, a.seq_q, a.seq_kv, a.seq_kv);
-  const int32_t hi = key_limit<CAUSAL>(last_row, a.seq_q, a.seq_kv, a.seq_kv);
-  const int32_t nblocks = (hi + G::kRows - 1) / G::kRows;
-  const int32_t b_begin = (int32_t)(((int64_t)nblocks * wave) / G::kWaves);
-  const int32_t b_end = (int32_t)(((int64_t)nblocks * (wave + 1)) / G::kWaves);
-
-  // lse2 and D of this lane's query (the preprocess pads past seq_q).
-  const float* const meta = a.meta + ((size_t)bh * a.nqb + qb) * kBwdMetaFloats;
-  const float my_l2 = meta[lm];
-  const float my_d = meta[G::kRows + lm];
+  const int32_t wave_lo = key_limit<CAUSAL>(qw0, a.seq_q, a.seq_kv, a.seq_kv);
+  const int32_t wave_hi = key_limit<CAUSAL>(min(qw0 + 31, a.seq_q - 1), a.seq_q, a.seq_kv, a.seq_kv);
 
   const int64_t q_off = head_offset(bh, a.heads, a.qs_b, a.qs_h);
   const int64_t kv_off = head_offset(bh, a.heads, a.kvs_b, a.kvs_h);
-  const unsigned q_row = (unsigned)(a.qs_s * 2), kv_row = (unsigned)(a.kvs_s * 2);
-  const unsigned g_row = (unsigned)G::kRowBytes;
-  const __amdgpu_buffer_rsrc_t q_rsrc = raw_buffer(a.q16 + q_off, strided_range(a.seq_q, a.qs_s, D, 2));
-  const __amdgpu_buffer_rsrc_t g_rsrc =
-      raw_buffer(a.dout16 + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * g_row);
+  const unsigned kv_row = (unsigned)(a.kvs_s * 2);
   const unsigned kv_range = strided_range(a.seq_kv, a.kvs_s, D, 2);
   const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(a.k16 + kv_off, kv_range);
   const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(a.v16 + kv_off, kv_range);
@@ -516,42 +512,61 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   if (MASKED)
     w_rsrc = raw_buffer(a.mask_bits + head_offset(bh, a.heads, a.mbits_sb, a.mbits_sh),
                         (unsigned)a.seq_q * (unsigned)a.mask_words * 4u);
-  auto copy_k = [&](int32_t b) {  // K tile, then the rows' mask words of block b
-    const unsigned row0 = (unsigned)(G::kRows * b) * kv_row;
+
+  // Copies of key block T into its ring slot: the K and V tiles split over the 8 waves;
+  // with a hard mask waves 0-3 add the words of 64 rows each.
+  auto issue = [&](int32_t T) {
+    unsigned char* const slot = lds + (T % W::kSlots) * kSlotBytes;
+    const unsigned row0 = (unsigned)(G::kRows * T) * kv_row;
 #pragma unroll
-    for (int t = 0; t < G::kDmaPerTile; ++t)
-      dma_load_x4(k_rsrc, row0 + tile_src<D, true>(t, lane, kv_row), lds_address(k_slot + 1024 * t));
-    if (MASKED)
-      dma_load_x1(w_rsrc, ((unsigned)(q0 + (lane & 31)) * (unsigned)a.mask_words + (unsigned)b) * 4u,
-                  lds_address(w_slot));
+    for (int u = 0; u < W::kTileCopiesPerWave; ++u) {
+      const int c = u * W::kWaves + wave;  // K copies, then V copies
+      if (c < W::kDma)
+        dma_load_x4(k_rsrc, row0 + tile_src<D, true>(c, lane, kv_row), lds_address(slot + 1024 * c));
+      else
+        dma_load_x4(v_rsrc, row0 + tile_src<D, true>(c - W::kDma, lane, kv_row), lds_address(slot + 1024 * c));
+    }
+    if (MASKED && wave < 4)
+      dma_load_x1(w_rsrc, ((unsigned)(q0 + 64 * wave + lane) * (unsigned)a.mask_words + (unsigned)T) * 4u,
+                  lds_address(slot + 2 * G::kTileBytes + 256 * wave));
   };
-  auto copy_v = [&](int32_t b) {
-    const unsigned row0 = (unsigned)(G::kRows * b) * kv_row;
-#pragma unroll
-    for (int t = 0; t < G::kDmaPerTile; ++t)
-      dma_load_x4(v_rsrc, row0 + tile_src<D, true>(t, lane, kv_row), lds_address(v_slot + 1024 * t));
+  // Wait until at most the copies of the last n blocks issued are in flight.
+  auto wait_blocks = [&](int n) {
+    if (MASKED && wave < 4) {
+      constexpr int c = W::kTileCopiesPerWave + 1;
+      if (n >= 2) wait_vmcnt<2 * c>();
+      else if (n == 1) wait_vmcnt<c>();
+      else wait_vmcnt<0>();
+    } else {
+      constexpr int c = W::kTileCopiesPerWave;
+      if (n >= 2) wait_vmcnt<2 * c>();
+      else if (n == 1) wait_vmcnt<c>();
+      else wait_vmcnt<0>();
+    }
   };
 
-  // The Q and dO tiles of this block (unpermuted), staged through wave 0's slot, into the
-  // B operands: lane (query m, h) holds head dims 16*st + 8*h .. + 7 of query m.
+  // This wave's rows: lse2 and D (the preprocess pads past seq_q), and Q and dO as B
+  // operands: lane (query m, h) holds head dims 16*st + 8*h .. + 7 of row qw0 + m (zeros
+  // past seq_q).
+  float my_l2 = INFINITY, my_d = 0.f;
   bf16x8 qr[G::kSteps], gr[G::kSteps];
   {
-#pragma unroll
-    for (int i = 0; i < G::kDmaPerTile / G::kWaves; ++i) {
-      const int t = i * G::kWaves + wave;
-      dma_load_x4(q_rsrc, (unsigned)q0 * q_row + tile_src<D, false>(t, lane, q_row), lds_address(lds + 1024 * t));
-      dma_load_x4(g_rsrc, (unsigned)q0 * g_row + tile_src<D, false>(t, lane, g_row),
-                  lds_address(lds + G::kTileBytes + 1024 * t));
+    const bool row_ok = my_row < a.seq_q;
+    if (wave_live) {
+      const float* const meta = a.meta + ((size_t)bh * a.nqb + qw0 / G::kRows) * kBwdMetaFloats;
+      my_l2 = meta[lm];
+      my_d = meta[G::kRows + lm];
     }
-    wait_vmcnt<0>();
-    __syncthreads();
+    const unsigned short* const qrow = a.q16 + q_off + (int64_t)(row_ok ? my_row : 0) * a.qs_s;
+    const unsigned short* const grow = a.dout16 + ((size_t)bh * a.seq_q + (row_ok ? my_row : 0)) * D;
 #pragma unroll
     for (int st = 0; st < G::kSteps; ++st) {
-      qr[st] = row_chunk<D>(lds, lm, 2 * st + lh);
-      gr[st] = row_chunk<D>(lds + G::kTileBytes, lm, 2 * st + lh);
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      const u32x4 xq = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * lh) : zero;
+      const u32x4 xg = row_ok ? *reinterpret_cast<const u32x4*>(grow + 16 * st + 8 * lh) : zero;
+      qr[st] = __builtin_bit_cast(bf16x8, xq);
+      gr[st] = __builtin_bit_cast(bf16x8, xg);
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __syncthreads();                     // before wave 0 reuses its slot
   }
 
   f32x16 dq[G::kNch];
@@ -560,72 +575,67 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[cb][r] = 0.f;
 
-  if (b_begin < b_end) {
-    copy_v(b_begin);
-    copy_k(b_begin);
-  }
-  for (int32_t b = b_begin; b < b_end; ++b) {
-    const int32_t j0 = G::kRows * b;
-    wait_vmcnt<G::kDmaPerTile>();  // V block b (K block b may still be in flight)
+#pragma unroll
+  for (int T = 0; T < W::kSlots - 1; ++T)
+    if (T < nblk) issue(T);
+  for (int32_t T = 0; T < nblk; ++T) {
+    wait_blocks(min(nblk - 1 - T, W::kSlots - 2));
+    __syncthreads();  // block T has landed; step T - 1 is done with its slot
+    if (T + W::kSlots - 1 < nblk) issue(T + W::kSlots - 1);
+    const int32_t j0 = G::kRows * T;
+    if (!wave_live || j0 >= wave_hi) continue;
+    const unsigned char* const k_slot = lds + (T % W::kSlots) * kSlotBytes;
+    const unsigned char* const v_slot = k_slot + G::kTileBytes;
     f32x16 dp, s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) dp[r] = s[r] = 0.f;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int st = 0; st < G::kSteps; ++st) dp = mfma16<F16>(row_chunk<D>(v_slot, lm, 2 * st + lh), gr[st], dp);
-    if (b + 1 < b_end) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading the V slot
-      copy_v(b + 1);
-      wait_vmcnt<G::kDmaPerTile>();        // K block b (V block b+1 may still be in flight)
-    } else {
-      wait_vmcnt<0>();
-    }
 #pragma unroll
     for (int st = 0; st < G::kSteps; ++st) s = mfma16<F16>(row_chunk<D>(k_slot, lm, 2 * st + lh), qr[st], s);
-    const bool edge = j0 + G::kRows > lo;  // some key of the block lies past the first row's limit
-    const uint32_t mw = MASKED ? *reinterpret_cast<const uint32_t*>(w_slot + 4 * lm) : ~0u;
+    __builtin_amdgcn_s_setprio(0);
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[r] = s[r] * a.c - my_l2;
+    if (j0 + G::kRows > wave_lo) {  // some key of the block lies past the first row's limit
+      // Key j0 + perm_acc_row(r, lh) is admitted iff 16 (r / 8) + r % 8 < rel (the empty
+      // asm keeps the comparisons inside this branch).
+      int32_t rel = lim - j0 - 8 * lh;
+      asm volatile("" : "+v"(rel));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[r] = 16 * (r / 8) + r % 8 < rel ? t[r] : -INFINITY;
+    }
+    if (MASKED) {
+      const uint32_t mw = *reinterpret_cast<const uint32_t*>(v_slot + G::kTileBytes + 4 * (32 * wave + lm));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[r] = ((mw >> perm_acc_row(r, lh)) & 1u) ? t[r] : -INFINITY;
+    }
     bf16x8 pds[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float t = s[r] * a.c - my_l2;
-      if (edge) t = (j0 + perm_acc_row(r, lh) < lim) ? t : -INFINITY;
-      if (MASKED) t = ((mw >> perm_acc_row(r, lh)) & 1u) ? t : -INFINITY;
-      const float p = __builtin_amdgcn_exp2f(t);
+      const float p = __builtin_amdgcn_exp2f(t[r]);
       pds[r / 8][r % 8] = round16<F16>(p * (dp[r] - my_d));
     }
     // dQ^T += K^T dS^T
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int cb = 0; cb < G::kNch; ++cb) dq[cb] = mfma16<F16>(tr_operand<D>(k_slot, lane, t2, cb), pds[t2], dq[cb]);
-    if (b + 1 < b_end) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading the K slot
-      copy_k(b + 1);
-    }
+    __builtin_amdgcn_s_setprio(0);
   }
 
-  __syncthreads();
-  float* const part = reinterpret_cast<float*>(lds);
-  store_partial<D>(part, wave, lm, lh, dq);
-  __syncthreads();
-  constexpr int kThreadsPerRow = D / 4;
-  constexpr int kRowsPerPass = 256 / kThreadsPerRow;
+  // Lane (query m, h) holds head dims 32*cb + 8*g4 + 4*h .. + 3 of row qw0 + m.
+  if (!wave_live || my_row >= a.seq_q) return;
+  float* const out = a.dq + q_off + (int64_t)my_row * a.qs_s;
 #pragma unroll
-  for (int pass = 0; pass < G::kRows / kRowsPerPass; ++pass) {
-    const int qi = pass * kRowsPerPass + tid / kThreadsPerRow;
-    const int c4 = tid % kThreadsPerRow;
-    const int32_t row = q0 + qi;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < G::kNch; ++cb)
 #pragma unroll
-    for (int w = 0; w < G::kWaves; ++w) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(part + (w * G::kRows + qi) * G::kPStride + 4 * c4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += x[e];
-    }
-    if (row >= a.seq_q) continue;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] *= a.scale;
-    *reinterpret_cast<f32x4*>(a.dq + q_off + (int64_t)row * a.qs_s + 4 * c4) = acc;
-  }
+    for (int g4 = 0; g4 < 4; ++g4)
+      *reinterpret_cast<f32x4*>(out + 32 * cb + 8 * g4 + 4 * lh) =
+          f32x4{dq[cb][4 * g4] * a.scale, dq[cb][4 * g4 + 1] * a.scale, dq[cb][4 * g4 + 2] * a.scale,
+                dq[cb][4 * g4 + 3] * a.scale};
 }
 
 template <int D, bool CAUSAL, bool MASKED, bool F16>
@@ -645,8 +655,8 @@ hipError_t launch_bwd_bf16_variant(const BwdArgs& a0, hipStream_t s, hipEvent_t 
   }
   if (ev_dkdv && hipEventRecord(ev_dkdv, s) != hipSuccess) return hipErrorInvalidValue;
   if (nq > 0) {
-    a.nwg = nq;
-    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, CAUSAL, MASKED, F16>), dim3(nq), dim3(256), 0, s, a);
+    a.nwg = (uint32_t)(a.bh * ((a.nqb + QGeom<D>::kWaves - 1) / QGeom<D>::kWaves));
+    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, CAUSAL, MASKED, F16>), dim3(a.nwg), dim3(512), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   return hipSuccess;
