@@ -328,14 +328,21 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
     return jk < a.seq_kv && (!CAUSAL || G::kRows * qb + G::kRows - 1 + delta >= jk);
   };
 
-  if (nblk > 0) issue(0);
-  if (nblk > 1) issue(1);
-  for (int32_t T = 0; T <= nblk; ++T) {
-    if (T + 1 < nblk) wait_all_but_last_block();
-    else wait_vmcnt<0>();
-    __syncthreads();  // block T has landed; step T - 1 is done with its slots and P
-    if (T + 2 < nblk) issue(T + 2);
-    if (pwave) {
+  // The step loop (its waits, barrier and copies), run by every wave with its role's work.
+  // Each role has its own copy of the loop, so that its accumulators keep their registers.
+  auto run_steps = [&](auto&& work) {
+    if (nblk > 0) issue(0);
+    if (nblk > 1) issue(1);
+    for (int32_t T = 0; T <= nblk; ++T) {
+      if (T + 1 < nblk) wait_all_but_last_block();
+      else wait_vmcnt<0>();
+      __syncthreads();  // block T has landed; step T - 1 is done with its slots and P
+      if (T + 2 < nblk) issue(T + 2);
+      work(T);
+    }
+  };
+  if (pwave) {
+    run_steps([&](int32_t T) {
       const int32_t qb = qb_first + T;
       if (T < nblk && reaches(qb)) {
         const int32_t i0 = G::kRows * qb;
@@ -400,7 +407,9 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
           for (int cb = 0; cb < G::kNch; ++cb) acc[cb] = mfma16<F16>(tr_operand<D>(g_slot, lane, t2, cb), pp[t2], acc[cb]);
         __builtin_amdgcn_s_setprio(0);
       }
-    } else {
+    });
+  } else {
+    run_steps([&](int32_t T) {
       const int32_t qb = qb_first + T - 1;
       if (T >= 1 && reaches(qb)) {
         const unsigned char* const q_slot = lds + ((T - 1) % W::kSlots) * kSlotBytes;
@@ -436,7 +445,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
           for (int cb = 0; cb < G::kNch; ++cb) acc[cb] = mfma16<F16>(tr_operand<D>(q_slot, lane, t2, cb), pds[t2], acc[cb]);
         __builtin_amdgcn_s_setprio(0);
       }
-    }
+    });
   }
 
   // Lane (key m, h) holds head dims 32*cb + 8*g4 + 4*h .. + 3 of key jk + m.
