@@ -136,6 +136,22 @@ __device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, int lane
   return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
 }
 
+// N MFMAs, the i-th on the A operand op(i) (an LDS read) and run by mf(i, a); the reads
+// are issued kPf MFMAs ahead of their use, and scheduling barriers keep them there.
+template <int N, int kPf, typename Op, typename Mf>
+__device__ __forceinline__ void mfma_stream(Op op, Mf mf) {
+  bf16x8 buf[kPf + 1];
+#pragma unroll
+  for (int i = 0; i < kPf && i < N; ++i) buf[i] = op(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + kPf < N) buf[(i + kPf) % (kPf + 1)] = op(i + kPf);
+    __builtin_amdgcn_sched_barrier(0);
+    mf(i, buf[i % (kPf + 1)]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // ---------------------------------------------------------------- preprocess
 
 // Per 32-row query block: lse2 = LSE log2(e) (+inf for a row without admitted keys or past
@@ -578,6 +594,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
     }
   }
 
+  constexpr int kPf = 3;  // MFMA operand reads in flight ahead of their MFMA
   f32x16 dq[G::kNch];
 #pragma unroll
   for (int cb = 0; cb < G::kNch; ++cb)
@@ -599,10 +616,13 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dp[r] = s[r] = 0.f;
     __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int st = 0; st < G::kSteps; ++st) dp = mfma16<F16>(row_chunk<D>(v_slot, lm, 2 * st + lh), gr[st], dp);
-#pragma unroll
-    for (int st = 0; st < G::kSteps; ++st) s = mfma16<F16>(row_chunk<D>(k_slot, lm, 2 * st + lh), qr[st], s);
+    // dP^T and S^T, their k-steps interleaved.
+    mfma_stream<2 * G::kSteps, kPf>(
+        [&](int i) { return row_chunk<D>(i % 2 ? k_slot : v_slot, lm, 2 * (i / 2) + lh); },
+        [&](int i, bf16x8 x) {
+          if (i % 2) s = mfma16<F16>(x, qr[i / 2], s);
+          else dp = mfma16<F16>(x, gr[i / 2], dp);
+        });
     __builtin_amdgcn_s_setprio(0);
     float t[16];
 #pragma unroll
@@ -628,10 +648,9 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
     }
     // dQ^T += K^T dS^T
     __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int cb = 0; cb < G::kNch; ++cb) dq[cb] = mfma16<F16>(tr_operand<D>(k_slot, lane, t2, cb), pds[t2], dq[cb]);
+    mfma_stream<2 * G::kNch, kPf>(
+        [&](int i) { return tr_operand<D>(k_slot, lane, i / G::kNch, i % G::kNch); },
+        [&](int i, bf16x8 x) { dq[i % G::kNch] = mfma16<F16>(x, pds[i / G::kNch], dq[i % G::kNch]); });
     __builtin_amdgcn_s_setprio(0);
   }
 
