@@ -32,3 +32,8 @@ def pytest_terminal_summary(terminalreporter):
         terminalreporter.write_sep("-", "parity statistics (every output against the oracle)")
         for line in lines:
             terminalreporter.write_line(line)
+    worst = getattr(mod, "BWD_WORST", None) if mod is not None else None
+    if worst:
+        terminalreporter.write_sep("-", "backward errors as fractions of their derived bars")
+        for dtype, (e, l2, le, ll) in sorted(worst.items()):
+            terminalreporter.write_line(f"{dtype}: worst element {e:.4f} ({le}); worst L2 {l2:.4f} ({ll})")

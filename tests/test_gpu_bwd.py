@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import gen
+import helpers
 import oracle
 from helpers import empty_rows, workload_case
 
@@ -76,6 +77,7 @@ def check_grads(got, ref, bound, label):
         d2, r2, m2 = (float(np.linalg.norm(x)) for x in (a - b, b, m))
         bar2 = GRAD_REL_L2 * r2 + GRAD_NOISE * m2
         assert d2 <= bar2, f"{label}: {name} L2 error {d2:.3e} > {bar2:.3e} (||ref|| {r2:.3e}, ||M|| {m2:.3e})"
+        helpers.bwd_regression("f32", worst / GRAD_TAU, d2 / bar2 if bar2 > 0 else 0.0, f"{label} {name}")
         stats[name] = dict(err_over_scale=worst, rel_l2=d2 / r2 if r2 > 0 else None,
                            max_abs=float(err.max()), max_ref=float(np.abs(b).max()))
     return stats

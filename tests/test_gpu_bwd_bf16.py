@@ -23,6 +23,7 @@ import numpy as np
 import pytest
 
 import gen
+import helpers
 import oracle
 from helpers import empty_rows, to_device, workload_case
 
@@ -79,6 +80,8 @@ def check_grads(got, ref, bound, label):
                                         f"its scale {m[idx]:.3e} (bar {BF16_GRAD_TAU:.3e})")
         d2, r2, m2 = (float(np.linalg.norm(x)) for x in (a - b, b, m))
         assert d2 <= BF16_GRAD_L2 * m2, f"{label}: {name} L2 error {d2:.3e} > {BF16_GRAD_L2:.3e} * ||M|| {m2:.3e}"
+        helpers.bwd_regression("bf16", worst / BF16_GRAD_TAU, d2 / (BF16_GRAD_L2 * m2) if m2 > 0 else 0.0,
+                               f"{label} {name}")
         stats[name] = dict(err_over_scale=worst, l2_over_m=d2 / m2 if m2 > 0 else None,
                            rel_l2=d2 / r2 if r2 > 0 else None)
     return stats

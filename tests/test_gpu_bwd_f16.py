@@ -25,6 +25,7 @@ import numpy as np
 import pytest
 
 import gen
+import helpers
 import oracle
 from helpers import to_device, workload_case
 
@@ -111,6 +112,9 @@ def check_grads(got, ref, bound, under, label):
         d2 = float(np.linalg.norm(a - b))
         l2_bar = F16_GRAD_L2 * float(np.linalg.norm(m)) + F16_UNDERFLOW * float(np.linalg.norm(u))
         assert d2 <= l2_bar, f"{label}: {name} L2 error {d2:.3e} > {l2_bar:.3e}"
+        pos = bar > 0
+        frac = float((err[pos] / bar[pos]).max()) if pos.any() else 0.0
+        helpers.bwd_regression("f16", frac, d2 / l2_bar if l2_bar > 0 else 0.0, f"{label} {name}")
 
 
 SHAPES = [  # (B, H, sq, skv): several blocks with ragged tails, cross shapes both ways

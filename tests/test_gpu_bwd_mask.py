@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import gen
+import helpers
 import oracle
 from helpers import to_device
 from test_gpu_bwd_f16 import underflow_scale
@@ -68,9 +69,15 @@ def _check(got, ref, bound, dtype, label, under=(0.0, 0.0, 0.0)):
         err = np.abs(a - b)
         zero = m == 0
         assert np.all(a[zero] == 0.0), f"{label}: {name} nonzero where every term is zero"
-        assert np.all(err <= TAU[dtype] * m + F16_UNDERFLOW * u), f"{label}: {name} error beyond its bar"
-        assert float(np.linalg.norm(a - b)) <= (L2[dtype] * float(np.linalg.norm(m)) + 1e-5 * float(np.linalg.norm(b))
-                                                + F16_UNDERFLOW * float(np.linalg.norm(u))), f"{label}: {name} L2 error"
+        bar = TAU[dtype] * m + F16_UNDERFLOW * u
+        assert np.all(err <= bar), f"{label}: {name} error beyond its bar"
+        d2 = float(np.linalg.norm(a - b))
+        l2_bar = (L2[dtype] * float(np.linalg.norm(m)) + 1e-5 * float(np.linalg.norm(b))
+                  + F16_UNDERFLOW * float(np.linalg.norm(u)))
+        assert d2 <= l2_bar, f"{label}: {name} L2 error"
+        pos = bar > 0
+        frac = float((err[pos] / bar[pos]).max()) if pos.any() else 0.0
+        helpers.bwd_regression(dtype, frac, d2 / l2_bar if l2_bar > 0 else 0.0, f"{label} {name}")
 
 
 FORMS = {"shared": (1, 1), "per_head": (1, "H"), "full": ("B", "H")}
