@@ -89,10 +89,14 @@ __device__ __forceinline__ int swap_bits_2_3(int p) {
 // 16 rows of a row read must land on 16 different chunks, and the 4 rows of a
 // transposing read on 4 different 64-byte groups; 4*(p&3) + ((p>>2)&3) does both.
 // d = 64 (128-byte rows, two rows per bank cycle): the same over rows of one parity,
-// 4*((p>>1)&1) + ((p>>2)&3).
+// 4*((p>>1)&1) + ((p>>2)&3). d = 32 (64-byte rows, four per bank cycle): rows p and
+// p + 4k share banks, so (p>>2)&3 separates the four of a row read; the four rows of a
+// transposing read are 256 consecutive bytes whatever the chunk order within them.
 template <int D>
 __device__ __forceinline__ int swz(int p) {
-  return D == 128 ? 4 * (p & 3) + ((p >> 2) & 3) : 4 * ((p >> 1) & 1) + ((p >> 2) & 3);
+  static_assert(D == 32 || D == 64 || D == 128, "16-bit backward tile swizzle");
+  return D == 128 ? 4 * (p & 3) + ((p >> 2) & 3)
+                  : D == 64 ? 4 * ((p >> 1) & 1) + ((p >> 2) & 3) : ((p >> 2) & 3);
 }
 
 // Byte offset, from the tile's first row in global memory (rows row_bytes apart), of the
@@ -218,11 +222,31 @@ struct KVGeom {
   static constexpr int kSlots = 4;
   static constexpr int kTileBytes = HGeom<D>::kTileBytes;
   static constexpr int kDma = HGeom<D>::kDmaPerTile;            // 1 KB copies per tile
-  static constexpr int kTileCopiesPerWave = 2 * kDma / kWaves;  // Q and dO of one block
+  static constexpr int kTileCopies = 2 * kDma;                  // Q and dO of one block
+  // Copies each wave issues per block: the same number for every wave, or (d = 32, four
+  // copies) one for each of waves 0..3.
+  static constexpr int kTileCopiesPerWave = kTileCopies >= kWaves ? kTileCopies / kWaves : 1;
   static constexpr int kXBytes = 16 * 64 * 4;                   // a wave's 16 P values per lane
-  static_assert(kTileCopiesPerWave >= 1 && kTileCopiesPerWave * kWaves == 2 * kDma, "copy split");
+  static_assert(kTileCopies < kWaves ? kTileCopies * 2 == kWaves : kTileCopiesPerWave * kWaves == kTileCopies,
+                "copy split");
   static_assert(2 * kKB * kTileBytes <= kSlots * 2 * kTileBytes, "K and V stage in the ring");
 };
+
+// A vmcnt wait with a wave-uniform count (0..8; counts above 8 wait for 8, which is
+// stricter and so still correct).
+__device__ __forceinline__ void wait_vmcnt_n(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    default: wait_vmcnt<8>(); break;
+  }
+}
 
 template <int D, bool CAUSAL, bool MASKED, bool F16>
 __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
@@ -284,6 +308,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < W::kTileCopiesPerWave; ++u) {
       const int c = u * W::kWaves + wave;  // 0 .. 2 kDma - 1: Q copies, then dO copies
+      if (c >= W::kTileCopies) break;      // d = 32: waves 4..7 copy no tile
       if (c < W::kDma)
         dma_load_x4(q_rsrc, (unsigned)(G::kRows * qb) * q_row + tile_src<D, true>(c, lane, q_row),
                     lds_address(slot + 1024 * c));
@@ -302,10 +327,9 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
   };
   // Wait until this wave's copies of every block but the last one issued have landed.
-  auto wait_all_but_last_block = [&]() {
-    if (wave == 0 || (MASKED && (wave == 1 || wave == 2))) wait_vmcnt<W::kTileCopiesPerWave + 1>();
-    else wait_vmcnt<W::kTileCopiesPerWave>();
-  };
+  const int copies_per_block = (wave < W::kTileCopies ? W::kTileCopiesPerWave : 0) + (wave == 0 ? 1 : 0) +
+                               (MASKED && (wave == 1 || wave == 2) ? 1 : 0);
+  auto wait_all_but_last_block = [&]() { wait_vmcnt_n(copies_per_block); };
 
   // The four key blocks' K and V tiles (unpermuted), staged through the ring (each wave
   // copies a share), into the B operands: the P wave of key block kb takes K, the dS wave
@@ -492,8 +516,11 @@ struct QGeom {
   static constexpr int kQ = 32 * kWaves;  // queries per workgroup
   static constexpr int kSlots = 4;
   static constexpr int kDma = HGeom<D>::kDmaPerTile;
-  static constexpr int kTileCopiesPerWave = 2 * kDma / kWaves;  // K and V of one block
-  static_assert(kTileCopiesPerWave >= 1 && kTileCopiesPerWave * kWaves == 2 * kDma, "copy split");
+  static constexpr int kTileCopies = 2 * kDma;  // K and V of one block
+  // As for the dK/dV kernel: d = 32 has four copies, one for each of waves 0..3.
+  static constexpr int kTileCopiesPerWave = kTileCopies >= kWaves ? kTileCopies / kWaves : 1;
+  static_assert(kTileCopies < kWaves ? kTileCopies * 2 == kWaves : kTileCopiesPerWave * kWaves == kTileCopies,
+                "copy split");
 };
 
 template <int D, bool CAUSAL, bool MASKED, bool F16>
@@ -546,6 +573,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < W::kTileCopiesPerWave; ++u) {
       const int c = u * W::kWaves + wave;  // K copies, then V copies
+      if (c >= W::kTileCopies) break;      // d = 32: waves 4..7 copy no tile
       if (c < W::kDma)
         dma_load_x4(k_rsrc, row0 + tile_src<D, true>(c, lane, kv_row), lds_address(slot + 1024 * c));
       else
@@ -556,19 +584,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
                   lds_address(slot + 2 * G::kTileBytes + 256 * wave));
   };
   // Wait until at most the copies of the last n blocks issued are in flight.
-  auto wait_blocks = [&](int n) {
-    if (MASKED && wave < 4) {
-      constexpr int c = W::kTileCopiesPerWave + 1;
-      if (n >= 2) wait_vmcnt<2 * c>();
-      else if (n == 1) wait_vmcnt<c>();
-      else wait_vmcnt<0>();
-    } else {
-      constexpr int c = W::kTileCopiesPerWave;
-      if (n >= 2) wait_vmcnt<2 * c>();
-      else if (n == 1) wait_vmcnt<c>();
-      else wait_vmcnt<0>();
-    }
-  };
+  const int copies_per_block = (wave < W::kTileCopies ? W::kTileCopiesPerWave : 0) + (MASKED && wave < 4 ? 1 : 0);
+  auto wait_blocks = [&](int n) { wait_vmcnt_n(copies_per_block * min(n, 2)); };
 
   // This wave's rows: lse2 and D (the preprocess pads past seq_q), and Q and dO as B
   // operands: lane (query m, h) holds head dims 16*st + 8*h .. + 7 of row qw0 + m (zeros
@@ -704,6 +721,9 @@ hipError_t launch_bwd_bf16_d(const BwdArgs& a, bool causal, hipStream_t s, hipEv
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, bool causal, hipStream_t s,
                            hipEvent_t ev_pre, hipEvent_t ev_dkdv) {
+  if (head_dim == 32)
+    return a.in_f16 ? launch_bwd_bf16_d<32, true>(a, causal, s, ev_pre, ev_dkdv)
+                    : launch_bwd_bf16_d<32, false>(a, causal, s, ev_pre, ev_dkdv);
   if (head_dim == 64)
     return a.in_f16 ? launch_bwd_bf16_d<64, true>(a, causal, s, ev_pre, ev_dkdv)
                     : launch_bwd_bf16_d<64, false>(a, causal, s, ev_pre, ev_dkdv);

@@ -47,12 +47,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
+// D/32 consecutive floats: a lane's share of one gradient row, or of one tile row.
 template <int N>
-struct FVecB;
-template <>
-struct FVecB<2> { typedef f32x2 T; };
-template <>
-struct FVecB<4> { typedef f32x4 T; };
+struct FVecB {
+  typedef float T __attribute__((ext_vector_type(N)));
+};
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -571,6 +570,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool causal, hipStream_t s, hipEvent_t
 
 hipError_t launch_bwd_f32(const BwdArgs& a, int head_dim, bool causal, hipStream_t s,
                           hipEvent_t ev_pre, hipEvent_t ev_dkdv) {
+  if (head_dim == 32) return launch_bwd_d<32>(a, causal, s, ev_pre, ev_dkdv);
   if (head_dim == 64) return launch_bwd_d<64>(a, causal, s, ev_pre, ev_dkdv);
   if (head_dim == 128) return launch_bwd_d<128>(a, causal, s, ev_pre, ev_dkdv);
   return hipErrorInvalidValue;

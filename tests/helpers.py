@@ -28,7 +28,7 @@ BF16_LSE_TOL = 1e-4
 # kernels show use only a small part of them. A gradient tensor whose worst element, or whose
 # L2 error, uses more than BWD_REGRESSION[dtype] = (element, L2) of its derived bars fails:
 # about three times the largest fractions measured over all backward GPU tests (element and
-# L2: fp32 0.022 and 0.061, bf16 0.097 and 0.198, fp16 0.088 and 0.137; the kernels are
+# L2: fp32 0.022 and 0.061, bf16 0.100 and 0.198, fp16 0.095 and 0.142; the kernels are
 # deterministic, so these do not vary between runs), so that a drift of that size is caught.
 # BWD_WORST keeps the largest fractions seen in the session (printed at the end).
 BWD_REGRESSION = {"f32": (0.07, 0.2), "bf16": (0.3, 0.6), "f16": (0.3, 0.4)}

@@ -108,7 +108,7 @@ def _small(shape, causal, d):
     return (q, k, v, g), scale, _oracle(q, k, v, g, scale, causal)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_bwd_parity_small(shape, causal, d):
@@ -118,7 +118,7 @@ def test_bwd_parity_small(shape, causal, d):
     print(f"{shape} causal={causal} d={d}: {stats}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 def test_bwd_rows_without_keys(d):
     """Causal with sq > skv: the first sq - skv rows admit no key; their dq is exactly 0."""
     q, k, v, g = _case(41, 1, 2, 150, 60, d)
@@ -130,7 +130,7 @@ def test_bwd_rows_without_keys(d):
     assert np.all(got[0][:, :, er] == 0.0)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 def test_bwd_no_keys_gives_zero_dq(d):
     q, _, _, g = _case(42, 2, 2, 70, 1, d)
     k = np.zeros((2, 2, 0, d), np.float32)
@@ -139,7 +139,7 @@ def test_bwd_no_keys_gives_zero_dq(d):
     assert np.all(dq == 0.0) and not np.any(np.signbit(dq))
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 def test_bwd_no_queries_gives_zero_dk_dv(d):
     _, k, v, _ = _case(43, 1, 3, 1, 90, d)
     q = np.zeros((1, 3, 0, d), np.float32)

@@ -112,7 +112,7 @@ def _small(shape, causal, d):
     return bits, g, scale, _oracle(q, k, v, g, scale, causal)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_bwd_bf16_parity_small(shape, causal, d):
@@ -121,7 +121,7 @@ def test_bwd_bf16_parity_small(shape, causal, d):
     print(shape, causal, d, check_grads(got, ref, bound, f"{shape} causal={causal} d={d}"))
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 def test_bwd_bf16_rows_without_keys(d):
     """Causal with more queries than keys: the first sq - skv rows admit nothing."""
     (q, k, v), bits, g = _case(801 + d, 1, 2, 150, 100, d)
@@ -132,7 +132,7 @@ def test_bwd_bf16_rows_without_keys(d):
     check_grads(got, ref, bound, "empty rows")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 def test_bwd_bf16_no_keys_and_no_queries(d):
     import torch
 

@@ -24,7 +24,7 @@ def _gpu():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(2, 3, 130, 77), (1, 2, 200, 333), (2, 1, 257, 129)],
                          ids=lambda s: "x".join(map(str, s)))
