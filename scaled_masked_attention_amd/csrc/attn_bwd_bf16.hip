@@ -509,7 +509,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
 // dP^T = V dO^T, and accumulates dQ^T += K^T dS^T. The waves step through the key blocks
 // the workgroup's rows admit together: key block T's K and V tiles (permuted) and, with a
 // hard mask, the rows' words of block T are copied straight into a ring of four LDS slots
-// three steps ahead, each wave issuing a share. One barrier per step.
+// two steps ahead, each wave issuing a share; waves 4-7 run each block's dQ product one
+// step late, so that block stays in the ring a step longer. One barrier per step.
 template <int D>
 struct QGeom {
   static constexpr int kWaves = 8;
@@ -618,13 +619,33 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[cb][r] = 0.f;
 
+  // dQ^T += K^T dS^T for the block in k_slot.
+  auto dq_product = [&](const unsigned char* k_slot, const bf16x8 (&pds)[2]) {
+    __builtin_amdgcn_s_setprio(1);
+    mfma_stream<2 * G::kNch, kPf>(
+        [&](int i) { return tr_operand<D>(k_slot, lane, i / G::kNch, i % G::kNch); },
+        [&](int i, bf16x8 x) { dq[i % G::kNch] = mfma16<F16>(x, pds[i / G::kNch], dq[i % G::kNch]); });
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Waves 4-7 (each sharing a SIMD with wave - 4) run their dQ product of block T at the
+  // start of step T + 1, so that the two waves of a SIMD are half a step apart and one's
+  // MFMAs meet the other's softmax.
+  const bool late = wave >= 4;
+  bf16x8 pds_late[2];
+  bool pending = false;
+  const unsigned char* late_slot = lds;
+  constexpr int kAhead = W::kSlots - 2;  // blocks copied ahead: a late wave still reads block T - 1
 #pragma unroll
-  for (int T = 0; T < W::kSlots - 1; ++T)
+  for (int T = 0; T < kAhead; ++T)
     if (T < nblk) issue(T);
   for (int32_t T = 0; T < nblk; ++T) {
-    wait_blocks(min(nblk - 1 - T, W::kSlots - 2));
-    __syncthreads();  // block T has landed; step T - 1 is done with its slot
-    if (T + W::kSlots - 1 < nblk) issue(T + W::kSlots - 1);
+    wait_blocks(min(nblk - 1 - T, kAhead - 1));
+    __syncthreads();  // block T has landed; step T - 1 is done with block T - 2's slot
+    if (T + kAhead < nblk) issue(T + kAhead);
+    if (late && pending) {
+      dq_product(late_slot, pds_late);
+      pending = false;
+    }
     const int32_t j0 = G::kRows * T;
     if (!wave_live || j0 >= wave_hi) continue;
     const unsigned char* const k_slot = lds + (T % W::kSlots) * kSlotBytes;
@@ -663,13 +684,16 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
       const float p = __builtin_amdgcn_exp2f(t[r]);
       pds[r / 8][r % 8] = round16<F16>(p * (dp[r] - my_d));
     }
-    // dQ^T += K^T dS^T
-    __builtin_amdgcn_s_setprio(1);
-    mfma_stream<2 * G::kNch, kPf>(
-        [&](int i) { return tr_operand<D>(k_slot, lane, i / G::kNch, i % G::kNch); },
-        [&](int i, bf16x8 x) { dq[i % G::kNch] = mfma16<F16>(x, pds[i / G::kNch], dq[i % G::kNch]); });
-    __builtin_amdgcn_s_setprio(0);
+    if (late) {
+      pds_late[0] = pds[0];
+      pds_late[1] = pds[1];
+      late_slot = k_slot;
+      pending = true;
+    } else {
+      dq_product(k_slot, pds);
+    }
   }
+  if (pending) dq_product(late_slot, pds_late);
 
   // Lane (query m, h) holds head dims 32*cb + 8*g4 + 4*h .. + 3 of row qw0 + m.
   if (!wave_live || my_row >= a.seq_q) return;
