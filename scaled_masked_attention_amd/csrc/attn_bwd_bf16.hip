@@ -382,7 +382,22 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
   };
   if (pwave) {
+    // The P wave runs a block's dV product at the start of the next step, ahead of the
+    // next block's S MFMAs: its partner dS wave starts each step with MFMAs too, and the
+    // P wave's softmax then meets the dS wave's dK MFMAs.
+    bf16x8 pp_late[2];
+    bool pending = false;
+    const unsigned char* g_late = lds;
     run_steps([&](int32_t T) {
+      if (pending) {
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int cb = 0; cb < G::kNch; ++cb) acc[cb] = mfma16<F16>(tr_operand<D>(g_late, lane, t2, cb), pp_late[t2], acc[cb]);
+        __builtin_amdgcn_s_setprio(0);
+        pending = false;
+      }
       const int32_t qb = qb_first + T;
       if (T < nblk && reaches(qb)) {
         const int32_t i0 = G::kRows * qb;
@@ -439,13 +454,11 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
         unsigned char* const xp = xbuf + (2 * kb + (T & 1)) * W::kXBytes + 16 * lane;
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) *reinterpret_cast<f32x4*>(xp + 1024 * c4) = p32[c4];
-        // dV^T += dO^T P
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int cb = 0; cb < G::kNch; ++cb) acc[cb] = mfma16<F16>(tr_operand<D>(g_slot, lane, t2, cb), pp[t2], acc[cb]);
-        __builtin_amdgcn_s_setprio(0);
+        // dV^T += dO^T P, at the start of the next step
+        pp_late[0] = pp[0];
+        pp_late[1] = pp[1];
+        g_late = g_slot;
+        pending = true;
       }
     });
   } else {
