@@ -354,7 +354,7 @@ BWD_PREFIX = "bwd_"
 def gen_workloads():
     import gen
 
-    bwd = [BWD_PREFIX + n for n, w in gen.WORKLOADS.items() if w.head_dim in (64, 128)]
+    bwd = [BWD_PREFIX + n for n, w in gen.WORKLOADS.items() if w.head_dim in (32, 64, 128)]
     return list(gen.WORKLOADS) + bwd + list(gen.ROW_WORKLOADS)
 
 
