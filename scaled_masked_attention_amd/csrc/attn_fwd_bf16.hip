@@ -9,10 +9,11 @@
 // F16). The probabilities are rounded to the input's 16-bit type (nearest
 // even) for the P V product; the row sums use the fp32 probabilities.
 //
-// Workgroup: 8 waves x 32 query rows = 256 rows, two waves per SIMD. Key tiles
-// of 64 rows go HBM/L2 -> LDS through buffer-resource direct-to-LDS loads into
-// a ring of four slots, two tiles ahead of their use, without passing through
-// registers; loads past the last key return zeros.
+// Workgroup: 8 waves x 32 query rows = 256 rows, two waves per SIMD (at head
+// dim 256: 4 blocks of 32 rows, two waves each, see BGeom). Key tiles of 64 rows
+// (32 at d = 256) go HBM/L2 -> LDS through buffer-resource direct-to-LDS loads
+// into a ring of four slots, two tiles ahead of their use, without passing
+// through registers; loads past the last key return zeros.
 //
 // S^T = K Q^T: lane (m, h) supplies K[key m] and Q[query m] at head dims
 // h*D/2 + 8*step .. + 7 and receives the scores of query (lane % 32). K rows
