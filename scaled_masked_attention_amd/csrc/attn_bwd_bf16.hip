@@ -6,7 +6,8 @@
 // backward; the operand precision of oxicuda `gemm_mixed_precision`: 16-bit operands, fp32
 // accumulation and result).
 //
-// The arithmetic and the three launches are those of the fp32 backward:
+// The arithmetic and the three launches (preprocess, dK/dV, dQ) are those of the fp32
+// backward, with workgroups shaped for 16-bit MFMA and two waves per SIMD:
 //   P_ij = 2^(c s_ij - lse2_i), D_i = dO_i . O_i, dP_ij = dO_i . v_j, dS_ij = P_ij (dP_ij - D_i),
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j,
 // with three roundings to the input type (nearest even) for the products: dO once, in
@@ -28,7 +29,8 @@
 //    the transposing read ds_read_b64_tr_b16: tile rows 16t + 4h + 0..3 and
 //    16t + 8 + 4h + 0..3 hold original rows 16t + 8h + 0..7.
 //  - The B operands of the score products (K and V in the dK/dV kernel, Q and dO in the
-//    dQ kernel) stay in registers for the whole pass, read once from unpermuted tiles.
+//    dQ kernel) stay in registers for the whole pass, read once: K and V from unpermuted
+//    LDS tiles, Q and dO straight from global memory.
 //  - Every tile is XOR-swizzled in 16-byte chunks (swz below), which keeps both the
 //    16-byte row reads (16 lanes, 16 consecutive rows, one chunk) and the transposing
 //    reads (32 lanes, 4 consecutive rows, one 64-byte group) free of bank conflicts.
