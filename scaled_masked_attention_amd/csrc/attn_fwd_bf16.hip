@@ -10,10 +10,10 @@
 // even) for the P V product; the row sums use the fp32 probabilities.
 //
 // Workgroup: 8 waves x 32 query rows = 256 rows, two waves per SIMD (at head
-// dim 256: 4 blocks of 32 rows, two waves each, see BGeom). Key tiles of 64 rows
-// (32 at d = 256) go HBM/L2 -> LDS through buffer-resource direct-to-LDS loads
-// into a ring of four slots, two tiles ahead of their use, without passing
-// through registers; loads past the last key return zeros.
+// dim 256: 4 waves x 32 rows, one wave per SIMD, see BGeom). Key tiles of 64
+// rows (32 at d = 256) go HBM/L2 -> LDS through buffer-resource direct-to-LDS
+// loads into a ring of four slots, two tiles ahead of their use, without
+// passing through registers; loads past the last key return zeros.
 //
 // S^T = K Q^T: lane (m, h) supplies K[key m] and Q[query m] at head dims
 // h*D/2 + 8*step .. + 7 and receives the scores of query (lane % 32). K rows
@@ -28,6 +28,12 @@
 // do S(t), softmax(t), PV(t); waves 4-7 do PV(t-1), S(t), softmax(t). One
 // wave's softmax (VALU, transcendental) then meets the other's MFMAs in two
 // of the three phases.
+//
+// This file is built with VGPR-form MFMAs (accumulators in the architectural
+// registers). At d = 256 a wave needs more than 256 registers, and the
+// compiler's default there puts the accumulators in AGPRs and copies all of O
+// back to VGPRs on every tile for the rare rescale, about 150 extra VALU
+// instructions per tile.
 #include "attn_common.h"
 
 namespace sma {
@@ -61,20 +67,20 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-// Geometry per head dim. At d = 256 a 32-row block's O alone would take 128
-// registers of one wave, so two waves share each block (kSplitO): both form the
-// block's scores and softmax, each accumulates half of O's head dims. The
-// workgroup is 8 waves over 4 row blocks, and tiles have 32 keys (64 KB of K and
-// V per ring slot would not fit 4 slots). At d = 32 a tensor's tile is 256
-// chunks: waves 0-3 copy K, waves 4-7 copy V.
+// Geometry per head dim. At d = 256 a 32-row block's O alone takes 128
+// registers and Q 64 more, past the 256 a wave may hold at two waves per SIMD:
+// the workgroup is then 4 waves, one per SIMD (up to 512 registers each), and
+// tiles have 32 keys (64 KB of K and V per ring slot would not fit 4 slots).
+// With no second wave on its SIMD, a d = 256 wave runs every step in the
+// early order. At d = 32 a tensor's tile is 256 chunks: waves 0-3 copy K,
+// waves 4-7 copy V.
 template <int D>
 struct BGeom {
-  static constexpr int kWaves = 8;
+  static constexpr int kWaves = D == 256 ? 4 : 8;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr bool kSplitO = D == 256;         // two waves per row block, half of O each
+  static constexpr bool kPaired = kWaves == 8;       // two waves per SIMD, half a step apart
   static constexpr int kQW = 32;                     // query rows per wave
-  static constexpr int kRowBlocks = kSplitO ? kWaves / 2 : kWaves;
-  static constexpr int kQ = kRowBlocks * kQW;        // query rows per workgroup
+  static constexpr int kQ = kWaves * kQW;            // query rows per workgroup
   static constexpr int kK = D == 256 ? kBF16D256KeysPerTile : kBF16KeysPerTile;  // keys per tile
   static constexpr int kKB = kK / 32;                // 32-key blocks per tile
   static constexpr int kSlots = 4;                   // LDS ring of K/V tiles
@@ -86,7 +92,7 @@ struct BGeom {
   static constexpr int kLoadsPerTile = kSplitKV ? kLoadsPerThread : 2 * kLoadsPerThread;
   static constexpr int kHalf = D / 2;
   static constexpr int kSteps = D / 16;              // QK^T k-steps (8 dims per lane half)
-  static constexpr int kNch = (kSplitO ? D / 2 : D) / 32;  // a wave's 32-wide output chunks
+  static constexpr int kNch = D / 32;                // 32-wide output chunks
   static_assert(kQ == (D == 256 ? kBF16D256QueriesPerWG : kBF16QueriesPerWG), "planner geometry");
   static_assert(kLoadsPerThread >= 1 && kLoadsPerThread * 64 * kCopyWaves == kTileChunks,
                 "tile split");
@@ -142,10 +148,7 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
 
   const TileId t = decode_tile(blockIdx.x, a);
   const int32_t q0 = t.qb * G::kQ;
-  // This wave's row block, and (d = 256) which half of O's head dims it accumulates.
-  const int rblk = G::kSplitO ? wave % G::kRowBlocks : wave;
-  const int ohalf = G::kSplitO ? wave / G::kRowBlocks : 0;
-  const int32_t qw0 = q0 + rblk * G::kQW;
+  const int32_t qw0 = q0 + wave * G::kQW;
   const int32_t ks = t.split * a.split_len;
   const int32_t split_end = min(a.seq_kv, ks + a.split_len);
   const int32_t wg_last_row = min(q0 + G::kQ - 1, a.seq_q - 1);
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
       const int kb = i / (2 * G::kNch), t2 = (i / G::kNch) % 2, cb = i % G::kNch;
       const int r_lo = 32 * kb + 16 * t2 + 8 * lh + srole / 4;
       const int r_hi = r_lo + 4;
-      const int chunk = 4 * (ohalf * G::kNch + cb) + colq;
+      const int chunk = 4 * cb + colq;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s16x4*)(vtile + r_lo * (2 * D) +
                                                      16 * (chunk ^ v_swz<D>(r_lo)) + half8));
@@ -398,9 +401,7 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
     l_run += psum;
   };
 
-  // (At d = 256 the two waves of a row block keep one phase: the late copy of P
-  // and its second P V call site would push the kernel past 256 registers.)
-  const bool late = !G::kSplitO && wave >= G::kWaves / 2;
+  const bool late = G::kPaired && wave >= G::kWaves / 2;
   V8 pb_late[G::kKB][2];
   bool late_pending = false;
   int late_slot = 0;
@@ -454,13 +455,12 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
     const int64_t o_off = head_offset(t.bh, a.heads, a.qs_b, a.qs_h) + (int64_t)my_row * a.qs_s;
     if (a.o_bf16) orow16 = a.o_bf16 + o_off;
     else orow = a.o + o_off;
-    if (a.lse && lh == 0 && ohalf == 0) a.lse[row_id] = empty ? -INFINITY : lse2 * 0.69314718055994530942f;
+    if (a.lse && lh == 0) a.lse[row_id] = empty ? -INFINITY : lse2 * 0.69314718055994530942f;
   } else {
     const size_t prow = (size_t)t.split * ((size_t)a.bh * a.seq_q) + row_id;
     orow = a.part_o + prow * D;
-    if (lh == 0 && ohalf == 0) a.part_lse[prow] = lse2;
+    if (lh == 0) a.part_lse[prow] = lse2;
   }
-  const int c0 = 32 * G::kNch * ohalf;  // this wave's first head dim of O
 #pragma unroll
   for (int cb = 0; cb < G::kNch; ++cb)
 #pragma unroll
@@ -469,10 +469,10 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
 #pragma unroll
       for (int e = 0; e < 4; ++e) out[e] = empty ? 0.f : oacc[cb][4 * g4 + e] * inv;
       if (orow16)
-        *reinterpret_cast<u32x2*>(orow16 + c0 + 32 * cb + 8 * g4 + 4 * lh) =
+        *reinterpret_cast<u32x2*>(orow16 + 32 * cb + 8 * g4 + 4 * lh) =
             u32x2{pack_out16(out[0], out[1], a.o_f16), pack_out16(out[2], out[3], a.o_f16)};
       else
-        *reinterpret_cast<f32x4*>(orow + c0 + 32 * cb + 8 * g4 + 4 * lh) = out;
+        *reinterpret_cast<f32x4*>(orow + 32 * cb + 8 * g4 + 4 * lh) = out;
     }
 }
 
