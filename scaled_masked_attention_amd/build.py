@@ -24,19 +24,21 @@ SOURCES = ["sma_host.cpp", "attn_fwd_f32.hip", "attn_fwd_f32_wsplit.hip", "attn_
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Packed fp32 VALU forms are switched off for every HIP translation unit.
+# Packed fp32 VALU forms are switched off for every HIP translation unit. MFMAs
+# take their VGPR form (accumulators in the architectural registers): for a
+# kernel that holds more than 256 registers per wave the compiler's default puts
+# the accumulators in AGPRs and then copies them between register files inside
+# the loops (the 16-bit forward at head dim 256 paid about 150 VALU instructions
+# per key tile for it, and every fp32 kernel runs 2-8 % faster without it).
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=true",
           "-I", INCLUDE, "-I", CSRC]
-# Per-source additions. The 16-bit forward takes VGPR-form MFMAs: its head-dim-256
-# kernel holds more than 256 registers per wave, where the default (AGPR-form
-# accumulators) copies O between register files on every key tile.
-EXTRA = {"attn_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in l)

@@ -29,7 +29,7 @@
 // wave's softmax (VALU, transcendental) then meets the other's MFMAs in two
 // of the three phases.
 //
-// This file is built with VGPR-form MFMAs (accumulators in the architectural
+// The library is built with VGPR-form MFMAs (accumulators in the architectural
 // registers). At d = 256 a wave needs more than 256 registers, and the
 // compiler's default there puts the accumulators in AGPRs and copies all of O
 // back to VGPRs on every tile for the rare rescale, about 150 extra VALU
