@@ -354,7 +354,9 @@ BWD_PREFIX = "bwd_"
 def gen_workloads():
     import gen
 
-    bwd = [BWD_PREFIX + n for n, w in gen.WORKLOADS.items() if w.head_dim in (32, 64, 128)]
+    # The backward runs head dims 32-128, and 256 with 16-bit inputs.
+    bwd = [BWD_PREFIX + n for n, w in gen.WORKLOADS.items()
+           if w.head_dim in (32, 64, 128) or (w.head_dim == 256 and w.dtype != "f32")]
     return list(gen.WORKLOADS) + bwd + list(gen.ROW_WORKLOADS)
 
 

@@ -307,7 +307,8 @@ size_t sma_attention_fwd_masked_workspace_bytes(int in_dtype, size_t batch, size
  *                    (beyond 65504 the results are not finite; under 2^-14 bits are
  *                    lost), as loss scaling does. o, dout, lse and the three
  *                    gradients are always fp32 (o as sma_attention_fwd returns it).
- *   head_dim         32, 64 or 128 (others -> UNSUPPORTED).
+ *   head_dim         32, 64 or 128; 256 with bf16 or fp16 inputs (others, and 256 with
+ *                    fp32 inputs, -> UNSUPPORTED).
  *   scale, causal, stream   as for sma_attention_fwd.
  *   workspace        required device scratch of at least
  *                    sma_attention_bwd_workspace_bytes bytes (smaller or NULL

@@ -7,7 +7,8 @@
 // accumulation and result).
 //
 // The arithmetic and the three launches (preprocess, dK/dV, dQ) are those of the fp32
-// backward, with workgroups shaped for 16-bit MFMA and two waves per SIMD:
+// backward, with workgroups shaped for 16-bit MFMA and two waves per SIMD (one at head
+// dim 256, where a wave's accumulators and operands pass 256 registers):
 //   P_ij = 2^(c s_ij - lse2_i), D_i = dO_i . O_i, dP_ij = dO_i . v_j, dS_ij = P_ij (dP_ij - D_i),
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j,
 // with three roundings to the input type (nearest even) for the products: dO once, in
@@ -87,17 +88,18 @@ __device__ __forceinline__ int perm_acc_row(int r, int h) { return 16 * (r / 8) 
 __device__ __forceinline__ int swap_bits_2_3(int p) {
   return (p & ~0xC) | ((p & 4) << 1) | ((p & 8) >> 1);
 }
-// Chunk swizzle of tile row p. d = 128 (256-byte rows, every row on all 64 banks): the
-// 16 rows of a row read must land on 16 different chunks, and the 4 rows of a
-// transposing read on 4 different 64-byte groups; 4*(p&3) + ((p>>2)&3) does both.
+// Chunk swizzle of tile row p. d = 128 and 256 (rows of 256 bytes or more, every row
+// on all 64 banks, chunk c on the banks of c mod 16): the 16 rows of a row read must
+// land on 16 different chunks mod 16, and the 4 rows of a transposing read on 4
+// different 64-byte groups; 4*(p&3) + ((p>>2)&3) does both.
 // d = 64 (128-byte rows, two rows per bank cycle): the same over rows of one parity,
 // 4*((p>>1)&1) + ((p>>2)&3). d = 32 (64-byte rows, four per bank cycle): rows p and
 // p + 4k share banks, so (p>>2)&3 separates the four of a row read; the four rows of a
 // transposing read are 256 consecutive bytes whatever the chunk order within them.
 template <int D>
 __device__ __forceinline__ int swz(int p) {
-  static_assert(D == 32 || D == 64 || D == 128, "16-bit backward tile swizzle");
-  return D == 128 ? 4 * (p & 3) + ((p >> 2) & 3)
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "16-bit backward tile swizzle");
+  return D >= 128 ? 4 * (p & 3) + ((p >> 2) & 3)
                   : D == 64 ? 4 * ((p >> 1) & 1) + ((p >> 2) & 3) : ((p >> 2) & 3);
 }
 
@@ -209,17 +211,18 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(BwdArgs a) {
 // back from LDS, forms dS = P (dP - D) and accumulates dK^T += Q^T dS. A wave keeps only
 // its key block's K or V (the B operand of S or dP) and one accumulator set in registers,
 // so two waves fit a SIMD; the two waves of a key block share one, and one's MFMAs run
-// while the other works on the VALU.
+// while the other works on the VALU. At head dim 256 (64 registers of K or V, 128 of
+// accumulators) the workgroup is 64 keys, two key blocks and 4 waves, one per SIMD.
 //
-// All 8 waves step through the query blocks together. Query block T's Q and dO tiles
+// All the waves step through the query blocks together. Query block T's Q and dO tiles
 // (permuted), its lse2/D and, with a hard mask, the four key blocks' mask words of its rows
 // are copied straight into a ring of four LDS slots two steps ahead, each wave issuing a
 // share. In step T the P waves work on block T and the dS waves on block T - 1, whose P
 // the P waves left in LDS (fp32, double buffered) in step T - 1. One barrier per step.
 template <int D>
 struct KVGeom {
-  static constexpr int kWaves = 8;
-  static constexpr int kKB = 4;                                 // 32-key blocks per workgroup
+  static constexpr int kWaves = D == 256 ? 4 : 8;
+  static constexpr int kKB = kWaves / 2;                        // 32-key blocks per workgroup
   static constexpr int kKeys = 32 * kKB;
   static constexpr int kSlots = 4;
   static constexpr int kTileBytes = HGeom<D>::kTileBytes;
@@ -232,26 +235,23 @@ struct KVGeom {
   static_assert(kTileCopies < kWaves ? kTileCopies * 2 == kWaves : kTileCopiesPerWave * kWaves == kTileCopies,
                 "copy split");
   static_assert(2 * kKB * kTileBytes <= kSlots * 2 * kTileBytes, "K and V stage in the ring");
+  static constexpr int kMaskWaves = kKB / 2;  // waves 1.. that copy mask words (32 rows x 2 key blocks each)
 };
 
-// A vmcnt wait with a wave-uniform count (0..8; counts above 8 wait for 8, which is
+// A vmcnt wait with a wave-uniform count (0..20; counts above 20 wait for 20, which is
 // stricter and so still correct).
+template <int N = 0>
 __device__ __forceinline__ void wait_vmcnt_n(int n) {
-  switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    default: wait_vmcnt<8>(); break;
+  if constexpr (N >= 20) {
+    wait_vmcnt<20>();
+  } else {
+    if (n == N) wait_vmcnt<N>();
+    else wait_vmcnt_n<N + 1>(n);
   }
 }
 
 template <int D, bool CAUSAL, bool MASKED, bool F16>
-__global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * KVGeom<D>::kWaves) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   using G = HGeom<D>;
   using W = KVGeom<D>;
   // Slot: Q tile, dO tile, lse2/D, and with a hard mask [key block][row] words.
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
                         (unsigned)a.seq_q * (unsigned)a.mask_words * 4u);
 
   // Copies of query block T (absolute block qb_first + T) into its ring slot: the Q and dO
-  // tiles split over the 8 waves; wave 0 adds lse2/D, waves 1 and 2 the mask words
+  // tiles split over the waves; wave 0 adds lse2/D, waves 1 .. kKB/2 the mask words
   // (lane l of wave 1 + h: key block 2h + l / 32, row l % 32).
   auto issue = [&](int32_t T) {
     const int32_t qb = qb_first + T;
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
     if (wave == 0)
       dma_load_x1(m_rsrc, (unsigned)qb * (unsigned)G::kMetaBytes + 4u * lane,
                   lds_address(slot + 2 * G::kTileBytes));
-    if (MASKED && (wave == 1 || wave == 2)) {
+    if (MASKED && wave >= 1 && wave <= W::kMaskWaves) {
       const int kbw = 2 * (wave - 1) + (lane >> 5);
       dma_load_x1(w_rsrc, ((unsigned)(G::kRows * qb + (lane & 31)) * (unsigned)a.mask_words +
                            (unsigned)(j0 / 32 + kbw)) * 4u,
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   };
   // Wait until this wave's copies of every block but the last one issued have landed.
   const int copies_per_block = (wave < W::kTileCopies ? W::kTileCopiesPerWave : 0) + (wave == 0 ? 1 : 0) +
-                               (MASKED && (wave == 1 || wave == 2) ? 1 : 0);
+                               (MASKED && wave >= 1 && wave <= W::kMaskWaves ? 1 : 0);
   auto wait_all_but_last_block = [&]() { wait_vmcnt_n(copies_per_block); };
 
   // The four key blocks' K and V tiles (unpermuted), staged through the ring (each wave
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
 // step late, so that block stays in the ring a step longer. One barrier per step.
 template <int D>
 struct QGeom {
-  static constexpr int kWaves = 8;
+  static constexpr int kWaves = D == 256 ? 4 : 8;  // head dim 256: one wave per SIMD
   static constexpr int kQ = 32 * kWaves;  // queries per workgroup
   static constexpr int kSlots = 4;
   static constexpr int kDma = HGeom<D>::kDmaPerTile;
@@ -540,7 +540,7 @@ struct QGeom {
 };
 
 template <int D, bool CAUSAL, bool MASKED, bool F16>
-__global__ __launch_bounds__(512) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * QGeom<D>::kWaves) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   using G = HGeom<D>;
   using W = QGeom<D>;
   // Slot: K tile, V tile, and with a hard mask the workgroup rows' words of the key block.
@@ -581,8 +581,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
     w_rsrc = raw_buffer(a.mask_bits + head_offset(bh, a.heads, a.mbits_sb, a.mbits_sh),
                         (unsigned)a.seq_q * (unsigned)a.mask_words * 4u);
 
-  // Copies of key block T into its ring slot: the K and V tiles split over the 8 waves;
-  // with a hard mask waves 0-3 add the words of 64 rows each.
+  // Copies of key block T into its ring slot: the K and V tiles split over the waves;
+  // with a hard mask waves 0 .. kQ/64 - 1 add the words of 64 rows each.
   auto issue = [&](int32_t T) {
     unsigned char* const slot = lds + (T % W::kSlots) * kSlotBytes;
     const unsigned row0 = (unsigned)(G::kRows * T) * kv_row;
@@ -595,12 +595,12 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
       else
         dma_load_x4(v_rsrc, row0 + tile_src<D, true>(c - W::kDma, lane, kv_row), lds_address(slot + 1024 * c));
     }
-    if (MASKED && wave < 4)
+    if (MASKED && wave < W::kQ / 64)
       dma_load_x1(w_rsrc, ((unsigned)(q0 + 64 * wave + lane) * (unsigned)a.mask_words + (unsigned)T) * 4u,
                   lds_address(slot + 2 * G::kTileBytes + 256 * wave));
   };
   // Wait until at most the copies of the last n blocks issued are in flight.
-  const int copies_per_block = (wave < W::kTileCopies ? W::kTileCopiesPerWave : 0) + (MASKED && wave < 4 ? 1 : 0);
+  const int copies_per_block = (wave < W::kTileCopies ? W::kTileCopiesPerWave : 0) + (MASKED && wave < W::kQ / 64 ? 1 : 0);
   auto wait_blocks = [&](int n) { wait_vmcnt_n(copies_per_block * min(n, 2)); };
 
   // This wave's rows: lse2 and D (the preprocess pads past seq_q), and Q and dO as B
@@ -644,8 +644,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_bf16_kernel(BwdArgs a) {
   };
   // Waves 4-7 (each sharing a SIMD with wave - 4) run their dQ product of block T at the
   // start of step T + 1, so that the two waves of a SIMD are half a step apart and one's
-  // MFMAs meet the other's softmax.
-  const bool late = wave >= 4;
+  // MFMAs meet the other's softmax (not at head dim 256: one wave per SIMD).
+  const bool late = W::kWaves == 8 && wave >= 4;
   bf16x8 pds_late[2];
   bool pending = false;
   const unsigned char* late_slot = lds;
@@ -734,13 +734,15 @@ hipError_t launch_bwd_bf16_variant(const BwdArgs& a0, hipStream_t s, hipEvent_t 
   if (ev_pre && hipEventRecord(ev_pre, s) != hipSuccess) return hipErrorInvalidValue;
   if (nk > 0) {
     a.nwg = (uint32_t)(a.bh * ((a.nkb + KVGeom<D>::kKB - 1) / KVGeom<D>::kKB));
-    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, CAUSAL, MASKED, F16>), dim3(a.nwg), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, CAUSAL, MASKED, F16>), dim3(a.nwg),
+                       dim3(64 * KVGeom<D>::kWaves), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   if (ev_dkdv && hipEventRecord(ev_dkdv, s) != hipSuccess) return hipErrorInvalidValue;
   if (nq > 0) {
     a.nwg = (uint32_t)(a.bh * ((a.nqb + QGeom<D>::kWaves - 1) / QGeom<D>::kWaves));
-    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, CAUSAL, MASKED, F16>), dim3(a.nwg), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, CAUSAL, MASKED, F16>), dim3(a.nwg),
+                       dim3(64 * QGeom<D>::kWaves), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   return hipSuccess;
@@ -769,6 +771,9 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, bool causal, hipStrea
   if (head_dim == 128)
     return a.in_f16 ? launch_bwd_bf16_d<128, true>(a, causal, s, ev_pre, ev_dkdv)
                     : launch_bwd_bf16_d<128, false>(a, causal, s, ev_pre, ev_dkdv);
+  if (head_dim == 256)
+    return a.in_f16 ? launch_bwd_bf16_d<256, true>(a, causal, s, ev_pre, ev_dkdv)
+                    : launch_bwd_bf16_d<256, false>(a, causal, s, ev_pre, ev_dkdv);
   return hipErrorInvalidValue;
 }
 

@@ -654,8 +654,8 @@ int check_bwd_shape(int in_dtype, size_t batch, size_t heads, size_t seq_q, size
                     size_t d, double scale, BwdShape* b, int layout = SMA_LAYOUT_BHSD) {
   int st = check_shape(in_dtype, SMA_DTYPE_F32, batch, heads, seq_q, seq_kv, d, scale, &b->s, layout);
   if (st != SMA_OK) return st;
-  // fp32, bf16 or fp16 Q, K, V; head dims 32, 64 and 128.
-  if (d != 32 && d != 64 && d != 128) return SMA_ERR_UNSUPPORTED;
+  // fp32, bf16 or fp16 Q, K, V; head dims 32, 64 and 128, and 256 with 16-bit inputs.
+  if (d != 32 && d != 64 && d != 128 && !(d == 256 && in_dtype != SMA_DTYPE_F32)) return SMA_ERR_UNSUPPORTED;
   // The kernels address one (batch, head) through 32-bit buffer offsets: rows of
   // row_elems elements (heads*d under [B,S,H,d]), with a block of slack.
   const size_t blk = sma::kBwdRowsPerBlock;

@@ -369,8 +369,10 @@ def test_backward_workspace_and_host_checks():
     # 16-bit inputs take a larger workspace (the 16-bit copy of dO): the fp32 size is too small
     assert call(idt=BF16, wsb=8 * 256) == INVAL and call(idt=BF16, d=96) == UNSUP
     assert call(idt=F16, wsb=8 * 256) == INVAL and call(idt=F16, d=96) == UNSUP
-    assert call(d=256) == UNSUP                                             # forward-only head dim
+    assert call(d=256) == UNSUP                                 # fp32: not built for head dim 256
     assert sma.attention_bwd_workspace_bytes(F32, 1, 1, 33, 50, 256, False) == 0
+    assert sma.attention_bwd_workspace_bytes(BF16, 1, 1, 33, 50, 256, False) == 2 * 256 + 33 * 256 * 2  # 16-bit: built
+    assert sma.attention_bwd_workspace_bytes(F16, 1, 1, 33, 50, 256, False) > 0
     assert sma.attention_bwd_workspace_bytes(F32, 1, 1, 33, 50, 32, False) == 2 * 256  # head dim 32
     assert call(sq=(1 << 23), d=64) == UNSUP                                 # 32-bit tile offsets
     assert call(q=q + 8) == MISAL and call(dk=dk + 4) == MISAL and call(lse=lse + 2) == MISAL

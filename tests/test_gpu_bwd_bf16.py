@@ -112,7 +112,7 @@ def _small(shape, causal, d):
     return bits, g, scale, _oracle(q, k, v, g, scale, causal)
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_bwd_bf16_parity_small(shape, causal, d):
@@ -121,7 +121,7 @@ def test_bwd_bf16_parity_small(shape, causal, d):
     print(shape, causal, d, check_grads(got, ref, bound, f"{shape} causal={causal} d={d}"))
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 def test_bwd_bf16_rows_without_keys(d):
     """Causal with more queries than keys: the first sq - skv rows admit nothing."""
     (q, k, v), bits, g = _case(801 + d, 1, 2, 150, 100, d)
@@ -132,7 +132,7 @@ def test_bwd_bf16_rows_without_keys(d):
     check_grads(got, ref, bound, "empty rows")
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 def test_bwd_bf16_no_keys_and_no_queries(d):
     import torch
 
@@ -218,7 +218,7 @@ def test_bwd_bf16_binding_checks():
         sma.attention_bwd(q, q, q, o, lse, o.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("name", ["bf16_causal_b1h32_s16384_d128"])
+@pytest.mark.parametrize("name", ["bf16_causal_b1h32_s16384_d128", "bf16_causal_b1h32_s16384_d256"])
 def test_bwd_bf16_full_size_exact_subproblems(name):
     """The full workload in one launch sequence; exact oracle values from sub-problems that
     bottom-right causal alignment keeps intact. The last T query rows with every key form a

@@ -123,7 +123,7 @@ SHAPES = [  # (B, H, sq, skv): several blocks with ragged tails, cross shapes bo
 ]
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_bwd_f16_parity_small(shape, causal, d):

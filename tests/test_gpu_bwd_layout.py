@@ -23,8 +23,8 @@ def _gpu():
     sma.library()
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("d", [32, 64, 128])
+# (the fp32 backward is not built for head dim 256)
+@pytest.mark.parametrize("dtype,d", [(t, d) for t in ("f32", "bf16", "f16") for d in (32, 64, 128, 256) if not (t == "f32" and d == 256)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(2, 3, 130, 77), (1, 2, 200, 333), (2, 1, 257, 129)],
                          ids=lambda s: "x".join(map(str, s)))

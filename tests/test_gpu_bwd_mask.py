@@ -83,10 +83,10 @@ def _check(got, ref, bound, dtype, label, under=(0.0, 0.0, 0.0)):
 FORMS = {"shared": (1, 1), "per_head": (1, "H"), "full": ("B", "H")}
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+# (the fp32 backward is not built for head dim 256)
+@pytest.mark.parametrize("dtype,d", [(t, d) for t in ("f32", "bf16", "f16") for d in (32, 64, 128, 256) if not (t == "f32" and d == 256)])
 @pytest.mark.parametrize("form", list(FORMS))
 @pytest.mark.parametrize("density", [0.3, 0.9])
-@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_masked_backward_parity(causal, d, density, form, dtype):
     B, H, sq, skv = 2, 2, 130, 177
