@@ -9,11 +9,11 @@
 // F16). The probabilities are rounded to the input's 16-bit type (nearest
 // even) for the P V product; the row sums use the fp32 probabilities.
 //
-// Workgroup: 8 waves x 32 query rows = 256 rows, two waves per SIMD (at head
-// dim 256: 4 waves x 32 rows, one wave per SIMD, see BGeom). Key tiles of 64
-// rows (32 at d = 256) go HBM/L2 -> LDS through buffer-resource direct-to-LDS
-// loads into a ring of four slots, two tiles ahead of their use, without
-// passing through registers; loads past the last key return zeros.
+// Head dims 32-128: 8 waves x 32 query rows = 256 rows, two waves per SIMD. Key
+// tiles of 64 rows go HBM/L2 -> LDS through buffer-resource direct-to-LDS loads
+// into a ring of four slots, two tiles ahead of their use, without passing
+// through registers; loads past the last key return zeros. Head dim 256 runs
+// the role-split kernel further down (attn_fwd_bf16_rs_kernel).
 //
 // S^T = K Q^T: lane (m, h) supplies K[key m] and Q[query m] at head dims
 // h*D/2 + 8*step .. + 7 and receives the scores of query (lane % 32). K rows
@@ -30,11 +30,9 @@
 // of the three phases.
 //
 // The library is built with VGPR-form MFMAs (accumulators in the architectural
-// registers). At d = 256 a wave needs more than 256 registers, and the
-// compiler's default there puts the accumulators in AGPRs and copies all of O
-// back to VGPRs on every tile for the rare rescale, about 150 extra VALU
-// instructions per tile.
+// registers).
 #include "attn_common.h"
+
 
 namespace sma {
 namespace {
@@ -67,21 +65,16 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-// Geometry per head dim. At d = 256 a 32-row block's O alone takes 128
-// registers and Q 64 more, past the 256 a wave may hold at two waves per SIMD:
-// the workgroup is then 4 waves, one per SIMD (up to 512 registers each), and
-// tiles have 32 keys (64 KB of K and V per ring slot would not fit 4 slots).
-// With no second wave on its SIMD, a d = 256 wave runs every step in the
-// early order. At d = 32 a tensor's tile is 256 chunks: waves 0-3 copy K,
-// waves 4-7 copy V.
+// Geometry per head dim (32, 64, 128). At d = 32 a tensor's tile is 256 chunks:
+// waves 0-3 copy K, waves 4-7 copy V.
 template <int D>
 struct BGeom {
-  static constexpr int kWaves = D == 256 ? 4 : 8;
+  static_assert(D == 32 || D == 64 || D == 128, "the 8-wave kernel's head dims");
+  static constexpr int kWaves = 8;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr bool kPaired = kWaves == 8;       // two waves per SIMD, half a step apart
   static constexpr int kQW = 32;                     // query rows per wave
   static constexpr int kQ = kWaves * kQW;            // query rows per workgroup
-  static constexpr int kK = D == 256 ? kBF16D256KeysPerTile : kBF16KeysPerTile;  // keys per tile
+  static constexpr int kK = kBF16KeysPerTile;        // keys per tile
   static constexpr int kKB = kK / 32;                // 32-key blocks per tile
   static constexpr int kSlots = 4;                   // LDS ring of K/V tiles
   static constexpr int kChunksPerRow = D / 8;        // 16-byte chunks per K or V row
@@ -93,7 +86,7 @@ struct BGeom {
   static constexpr int kHalf = D / 2;
   static constexpr int kSteps = D / 16;              // QK^T k-steps (8 dims per lane half)
   static constexpr int kNch = D / 32;                // 32-wide output chunks
-  static_assert(kQ == (D == 256 ? kBF16D256QueriesPerWG : kBF16QueriesPerWG), "planner geometry");
+  static_assert(kQ == kBF16QueriesPerWG, "planner geometry");
   static_assert(kLoadsPerThread >= 1 && kLoadsPerThread * 64 * kCopyWaves == kTileChunks,
                 "tile split");
 };
@@ -401,7 +394,7 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
     l_run += psum;
   };
 
-  const bool late = G::kPaired && wave >= G::kWaves / 2;
+  const bool late = wave >= G::kWaves / 2;
   V8 pb_late[G::kKB][2];
   bool late_pending = false;
   int late_slot = 0;
@@ -476,6 +469,373 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
     }
 }
 
+// ---------------------------------------------------------------- role-split kernel
+// Head dim 256, where one wave holding both Q (64 registers) and all of O (128) would
+// leave a SIMD a single wave. A workgroup of 12 waves is 6 pairs and 192 query rows. For
+// pair p (rows q0 + 32p .. + 31), wave p (the S wave) holds Q, forms S^T = K Q^T, the
+// lazy running max, the probabilities and the row sums, and leaves P (in the input's
+// 16-bit type, already in the B-operand layout of the P V product) and the tile's
+// rescale factor in LDS; wave 6 + p (the O wave) holds O and forms
+// O^T = alpha O^T + V^T P^T one tile behind. Neither role needs more than 168
+// registers, so three waves share each SIMD, and one wave's MFMAs run while another
+// works on the VALU. K tiles of 32 keys come through a 3-slot ring and V tiles through a
+// 4-slot ring, both two tiles ahead of the S waves, copied by waves 0-7; one barrier per
+// tile.
+template <int D>
+struct RGeom {
+  static constexpr int kPairs = 6;
+  static constexpr int kWaves = 2 * kPairs;
+  static constexpr int kCopyWaves = 8;  // waves 0-7 issue the tile copies
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kQW = 32;
+  static constexpr int kQ = kPairs * kQW;
+  static constexpr int kK = kBF16D256KeysPerTile;
+  static constexpr int kKB = kK / 32;
+  static constexpr int kKSlots = 3;
+  static constexpr int kVSlots = 4;
+  static constexpr int kChunksPerRow = D / 8;
+  static constexpr int kTileChunks = kK * kChunksPerRow;
+  static constexpr int kLoadsPerThread = kTileChunks / (64 * kCopyWaves);  // per tensor and tile
+  static constexpr int kLoadsPerTile = 2 * kLoadsPerThread;
+  static constexpr int kHalf = D / 2;
+  static constexpr int kSteps = D / 16;
+  static constexpr int kNch = D / 32;
+  static_assert(kQ == kBF16D256QueriesPerWG, "planner geometry");
+  static_assert(D == 256, "role-split geometry");
+  static_assert(kLoadsPerThread >= 1 && kLoadsPerThread * 64 * kCopyWaves == kTileChunks, "tile split");
+};
+
+template <int D, bool CAUSAL, bool F16, bool MASKED>
+__global__ __launch_bounds__(RGeom<D>::kThreads) void attn_fwd_bf16_rs_kernel(FwdArgs a) {
+  using G = RGeom<D>;
+  using H = Half<F16>;
+  using V8 = typename H::V8;
+  __shared__ __attribute__((aligned(16))) u32x4 k_lds[G::kKSlots][G::kTileChunks];
+  __shared__ __attribute__((aligned(16))) u32x4 v_lds[G::kVSlots][G::kTileChunks];
+  // P of a tile per pair and parity: [2 kb + t2][lane] holds lane's B operand of P V
+  // k-step (kb, t2); the rescale factor per lane (1 when the max did not move); and
+  // the S waves' final row sums.
+  __shared__ __attribute__((aligned(16))) u32x4 p_lds[G::kPairs][2][2 * G::kKB][64];
+  __shared__ float a_lds[G::kPairs][2][64];
+  __shared__ float l_lds[G::kPairs][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool swave = wave < G::kPairs;
+  const int pair = swave ? wave : wave - G::kPairs;
+  const int lm = lane & 31;
+  const int lh = lane >> 5;
+
+  const TileId t = decode_tile(blockIdx.x, a);
+  const int32_t q0 = t.qb * G::kQ;
+  const int32_t qw0 = q0 + pair * G::kQW;
+  const int32_t ks = t.split * a.split_len;
+  const int32_t split_end = min(a.seq_kv, ks + a.split_len);
+  const int32_t wg_last_row = min(q0 + G::kQ - 1, a.seq_q - 1);
+  const int32_t ke = key_limit<CAUSAL>(wg_last_row, a.seq_q, a.seq_kv, split_end);
+  const int32_t ntiles = ke > ks ? (ke - ks + G::kK - 1) / G::kK : 0;
+
+  const bool wave_live = qw0 < a.seq_q;
+  const int32_t wave_lo = key_limit<CAUSAL>(qw0, a.seq_q, a.seq_kv, split_end);
+  const int32_t wave_hi = key_limit<CAUSAL>(min(qw0 + G::kQW - 1, a.seq_q - 1), a.seq_q,
+                                            a.seq_kv, split_end);
+  const int32_t my_row = qw0 + lm;
+  const int32_t lim = key_limit<CAUSAL>(my_row, a.seq_q, a.seq_kv, split_end);
+
+  const unsigned kv_bytes = strided_range(a.seq_kv, a.kvs_s, D, 2);
+  const unsigned kv_row = (unsigned)(a.kvs_s * 2);
+  const int64_t kv_off = head_offset(t.bh, a.heads, a.kvs_b, a.kvs_h);
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      raw_buffer(static_cast<const unsigned short*>(a.k) + kv_off, kv_bytes);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      raw_buffer(static_cast<const unsigned short*>(a.v) + kv_off, kv_bytes);
+  // As in the kernel above: position p = (u*waves + wave)*64 + lane of a tile is row
+  // p / chunks_per_row, chunk p % chunks_per_row, under the K row permutation and the
+  // swizzles.
+  constexpr int kRowsPerU = G::kCopyWaves * 64 / G::kChunksPerRow;
+  const int rho0 = (wave * 64 + lane) / G::kChunksPerRow;
+  const int pc = lane % G::kChunksPerRow;
+  auto k_src = [&](int u) {
+    const int rho = rho0 + u * kRowsPerU;
+    return (unsigned)((rho & ~31) | swap_bits_2_3(rho & 31)) * kv_row + 16u * (unsigned)(pc ^ k_swz<D>(rho));
+  };
+  auto v_src = [&](int u) {
+    const int rho = rho0 + u * kRowsPerU;
+    return (unsigned)rho * kv_row + 16u * (unsigned)(pc ^ v_swz<D>(rho));
+  };
+  auto issue_tile = [&](int32_t T) {
+    const unsigned tile_ofs = (unsigned)(ks + T * G::kK) * kv_row;
+    const int ksl = T % G::kKSlots, vsl = T % G::kVSlots;
+    if (wave >= G::kCopyWaves) return;
+#pragma unroll
+    for (int u = 0; u < G::kLoadsPerThread; ++u) {
+      const int base = (u * G::kCopyWaves + wave) * 64;
+      dma_load_x4(k_rsrc, k_src(u) + tile_ofs, lds_address(&k_lds[ksl][base]));
+      dma_load_x4(v_rsrc, v_src(u) + tile_ofs, lds_address(&v_lds[vsl][base]));
+    }
+  };
+
+  // The hard mask, packed by columns as for the kernel above (one 32-row block per pair).
+  const uint32_t* mcols = nullptr;
+  const uint32_t* mcls = nullptr;
+  if (MASKED) {
+    const int64_t rb = qw0 / 32;
+    mcols = a.mask_bits + head_offset(t.bh, a.heads, a.mbits_sb, a.mbits_sh) + rb * a.mask_words;
+    mcls = a.mask_cls + head_offset(t.bh, a.heads, a.mcls_sb, a.mcls_sh) + rb * a.mask_tiles;
+  }
+  // Whether tile T holds keys of this pair's rows that are not all closed by the mask
+  // (both waves of the pair evaluate it alike), and the tile's mask class.
+  auto tile_class = [&](int32_t T) -> uint32_t {
+    if (!wave_live || ks + T * G::kK >= wave_hi) return 0u;
+    return MASKED ? scalar_load<uint32_t>(mcls + (ks + T * G::kK) / 64) : 1u;
+  };
+
+  // The step loop (its waits, barrier and copies), run by every wave with its role's
+  // work; each role has its own copy of the loop, so that its registers stay put.
+  auto run_steps = [&](auto&& work) {
+    if (ntiles > 0) issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    for (int32_t T = 0; T <= ntiles; ++T) {
+      if (T + 1 < ntiles) wait_vmcnt<G::kLoadsPerTile>();
+      else wait_vmcnt<0>();
+      __syncthreads();  // tile T has landed; step T - 1 is done with its slots and P
+      if (T + 2 < ntiles) issue_tile(T + 2);
+      work(T);
+    }
+  };
+
+  const float c = fmaxf(a.c, 1.17549435e-38f);  // as in the kernel above
+  const size_t row_id = (size_t)t.bh * a.seq_q + my_row;
+
+  if (swave) {
+    // Q operands in registers (the copies below are invisible to the compiler's load
+    // counting, so its own loads must be done first).
+    V8 qr[G::kSteps];
+    {
+      const unsigned short* qp = static_cast<const unsigned short*>(a.q) +
+                                 head_offset(t.bh, a.heads, a.qs_b, a.qs_h) +
+                                 (int64_t)min(my_row, a.seq_q - 1) * a.qs_s + lh * G::kHalf;
+      const unsigned flip = a.negate_q ? 0x80008000u : 0u;
+#pragma unroll
+      for (int s = 0; s < G::kSteps; ++s) {
+        u32x4 x = *reinterpret_cast<const u32x4*>(qp + 8 * s);
+        x ^= flip;
+        qr[s] = __builtin_bit_cast(V8, x);
+      }
+    }
+    wait_vmcnt<0>();
+    float m_run = -INFINITY, l_run = 0.f;
+    run_steps([&](int32_t T) {
+      if (T >= ntiles) return;
+      const uint32_t cls = tile_class(T);
+      if (cls == 0u) return;
+      const int32_t j0 = ks + T * G::kK;
+      const unsigned char* ktile = reinterpret_cast<const unsigned char*>(&k_lds[T % G::kKSlots][0]);
+      auto k_operand = [&](int kb, int st) {
+        const int rho = 32 * kb + lm;
+        const int chunk = lh * G::kSteps + st;
+        return __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(
+                                          ktile + rho * (2 * D) + 16 * (chunk ^ k_swz<D>(rho))));
+      };
+      f32x16 sacc[G::kKB];
+#pragma unroll
+      for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      constexpr int kPf = 2;
+      V8 kop[kPf + 1][G::kKB];
+#pragma unroll
+      for (int st = 0; st < kPf; ++st)
+#pragma unroll
+        for (int kb = 0; kb < G::kKB; ++kb) kop[st][kb] = k_operand(kb, st);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int st = 0; st < G::kSteps; ++st) {
+        if (st + kPf < G::kSteps)
+#pragma unroll
+          for (int kb = 0; kb < G::kKB; ++kb) kop[(st + kPf) % (kPf + 1)][kb] = k_operand(kb, st + kPf);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < G::kKB; ++kb) sacc[kb] = H::mfma(kop[st % (kPf + 1)][kb], qr[st], sacc[kb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+
+      if (j0 + G::kK > wave_lo) {
+        int32_t rel = lim - j0 - 8 * lh;  // key 32kb + 16(r/8) + r%8 allowed iff < rel
+        asm volatile("" : "+v"(rel));
+#pragma unroll
+        for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sacc[kb][r] = (32 * kb + 16 * (r / 8) + (r % 8) < rel) ? sacc[kb][r] : -INFINITY;
+      }
+      if (MASKED && cls == 2u) {
+        const float ninf = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            typedef unsigned u32x16 __attribute__((ext_vector_type(16)));
+            const u32x16 w = scalar_load<u32x16>(mcols + (j0 + 32 * kb + 16 * g));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const uint64_t lanes = (uint64_t)w[2 * i] | ((uint64_t)w[2 * i + 1] << 32);
+              float x = sacc[kb][8 * g + i];
+              asm("v_cndmask_b32_e64 %0, %1, %0, %2" : "+v"(x) : "v"(ninf), "s"(lanes));
+              sacc[kb][8 * g + i] = x;
+            }
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float tmax = mx == -INFINITY ? -INFINITY : mx * c;
+      float alpha = 1.f;
+      if (__any(tmax > m_run + kTau)) {
+        const float m_new = fmaxf(m_run, tmax);
+        alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+      float psum = 0.f;
+      V8 pb[G::kKB][2];
+#pragma unroll
+      for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * t2 + e], c, neg_m));
+            psum += p;
+            pb[kb][t2][e] = (typename H::E)p;
+          }
+      l_run += psum;
+      const int par = T & 1;
+#pragma unroll
+      for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) p_lds[pair][par][2 * kb + t2][lane] = __builtin_bit_cast(u32x4, pb[kb][t2]);
+      a_lds[pair][par][lane] = alpha;
+    });
+    // Epilogue: the row sums for the O wave, and the LSE.
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    l_lds[pair][lane] = l_tot;
+    __syncthreads();
+    if (!wave_live || my_row >= a.seq_q || lh != 0) return;
+    const bool empty = !(l_tot > 0.f);
+    const float lse2 = empty ? -INFINITY : m_run + __builtin_amdgcn_logf(l_tot);
+    if (a.nsplit == 1) {
+      if (a.lse) a.lse[row_id] = empty ? -INFINITY : lse2 * 0.69314718055994530942f;
+    } else {
+      a.part_lse[(size_t)t.split * ((size_t)a.bh * a.seq_q) + row_id] = lse2;
+    }
+  } else {
+    f32x16 oacc[G::kNch];
+#pragma unroll
+    for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
+    const int srole = lane & 15;
+    const int colq = 2 * ((lane >> 4) & 1) + ((srole & 3) >> 1);
+    const int half8 = 8 * (srole & 1);
+    run_steps([&](int32_t T) {
+      if (T == 0 || tile_class(T - 1) == 0u) return;
+      const int par = (T - 1) & 1;
+      const float alpha = a_lds[pair][par][lane];
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+      }
+      V8 pb[G::kKB][2];
+#pragma unroll
+      for (int kb = 0; kb < G::kKB; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) pb[kb][t2] = __builtin_bit_cast(V8, p_lds[pair][par][2 * kb + t2][lane]);
+      const unsigned char* vtile = reinterpret_cast<const unsigned char*>(&v_lds[(T - 1) % G::kVSlots][0]);
+      auto v_operand = [&](int i) {
+        const int kb = i / (2 * G::kNch), t2 = (i / G::kNch) % 2, cb = i % G::kNch;
+        const int r_lo = 32 * kb + 16 * t2 + 8 * lh + srole / 4;
+        const int r_hi = r_lo + 4;
+        const int chunk = 4 * cb + colq;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vtile + r_lo * (2 * D) +
+                                                       16 * (chunk ^ v_swz<D>(r_lo)) + half8));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vtile + r_hi * (2 * D) +
+                                                       16 * (chunk ^ v_swz<D>(r_hi)) + half8));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        return __builtin_bit_cast(V8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+      };
+      constexpr int kN = 2 * G::kKB * G::kNch;
+      constexpr int kPf = 1;  // one operand ahead: the O wave has 40 registers beside its accumulators
+      V8 vop[kPf + 1];
+#pragma unroll
+      for (int i = 0; i < kPf; ++i) vop[i] = v_operand(i);
+#pragma unroll
+      for (int i = 0; i < kN; ++i) {
+        if (i + kPf < kN) vop[(i + kPf) % (kPf + 1)] = v_operand(i + kPf);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kb = i / (2 * G::kNch), t2 = (i / G::kNch) % 2, cb = i % G::kNch;
+        oacc[cb] = H::mfma(vop[i % (kPf + 1)], pb[kb][t2], oacc[cb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+    __syncthreads();  // the S waves' row sums
+    const float l_tot = l_lds[pair][lane];
+    if (!wave_live || my_row >= a.seq_q) return;
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : 1.0f / l_tot;
+    float* orow = nullptr;
+    unsigned short* orow16 = nullptr;
+    if (a.nsplit == 1) {
+      const int64_t o_off = head_offset(t.bh, a.heads, a.qs_b, a.qs_h) + (int64_t)my_row * a.qs_s;
+      if (a.o_bf16) orow16 = a.o_bf16 + o_off;
+      else orow = a.o + o_off;
+    } else {
+      orow = a.part_o + ((size_t)t.split * ((size_t)a.bh * a.seq_q) + row_id) * D;
+    }
+#pragma unroll
+    for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = empty ? 0.f : oacc[cb][4 * g4 + e] * inv;
+        if (orow16)
+          *reinterpret_cast<u32x2*>(orow16 + 32 * cb + 8 * g4 + 4 * lh) =
+              u32x2{pack_out16(out[0], out[1], a.o_f16), pack_out16(out[2], out[3], a.o_f16)};
+        else
+          *reinterpret_cast<f32x4*>(orow + 32 * cb + 8 * g4 + 4 * lh) = out;
+      }
+  }
+}
+
+template <bool CAUSAL>
+hipError_t launch_bf16_rs(const FwdArgs& a, bool f16, hipStream_t s) {
+  constexpr int D = 256;
+  const dim3 grid(a.nwg), block(RGeom<D>::kThreads);
+  if (a.mask_bits) {
+    if (f16) hipLaunchKernelGGL((attn_fwd_bf16_rs_kernel<D, CAUSAL, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16_rs_kernel<D, CAUSAL, false, true>), grid, block, 0, s, a);
+  } else {
+    if (f16) hipLaunchKernelGGL((attn_fwd_bf16_rs_kernel<D, CAUSAL, true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16_rs_kernel<D, CAUSAL, false, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bf16_variant(const FwdArgs& a, bool f16, hipStream_t s) {
   const dim3 grid(a.nwg), block(BGeom<D>::kThreads);
@@ -496,7 +856,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, bool causal, bool f16
     case 32: return causal ? launch_bf16_variant<32, true>(a, f16, s) : launch_bf16_variant<32, false>(a, f16, s);
     case 64: return causal ? launch_bf16_variant<64, true>(a, f16, s) : launch_bf16_variant<64, false>(a, f16, s);
     case 128: return causal ? launch_bf16_variant<128, true>(a, f16, s) : launch_bf16_variant<128, false>(a, f16, s);
-    case 256: return causal ? launch_bf16_variant<256, true>(a, f16, s) : launch_bf16_variant<256, false>(a, f16, s);
+    case 256: return causal ? launch_bf16_rs<true>(a, f16, s) : launch_bf16_rs<false>(a, f16, s);
     default: return hipErrorInvalidValue;
   }
 }

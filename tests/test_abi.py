@@ -255,10 +255,10 @@ def test_plan_rejects():
     for d in (32, 256):
         assert P(F32, 1, 1, 8, 8, d, False, kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=1).nsplit == 1
         assert P(BF16, 1, 1, 8, 8, d, False, kernel=sma.SMA_KERNEL_BF16_QBLOCK, nsplit=1).nsplit == 1
-    # the 16-bit kernel's geometry: 256 rows and 64-key tiles, 128 rows and 32-key tiles at d = 256
+    # the 16-bit kernel's geometry: 256 rows and 64-key tiles, 192 rows and 32-key tiles at d = 256
     K16 = sma.SMA_KERNEL_BF16_QBLOCK
     assert P(BF16, 1, 4, 1000, 1000, 32, True, kernel=K16, nsplit=1).workgroups == 4 * 4
-    assert P(BF16, 1, 4, 1000, 1000, 256, True, kernel=K16, nsplit=1).workgroups == 4 * 8
+    assert P(BF16, 1, 4, 1000, 1000, 256, True, kernel=K16, nsplit=1).workgroups == 4 * 6
     p = P(F16, 1, 1, 128, 4096, 256, False, num_cus=256)  # one 128-row block: split in 32-key tiles
     assert p.nsplit == 32 and p.workspace_bytes >= 32 * 128 * 257 * 4
     lib = sma.library()

@@ -5,6 +5,7 @@ Each case runs two calls in a row, the second on a smaller input, and compares
 every output with sma_attention_fwd_ex given a torch workspace and the same
 plan (the same kernels, so bitwise equal) and with the oracle at the parity
 bars. A plan whose split does not fit the scratch is refused before launch."""
+import gc
 import math
 
 import numpy as np
@@ -50,11 +51,18 @@ def _run(noalloc, vals, bits, dtype, causal, kernel, nsplit, layout="bhsd"):
     s = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
     if noalloc:
-        before = torch.cuda.memory_allocated()
-        sma.attention_fwd_noalloc_raw(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(),
-                                      lse.data_ptr(), in_dt, sma.SMA_DTYPE_F32, B, H, sq, skv, d,
-                                      scale, causal, pl, s, layout=lay)
-        assert torch.cuda.memory_allocated() == before
+        # Python's collector could free an unrelated tensor left by an earlier test in the
+        # middle of the call, which would read as a change: collect first, then hold it off.
+        gc.collect()
+        gc.disable()
+        try:
+            before = torch.cuda.memory_allocated()
+            sma.attention_fwd_noalloc_raw(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(),
+                                          lse.data_ptr(), in_dt, sma.SMA_DTYPE_F32, B, H, sq, skv, d,
+                                          scale, causal, pl, s, layout=lay)
+            assert torch.cuda.memory_allocated() == before
+        finally:
+            gc.enable()
     else:
         need = pl.workspace_bytes if pl is not None else sma.workspace_bytes(
             in_dt, B, H, sq, skv, d, causal, layout=layout)
