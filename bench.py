@@ -60,8 +60,15 @@ def min_bytes(w, o_elem: int = 4) -> int:
     return bh * ((w.seq_q + 2 * w.seq_kv) * w.head_dim * e + w.seq_q * w.head_dim * o_elem + w.seq_q * 4)
 
 
-# Device function of each sma_kernel code (the name rocprofv3 reports).
+# Device function of each sma_kernel code (the name rocprofv3 reports); the 16-bit kernel
+# code runs the role-split function at head dim 256.
 KERNEL_FUNCTIONS = {0: "attn_fwd_f32_kernel", 1: "attn_fwd_f32_wsplit_kernel", 2: "attn_fwd_bf16_kernel"}
+
+
+def kernel_function(plan_kernel: int, head_dim: int) -> str:
+    if plan_kernel == 2 and head_dim == 256:
+        return "attn_fwd_bf16_rs_kernel"
+    return KERNEL_FUNCTIONS[plan_kernel]
 
 
 class HipEvents:
@@ -299,6 +306,7 @@ KERNEL_SOURCES = {"attn_fwd_f32_kernel": ["attn_fwd_f32.hip", "attn_common.h"],
                   "attn_bwd_dkdv_bf16_kernel": ["attn_bwd_bf16.hip", "attn_common.h"],
                   "attn_fwd_f32_wsplit_kernel": ["attn_fwd_f32_wsplit.hip", "attn_common.h"],
                   "attn_fwd_bf16_kernel": ["attn_fwd_bf16.hip", "attn_common.h"],
+                  "attn_fwd_bf16_rs_kernel": ["attn_fwd_bf16.hip", "attn_common.h"],
                   "row_softmax": ["row_softmax.hip"]}
 
 
@@ -817,8 +825,9 @@ def main():
     exact = 4.0 * d * allowed_pairs(w)
     achieved = exact / (k_avg * 1e-3) / 1e12
     # the committed counter passes were taken with fp32 output in [B,H,S,d]
-    traffic = None if (o16 or masked or args.layout != "bhsd") else read_traffic(KERNEL_FUNCTIONS[plan.kernel], w.name,
-                                            kernel_source_digest(KERNEL_FUNCTIONS[plan.kernel]))
+    kfn = kernel_function(plan.kernel, d)
+    traffic = None if (o16 or masked or args.layout != "bhsd") else read_traffic(kfn, w.name,
+                                                                                 kernel_source_digest(kfn))
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "settle_steps": settled, "ms_per_step": round(ms_per_step, 5),
@@ -833,7 +842,7 @@ def main():
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": (f"{KERNEL_FUNCTIONS[plan.kernel]}<{d},{str(w.causal).lower()}"
+                     "kernel": (f"{kfn}<{d},{str(w.causal).lower()}"
                                 + (",f16>" if w.dtype == "f16" else ">")),
                      "kernel_avg_ms": round(k_avg, 5),
                      "kernel_ms": step_stats(launches),
