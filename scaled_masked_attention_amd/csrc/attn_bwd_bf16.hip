@@ -7,8 +7,8 @@
 // accumulation and result).
 //
 // The arithmetic and the three launches (preprocess, dK/dV, dQ) are those of the fp32
-// backward, with workgroups shaped for 16-bit MFMA and two waves per SIMD (one at head
-// dim 256, where a wave's accumulators and operands pass 256 registers):
+// backward, with workgroups shaped for 16-bit MFMA and two waves per SIMD (the dQ kernel
+// runs one at head dim 256, where its rows' Q, dO and accumulators pass 256 registers):
 //   P_ij = 2^(c s_ij - lse2_i), D_i = dO_i . O_i, dP_ij = dO_i . v_j, dS_ij = P_ij (dP_ij - D_i),
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j,
 // with three roundings to the input type (nearest even) for the products: dO once, in
@@ -144,6 +144,55 @@ __device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, int lane
   return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
 }
 
+// The same reads from a tile whose LDS address is a multiple of 2*D bytes (D >= 128),
+// with every address formed inside the step from one base register and a constant. The
+// swizzle only flips bits 4..7 of a row's byte offset, so with the row's own part folded
+// into the base, chunk 2*st + h of row p sits at (base ^ 32*(st % 8)) + 256*(st / 8), and
+// the chunks of a transposing read at (base ^ 64*(cb % 4)) + 256*(cb / 4) + 32*D*t2 (the
+// swizzle of rows 16*t2 + r does not depend on t2). The empty asm makes the base opaque,
+// so the compiler cannot hoist one precomputed offset per chunk out of the step loop and
+// hold them all in registers.
+template <int D>
+__device__ __forceinline__ unsigned row_base(unsigned tile, int p, int h) {
+  static_assert(D >= 128, "swizzle confined to bits 4..7");
+  unsigned b = tile + (unsigned)(p * 2 * D + 16 * (swz<D>(p) ^ h));
+  asm volatile("" : "+v"(b));
+  return b;
+}
+// The base again, opaque at this point of the program: a read formed from it cannot be
+// hoisted above an earlier pin, which keeps streamed reads in their place.
+__device__ __forceinline__ unsigned pin(unsigned& base) {
+  asm volatile("" : "+v"(base));
+  return base;
+}
+// An MFMA result, opaque at this point: the MFMA stays ahead of every later pin.
+__device__ __forceinline__ void pin_acc(f32x16& c) { asm volatile("" : "+v"(c)); }
+__device__ __forceinline__ bf16x8 row_read(unsigned base, int st) {
+  const unsigned a = (base ^ (32u * (unsigned)(st & 7))) + 256u * (unsigned)(st >> 3);
+  return __builtin_bit_cast(bf16x8, *(__attribute__((address_space(3))) const u32x4*)(size_t)a);
+}
+template <int D>
+__device__ __forceinline__ unsigned tr_base(unsigned tile, int lane, bool hi) {
+  static_assert(D >= 128, "swizzle confined to bits 4..7");
+  const int s = lane & 15;
+  const int colq = 2 * ((lane >> 4) & 1) + ((s & 3) >> 1);
+  const int r = 4 * (lane >> 5) + s / 4 + (hi ? 8 : 0);
+  unsigned b = tile + (unsigned)(r * 2 * D + 16 * (swz<D>(r) ^ colq) + 8 * (s & 1));
+  asm volatile("" : "+v"(b));
+  return b;
+}
+template <int D>
+__device__ __forceinline__ bf16x8 tr_read(unsigned lo_base, unsigned hi_base, int t2, int cb) {
+  const unsigned x = 64u * (unsigned)(cb & 3);
+  const unsigned imm = 256u * (unsigned)(cb >> 2) + 32u * D * (unsigned)t2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(size_t)((lo_base ^ x) + imm));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(size_t)((hi_base ^ x) + imm));
+  const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+}
+
 // N MFMAs, the i-th on the A operand op(i) (an LDS read) and run by mf(i, a); the reads
 // are issued kPf MFMAs ahead of their use, and scheduling barriers keep them there.
 template <int N, int kPf, typename Op, typename Mf>
@@ -211,20 +260,25 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(BwdArgs a) {
 // back from LDS, forms dS = P (dP - D) and accumulates dK^T += Q^T dS. A wave keeps only
 // its key block's K or V (the B operand of S or dP) and one accumulator set in registers,
 // so two waves fit a SIMD; the two waves of a key block share one, and one's MFMAs run
-// while the other works on the VALU. At head dim 256 (64 registers of K or V, 128 of
-// accumulators) the workgroup is 64 keys, two key blocks and 4 waves, one per SIMD.
+// while the other works on the VALU. At head dim 256 a wave holds 64 registers of K or V
+// and 128 of accumulators, which leaves about 60 of the 256 that two waves per SIMD allow:
+// there its operand reads are streamed two MFMAs ahead at addresses formed in the step
+// (row_read, tr_read), so that no per-chunk offset or operand queue outgrows them.
 //
 // All the waves step through the query blocks together. Query block T's Q and dO tiles
 // (permuted), its lse2/D and, with a hard mask, the four key blocks' mask words of its rows
-// are copied straight into a ring of four LDS slots two steps ahead, each wave issuing a
-// share. In step T the P waves work on block T and the dS waves on block T - 1, whose P
-// the P waves left in LDS (fp32, double buffered) in step T - 1. One barrier per step.
+// are copied straight into a ring of four LDS slots two steps ahead (three slots, one step
+// ahead, at head dim 256, for the LDS), each wave issuing a share. In step T the P waves
+// work on block T and the dS waves on block T - 1, whose P the P waves left in LDS (fp32,
+// double buffered) in step T - 1. One barrier per step.
 template <int D>
 struct KVGeom {
-  static constexpr int kWaves = D == 256 ? 4 : 8;
+  static constexpr int kWaves = 8;
   static constexpr int kKB = kWaves / 2;                        // 32-key blocks per workgroup
   static constexpr int kKeys = 32 * kKB;
-  static constexpr int kSlots = 4;
+  // Ring slots, and blocks copied ahead (a dS wave still reads block T - 1 in step T).
+  static constexpr int kSlots = D == 256 ? 3 : 4;
+  static constexpr int kAhead = kSlots - 2;
   static constexpr int kTileBytes = HGeom<D>::kTileBytes;
   static constexpr int kDma = HGeom<D>::kDmaPerTile;            // 1 KB copies per tile
   static constexpr int kTileCopies = 2 * kDma;                  // Q and dO of one block
@@ -234,8 +288,8 @@ struct KVGeom {
   static constexpr int kXBytes = 16 * 64 * 4;                   // a wave's 16 P values per lane
   static_assert(kTileCopies < kWaves ? kTileCopies * 2 == kWaves : kTileCopiesPerWave * kWaves == kTileCopies,
                 "copy split");
-  static_assert(2 * kKB * kTileBytes <= kSlots * 2 * kTileBytes, "K and V stage in the ring");
   static constexpr int kMaskWaves = kKB / 2;  // waves 1.. that copy mask words (32 rows x 2 key blocks each)
+  static_assert(kMaskWaves < kKB, "the lse2/D and mask copies come from P waves (0 .. kKB - 1)");
 };
 
 // A vmcnt wait with a wave-uniform count (0..20; counts above 20 wait for 20, which is
@@ -256,9 +310,14 @@ __global__ __launch_bounds__(64 * KVGeom<D>::kWaves) void attn_bwd_dkdv_bf16_ker
   using W = KVGeom<D>;
   // Slot: Q tile, dO tile, lse2/D, and with a hard mask [key block][row] words.
   constexpr int kMaskBytes = MASKED ? W::kKB * G::kRows * 4 : 0;
-  constexpr int kSlotBytes = 2 * G::kTileBytes + G::kMetaBytes + kMaskBytes;
+  // Head dim 256 reads its tiles at XOR-formed addresses (row_read, tr_read): every tile
+  // starts on a multiple of 512 bytes.
+  constexpr int kAlign = D == 256 ? 2 * D : 16;
+  constexpr int kSlotBytes = (2 * G::kTileBytes + G::kMetaBytes + kMaskBytes + kAlign - 1) / kAlign * kAlign;
   constexpr int kRingBytes = W::kSlots * kSlotBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kRingBytes + 2 * W::kKB * W::kXBytes];
+  constexpr int kLdsBytes = kRingBytes + 2 * W::kKB * W::kXBytes;
+  static_assert(2 * W::kKB * G::kTileBytes <= kLdsBytes, "K and V stage through the LDS");
+  __shared__ __attribute__((aligned(kAlign))) unsigned char lds[kLdsBytes];
   unsigned char* const xbuf = lds + kRingBytes;  // [key block][parity][4][64 lanes][4 floats]
 
   const int tid = threadIdx.x;
@@ -303,8 +362,11 @@ __global__ __launch_bounds__(64 * KVGeom<D>::kWaves) void attn_bwd_dkdv_bf16_ker
 
   // Copies of query block T (absolute block qb_first + T) into its ring slot: the Q and dO
   // tiles split over the waves; wave 0 adds lse2/D, waves 1 .. kKB/2 the mask words
-  // (lane l of wave 1 + h: key block 2h + l / 32, row l % 32).
-  auto issue = [&](int32_t T) {
+  // (lane l of wave 1 + h: key block 2h + l / 32, row l % 32). These are P waves: `pw`
+  // (std::true_type in their loop) compiles the lse2/D and mask copies out of the dS
+  // waves' loop, whose registers they would otherwise hold.
+  auto issue = [&](int32_t T, auto pw) {
+    constexpr bool kP = decltype(pw)::value;
     const int32_t qb = qb_first + T;
     unsigned char* const slot = lds + (T % W::kSlots) * kSlotBytes;
 #pragma unroll
@@ -318,10 +380,10 @@ __global__ __launch_bounds__(64 * KVGeom<D>::kWaves) void attn_bwd_dkdv_bf16_ker
         dma_load_x4(g_rsrc, (unsigned)(G::kRows * qb) * g_row + tile_src<D, true>(c - W::kDma, lane, g_row),
                     lds_address(slot + 1024 * c));
     }
-    if (wave == 0)
+    if (kP && wave == 0)
       dma_load_x1(m_rsrc, (unsigned)qb * (unsigned)G::kMetaBytes + 4u * lane,
                   lds_address(slot + 2 * G::kTileBytes));
-    if (MASKED && wave >= 1 && wave <= W::kMaskWaves) {
+    if (MASKED && kP && wave >= 1 && wave <= W::kMaskWaves) {
       const int kbw = 2 * (wave - 1) + (lane >> 5);
       dma_load_x1(w_rsrc, ((unsigned)(G::kRows * qb + (lane & 31)) * (unsigned)a.mask_words +
                            (unsigned)(j0 / 32 + kbw)) * 4u,
@@ -372,14 +434,15 @@ __global__ __launch_bounds__(64 * KVGeom<D>::kWaves) void attn_bwd_dkdv_bf16_ker
 
   // The step loop (its waits, barrier and copies), run by every wave with its role's work.
   // Each role has its own copy of the loop, so that its accumulators keep their registers.
-  auto run_steps = [&](auto&& work) {
-    if (nblk > 0) issue(0);
-    if (nblk > 1) issue(1);
+  auto run_steps = [&](auto pw, auto&& work) {
+#pragma unroll
+    for (int u = 0; u < W::kAhead; ++u)
+      if (u < nblk) issue(u, pw);
     for (int32_t T = 0; T <= nblk; ++T) {
-      if (T + 1 < nblk) wait_all_but_last_block();
+      if (W::kAhead == 2 && T + 1 < nblk) wait_all_but_last_block();
       else wait_vmcnt<0>();
       __syncthreads();  // block T has landed; step T - 1 is done with its slots and P
-      if (T + 2 < nblk) issue(T + 2);
+      if (T + W::kAhead < nblk) issue(T + W::kAhead, pw);
       work(T);
     }
   };
@@ -390,13 +453,24 @@ __global__ __launch_bounds__(64 * KVGeom<D>::kWaves) void attn_bwd_dkdv_bf16_ker
     bf16x8 pp_late[2];
     bool pending = false;
     const unsigned char* g_late = lds;
-    run_steps([&](int32_t T) {
+    run_steps(std::true_type{}, [&](int32_t T) {
       if (pending) {
         __builtin_amdgcn_s_setprio(1);
+        if constexpr (D == 256) {
+          unsigned tl = tr_base<D>(lds_address(g_late), lane, false);
+          unsigned th = tr_base<D>(lds_address(g_late), lane, true);
+          mfma_stream<2 * G::kNch, 2>(
+              [&](int i) { return tr_read<D>(pin(tl), pin(th), i / G::kNch, i % G::kNch); },
+              [&](int i, bf16x8 x) {
+                acc[i % G::kNch] = mfma16<F16>(x, pp_late[i / G::kNch], acc[i % G::kNch]);
+                pin_acc(acc[i % G::kNch]);
+              });
+        } else {
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
+          for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-          for (int cb = 0; cb < G::kNch; ++cb) acc[cb] = mfma16<F16>(tr_operand<D>(g_late, lane, t2, cb), pp_late[t2], acc[cb]);
+            for (int cb = 0; cb < G::kNch; ++cb) acc[cb] = mfma16<F16>(tr_operand<D>(g_late, lane, t2, cb), pp_late[t2], acc[cb]);
+        }
         __builtin_amdgcn_s_setprio(0);
         pending = false;
       }
@@ -407,20 +481,51 @@ __global__ __launch_bounds__(64 * KVGeom<D>::kWaves) void attn_bwd_dkdv_bf16_ker
         const unsigned char* const g_slot = q_slot + G::kTileBytes;
         const unsigned char* const m_slot = g_slot + G::kTileBytes;
         // lse2 of this lane's queries perm_acc_row(r, lh): rows 16t + 8h + 0..7, t = 0, 1.
+        // Head dim 256 reads them after the score chain, which holds the most registers.
         f32x4 l2[4];
+        if constexpr (D != 256) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          l2[q4] = *reinterpret_cast<const f32x4*>(m_slot + 4 * (16 * (q4 / 2) + 8 * lh + 4 * (q4 % 2)));
+          for (int q4 = 0; q4 < 4; ++q4)
+            l2[q4] = *reinterpret_cast<const f32x4*>(m_slot + 4 * (16 * (q4 / 2) + 8 * lh + 4 * (q4 % 2)));
+        }
         f32x16 s;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
         __builtin_amdgcn_s_setprio(1);
+        if constexpr (D == 256) {
+          unsigned rb = row_base<D>(lds_address(q_slot), lm, lh);
+          mfma_stream<G::kSteps, 2>([&](int st) { return row_read(pin(rb), st); },
+                                    [&](int st, bf16x8 x) { s = mfma16<F16>(x, kv[st], s); pin_acc(s); });
+        } else {
 #pragma unroll
-        for (int st = 0; st < G::kSteps; ++st) s = mfma16<F16>(row_chunk<D>(q_slot, lm, 2 * st + lh), kv[st], s);
+          for (int st = 0; st < G::kSteps; ++st) s = mfma16<F16>(row_chunk<D>(q_slot, lm, 2 * st + lh), kv[st], s);
+        }
         __builtin_amdgcn_s_setprio(0);
+        // With a hard mask at head dim 256, this lane's bits of the 16 rows' words are
+        // gathered into one register (bit r: row perm_acc_row(r, lh)) before lse2 is read.
+        uint32_t mbits = 0;
+        if constexpr (D == 256 && MASKED) {
+          unsigned wa = lds_address(m_slot + G::kMetaBytes + 4 * G::kRows * kb) + 32u * (unsigned)lh;
+          pin(wa);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const u32x4 w4 =
+                *(__attribute__((address_space(3))) const u32x4*)(size_t)(wa + 4u * (16 * (q4 / 2) + 4 * (q4 % 2)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mbits |= ((w4[e] >> lm) & 1u) << (4 * q4 + e);
+          }
+          asm volatile("" : "+v"(mbits));
+        }
+        if constexpr (D == 256) {
+          unsigned ma = lds_address(m_slot) + 32u * (unsigned)lh;
+          pin(ma);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            l2[q4] = *(__attribute__((address_space(3))) const f32x4*)(size_t)(ma + 4u * (16 * (q4 / 2) + 4 * (q4 % 2)));
+        }
         const bool diag = CAUSAL && (jk + G::kRows - 1 > i0 + delta);
         uint32_t mw[16];  // mask word of query row perm_acc_row(r, lh); bit lm is this lane's key
-        if (MASKED) {
+        if (MASKED && D != 256) {
           const unsigned char* const w_slot = m_slot + G::kMetaBytes + 4 * G::kRows * kb;
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
@@ -443,7 +548,8 @@ __global__ __launch_bounds__(64 * KVGeom<D>::kWaves) void attn_bwd_dkdv_bf16_ker
         }
         if (MASKED) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) t[r] = ((mw[r] >> lm) & 1u) ? t[r] : -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            t[r] = (D == 256 ? (mbits >> r) & 1u : (mw[r] >> lm) & 1u) ? t[r] : -INFINITY;
         }
         f32x4 p32[4];
         bf16x8 pp[2];
@@ -464,7 +570,7 @@ __global__ __launch_bounds__(64 * KVGeom<D>::kWaves) void attn_bwd_dkdv_bf16_ker
       }
     });
   } else {
-    run_steps([&](int32_t T) {
+    run_steps(std::false_type{}, [&](int32_t T) {
       const int32_t qb = qb_first + T - 1;
       if (T >= 1 && reaches(qb)) {
         const unsigned char* const q_slot = lds + ((T - 1) % W::kSlots) * kSlotBytes;
@@ -474,8 +580,14 @@ __global__ __launch_bounds__(64 * KVGeom<D>::kWaves) void attn_bwd_dkdv_bf16_ker
 #pragma unroll
         for (int r = 0; r < 16; ++r) dp[r] = 0.f;
         __builtin_amdgcn_s_setprio(1);
+        if constexpr (D == 256) {
+          unsigned rb = row_base<D>(lds_address(g_slot), lm, lh);
+          mfma_stream<G::kSteps, 2>([&](int st) { return row_read(pin(rb), st); },
+                                    [&](int st, bf16x8 x) { dp = mfma16<F16>(x, kv[st], dp); pin_acc(dp); });
+        } else {
 #pragma unroll
-        for (int st = 0; st < G::kSteps; ++st) dp = mfma16<F16>(row_chunk<D>(g_slot, lm, 2 * st + lh), kv[st], dp);
+          for (int st = 0; st < G::kSteps; ++st) dp = mfma16<F16>(row_chunk<D>(g_slot, lm, 2 * st + lh), kv[st], dp);
+        }
         __builtin_amdgcn_s_setprio(0);
         f32x4 dd[4];
 #pragma unroll
@@ -494,10 +606,21 @@ __global__ __launch_bounds__(64 * KVGeom<D>::kWaves) void attn_bwd_dkdv_bf16_ker
         }
         // dK^T += Q^T dS (the scale is applied once, at the end)
         __builtin_amdgcn_s_setprio(1);
+        if constexpr (D == 256) {
+          unsigned tl = tr_base<D>(lds_address(q_slot), lane, false);
+          unsigned th = tr_base<D>(lds_address(q_slot), lane, true);
+          mfma_stream<2 * G::kNch, 2>(
+              [&](int i) { return tr_read<D>(pin(tl), pin(th), i / G::kNch, i % G::kNch); },
+              [&](int i, bf16x8 x) {
+                acc[i % G::kNch] = mfma16<F16>(x, pds[i / G::kNch], acc[i % G::kNch]);
+                pin_acc(acc[i % G::kNch]);
+              });
+        } else {
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
+          for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-          for (int cb = 0; cb < G::kNch; ++cb) acc[cb] = mfma16<F16>(tr_operand<D>(q_slot, lane, t2, cb), pds[t2], acc[cb]);
+            for (int cb = 0; cb < G::kNch; ++cb) acc[cb] = mfma16<F16>(tr_operand<D>(q_slot, lane, t2, cb), pds[t2], acc[cb]);
+        }
         __builtin_amdgcn_s_setprio(0);
       }
     });
