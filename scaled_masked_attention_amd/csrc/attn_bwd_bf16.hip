@@ -7,8 +7,8 @@
 // accumulation and result).
 //
 // The arithmetic and the three launches (preprocess, dK/dV, dQ) are those of the fp32
-// backward, with workgroups shaped for 16-bit MFMA and two waves per SIMD (the dQ kernel
-// runs one at head dim 256, where its rows' Q, dO and accumulators pass 256 registers):
+// backward, with workgroups shaped for 16-bit MFMA and two waves per SIMD (at head dim
+// 256 the dQ work is split by role between the two waves of a SIMD):
 //   P_ij = 2^(c s_ij - lse2_i), D_i = dO_i . O_i, dP_ij = dO_i . v_j, dS_ij = P_ij (dP_ij - D_i),
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j,
 // with three roundings to the input type (nearest even) for the products: dO once, in
@@ -651,7 +651,8 @@ __global__ __launch_bounds__(64 * KVGeom<D>::kWaves) void attn_bwd_dkdv_bf16_ker
 // step late, so that block stays in the ring a step longer. One barrier per step.
 template <int D>
 struct QGeom {
-  static constexpr int kWaves = D == 256 ? 4 : 8;  // head dim 256: one wave per SIMD
+  static_assert(D <= 128, "head dim 256 runs attn_bwd_dq_bf16_rs_kernel");
+  static constexpr int kWaves = 8;
   static constexpr int kQ = 32 * kWaves;  // queries per workgroup
   static constexpr int kSlots = 4;
   static constexpr int kDma = HGeom<D>::kDmaPerTile;
@@ -767,8 +768,8 @@ __global__ __launch_bounds__(64 * QGeom<D>::kWaves) void attn_bwd_dq_bf16_kernel
   };
   // Waves 4-7 (each sharing a SIMD with wave - 4) run their dQ product of block T at the
   // start of step T + 1, so that the two waves of a SIMD are half a step apart and one's
-  // MFMAs meet the other's softmax (not at head dim 256: one wave per SIMD).
-  const bool late = W::kWaves == 8 && wave >= 4;
+  // MFMAs meet the other's softmax.
+  const bool late = wave >= 4;
   bf16x8 pds_late[2];
   bool pending = false;
   const unsigned char* late_slot = lds;
@@ -845,6 +846,227 @@ __global__ __launch_bounds__(64 * QGeom<D>::kWaves) void attn_bwd_dq_bf16_kernel
                 dq[cb][4 * g4 + 3] * a.scale};
 }
 
+// Head dim 256, where a wave cannot hold its rows' Q and dO (128 registers) beside their
+// dQ accumulators (128) at two waves per SIMD. The work of a 32-row query block is split by
+// role between two waves that share a SIMD, as in the dK/dV kernel:
+//  - the S wave keeps the rows' Q, forms S^T = K Q^T and P = 2^(c S - lse2) for key block
+//    T and leaves P in LDS (fp32, double buffered);
+//  - the dS wave keeps the rows' dO and the dQ accumulators and works on block T - 1: it
+//    forms dP^T = V dO^T, reads that block's P, forms dS = P (dP - D) and accumulates
+//    dQ^T += K^T dS^T.
+// A workgroup owns 128 queries, 4 pairs (wave p and wave p + 4). Key block T's K and V tiles
+// (permuted) and, with a hard mask, the rows' words are copied straight into a ring of
+// three LDS slots one step ahead; the operand reads are streamed two MFMAs ahead at
+// XOR-formed addresses (row_read, tr_read). One barrier per step.
+struct QRGeom {
+  static constexpr int D = 256;
+  static constexpr int kPairs = 4;
+  static constexpr int kWaves = 2 * kPairs;
+  static constexpr int kQ = 32 * kPairs;  // queries per workgroup
+  static constexpr int kSlots = 3;
+  static constexpr int kDma = HGeom<D>::kDmaPerTile;
+  static constexpr int kTileCopies = 2 * kDma;  // K and V of one block
+  static constexpr int kTileCopiesPerWave = kTileCopies / kWaves;
+  static constexpr int kXBytes = 16 * 64 * 4;  // a wave's 16 P values per lane
+  static_assert(kTileCopiesPerWave * kWaves == kTileCopies, "copy split");
+};
+
+template <bool CAUSAL, bool MASKED, bool F16>
+__global__ __launch_bounds__(64 * QRGeom::kWaves) void attn_bwd_dq_bf16_rs_kernel(BwdArgs a) {
+  constexpr int D = QRGeom::D;
+  using G = HGeom<D>;
+  using W = QRGeom;
+  // Slot: K tile, V tile, and with a hard mask the workgroup rows' words of the key block;
+  // every tile on a multiple of 512 bytes (the XOR-formed addresses).
+  constexpr int kMaskBytes = MASKED ? 4 * W::kQ : 0;
+  constexpr int kSlotBytes = (2 * G::kTileBytes + kMaskBytes + 2 * D - 1) / (2 * D) * (2 * D);
+  constexpr int kRingBytes = W::kSlots * kSlotBytes;
+  __shared__ __attribute__((aligned(2 * D))) unsigned char lds[kRingBytes + 2 * W::kPairs * W::kXBytes];
+  unsigned char* const xbuf = lds + kRingBytes;  // [pair][parity][4][64 lanes][4 floats]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool swave = wave < W::kPairs;
+  const int pair = swave ? wave : wave - W::kPairs;
+  const int lm = lane & 31;
+  const int lh = lane >> 5;
+
+  // Workgroups of a head are consecutive, the last queries (the most key blocks under a
+  // causal mask) first.
+  const uint32_t nqw = (uint32_t)(a.nqb + W::kPairs - 1) / W::kPairs;
+  const uint32_t lam = xcd_remap(blockIdx.x, a.nwg);
+  const int64_t bh = (int64_t)(lam / nqw);
+  const int32_t q0 = (int32_t)(nqw - 1 - lam % nqw) * W::kQ;
+  const int32_t qw0 = q0 + 32 * pair;  // the pair's first row
+  const bool pair_live = qw0 < a.seq_q;
+
+  const int32_t my_row = qw0 + lm;
+  const int32_t last_row = min(q0 + W::kQ - 1, a.seq_q - 1);
+  const int32_t nblk = (key_limit<CAUSAL>(last_row, a.seq_q, a.seq_kv, a.seq_kv) + G::kRows - 1) / G::kRows;
+  const int32_t lim = key_limit<CAUSAL>(my_row, a.seq_q, a.seq_kv, a.seq_kv);
+  const int32_t pair_lo = key_limit<CAUSAL>(qw0, a.seq_q, a.seq_kv, a.seq_kv);
+  const int32_t pair_hi = key_limit<CAUSAL>(min(qw0 + 31, a.seq_q - 1), a.seq_q, a.seq_kv, a.seq_kv);
+  // Whether key block T holds a key some row of the pair admits (the same for both waves).
+  auto works = [&](int32_t T) { return pair_live && G::kRows * T < pair_hi; };
+
+  const int64_t q_off = head_offset(bh, a.heads, a.qs_b, a.qs_h);
+  const int64_t kv_off = head_offset(bh, a.heads, a.kvs_b, a.kvs_h);
+  const unsigned kv_row = (unsigned)(a.kvs_s * 2);
+  const unsigned kv_range = strided_range(a.seq_kv, a.kvs_s, D, 2);
+  const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(a.k16 + kv_off, kv_range);
+  const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(a.v16 + kv_off, kv_range);
+  __amdgpu_buffer_rsrc_t w_rsrc;  // rows past seq_q read as 0: nothing admitted
+  if (MASKED)
+    w_rsrc = raw_buffer(a.mask_bits + head_offset(bh, a.heads, a.mbits_sb, a.mbits_sh),
+                        (unsigned)a.seq_q * (unsigned)a.mask_words * 4u);
+
+  // Copies of key block T into its ring slot: the K and V tiles split over the waves; with
+  // a hard mask waves 0 .. kQ/64 - 1 (S waves) add the words of 64 rows each.
+  auto issue = [&](int32_t T, auto sw) {
+    constexpr bool kS = decltype(sw)::value;
+    unsigned char* const slot = lds + (T % W::kSlots) * kSlotBytes;
+    const unsigned row0 = (unsigned)(G::kRows * T) * kv_row;
+#pragma unroll
+    for (int u = 0; u < W::kTileCopiesPerWave; ++u) {
+      const int c = u * W::kWaves + wave;  // K copies, then V copies
+      if (c < W::kDma)
+        dma_load_x4(k_rsrc, row0 + tile_src<D, true>(c, lane, kv_row), lds_address(slot + 1024 * c));
+      else
+        dma_load_x4(v_rsrc, row0 + tile_src<D, true>(c - W::kDma, lane, kv_row), lds_address(slot + 1024 * c));
+    }
+    if (MASKED && kS && wave < W::kQ / 64)
+      dma_load_x1(w_rsrc, ((unsigned)(q0 + 64 * wave + lane) * (unsigned)a.mask_words + (unsigned)T) * 4u,
+                  lds_address(slot + 2 * G::kTileBytes + 256 * wave));
+  };
+  static_assert(W::kQ / 64 <= W::kPairs, "the mask copies come from S waves");
+
+  // The step loop, run by every wave with its role's work (one copy per role, so that its
+  // registers stay put): block T lands, one barrier, block T + 1 is issued.
+  auto run_steps = [&](auto sw, auto&& work) {
+    if (nblk > 0) issue(0, sw);
+    for (int32_t T = 0; T <= nblk; ++T) {
+      wait_vmcnt<0>();
+      __syncthreads();  // block T has landed; step T - 1 is done with block T - 2's slot and its P
+      if (T + 1 < nblk) issue(T + 1, sw);
+      work(T);
+    }
+  };
+
+  // This pair's rows: lane (query m, h) holds head dims 16*st + 8*h .. + 7 of row qw0 + m
+  // (zeros past seq_q) of Q (S wave) or dO (dS wave), as the B operands of the score
+  // products; lse2 or D of row qw0 + m (the preprocess pads past seq_q).
+  bf16x8 rows[G::kSteps];
+  float my_meta = swave ? INFINITY : 0.f;
+  {
+    const bool row_ok = my_row < a.seq_q;
+    if (pair_live) {
+      const float* const meta = a.meta + ((size_t)bh * a.nqb + qw0 / G::kRows) * kBwdMetaFloats;
+      my_meta = meta[(swave ? 0 : G::kRows) + lm];
+    }
+    const unsigned short* const src =
+        swave ? a.q16 + q_off + (int64_t)(row_ok ? my_row : 0) * a.qs_s
+              : a.dout16 + ((size_t)bh * a.seq_q + (row_ok ? my_row : 0)) * D;
+#pragma unroll
+    for (int st = 0; st < G::kSteps; ++st) {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      const u32x4 x = row_ok ? *reinterpret_cast<const u32x4*>(src + 16 * st + 8 * lh) : zero;
+      rows[st] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  if (swave) {
+    run_steps(std::true_type{}, [&](int32_t T) {
+      if (!works(T)) return;
+      const int32_t j0 = G::kRows * T;
+      const unsigned char* const k_slot = lds + (T % W::kSlots) * kSlotBytes;
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+      __builtin_amdgcn_s_setprio(1);
+      unsigned rb = row_base<D>(lds_address(k_slot), lm, lh);
+      mfma_stream<G::kSteps, 2>([&](int st) { return row_read(pin(rb), st); },
+                                [&](int st, bf16x8 x) { s = mfma16<F16>(x, rows[st], s); pin_acc(s); });
+      __builtin_amdgcn_s_setprio(0);
+      float t[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[r] = s[r] * a.c - my_meta;
+      if (j0 + G::kRows > pair_lo) {  // some key of the block lies past the first row's limit
+        // Key j0 + perm_acc_row(r, lh) is admitted iff 16 (r / 8) + r % 8 < rel (the empty
+        // asm keeps the comparisons inside this branch).
+        int32_t rel = lim - j0 - 8 * lh;
+        asm volatile("" : "+v"(rel));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[r] = 16 * (r / 8) + r % 8 < rel ? t[r] : -INFINITY;
+      }
+      if (MASKED) {
+        const uint32_t mw = *reinterpret_cast<const uint32_t*>(k_slot + 2 * G::kTileBytes + 4 * (32 * pair + lm));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[r] = ((mw >> perm_acc_row(r, lh)) & 1u) ? t[r] : -INFINITY;
+      }
+      unsigned char* const xp = xbuf + (2 * pair + (T & 1)) * W::kXBytes + 16 * lane;
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4)
+        *reinterpret_cast<f32x4*>(xp + 1024 * c4) =
+            f32x4{__builtin_amdgcn_exp2f(t[4 * c4]), __builtin_amdgcn_exp2f(t[4 * c4 + 1]),
+                  __builtin_amdgcn_exp2f(t[4 * c4 + 2]), __builtin_amdgcn_exp2f(t[4 * c4 + 3])};
+    });
+    return;  // the dS wave of the pair writes its dQ
+  }
+
+  f32x16 dq[G::kNch];
+#pragma unroll
+  for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[cb][r] = 0.f;
+  run_steps(std::false_type{}, [&](int32_t T) {
+    if (T < 1 || !works(T - 1)) return;
+    const unsigned char* const k_slot = lds + ((T - 1) % W::kSlots) * kSlotBytes;
+    const unsigned char* const v_slot = k_slot + G::kTileBytes;
+    f32x16 dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+    __builtin_amdgcn_s_setprio(1);
+    unsigned rb = row_base<D>(lds_address(v_slot), lm, lh);
+    mfma_stream<G::kSteps, 2>([&](int st) { return row_read(pin(rb), st); },
+                              [&](int st, bf16x8 x) { dp = mfma16<F16>(x, rows[st], dp); pin_acc(dp); });
+    __builtin_amdgcn_s_setprio(0);
+    const unsigned char* const xp = xbuf + (2 * pair + ((T - 1) & 1)) * W::kXBytes + 16 * lane;
+    bf16x8 pds[2];
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const f32x4 p4 = *reinterpret_cast<const f32x4*>(xp + 1024 * c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * c4 + e;
+        pds[r / 8][r % 8] = round16<F16>(p4[e] * (dp[r] - my_meta));
+      }
+    }
+    // dQ^T += K^T dS^T (the scale is applied once, at the end)
+    __builtin_amdgcn_s_setprio(1);
+    unsigned tl = tr_base<D>(lds_address(k_slot), lane, false);
+    unsigned th = tr_base<D>(lds_address(k_slot), lane, true);
+    mfma_stream<2 * G::kNch, 2>(
+        [&](int i) { return tr_read<D>(pin(tl), pin(th), i / G::kNch, i % G::kNch); },
+        [&](int i, bf16x8 x) {
+          dq[i % G::kNch] = mfma16<F16>(x, pds[i / G::kNch], dq[i % G::kNch]);
+          pin_acc(dq[i % G::kNch]);
+        });
+    __builtin_amdgcn_s_setprio(0);
+  });
+
+  // Lane (query m, h) holds head dims 32*cb + 8*g4 + 4*h .. + 3 of row qw0 + m.
+  if (!pair_live || my_row >= a.seq_q) return;
+  float* const out = a.dq + q_off + (int64_t)my_row * a.qs_s;
+#pragma unroll
+  for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+      *reinterpret_cast<f32x4*>(out + 32 * cb + 8 * g4 + 4 * lh) =
+          f32x4{dq[cb][4 * g4] * a.scale, dq[cb][4 * g4 + 1] * a.scale, dq[cb][4 * g4 + 2] * a.scale,
+                dq[cb][4 * g4 + 3] * a.scale};
+}
+
 template <int D, bool CAUSAL, bool MASKED, bool F16>
 hipError_t launch_bwd_bf16_variant(const BwdArgs& a0, hipStream_t s, hipEvent_t ev_pre,
                                    hipEvent_t ev_dkdv) {
@@ -863,9 +1085,15 @@ hipError_t launch_bwd_bf16_variant(const BwdArgs& a0, hipStream_t s, hipEvent_t 
   }
   if (ev_dkdv && hipEventRecord(ev_dkdv, s) != hipSuccess) return hipErrorInvalidValue;
   if (nq > 0) {
-    a.nwg = (uint32_t)(a.bh * ((a.nqb + QGeom<D>::kWaves - 1) / QGeom<D>::kWaves));
-    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, CAUSAL, MASKED, F16>), dim3(a.nwg),
-                       dim3(64 * QGeom<D>::kWaves), 0, s, a);
+    if constexpr (D == 256) {
+      a.nwg = (uint32_t)(a.bh * ((a.nqb + QRGeom::kPairs - 1) / QRGeom::kPairs));
+      hipLaunchKernelGGL((attn_bwd_dq_bf16_rs_kernel<CAUSAL, MASKED, F16>), dim3(a.nwg),
+                         dim3(64 * QRGeom::kWaves), 0, s, a);
+    } else {
+      a.nwg = (uint32_t)(a.bh * ((a.nqb + QGeom<D>::kWaves - 1) / QGeom<D>::kWaves));
+      hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, CAUSAL, MASKED, F16>), dim3(a.nwg),
+                         dim3(64 * QGeom<D>::kWaves), 0, s, a);
+    }
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   return hipSuccess;
