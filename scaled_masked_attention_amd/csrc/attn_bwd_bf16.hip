@@ -820,8 +820,13 @@ __global__ __launch_bounds__(64 * QGeom<D>::kWaves) void attn_bwd_dq_bf16_kernel
     bf16x8 pds[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+      // dS in fp32, then rounded to the input type. For fp16 the compiler would otherwise
+      // round the exact product once (v_fma_mixlo_f16), which now and then differs from the
+      // dS that the dK/dV kernel rounds: the empty asm keeps the fp32 product.
       const float p = __builtin_amdgcn_exp2f(t[r]);
-      pds[r / 8][r % 8] = round16<F16>(p * (dp[r] - my_d));
+      float ds = p * (dp[r] - my_d);
+      if constexpr (F16) asm("" : "+v"(ds));
+      pds[r / 8][r % 8] = round16<F16>(ds);
     }
     if (late) {
       pds_late[0] = pds[0];
