@@ -68,6 +68,8 @@ KERNEL_FUNCTIONS = {0: "attn_fwd_f32_kernel", 1: "attn_fwd_f32_wsplit_kernel", 2
 def kernel_function(plan_kernel: int, head_dim: int) -> str:
     if plan_kernel == 2 and head_dim == 256:
         return "attn_fwd_bf16_rs_kernel"
+    if plan_kernel == 2 and head_dim == 128:
+        return "attn_fwd_bf16_rb2_kernel"
     return KERNEL_FUNCTIONS[plan_kernel]
 
 
@@ -307,6 +309,7 @@ KERNEL_SOURCES = {"attn_fwd_f32_kernel": ["attn_fwd_f32.hip", "attn_common.h"],
                   "attn_fwd_f32_wsplit_kernel": ["attn_fwd_f32_wsplit.hip", "attn_common.h"],
                   "attn_fwd_bf16_kernel": ["attn_fwd_bf16.hip", "attn_common.h"],
                   "attn_fwd_bf16_rs_kernel": ["attn_fwd_bf16.hip", "attn_common.h"],
+                  "attn_fwd_bf16_rb2_kernel": ["attn_fwd_bf16.hip", "attn_common.h"],
                   "row_softmax": ["row_softmax.hip"]}
 
 

@@ -89,9 +89,9 @@ typedef enum {
   SMA_KERNEL_F32_KSPLIT = 1,    /* fp32: 32 query rows per workgroup, keys split over its four
                                    waves and merged in-workgroup; never needs a workspace (the
                                    automatic fp32 choice unless its grid is small and rows long) */
-  SMA_KERNEL_BF16_QBLOCK = 2    /* bf16 or fp16: 256 query rows per workgroup (192 at head dim
-                                   256); keys optionally split across workgroups, merged by a
-                                   second kernel */
+  SMA_KERNEL_BF16_QBLOCK = 2    /* bf16 or fp16: 256 query rows per workgroup (512 at head dim
+                                   128, 192 at 256); keys optionally split across workgroups,
+                                   merged by a second kernel */
 } sma_kernel;
 
 /* How a call is carried out: filled by sma_attention_fwd_plan, read by

@@ -9,11 +9,13 @@
 // F16). The probabilities are rounded to the input's 16-bit type (nearest
 // even) for the P V product; the row sums use the fp32 probabilities.
 //
-// Head dims 32-128: 8 waves x 32 query rows = 256 rows, two waves per SIMD. Key
+// Head dims 32 and 64: 8 waves x 32 query rows = 256 rows, two waves per SIMD. Key
 // tiles of 64 rows go HBM/L2 -> LDS through buffer-resource direct-to-LDS loads
 // into a ring of four slots, two tiles ahead of their use, without passing
-// through registers; loads past the last key return zeros. Head dim 256 runs
-// the role-split kernel further down (attn_fwd_bf16_rs_kernel).
+// through registers; loads past the last key return zeros. Head dim 128 runs the
+// same scheme with two 32-row blocks per wave (512 rows, 32-key tiles) so that each
+// operand read from LDS feeds two MFMAs (attn_fwd_bf16_rb2_kernel), and head dim
+// 256 the role-split kernel (attn_fwd_bf16_rs_kernel), both further down.
 //
 // S^T = K Q^T: lane (m, h) supplies K[key m] and Q[query m] at head dims
 // h*D/2 + 8*step .. + 7 and receives the scores of query (lane % 32). K rows
@@ -69,7 +71,7 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 // waves 0-3 copy K, waves 4-7 copy V.
 template <int D>
 struct BGeom {
-  static_assert(D == 32 || D == 64 || D == 128, "the 8-wave kernel's head dims");
+  static_assert(D == 32 || D == 64, "the 32-row kernel's head dims (128: attn_fwd_bf16_rb2_kernel)");
   static constexpr int kWaves = 8;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kQW = 32;                     // query rows per wave
@@ -836,6 +838,378 @@ hipError_t launch_bf16_rs(const FwdArgs& a, bool f16, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- two row blocks per wave
+// Head dim 128: each wave owns 64 query rows as two 32-row blocks,
+// so that every K operand of the score product and every V^T operand of the P V product
+// read from LDS feeds two MFMAs (one per row block) instead of one. 8 waves x 64 rows =
+// 512 rows per workgroup, two waves per SIMD; key tiles of 32 rows (a wave's two score
+// blocks then take 32 registers) in a ring of four LDS slots, two tiles ahead. LDS
+// addresses are formed inside the step from one base register and an XOR constant (the
+// swizzles only flip bits 4..7 of a row's byte offset), and the operand reads are
+// streamed ahead of their MFMAs, pinned there by empty asm.
+struct B2Geom {
+  static constexpr int D = 128;
+  static_assert(kBF16D128QueriesPerWG == 8 * 64 && kBF16D128KeysPerTile == 32, "planner geometry");
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRB = 2;                      // 32-row blocks per wave
+  static constexpr int kQW = 32 * kRB;               // query rows per wave
+  static constexpr int kQ = kWaves * kQW;            // query rows per workgroup
+  static constexpr int kK = 32;                      // keys per tile
+  static constexpr int kSlots = 4;
+  static constexpr int kChunksPerRow = D / 8;        // 16
+  static constexpr int kTileChunks = kK * kChunksPerRow;  // 512: one per thread and tensor
+  static constexpr int kTileBytes = 16 * kTileChunks;
+  static constexpr int kHalf = D / 2;
+  static constexpr int kSteps = D / 16;              // 8
+  static constexpr int kNch = D / 32;                // 4
+  static_assert(kTileChunks == kThreads, "one K and one V chunk per thread and tile");
+};
+
+__device__ __forceinline__ unsigned pin_u(unsigned& x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ void pin_f16x(f32x16& c) { asm volatile("" : "+v"(c)); }
+
+template <bool CAUSAL, bool F16, bool MASKED>
+__global__ __launch_bounds__(B2Geom::kThreads) void attn_fwd_bf16_rb2_kernel(FwdArgs a) {
+  using G = B2Geom;
+  constexpr int D = G::D;
+  using H = Half<F16>;
+  using V8 = typename H::V8;
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds[G::kSlots][G::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds[G::kSlots][G::kTileBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lm = lane & 31;
+  const int lh = lane >> 5;
+
+  const TileId t = decode_tile(blockIdx.x, a);
+  const int32_t q0 = t.qb * G::kQ;
+  const int32_t qw0 = q0 + wave * G::kQW;
+  const int32_t ks = t.split * a.split_len;
+  const int32_t split_end = min(a.seq_kv, ks + a.split_len);
+  const int32_t wg_last_row = min(q0 + G::kQ - 1, a.seq_q - 1);
+  const int32_t ke = key_limit<CAUSAL>(wg_last_row, a.seq_q, a.seq_kv, split_end);
+  const int32_t ntiles = ke > ks ? (ke - ks + G::kK - 1) / G::kK : 0;
+
+  const bool wave_live = qw0 < a.seq_q;
+  const int32_t wave_hi = key_limit<CAUSAL>(min(qw0 + G::kQW - 1, a.seq_q - 1), a.seq_q, a.seq_kv, split_end);
+  int32_t rb_lo[G::kRB], lim[G::kRB];
+#pragma unroll
+  for (int rb = 0; rb < G::kRB; ++rb) {
+    rb_lo[rb] = key_limit<CAUSAL>(min(qw0 + 32 * rb, a.seq_q - 1), a.seq_q, a.seq_kv, split_end);
+    lim[rb] = key_limit<CAUSAL>(qw0 + 32 * rb + lm, a.seq_q, a.seq_kv, split_end);
+  }
+
+  // A hard mask, packed by columns (MaskColArgs) as for the 32-row kernel: each row block
+  // has one row-bit word per key and a class per 64-key tile (0 nothing admitted, 1
+  // everything, 2 mixed), read with scalar loads. A row block past the last query row
+  // reads nothing and counts as closed.
+  const uint32_t* mcols[G::kRB] = {};
+  const uint32_t* mcls[G::kRB] = {};
+  if (MASKED) {
+#pragma unroll
+    for (int rb = 0; rb < G::kRB; ++rb) {
+      const int64_t blk = qw0 / 32 + rb;
+      mcols[rb] = a.mask_bits + head_offset(t.bh, a.heads, a.mbits_sb, a.mbits_sh) + blk * a.mask_words;
+      mcls[rb] = a.mask_cls + head_offset(t.bh, a.heads, a.mcls_sb, a.mcls_sh) + blk * a.mask_tiles;
+    }
+  }
+
+  // Q operands of both row blocks in registers for the whole pass.
+  V8 qr[G::kRB][G::kSteps];
+  {
+    const unsigned flip = a.negate_q ? 0x80008000u : 0u;
+#pragma unroll
+    for (int rb = 0; rb < G::kRB; ++rb) {
+      const unsigned short* qp = static_cast<const unsigned short*>(a.q) +
+                                 head_offset(t.bh, a.heads, a.qs_b, a.qs_h) +
+                                 (int64_t)min(qw0 + 32 * rb + lm, a.seq_q - 1) * a.qs_s + lh * G::kHalf;
+#pragma unroll
+      for (int st = 0; st < G::kSteps; ++st) {
+        u32x4 x = *reinterpret_cast<const u32x4*>(qp + 8 * st);
+        x ^= flip;
+        qr[rb][st] = __builtin_bit_cast(V8, x);
+      }
+    }
+  }
+  wait_vmcnt<0>();
+
+  const unsigned kv_bytes = strided_range(a.seq_kv, a.kvs_s, D, 2);
+  const unsigned kv_row = (unsigned)(a.kvs_s * 2);
+  const int64_t kv_off = head_offset(t.bh, a.heads, a.kvs_b, a.kvs_h);
+  const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(static_cast<const unsigned short*>(a.k) + kv_off, kv_bytes);
+  const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(static_cast<const unsigned short*>(a.v) + kv_off, kv_bytes);
+  // Thread (wave, lane) fills LDS chunk p = 64 wave + lane of each tile: row rho = p / 16,
+  // position pc = p % 16, holding logical chunk pc ^ swizzle of the (permuted) row.
+  // The lane's offsets are formed again at each copy from an opaque lane index, rather
+  // than held in registers across the step loop.
+  auto issue_tile = [&](int32_t T) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int rho = (64 * wave + ln) / G::kChunksPerRow;
+    const int pc = ln % G::kChunksPerRow;
+    const unsigned tile_ofs = (unsigned)(ks + T * G::kK) * kv_row;
+    const int slot = T % G::kSlots;
+    dma_load_x4(k_rsrc, (unsigned)swap_bits_2_3(rho) * kv_row + 16u * (unsigned)(pc ^ k_swz<D>(rho)) + tile_ofs,
+                lds_address(&k_lds[slot][1024 * wave]));
+    dma_load_x4(v_rsrc, (unsigned)rho * kv_row + 16u * (unsigned)(pc ^ v_swz<D>(rho)) + tile_ofs,
+                lds_address(&v_lds[slot][1024 * wave]));
+  };
+
+  f32x16 oacc[G::kRB][G::kNch];
+#pragma unroll
+  for (int rb = 0; rb < G::kRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[rb][cb][r] = 0.f;
+  float m_run[G::kRB], l_run[G::kRB];
+#pragma unroll
+  for (int rb = 0; rb < G::kRB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+  }
+  const float c = fmaxf(a.c, 1.17549435e-38f);
+
+  // Lane parts of the LDS addresses (tile bases are multiples of 1 KB):
+  //  - K row read, logical chunk lh*8 + st of row lm: position (lh*8 + st) ^ (lm & 15), so
+  //    the byte offset is k_lane ^ 16 st;
+  //  - V^T transposing read of k-step t2 and output chunk cb: rows 16 t2 + 8 lh + s/4 (and
+  //    + 4), chunk 4 cb + colq, swizzled by 4 (s/4); the byte offset is
+  //    (v_lane ^ 64 cb) + 4096 t2 (+ 1024 for the second row).
+  const int srole = lane & 15;
+  const int colq = 2 * ((lane >> 4) & 1) + ((srole & 3) >> 1);
+  const unsigned k_lane = (unsigned)(lm * 2 * D + 16 * (8 * lh ^ (lm & 15)));
+  const unsigned v_lane = (unsigned)((8 * lh + srole / 4) * 2 * D + 64 * (srole / 4) + 16 * colq + 8 * (srole & 1));
+
+  // O^T += V^T P^T for both row blocks: each V^T operand feeds two MFMAs.
+  auto pv_tile = [&](int slot, const V8 (&pb)[G::kRB][2]) {
+    unsigned vb = lds_address(&v_lds[slot][0]) + v_lane;
+    auto v_operand = [&](int i) {  // i = 4 t2 + cb
+      const int t2 = i / G::kNch, cb = i % G::kNch;
+      const unsigned x = (pin_u(vb) ^ (64u * (unsigned)cb)) + 4096u * (unsigned)t2;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(size_t)x);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(size_t)(x + 1024u));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+      return __builtin_bit_cast(V8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+    };
+    constexpr int kN = 2 * G::kNch;  // V^T operands per tile
+    constexpr int kPf = 2;
+    V8 vop[kPf + 1];
+#pragma unroll
+    for (int i = 0; i < kPf; ++i) vop[i] = v_operand(i);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      if (i + kPf < kN) vop[(i + kPf) % (kPf + 1)] = v_operand(i + kPf);
+      __builtin_amdgcn_sched_barrier(0);
+      const int t2 = i / G::kNch, cb = i % G::kNch;
+#pragma unroll
+      for (int rb = 0; rb < G::kRB; ++rb) {
+        oacc[rb][cb] = H::mfma(vop[i % (kPf + 1)], pb[rb][t2], oacc[rb][cb]);
+        pin_f16x(oacc[rb][cb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Scores of both row blocks, lazy running max and probabilities of tile T.
+  auto scores_and_p = [&](int32_t T, int slot, V8 (&pb)[G::kRB][2], const uint32_t (&cls)[G::kRB]) {
+    const int32_t j0 = ks + T * G::kK;
+    f32x16 sacc[G::kRB];
+#pragma unroll
+    for (int rb = 0; rb < G::kRB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
+    unsigned kb = lds_address(&k_lds[slot][0]) + k_lane;
+    auto k_operand = [&](int st) {
+      const unsigned x = pin_u(kb) ^ (16u * (unsigned)st);
+      return __builtin_bit_cast(V8, *(__attribute__((address_space(3))) const u32x4*)(size_t)x);
+    };
+    constexpr int kPf = 2;
+    V8 kop[kPf + 1];
+#pragma unroll
+    for (int st = 0; st < kPf; ++st) kop[st] = k_operand(st);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int st = 0; st < G::kSteps; ++st) {
+      if (st + kPf < G::kSteps) kop[(st + kPf) % (kPf + 1)] = k_operand(st + kPf);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < G::kRB; ++rb) {
+        sacc[rb] = H::mfma(kop[st % (kPf + 1)], qr[rb][st], sacc[rb]);
+        pin_f16x(sacc[rb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+
+#pragma unroll
+    for (int rb = 0; rb < G::kRB; ++rb) {
+      if (j0 + G::kK > rb_lo[rb]) {
+        int32_t rel = lim[rb] - j0 - 8 * lh;  // key 16(r/8) + r%8 (+ 8 lh) allowed iff < rel
+        asm volatile("" : "+v"(rel));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[rb][r] = (16 * (r / 8) + (r % 8) < rel) ? sacc[rb][r] : -INFINITY;
+      }
+      if (MASKED && cls[rb] != 1u) {
+        // Score register r holds key 16(r/8) + r%8 (lanes 0-31) and that key + 8 (lanes
+        // 32-63); their two column words, stored side by side, are its lane mask. A row
+        // block the tile closes (class 0, while the other one is open) takes zero words.
+        const float ninf = -INFINITY;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          typedef unsigned u32x16 __attribute__((ext_vector_type(16)));
+          u32x16 w = {};
+          if (cls[rb] == 2u) w = scalar_load<u32x16>(mcols[rb] + (j0 + 16 * g));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint64_t lanes = (uint64_t)w[2 * i] | ((uint64_t)w[2 * i + 1] << 32);
+            float x = sacc[rb][8 * g + i];
+            asm("v_cndmask_b32_e64 %0, %1, %0, %2" : "+v"(x) : "v"(ninf), "s"(lanes));
+            sacc[rb][8 * g + i] = x;
+          }
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[rb][r]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float tmax = mx == -INFINITY ? -INFINITY : mx * c;
+      if (__any(tmax > m_run[rb] + kTau)) {
+        const float m_new = fmaxf(m_run[rb], tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - (m_new == -INFINITY ? 0.f : m_new));
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[rb][cb][r] *= alpha;
+        m_run[rb] = m_new;
+      }
+      const float neg_m = m_run[rb] == -INFINITY ? 0.f : -m_run[rb];
+      float psum = 0.f;
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][8 * t2 + e], c, neg_m));
+          psum += p;
+          pb[rb][t2][e] = (typename H::E)p;
+        }
+      l_run[rb] += psum;
+    }
+  };
+
+  // Waves 4-7 (each sharing a SIMD with wave - 4) run a tile's P V product at the start of
+  // the next step. Each role has its own copy of the step loop, so that the late waves'
+  // held probabilities are not live across the other role's score chain.
+  auto run_steps = [&](auto late_c) {
+    constexpr bool kLate = decltype(late_c)::value;
+    V8 pb_late[G::kRB][2];
+    bool late_pending = false;
+    int late_slot = 0;
+    if (ntiles > 0) issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    for (int32_t T = 0; T < ntiles; ++T) {
+      if (T + 1 < ntiles) wait_vmcnt<2>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (T + 2 < ntiles) issue_tile(T + 2);
+      if (kLate && late_pending) {
+        pv_tile(late_slot, pb_late);
+        late_pending = false;
+      }
+      const int slot = T % G::kSlots;
+      const int32_t j0 = ks + T * G::kK;
+      // The tile's mask class per row block (1 without a mask); a tile the mask closes for
+      // both is skipped.
+      uint32_t cls[G::kRB] = {1u, 1u};
+      bool open = true;
+      if (MASKED && wave_live && j0 < wave_hi) {
+#pragma unroll
+        for (int rb = 0; rb < G::kRB; ++rb)
+          cls[rb] = qw0 + 32 * rb < a.seq_q ? scalar_load<uint32_t>(mcls[rb] + j0 / 64) : 0u;
+        open = (cls[0] | cls[1]) != 0u;
+      }
+      if (wave_live && j0 < wave_hi && open) {
+        V8 pb[G::kRB][2];
+        scores_and_p(T, slot, pb, cls);
+        if constexpr (kLate) {
+#pragma unroll
+          for (int rb = 0; rb < G::kRB; ++rb)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) pb_late[rb][t2] = pb[rb][t2];
+          late_pending = true;
+          late_slot = slot;
+        } else {
+          pv_tile(slot, pb);
+        }
+      }
+    }
+    if (kLate && late_pending) pv_tile(late_slot, pb_late);
+  };
+  if (wave >= G::kWaves / 2) run_steps(std::true_type{});
+  else run_steps(std::false_type{});
+
+#pragma unroll
+  for (int rb = 0; rb < G::kRB; ++rb) {
+    const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32);
+    const int32_t row = qw0 + 32 * rb + lm;
+    if (!wave_live || row >= a.seq_q) continue;
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : 1.0f / l_tot;
+    const float lse2 = empty ? -INFINITY : m_run[rb] + __builtin_amdgcn_logf(l_tot);
+    const size_t row_id = (size_t)t.bh * a.seq_q + row;
+    float* orow = nullptr;
+    unsigned short* orow16 = nullptr;
+    if (a.nsplit == 1) {
+      const int64_t o_off = head_offset(t.bh, a.heads, a.qs_b, a.qs_h) + (int64_t)row * a.qs_s;
+      if (a.o_bf16) orow16 = a.o_bf16 + o_off;
+      else orow = a.o + o_off;
+      if (a.lse && lh == 0) a.lse[row_id] = empty ? -INFINITY : lse2 * 0.69314718055994530942f;
+    } else {
+      const size_t prow = (size_t)t.split * ((size_t)a.bh * a.seq_q) + row_id;
+      orow = a.part_o + prow * D;
+      if (lh == 0) a.part_lse[prow] = lse2;
+    }
+#pragma unroll
+    for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = empty ? 0.f : oacc[rb][cb][4 * g4 + e] * inv;
+        if (orow16)
+          *reinterpret_cast<u32x2*>(orow16 + 32 * cb + 8 * g4 + 4 * lh) =
+              u32x2{pack_out16(out[0], out[1], a.o_f16), pack_out16(out[2], out[3], a.o_f16)};
+        else
+          *reinterpret_cast<f32x4*>(orow + 32 * cb + 8 * g4 + 4 * lh) = out;
+      }
+  }
+}
+
+template <bool CAUSAL>
+hipError_t launch_bf16_rb2(const FwdArgs& a, bool f16, hipStream_t s) {
+  const dim3 grid(a.nwg), block(B2Geom::kThreads);
+  if (a.mask_bits) {
+    if (f16) hipLaunchKernelGGL((attn_fwd_bf16_rb2_kernel<CAUSAL, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16_rb2_kernel<CAUSAL, false, true>), grid, block, 0, s, a);
+  } else {
+    if (f16) hipLaunchKernelGGL((attn_fwd_bf16_rb2_kernel<CAUSAL, true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16_rb2_kernel<CAUSAL, false, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bf16_variant(const FwdArgs& a, bool f16, hipStream_t s) {
   const dim3 grid(a.nwg), block(BGeom<D>::kThreads);
@@ -855,7 +1229,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, bool causal, bool f16
   switch (head_dim) {
     case 32: return causal ? launch_bf16_variant<32, true>(a, f16, s) : launch_bf16_variant<32, false>(a, f16, s);
     case 64: return causal ? launch_bf16_variant<64, true>(a, f16, s) : launch_bf16_variant<64, false>(a, f16, s);
-    case 128: return causal ? launch_bf16_variant<128, true>(a, f16, s) : launch_bf16_variant<128, false>(a, f16, s);
+    case 128: return causal ? launch_bf16_rb2<true>(a, f16, s) : launch_bf16_rb2<false>(a, f16, s);
     case 256: return causal ? launch_bf16_rs<true>(a, f16, s) : launch_bf16_rs<false>(a, f16, s);
     default: return hipErrorInvalidValue;
   }

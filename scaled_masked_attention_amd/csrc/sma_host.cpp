@@ -89,12 +89,14 @@ struct Plan {
 int queries_per_wg(int kernel, size_t d) {
   switch (kernel) {
     case SMA_KERNEL_F32_KSPLIT: return sma::kF32WsplitQueriesPerWG;
-    case SMA_KERNEL_BF16_QBLOCK: return d == 256 ? sma::kBF16D256QueriesPerWG : sma::kBF16QueriesPerWG;
+    case SMA_KERNEL_BF16_QBLOCK:
+      return d == 256 ? sma::kBF16D256QueriesPerWG : d == 128 ? sma::kBF16D128QueriesPerWG : sma::kBF16QueriesPerWG;
     default: return sma::kF32QueriesPerWG;
   }
 }
 int keys_per_tile(int kernel, size_t d) {
-  if (kernel == SMA_KERNEL_BF16_QBLOCK) return d == 256 ? sma::kBF16D256KeysPerTile : sma::kBF16KeysPerTile;
+  if (kernel == SMA_KERNEL_BF16_QBLOCK)
+    return d == 256 ? sma::kBF16D256KeysPerTile : d == 128 ? sma::kBF16D128KeysPerTile : sma::kBF16KeysPerTile;
   return sma::kF32KeysPerTile;
 }
 bool kernel_fits_dtype(int kernel, int in_dtype) {

@@ -136,6 +136,9 @@ constexpr int kF32KeysPerTile = 32;
 constexpr int kF32WsplitQueriesPerWG = 32;  // in-workgroup key-split kernel
 constexpr int kBF16QueriesPerWG = 256;
 constexpr int kBF16KeysPerTile = 64;
+// The 16-bit kernel at head dim 128 (two 32-row blocks per wave, 32-key tiles).
+constexpr int kBF16D128QueriesPerWG = 512;
+constexpr int kBF16D128KeysPerTile = 32;
 // The 16-bit kernel at head dim 256 (the role-split kernel: 6 pairs of 32 rows, 32-key tiles).
 constexpr int kBF16D256QueriesPerWG = 192;
 constexpr int kBF16D256KeysPerTile = 32;

@@ -187,10 +187,10 @@ def test_plan_auto_choices():
     p = P(F32, 1, 4, 200, 3000, 128, False, num_cus=256)  # few 32-row blocks, long rows
     assert p.kernel == sma.SMA_KERNEL_F32_QBLOCK and p.nsplit > 1
     assert p.workspace_bytes == sma.workspace_bytes(F32, 1, 4, 200, 3000, 128, False, 256)
-    p = P(BF16, 1, 32, 16384, 16384, 128, True, num_cus=256)
-    assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_BF16_QBLOCK, 1, 32 * 64)
+    p = P(BF16, 1, 32, 16384, 16384, 128, True, num_cus=256)  # 512-row workgroups at d = 128
+    assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_BF16_QBLOCK, 1, 32 * 32)
     p = P(F16, 1, 32, 16384, 16384, 128, True, num_cus=256)
-    assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_BF16_QBLOCK, 1, 32 * 64)
+    assert (p.kernel, p.nsplit, p.workgroups) == (sma.SMA_KERNEL_BF16_QBLOCK, 1, 32 * 32)
     p = P(F32, 1, 1, 1, 4096, 64, False, num_cus=256)  # one query row, many keys
     assert p.kernel == sma.SMA_KERNEL_F32_QBLOCK and p.nsplit == 32
     # head dim 32 follows the 64/128 rule; 256 goes to the 128-row fp32 kernel, where one
@@ -255,10 +255,16 @@ def test_plan_rejects():
     for d in (32, 256):
         assert P(F32, 1, 1, 8, 8, d, False, kernel=sma.SMA_KERNEL_F32_QBLOCK, nsplit=1).nsplit == 1
         assert P(BF16, 1, 1, 8, 8, d, False, kernel=sma.SMA_KERNEL_BF16_QBLOCK, nsplit=1).nsplit == 1
-    # the 16-bit kernel's geometry: 256 rows and 64-key tiles, 192 rows and 32-key tiles at d = 256
+    # the 16-bit kernels' geometry: 256 rows and 64-key tiles at d = 32 and 64, 512 rows and
+    # 32-key tiles at d = 128, 192 rows and 32-key tiles at d = 256
     K16 = sma.SMA_KERNEL_BF16_QBLOCK
     assert P(BF16, 1, 4, 1000, 1000, 32, True, kernel=K16, nsplit=1).workgroups == 4 * 4
+    assert P(BF16, 1, 4, 1000, 1000, 64, True, kernel=K16, nsplit=1).workgroups == 4 * 4
+    assert P(BF16, 1, 4, 1000, 1000, 128, True, kernel=K16, nsplit=1).workgroups == 4 * 2
     assert P(BF16, 1, 4, 1000, 1000, 256, True, kernel=K16, nsplit=1).workgroups == 4 * 6
+    # a forced split at d = 128 rounds its key range to the 32-key tile
+    p = P(BF16, 1, 1, 512, 1000, 128, False, kernel=K16, nsplit=3)
+    assert p.nsplit == 3 and p.workgroups == 3
     p = P(F16, 1, 1, 128, 4096, 256, False, num_cus=256)  # one 128-row block: split in 32-key tiles
     assert p.nsplit == 32 and p.workspace_bytes >= 32 * 128 * 257 * 4
     lib = sma.library()
