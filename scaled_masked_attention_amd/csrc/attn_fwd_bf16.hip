@@ -9,13 +9,14 @@
 // F16). The probabilities are rounded to the input's 16-bit type (nearest
 // even) for the P V product; the row sums use the fp32 probabilities.
 //
-// Head dims 32 and 64: 8 waves x 32 query rows = 256 rows, two waves per SIMD. Key
-// tiles of 64 rows go HBM/L2 -> LDS through buffer-resource direct-to-LDS loads
-// into a ring of four slots, two tiles ahead of their use, without passing
-// through registers; loads past the last key return zeros. Head dim 128 runs the
-// same scheme with two 32-row blocks per wave (512 rows, 32-key tiles) so that each
-// operand read from LDS feeds two MFMAs (attn_fwd_bf16_rb2_kernel), and head dim
-// 256 the role-split kernel (attn_fwd_bf16_rs_kernel), both further down.
+// Head dims 32 and 64, and 128 with a hard mask: 8 waves x 32 query rows = 256
+// rows, two waves per SIMD. Key tiles of 64 rows go HBM/L2 -> LDS through
+// buffer-resource direct-to-LDS loads into a ring of four slots, two tiles ahead of
+// their use, without passing through registers; loads past the last key return
+// zeros. Head dim 128 otherwise runs the same scheme with two 32-row blocks per wave
+// (512 rows, 32-key tiles) so that each operand read from LDS feeds two MFMAs
+// (attn_fwd_bf16_rb2_kernel), and head dim 256 the role-split kernel
+// (attn_fwd_bf16_rs_kernel), both further down.
 //
 // S^T = K Q^T: lane (m, h) supplies K[key m] and Q[query m] at head dims
 // h*D/2 + 8*step .. + 7 and receives the scores of query (lane % 32). K rows
@@ -71,7 +72,7 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 // waves 0-3 copy K, waves 4-7 copy V.
 template <int D>
 struct BGeom {
-  static_assert(D == 32 || D == 64, "the 32-row kernel's head dims (128: attn_fwd_bf16_rb2_kernel)");
+  static_assert(D == 32 || D == 64 || D == 128, "the 32-row kernel's head dims (128 with a hard mask)");
   static constexpr int kWaves = 8;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kQW = 32;                     // query rows per wave
@@ -839,7 +840,7 @@ hipError_t launch_bf16_rs(const FwdArgs& a, bool f16, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- two row blocks per wave
-// Head dim 128: each wave owns 64 query rows as two 32-row blocks,
+// Head dim 128 without a hard mask: each wave owns 64 query rows as two 32-row blocks,
 // so that every K operand of the score product and every V^T operand of the P V product
 // read from LDS feeds two MFMAs (one per row block) instead of one. 8 waves x 64 rows =
 // 512 rows per workgroup, two waves per SIMD; key tiles of 32 rows (a wave's two score
@@ -872,7 +873,7 @@ __device__ __forceinline__ unsigned pin_u(unsigned& x) {
 }
 __device__ __forceinline__ void pin_f16x(f32x16& c) { asm volatile("" : "+v"(c)); }
 
-template <bool CAUSAL, bool F16, bool MASKED>
+template <bool CAUSAL, bool F16>
 __global__ __launch_bounds__(B2Geom::kThreads) void attn_fwd_bf16_rb2_kernel(FwdArgs a) {
   using G = B2Geom;
   constexpr int D = G::D;
@@ -903,21 +904,6 @@ __global__ __launch_bounds__(B2Geom::kThreads) void attn_fwd_bf16_rb2_kernel(Fwd
   for (int rb = 0; rb < G::kRB; ++rb) {
     rb_lo[rb] = key_limit<CAUSAL>(min(qw0 + 32 * rb, a.seq_q - 1), a.seq_q, a.seq_kv, split_end);
     lim[rb] = key_limit<CAUSAL>(qw0 + 32 * rb + lm, a.seq_q, a.seq_kv, split_end);
-  }
-
-  // A hard mask, packed by columns (MaskColArgs) as for the 32-row kernel: each row block
-  // has one row-bit word per key and a class per 64-key tile (0 nothing admitted, 1
-  // everything, 2 mixed), read with scalar loads. A row block past the last query row
-  // reads nothing and counts as closed.
-  const uint32_t* mcols[G::kRB] = {};
-  const uint32_t* mcls[G::kRB] = {};
-  if (MASKED) {
-#pragma unroll
-    for (int rb = 0; rb < G::kRB; ++rb) {
-      const int64_t blk = qw0 / 32 + rb;
-      mcols[rb] = a.mask_bits + head_offset(t.bh, a.heads, a.mbits_sb, a.mbits_sh) + blk * a.mask_words;
-      mcls[rb] = a.mask_cls + head_offset(t.bh, a.heads, a.mcls_sb, a.mcls_sh) + blk * a.mask_tiles;
-    }
   }
 
   // Q operands of both row blocks in registers for the whole pass.
@@ -1020,7 +1006,7 @@ __global__ __launch_bounds__(B2Geom::kThreads) void attn_fwd_bf16_rb2_kernel(Fwd
   };
 
   // Scores of both row blocks, lazy running max and probabilities of tile T.
-  auto scores_and_p = [&](int32_t T, int slot, V8 (&pb)[G::kRB][2], const uint32_t (&cls)[G::kRB]) {
+  auto scores_and_p = [&](int32_t T, int slot, V8 (&pb)[G::kRB][2]) {
     const int32_t j0 = ks + T * G::kK;
     f32x16 sacc[G::kRB];
 #pragma unroll
@@ -1057,25 +1043,6 @@ __global__ __launch_bounds__(B2Geom::kThreads) void attn_fwd_bf16_rb2_kernel(Fwd
         asm volatile("" : "+v"(rel));
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[rb][r] = (16 * (r / 8) + (r % 8) < rel) ? sacc[rb][r] : -INFINITY;
-      }
-      if (MASKED && cls[rb] != 1u) {
-        // Score register r holds key 16(r/8) + r%8 (lanes 0-31) and that key + 8 (lanes
-        // 32-63); their two column words, stored side by side, are its lane mask. A row
-        // block the tile closes (class 0, while the other one is open) takes zero words.
-        const float ninf = -INFINITY;
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          typedef unsigned u32x16 __attribute__((ext_vector_type(16)));
-          u32x16 w = {};
-          if (cls[rb] == 2u) w = scalar_load<u32x16>(mcols[rb] + (j0 + 16 * g));
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint64_t lanes = (uint64_t)w[2 * i] | ((uint64_t)w[2 * i + 1] << 32);
-            float x = sacc[rb][8 * g + i];
-            asm("v_cndmask_b32_e64 %0, %1, %0, %2" : "+v"(x) : "v"(ninf), "s"(lanes));
-            sacc[rb][8 * g + i] = x;
-          }
-        }
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -1129,20 +1096,9 @@ __global__ __launch_bounds__(B2Geom::kThreads) void attn_fwd_bf16_rb2_kernel(Fwd
         late_pending = false;
       }
       const int slot = T % G::kSlots;
-      const int32_t j0 = ks + T * G::kK;
-      // The tile's mask class per row block (1 without a mask); a tile the mask closes for
-      // both is skipped.
-      uint32_t cls[G::kRB] = {1u, 1u};
-      bool open = true;
-      if (MASKED && wave_live && j0 < wave_hi) {
-#pragma unroll
-        for (int rb = 0; rb < G::kRB; ++rb)
-          cls[rb] = qw0 + 32 * rb < a.seq_q ? scalar_load<uint32_t>(mcls[rb] + j0 / 64) : 0u;
-        open = (cls[0] | cls[1]) != 0u;
-      }
-      if (wave_live && j0 < wave_hi && open) {
+      if (wave_live && ks + T * G::kK < wave_hi) {
         V8 pb[G::kRB][2];
-        scores_and_p(T, slot, pb, cls);
+        scores_and_p(T, slot, pb);
         if constexpr (kLate) {
 #pragma unroll
           for (int rb = 0; rb < G::kRB; ++rb)
@@ -1200,13 +1156,8 @@ __global__ __launch_bounds__(B2Geom::kThreads) void attn_fwd_bf16_rb2_kernel(Fwd
 template <bool CAUSAL>
 hipError_t launch_bf16_rb2(const FwdArgs& a, bool f16, hipStream_t s) {
   const dim3 grid(a.nwg), block(B2Geom::kThreads);
-  if (a.mask_bits) {
-    if (f16) hipLaunchKernelGGL((attn_fwd_bf16_rb2_kernel<CAUSAL, true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_fwd_bf16_rb2_kernel<CAUSAL, false, true>), grid, block, 0, s, a);
-  } else {
-    if (f16) hipLaunchKernelGGL((attn_fwd_bf16_rb2_kernel<CAUSAL, true, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_fwd_bf16_rb2_kernel<CAUSAL, false, false>), grid, block, 0, s, a);
-  }
+  if (f16) hipLaunchKernelGGL((attn_fwd_bf16_rb2_kernel<CAUSAL, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((attn_fwd_bf16_rb2_kernel<CAUSAL, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -1216,6 +1167,8 @@ hipError_t launch_bf16_variant(const FwdArgs& a, bool f16, hipStream_t s) {
   if (a.mask_bits) {
     if (f16) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, true, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, false, true>), grid, block, 0, s, a);
+  } else if constexpr (D == 128) {  // head dim 128 without a mask runs attn_fwd_bf16_rb2_kernel
+    return hipErrorInvalidValue;
   } else {
     if (f16) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, true, false>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, false, false>), grid, block, 0, s, a);
@@ -1229,7 +1182,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, bool causal, bool f16
   switch (head_dim) {
     case 32: return causal ? launch_bf16_variant<32, true>(a, f16, s) : launch_bf16_variant<32, false>(a, f16, s);
     case 64: return causal ? launch_bf16_variant<64, true>(a, f16, s) : launch_bf16_variant<64, false>(a, f16, s);
-    case 128: return causal ? launch_bf16_rb2<true>(a, f16, s) : launch_bf16_rb2<false>(a, f16, s);
+    case 128:  // with a hard mask the 32-row kernel (the planner's geometry follows)
+      if (a.mask_bits) return causal ? launch_bf16_variant<128, true>(a, f16, s) : launch_bf16_variant<128, false>(a, f16, s);
+      return causal ? launch_bf16_rb2<true>(a, f16, s) : launch_bf16_rb2<false>(a, f16, s);
     case 256: return causal ? launch_bf16_rs<true>(a, f16, s) : launch_bf16_rs<false>(a, f16, s);
     default: return hipErrorInvalidValue;
   }

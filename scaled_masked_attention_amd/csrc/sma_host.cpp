@@ -29,6 +29,7 @@ struct Shape {
   size_t row_elems;                      // elements between consecutive rows of one head
   size_t bh, rows;                       // batch*heads, batch*heads*seq_q
   size_t q_bytes, kv_bytes, o_bytes, lse_bytes;
+  bool masked;                           // a hard mask (the 16-bit kernel at head dim 128 differs)
 };
 
 bool mul(size_t a, size_t b, size_t* out) {
@@ -86,17 +87,22 @@ struct Plan {
   size_t part_lse_off = 0;   // byte offset of the partial LSE array in the workspace
 };
 
-int queries_per_wg(int kernel, size_t d) {
+// The 16-bit kernel at head dim 128 takes two 32-row blocks per wave (512 rows, 32-key
+// tiles) without a hard mask; with one it runs the 32-row kernel of the other head dims,
+// whose 64-key tiles read the mask's column words half as often per key.
+int queries_per_wg(int kernel, const Shape& s) {
   switch (kernel) {
     case SMA_KERNEL_F32_KSPLIT: return sma::kF32WsplitQueriesPerWG;
     case SMA_KERNEL_BF16_QBLOCK:
-      return d == 256 ? sma::kBF16D256QueriesPerWG : d == 128 ? sma::kBF16D128QueriesPerWG : sma::kBF16QueriesPerWG;
+      return s.d == 256 ? sma::kBF16D256QueriesPerWG
+             : s.d == 128 && !s.masked ? sma::kBF16D128QueriesPerWG : sma::kBF16QueriesPerWG;
     default: return sma::kF32QueriesPerWG;
   }
 }
-int keys_per_tile(int kernel, size_t d) {
+int keys_per_tile(int kernel, const Shape& s) {
   if (kernel == SMA_KERNEL_BF16_QBLOCK)
-    return d == 256 ? sma::kBF16D256KeysPerTile : d == 128 ? sma::kBF16D128KeysPerTile : sma::kBF16KeysPerTile;
+    return s.d == 256 ? sma::kBF16D256KeysPerTile
+           : s.d == 128 && !s.masked ? sma::kBF16D128KeysPerTile : sma::kBF16KeysPerTile;
   return sma::kF32KeysPerTile;
 }
 bool kernel_fits_dtype(int kernel, int in_dtype) {
@@ -110,7 +116,7 @@ size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 // GPU: aim for one resident workgroup per slot, keep at least four key tiles
 // per split.
 size_t auto_splits(const Shape& s, int kernel, size_t base, int num_cus) {
-  const size_t kt = (size_t)keys_per_tile(kernel, s.d);
+  const size_t kt = (size_t)keys_per_tile(kernel, s);
   // Resident workgroups per CU: one for the 16-bit kernel and for head dim 256
   // (LDS-limited), two otherwise.
   const size_t per_cu = kernel == SMA_KERNEL_BF16_QBLOCK || s.d > 128 ? 1 : 2;
@@ -160,8 +166,8 @@ int auto_kernel(const Shape& s, int num_cus) {
 Plan plan_for(const Shape& s, int kernel, size_t nsplit, int num_cus) {
   Plan p;
   p.kernel = kernel;
-  const size_t qpw = (size_t)queries_per_wg(kernel, s.d);
-  const size_t kt = (size_t)keys_per_tile(kernel, s.d);
+  const size_t qpw = (size_t)queries_per_wg(kernel, s);
+  const size_t kt = (size_t)keys_per_tile(kernel, s);
   p.nqb = (int32_t)((s.seq_q + qpw - 1) / qpw);
   const size_t base = s.bh * (size_t)p.nqb;
   if (kernel == SMA_KERNEL_F32_KSPLIT || s.seq_kv == 0) nsplit = 1;
@@ -349,6 +355,7 @@ int fwd_core(const void* q, const void* k, const void* v, void* o, float* lse, i
                         scale, workspace, workspace_bytes, &sh, layout);
   if (st != SMA_OK) return st;
   const bool masked = mask.mask != nullptr;
+  sh.masked = masked;
   if (masked || mask.batches || mask.heads) {
     if (!masked && sh.rows > 0 && seq_kv > 0) return SMA_ERR_NULL_POINTER;
     st = check_mask(sh, mask, o, lse, workspace, workspace_bytes);
@@ -594,12 +601,14 @@ size_t sma_attention_fwd_masked_workspace_bytes(int in_dtype, size_t batch, size
   m.batches = mask_batches;
   m.heads = mask_heads;
   if ((mask_batches != 1 && mask_batches != batch) || (mask_heads != 1 && mask_heads != heads)) return 0;
-  // The packed mask, then what the library's key split needs on the current device.
-  sma_plan p;
-  if (sma_attention_fwd_plan(in_dtype, batch, heads, seq_q, seq_kv, head_dim, causal, layout,
-                             SMA_KERNEL_AUTO, 0, 0, &p) != SMA_OK)
-    return 0;
-  return mask_bits_bytes(sh, m) + p.workspace_bytes;
+  // The packed mask, then what the library's key split needs on the current device (the
+  // plan of a masked call, whose geometry can differ from the unmasked one).
+  (void)causal;
+  sh.masked = true;
+  int cus = 0;
+  if (current_device_cus(&cus) != SMA_OK) cus = 256;
+  const size_t split = sh.rows > 0 ? auto_plan(sh, cus).ws_bytes : 0;
+  return mask_bits_bytes(sh, m) + split;
 }
 
 int sma_attention_fwd_timed(const void* q, const void* k, const void* v, void* o, float* lse,

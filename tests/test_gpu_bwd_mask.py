@@ -107,13 +107,24 @@ def test_masked_backward_parity(causal, d, density, form, dtype):
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_all_ones_mask_is_bitwise_the_unmasked_backward(dtype, causal):
+    """Both calls take the same O and LSE (the unmasked forward's: with a mask the 16-bit
+    forward at head dim 128 runs another kernel, whose O differs in its roundings), so only
+    the backward's mask path is compared."""
+    import torch
+
+    import scaled_masked_attention_amd as sma
+
     (q, k, v), bits = gen.random_case(1610, (1, 3, 200, 128), (1, 3, 230, 128), dtype=dtype)
     g = gen.upstream_grad(1610, (1, 3, 200, 128))
-    ones = np.ones((1, 1, 200, 230), np.uint8)
-    a = _run(q, k, v, bits, g, ones, 0.09, causal, dtype)
-    b = _run(q, k, v, bits, g, None, 0.09, causal, dtype)
+    tq, tk, tv = to_device((q, k, v), bits, dtype)
+    tg = torch.from_numpy(np.ascontiguousarray(g)).to("cuda")
+    ones = torch.ones((1, 1, 200, 230), dtype=torch.uint8, device="cuda")
+    o, lse = sma.attention_fwd(tq, tk, tv, scale=0.09, causal=causal, return_lse=True)
+    a = sma.attention_bwd(tq, tk, tv, o, lse, tg, scale=0.09, causal=causal, mask=ones)
+    b = sma.attention_bwd(tq, tk, tv, o, lse, tg, scale=0.09, causal=causal)
+    torch.cuda.synchronize()
     for x, y in zip(a, b):
-        assert np.array_equal(x.cpu().numpy(), y.cpu().numpy())
+        assert torch.equal(x, y)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
