@@ -932,18 +932,25 @@ __global__ __launch_bounds__(B2Geom::kThreads) void attn_fwd_bf16_rb2_kernel(Fwd
   const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(static_cast<const unsigned short*>(a.v) + kv_off, kv_bytes);
   // Thread (wave, lane) fills LDS chunk p = 64 wave + lane of each tile: row rho = p / 16,
   // position pc = p % 16, holding logical chunk pc ^ swizzle of the (permuted) row.
-  // The lane's offsets are formed again at each copy from an opaque lane index, rather
-  // than held in registers across the step loop.
+  // The lane's source offsets are formed again at each copy from an opaque lane index
+  // rather than held in registers across the step loop. LDS chunk 64 wave + lane is tile
+  // row rho = 4 wave + t (t = lane / 16), position lane % 16: with bits 2 and 3 of rho
+  // swapped for K, that row is 4 swap01(wave) + t, and the K swizzle 4 (wave % 4) + t and
+  // the V swizzle 4 t are XORed into the position. Only t and what depends on it are
+  // per lane; the rest is wave-uniform.
+  static_assert(G::kChunksPerRow == 16, "row and chunk of a copied LDS chunk by shifts");
+  const unsigned uw = (unsigned)wave;
+  const unsigned k_row0 = 4u * ((uw & 4u) | ((uw & 1u) << 1) | ((uw & 2u) >> 1));
   auto issue_tile = [&](int32_t T) {
-    int ln = lane;
+    unsigned ln = (unsigned)lane;
     asm volatile("" : "+v"(ln));
-    const int rho = (64 * wave + ln) / G::kChunksPerRow;
-    const int pc = ln % G::kChunksPerRow;
+    const unsigned t = ln >> 4, pc = ln & 15u;
+    const unsigned tk = t * kv_row;
     const unsigned tile_ofs = (unsigned)(ks + T * G::kK) * kv_row;
     const int slot = T % G::kSlots;
-    dma_load_x4(k_rsrc, (unsigned)swap_bits_2_3(rho) * kv_row + 16u * (unsigned)(pc ^ k_swz<D>(rho)) + tile_ofs,
+    dma_load_x4(k_rsrc, tk + 16u * (pc ^ (4u * (uw & 3u) + t)) + (tile_ofs + k_row0 * kv_row),
                 lds_address(&k_lds[slot][1024 * wave]));
-    dma_load_x4(v_rsrc, (unsigned)rho * kv_row + 16u * (unsigned)(pc ^ v_swz<D>(rho)) + tile_ofs,
+    dma_load_x4(v_rsrc, tk + 16u * (pc ^ (4u * t)) + (tile_ofs + 4u * uw * kv_row),
                 lds_address(&v_lds[slot][1024 * wave]));
   };
 
@@ -1018,7 +1025,7 @@ __global__ __launch_bounds__(B2Geom::kThreads) void attn_fwd_bf16_rb2_kernel(Fwd
       const unsigned x = pin_u(kb) ^ (16u * (unsigned)st);
       return __builtin_bit_cast(V8, *(__attribute__((address_space(3))) const u32x4*)(size_t)x);
     };
-    constexpr int kPf = 2;
+    constexpr int kPf = 1;  // each K operand feeds two MFMAs: one step ahead is two MFMAs
     V8 kop[kPf + 1];
 #pragma unroll
     for (int st = 0; st < kPf; ++st) kop[st] = k_operand(st);
@@ -1048,10 +1055,12 @@ __global__ __launch_bounds__(B2Geom::kThreads) void attn_fwd_bf16_rb2_kernel(Fwd
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[rb][r]);
       {
+        // The two key halves of query m (lanes m and m + 32). Scores are never NaN, so a
+        // plain v_max_f32 does without the canonicalizing maxes fmaxf would add.
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        asm("v_max_f32 %0, %1, %2" : "=v"(mx) : "v"(__uint_as_float(sw[0])), "v"(__uint_as_float(sw[1])));
       }
-      const float tmax = mx == -INFINITY ? -INFINITY : mx * c;
+      const float tmax = mx * c;  // c > 0: -inf stays -inf
       if (__any(tmax > m_run[rb] + kTau)) {
         const float m_new = fmaxf(m_run[rb], tmax);
         const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - (m_new == -INFINITY ? 0.f : m_new));
