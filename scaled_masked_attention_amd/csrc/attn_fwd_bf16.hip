@@ -367,9 +367,10 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
     {  // lanes m and m + 32 hold the two key halves of query m (a VALU swap, not an LDS round trip)
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                        false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      // scores are never NaN: a plain v_max_f32, without fmaxf's canonicalizing maxes
+      asm("v_max_f32 %0, %1, %2" : "=v"(mx) : "v"(__uint_as_float(sw[0])), "v"(__uint_as_float(sw[1])));
     }
-    const float tmax = mx == -INFINITY ? -INFINITY : mx * c;
+    const float tmax = mx * c;  // c > 0: -inf stays -inf
     if (__any(tmax > m_run + kTau)) {
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
@@ -699,9 +700,9 @@ __global__ __launch_bounds__(RGeom<D>::kThreads) void attn_fwd_bf16_rs_kernel(Fw
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                          false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        asm("v_max_f32 %0, %1, %2" : "=v"(mx) : "v"(__uint_as_float(sw[0])), "v"(__uint_as_float(sw[1])));
       }
-      const float tmax = mx == -INFINITY ? -INFINITY : mx * c;
+      const float tmax = mx * c;  // c > 0: -inf stays -inf
       float alpha = 1.f;
       if (__any(tmax > m_run + kTau)) {
         const float m_new = fmaxf(m_run, tmax);
