@@ -640,6 +640,359 @@ __global__ __launch_bounds__(64 * KVGeom<D>::kWaves) void attn_bwd_dkdv_bf16_ker
                 acc[cb][4 * g4 + 3] * mul};
 }
 
+// Head dim 128: the same roles with two key blocks per wave, so that each Q or dO operand
+// read from LDS (row or transposing) feeds two MFMAs, one per key block. A workgroup owns
+// 256 keys as 8 key blocks and 8 waves: for pair p, the P wave p keeps K of key blocks
+// 2p and 2p + 1 (64 registers) and their dV accumulators (128), the dS wave 4 + p their V
+// and dK accumulators. Query block T's Q and dO tiles, lse2/D and, with a hard mask, the
+// eight key blocks' words of its rows go through a 4-slot ring two steps ahead; P leaves
+// the P wave through LDS (fp32, double buffered, per key block). Operand reads are
+// streamed at XOR-formed addresses and lse2, D and the mask bits are read late and in
+// small pieces, which keeps each role inside the 256 registers of two waves per SIMD.
+struct KV2Geom {
+  static constexpr int D = 128;
+  static constexpr int kPairs = 4;
+  static constexpr int kWaves = 2 * kPairs;
+  static constexpr int kKBW = 2;                  // key blocks per wave
+  static constexpr int kKB = kPairs * kKBW;       // key blocks per workgroup
+  static constexpr int kKeys = 32 * kKB;
+  static constexpr int kSlots = 4;
+  static constexpr int kTileCopies = 2 * HGeom<D>::kDmaPerTile;  // Q and dO of one block
+  static constexpr int kTileCopiesPerWave = kTileCopies / kWaves;
+  static constexpr int kXBytes = 16 * 64 * 4;     // one key block's 16 P values per lane
+  static_assert(kTileCopiesPerWave * kWaves == kTileCopies, "copy split");
+  static_assert(kKB == 2 * kPairs && kPairs == 4, "mask copies: P wave w takes key blocks 2w, 2w + 1");
+};
+
+template <bool CAUSAL, bool MASKED, bool F16>
+__global__ __launch_bounds__(64 * KV2Geom::kWaves) void attn_bwd_dkdv_bf16_kb2_kernel(BwdArgs a) {
+  constexpr int D = KV2Geom::D;
+  using G = HGeom<D>;
+  using W = KV2Geom;
+  // Slot: Q tile, dO tile, lse2/D, and with a hard mask [key block][row] words; every tile on
+  // a multiple of 256 bytes (the XOR-formed addresses).
+  constexpr int kMaskBytes = MASKED ? W::kKB * G::kRows * 4 : 0;
+  constexpr int kSlotBytes = (2 * G::kTileBytes + G::kMetaBytes + kMaskBytes + 255) / 256 * 256;
+  constexpr int kRingBytes = W::kSlots * kSlotBytes;
+  constexpr int kLdsBytes = kRingBytes + 2 * W::kKB * W::kXBytes;
+  static_assert(2 * W::kKB * G::kTileBytes <= kLdsBytes, "K and V stage through the LDS");
+  __shared__ __attribute__((aligned(256))) unsigned char lds[kLdsBytes];
+  unsigned char* const xbuf = lds + kRingBytes;  // [key block][parity][4][64 lanes][4 floats]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool pwave = wave < W::kPairs;
+  const int pair = pwave ? wave : wave - W::kPairs;
+  const int lm = lane & 31;
+  const int lh = lane >> 5;
+
+  const uint32_t nkw = (uint32_t)(a.nkb + W::kKB - 1) / W::kKB;
+  const uint32_t lam = xcd_remap(blockIdx.x, a.nwg);
+  const int64_t bh = (int64_t)(lam / nkw);
+  const int32_t j0 = (int32_t)(lam % nkw) * W::kKeys;
+  const int32_t jk0 = j0 + 64 * pair;  // this pair's first key (key blocks 2p, 2p + 1)
+  const int32_t delta = a.seq_kv - a.seq_q;
+  int32_t qb_first = 0;
+  if (CAUSAL) {
+    const int32_t i_min = j0 - delta;
+    qb_first = i_min <= 0 ? 0 : i_min / G::kRows;
+  }
+  const int32_t nblk = a.nqb > qb_first ? a.nqb - qb_first : 0;
+
+  const int64_t q_off = head_offset(bh, a.heads, a.qs_b, a.qs_h);
+  const int64_t kv_off = head_offset(bh, a.heads, a.kvs_b, a.kvs_h);
+  const unsigned q_row = (unsigned)(a.qs_s * 2), kv_row = (unsigned)(a.kvs_s * 2);
+  const unsigned g_row = (unsigned)G::kRowBytes;
+  const __amdgpu_buffer_rsrc_t q_rsrc = raw_buffer(a.q16 + q_off, strided_range(a.seq_q, a.qs_s, D, 2));
+  const __amdgpu_buffer_rsrc_t g_rsrc =
+      raw_buffer(a.dout16 + (size_t)bh * a.seq_q * D, (unsigned)a.seq_q * g_row);
+  const __amdgpu_buffer_rsrc_t m_rsrc =
+      raw_buffer(a.meta + (size_t)bh * a.nqb * kBwdMetaFloats, (unsigned)a.nqb * (unsigned)G::kMetaBytes);
+  __amdgpu_buffer_rsrc_t w_rsrc;
+  if (MASKED)
+    w_rsrc = raw_buffer(a.mask_bits + head_offset(bh, a.heads, a.mbits_sb, a.mbits_sh),
+                        (unsigned)a.seq_q * (unsigned)a.mask_words * 4u);
+
+  // Copies of query block T into its ring slot: the Q and dO tiles split over the waves;
+  // the P waves add lse2/D (wave 0) and the mask words (wave w: key blocks 2w + lane / 32,
+  // row lane % 32). `pw` compiles those out of the dS waves' loop.
+  // The lane's source offsets are formed again at each copy from an opaque lane index
+  // rather than held in registers across the step loop. Wave w's copy of a tile (Q for
+  // u = 0, dO for u = 1) is LDS rows 4 w + t (t = lane / 16), whose source rows are
+  // swap_bits_2_3(4 w) + t and whose chunk position lane % 16 holds logical chunk
+  // (lane % 16) ^ (4 t + w % 4): what tile_src gives, with only t per lane.
+  static_assert(W::kTileCopiesPerWave == 2 && G::kDmaPerTile == W::kWaves && G::kChunks == 16,
+                "one Q and one dO copy per wave, 16 chunks per row");
+  const unsigned src_row0 = (unsigned)swap_bits_2_3(4 * wave);
+  auto issue = [&](int32_t T, auto pw) {
+    constexpr bool kP = decltype(pw)::value;
+    unsigned ln = (unsigned)lane;
+    asm volatile("" : "+v"(ln));
+    const unsigned t = ln >> 4;
+    const unsigned x = 16u * ((ln & 15u) ^ (4u * t + (unsigned)(wave & 3)));
+    const unsigned r0 = (unsigned)(G::kRows * (qb_first + T)) + src_row0;
+    unsigned char* const slot = lds + (T % W::kSlots) * kSlotBytes;
+    dma_load_x4(q_rsrc, (r0 + t) * q_row + x, lds_address(slot + 1024 * wave));
+    dma_load_x4(g_rsrc, (r0 + t) * g_row + x, lds_address(slot + 1024 * (G::kDmaPerTile + wave)));
+    const int32_t qb = qb_first + T;
+    if (kP && wave == 0)
+      dma_load_x1(m_rsrc, (unsigned)qb * (unsigned)G::kMetaBytes + 4u * ln, lds_address(slot + 2 * G::kTileBytes));
+    if (MASKED && kP) {
+      const unsigned kbw = 2u * (unsigned)wave + (ln >> 5);
+      dma_load_x1(w_rsrc, ((unsigned)(G::kRows * qb) + (ln & 31u)) * (unsigned)a.mask_words * 4u +
+                              ((unsigned)(j0 / 32) + kbw) * 4u,
+                  lds_address(slot + 2 * G::kTileBytes + G::kMetaBytes + 256 * wave));
+    }
+  };
+  const int copies_per_block = W::kTileCopiesPerWave + (pwave && wave == 0 ? 1 : 0) + (MASKED && pwave ? 1 : 0);
+
+  // K (P waves) or V (dS waves) of the pair's two key blocks, staged through the LDS, into
+  // B operands: lane (key m, h) holds head dims 16 st + 8 h .. + 7 of key jk0 + 32 b + m.
+  const unsigned kv_range = strided_range(a.seq_kv, a.kvs_s, D, 2);
+  bf16x8 kv[W::kKBW][G::kSteps];
+  {
+    const __amdgpu_buffer_rsrc_t k_rsrc = raw_buffer(a.k16 + kv_off, kv_range);
+    const __amdgpu_buffer_rsrc_t v_rsrc = raw_buffer(a.v16 + kv_off, kv_range);
+    constexpr int kCopies = 2 * W::kKB * G::kDmaPerTile;  // K tiles, then V tiles
+#pragma unroll
+    for (int u = 0; u < kCopies / W::kWaves; ++u) {
+      const int c = u * W::kWaves + wave;
+      const int tensor = c / (W::kKB * G::kDmaPerTile), kbc = (c / G::kDmaPerTile) % W::kKB, t = c % G::kDmaPerTile;
+      const unsigned src = (unsigned)(j0 + 32 * kbc) * kv_row + tile_src<D, false>(t, lane, kv_row);
+      dma_load_x4(tensor == 0 ? k_rsrc : v_rsrc, src, lds_address(lds + 1024 * c));
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < W::kKBW; ++b) {
+      const unsigned char* tile = lds + ((pwave ? 0 : W::kKB) + 2 * pair + b) * G::kTileBytes;
+#pragma unroll
+      for (int st = 0; st < G::kSteps; ++st) kv[b][st] = row_chunk<D>(tile, lm, 2 * st + lh);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the operand reads have returned
+    __syncthreads();                     // before the ring takes the space
+  }
+
+  f32x16 acc[W::kKBW][G::kNch];  // dV (P waves) or dK (dS waves) of the two key blocks
+#pragma unroll
+  for (int b = 0; b < W::kKBW; ++b)
+#pragma unroll
+    for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[b][cb][r] = 0.f;
+
+  // Whether query block qb admits a key of the pair (then the pair computes both key
+  // blocks: the causal bound excludes what the second one does not admit).
+  auto reaches = [&](int32_t qb) {
+    return jk0 < a.seq_kv && (!CAUSAL || G::kRows * qb + G::kRows - 1 + delta >= jk0);
+  };
+
+  auto run_steps = [&](auto pw, auto&& work) {
+    if (nblk > 0) issue(0, pw);
+    if (nblk > 1) issue(1, pw);
+    for (int32_t T = 0; T <= nblk; ++T) {
+      if (T + 1 < nblk) wait_vmcnt_n(copies_per_block);
+      else wait_vmcnt<0>();
+      __syncthreads();  // block T has landed; step T - 1 is done with its slots and P
+      if (T + 2 < nblk) issue(T + 2, pw);
+      work(T);
+    }
+  };
+
+  // Read bases from an opaque lane index, formed in each step (a few instructions) rather
+  // than held in registers across it.
+  auto opaque_lane = [&]() {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    return ln;
+  };
+
+  if (pwave) {
+    bf16x8 pp_late[W::kKBW][2];
+    bool pending = false;
+    const unsigned char* g_late = lds;
+    run_steps(std::true_type{}, [&](int32_t T) {
+      if (pending) {  // dV^T += dO^T P of the previous block, for both key blocks
+        __builtin_amdgcn_s_setprio(1);
+        const int ln = opaque_lane();
+        unsigned tl = tr_base<D>(lds_address(g_late), ln, false);
+        unsigned th = tr_base<D>(lds_address(g_late), ln, true);
+        mfma_stream<2 * G::kNch, 2>(
+            [&](int i) { return tr_read<D>(pin(tl), pin(th), i / G::kNch, i % G::kNch); },
+            [&](int i, bf16x8 x) {
+#pragma unroll
+              for (int b = 0; b < W::kKBW; ++b) {
+                acc[b][i % G::kNch] = mfma16<F16>(x, pp_late[b][i / G::kNch], acc[b][i % G::kNch]);
+                pin_acc(acc[b][i % G::kNch]);
+              }
+            });
+        __builtin_amdgcn_s_setprio(0);
+        pending = false;
+      }
+      const int32_t qb = qb_first + T;
+      if (T < nblk && reaches(qb)) {
+        const int32_t i0 = G::kRows * qb;
+        const unsigned char* const q_slot = lds + (T % W::kSlots) * kSlotBytes;
+        const unsigned char* const g_slot = q_slot + G::kTileBytes;
+        const unsigned char* const m_slot = g_slot + G::kTileBytes;
+        f32x16 s[W::kKBW];
+#pragma unroll
+        for (int b = 0; b < W::kKBW; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[b][r] = 0.f;
+        __builtin_amdgcn_s_setprio(1);
+        const int lq = opaque_lane();
+        unsigned rb = row_base<D>(lds_address(q_slot), lq & 31, lq >> 5);
+        mfma_stream<G::kSteps, 1>([&](int st) { return row_read(pin(rb), st); },
+                                  [&](int st, bf16x8 x) {
+#pragma unroll
+                                    for (int b = 0; b < W::kKBW; ++b) {
+                                      s[b] = mfma16<F16>(x, kv[b][st], s[b]);
+                                      pin_acc(s[b]);
+                                    }
+                                  });
+        __builtin_amdgcn_s_setprio(0);
+        unsigned ma = lds_address(m_slot) + 32u * (unsigned)lh;  // lse2 of rows 16t + 8 lh + 0..7
+        pin(ma);
+        bf16x8 pp[W::kKBW][2];
+#pragma unroll
+        for (int b = 0; b < W::kKBW; ++b) {
+          const int32_t jk = jk0 + 32 * b;
+          uint32_t mbits = 0;  // bit r: row perm_acc_row(r, lh) admits key jk + lm
+          if (MASKED) {
+            unsigned wa = lds_address(m_slot + G::kMetaBytes + 4 * G::kRows * (2 * pair + b)) + 32u * (unsigned)lh;
+            pin(wa);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const u32x4 w4 =
+                  *(__attribute__((address_space(3))) const u32x4*)(size_t)(wa + 4u * (16 * (q4 / 2) + 4 * (q4 % 2)));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) mbits |= ((w4[e] >> lm) & 1u) << (4 * q4 + e);
+            }
+            asm volatile("" : "+v"(mbits));
+          }
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {  // exponents in place of the scores
+            const f32x4 l4 =
+                *(__attribute__((address_space(3))) const f32x4*)(size_t)(ma + 4u * (16 * (q4 / 2) + 4 * (q4 % 2)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[b][4 * q4 + e] = s[b][4 * q4 + e] * a.c - l4[e];
+          }
+          if (CAUSAL && jk + G::kRows - 1 > i0 + delta) {
+            // Key jk + lm is admitted to row i0 + perm_acc_row(r, lh) iff
+            // 16 (r / 8) + r % 8 >= rel. The empty asm keeps the bound, and with it the
+            // comparisons, inside this branch.
+            int32_t rel = jk + lm - i0 - delta - 8 * lh;
+            asm volatile("" : "+v"(rel));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[b][r] = 16 * (r / 8) + r % 8 >= rel ? s[b][r] : -INFINITY;
+          }
+          if (MASKED) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[b][r] = ((mbits >> r) & 1u) ? s[b][r] : -INFINITY;
+          }
+          unsigned char* const xp = xbuf + ((2 * (2 * pair + b)) + (T & 1)) * W::kXBytes + 16 * lane;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4 p4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * q4 + e;
+              const float p = __builtin_amdgcn_exp2f(s[b][r]);
+              p4[e] = p;
+              pp[b][r / 8][r % 8] = round16<F16>(p);
+            }
+            *reinterpret_cast<f32x4*>(xp + 1024 * q4) = p4;
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < W::kKBW; ++b) {
+          pp_late[b][0] = pp[b][0];
+          pp_late[b][1] = pp[b][1];
+        }
+        g_late = g_slot;
+        pending = true;
+      }
+    });
+  } else {
+    run_steps(std::false_type{}, [&](int32_t T) {
+      const int32_t qb = qb_first + T - 1;
+      if (T >= 1 && reaches(qb)) {
+        const unsigned char* const q_slot = lds + ((T - 1) % W::kSlots) * kSlotBytes;
+        const unsigned char* const g_slot = q_slot + G::kTileBytes;
+        const unsigned char* const m_slot = g_slot + G::kTileBytes;
+        f32x16 dp[W::kKBW];
+#pragma unroll
+        for (int b = 0; b < W::kKBW; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dp[b][r] = 0.f;
+        __builtin_amdgcn_s_setprio(1);
+        const int lq = opaque_lane();
+        unsigned rb = row_base<D>(lds_address(g_slot), lq & 31, lq >> 5);
+        mfma_stream<G::kSteps, 1>([&](int st) { return row_read(pin(rb), st); },
+                                  [&](int st, bf16x8 x) {
+#pragma unroll
+                                    for (int b = 0; b < W::kKBW; ++b) {
+                                      dp[b] = mfma16<F16>(x, kv[b][st], dp[b]);
+                                      pin_acc(dp[b]);
+                                    }
+                                  });
+        __builtin_amdgcn_s_setprio(0);
+        unsigned da = lds_address(m_slot) + 4u * (unsigned)G::kRows + 32u * (unsigned)lh;  // D of the same rows
+        pin(da);
+        bf16x8 pds[W::kKBW][2];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 d4 =
+              *(__attribute__((address_space(3))) const f32x4*)(size_t)(da + 4u * (16 * (q4 / 2) + 4 * (q4 % 2)));
+#pragma unroll
+          for (int b = 0; b < W::kKBW; ++b) {
+            const f32x4 p4 = *reinterpret_cast<const f32x4*>(
+                xbuf + ((2 * (2 * pair + b)) + ((T - 1) & 1)) * W::kXBytes + 16 * lane + 1024 * q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * q4 + e;
+              pds[b][r / 8][r % 8] = round16<F16>(p4[e] * (dp[b][r] - d4[e]));
+            }
+          }
+        }
+        // dK^T += Q^T dS for both key blocks (the scale is applied once, at the end)
+        __builtin_amdgcn_s_setprio(1);
+        const int ln = opaque_lane();
+        unsigned tl = tr_base<D>(lds_address(q_slot), ln, false);
+        unsigned th = tr_base<D>(lds_address(q_slot), ln, true);
+        mfma_stream<2 * G::kNch, 2>(
+            [&](int i) { return tr_read<D>(pin(tl), pin(th), i / G::kNch, i % G::kNch); },
+            [&](int i, bf16x8 x) {
+#pragma unroll
+              for (int b = 0; b < W::kKBW; ++b) {
+                acc[b][i % G::kNch] = mfma16<F16>(x, pds[b][i / G::kNch], acc[b][i % G::kNch]);
+                pin_acc(acc[b][i % G::kNch]);
+              }
+            });
+        __builtin_amdgcn_s_setprio(0);
+      }
+    });
+  }
+
+  // Lane (key m, h) holds head dims 32 cb + 8 g4 + 4 h .. + 3 of key jk0 + 32 b + m.
+  const float mul = pwave ? 1.0f : a.scale;
+#pragma unroll
+  for (int b = 0; b < W::kKBW; ++b) {
+    const int32_t j = jk0 + 32 * b + lm;
+    if (j >= a.seq_kv) continue;
+    float* const out = (pwave ? a.dv : a.dk) + kv_off + (int64_t)j * a.kvs_s;
+#pragma unroll
+    for (int cb = 0; cb < G::kNch; ++cb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(out + 32 * cb + 8 * g4 + 4 * lh) =
+            f32x4{acc[b][cb][4 * g4] * mul, acc[b][cb][4 * g4 + 1] * mul, acc[b][cb][4 * g4 + 2] * mul,
+                  acc[b][cb][4 * g4 + 3] * mul};
+  }
+}
+
 // ---------------------------------------------------------------- dQ
 
 // A workgroup owns 256 queries of one (batch, head), a 32-row block per wave; each wave
@@ -1083,9 +1436,15 @@ hipError_t launch_bwd_bf16_variant(const BwdArgs& a0, hipStream_t s, hipEvent_t 
   }
   if (ev_pre && hipEventRecord(ev_pre, s) != hipSuccess) return hipErrorInvalidValue;
   if (nk > 0) {
-    a.nwg = (uint32_t)(a.bh * ((a.nkb + KVGeom<D>::kKB - 1) / KVGeom<D>::kKB));
-    hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, CAUSAL, MASKED, F16>), dim3(a.nwg),
-                       dim3(64 * KVGeom<D>::kWaves), 0, s, a);
+    if constexpr (D == 128) {
+      a.nwg = (uint32_t)(a.bh * ((a.nkb + KV2Geom::kKB - 1) / KV2Geom::kKB));
+      hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kb2_kernel<CAUSAL, MASKED, F16>), dim3(a.nwg),
+                         dim3(64 * KV2Geom::kWaves), 0, s, a);
+    } else {
+      a.nwg = (uint32_t)(a.bh * ((a.nkb + KVGeom<D>::kKB - 1) / KVGeom<D>::kKB));
+      hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, CAUSAL, MASKED, F16>), dim3(a.nwg),
+                         dim3(64 * KVGeom<D>::kWaves), 0, s, a);
+    }
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   if (ev_dkdv && hipEventRecord(ev_dkdv, s) != hipSuccess) return hipErrorInvalidValue;
