@@ -306,6 +306,7 @@ def read_traffic(kernel_function: str, workload: str, kernel_src_digest: str):
 KERNEL_SOURCES = {"attn_fwd_f32_kernel": ["attn_fwd_f32.hip", "attn_common.h"],
                   "attn_bwd_dkdv_f32_kernel": ["attn_bwd_f32.hip", "attn_common.h"],
                   "attn_bwd_dkdv_bf16_kernel": ["attn_bwd_bf16.hip", "attn_common.h"],
+                  "attn_bwd_dkdv_bf16_kb2_kernel": ["attn_bwd_bf16.hip", "attn_common.h"],
                   "attn_fwd_f32_wsplit_kernel": ["attn_fwd_f32_wsplit.hip", "attn_common.h"],
                   "attn_fwd_bf16_kernel": ["attn_fwd_bf16.hip", "attn_common.h"],
                   "attn_fwd_bf16_rs_kernel": ["attn_fwd_bf16.hip", "attn_common.h"],
@@ -515,7 +516,8 @@ def bench_bwd(args, w, name):
     pairs = allowed_pairs(w)
     kernel_flops = 8.0 * d * pairs  # S, dP, dV and dK: four products over the admitted pairs
     achieved = kernel_flops / (k_avg * 1e-3) / 1e12
-    kname = "attn_bwd_dkdv_f32_kernel" if w.dtype == "f32" else "attn_bwd_dkdv_bf16_kernel"
+    kname = ("attn_bwd_dkdv_f32_kernel" if w.dtype == "f32" else
+             "attn_bwd_dkdv_bf16_kb2_kernel" if d == 128 else "attn_bwd_dkdv_bf16_kernel")
     traffic = read_traffic(kname, name, kernel_source_digest(kname))
     line = {
         "metric": BWD_METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -529,7 +531,8 @@ def bench_bwd(args, w, name):
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": f"{kname}<{d},{str(w.causal).lower()}" + (",f16>" if w.dtype == "f16" else ">"),
+                     "kernel": (f"{kname}<{str(w.causal).lower()}" if kname.endswith("kb2_kernel")
+                                else f"{kname}<{d},{str(w.causal).lower()}") + (",f16>" if w.dtype == "f16" else ">"),
                      "kernel_avg_ms": round(k_avg, 5), "kernel_ms": step_stats(launches),
                      "frac_at_sampled_sclk": clock_adjusted(achieved / peak, clock_info),
                      "kernel_timing": "HIP events recorded by the library around each dK/dV launch",
