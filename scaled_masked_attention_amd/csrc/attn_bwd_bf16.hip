@@ -1022,8 +1022,11 @@ __global__ __launch_bounds__(64 * QGeom<D>::kWaves) void attn_bwd_dq_bf16_kernel
   using W = QGeom<D>;
   // Slot: K tile, V tile, and with a hard mask the workgroup rows' words of the key block.
   constexpr int kMaskBytes = MASKED ? 4 * W::kQ : 0;
-  constexpr int kSlotBytes = 2 * G::kTileBytes + kMaskBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[W::kSlots * kSlotBytes];
+  // Head dim 128 reads its tiles at XOR-formed addresses (row_read, tr_read): every tile
+  // starts on a multiple of 256 bytes.
+  constexpr int kAlign = D == 128 ? 2 * D : 16;
+  constexpr int kSlotBytes = (2 * G::kTileBytes + kMaskBytes + kAlign - 1) / kAlign * kAlign;
+  __shared__ __attribute__((aligned(kAlign))) unsigned char lds[W::kSlots * kSlotBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1114,9 +1117,20 @@ __global__ __launch_bounds__(64 * QGeom<D>::kWaves) void attn_bwd_dq_bf16_kernel
   // dQ^T += K^T dS^T for the block in k_slot.
   auto dq_product = [&](const unsigned char* k_slot, const bf16x8 (&pds)[2]) {
     __builtin_amdgcn_s_setprio(1);
-    mfma_stream<2 * G::kNch, kPf>(
-        [&](int i) { return tr_operand<D>(k_slot, lane, i / G::kNch, i % G::kNch); },
-        [&](int i, bf16x8 x) { dq[i % G::kNch] = mfma16<F16>(x, pds[i / G::kNch], dq[i % G::kNch]); });
+    if constexpr (D == 128) {
+      unsigned tl = tr_base<D>(lds_address(k_slot), lane, false);
+      unsigned th = tr_base<D>(lds_address(k_slot), lane, true);
+      mfma_stream<2 * G::kNch, kPf>(
+          [&](int i) { return tr_read<D>(pin(tl), pin(th), i / G::kNch, i % G::kNch); },
+          [&](int i, bf16x8 x) {
+            dq[i % G::kNch] = mfma16<F16>(x, pds[i / G::kNch], dq[i % G::kNch]);
+            pin_acc(dq[i % G::kNch]);
+          });
+    } else {
+      mfma_stream<2 * G::kNch, kPf>(
+          [&](int i) { return tr_operand<D>(k_slot, lane, i / G::kNch, i % G::kNch); },
+          [&](int i, bf16x8 x) { dq[i % G::kNch] = mfma16<F16>(x, pds[i / G::kNch], dq[i % G::kNch]); });
+    }
     __builtin_amdgcn_s_setprio(0);
   };
   // Waves 4-7 (each sharing a SIMD with wave - 4) run their dQ product of block T at the
@@ -1147,12 +1161,27 @@ __global__ __launch_bounds__(64 * QGeom<D>::kWaves) void attn_bwd_dq_bf16_kernel
     for (int r = 0; r < 16; ++r) dp[r] = s[r] = 0.f;
     __builtin_amdgcn_s_setprio(1);
     // dP^T and S^T, their k-steps interleaved.
-    mfma_stream<2 * G::kSteps, kPf>(
-        [&](int i) { return row_chunk<D>(i % 2 ? k_slot : v_slot, lm, 2 * (i / 2) + lh); },
-        [&](int i, bf16x8 x) {
-          if (i % 2) s = mfma16<F16>(x, qr[i / 2], s);
-          else dp = mfma16<F16>(x, gr[i / 2], dp);
-        });
+    if constexpr (D == 128) {
+      unsigned kb = row_base<D>(lds_address(k_slot), lm, lh), vb = row_base<D>(lds_address(v_slot), lm, lh);
+      mfma_stream<2 * G::kSteps, kPf>(
+          [&](int i) { return row_read(i % 2 ? pin(kb) : pin(vb), i / 2); },
+          [&](int i, bf16x8 x) {
+            if (i % 2) {
+              s = mfma16<F16>(x, qr[i / 2], s);
+              pin_acc(s);
+            } else {
+              dp = mfma16<F16>(x, gr[i / 2], dp);
+              pin_acc(dp);
+            }
+          });
+    } else {
+      mfma_stream<2 * G::kSteps, kPf>(
+          [&](int i) { return row_chunk<D>(i % 2 ? k_slot : v_slot, lm, 2 * (i / 2) + lh); },
+          [&](int i, bf16x8 x) {
+            if (i % 2) s = mfma16<F16>(x, qr[i / 2], s);
+            else dp = mfma16<F16>(x, gr[i / 2], dp);
+          });
+    }
     __builtin_amdgcn_s_setprio(0);
     float t[16];
 #pragma unroll
