@@ -845,7 +845,8 @@ hipError_t launch_bf16_rs(const FwdArgs& a, bool f16, hipStream_t s) {
 // so that every K operand of the score product and every V^T operand of the P V product
 // read from LDS feeds two MFMAs (one per row block) instead of one. 8 waves x 64 rows =
 // 512 rows per workgroup, two waves per SIMD; key tiles of 32 rows (a wave's two score
-// blocks then take 32 registers) in a ring of four LDS slots, two tiles ahead. LDS
+// blocks then take 32 registers) in a ring of eight LDS slots, copied a pair at a time
+// two tiles ahead, with one workgroup barrier per pair of tiles. LDS
 // addresses are formed inside the step from one base register and an XOR constant (the
 // swizzles only flip bits 4..7 of a row's byte offset), and the operand reads are
 // streamed ahead of their MFMAs, pinned there by empty asm.
@@ -858,7 +859,7 @@ struct B2Geom {
   static constexpr int kQW = 32 * kRB;               // query rows per wave
   static constexpr int kQ = kWaves * kQW;            // query rows per workgroup
   static constexpr int kK = 32;                      // keys per tile
-  static constexpr int kSlots = 4;
+  static constexpr int kSlots = 8;                  // tiles T-1 .. T+3 live at step T
   static constexpr int kChunksPerRow = D / 8;        // 16
   static constexpr int kTileChunks = kK * kChunksPerRow;  // 512: one per thread and tensor
   static constexpr int kTileBytes = 16 * kTileChunks;
@@ -1097,10 +1098,15 @@ __global__ __launch_bounds__(B2Geom::kThreads) void attn_fwd_bf16_rb2_kernel(Fwd
     if (ntiles > 0) issue_tile(0);
     if (ntiles > 1) issue_tile(1);
     for (int32_t T = 0; T < ntiles; ++T) {
-      if (T + 1 < ntiles) wait_vmcnt<2>();
-      else wait_vmcnt<0>();
-      __syncthreads();
-      if (T + 2 < ntiles) issue_tile(T + 2);
+      // One barrier per pair of tiles: at an even step both tiles of the pair have
+      // landed (nothing else is in flight) and the next pair goes into slots whose
+      // tiles every wave finished two or more steps ago.
+      if ((T & 1) == 0) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (T + 2 < ntiles) issue_tile(T + 2);
+        if (T + 3 < ntiles) issue_tile(T + 3);
+      }
       if (kLate && late_pending) {
         pv_tile(late_slot, pb_late);
         late_pending = false;
