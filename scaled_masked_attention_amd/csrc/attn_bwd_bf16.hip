@@ -999,15 +999,16 @@ __global__ __launch_bounds__(64 * KV2Geom::kWaves) void attn_bwd_dkdv_bf16_kb2_k
 // keeps its rows' Q and dO in registers as the B operands of S^T = K Q^T and
 // dP^T = V dO^T, and accumulates dQ^T += K^T dS^T. The waves step through the key blocks
 // the workgroup's rows admit together: key block T's K and V tiles (permuted) and, with a
-// hard mask, the rows' words of block T are copied straight into a ring of four LDS slots
-// two steps ahead, each wave issuing a share; waves 4-7 run each block's dQ product one
-// step late, so that block stays in the ring a step longer. One barrier per step.
+// hard mask, the rows' words of block T are copied straight into a ring of eight LDS
+// slots, a pair of blocks at a time two steps ahead, each wave issuing a share; waves 4-7
+// run each block's dQ product one step late, so that block stays in the ring a step
+// longer. One barrier per pair of steps.
 template <int D>
 struct QGeom {
   static_assert(D <= 128, "head dim 256 runs attn_bwd_dq_bf16_rs_kernel");
   static constexpr int kWaves = 8;
   static constexpr int kQ = 32 * kWaves;  // queries per workgroup
-  static constexpr int kSlots = 4;
+  static constexpr int kSlots = 8;  // blocks T - 1 .. T + 3 live in step T
   static constexpr int kDma = HGeom<D>::kDmaPerTile;
   static constexpr int kTileCopies = 2 * kDma;  // K and V of one block
   // As for the dK/dV kernel: d = 32 has four copies, one for each of waves 0..3.
@@ -1079,9 +1080,6 @@ __global__ __launch_bounds__(64 * QGeom<D>::kWaves) void attn_bwd_dq_bf16_kernel
       dma_load_x1(w_rsrc, ((unsigned)(q0 + 64 * wave + lane) * (unsigned)a.mask_words + (unsigned)T) * 4u,
                   lds_address(slot + 2 * G::kTileBytes + 256 * wave));
   };
-  // Wait until at most the copies of the last n blocks issued are in flight.
-  const int copies_per_block = (wave < W::kTileCopies ? W::kTileCopiesPerWave : 0) + (MASKED && wave < W::kQ / 64 ? 1 : 0);
-  auto wait_blocks = [&](int n) { wait_vmcnt_n(copies_per_block * min(n, 2)); };
 
   // This wave's rows: lse2 and D (the preprocess pads past seq_q), and Q and dO as B
   // operands: lane (query m, h) holds head dims 16*st + 8*h .. + 7 of row qw0 + m (zeros
@@ -1140,14 +1138,19 @@ __global__ __launch_bounds__(64 * QGeom<D>::kWaves) void attn_bwd_dq_bf16_kernel
   bf16x8 pds_late[2];
   bool pending = false;
   const unsigned char* late_slot = lds;
-  constexpr int kAhead = W::kSlots - 2;  // blocks copied ahead: a late wave still reads block T - 1
-#pragma unroll
-  for (int T = 0; T < kAhead; ++T)
-    if (T < nblk) issue(T);
+  // Blocks are copied a pair at a time, two steps ahead, with one barrier per pair: at an
+  // even step T blocks T and T + 1 have landed (nothing else is in flight) and every wave
+  // is done with step T - 1, so blocks T + 2 and T + 3 may take the slots of T - 6 and
+  // T - 5 (a late wave still reads block T - 1 in step T).
+  if (0 < nblk) issue(0);
+  if (1 < nblk) issue(1);
   for (int32_t T = 0; T < nblk; ++T) {
-    wait_blocks(min(nblk - 1 - T, kAhead - 1));
-    __syncthreads();  // block T has landed; step T - 1 is done with block T - 2's slot
-    if (T + kAhead < nblk) issue(T + kAhead);
+    if ((T & 1) == 0) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (T + 2 < nblk) issue(T + 2);
+      if (T + 3 < nblk) issue(T + 3);
+    }
     if (late && pending) {
       dq_product(late_slot, pds_late);
       pending = false;
