@@ -79,7 +79,8 @@ struct BGeom {
   static constexpr int kQ = kWaves * kQW;            // query rows per workgroup
   static constexpr int kK = kBF16KeysPerTile;        // keys per tile
   static constexpr int kKB = kK / 32;                // 32-key blocks per tile
-  static constexpr int kSlots = 4;                   // LDS ring of K/V tiles
+  // Five slots (all 160 KB of LDS at head dim 128): see the step loop.
+  static constexpr int kSlots = 5;                   // LDS ring of K/V tiles
   static constexpr int kChunksPerRow = D / 8;        // 16-byte chunks per K or V row
   static constexpr int kTileChunks = kK * kChunksPerRow;
   static constexpr bool kSplitKV = kTileChunks < kThreads;      // half the waves per tensor
@@ -219,9 +220,8 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
     mcols = a.mask_bits + head_offset(t.bh, a.heads, a.mbits_sb, a.mbits_sh) + rb * a.mask_words;
     mcls = a.mask_cls + head_offset(t.bh, a.heads, a.mcls_sb, a.mcls_sh) + rb * a.mask_tiles;
   }
-  auto issue_tile = [&](int32_t T) {
+  auto issue_tile = [&](int32_t T, int slot) {
     const unsigned row0 = (unsigned)(ks + T * G::kK);
-    const int slot = T % G::kSlots;
 #pragma unroll
     for (int u = 0; u < G::kLoadsPerThread; ++u) {
       const int base = (u * G::kCopyWaves + cw) * 64;
@@ -403,21 +403,24 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
   bool late_pending = false;
   int late_slot = 0;
 
-  // Tile T is loaded during steps T-2 and T-1 and used in step T (and in
-  // step T+1 by the late waves' PV). At the top of step T: tile T resident
-  // for every wave, every wave done with tile T-2, whose slot receives T+2.
-  if (ntiles > 0) issue_tile(0);
-  if (ntiles > 1) issue_tile(1);
+  // Tile T is copied in step T-2 and used in step T (and in step T+1 by the
+  // late waves' PV), with one barrier per pair of steps: at an even step T
+  // tiles T and T+1 are resident (nothing else is in flight). The last
+  // barrier before step T leaves every wave done with step T-2 at least, so
+  // the slot of tile T-3 is free for T+2; tiles T-1 .. T+2 are live.
+  if (ntiles > 0) issue_tile(0, 0);
+  if (ntiles > 1) issue_tile(1, 1);
+  int slot = 0, slot2 = 2;  // the slots of tiles T and T+2 (ring positions, wave-uniform)
   for (int32_t T = 0; T < ntiles; ++T) {
-    if (T + 1 < ntiles) wait_vmcnt<G::kLoadsPerTile>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    if (T + 2 < ntiles) issue_tile(T + 2);
+    if ((T & 1) == 0) {
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    if (T + 2 < ntiles) issue_tile(T + 2, slot2);
     if (late && late_pending) {
       pv_tile(late_slot, pb_late);
       late_pending = false;
     }
-    const int slot = T % G::kSlots;
     // The tile's mask class (1 without a mask); a tile the mask closes is skipped.
     uint32_t cls = 1u;
     if (MASKED && wave_live && ks + T * G::kK < wave_hi)
@@ -436,6 +439,8 @@ __global__ __launch_bounds__(BGeom<D>::kThreads) void attn_fwd_bf16_kernel(FwdAr
         pv_tile(slot, pb);
       }
     }
+    slot = slot + 1 == G::kSlots ? 0 : slot + 1;
+    slot2 = slot2 + 1 == G::kSlots ? 0 : slot2 + 1;
   }
   if (late_pending) pv_tile(late_slot, pb_late);
 
