@@ -11,9 +11,9 @@
 //
 // Head dims 32 and 64, and 128 with a hard mask: 8 waves x 32 query rows = 256
 // rows, two waves per SIMD. Key tiles of 64 rows go HBM/L2 -> LDS through
-// buffer-resource direct-to-LDS loads into a ring of four slots, two tiles ahead of
-// their use, without passing through registers; loads past the last key return
-// zeros. Head dim 128 otherwise runs the same scheme with two 32-row blocks per wave
+// buffer-resource direct-to-LDS loads into a ring of five slots, each two steps ahead
+// of its use and one workgroup barrier per pair of steps, without passing through
+// registers; loads past the last key return zeros. Head dim 128 otherwise runs the same scheme with two 32-row blocks per wave
 // (512 rows, 32-key tiles) so that each operand read from LDS feeds two MFMAs
 // (attn_fwd_bf16_rb2_kernel), and head dim 256 the role-split kernel
 // (attn_fwd_bf16_rs_kernel), both further down.
